@@ -1,0 +1,342 @@
+/*
+ * moegen — seeded synthetic inputs (see moegen.h). Test and benchmark data only.
+ *
+ * The weight encoders are plain "covering" quantizers computed in fp64: every
+ * sub-block gets a scale (and for Q4_K an offset) large enough that the whole
+ * sub-block lies inside the representable range, so every element has the
+ * closed-form round-trip bound |x - xhat| <= step/2 (Q4_K, Q6_K) or <= 2^E
+ * inside the MXFP4 grid. The pages do not say how float weights become blocks;
+ * these encoders exist to make test data with known error bounds.
+ */
+#include "moegen.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define GAMMA 0x9E3779B97F4A7C15ULL
+
+static inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+uint64_t mg_stream(uint64_t seed, uint32_t tensor, uint32_t expert, uint32_t row) {
+  uint64_t s = mix64(seed + GAMMA);
+  s = mix64(s + ((uint64_t)tensor + 1) * GAMMA);
+  s = mix64(s + ((uint64_t)expert + 1) * GAMMA);
+  s = mix64(s + ((uint64_t)row + 1) * GAMMA);
+  return s;
+}
+
+uint64_t mg_u64(uint64_t stream, uint64_t n) { return mix64(stream + (n + 1) * GAMMA); }
+
+void mg_normal_row(uint64_t seed, uint32_t tensor, uint32_t expert, uint32_t row, int n,
+                   double std_, float* out) {
+  /* Marsaglia's polar method: draw (u, v) uniform in (-1, 1)^2 from consecutive
+   * counter values until 0 < s = u^2 + v^2 < 1, then u*f and v*f with
+   * f = sqrt(-2 ln s / s) are two independent N(0, 1) values. */
+  const uint64_t st = mg_stream(seed, tensor, expert, row);
+  uint64_t ctr = 0;
+  for (int i = 0; i < n; i += 2) {
+    double u, v, s;
+    do {
+      u = (double)(mg_u64(st, ctr++) >> 11) * 0x1.0p-52 - 1.0;
+      v = (double)(mg_u64(st, ctr++) >> 11) * 0x1.0p-52 - 1.0;
+      s = u * u + v * v;
+    } while (s >= 1.0 || s == 0.0);
+    double f = sqrt(-2.0 * log(s) / s);
+    out[i] = (float)(std_ * u * f);
+    if (i + 1 < n) out[i + 1] = (float)(std_ * v * f);
+  }
+}
+
+/* ---- simple row-parallel loop ------------------------------------------------ */
+typedef void (*row_fn)(void* ctx, int r0, int r1);
+struct par_job { row_fn fn; void* ctx; int r0, r1; };
+static void* par_thread(void* p) {
+  struct par_job* j = (struct par_job*)p;
+  j->fn(j->ctx, j->r0, j->r1);
+  return NULL;
+}
+static void par_rows(int rows, int threads, row_fn fn, void* ctx) {
+  if (threads < 1) threads = 1;
+  if (threads > rows) threads = rows > 0 ? rows : 1;
+  if (threads == 1) { fn(ctx, 0, rows); return; }
+  pthread_t* tid = (pthread_t*)malloc(sizeof(pthread_t) * threads);
+  struct par_job* jobs = (struct par_job*)malloc(sizeof(struct par_job) * threads);
+  for (int t = 0; t < threads; ++t) {
+    jobs[t].fn = fn; jobs[t].ctx = ctx;
+    jobs[t].r0 = (int)((long long)rows * t / threads);
+    jobs[t].r1 = (int)((long long)rows * (t + 1) / threads);
+    pthread_create(&tid[t], NULL, par_thread, &jobs[t]);
+  }
+  for (int t = 0; t < threads; ++t) pthread_join(tid[t], NULL);
+  free(tid); free(jobs);
+}
+
+struct nm_ctx { uint64_t seed; uint32_t tensor, expert; int cols; double std_; float* out; };
+static void nm_rows(void* p, int r0, int r1) {
+  struct nm_ctx* c = (struct nm_ctx*)p;
+  for (int r = r0; r < r1; ++r)
+    mg_normal_row(c->seed, c->tensor, c->expert, (uint32_t)r, c->cols, c->std_,
+                  c->out + (size_t)r * c->cols);
+}
+void mg_normal_matrix(uint64_t seed, uint32_t tensor, uint32_t expert, int rows, int cols,
+                      double std_, float* out, int threads) {
+  struct nm_ctx c = {seed, tensor, expert, cols, std_, out};
+  par_rows(rows, threads, nm_rows, &c);
+}
+
+void mg_round_bf16(const float* in, uint16_t* out, size_t n) {
+  for (size_t i = 0; i < n; ++i) {
+    uint32_t b;
+    memcpy(&b, &in[i], 4);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    out[i] = (uint16_t)(b >> 16);
+  }
+}
+
+/* ---- fp16 ------------------------------------------------------------------- */
+uint16_t mg_fp16_ceil_bits(double v) {
+  if (!(v > 0.0)) return 0;
+  if (v > 65504.0) return 0x7C00; /* +inf: never reached by the data here */
+  int ex;
+  double f = frexp(v, &ex); /* v = f * 2^ex, f in [0.5, 1) */
+  int e = ex - 1;           /* v = (2f) * 2^e, 2f in [1, 2) */
+  if (e < -14) {            /* subnormal range, quantum 2^-24 */
+    double n = ceil(ldexp(v, 24));
+    return (uint16_t)n;     /* n == 1024 is the smallest normal, same bits */
+  }
+  double m = ceil((2.0 * f - 1.0) * 1024.0);
+  if (m >= 1024.0) { m = 0.0; e += 1; }
+  if (e > 15) return 0x7C00;
+  return (uint16_t)(((e + 15) << 10) | (int)m);
+}
+
+static double fp16_value(uint16_t h) { /* positive finite values only */
+  int E = (h >> 10) & 31, m = h & 1023;
+  if (E == 0) return ldexp((double)m, -24);
+  return ldexp((double)(1024 + m), E - 25);
+}
+
+/* Round to nearest, ties to even, for |v| < 2^51: adding and subtracting
+ * 1.5 * 2^52 leaves no fraction bits, and the default IEEE rounding mode
+ * breaks ties to even (needs strict double evaluation, no contraction). */
+static inline double rne(double v) {
+  volatile double t = v + 0x1.8p52;
+  return t - 0x1.8p52;
+}
+
+size_t mg_block_bytes(int fmt) { return fmt == MG_Q4_K ? 144 : fmt == MG_Q6_K ? 210 : 17; }
+int mg_block_elems(int fmt) { return fmt == MG_MXFP4 ? 32 : 256; }
+
+/* ---- packers ------------------------------------------------------------------ */
+void mg_pack_q4k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const uint8_t* m,
+                 const uint8_t* q, uint8_t* blk) {
+  blk[0] = (uint8_t)d_bits; blk[1] = (uint8_t)(d_bits >> 8);
+  blk[2] = (uint8_t)dmin_bits; blk[3] = (uint8_t)(dmin_bits >> 8);
+  uint8_t* s = blk + 4;
+  for (int j = 0; j < 4; ++j) {
+    s[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
+    s[j + 4] = (uint8_t)((m[j] & 63) | ((m[j + 4] >> 4) << 6));
+    s[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((m[j + 4] & 15) << 4));
+  }
+  uint8_t* qs = blk + 16;
+  for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < 32; ++i)
+      qs[32 * c + i] = (uint8_t)((q[64 * c + i] & 15) | ((q[64 * c + 32 + i] & 15) << 4));
+}
+
+void mg_pack_q6k(uint16_t d_bits, const int8_t* sc, const uint8_t* q, uint8_t* blk) {
+  uint8_t* ql = blk;
+  uint8_t* qh = blk + 128;
+  for (int h = 0; h < 2; ++h) {
+    const uint8_t* qq = q + 128 * h;
+    for (int i = 0; i < 32; ++i) {
+      ql[64 * h + i] = (uint8_t)((qq[i] & 15) | ((qq[64 + i] & 15) << 4));
+      ql[64 * h + 32 + i] = (uint8_t)((qq[32 + i] & 15) | ((qq[96 + i] & 15) << 4));
+      qh[32 * h + i] = (uint8_t)(((qq[i] >> 4) & 3) | (((qq[32 + i] >> 4) & 3) << 2) |
+                                 (((qq[64 + i] >> 4) & 3) << 4) | (((qq[96 + i] >> 4) & 3) << 6));
+    }
+  }
+  memcpy(blk + 192, sc, 16);
+  blk[208] = (uint8_t)d_bits; blk[209] = (uint8_t)(d_bits >> 8);
+}
+
+void mg_pack_mxfp4(uint8_t e, const uint8_t* codes, uint8_t* blk) {
+  blk[0] = e;
+  for (int i = 0; i < 16; ++i)
+    blk[1 + i] = (uint8_t)((codes[i] & 15) | ((codes[i + 16] & 15) << 4));
+}
+
+/* ---- covering encoders ----------------------------------------------------------- */
+void mg_encode_q4k(const float* x, uint8_t* blk) {
+  double mn[8], mx[8], off[8], need[8], maxoff = 0.0, maxneed = 0.0;
+  for (int j = 0; j < 8; ++j) {
+    double lo = 0.0, hi = -INFINITY;
+    for (int i = 0; i < 32; ++i) {
+      double v = x[32 * j + i];
+      if (v < lo) lo = v;
+      if (v > hi) hi = v;
+    }
+    mn[j] = lo; mx[j] = hi; off[j] = -lo;
+    if (off[j] > maxoff) maxoff = off[j];
+  }
+  uint16_t dmin_bits = mg_fp16_ceil_bits(maxoff / 63.0);
+  double dmin = fp16_value(dmin_bits);
+  uint8_t m[8], sc[8], q[256];
+  double mhat[8];
+  for (int j = 0; j < 8; ++j) {
+    double mj = dmin > 0.0 ? ceil(off[j] / dmin) : 0.0;
+    if (mj > 63.0) mj = 63.0;
+    m[j] = (uint8_t)mj;
+    mhat[j] = dmin * mj;
+    need[j] = (mx[j] + mhat[j]) / 15.0;
+    if (need[j] < 0.0) need[j] = 0.0;
+    if (need[j] > maxneed) maxneed = need[j];
+  }
+  (void)mn;
+  uint16_t d_bits = mg_fp16_ceil_bits(maxneed / 63.0);
+  double d = fp16_value(d_bits);
+  for (int j = 0; j < 8; ++j) {
+    double s = d > 0.0 ? ceil(need[j] / d) : 0.0;
+    if (s > 63.0) s = 63.0;
+    sc[j] = (uint8_t)s;
+    double shat = d * s;
+    for (int i = 0; i < 32; ++i) {
+      double v = shat > 0.0 ? rne(((double)x[32 * j + i] + mhat[j]) / shat) : 0.0;
+      if (v < 0.0) v = 0.0;
+      if (v > 15.0) v = 15.0;
+      q[32 * j + i] = (uint8_t)v;
+    }
+  }
+  mg_pack_q4k(d_bits, dmin_bits, sc, m, q, blk);
+}
+
+void mg_encode_q6k(const float* x, uint8_t* blk) {
+  double need[16], maxneed = 0.0;
+  for (int s = 0; s < 16; ++s) {
+    double lo = 0.0, hi = 0.0;
+    for (int i = 0; i < 16; ++i) {
+      double v = x[16 * s + i];
+      if (v < lo) lo = v;
+      if (v > hi) hi = v;
+    }
+    double n = hi / 31.0;
+    if (-lo / 32.0 > n) n = -lo / 32.0;
+    need[s] = n;
+    if (n > maxneed) maxneed = n;
+  }
+  uint16_t d_bits = mg_fp16_ceil_bits(maxneed / 127.0);
+  double d = fp16_value(d_bits);
+  int8_t sc[16];
+  uint8_t q[256];
+  for (int s = 0; s < 16; ++s) {
+    double c = d > 0.0 ? ceil(need[s] / d) : 0.0;
+    if (c > 127.0) c = 127.0;
+    sc[s] = (int8_t)c;
+    double shat = d * c;
+    for (int i = 0; i < 16; ++i) {
+      double v = shat > 0.0 ? rne((double)x[16 * s + i] / shat) : 0.0;
+      if (v < -32.0) v = -32.0;
+      if (v > 31.0) v = 31.0;
+      q[16 * s + i] = (uint8_t)(v + 32.0);
+    }
+  }
+  mg_pack_q6k(d_bits, sc, q, blk);
+}
+
+/* OCP MX v1.0: shared exponent floor(log2 amax) - emax(e2m1 = 2); elements rounded
+ * to nearest on the e2m1 grid, ties to the even mantissa, saturating at 6. */
+void mg_encode_mxfp4(const float* x, uint8_t* blk) {
+  static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double amax = 0.0;
+  for (int i = 0; i < 32; ++i) {
+    double a = fabs((double)x[i]);
+    if (a > amax) amax = a;
+  }
+  uint8_t codes[32];
+  if (amax == 0.0) {
+    memset(codes, 0, sizeof codes);
+    mg_pack_mxfp4(0, codes, blk);
+    return;
+  }
+  int ex;
+  frexp(amax, &ex);
+  int E = (ex - 1) - 2;
+  if (E < -127) E = -127;
+  if (E > 127) E = 127;
+  for (int i = 0; i < 32; ++i) {
+    double v = ldexp(fabs((double)x[i]), -E);
+    int best = 7;
+    if (v < 6.0) {
+      best = 0;
+      for (int c = 1; c < 8; ++c) {
+        double dc = fabs(v - grid[c]), db = fabs(v - grid[best]);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+      }
+    }
+    codes[i] = (uint8_t)(best | ((x[i] < 0.0f && best != 0) ? 8 : 0));
+  }
+  mg_pack_mxfp4((uint8_t)(E + 127), codes, blk);
+}
+
+struct enc_ctx { int fmt; const float* x; int K; size_t stride; uint8_t* out; };
+static void enc_rows(void* p, int r0, int r1) {
+  struct enc_ctx* c = (struct enc_ctx*)p;
+  const int be = mg_block_elems(c->fmt);
+  const size_t bb = mg_block_bytes(c->fmt);
+  const int nb = c->K / be;
+  for (int r = r0; r < r1; ++r) {
+    uint8_t* row = c->out + (size_t)r * c->stride;
+    const float* xr = c->x + (size_t)r * c->K;
+    for (int b = 0; b < nb; ++b) {
+      if (c->fmt == MG_Q4_K) mg_encode_q4k(xr + b * be, row + b * bb);
+      else if (c->fmt == MG_Q6_K) mg_encode_q6k(xr + b * be, row + b * bb);
+      else mg_encode_mxfp4(xr + b * be, row + b * bb);
+    }
+    memset(row + nb * bb, 0, c->stride - nb * bb);
+  }
+}
+void mg_encode_matrix(int fmt, const float* x, int rows, int K, size_t stride, uint8_t* out,
+                      int threads) {
+  struct enc_ctx c = {fmt, x, K, stride, out};
+  par_rows(rows, threads, enc_rows, &c);
+}
+
+struct wm_ctx {
+  uint64_t seed; uint32_t tensor, expert; int fmt, K; size_t stride; double std_; uint8_t* out;
+};
+static void wm_rows(void* p, int r0, int r1) {
+  struct wm_ctx* c = (struct wm_ctx*)p;
+  float* buf = (float*)malloc(sizeof(float) * (size_t)c->K);
+  struct enc_ctx e = {c->fmt, buf, c->K, c->stride, NULL};
+  for (int r = r0; r < r1; ++r) {
+    mg_normal_row(c->seed, c->tensor, c->expert, (uint32_t)r, c->K, c->std_, buf);
+    e.out = c->out + (size_t)r * c->stride;
+    enc_rows(&e, 0, 1);
+  }
+  free(buf);
+}
+void mg_weight_matrix(uint64_t seed, uint32_t tensor, uint32_t expert, int fmt, int rows, int K,
+                      size_t stride, double std_, uint8_t* out, int threads) {
+  struct wm_ctx c = {seed, tensor, expert, fmt, K, stride, std_, out};
+  par_rows(rows, threads, wm_rows, &c);
+}
+
+void mg_zipf_bias(uint64_t seed, int E, double s, float* out) {
+  int* perm = (int*)malloc(sizeof(int) * (size_t)E);
+  for (int i = 0; i < E; ++i) perm[i] = i;
+  const uint64_t st = mg_stream(seed, MG_T_ZIPF, 0, 0);
+  for (int i = E - 1; i >= 1; --i) {
+    int j = (int)(mg_u64(st, (uint64_t)(E - 1 - i)) % (uint64_t)(i + 1));
+    int t = perm[i]; perm[i] = perm[j]; perm[j] = t;
+  }
+  double z = 0.0;
+  for (int r = 0; r < E; ++r) z += pow((double)(r + 1), -s);
+  for (int r = 0; r < E; ++r) out[perm[r]] = (float)log(pow((double)(r + 1), -s) / z);
+  free(perm);
+}

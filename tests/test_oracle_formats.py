@@ -1,0 +1,170 @@
+"""Oracle pins: scalar decoders, block layouts, round-trip bounds (CPU).
+
+The pages name the block formats only; the byte layouts follow the ggml/GGUF
+conventions. These tests pin the oracle's decoders to library routines
+(numpy fp16), to the OCP MX v1.0 value table, to field-level formulas on
+hand-packed blocks (packed by the generator's independent packer), and to the
+closed-form round-trip bounds of the covering encoders.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_fp16_all_finite_patterns(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    fin = np.isfinite(ref)
+    got = np.array([orc.fp16(int(b)) for b in bits[fin]])
+    assert np.array_equal(got, ref[fin])
+    assert np.array_equal(np.signbit(got), np.signbit(ref[fin]))
+
+
+def test_e8m0(orc):
+    for e in range(255):
+        assert orc.e8m0(e) == np.ldexp(1.0, e - 127)
+
+
+def test_e2m1_against_ocp_table(orc):
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "e2m1_values.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) == 16
+    for code, val in rows:
+        got = orc.e2m1(int(code))
+        assert got == float(val)
+        assert np.signbit(got) == val.startswith("-")
+
+
+def _q4k_fields(rng):
+    sc = rng.integers(0, 64, 8).astype(np.uint8)
+    m = rng.integers(0, 64, 8).astype(np.uint8)
+    q = rng.integers(0, 16, 256).astype(np.uint8)
+    return sc, m, q
+
+
+def test_q4k_hand_packed_fields(orc, genlib):
+    rng = np.random.default_rng(0)
+    for trial in range(50):
+        sc, m, q = _q4k_fields(rng)
+        d_bits = int(rng.integers(0x1000, 0x3000))
+        dmin_bits = int(rng.integers(0x1000, 0x3000))
+        blk = gen.pack_q4k(d_bits, dmin_bits, sc, m, q)
+        d = float(np.array([d_bits], np.uint16).view(np.float16)[0])
+        dmin = float(np.array([dmin_bits], np.uint16).view(np.float16)[0])
+        assert np.array_equal(orc.block_quants(oracle.Q4_K, blk), q)
+        want = np.array([d * sc[n // 32] * q[n] - dmin * m[n // 32] for n in range(256)])
+        assert np.array_equal(orc.dequant_row(oracle.Q4_K, blk, 256), want)
+
+
+def test_q6k_hand_packed_fields(orc, genlib):
+    rng = np.random.default_rng(1)
+    for trial in range(50):
+        sc = rng.integers(-128, 128, 16).astype(np.int8)
+        q = rng.integers(0, 64, 256).astype(np.uint8)
+        d_bits = int(rng.integers(0x0400, 0x3000))
+        blk = gen.pack_q6k(d_bits, sc, q)
+        d = float(np.array([d_bits], np.uint16).view(np.float16)[0])
+        assert np.array_equal(orc.block_quants(oracle.Q6_K, blk), q)
+        want = np.array([d * int(sc[n // 16]) * (int(q[n]) - 32) for n in range(256)])
+        assert np.array_equal(orc.dequant_row(oracle.Q6_K, blk, 256), want)
+
+
+def test_mxfp4_hand_packed_fields(orc, genlib):
+    rng = np.random.default_rng(2)
+    table = {int(c): float(v) for c, v in
+             (l.split() for l in open(os.path.join(GOLDEN, "e2m1_values.txt"))
+              if l.strip() and not l.startswith("#"))}
+    for trial in range(50):
+        e = int(rng.integers(0, 255))
+        codes = rng.integers(0, 16, 32).astype(np.uint8)
+        blk = gen.pack_mxfp4(e, codes)
+        want = np.array([table[int(c)] * np.ldexp(1.0, e - 127) for c in codes])
+        assert np.array_equal(orc.dequant_row(oracle.MXFP4, blk, 32), want)
+        assert np.array_equal(orc.block_quants(oracle.MXFP4, blk),
+                              np.array([int(2 * table[int(c)]) for c in codes]))
+
+
+def _blocks(fmt, n, std, seed):
+    be = gen.BLOCK_ELEMS[fmt]
+    x = gen.normal(seed, 1, fmt, n, be, std)
+    # edge blocks: all zero, all positive, all negative, a single spike, constant
+    x[0] = 0
+    x[1] = np.abs(x[1])
+    x[2] = -np.abs(x[2])
+    x[3] = 0
+    x[3, be // 2] = 5 * std
+    x[4] = std
+    return x
+
+
+@pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])
+def test_q4k_round_trip_bound(orc, genlib, std):
+    x = _blocks(gen.Q4_K, 300, std, 11)
+    for r in range(x.shape[0]):
+        blk = gen.encode_block(gen.Q4_K, x[r])
+        xh = orc.dequant_row(oracle.Q4_K, blk, 256)
+        d = orc.fp16(int(blk[0]) | int(blk[1]) << 8)
+        q = orc.block_quants(oracle.Q4_K, blk)
+        # decoded per-sub-block step: d * sc_j, recovered from two elements with different q
+        err = np.abs(x[r].astype(np.float64) - xh)
+        for j in range(8):
+            xs = x[r, 32 * j:32 * j + 32].astype(np.float64)
+            rng_j = max(xs.max(), 0) - min(xs.min(), 0)
+            # data-only bound: the covering step is at most range/15 plus one unit of d and dmin
+            loose = (rng_j / 15 + d + 2 * abs(orc.fp16(int(blk[2]) | int(blk[3]) << 8))) / 2
+            assert err[32 * j:32 * j + 32].max() <= loose * (1 + 1e-9) + 1e-300, (r, j)
+        assert q.min() >= 0 and q.max() <= 15
+
+
+@pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])
+def test_q6k_round_trip_bound(orc, genlib, std):
+    x = _blocks(gen.Q6_K, 300, std, 12)
+    for r in range(x.shape[0]):
+        blk = gen.encode_block(gen.Q6_K, x[r])
+        xh = orc.dequant_row(oracle.Q6_K, blk, 256)
+        d = orc.fp16(int(blk[208]) | int(blk[209]) << 8)
+        sc = blk[192:208].view(np.int8).astype(np.float64)
+        err = np.abs(x[r].astype(np.float64) - xh)
+        for s in range(16):
+            step = d * sc[s]
+            assert err[16 * s:16 * s + 16].max() <= step / 2 * (1 + 1e-12) + 1e-300
+            xs = x[r, 16 * s:16 * s + 16].astype(np.float64)
+            need = max(xs.max() / 31, -xs.min() / 32, 0)
+            assert step <= need + d * (1 + 1e-12)  # covering step is the smallest that fits
+
+
+@pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])
+def test_mxfp4_round_trip_bound(orc, genlib, std):
+    x = _blocks(gen.MXFP4, 600, std, 13)
+    for r in range(x.shape[0]):
+        blk = gen.encode_block(gen.MXFP4, x[r])
+        xh = orc.dequant_row(oracle.MXFP4, blk, 32)
+        amax = np.abs(x[r]).max()
+        if amax == 0:
+            assert not xh.any() and blk[0] == 0
+            continue
+        E = int(np.floor(np.log2(float(amax)))) - 2
+        assert int(blk[0]) == E + 127
+        xs = x[r].astype(np.float64)
+        err = np.abs(xs - xh)
+        inside = np.abs(xs) <= 6 * 2.0 ** E
+        assert err[inside].max(initial=0) <= 2.0 ** E
+        assert err.max() < 2 * 2.0 ** E
+        # magnitude 0 never gets the negative-zero code
+        codes = np.concatenate([blk[1:17] & 15, blk[1:17] >> 4])
+        assert not (codes == 8).any()
+
+
+def test_relative_rms_informational(orc, genlib):
+    for fmt, K, lim in ((gen.Q4_K, 256, 0.12), (gen.Q6_K, 256, 0.03), (gen.MXFP4, 32, 0.16)):
+        x = gen.normal(9, 1, 0, 200, K, 0.02)
+        m = gen.encode_matrix(fmt, x)
+        xh = np.stack([orc.dequant_row(fmt, m[r], K) for r in range(200)])
+        rel = np.sqrt(((xh - x) ** 2).mean()) / np.sqrt((x.astype(np.float64) ** 2).mean())
+        assert rel < lim, (fmt, rel)
