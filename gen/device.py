@@ -1,0 +1,103 @@
+"""Upload a generated layer to the GPU and describe it to the library.
+
+Input plumbing for the tests and the benchmark: device tensors (torch), the
+per-expert device pointer tables and a filled ``MoeLayerDesc``. Layer copies
+are device-to-device clones at distinct addresses, so a rotation over copies
+reads HBM instead of caches.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import quantized_moe_expert_route_amd as M
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def x_to_device(data, x_np: np.ndarray | None = None, xb_np: np.ndarray | None = None,
+                device="cuda"):
+    """x as the layer receives it: fp32 [T, H], or bf16 when the workload says so.
+    Returns (tensor, dtype enum)."""
+    cfg = data.cfg
+    if cfg.x_bf16:
+        xb = data.x_bf16 if xb_np is None else xb_np
+        t = _dev(xb.view(np.int16), device).view(torch.bfloat16)
+        return t, M.MOE_DTYPE_BF16
+    x = data.x if x_np is None else x_np
+    return _dev(x.astype(np.float32), device), M.MOE_DTYPE_F32
+
+
+class DeviceLayer:
+    def __init__(self, data, copies: int = 1, present=None, route_scale=None, norm_topk=None,
+                 use_shared: bool = True, sh_gate_vec=None, sel_bias="data", device="cuda"):
+        cfg = data.cfg
+        self.cfg = cfg
+        self.device = device
+        E = cfg.E
+        present = np.ones(E, bool) if present is None else np.asarray(present, bool)
+        self.present = present
+        pool0 = _dev(data.pool, device)
+        self.pools = [pool0] + [pool0.clone() for _ in range(1, copies)]
+        self.w_router = _dev(data.w_router, device)
+        sb = data.sel_bias if isinstance(sel_bias, str) else sel_bias
+        self.sel_bias = None if sb is None else _dev(sb.astype(np.float32), device)
+        self.b_gate = self.b_up = self.b_down = None
+        if data.b_gate is not None:
+            self.b_gate = _dev(data.b_gate, device)
+            self.b_up = _dev(data.b_up, device)
+            self.b_down = _dev(data.b_down, device)
+        self.sh_gate_vec = None if sh_gate_vec is None else _dev(
+            np.asarray(sh_gate_vec, np.float32), device)
+        es = cfg.expert_bytes
+        self._tables = []
+        self.descs = []
+        for pool in self.pools:
+            base = pool.data_ptr()
+            g = [base + e * es if present[e] else 0 for e in range(E)]
+            u = [base + e * es + cfg.gate_bytes if present[e] else 0 for e in range(E)]
+            dn = [base + e * es + 2 * cfg.gate_bytes if present[e] else 0 for e in range(E)]
+            tg = torch.tensor(g, dtype=torch.int64, device=device)
+            tu = torch.tensor(u, dtype=torch.int64, device=device)
+            td = torch.tensor(dn, dtype=torch.int64, device=device)
+            keep = [tg, tu, td]
+            d = M.MoeLayerDesc()
+            d.hidden, d.ffn, d.n_expert, d.top_k = cfg.H, cfg.F, E, cfg.k
+            d.router = cfg.router
+            d.norm_topk = cfg.norm_topk if norm_topk is None else norm_topk
+            d.route_scale = cfg.route_scale if route_scale is None else route_scale
+            d.w_router = self.w_router.data_ptr()
+            d.sel_bias = None if self.sel_bias is None else self.sel_bias.data_ptr()
+            d.fmt_gate = d.fmt_up = cfg.fmt_gu
+            d.fmt_down = cfg.fmt_d
+            d.stride_gate = d.stride_up = cfg.stride_gu
+            d.stride_down = cfg.stride_d
+            d.gate, d.up, d.down = tg.data_ptr(), tu.data_ptr(), td.data_ptr()
+            if self.b_gate is not None:
+                bt = []
+                for b, n in ((self.b_gate, cfg.F), (self.b_up, cfg.F), (self.b_down, cfg.H)):
+                    t = torch.tensor([b.data_ptr() + e * n * 4 for e in range(E)],
+                                     dtype=torch.int64, device=device)
+                    bt.append(t)
+                keep += bt
+                d.b_gate, d.b_up, d.b_down = (t.data_ptr() for t in bt)
+            d.act = cfg.act
+            d.act_alpha, d.act_limit = cfg.act_alpha, cfg.act_limit
+            if cfg.shared and use_shared:
+                sh = base + E * es
+                d.sh_gate, d.sh_up, d.sh_down = sh, sh + cfg.gate_bytes, sh + 2 * cfg.gate_bytes
+            d.sh_gate_vec = None if self.sh_gate_vec is None else self.sh_gate_vec.data_ptr()
+            self._tables.append(keep)
+            self.descs.append(d)
+
+    @property
+    def desc(self) -> M.MoeLayerDesc:
+        return self.descs[0]
+
+    def workspace(self, T: int) -> torch.Tensor:
+        n = M.moe_workspace_size(self.desc, T)
+        if n == 0:
+            raise ValueError("invalid descriptor or token count")
+        return torch.empty(n, dtype=torch.uint8, device=self.device)

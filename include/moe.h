@@ -1,0 +1,213 @@
+/*
+ * moe.h — C ABI of the routed-expert MoE FFN layer for AMD Instinct MI355X (gfx950).
+ *
+ * One MoE layer, per token t of a chunk of T tokens:
+ *   1. x[t] is quantized per block to int8 with one fp32 scale (q8 activations).
+ *   2. A router scores all E experts, top-k picks k of them (ties go to the
+ *      lower expert index) and gives them routing weights (softmax or sigmoid).
+ *   3. Each selected expert's block-quantized gate/up rows are integer dot
+ *      products with q8(x), rescaled per quant block; SwiGLU gives h, which is
+ *      re-quantized to q8 and multiplied by the expert's down rows the same way.
+ *   4. y[t] = sum over the k slots of weight * expert output, plus an optional
+ *      always-on shared expert.
+ * Sources: the Pulsar README (model list: routers and experts of the supported
+ * families; numerics notes: activations quantized to q8_0/q8_K with integer
+ * dots; MoE expert resolve: launches get explicit per-expert gate/up/down
+ * device pointers and a NULL one means "not mine"; prefill notes: grouped
+ * int8 tensor-core MoE that rescales per quant block). Block layouts follow the
+ * ggml/GGUF conventions for Q4_K (144 B / 256 weights), Q6_K (210 B / 256) and
+ * OCP MX v1.0 for MXFP4 (17 B / 32).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; descriptors
+ *    and moe_qact structs are HOST structs read during the call only.
+ *  - Work is enqueued on the caller's stream and nothing else: no allocation,
+ *    no host synchronization, no device-to-host copy. Calls can be captured
+ *    into a HIP graph. Results are valid once the stream has synchronized.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is enqueued and the status says why. A failed kernel launch
+ *    returns MOE_EHIP. No C++ exception crosses this boundary.
+ *  - The library keeps no global mutable state; calls are reentrant. Two calls
+ *    that share a workspace must be ordered on one stream.
+ *  - Same inputs on the same path give the same bytes (no float atomics).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,         /* bad argument: NULL, shape, stride, alignment, enum */
+  MOE_EUNSUPPORTED = 2,   /* valid but not implemented combination */
+  MOE_ENOWORKSPACE = 3,   /* workspace smaller than moe_workspace_size() */
+  MOE_EHIP = 4            /* a HIP launch failed */
+} moe_status;
+
+/* Stored weight block formats. */
+typedef enum { MOE_WFMT_Q4_K = 0, MOE_WFMT_Q6_K = 1, MOE_WFMT_MXFP4 = 2 } moe_wfmt;
+/* Activation quant formats: Q8_K = blocks of 256 with 16-element sums
+ * (consumed by Q4_K and Q6_K rows); Q8_32 = blocks of 32 (MXFP4 rows). */
+typedef enum { MOE_AFMT_Q8_K = 0, MOE_AFMT_Q8_32 = 1 } moe_afmt;
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 } moe_router;
+/* SWIGLU: h = silu(g) * u. SWIGLU_OAI (gpt-oss): g' = min(g, limit),
+ * u' = clamp(u, -limit, limit), h = g' * sigmoid(alpha * g') * (u' + 1). */
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
+
+/* q8 activations of T rows of width H, structure-of-arrays:
+ *   qs    int8  [T, H]      quants, |q| <= 127
+ *   d     fp32  [T, H / B]  per-block scale (B = 256 for Q8_K, 32 for Q8_32), a = d * q
+ *   bsums int16 [T, H / 16] sum of the quants of each 16 elements (Q8_K only;
+ *                           NULL for Q8_32)
+ * All three are device pointers, 16-byte aligned. */
+typedef struct {
+  int8_t* qs;
+  float* d;
+  int16_t* bsums;
+  int32_t fmt; /* moe_afmt */
+  int32_t T;
+  int32_t H;
+} moe_qact;
+
+/* One MoE layer. Host struct; every pointer in it is a device pointer.
+ *  hidden (H), ffn (F): H and F must be multiples of the block size of the
+ *    formats that consume them (256 for Q4_K/Q6_K, 32 for MXFP4).
+ *  n_expert (E) in [1, MOE_MAX_EXPERTS], top_k (k) in [1, min(E, MOE_MAX_TOPK)].
+ *  router, norm_topk: SOFTMAX with norm_topk = 1 is the softmax over the k
+ *    selected logits; norm_topk = 0 is the softmax over all E evaluated at the
+ *    selected experts. SIGMOID: sigmoid of the selected logits, divided by
+ *    their sum when norm_topk = 1. Weights are then multiplied by route_scale.
+ *  w_router fp32 [E, H] row-major. Logits are accumulated in fp64 and rounded
+ *    once to fp32.
+ *  sel_bias fp32 [E] or NULL: added (one fp32 add) to the logits for selection
+ *    only; routing weights use the unbiased logits.
+ *  fmt_* / stride_*: weight format and row stride in bytes of the gate and up
+ *    matrices ([F rows of H]) and of down ([H rows of F]). Rows are contiguous
+ *    block streams; stride >= row bytes, stride % 16 == 0. gate and up must
+ *    have the same format.
+ *  gate, up, down: device arrays of E device pointers to each expert's
+ *    matrices (16-byte aligned). gate[e] == NULL means expert e is not present
+ *    here: its slots contribute nothing and the other weights are not
+ *    renormalized. When gate[e] != NULL, up[e] and down[e] must be valid.
+ *  b_gate, b_up ([F]) and b_down ([H]): NULL, or device arrays of E device
+ *    pointers to fp32 biases. Gate/up biases are added before the activation,
+ *    the down bias to the expert output before the routing weight.
+ *  act, act_alpha, act_limit: moe_act and its constants.
+ *  sh_gate, sh_up, sh_down: the shared expert (same formats, strides and
+ *    shape as the routed experts) or all NULL. sh_gate_vec fp32 [H] or NULL:
+ *    shared-expert weight sigmoid(sh_gate_vec . x), or 1 when NULL.
+ */
+typedef struct {
+  int32_t hidden;
+  int32_t ffn;
+  int32_t n_expert;
+  int32_t top_k;
+  int32_t router;
+  int32_t norm_topk;
+  float route_scale;
+  const float* w_router;
+  const float* sel_bias;
+  int32_t fmt_gate, fmt_up, fmt_down;
+  size_t stride_gate, stride_up, stride_down;
+  const void* const* gate;
+  const void* const* up;
+  const void* const* down;
+  const float* const* b_gate;
+  const float* const* b_up;
+  const float* const* b_down;
+  int32_t act;
+  float act_alpha;
+  float act_limit;
+  const void* sh_gate;
+  const void* sh_up;
+  const void* sh_down;
+  const float* sh_gate_vec;
+} moe_layer_desc;
+
+/* ABI version (MOE_ABI_VERSION) and a static message for a status. */
+MOE_API int moe_abi_version(void);
+MOE_API const char* moe_status_str(moe_status s);
+
+/* Bytes of device workspace (256-byte aligned base) that moe_route_topk,
+ * moe_expert_ffn and moe_layer_forward need for T tokens of this layer.
+ * Returns 0 if the descriptor or T is invalid. The workspace is scratch: its
+ * contents on entry do not matter. */
+MOE_API size_t moe_workspace_size(const moe_layer_desc* desc, int T);
+
+/* Activation quantization. x: device [T, H] fp32 or bf16 (bf16 is upcast
+ * exactly). Per block of B values: amax = max |x|; amax == 0 gives d = 0 and
+ * q = 0; otherwise iscale = 127/amax, q = clamp(rne(x * iscale), -127, 127) and
+ * d = amax/127, every step in IEEE fp32. out: host struct whose qs, d (and
+ * bsums for Q8_K) point to caller device buffers; fmt, T and H are filled in.
+ * Source: Pulsar README, numerics notes (activations quantized to q8_0/q8_K). */
+MOE_API moe_status moe_quantize_act_q8k(const void* x, moe_dtype dtype, int T, int H, moe_afmt fmt,
+                                moe_qact* out, hipStream_t stream);
+
+/* Router + top-k. x: device [T, H] (fp32 or bf16). Writes ids int32 [T, k]
+ * (experts in rank order: key descending, index ascending on ties, where key is
+ * the fp32 logit, plus sel_bias if set, with -0 treated as +0), w fp32 [T, k]
+ * routing weights, and logits fp32 [T, E] if non-NULL. ws: workspace of at
+ * least moe_workspace_size(desc, T) bytes.
+ * Source: Pulsar README, model list (softmax routers of qwen3moe/gpt-oss,
+ * sigmoid-gated routers with shared experts of the deepseek/qwen35 families). */
+MOE_API moe_status moe_route_topk(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
+                          int32_t* ids, float* w, float* logits, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Expert FFN for given routing. xq: q8 of x in the format the gate/up rows
+ * consume (Q8_K for Q4_K/Q6_K, Q8_32 for MXFP4). x: the unquantized input, only
+ * read when sh_gate_vec is set (else may be NULL). ids int32 [T, k], w fp32
+ * [T, k] device arrays (ids must lie in [0, E)). y fp32 [T, H] is overwritten.
+ * Source: Pulsar README, MoE expert resolve and numerics notes. */
+MOE_API moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq, const void* x,
+                          moe_dtype dtype, int T, const int32_t* ids, const float* w, float* y,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Whole layer: quantize, route, expert FFN. y fp32 [T, H] overwritten;
+ * ids_out [T, k] and w_out [T, k] are optional copies of the routing. */
+MOE_API moe_status moe_layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
+                             float* y, int32_t* ids_out, float* w_out, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward with timing hooks: if events is non-NULL, events[0] is
+ * recorded on the stream before the first kernel and events[i] right after the
+ * i-th kernel, for i < n_events. moe_layer_stage_count() gives how many
+ * kernels the call launches and moe_layer_stage_name() names them. */
+MOE_API moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, moe_dtype dtype,
+                                   int T, float* y, int32_t* ids_out, float* w_out, void* ws,
+                                   size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                                   int n_events);
+MOE_API int moe_layer_stage_count(const moe_layer_desc* desc, int T);
+MOE_API const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage);
+
+/* Test export: integer block partials of n_rows weight rows (device, K
+ * columns, byte stride `stride`) against token `token` of xq, computed by the
+ * same device routines the FFN kernels use. out int32 [n_rows, K / Bw, 2]:
+ *   Q4_K : (S1, S2) with S1 = sum_j sc_j * dot_j, S2 = sum_j m_j * (bsums of sub-block j)
+ *   Q6_K : (S, 0)   with S  = sum_s sc_s * sum_i (q_i - 32) * a_i
+ *   MXFP4: (S, 0)   with S  = sum_i (2 * e2m1_i) * a_i  */
+MOE_API moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,
+                               const moe_qact* xq, int token, int32_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,240 @@
+"""Python binding of the MI355X routed-expert MoE FFN library (libmoe_route.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in ``include/moe.h``. Functions keep the C names and
+argument order. Tensor arguments may be torch tensors (their device pointer is
+passed), raw integer addresses, or None (NULL). ``stream`` may be a
+``torch.cuda.Stream``, a raw ``hipStream_t`` integer, or None (torch's current
+stream). A non-OK status raises ``MoeError``.
+
+The library is built in-tree by ``quantized_moe_expert_route_amd._build.build()``;
+importing this module does not build it, and using it without the built library
+raises immediately (there is no fallback implementation).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_route.so")
+
+# enums (include/moe.h)
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOWORKSPACE, MOE_EHIP = range(5)
+MOE_WFMT_Q4_K, MOE_WFMT_Q6_K, MOE_WFMT_MXFP4 = range(3)
+MOE_AFMT_Q8_K, MOE_AFMT_Q8_32 = range(2)
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = range(2)
+MOE_ROUTER_SOFTMAX, MOE_ROUTER_SIGMOID = range(2)
+MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = range(2)
+MOE_MAX_EXPERTS = 1024
+MOE_MAX_TOPK = 16
+
+ABI_FUNCTIONS = (
+    "moe_abi_version", "moe_status_str", "moe_workspace_size", "moe_quantize_act_q8k",
+    "moe_route_topk", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_timed",
+    "moe_layer_stage_count", "moe_layer_stage_name", "moe_test_block_dots",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {moe_status_str(status)} (status {status})")
+
+
+class MoeQact(C.Structure):
+    _fields_ = [("qs", C.c_void_p), ("d", C.c_void_p), ("bsums", C.c_void_p),
+                ("fmt", C.c_int32), ("T", C.c_int32), ("H", C.c_int32)]
+
+
+class MoeLayerDesc(C.Structure):
+    _fields_ = [
+        ("hidden", C.c_int32), ("ffn", C.c_int32), ("n_expert", C.c_int32), ("top_k", C.c_int32),
+        ("router", C.c_int32), ("norm_topk", C.c_int32), ("route_scale", C.c_float),
+        ("w_router", C.c_void_p), ("sel_bias", C.c_void_p),
+        ("fmt_gate", C.c_int32), ("fmt_up", C.c_int32), ("fmt_down", C.c_int32),
+        ("stride_gate", C.c_size_t), ("stride_up", C.c_size_t), ("stride_down", C.c_size_t),
+        ("gate", C.c_void_p), ("up", C.c_void_p), ("down", C.c_void_p),
+        ("b_gate", C.c_void_p), ("b_up", C.c_void_p), ("b_down", C.c_void_p),
+        ("act", C.c_int32), ("act_alpha", C.c_float), ("act_limit", C.c_float),
+        ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
+        ("sh_gate_vec", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe_route.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "quantized_moe_expert_route_amd._build.build() (no fallback)")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, sz = C.c_void_p, C.c_int, C.c_size_t
+        D = C.POINTER(MoeLayerDesc)
+        Q = C.POINTER(MoeQact)
+        L.moe_abi_version.argtypes = []
+        L.moe_abi_version.restype = i32
+        L.moe_status_str.argtypes = [i32]
+        L.moe_status_str.restype = C.c_char_p
+        L.moe_workspace_size.argtypes = [D, i32]
+        L.moe_workspace_size.restype = sz
+        L.moe_quantize_act_q8k.argtypes = [vp, i32, i32, i32, i32, Q, vp]
+        L.moe_route_topk.argtypes = [D, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_ffn.argtypes = [D, Q, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_layer_forward.argtypes = [D, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_layer_forward_timed.argtypes = [D, vp, i32, i32, vp, vp, vp, vp, sz, vp,
+                                              C.POINTER(vp), i32]
+        L.moe_layer_stage_count.argtypes = [D, i32]
+        L.moe_layer_stage_count.restype = i32
+        L.moe_layer_stage_name.argtypes = [D, i32, i32]
+        L.moe_layer_stage_name.restype = C.c_char_p
+        L.moe_test_block_dots.argtypes = [i32, vp, i32, i32, sz, Q, i32, vp, vp]
+        for n in ("moe_quantize_act_q8k", "moe_route_topk", "moe_expert_ffn", "moe_layer_forward",
+                  "moe_layer_forward_timed", "moe_test_block_dots"):
+            getattr(L, n).restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    raise TypeError(f"cannot pass {type(t)} as a device pointer")
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(fn: str, st: int):
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_status_str(s: int) -> str:
+    return lib().moe_status_str(s).decode()
+
+
+def moe_workspace_size(desc: MoeLayerDesc, T: int) -> int:
+    return lib().moe_workspace_size(C.byref(desc), T)
+
+
+def moe_quantize_act_q8k(x, dtype: int, T: int, H: int, fmt: int, out: MoeQact, stream=None):
+    _check("moe_quantize_act_q8k",
+           lib().moe_quantize_act_q8k(_ptr(x), dtype, T, H, fmt, C.byref(out), _stream(stream)))
+
+
+def moe_route_topk(desc, x, dtype, T, ids, w, logits, ws, ws_bytes, stream=None):
+    _check("moe_route_topk",
+           lib().moe_route_topk(C.byref(desc), _ptr(x), dtype, T, _ptr(ids), _ptr(w),
+                                _ptr(logits), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_expert_ffn(desc, xq: MoeQact, x, dtype, T, ids, w, y, ws, ws_bytes, stream=None):
+    _check("moe_expert_ffn",
+           lib().moe_expert_ffn(C.byref(desc), C.byref(xq), _ptr(x), dtype, T, _ptr(ids),
+                                _ptr(w), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer_forward(desc, x, dtype, T, y, ids_out, w_out, ws, ws_bytes, stream=None):
+    _check("moe_layer_forward",
+           lib().moe_layer_forward(C.byref(desc), _ptr(x), dtype, T, _ptr(y), _ptr(ids_out),
+                                   _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer_forward_timed(desc, x, dtype, T, y, ids_out, w_out, ws, ws_bytes, stream,
+                            events: list[int]):
+    arr = (C.c_void_p * len(events))(*events)
+    _check("moe_layer_forward_timed",
+           lib().moe_layer_forward_timed(C.byref(desc), _ptr(x), dtype, T, _ptr(y),
+                                         _ptr(ids_out), _ptr(w_out), _ptr(ws), ws_bytes,
+                                         _stream(stream), arr, len(events)))
+
+
+def moe_layer_stage_count(desc, T: int) -> int:
+    return lib().moe_layer_stage_count(C.byref(desc), T)
+
+
+def moe_layer_stage_name(desc, T: int, stage: int) -> str | None:
+    r = lib().moe_layer_stage_name(C.byref(desc), T, stage)
+    return None if r is None else r.decode()
+
+
+def moe_test_block_dots(fmt, rows, n_rows, K, stride, xq: MoeQact, token, out, stream=None):
+    _check("moe_test_block_dots",
+           lib().moe_test_block_dots(fmt, _ptr(rows), n_rows, K, stride, C.byref(xq), token,
+                                     _ptr(out), _stream(stream)))
+
+
+def qact(qs, d, bsums, fmt: int, T: int, H: int) -> MoeQact:
+    """A moe_qact over caller buffers."""
+    return MoeQact(_ptr(qs), _ptr(d), _ptr(bsums), fmt, T, H)
+
+
+# ------------------------------------------------------------------ HIP events
+_hip = None
+
+
+def hip():
+    """libamdhip64 for events on the library's stream (timing only)."""
+    global _hip
+    if _hip is None:
+        h = C.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        h.hipEventDestroy.argtypes = [C.c_void_p]
+        h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        h.hipEventSynchronize.argtypes = [C.c_void_p]
+        h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        _hip = h
+    return _hip
+
+
+class HipEvent:
+    def __init__(self):
+        self.h = C.c_void_p()
+        r = hip().hipEventCreate(C.byref(self.h))
+        if r != 0:
+            raise RuntimeError(f"hipEventCreate failed ({r})")
+
+    @property
+    def handle(self) -> int:
+        return self.h.value
+
+    def record(self, stream=None):
+        r = hip().hipEventRecord(self.h, _stream(stream))
+        if r != 0:
+            raise RuntimeError(f"hipEventRecord failed ({r})")
+
+    def synchronize(self):
+        hip().hipEventSynchronize(self.h)
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        out = C.c_float()
+        r = hip().hipEventElapsedTime(C.byref(out), self.h, end.h)
+        if r != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({r})")
+        return out.value
+
+    def __del__(self):
+        try:
+            if self.h:
+                hip().hipEventDestroy(self.h)
+        except Exception:
+            pass

@@ -1,0 +1,359 @@
+// C ABI of the routed-expert MoE FFN layer: argument validation, workspace
+// layout, path choice and the launch sequence. All device work is enqueued on
+// the caller's stream; nothing here allocates or synchronizes.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kMaxTokens = 2048;
+
+int block_elems(int fmt) { return fmt == FMT_MXFP4 ? 32 : 256; }
+size_t block_bytes(int fmt) { return fmt == FMT_Q4_K ? 144 : fmt == FMT_Q6_K ? 210 : 17; }
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status validate_desc(const moe_layer_desc* d) {
+  if (!d) return MOE_EINVAL;
+  const int H = d->hidden, F = d->ffn, E = d->n_expert, k = d->top_k;
+  if (H <= 0 || F <= 0) return MOE_EINVAL;
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_EINVAL;
+  if (k < 1 || k > E || k > MOE_MAX_TOPK) return MOE_EINVAL;
+  if (d->router != MOE_ROUTER_SOFTMAX && d->router != MOE_ROUTER_SIGMOID) return MOE_EINVAL;
+  if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_EINVAL;
+  if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
+  for (int f : {d->fmt_gate, d->fmt_up, d->fmt_down})
+    if (f != MOE_WFMT_Q4_K && f != MOE_WFMT_Q6_K && f != MOE_WFMT_MXFP4) return MOE_EINVAL;
+  if (d->fmt_gate != d->fmt_up) return MOE_EUNSUPPORTED;
+  if (H % block_elems(d->fmt_gate) != 0 || H % 32 != 0) return MOE_EINVAL;
+  if (F % block_elems(d->fmt_down) != 0 || F % 32 != 0) return MOE_EINVAL;
+  const size_t rb_gu = static_cast<size_t>(H / block_elems(d->fmt_gate)) * block_bytes(d->fmt_gate);
+  const size_t rb_d = static_cast<size_t>(F / block_elems(d->fmt_down)) * block_bytes(d->fmt_down);
+  if (d->stride_gate < rb_gu || d->stride_gate % 16) return MOE_EINVAL;
+  if (d->stride_up < rb_gu || d->stride_up % 16) return MOE_EINVAL;
+  if (d->stride_down < rb_d || d->stride_down % 16) return MOE_EINVAL;
+  if (!d->w_router || !aligned(d->w_router, 16)) return MOE_EINVAL;
+  if (!d->gate || !d->up || !d->down) return MOE_EINVAL;
+  if (!aligned(d->gate, 8) || !aligned(d->up, 8) || !aligned(d->down, 8)) return MOE_EINVAL;
+  if ((d->b_gate == nullptr) != (d->b_up == nullptr)) return MOE_EINVAL;
+  if (d->sel_bias && !aligned(d->sel_bias, 4)) return MOE_EINVAL;
+  const int nsh = (d->sh_gate != nullptr) + (d->sh_up != nullptr) + (d->sh_down != nullptr);
+  if (nsh != 0 && nsh != 3) return MOE_EINVAL;
+  if (nsh == 3 && (!aligned(d->sh_gate, 16) || !aligned(d->sh_up, 16) || !aligned(d->sh_down, 16)))
+    return MOE_EINVAL;
+  if (d->sh_gate_vec && (nsh == 0 || !aligned(d->sh_gate_vec, 16))) return MOE_EINVAL;
+  if (!(d->act_limit > 0.0f) && d->act == MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+moe_status validate_x(const void* x, moe_dtype dtype) {
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return MOE_EINVAL;
+  if (!x || !aligned(x, 16)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+KArgs make_args(const moe_layer_desc* d, int T) {
+  KArgs a;
+  memset(&a, 0, sizeof a);
+  a.H = d->hidden; a.F = d->ffn; a.E = d->n_expert; a.k = d->top_k; a.T = T;
+  a.router = d->router; a.norm_topk = d->norm_topk; a.route_scale = d->route_scale;
+  a.w_router = d->w_router; a.sel_bias = d->sel_bias;
+  a.fmt_gu = d->fmt_gate; a.fmt_d = d->fmt_down;
+  a.stride_gate = d->stride_gate; a.stride_up = d->stride_up; a.stride_down = d->stride_down;
+  a.gate = d->gate; a.up = d->up; a.down = d->down;
+  a.b_gate = d->b_gate; a.b_up = d->b_up; a.b_down = d->b_down;
+  a.act = d->act; a.act_alpha = d->act_alpha; a.act_limit = d->act_limit;
+  a.sh_gate = d->sh_gate; a.sh_up = d->sh_up; a.sh_down = d->sh_down;
+  a.sh_gate_vec = d->sh_gate_vec;
+  a.has_shared = d->sh_gate != nullptr;
+  return a;
+}
+
+void bind_ws(KArgs& a, const WsLayout& L, void* ws) {
+  unsigned char* b = static_cast<unsigned char*>(ws);
+  a.counters = reinterpret_cast<uint32_t*>(b + L.counters);
+  a.xqs = reinterpret_cast<int8_t*>(b + L.xqs);
+  a.xd = reinterpret_cast<float*>(b + L.xd);
+  a.xbs = reinterpret_cast<int16_t*>(b + L.xbs);
+  a.logits = reinterpret_cast<float*>(b + L.logits);
+  a.ids = reinterpret_cast<int32_t*>(b + L.ids);
+  a.w = reinterpret_cast<float*>(b + L.w);
+  a.shw = reinterpret_cast<float*>(b + L.shw);
+  a.h = reinterpret_cast<float*>(b + L.h);
+  a.counts = reinterpret_cast<int32_t*>(b + L.counts);
+  a.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  a.pair_list = reinterpret_cast<int32_t*>(b + L.pair_list);
+  a.active = reinterpret_cast<int32_t*>(b + L.active);
+  a.hqs = reinterpret_cast<int8_t*>(b + L.hqs);
+  a.hd = reinterpret_cast<float*>(b + L.hd);
+  a.hbs = reinterpret_cast<int16_t*>(b + L.hbs);
+  a.part = reinterpret_cast<float*>(b + L.part);
+}
+
+// Records events[i] if in range (timing hook of moe_layer_forward_timed).
+struct Stages {
+  hipEvent_t* ev;
+  int n;
+  int i;
+  hipStream_t s;
+  hipError_t mark() {
+    if (ev && i < n) {
+      hipError_t e = hipEventRecord(ev[i], s);
+      ++i;
+      return e;
+    }
+    ++i;
+    return hipSuccess;
+  }
+};
+
+}  // namespace
+
+// Dispatch rule between the two expert-FFN paths (see the header of
+// moe_kernels.hip): chunks of up to 4 tokens take the per-(token, slot) GEMV
+// path; larger chunks take the expert-grouped path, whose int8 MFMA tiles
+// amortize each weight read over all tokens routed to the expert.
+bool use_grouped(int T, int k) {
+  (void)T; (void)k;
+  return false;
+}
+
+WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped) {
+  WsLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t P = static_cast<size_t>(T) * k + static_cast<size_t>(T) * has_shared;
+  L.counters = take(256);
+  L.xqs = take(static_cast<size_t>(T) * H);
+  L.xd = take(static_cast<size_t>(T) * (H / 32) * 4);
+  L.xbs = take(static_cast<size_t>(T) * (H / 16) * 2);
+  L.logits = take(static_cast<size_t>(T) * E * 4);
+  L.ids = take(static_cast<size_t>(T) * k * 4);
+  L.w = take(static_cast<size_t>(T) * k * 4);
+  L.shw = take(static_cast<size_t>(T) * 4);
+  L.h = take(P * F * 4);
+  if (grouped) {
+    L.counts = take(static_cast<size_t>(E + 1) * 4);
+    L.offsets = take(static_cast<size_t>(E + 2) * 4);
+    L.pair_list = take(static_cast<size_t>(T) * k * 4);
+    L.active = take(static_cast<size_t>(E + 1) * 4);
+    L.hqs = take(P * F);
+    L.hd = take(P * (F / 32) * 4);
+    L.hbs = take(P * (F / 16) * 2);
+    L.part = take(P * H * 4);
+  } else {
+    L.counts = L.offsets = L.pair_list = L.active = L.hqs = L.hd = L.hbs = L.part = 0;
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported combination";
+    case MOE_ENOWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t moe_workspace_size(const moe_layer_desc* desc, int T) {
+  if (validate_desc(desc) != MOE_OK || T < 0 || T > kMaxTokens) return 0;
+  const bool g = use_grouped(T, desc->top_k);
+  return ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
+                   desc->sh_gate != nullptr, g).total;
+}
+
+moe_status moe_quantize_act_q8k(const void* x, moe_dtype dtype, int T, int H, moe_afmt fmt,
+                                moe_qact* out, hipStream_t stream) {
+  if (validate_x(x, dtype) != MOE_OK || !out) return MOE_EINVAL;
+  if (fmt != MOE_AFMT_Q8_K && fmt != MOE_AFMT_Q8_32) return MOE_EINVAL;
+  const int B = fmt == MOE_AFMT_Q8_K ? 256 : 32;
+  if (T < 0 || H <= 0 || H % B != 0) return MOE_EINVAL;
+  if (!out->qs || !out->d || !aligned(out->qs, 16) || !aligned(out->d, 4)) return MOE_EINVAL;
+  if (fmt == MOE_AFMT_Q8_K && (!out->bsums || !aligned(out->bsums, 4))) return MOE_EINVAL;
+  out->fmt = fmt;
+  out->T = T;
+  out->H = H;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_quant(x, dtype, T, H, B, out->qs, out->d,
+                                 fmt == MOE_AFMT_Q8_K ? out->bsums : nullptr, nullptr, 0, stream));
+}
+
+moe_status moe_route_topk(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
+                          int32_t* ids, float* w, float* logits, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st != MOE_OK) return st;
+  if (validate_x(x, dtype) != MOE_OK) return MOE_EINVAL;
+  if (T < 0 || T > kMaxTokens || !ids || !w) return MOE_EINVAL;
+  if (!aligned(ids, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4))) return MOE_EINVAL;
+  if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
+  const bool g = use_grouped(T, desc->top_k);
+  const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
+                               desc->sh_gate != nullptr, g);
+  if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
+  if (T == 0) return MOE_OK;
+  KArgs a = make_args(desc, T);
+  bind_ws(a, L, ws);
+  a.x = x; a.x_dtype = dtype;
+  a.ids = ids; a.w = w;
+  if (logits) a.logits = logits;
+  a.sh_gate_vec = nullptr;  // the shared gate is not part of routing
+  hipError_t e = launch_router(a, false, stream);
+  if (e == hipSuccess) e = launch_topk(a, stream);
+  return hip_status(e);
+}
+
+// Host-side check that the chosen path's launch shapes fit, before anything is enqueued.
+static bool path_fits(const KArgs& a) { return gemv_fits(a); }
+
+static moe_status expert_ffn_impl(KArgs& a, hipStream_t stream, Stages& st) {
+  hipError_t e = hipSuccess;
+  // GEMV path: per (token, slot) gate/up, then per-token down + combine
+  e = launch_gateup_gemv(a, stream);
+  if (e == hipSuccess) e = st.mark();
+  if (e == hipSuccess) e = launch_down_gemv(a, stream);
+  if (e == hipSuccess) e = st.mark();
+  return hip_status(e);
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq, const void* x,
+                          moe_dtype dtype, int T, const int32_t* ids, const float* w, float* y,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st != MOE_OK) return st;
+  if (T < 0 || T > kMaxTokens || !xq || !ids || !w || !y) return MOE_EINVAL;
+  const int want_afmt = desc->fmt_gate == MOE_WFMT_MXFP4 ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K;
+  if (xq->fmt != want_afmt || xq->T < T || xq->H != desc->hidden) return MOE_EINVAL;
+  if (!xq->qs || !xq->d || !aligned(xq->qs, 16)) return MOE_EINVAL;
+  if (want_afmt == MOE_AFMT_Q8_K && !xq->bsums) return MOE_EINVAL;
+  if (desc->sh_gate_vec && validate_x(x, dtype) != MOE_OK) return MOE_EINVAL;
+  if (!aligned(ids, 4) || !aligned(w, 4) || !aligned(y, 16)) return MOE_EINVAL;
+  if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
+  const bool g = use_grouped(T, desc->top_k);
+  const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
+                               desc->sh_gate != nullptr, g);
+  if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
+  if (T == 0) return MOE_OK;
+  KArgs a = make_args(desc, T);
+  bind_ws(a, L, ws);
+  a.x = x; a.x_dtype = dtype;
+  a.xqs = xq->qs; a.xd = xq->d; a.xbs = xq->bsums;
+  a.ids = const_cast<int32_t*>(ids);
+  a.w = const_cast<float*>(w);
+  a.y = y;
+  if (!path_fits(a)) return MOE_EUNSUPPORTED;
+  if (desc->sh_gate_vec) {
+    hipError_t e = launch_shared_gate(a, stream);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
+  Stages stg{nullptr, 0, 0, stream};
+  return expert_ffn_impl(a, stream, stg);
+}
+
+static moe_status layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
+                                float* y, int32_t* ids_out, float* w_out, void* ws,
+                                size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                                int n_events) {
+  moe_status st = validate_desc(desc);
+  if (st != MOE_OK) return st;
+  if (validate_x(x, dtype) != MOE_OK) return MOE_EINVAL;
+  if (T < 0 || T > kMaxTokens || !y || !aligned(y, 16)) return MOE_EINVAL;
+  if ((ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4))) return MOE_EINVAL;
+  if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
+  if (events && n_events < 0) return MOE_EINVAL;
+  const bool g = use_grouped(T, desc->top_k);
+  const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
+                               desc->sh_gate != nullptr, g);
+  if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
+  if (T == 0) return MOE_OK;
+  KArgs a = make_args(desc, T);
+  bind_ws(a, L, ws);
+  a.x = x; a.x_dtype = dtype;
+  a.y = y;
+  if (ids_out) a.ids = ids_out;
+  if (w_out) a.w = w_out;
+  if (!path_fits(a)) return MOE_EUNSUPPORTED;
+  Stages stg{events, n_events, 0, stream};
+  hipError_t e = stg.mark();
+  const int Bx = desc->fmt_gate == MOE_WFMT_MXFP4 ? 32 : 256;
+  if (e == hipSuccess)
+    e = launch_quant(x, dtype, T, a.H, Bx, a.xqs, a.xd, Bx == 256 ? a.xbs : nullptr, a.counters,
+                     64, stream);
+  if (e == hipSuccess) e = stg.mark();
+  const bool fuse = T <= 8;
+  if (e == hipSuccess) e = launch_router(a, fuse, stream);
+  if (e == hipSuccess) e = stg.mark();
+  if (!fuse) {
+    if (e == hipSuccess) e = launch_topk(a, stream);
+    if (e == hipSuccess) e = stg.mark();
+  }
+  if (e != hipSuccess) return MOE_EHIP;
+  return expert_ffn_impl(a, stream, stg);
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
+                             float* y, int32_t* ids_out, float* w_out, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  return layer_forward(desc, x, dtype, T, y, ids_out, w_out, ws, ws_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, moe_dtype dtype,
+                                   int T, float* y, int32_t* ids_out, float* w_out, void* ws,
+                                   size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                                   int n_events) {
+  return layer_forward(desc, x, dtype, T, y, ids_out, w_out, ws, ws_bytes, stream, events,
+                       n_events);
+}
+
+int moe_layer_stage_count(const moe_layer_desc* desc, int T) {
+  if (validate_desc(desc) != MOE_OK || T <= 0 || T > kMaxTokens) return 0;
+  return T <= 8 ? 4 : 5;
+}
+
+const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {
+  static const char* small[] = {"quant_act", "router_topk", "gateup", "down_combine"};
+  static const char* large[] = {"quant_act", "router", "topk", "gateup", "down_combine"};
+  const int n = moe_layer_stage_count(desc, T);
+  if (stage < 0 || stage >= n) return nullptr;
+  return T <= 8 ? small[stage] : large[stage];
+}
+
+moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,
+                               const moe_qact* xq, int token, int32_t* out, hipStream_t stream) {
+  if (fmt != MOE_WFMT_Q4_K && fmt != MOE_WFMT_Q6_K && fmt != MOE_WFMT_MXFP4) return MOE_EINVAL;
+  if (!rows || !aligned(rows, 16) || !out || !xq || n_rows < 0 || K <= 0) return MOE_EINVAL;
+  if (K % block_elems(fmt) != 0) return MOE_EINVAL;
+  const size_t rb = static_cast<size_t>(K / block_elems(fmt)) * block_bytes(fmt);
+  if (stride < rb || stride % 16) return MOE_EINVAL;
+  const int want = fmt == MOE_WFMT_MXFP4 ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K;
+  if (xq->fmt != want || xq->H != K || token < 0 || token >= xq->T) return MOE_EINVAL;
+  if (!xq->qs || !xq->d || (want == MOE_AFMT_Q8_K && !xq->bsums)) return MOE_EINVAL;
+  if (n_rows == 0) return MOE_OK;
+  const int B = want == MOE_AFMT_Q8_K ? 256 : 32;
+  return hip_status(launch_block_dots(
+      fmt, rows, n_rows, K, stride, xq->qs + static_cast<size_t>(token) * K,
+      xq->d + static_cast<size_t>(token) * (K / B),
+      want == MOE_AFMT_Q8_K ? xq->bsums + static_cast<size_t>(token) * (K / 16) : nullptr, out,
+      stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal interface between the C ABI (moe_api.cpp) and the HIP kernels
+// (moe_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace moe {
+
+enum { FMT_Q4_K = 0, FMT_Q6_K = 1, FMT_MXFP4 = 2 };
+
+// Everything a kernel may need, resolved on the host. Passed by value.
+struct KArgs {
+  int H, F, E, k, T;
+  int router, norm_topk;
+  float route_scale;
+  const float* w_router;
+  const float* sel_bias;
+  int fmt_gu, fmt_d;
+  size_t stride_gate, stride_up, stride_down;
+  const void* const* gate;
+  const void* const* up;
+  const void* const* down;
+  const float* const* b_gate;
+  const float* const* b_up;
+  const float* const* b_down;
+  int act;
+  float act_alpha, act_limit;
+  const void* sh_gate;
+  const void* sh_up;
+  const void* sh_down;
+  const float* sh_gate_vec;
+  int has_shared;
+  // inputs / outputs / scratch (device)
+  const void* x;
+  int x_dtype;
+  int8_t* xqs;      // [T, H]
+  float* xd;        // [T, H / Bx]
+  int16_t* xbs;     // [T, H / 16] (Q8_K) or nullptr
+  float* logits;    // [T, E]
+  int32_t* ids;     // [T, k]
+  float* w;         // [T, k]
+  float* shw;       // [T] shared-expert weight
+  float* h;         // [P, F], P = T * k + T * has_shared
+  float* y;         // [T, H]
+  uint32_t* counters;  // 64 words, zeroed by the first kernel of a call
+  // grouped path
+  int32_t* counts;     // [E + 1]
+  int32_t* offsets;    // [E + 2]
+  int32_t* pair_list;  // [T * k] pair ids p = t * k + slot, grouped by expert
+  int32_t* active;     // [E + 1] active experts in increasing order (+ shared)
+  int8_t* hqs;         // [P, F]
+  float* hd;           // [P, F / 32]
+  int16_t* hbs;        // [P, F / 16]
+  float* part;         // [P, H]
+};
+
+// Workspace layout (byte offsets from the base, each 256-aligned).
+struct WsLayout {
+  size_t counters, xqs, xd, xbs, logits, ids, w, shw, h, counts, offsets, pair_list, active,
+      hqs, hd, hbs, part, total;
+};
+WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped);
+
+// Dynamic LDS a workgroup may use (bytes).
+constexpr size_t kMaxLds = 64 * 1024;
+
+// Whether the GEMV kernels' LDS needs fit for this layer and chunk.
+bool gemv_fits(const KArgs& a);
+
+// Which expert-FFN path a chunk of T tokens takes (fixed rule, see moe_api.cpp).
+bool use_grouped(int T, int k);
+
+// Launchers. Each returns hipSuccess or the launch error.
+hipError_t launch_quant(const void* x, int dtype, int T, int H, int B, int8_t* qs, float* d,
+                        int16_t* bs, uint32_t* zero_words, int n_zero, hipStream_t s);
+hipError_t launch_shared_gate(const KArgs& a, hipStream_t s);
+hipError_t launch_router(const KArgs& a, bool fuse_topk, hipStream_t s);
+hipError_t launch_topk(const KArgs& a, hipStream_t s);
+hipError_t launch_gateup_gemv(const KArgs& a, hipStream_t s);
+hipError_t launch_down_gemv(const KArgs& a, hipStream_t s);
+hipError_t launch_bucket(const KArgs& a, hipStream_t s);
+hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s);
+hipError_t launch_hquant(const KArgs& a, hipStream_t s);
+hipError_t launch_down_grouped(const KArgs& a, hipStream_t s);
+hipError_t launch_combine(const KArgs& a, hipStream_t s);
+hipError_t launch_copy_routing(const KArgs& a, int32_t* ids_out, float* w_out, hipStream_t s);
+hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_t stride,
+                             const int8_t* qs, const float* d, const int16_t* bs,
+                             int32_t* out, hipStream_t s);
+
+}  // namespace moe

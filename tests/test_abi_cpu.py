@@ -1,0 +1,175 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and host-side validation rejects bad arguments before any
+work is enqueued. Every call here fails validation (or is a T = 0 no-op), so
+nothing reaches a kernel launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import gen
+import quantized_moe_expert_route_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-aligned address that is never dereferenced
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_header_symbols():
+    L = M.lib()
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(M.ABI_FUNCTIONS)
+
+
+def test_version_and_status_strings():
+    assert M.moe_abi_version() == 1
+    for s in range(5):
+        assert M.moe_status_str(s)
+    assert M.moe_status_str(99) == "unknown status"
+
+
+def good_desc(cfg=None):
+    cfg = cfg or gen.CONFIGS["qwen3.6-35b-a3b"]
+    d = M.MoeLayerDesc()
+    d.hidden, d.ffn, d.n_expert, d.top_k = cfg.H, cfg.F, cfg.E, cfg.k
+    d.router = cfg.router
+    d.norm_topk = 1
+    d.route_scale = 1.0
+    d.w_router = FAKE
+    d.fmt_gate = d.fmt_up = cfg.fmt_gu
+    d.fmt_down = cfg.fmt_d
+    d.stride_gate = d.stride_up = cfg.stride_gu
+    d.stride_down = cfg.stride_d
+    d.gate, d.up, d.down = FAKE, FAKE + 4096, FAKE + 8192
+    d.act = cfg.act
+    d.act_alpha, d.act_limit = 1.702, 7.0
+    return d
+
+
+def test_workspace_size_valid_and_invalid():
+    d = good_desc()
+    n1 = M.moe_workspace_size(d, 1)
+    n16 = M.moe_workspace_size(d, 16)
+    assert n1 > 0 and n16 > n1 and n1 % 256 == 0
+    assert M.moe_workspace_size(d, 0) > 0
+    assert M.moe_workspace_size(d, -1) == 0
+    bad = good_desc()
+    bad.top_k = 0
+    assert M.moe_workspace_size(bad, 1) == 0
+
+
+MUTATIONS = [
+    ("hidden", 0), ("hidden", 2048 + 32), ("ffn", 100), ("n_expert", 0), ("n_expert", 1025),
+    ("top_k", 0), ("top_k", 257), ("top_k", 17), ("router", 2), ("norm_topk", 2), ("act", 5),
+    ("fmt_gate", 3), ("fmt_down", -1), ("stride_gate", 1024), ("stride_gate", 1152 + 8),
+    ("stride_down", 280), ("w_router", 0), ("w_router", FAKE + 4), ("gate", 0), ("down", 0),
+    ("up", FAKE + 2), ("sh_gate", FAKE),
+]
+
+
+@pytest.mark.parametrize("field,value", MUTATIONS)
+def test_desc_validation(field, value):
+    d = good_desc()
+    setattr(d, field, value)
+    assert M.moe_workspace_size(d, 1) == 0
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_layer_forward(d, FAKE, M.MOE_DTYPE_F32, 1, FAKE, None, None, FAKE, 1 << 40, stream=0)
+    assert ei.value.status in (M.MOE_EINVAL, M.MOE_EUNSUPPORTED)
+
+
+def test_gate_up_format_mismatch_unsupported():
+    d = good_desc()
+    d.fmt_up = M.MOE_WFMT_Q6_K
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_layer_forward(d, FAKE, 0, 1, FAKE, None, None, FAKE, 1 << 40, stream=0)
+    assert ei.value.status == M.MOE_EUNSUPPORTED
+
+
+def test_call_validation():
+    d = good_desc()
+    ws = M.moe_workspace_size(d, 4)
+    cases = [
+        lambda: M.moe_layer_forward(d, 0, 0, 4, FAKE, None, None, FAKE, ws, stream=0),
+        lambda: M.moe_layer_forward(d, FAKE + 8, 0, 4, FAKE, None, None, FAKE, ws, stream=0),
+        lambda: M.moe_layer_forward(d, FAKE, 7, 4, FAKE, None, None, FAKE, ws, stream=0),
+        lambda: M.moe_layer_forward(d, FAKE, 0, 4, 0, None, None, FAKE, ws, stream=0),
+        lambda: M.moe_layer_forward(d, FAKE, 0, 4, FAKE, None, None, 0, ws, stream=0),
+        lambda: M.moe_layer_forward(d, FAKE, 0, 4, FAKE, None, None, FAKE + 16, ws, stream=0),
+        lambda: M.moe_layer_forward(d, FAKE, 0, -1, FAKE, None, None, FAKE, ws, stream=0),
+        lambda: M.moe_layer_forward(d, FAKE, 0, 100000, FAKE, None, None, FAKE, 1 << 40,
+                                    stream=0),
+        lambda: M.moe_route_topk(d, FAKE, 0, 4, 0, FAKE, None, FAKE, ws, stream=0),
+        lambda: M.moe_route_topk(d, FAKE, 0, 4, FAKE, FAKE, None, None, ws, stream=0),
+    ]
+    for i, c in enumerate(cases):
+        with pytest.raises(M.MoeError) as ei:
+            c()
+        assert ei.value.status == M.MOE_EINVAL, i
+
+
+def test_short_workspace():
+    d = good_desc()
+    ws = M.moe_workspace_size(d, 4)
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_layer_forward(d, FAKE, 0, 4, FAKE, None, None, FAKE, ws - 1, stream=0)
+    assert ei.value.status == M.MOE_ENOWORKSPACE
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_route_topk(d, FAKE, 0, 4, FAKE, FAKE, None, FAKE, ws - 256, stream=0)
+    assert ei.value.status == M.MOE_ENOWORKSPACE
+
+
+def test_zero_tokens_is_a_noop():
+    d = good_desc()
+    ws = M.moe_workspace_size(d, 0)
+    M.moe_layer_forward(d, FAKE, 0, 0, FAKE, None, None, FAKE, ws, stream=0)
+    M.moe_route_topk(d, FAKE, 0, 0, FAKE, FAKE, None, FAKE, ws, stream=0)
+
+
+def test_quantize_and_expert_ffn_validation():
+    q = M.qact(FAKE, FAKE, FAKE, M.MOE_AFMT_Q8_K, 4, 2048)
+    for args in [(0, 0, 4, 2048, 0), (FAKE, 0, 4, 2000, 0), (FAKE, 0, 4, 2048, 2),
+                 (FAKE, 0, 4, 96, M.MOE_AFMT_Q8_K), (FAKE, 3, 4, 2048, 0)]:
+        with pytest.raises(M.MoeError):
+            M.moe_quantize_act_q8k(*args, q, stream=0)
+    qn = M.qact(FAKE, FAKE, None, M.MOE_AFMT_Q8_K, 4, 2048)
+    with pytest.raises(M.MoeError):
+        M.moe_quantize_act_q8k(FAKE, 0, 4, 2048, M.MOE_AFMT_Q8_K, qn, stream=0)
+    d = good_desc()
+    ws = M.moe_workspace_size(d, 4)
+    wrong_fmt = M.qact(FAKE, FAKE, FAKE, M.MOE_AFMT_Q8_32, 4, 2048)
+    short_T = M.qact(FAKE, FAKE, FAKE, M.MOE_AFMT_Q8_K, 3, 2048)
+    for xq in (wrong_fmt, short_T):
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_expert_ffn(d, xq, None, 0, 4, FAKE, FAKE, FAKE, FAKE, ws, stream=0)
+        assert ei.value.status == M.MOE_EINVAL
+
+
+def test_block_dots_validation():
+    q = M.qact(FAKE, FAKE, FAKE, M.MOE_AFMT_Q8_K, 1, 512)
+    bad = [
+        (M.MOE_WFMT_Q4_K, 0, 1, 512, 288, q, 0),
+        (M.MOE_WFMT_Q4_K, FAKE, 1, 500, 288, q, 0),
+        (M.MOE_WFMT_Q4_K, FAKE, 1, 512, 280, q, 0),
+        (M.MOE_WFMT_Q4_K, FAKE, 1, 512, 288, q, 1),
+        (M.MOE_WFMT_MXFP4, FAKE, 1, 512, 288, q, 0),
+        (5, FAKE, 1, 512, 288, q, 0),
+    ]
+    for a in bad:
+        with pytest.raises(M.MoeError):
+            M.moe_test_block_dots(*a, FAKE, stream=0)
+
+
+def test_stage_names():
+    d = good_desc()
+    assert M.moe_layer_stage_count(d, 1) == 4
+    assert [M.moe_layer_stage_name(d, 1, i) for i in range(4)][2] == "gateup"
+    assert M.moe_layer_stage_name(d, 1, 9) is None

@@ -1,0 +1,202 @@
+"""GPU parity of the individual steps: q8 activations (bit-exact), integer block
+partials (exact), router ids (exact) and weights."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import quantized_moe_expert_route_amd as M
+from gen.device import DeviceLayer, x_to_device
+from tests.gpu_common import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _x_cases(T, H, seed):
+    x = gen.normal(seed, gen.T_X, 77, T, H, 1.0)
+    if T > 1:
+        x[1] = 0.0                       # all-zero row
+    if T > 2:
+        x[2, :32] = 0.0                  # a zero block
+        x[2, 40] = 1e4                   # a spike
+    if T > 3:
+        x[3] *= 1e-6
+    return x
+
+
+@pytest.mark.parametrize("afmt,B", [(M.MOE_AFMT_Q8_K, 256), (M.MOE_AFMT_Q8_32, 32)])
+@pytest.mark.parametrize("T,H", [(1, 512), (5, 2048), (3, 7168), (2, 2880)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_quantize_bitexact(afmt, B, T, H, bf16):
+    if H % B:
+        pytest.skip("width not a multiple of the block")
+    say(f"quant afmt={afmt} T={T} H={H} bf16={bf16}")
+    x = _x_cases(T, H, 3)
+    if bf16:
+        xb = gen.round_bf16(x)
+        x = gen.bf16_to_f32(xb)
+        xt = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+        dt = M.MOE_DTYPE_BF16
+    else:
+        xt = torch.from_numpy(x).cuda()
+        dt = M.MOE_DTYPE_F32
+    qs = torch.empty((T, H), dtype=torch.int8, device="cuda")
+    d = torch.empty((T, H // B), dtype=torch.float32, device="cuda")
+    bs = torch.empty((T, H // 16), dtype=torch.int16, device="cuda") if B == 256 else None
+    q = M.qact(qs, d, bs, afmt, T, H)
+    M.moe_quantize_act_q8k(xt, dt, T, H, afmt, q)
+    torch.cuda.synchronize()
+    for t in range(T):
+        rq, rd, rb = oracle.quantize_q8(x[t], B)
+        assert np.array_equal(qs[t].cpu().numpy(), rq), t
+        assert np.array_equal(d[t].cpu().numpy().view(np.uint32), rd.view(np.uint32)), t
+        if B == 256:
+            assert np.array_equal(bs[t].cpu().numpy(), rb), t
+
+
+def _upload_q8(x_rows, B):
+    T, K = x_rows.shape
+    qs = np.zeros((T, K), np.int8)
+    d = np.zeros((T, K // B), np.float32)
+    bs = np.zeros((T, K // 16), np.int16)
+    for t in range(T):
+        a, b, c = oracle.quantize_q8(x_rows[t], B)
+        qs[t], d[t] = a, b
+        if c is not None:
+            bs[t] = c
+    tq, td, tb = (torch.from_numpy(v).cuda() for v in (qs, d, bs))
+    afmt = M.MOE_AFMT_Q8_K if B == 256 else M.MOE_AFMT_Q8_32
+    return (qs, d, bs), M.qact(tq, td, tb if B == 256 else None, afmt, T, K), (tq, td, tb)
+
+
+def _random_blocks(fmt, n_rows, K, rng):
+    """Blocks with arbitrary field values (negative Q6_K scales, every MXFP4 code)."""
+    nb = K // gen.BLOCK_ELEMS[fmt]
+    rows = []
+    for r in range(n_rows):
+        row = []
+        for b in range(nb):
+            if fmt == gen.Q4_K:
+                row.append(gen.pack_q4k(int(rng.integers(0x0400, 0x3C00)),
+                                        int(rng.integers(0x0400, 0x3C00)),
+                                        rng.integers(0, 64, 8), rng.integers(0, 64, 8),
+                                        rng.integers(0, 16, 256)))
+            elif fmt == gen.Q6_K:
+                row.append(gen.pack_q6k(int(rng.integers(0x0400, 0x3C00)),
+                                        rng.integers(-128, 128, 16).astype(np.int8),
+                                        rng.integers(0, 64, 256)))
+            else:
+                row.append(gen.pack_mxfp4(int(rng.integers(100, 150)), rng.integers(0, 16, 32)))
+        rows.append(np.concatenate(row))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("fmt,K", [(gen.Q4_K, 512), (gen.Q4_K, 7168), (gen.Q6_K, 768),
+                                   (gen.Q6_K, 2048), (gen.MXFP4, 2880), (gen.MXFP4, 96)])
+@pytest.mark.parametrize("kind", ["generated", "random_fields"])
+def test_block_dots_exact(fmt, K, kind):
+    say(f"block_dots fmt={fmt} K={K} {kind}")
+    B = 32 if fmt == gen.MXFP4 else 256
+    n_rows = 37
+    rng = np.random.default_rng(fmt * 100 + K)
+    if kind == "generated":
+        w = gen.normal(5, gen.T_DOWN, fmt, n_rows, K, 0.02)
+        w[0] = 0
+        mat = gen.encode_matrix(fmt, w)
+    else:
+        raw = _random_blocks(fmt, n_rows, K, rng)
+        stride = gen.row_stride(fmt, K)
+        mat = np.zeros((n_rows, stride), np.uint8)
+        mat[:, :raw.shape[1]] = raw
+    x = _x_cases(3, K, 9)
+    host, q, keep = _upload_q8(x, B)
+    rows = torch.from_numpy(mat).cuda()
+    nb = K // gen.BLOCK_ELEMS[fmt]
+    for token in range(3):
+        out = torch.full((n_rows, nb, 2), -7, dtype=torch.int32, device="cuda")
+        M.moe_test_block_dots(fmt, rows, n_rows, K, mat.shape[1], q, token, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for r in range(n_rows):
+            ref = oracle.block_partials(fmt, mat[r], K, host[0][token],
+                                        host[2][token] if B == 256 else None)
+            assert np.array_equal(got[r], ref), (token, r)
+
+
+def _route(dl, xt, dt, T, logits=True):
+    cfg = dl.cfg
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, cfg.E), dtype=torch.float32, device="cuda") if logits else None
+    ws = dl.workspace(T)
+    M.moe_route_topk(dl.desc, xt, dt, T, ids, w, lg, ws, ws.numel())
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy(), None if lg is None else lg.cpu().numpy()
+
+
+ROUTER_CASES = [("tiny", 5), ("qwen3.6-35b-a3b", 9), ("gpt-oss-20b", 3),
+                ("deepseek-v4-flash", 16), ("kimi-k2", 40)]
+
+
+@pytest.mark.parametrize("name,T", ROUTER_CASES)
+def test_route_topk(name, T):
+    cfg = gen.CONFIGS[name]
+    say(f"route {name} T={T}")
+    data = gen.make_layer(cfg, experts=[])
+    x, xb = gen.make_x(cfg, T=T, x_index=5)
+    dl = DeviceLayer(data)
+    xt, dt = x_to_device(data, x, xb)
+    ids, w, lg = _route(dl, xt, dt, T)
+    L = oracle.Layer(data)
+    for t in range(T):
+        ref_l = oracle.router_logits(data.w_router, x[t])
+        ulp = np.spacing(np.abs(ref_l))
+        assert np.all(np.abs(lg[t].astype(np.float64) - ref_l) <= ulp)
+        ref_ids = oracle.topk(ref_l, cfg.k, data.sel_bias)
+        ref_w = oracle.route_weights(ref_l, ref_ids, cfg.router, cfg.norm_topk, cfg.route_scale)
+        assert np.array_equal(ids[t], ref_ids), t
+        assert np.abs(w[t] - ref_w).max() <= 1e-6
+    _ = L
+
+
+def test_route_ties_and_zero_input():
+    cfg = gen.CONFIGS["qwen3.6-35b-a3b"].with_(E=64, k=8)
+    data = gen.make_layer(cfg, experts=[])
+    # duplicate router rows create exact logit ties
+    W = data.w_router
+    W[10] = W[3]
+    W[40] = W[3]
+    W[7] = W[20]
+    data.w_router = np.ascontiguousarray(W)
+    x, _ = gen.make_x(cfg, T=6)
+    x[0] = 0.0
+    x[1] = W[3] / np.linalg.norm(W[3]) * 10  # makes experts 3, 10, 40 the top three
+    dl = DeviceLayer(data)
+    ids, w, lg = _route(dl, torch.from_numpy(x).cuda(), M.MOE_DTYPE_F32, 6)
+    assert list(ids[0]) == list(range(8))
+    assert np.allclose(w[0], 1 / 8, atol=1e-7)
+    assert list(ids[1][:3]) == [3, 10, 40]
+    for t in range(6):
+        ref_l = oracle.router_logits(data.w_router, x[t])
+        assert np.array_equal(ids[t], oracle.topk(ref_l, cfg.k)), t
+    # sigmoid router, unnormalized, with route scale
+    cfg2 = cfg.with_(router=gen.SIGMOID, norm_topk=0, route_scale=2.5)
+    data2 = gen.make_layer(cfg2, experts=[])
+    dl2 = DeviceLayer(data2)
+    ids2, w2, _ = _route(dl2, torch.from_numpy(x).cuda(), M.MOE_DTYPE_F32, 6, logits=False)
+    for t in range(6):
+        ref_l = oracle.router_logits(data2.w_router, x[t])
+        rid = oracle.topk(ref_l, cfg.k)
+        assert np.array_equal(ids2[t], rid)
+        assert np.abs(w2[t] - oracle.route_weights(ref_l, rid, gen.SIGMOID, 0, 2.5)).max() <= 2e-6
+    # softmax over all experts (norm_topk = 0)
+    cfg3 = cfg.with_(norm_topk=0)
+    data3 = gen.make_layer(cfg3, experts=[])
+    dl3 = DeviceLayer(data3)
+    ids3, w3, _ = _route(dl3, torch.from_numpy(x).cuda(), M.MOE_DTYPE_F32, 6, logits=False)
+    for t in range(6):
+        ref_l = oracle.router_logits(data3.w_router, x[t])
+        rid = oracle.topk(ref_l, cfg.k)
+        assert np.array_equal(ids3[t], rid)
+        assert np.abs(w3[t] - oracle.route_weights(ref_l, rid, gen.SOFTMAX, 0)).max() <= 1e-6

@@ -1,0 +1,137 @@
+"""GPU parity of the whole layer against the oracle: ids exact, outputs within
+2e-3 of ||y||_2 per token; NULL-mask partition, determinism, edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import quantized_moe_expert_route_amd as M
+from gen.device import DeviceLayer, x_to_device
+from tests.gpu_common import Y_TOL, check_layer, rel_err, run_layer, say
+from tests.shrunk import SHRUNK
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", list(SHRUNK))
+def test_layer_shrunk(name):
+    check_layer(SHRUNK[name])
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 13), ("qwen3.6-35b-a3b", 1),
+                                    ("qwen3.6-35b-a3b", 4), ("gpt-oss-20b", 1),
+                                    ("gpt-oss-20b", 3)])
+def test_layer_full_decode(name, T):
+    check_layer(gen.CONFIGS[name], T=T, x_index=T)
+
+
+def test_layer_full_verify_chunk_sampled():
+    """DeepSeek-V4-Flash-shaped 16-token chunk at full size; the oracle checks
+    every token."""
+    check_layer(gen.CONFIGS["deepseek-v4-flash"], tokens=range(16), threads=16)
+
+
+def test_expert_ffn_given_routing():
+    cfg = SHRUNK["kimi-k2"]
+    data = gen.make_layer(cfg)
+    T = cfg.T
+    x, _ = gen.make_x(cfg, T=T, x_index=3)
+    rng = np.random.default_rng(0)
+    ids = np.stack([rng.choice(cfg.E, cfg.k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[0] = ids[1]  # tokens sharing experts
+    w = rng.random((T, cfg.k)).astype(np.float32)
+    dl = DeviceLayer(data)
+    qs = torch.empty((T, cfg.H), dtype=torch.int8, device="cuda")
+    d = torch.empty((T, cfg.H // 256), dtype=torch.float32, device="cuda")
+    bs = torch.empty((T, cfg.H // 16), dtype=torch.int16, device="cuda")
+    q = M.qact(qs, d, bs, M.MOE_AFMT_Q8_K, T, cfg.H)
+    xt = torch.from_numpy(x).cuda()
+    M.moe_quantize_act_q8k(xt, M.MOE_DTYPE_F32, T, cfg.H, M.MOE_AFMT_Q8_K, q)
+    y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+    ws = dl.workspace(T)
+    M.moe_expert_ffn(dl.desc, q, xt, M.MOE_DTYPE_F32, T, torch.from_numpy(ids).cuda(),
+                     torch.from_numpy(w).cuda(), y, ws, ws.numel())
+    torch.cuda.synchronize()
+    L = oracle.Layer(data)
+    for t in range(T):
+        ref = L.expert_part(x[t], ids[t], w[t])
+        assert rel_err(y[t].cpu().numpy(), ref) <= Y_TOL
+
+
+@pytest.mark.parametrize("name", ["qwen3.6-35b-a3b", "gpt-oss-20b", "deepseek-v4-flash"])
+def test_null_mask_partition(name):
+    """Experts split over two 'devices' by NULL pointers: the partial outputs sum
+    to the full output (the expert-parallel sharding pattern on one GPU)."""
+    cfg = SHRUNK[name].with_(shared=False)
+    data = gen.make_layer(cfg)
+    T = cfg.T
+    x, xb = gen.make_x(cfg, T=T, x_index=2)
+    mask = np.random.default_rng(7).random(cfg.E) < 0.5
+    outs = []
+    for present in (None, mask, ~mask):
+        dl = DeviceLayer(data, present=present)
+        xt, dt = x_to_device(data, x, xb)
+        outs.append(run_layer(dl, xt, dt, T))
+    (yf, idf, wf), (ya, ida, wa), (yb, idb, wb) = outs
+    assert np.array_equal(idf, ida) and np.array_equal(idf, idb)
+    assert np.array_equal(wf, wa)
+    assert rel_err(ya + yb, yf).max() <= 1e-5
+    L = oracle.Layer(data, present=mask)
+    ref = L.forward(x)
+    assert rel_err(ya, ref["y"]).max() <= Y_TOL
+
+
+def test_shared_gate_vector():
+    cfg = SHRUNK["qwen3.6-35b-a3b"]
+    data = gen.make_layer(cfg, with_sh_gate_vec=True)
+    check_layer(cfg, data=data, sh_gate_vec=data.sh_gate_vec)
+
+
+def test_determinism():
+    cfg = SHRUNK["deepseek-v4-flash"]
+    data = gen.make_layer(cfg)
+    x, xb = gen.make_x(cfg, T=cfg.T)
+    dl = DeviceLayer(data)
+    xt, dt = x_to_device(data, x, xb)
+    a = run_layer(dl, xt, dt, cfg.T)
+    b = run_layer(dl, xt, dt, cfg.T)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def test_zero_input_and_k_equals_E():
+    cfg = gen.CONFIGS["tiny"].with_(k=8)
+    data = gen.make_layer(cfg)
+    x = np.zeros((2, cfg.H), np.float32)
+    x[1], _ = gen.make_x(cfg, T=1)
+    dl = DeviceLayer(data)
+    y, ids, w = run_layer(dl, torch.from_numpy(x).cuda(), M.MOE_DTYPE_F32, 2)
+    assert list(ids[0]) == list(range(8))
+    assert not y[0].any()
+    ref = oracle.Layer(data).forward(x)
+    assert np.array_equal(ids, ref["ids"])
+    assert rel_err(y[1], ref["y"][1]) <= Y_TOL
+
+
+def test_zero_tokens_on_device():
+    cfg = gen.CONFIGS["tiny"]
+    data = gen.make_layer(cfg)
+    dl = DeviceLayer(data)
+    y = torch.full((1, cfg.H), 3.0, device="cuda")
+    ws = dl.workspace(0)
+    M.moe_layer_forward(dl.desc, torch.zeros((1, cfg.H), device="cuda"), 0, 0, y, None, None,
+                        ws, ws.numel())
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
+
+
+def test_layer_copies_identical():
+    cfg = SHRUNK["qwen3.6-35b-a3b"]
+    data = gen.make_layer(cfg)
+    x, _ = gen.make_x(cfg, T=2)
+    dl = DeviceLayer(data, copies=2)
+    xt = torch.from_numpy(x).cuda()
+    a = run_layer(dl, xt, 0, 2, copy=0)
+    b = run_layer(dl, xt, 0, 2, copy=1)
+    assert np.array_equal(a[0], b[0])
