@@ -187,10 +187,11 @@ MOE_API moe_status moe_layer_forward(const moe_layer_desc* desc, const void* x, 
                              float* y, int32_t* ids_out, float* w_out, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
-/* moe_layer_forward with timing hooks: if events is non-NULL, events[0] is
- * recorded on the stream before the first kernel and events[i] right after the
- * i-th kernel, for i < n_events. moe_layer_stage_count() gives how many
- * kernels the call launches and moe_layer_stage_name() names them. */
+/* moe_layer_forward with timing hooks: events holds n_events HIP events (may
+ * be NULL); kernel i of the call records events[2i] when it starts and
+ * events[2i + 1] when it ends (hipExtLaunchKernel start/stop events), for the
+ * pairs that fit in n_events. moe_layer_stage_count() gives how many kernels
+ * the call launches and moe_layer_stage_name() names them. */
 MOE_API moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, moe_dtype dtype,
                                    int T, float* y, int32_t* ids_out, float* w_out, void* ws,
                                    size_t ws_bytes, hipStream_t stream, hipEvent_t* events,

@@ -86,6 +86,7 @@ void bind_ws(KArgs& a, const WsLayout& L, void* ws) {
   a.ids = reinterpret_cast<int32_t*>(b + L.ids);
   a.w = reinterpret_cast<float*>(b + L.w);
   a.shw = reinterpret_cast<float*>(b + L.shw);
+  a.slots = reinterpret_cast<SlotRef*>(b + L.slots);
   a.h = reinterpret_cast<float*>(b + L.h);
   a.counts = reinterpret_cast<int32_t*>(b + L.counts);
   a.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
@@ -97,20 +98,19 @@ void bind_ws(KArgs& a, const WsLayout& L, void* ws) {
   a.part = reinterpret_cast<float*>(b + L.part);
 }
 
-// Records events[i] if in range (timing hook of moe_layer_forward_timed).
+// Per-kernel (start, stop) event pairs of moe_layer_forward_timed.
 struct Stages {
   hipEvent_t* ev;
   int n;
   int i;
-  hipStream_t s;
-  hipError_t mark() {
-    if (ev && i < n) {
-      hipError_t e = hipEventRecord(ev[i], s);
-      ++i;
-      return e;
+  Ev next() {
+    Ev e;
+    if (ev && 2 * i + 1 < n) {
+      e.start = ev[2 * i];
+      e.stop = ev[2 * i + 1];
     }
     ++i;
-    return hipSuccess;
+    return e;
   }
 };
 
@@ -130,7 +130,7 @@ WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool group
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   const size_t P = static_cast<size_t>(T) * k + static_cast<size_t>(T) * has_shared;
-  L.counters = take(256);
+  L.counters = take(4 * (P > 64 ? P : 64));
   L.xqs = take(static_cast<size_t>(T) * H);
   L.xd = take(static_cast<size_t>(T) * (H / 32) * 4);
   L.xbs = take(static_cast<size_t>(T) * (H / 16) * 2);
@@ -138,18 +138,19 @@ WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool group
   L.ids = take(static_cast<size_t>(T) * k * 4);
   L.w = take(static_cast<size_t>(T) * k * 4);
   L.shw = take(static_cast<size_t>(T) * 4);
+  L.slots = take(static_cast<size_t>(T) * k * sizeof(SlotRef));
   L.h = take(P * F * 4);
+  L.hqs = take(P * F);
+  L.hd = take(P * (F / 32) * 4);
+  L.hbs = take(P * (F / 16) * 2);
   if (grouped) {
     L.counts = take(static_cast<size_t>(E + 1) * 4);
     L.offsets = take(static_cast<size_t>(E + 2) * 4);
     L.pair_list = take(static_cast<size_t>(T) * k * 4);
     L.active = take(static_cast<size_t>(E + 1) * 4);
-    L.hqs = take(P * F);
-    L.hd = take(P * (F / 32) * 4);
-    L.hbs = take(P * (F / 16) * 2);
     L.part = take(P * H * 4);
   } else {
-    L.counts = L.offsets = L.pair_list = L.active = L.hqs = L.hd = L.hbs = L.part = 0;
+    L.counts = L.offsets = L.pair_list = L.active = L.part = 0;
   }
   L.total = off;
   return L;
@@ -194,7 +195,7 @@ moe_status moe_quantize_act_q8k(const void* x, moe_dtype dtype, int T, int H, mo
   out->H = H;
   if (T == 0) return MOE_OK;
   return hip_status(launch_quant(x, dtype, T, H, B, out->qs, out->d,
-                                 fmt == MOE_AFMT_Q8_K ? out->bsums : nullptr, nullptr, 0, stream));
+                                 fmt == MOE_AFMT_Q8_K ? out->bsums : nullptr, stream));
 }
 
 moe_status moe_route_topk(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
@@ -217,7 +218,7 @@ moe_status moe_route_topk(const moe_layer_desc* desc, const void* x, moe_dtype d
   a.ids = ids; a.w = w;
   if (logits) a.logits = logits;
   a.sh_gate_vec = nullptr;  // the shared gate is not part of routing
-  hipError_t e = launch_router(a, false, stream);
+  hipError_t e = launch_router(a, false, 0, stream, Ev{});
   if (e == hipSuccess) e = launch_topk(a, stream);
   return hip_status(e);
 }
@@ -225,13 +226,11 @@ moe_status moe_route_topk(const moe_layer_desc* desc, const void* x, moe_dtype d
 // Host-side check that the chosen path's launch shapes fit, before anything is enqueued.
 static bool path_fits(const KArgs& a) { return gemv_fits(a); }
 
-static moe_status expert_ffn_impl(KArgs& a, hipStream_t stream, Stages& st) {
-  hipError_t e = hipSuccess;
-  // GEMV path: per (token, slot) gate/up, then per-token down + combine
-  e = launch_gateup_gemv(a, stream);
-  if (e == hipSuccess) e = st.mark();
-  if (e == hipSuccess) e = launch_down_gemv(a, stream);
-  if (e == hipSuccess) e = st.mark();
+// Expert part of the layer: per-pair gate/up (+ top-k unless routing is
+// given), then per-token down + combine.
+static moe_status expert_ffn_impl(KArgs& a, bool routing_given, hipStream_t stream, Stages& st) {
+  hipError_t e = launch_gateup(a, routing_given, stream, st.next());
+  if (e == hipSuccess) e = launch_down(a, stream, st.next());
   return hip_status(e);
 }
 
@@ -261,12 +260,9 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq, const 
   a.w = const_cast<float*>(w);
   a.y = y;
   if (!path_fits(a)) return MOE_EUNSUPPORTED;
-  if (desc->sh_gate_vec) {
-    hipError_t e = launch_shared_gate(a, stream);
-    if (e != hipSuccess) return MOE_EHIP;
-  }
-  Stages stg{nullptr, 0, 0, stream};
-  return expert_ffn_impl(a, stream, stg);
+  if (desc->sh_gate_vec && launch_shared_gate(a, stream) != hipSuccess) return MOE_EHIP;
+  Stages stg{nullptr, 0, 0};
+  return expert_ffn_impl(a, true, stream, stg);
 }
 
 static moe_status layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
@@ -292,22 +288,10 @@ static moe_status layer_forward(const moe_layer_desc* desc, const void* x, moe_d
   if (ids_out) a.ids = ids_out;
   if (w_out) a.w = w_out;
   if (!path_fits(a)) return MOE_EUNSUPPORTED;
-  Stages stg{events, n_events, 0, stream};
-  hipError_t e = stg.mark();
-  const int Bx = desc->fmt_gate == MOE_WFMT_MXFP4 ? 32 : 256;
-  if (e == hipSuccess)
-    e = launch_quant(x, dtype, T, a.H, Bx, a.xqs, a.xd, Bx == 256 ? a.xbs : nullptr, a.counters,
-                     64, stream);
-  if (e == hipSuccess) e = stg.mark();
-  const bool fuse = T <= 8;
-  if (e == hipSuccess) e = launch_router(a, fuse, stream);
-  if (e == hipSuccess) e = stg.mark();
-  if (!fuse) {
-    if (e == hipSuccess) e = launch_topk(a, stream);
-    if (e == hipSuccess) e = stg.mark();
-  }
+  Stages stg{events, n_events, 0};
+  hipError_t e = launch_router(a, true, 0, stream, stg.next());
   if (e != hipSuccess) return MOE_EHIP;
-  return expert_ffn_impl(a, stream, stg);
+  return expert_ffn_impl(a, false, stream, stg);
 }
 
 moe_status moe_layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
@@ -326,15 +310,14 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, mo
 
 int moe_layer_stage_count(const moe_layer_desc* desc, int T) {
   if (validate_desc(desc) != MOE_OK || T <= 0 || T > kMaxTokens) return 0;
-  return T <= 8 ? 4 : 5;
+  return 3;
 }
 
 const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {
-  static const char* small[] = {"quant_act", "router_topk", "gateup", "down_combine"};
-  static const char* large[] = {"quant_act", "router", "topk", "gateup", "down_combine"};
+  static const char* names[] = {"router", "gateup", "down"};
   const int n = moe_layer_stage_count(desc, T);
   if (stage < 0 || stage >= n) return nullptr;
-  return T <= 8 ? small[stage] : large[stage];
+  return names[stage];
 }
 
 moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,

@@ -1,0 +1,586 @@
+#pragma once
+// Device-side building blocks of the routed-expert MoE FFN kernels (gfx950):
+// block formats, q8 activation quantization, lane reductions and top-k.
+//
+// Block formats (ggml/GGUF conventions; OCP MX v1.0 for MXFP4):
+//   Q4_K  144 B / 256: fp16 d, fp16 dmin, 12 B of 6-bit sub-block scales and
+//         mins, 128 B of nibbles (byte i of 32-byte chunk c: weight 64c+i low,
+//         64c+32+i high). w = d*sc_j*q - dmin*m_j, j = sub-block of 32.
+//   Q6_K  210 B / 256: ql[128], qh[64], int8 scales[16], fp16 d.
+//         w = d*sc_s*(q - 32), s = sub-block of 16.
+//   MXFP4 17 B / 32: E8M0 scale byte, 16 B of e2m1 nibbles (byte i: element i
+//         low, element i+16 high). w = e2m1 * 2^(e-127).
+// Every dot product is an integer (or exact fp32) sum of weight quants times
+// activation quants per block, rescaled per block in fp32: the integer-dot
+// numerics the Pulsar README describes for its q8_K/q8_0 activations.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace dev {
+
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Global-address-space views. Weight pointers often come from LDS tables, where
+// the compiler cannot prove they are global and would emit FLAT loads; FLAT
+// loads also count against lgkmcnt, so any later LDS wait would drain them.
+#define MOE_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const MOE_GLOBAL T* gp(const void* p) {
+  return (const MOE_GLOBAL T*)(p);
+}
+
+// Streaming (non-temporal) 16-byte load: expert weights are read once per call.
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(gp<u32x4>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_nt4(const void* p) {
+  return __builtin_nontemporal_load(gp<uint32_t>(p));
+}
+__device__ __forceinline__ uint16_t ld_nt2(const void* p) {
+  return __builtin_nontemporal_load(gp<uint16_t>(p));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float load_x(const void* x, int dtype, size_t i) {
+  return dtype == 0 ? static_cast<const float*>(x)[i]
+                    : bf16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+__device__ __forceinline__ int sdot4(int a, int b, int c) {
+  return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// Sum over aligned groups of 8 lanes with DPP; every lane of the group gets the sum.
+__device__ __forceinline__ int sum8(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  return v;
+}
+
+// ---- DPP reductions. Prefix over 16-lane rows with row_shr 1/2/4/8, then
+// row_bcast 15/31 carry row results upward; lane 63 ends with the full value,
+// which readlane makes wave-uniform. For sums, lanes without a source add 0;
+// for max, they keep their own value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add_f(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+  return v + __int_as_float(o);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_f(float v) {
+  const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK,
+                                            0xF, false);
+  return fmaxf(v, __int_as_float(o));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, ROW_MASK, 0xF,
+                                             false);
+  return v + __longlong_as_double((static_cast<long long>(hi) << 32) |
+                                  static_cast<uint32_t>(lo));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add_f<0x111, 0xF>(v);
+  v = dpp_add_f<0x112, 0xF>(v);
+  v = dpp_add_f<0x114, 0xF>(v);
+  v = dpp_add_f<0x118, 0xF>(v);
+  v = dpp_add_f<0x142, 0xA>(v);
+  v = dpp_add_f<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = dpp_max_f<0x111, 0xF>(v);
+  v = dpp_max_f<0x112, 0xF>(v);
+  v = dpp_max_f<0x114, 0xF>(v);
+  v = dpp_max_f<0x118, 0xF>(v);
+  v = dpp_max_f<0x142, 0xA>(v);
+  v = dpp_max_f<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v = dpp_add_d<0x111, 0xF>(v);
+  v = dpp_add_d<0x112, 0xF>(v);
+  v = dpp_add_d<0x114, 0xF>(v);
+  v = dpp_add_d<0x118, 0xF>(v);
+  v = dpp_add_d<0x142, 0xA>(v);
+  v = dpp_add_d<0x143, 0xC>(v);
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), 63);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 63);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+
+// Max over aligned groups of 8 lanes (every lane of the group gets it).
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  return v;
+}
+
+// Sum over aligned groups of 4 lanes (every lane of the quad gets it).
+__device__ __forceinline__ int sum4(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  return v;
+}
+
+// One step of a DPP max over 64-bit keys; lanes without a source keep their value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ unsigned long long dpp_max_step(unsigned long long v) {
+  const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+  const unsigned long long o = (static_cast<unsigned long long>(ohi) << 32) | olo;
+  return o > v ? o : v;
+}
+
+// Max of a 64-bit key over the wave (row_shr 1/2/4/8 inside 16-lane rows, then
+// row_bcast 15/31 across rows; lane 63 ends with the maximum), broadcast to all.
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  v = dpp_max_step<0x111, 0xF>(v);
+  v = dpp_max_step<0x112, 0xF>(v);
+  v = dpp_max_step<0x114, 0xF>(v);
+  v = dpp_max_step<0x118, 0xF>(v);
+  v = dpp_max_step<0x142, 0xA>(v);
+  v = dpp_max_step<0x143, 0xC>(v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// ------------------------------------------------------------ q8 quantization
+// One wave quantizes 256 consecutive values, 4 per lane (lane l: 4l..4l+3), as
+// blocks of B = 256 (one block) or B = 32 (eight blocks of 8 lanes).
+// fp32 recipe: amax; iscale = 127/amax (IEEE division); q = rne(v * iscale)
+// clamped to +-127; d = amax/127; amax == 0 gives d = 0 and q = 0.
+// Lanes past the end pass zeros (whole blocks only) and store nothing.
+template <int B>
+__device__ __forceinline__ float quant_wave_q(const float v[4], int q[4]) {
+  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  static_assert(B == 256 || B == 32, "block of 256 (one per wave) or 32 (8 lanes)");
+  amax = B == 256 ? wave_max(amax) : max8(amax);
+  if (amax == 0.0f) {
+    q[0] = q[1] = q[2] = q[3] = 0;
+    return 0.0f;
+  }
+  const float iscale = 127.0f / amax;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r = __builtin_rintf(v[i] * iscale);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    q[i] = static_cast<int>(r);
+  }
+  return amax / 127.0f;
+}
+
+// NJ independent 256-value pieces quantized in lock-step by one wave, so the
+// dependent chains (DPP max, divisions) of different pieces interleave.
+// Same fp32 recipe as quant_wave_q.
+template <int B, int NJ>
+__device__ __forceinline__ void quant_wave_batch(const float4 (&hv)[NJ], int (&q)[NJ][4],
+                                                 float (&dv)[NJ]) {
+  float am[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    am[j] = fmaxf(fmaxf(fabsf(hv[j].x), fabsf(hv[j].y)), fmaxf(fabsf(hv[j].z), fabsf(hv[j].w)));
+  if constexpr (B == 256) {
+#define MOE_BSTEP(CTRL, RM) _Pragma("unroll") for (int j = 0; j < NJ; ++j) am[j] = dpp_max_f<CTRL, RM>(am[j]);
+    MOE_BSTEP(0x111, 0xF) MOE_BSTEP(0x112, 0xF) MOE_BSTEP(0x114, 0xF) MOE_BSTEP(0x118, 0xF)
+    MOE_BSTEP(0x142, 0xA) MOE_BSTEP(0x143, 0xC)
+#undef MOE_BSTEP
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      am[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am[j]), 63));
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) am[j] = max8(am[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const float v[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w};
+    if (am[j] == 0.0f) {
+      q[j][0] = q[j][1] = q[j][2] = q[j][3] = 0;
+      dv[j] = 0.0f;
+    } else {
+      const float iscale = 127.0f / am[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float r = __builtin_rintf(v[i] * iscale);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        q[j][i] = static_cast<int>(r);
+      }
+      dv[j] = am[j] / 127.0f;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_q8x4(const int q[4]) {
+  return (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) |
+         (static_cast<uint32_t>(q[3] & 0xFF) << 24);
+}
+
+// Stores as int8 quants + scales (+ 16-element sums for B = 256).
+template <int B>
+__device__ __forceinline__ void quant_wave(const float v[4], bool valid, int lane, int8_t* qs,
+                                           float* d, int16_t* bs) {
+  int q[4];
+  const float dv = quant_wave_q<B>(v, q);
+  constexpr int G = B / 4;
+  if (valid) {
+    const uint32_t packed = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) |
+                            (static_cast<uint32_t>(q[3] & 0xFF) << 24);
+    reinterpret_cast<uint32_t*>(qs)[lane] = packed;
+    if ((lane % G) == 0) d[lane / G] = dv;
+  }
+  if (B == 256) {
+    const int sm = sum4(q[0] + q[1] + q[2] + q[3]);
+    if (valid && (lane & 3) == 0) bs[lane >> 2] = static_cast<int16_t>(sm);
+  }
+}
+
+// B = 32 quantization stored as fp16 pairs (a[i], a[i+16]) per block, the layout
+// the MXFP4 dot reads: ap gets 128 pairs for the 256-value piece.
+__device__ __forceinline__ void quant_wave_pairs(const float v[4], bool valid, int lane,
+                                                 half2_t* ap, float* d) {
+  int q[4];
+  const float dv = quant_wave_q<32>(v, q);
+  int o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)  // partner 16 elements ahead: lane + 4 (DPP row_shl:4)
+    o[i] = __builtin_amdgcn_update_dpp(0, q[i], 0x104, 0xF, 0xF, false);
+  const int bl = lane >> 3, off = 4 * (lane & 7);
+  if (valid && off < 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ap[16 * bl + off + i] = half2_t{static_cast<_Float16>(q[i]), static_cast<_Float16>(o[i])};
+  }
+  if (valid && (lane & 7) == 0) d[bl] = dv;
+}
+
+// Activations of one row vector as the dot routines read them (LDS).
+struct ActView {
+  const int8_t* qs;     // [K] (Q8_K)
+  const float* d;       // [K / B]
+  const int16_t* bs;    // [K / 16] (Q8_K)
+  const half2_t* ap;    // [K / 2] fp16 pairs (Q8_32): block b, i < 16: (a[32b+i], a[32b+16+i])
+};
+
+// ------------------------------------------------------------------ formats
+// Each format: BE elements and BB bytes per block, LPB lanes cooperate on one
+// block. load() reads the lane's share of a block from global memory;
+// partials() returns the block's integer partials (summed over the LPB lanes);
+// value() turns them into the fp32 block value d8 * (...).
+
+struct FmtQ4K {
+  static constexpr int BE = 256, BB = 144, LPB = 8;
+  struct Raw { uint4 hdr, q; };
+  __device__ static __forceinline__ void load(Raw& r, const uint8_t* blk, int sub) {
+    r.hdr = ld_nt16(blk);
+    r.q = ld_nt16(blk + 16 + 16 * sub);
+  }
+  // Lane `sub` holds qs bytes 16*sub..16*sub+15: chunk c = sub/2, half hh = sub%2, i.e.
+  // weights 64c+16hh+i (low nibbles, sub-block 2c) and 64c+32+16hh+i (high, 2c+1).
+  __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int sub) {
+    const int c = sub >> 1, hh = sub & 1;
+    const int4* ax = reinterpret_cast<const int4*>(a.qs + b * 256);
+    const int4 alo = ax[4 * c + hh];
+    const int4 ahi = ax[4 * c + 2 + hh];
+    int dl = 0, dh = 0;
+    dl = sdot4(r.q.x & 0x0F0F0F0F, alo.x, dl);
+    dl = sdot4(r.q.y & 0x0F0F0F0F, alo.y, dl);
+    dl = sdot4(r.q.z & 0x0F0F0F0F, alo.z, dl);
+    dl = sdot4(r.q.w & 0x0F0F0F0F, alo.w, dl);
+    dh = sdot4((r.q.x >> 4) & 0x0F0F0F0F, ahi.x, dh);
+    dh = sdot4((r.q.y >> 4) & 0x0F0F0F0F, ahi.y, dh);
+    dh = sdot4((r.q.z >> 4) & 0x0F0F0F0F, ahi.z, dh);
+    dh = sdot4((r.q.w >> 4) & 0x0F0F0F0F, ahi.w, dh);
+    // 6-bit scales/mins of the 8 sub-blocks as bytes: sub-blocks 0..3 sit in the
+    // low 6 bits of scale bytes 0..3 (sc) and 4..7 (m); 4..7 take their low 4
+    // bits from bytes 8..11 and their top 2 bits from bits 6..7 of bytes 0..7.
+    const uint32_t s0 = r.hdr.y, s1 = r.hdr.z, s2 = r.hdr.w;
+    const uint32_t sc03 = s0 & 0x3F3F3F3Fu, m03 = s1 & 0x3F3F3F3Fu;
+    const uint32_t sc47 = (s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u);
+    const uint32_t m47 = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
+    const uint32_t scw = c < 2 ? sc03 : sc47, mw = c < 2 ? m03 : m47;
+    const int sh = 16 * (c & 1);
+    const int sc0 = (scw >> sh) & 0xFF, sc1 = (scw >> (sh + 8)) & 0xFF;
+    const int m0 = (mw >> sh) & 0xFF, m1 = (mw >> (sh + 8)) & 0xFF;
+    const int16_t* bs = a.bs + b * 16;
+    const int S1 = sc0 * dl + sc1 * dh;
+    const int S2 = m0 * bs[4 * c + hh] + m1 * bs[4 * c + 2 + hh];
+    return make_int2(sum8(S1), sum8(S2));
+  }
+  __device__ static __forceinline__ float value(const Raw& r, int2 p, float d8) {
+    const float d = half_bits_to_f32(r.hdr.x & 0xFFFF), dmin = half_bits_to_f32(r.hdr.x >> 16);
+    return d8 * (d * static_cast<float>(p.x) - dmin * static_cast<float>(p.y));
+  }
+};
+
+// 8 bytes at a 2-byte aligned address: dwords at p & ~3, the next one, and the
+// one holding byte p + 7, so no dword read lies wholly outside [p, p + 8).
+__device__ __forceinline__ uint2 load8_unaligned(const uint8_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint8_t* w = reinterpret_cast<const uint8_t*>(a & ~static_cast<uintptr_t>(3));
+  const uint8_t* w_last = reinterpret_cast<const uint8_t*>((a + 7) & ~static_cast<uintptr_t>(3));
+  const uint32_t sh = static_cast<uint32_t>(a & 3);
+  const uint32_t w0 = ld_nt4(w), w1 = ld_nt4(w + 4), w2 = ld_nt4(w_last);
+  return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
+}
+
+struct FmtQ6K {
+  static constexpr int BE = 256, BB = 210, LPB = 8;
+  // Lane `sub`: half h = sub/4, j = sub%4 holds element i in [8j, 8j+8) of the four
+  // quarters of half h: ql[64h+8j..], ql[64h+32+8j..], qh[32h+8j..].
+  struct Raw { uint2 l0, l1, qh, sc; uint32_t dbits; };
+  __device__ static __forceinline__ void load(Raw& r, const uint8_t* blk, int sub) {
+    const int h = sub >> 2, j = sub & 3;
+    r.l0 = load8_unaligned(blk + 64 * h + 8 * j);
+    r.l1 = load8_unaligned(blk + 64 * h + 32 + 8 * j);
+    r.qh = load8_unaligned(blk + 128 + 32 * h + 8 * j);
+    r.sc = load8_unaligned(blk + 192 + 8 * h);
+    r.dbits = ld_nt2(blk + 208);
+  }
+  __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int sub) {
+    const int h = sub >> 2, j = sub & 3;
+    const int8_t* ab = a.qs + b * 256 + 128 * h + 8 * j;
+    const int16_t* bs = a.bs + b * 16;
+    int S = 0;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const uint2 lo = (qq & 1) ? r.l1 : r.l0;
+      const int lsh = (qq >> 1) * 4;
+      const int hsh = 2 * qq;
+      const uint32_t w0 = ((lo.x >> lsh) & 0x0F0F0F0Fu) | (((r.qh.x >> hsh) & 0x03030303u) << 4);
+      const uint32_t w1 = ((lo.y >> lsh) & 0x0F0F0F0Fu) | (((r.qh.y >> hsh) & 0x03030303u) << 4);
+      const int2 av = *reinterpret_cast<const int2*>(ab + 32 * qq);
+      int dot = sdot4(static_cast<int>(w0), av.x, 0);
+      dot = sdot4(static_cast<int>(w1), av.y, dot);
+      const int sidx = 2 * qq + (j >> 1);  // sub-block 8h + sidx
+      const uint32_t scw = sidx < 4 ? r.sc.x : r.sc.y;
+      const int sc = static_cast<int>(static_cast<int8_t>((scw >> (8 * (sidx & 3))) & 0xFF));
+      // q is stored with +32: subtract 32 * (sum of a over the sub-block) once per sub-block
+      const int corr = (j & 1) ? 0 : 32 * bs[8 * h + sidx];
+      S += sc * (dot - corr);
+    }
+    return make_int2(sum8(S), 0);
+  }
+  __device__ static __forceinline__ float value(const Raw& r, int2 p, float d8) {
+    return d8 * half_bits_to_f32(r.dbits) * static_cast<float>(p.x);
+  }
+};
+
+struct FmtMXFP4 {
+  static constexpr int BE = 32, BB = 17, LPB = 1;
+  struct Raw { uint32_t w[5]; uint32_t sh; };
+  __device__ static __forceinline__ void load(Raw& r, const uint8_t* blk, int) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(blk);
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(a & ~static_cast<uintptr_t>(3));
+    r.sh = static_cast<uint32_t>(a & 3);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) r.w[i] = ld_nt4(p + 4 * i);
+  }
+  __device__ static __forceinline__ uint32_t scale_byte(const Raw& r) {
+    return (r.w[0] >> (8 * r.sh)) & 0xFF;
+  }
+  // Exact: e2m1 values and int8 activations are exact in fp16, products exact in
+  // fp32 and every partial sum is a multiple of 0.5 below 2^23.
+  __device__ static __forceinline__ float dot(const Raw& r, const ActView& a, int b) {
+    const half2_t* ap = a.ap + 16 * b;
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qw = r.sh == 3 ? r.w[i + 1]
+                                    : __builtin_amdgcn_alignbyte(r.w[i + 1], r.w[i], r.sh + 1);
+      acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 0),
+                                   ap[4 * i + 0], acc, false);
+      acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 1),
+                                   ap[4 * i + 1], acc, false);
+      acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 2),
+                                   ap[4 * i + 2], acc, false);
+      acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 3),
+                                   ap[4 * i + 3], acc, false);
+    }
+    return acc;
+  }
+  __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int) {
+    return make_int2(static_cast<int>(2.0f * dot(r, a, b)), 0);
+  }
+  __device__ static __forceinline__ float value_from_dot(const Raw& r, float s, float d8) {
+    return d8 * __builtin_ldexpf(s, static_cast<int>(scale_byte(r)) - 127);
+  }
+};
+
+template <int FMT> struct FmtOf;
+template <> struct FmtOf<FMT_Q4_K> { using T = FmtQ4K; };
+template <> struct FmtOf<FMT_Q6_K> { using T = FmtQ6K; };
+template <> struct FmtOf<FMT_MXFP4> { using T = FmtMXFP4; };
+
+// fp32 value of one block for the lane's share (all LPB lanes get the value).
+template <class F>
+__device__ __forceinline__ float block_value(const typename F::Raw& r, const ActView& a, int b,
+                                             int sub) {
+  if constexpr (F::LPB == 1) {
+    return F::value_from_dot(r, F::dot(r, a, b), a.d[b]);
+  } else {
+    return F::value(r, F::partials(r, a, b, sub), a.d[b]);
+  }
+}
+
+// Stage q8 activations (global, one token) into LDS in the layout the format reads.
+template <int AFMT_MX>
+__device__ __forceinline__ void stage_act(const int8_t* qs, const float* d, const int16_t* bs,
+                                          int K, int8_t* lqs, float* ld, int16_t* lbs,
+                                          half2_t* lap) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if constexpr (!AFMT_MX) {
+    for (int i = tid; i < K / 16; i += nt) {
+      reinterpret_cast<int4*>(lqs)[i] = reinterpret_cast<const int4*>(qs)[i];
+      lbs[i] = bs[i];
+    }
+    for (int i = tid; i < K / 256; i += nt) ld[i] = d[i];
+  } else {
+    for (int i = tid; i < K / 2; i += nt) {
+      const int b = i / 16, ii = i % 16;
+      lap[i] = half2_t{static_cast<_Float16>(qs[32 * b + ii]),
+                       static_cast<_Float16>(qs[32 * b + 16 + ii])};
+    }
+    for (int i = tid; i < K / 32; i += nt) ld[i] = d[i];
+  }
+}
+
+__device__ __forceinline__ float act_fn(int act, float alpha, float limit, float g, float u) {
+  if (act == 0) return g / (1.0f + __expf(-g)) * u;
+  const float gc = fminf(g, limit);
+  const float uc = fminf(fmaxf(u, -limit), limit);
+  return gc / (1.0f + __expf(-alpha * gc)) * (uc + 1.0f);
+}
+
+// Order-preserving key: larger float -> larger key; -0 and +0 share a key.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  // keys are compared as unsigned: use the integer max on DPP-moved values
+#define MOE_DPP_UMAX(CTRL, RM) \
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, RM, 0xF, false)))
+  MOE_DPP_UMAX(0x111, 0xF);
+  MOE_DPP_UMAX(0x112, 0xF);
+  MOE_DPP_UMAX(0x114, 0xF);
+  MOE_DPP_UMAX(0x118, 0xF);
+  MOE_DPP_UMAX(0x142, 0xA);
+  MOE_DPP_UMAX(0x143, 0xC);
+#undef MOE_DPP_UMAX
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// Top-k of one token by one wave (all 64 lanes must call it). Rank order is
+// (key descending, index ascending) with key = logit (+ selection bias, one
+// fp32 add). Weights come from the unbiased logits: softmax over the selected
+// (norm_topk) or over all E, or sigmoid (normalized over the selected when
+// norm_topk), times route_scale. Lane r < k writes rank r to ids_out[r] and
+// w_out[r] (global or LDS). Each lane holds NC candidates (E <= 64 * NC),
+// expert e = lane + 64 * i in register i. Per rank: one 32-bit DPP max of the
+// keys, then ballots find the lowest index holding that key.
+template <int NC>
+__device__ __forceinline__ void wave_topk(const float* logits, const float* sel_bias, int E,
+                                          int k, int router, int norm_topk, float route_scale,
+                                          int* ids_out, float* w_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[NC];
+  float lg[NC];
+  float sb[NC];
+  // all loads issued before any use (clamped indices, masked afterwards)
+#pragma unroll
+  for (int i = 0; i < NC; ++i) lg[i] = logits[min(lane + 64 * i, E - 1)];
+  if (sel_bias) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) sb[i] = sel_bias[min(lane + 64 * i, E - 1)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) sb[i] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const bool valid = lane + 64 * i < E;
+    // key 0 is below every real key: an absent (or later removed) candidate
+    key[i] = valid ? float_key(sel_bias ? lg[i] + sb[i] : lg[i]) : 0u;
+    lg[i] = valid ? lg[i] : -INFINITY;
+  }
+  int my_id = 0;
+  float my_l = -INFINITY;
+  for (int r = 0; r < k; ++r) {
+    uint32_t bk = 0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) bk = max(bk, key[i]);
+    const uint32_t kmax = wave_max_u32(bk);
+    // lowest expert index holding kmax: first register i with a hit, then lowest lane
+    int e = -1;
+    float l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const unsigned long long m = __ballot(key[i] == kmax);
+      if (e < 0 && m != 0ull) {
+        const int ln = __builtin_ctzll(m);
+        e = ln + 64 * i;
+        l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lg[i]), ln));
+        if (lane == ln) key[i] = 0;
+      }
+    }
+    if (lane == r) {
+      my_id = e;
+      my_l = l;
+    }
+  }
+  // weights, one selected expert per lane (lanes >= k hold -inf / 0)
+  float w;
+  if (router == 0) {
+    float mx, z;
+    if (norm_topk) {
+      mx = wave_max(my_l);
+      const float ex = lane < k ? expf(my_l - mx) : 0.0f;
+      z = wave_sum(ex);
+      w = ex / z;
+    } else {
+      float lm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) lm = fmaxf(lm, lg[i]);
+      mx = wave_max(lm);
+      float zz = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) if (lane + 64 * i < E) zz += expf(lg[i] - mx);
+      z = wave_sum(zz);
+      w = lane < k ? expf(my_l - mx) / z : 0.0f;
+    }
+  } else {
+    const float sg = lane < k ? 1.0f / (1.0f + expf(-my_l)) : 0.0f;
+    w = norm_topk ? sg / wave_sum(sg) : sg;
+  }
+  if (lane < k) {
+    ids_out[lane] = my_id;
+    w_out[lane] = w * route_scale;
+  }
+}
+
+}  // namespace dev
+}  // namespace moe

@@ -11,6 +11,33 @@ namespace moe {
 
 enum { FMT_Q4_K = 0, FMT_Q6_K = 1, FMT_MXFP4 = 2 };
 
+// Unsigned division by a runtime constant d >= 1 without a divide sequence
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994): q = (umulhi(n, m) + n) >> s with
+// s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1; exact for n < 2^31.
+struct Div {
+  uint32_t d, m, s;
+  static Div make(uint32_t d_) {
+    uint32_t sh = 0;
+    while ((1ull << sh) < d_) ++sh;
+    const uint64_t m64 = ((1ull << 32) * ((1ull << sh) - d_)) / d_ + 1;
+    return Div{d_, static_cast<uint32_t>(m64), sh};
+  }
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    const uint32_t hi = static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> 32);
+    return (hi + n) >> s;
+  }
+  __host__ __device__ __forceinline__ uint32_t mod(uint32_t n, uint32_t q) const {
+    return n - q * d;
+  }
+};
+
+// Down-projection pointers of one (token, slot) pair, resolved by k_gateup.
+struct SlotRef {
+  const uint8_t* down;  // nullptr: expert not present (slot contributes nothing)
+  const float* bias;
+};
+
 // Everything a kernel may need, resolved on the host. Passed by value.
 struct KArgs {
   int H, F, E, k, T;
@@ -43,9 +70,10 @@ struct KArgs {
   int32_t* ids;     // [T, k]
   float* w;         // [T, k]
   float* shw;       // [T] shared-expert weight
+  SlotRef* slots;   // [T, k]
   float* h;         // [P, F], P = T * k + T * has_shared
   float* y;         // [T, H]
-  uint32_t* counters;  // 64 words, zeroed by the first kernel of a call
+  uint32_t* counters;  // one word per (token, slot) pair, reset by the router kernel
   // grouped path
   int32_t* counts;     // [E + 1]
   int32_t* offsets;    // [E + 2]
@@ -59,7 +87,7 @@ struct KArgs {
 
 // Workspace layout (byte offsets from the base, each 256-aligned).
 struct WsLayout {
-  size_t counters, xqs, xd, xbs, logits, ids, w, shw, h, counts, offsets, pair_list, active,
+  size_t counters, xqs, xd, xbs, logits, ids, w, shw, slots, h, counts, offsets, pair_list, active,
       hqs, hd, hbs, part, total;
 };
 WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped);
@@ -73,20 +101,23 @@ bool gemv_fits(const KArgs& a);
 // Which expert-FFN path a chunk of T tokens takes (fixed rule, see moe_api.cpp).
 bool use_grouped(int T, int k);
 
+// Optional per-kernel timing events, recorded by the dispatch itself
+// (hipExtLaunchKernel start/stop), i.e. the kernel's execution window.
+struct Ev {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Launchers. Each returns hipSuccess or the launch error.
 hipError_t launch_quant(const void* x, int dtype, int T, int H, int B, int8_t* qs, float* d,
-                        int16_t* bs, uint32_t* zero_words, int n_zero, hipStream_t s);
+                        int16_t* bs, hipStream_t s);
+hipError_t launch_zero(uint32_t* p, int n, hipStream_t s, Ev ev);
 hipError_t launch_shared_gate(const KArgs& a, hipStream_t s);
-hipError_t launch_router(const KArgs& a, bool fuse_topk, hipStream_t s);
+// Router logits; quant: also q8 of x; n_clear: counters to reset for k_gateup.
+hipError_t launch_router(const KArgs& a, bool quant, int n_clear, hipStream_t s, Ev ev);
 hipError_t launch_topk(const KArgs& a, hipStream_t s);
-hipError_t launch_gateup_gemv(const KArgs& a, hipStream_t s);
-hipError_t launch_down_gemv(const KArgs& a, hipStream_t s);
-hipError_t launch_bucket(const KArgs& a, hipStream_t s);
-hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s);
-hipError_t launch_hquant(const KArgs& a, hipStream_t s);
-hipError_t launch_down_grouped(const KArgs& a, hipStream_t s);
-hipError_t launch_combine(const KArgs& a, hipStream_t s);
-hipError_t launch_copy_routing(const KArgs& a, int32_t* ids_out, float* w_out, hipStream_t s);
+hipError_t launch_gateup(const KArgs& a, bool routing_given, hipStream_t s, Ev ev);
+hipError_t launch_down(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_t stride,
                              const int8_t* qs, const float* d, const int16_t* bs,
                              int32_t* out, hipStream_t s);

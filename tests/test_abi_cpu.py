@@ -170,6 +170,6 @@ def test_block_dots_validation():
 
 def test_stage_names():
     d = good_desc()
-    assert M.moe_layer_stage_count(d, 1) == 4
-    assert [M.moe_layer_stage_name(d, 1, i) for i in range(4)][2] == "gateup"
+    assert M.moe_layer_stage_count(d, 1) == 3
+    assert [M.moe_layer_stage_name(d, 1, i) for i in range(3)] == ["router", "gateup", "down"]
     assert M.moe_layer_stage_name(d, 1, 9) is None
