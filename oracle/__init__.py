@@ -269,7 +269,11 @@ class Layer:
         return out
 
     def expert_part(self, x_row: np.ndarray, ids: np.ndarray, w: np.ndarray) -> np.ndarray:
+        """Expert part of one token for given routing (k ids and weights; an id
+        outside [0, E) contributes nothing), plus the shared expert."""
         cfg = self.cfg
+        if len(ids) != cfg.k or len(w) != cfg.k:
+            raise ValueError(f"expert_part needs exactly k = {cfg.k} ids and weights")
         y = np.empty(cfg.H, np.float64)
         lib().or_expert_part_token(C.byref(self.L), _p(np.ascontiguousarray(x_row, np.float32)),
                                    _p(np.ascontiguousarray(ids, np.int32)),

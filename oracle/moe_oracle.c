@@ -329,7 +329,9 @@ static void add_experts(const or_layer* L, const float* x, const int32_t* ids,
   for (int i = 0; i < H; ++i) y[i] = 0.0;
   for (int j = 0; j < L->k; ++j) {
     int e = ids[j];
-    if (!L->gate[e]) continue; /* not present: contributes nothing */
+    /* an id outside [0, E) or a NULL expert is a slot that is "not mine": it
+       contributes nothing (given routing may carry such ids) */
+    if (e < 0 || e >= L->E || !L->gate[e]) continue;
     or_expert_ffn(L, L->gate[e], L->up[e], L->down[e], L->b_gate ? L->b_gate[e] : NULL,
                   L->b_up ? L->b_up[e] : NULL, L->b_down ? L->b_down[e] : NULL, xq.q, xq.d,
                   xq.bs, o, h32 ? h32 + (size_t)j * F : NULL);

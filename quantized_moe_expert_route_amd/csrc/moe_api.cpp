@@ -88,13 +88,14 @@ void bind_ws(KArgs& a, const WsLayout& L, void* ws) {
   a.shw = reinterpret_cast<float*>(b + L.shw);
   a.slots = reinterpret_cast<SlotRef*>(b + L.slots);
   a.h = reinterpret_cast<float*>(b + L.h);
-  a.counts = reinterpret_cast<int32_t*>(b + L.counts);
-  a.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
-  a.pair_list = reinterpret_cast<int32_t*>(b + L.pair_list);
-  a.active = reinterpret_cast<int32_t*>(b + L.active);
   a.hqs = reinterpret_cast<int8_t*>(b + L.hqs);
   a.hd = reinterpret_cast<float*>(b + L.hd);
   a.hbs = reinterpret_cast<int16_t*>(b + L.hbs);
+  a.rpart = reinterpret_cast<double*>(b + L.rpart);
+  a.pair_tmp = reinterpret_cast<int32_t*>(b + L.pair_tmp);
+  a.plist = reinterpret_cast<int2*>(b + L.plist);
+  a.present = reinterpret_cast<int32_t*>(b + L.present);
+  a.tiles = reinterpret_cast<GTile*>(b + L.tiles);
   a.part = reinterpret_cast<float*>(b + L.part);
 }
 
@@ -116,13 +117,15 @@ struct Stages {
 
 }  // namespace
 
-// Dispatch rule between the two expert-FFN paths (see the header of
-// moe_kernels.hip): chunks of up to 4 tokens take the per-(token, slot) GEMV
-// path; larger chunks take the expert-grouped path, whose int8 MFMA tiles
-// amortize each weight read over all tokens routed to the expert.
-bool use_grouped(int T, int k) {
-  (void)T; (void)k;
-  return false;
+// Dispatch rule between the two expert-FFN paths: chunks of up to 4 tokens,
+// and every chunk of a layer with an MXFP4 matrix, take the per-(token, slot)
+// GEMV path (moe_kernels.hip); larger chunks of K-quant layers take the
+// expert-grouped path (moe_grouped.hip), whose int8 MFMA tiles read each
+// selected expert's weights once per 16 tokens routed to it.
+constexpr int kGroupedMinTokens = 5;
+
+bool use_grouped(int T, int fmt_gate, int fmt_down) {
+  return T >= kGroupedMinTokens && fmt_gate != FMT_MXFP4 && fmt_down != FMT_MXFP4;
 }
 
 WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped) {
@@ -140,17 +143,20 @@ WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool group
   L.shw = take(static_cast<size_t>(T) * 4);
   L.slots = take(static_cast<size_t>(T) * k * sizeof(SlotRef));
   L.h = take(P * F * 4);
-  L.hqs = take(P * F);
-  L.hd = take(P * (F / 32) * 4);
-  L.hbs = take(P * (F / 16) * 2);
   if (grouped) {
-    L.counts = take(static_cast<size_t>(E + 1) * 4);
-    L.offsets = take(static_cast<size_t>(E + 2) * 4);
-    L.pair_list = take(static_cast<size_t>(T) * k * 4);
-    L.active = take(static_cast<size_t>(E + 1) * 4);
+    const RouterSplit rs = router_split(T, E, H);
+    L.hqs = take(P * F);
+    L.hd = take(P * (F / 256) * 4);
+    L.hbs = take(P * (F / 16) * 2);
+    L.rpart = take(static_cast<size_t>(rs.ks) * T * (E + 1) * 8);
+    L.pair_tmp = take(P * 4);
+    L.plist = take(P * 8);
+    L.present = take(P * 4);
+    L.tiles = take(static_cast<size_t>(max_tiles(T, k, E, has_shared)) * sizeof(GTile));
     L.part = take(P * H * 4);
   } else {
-    L.counts = L.offsets = L.pair_list = L.active = L.part = 0;
+    L.hqs = L.hd = L.hbs = 0;
+    L.rpart = L.pair_tmp = L.plist = L.present = L.tiles = L.part = 0;
   }
   L.total = off;
   return L;
@@ -177,7 +183,7 @@ const char* moe_status_str(moe_status s) {
 
 size_t moe_workspace_size(const moe_layer_desc* desc, int T) {
   if (validate_desc(desc) != MOE_OK || T < 0 || T > kMaxTokens) return 0;
-  const bool g = use_grouped(T, desc->top_k);
+  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
   return ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
                    desc->sh_gate != nullptr, g).total;
 }
@@ -207,7 +213,7 @@ moe_status moe_route_topk(const moe_layer_desc* desc, const void* x, moe_dtype d
   if (T < 0 || T > kMaxTokens || !ids || !w) return MOE_EINVAL;
   if (!aligned(ids, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4))) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
-  const bool g = use_grouped(T, desc->top_k);
+  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
   const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
                                desc->sh_gate != nullptr, g);
   if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
@@ -218,19 +224,37 @@ moe_status moe_route_topk(const moe_layer_desc* desc, const void* x, moe_dtype d
   a.ids = ids; a.w = w;
   if (logits) a.logits = logits;
   a.sh_gate_vec = nullptr;  // the shared gate is not part of routing
-  hipError_t e = launch_router(a, false, 0, stream, Ev{});
-  if (e == hipSuccess) e = launch_topk(a, stream);
+  hipError_t e;
+  if (g) {
+    const RouterSplit rs = router_split(T, desc->n_expert, desc->hidden);
+    e = launch_router_grouped(a, false, rs, stream, Ev{});
+    if (e == hipSuccess) e = launch_topk_sum(a, rs, stream, Ev{});
+  } else {
+    e = launch_router(a, false, 0, stream, Ev{});
+    if (e == hipSuccess) e = launch_topk(a, stream);
+  }
   return hip_status(e);
 }
 
 // Host-side check that the chosen path's launch shapes fit, before anything is enqueued.
-static bool path_fits(const KArgs& a) { return gemv_fits(a); }
+static bool path_fits(const KArgs& a, bool grouped) { return grouped || gemv_fits(a); }
 
-// Expert part of the layer: per-pair gate/up (+ top-k unless routing is
-// given), then per-token down + combine.
-static moe_status expert_ffn_impl(KArgs& a, bool routing_given, hipStream_t stream, Stages& st) {
-  hipError_t e = launch_gateup(a, routing_given, stream, st.next());
-  if (e == hipSuccess) e = launch_down(a, stream, st.next());
+// Expert part of the layer. GEMV path: per-pair gate/up (+ top-k unless routing
+// is given), then per-token down + combine. Grouped path (routing already in
+// a.ids / a.w): bucketing, tile gate/up, q8 of h, tile down, combine.
+static moe_status expert_ffn_impl(KArgs& a, bool grouped, bool routing_given, hipStream_t stream,
+                                  Stages& st) {
+  hipError_t e;
+  if (grouped) {
+    e = launch_bucket(a, stream, st.next());
+    if (e == hipSuccess) e = launch_gateup_grouped(a, stream, st.next());
+    if (e == hipSuccess) e = launch_hquant(a, stream, st.next());
+    if (e == hipSuccess) e = launch_down_grouped(a, stream, st.next());
+    if (e == hipSuccess) e = launch_combine(a, stream, st.next());
+  } else {
+    e = launch_gateup(a, routing_given, stream, st.next());
+    if (e == hipSuccess) e = launch_down(a, stream, st.next());
+  }
   return hip_status(e);
 }
 
@@ -242,12 +266,12 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq, const 
   if (T < 0 || T > kMaxTokens || !xq || !ids || !w || !y) return MOE_EINVAL;
   const int want_afmt = desc->fmt_gate == MOE_WFMT_MXFP4 ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K;
   if (xq->fmt != want_afmt || xq->T < T || xq->H != desc->hidden) return MOE_EINVAL;
-  if (!xq->qs || !xq->d || !aligned(xq->qs, 16)) return MOE_EINVAL;
-  if (want_afmt == MOE_AFMT_Q8_K && !xq->bsums) return MOE_EINVAL;
+  if (!xq->qs || !xq->d || !aligned(xq->qs, 16) || !aligned(xq->d, 4)) return MOE_EINVAL;
+  if (want_afmt == MOE_AFMT_Q8_K && (!xq->bsums || !aligned(xq->bsums, 4))) return MOE_EINVAL;
   if (desc->sh_gate_vec && validate_x(x, dtype) != MOE_OK) return MOE_EINVAL;
   if (!aligned(ids, 4) || !aligned(w, 4) || !aligned(y, 16)) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
-  const bool g = use_grouped(T, desc->top_k);
+  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
   const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
                                desc->sh_gate != nullptr, g);
   if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
@@ -259,10 +283,10 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq, const 
   a.ids = const_cast<int32_t*>(ids);
   a.w = const_cast<float*>(w);
   a.y = y;
-  if (!path_fits(a)) return MOE_EUNSUPPORTED;
+  if (!path_fits(a, g)) return MOE_EUNSUPPORTED;
   if (desc->sh_gate_vec && launch_shared_gate(a, stream) != hipSuccess) return MOE_EHIP;
   Stages stg{nullptr, 0, 0};
-  return expert_ffn_impl(a, true, stream, stg);
+  return expert_ffn_impl(a, g, true, stream, stg);
 }
 
 static moe_status layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
@@ -276,7 +300,7 @@ static moe_status layer_forward(const moe_layer_desc* desc, const void* x, moe_d
   if ((ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4))) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
   if (events && n_events < 0) return MOE_EINVAL;
-  const bool g = use_grouped(T, desc->top_k);
+  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
   const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
                                desc->sh_gate != nullptr, g);
   if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
@@ -287,11 +311,18 @@ static moe_status layer_forward(const moe_layer_desc* desc, const void* x, moe_d
   a.y = y;
   if (ids_out) a.ids = ids_out;
   if (w_out) a.w = w_out;
-  if (!path_fits(a)) return MOE_EUNSUPPORTED;
+  if (!path_fits(a, g)) return MOE_EUNSUPPORTED;
   Stages stg{events, n_events, 0};
+  if (g) {
+    const RouterSplit rs = router_split(T, desc->n_expert, desc->hidden);
+    hipError_t e = launch_router_grouped(a, true, rs, stream, stg.next());
+    if (e == hipSuccess) e = launch_topk_sum(a, rs, stream, stg.next());
+    if (e != hipSuccess) return MOE_EHIP;
+    return expert_ffn_impl(a, true, false, stream, stg);
+  }
   hipError_t e = launch_router(a, true, 0, stream, stg.next());
   if (e != hipSuccess) return MOE_EHIP;
-  return expert_ffn_impl(a, false, stream, stg);
+  return expert_ffn_impl(a, false, false, stream, stg);
 }
 
 moe_status moe_layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
@@ -310,14 +341,16 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, mo
 
 int moe_layer_stage_count(const moe_layer_desc* desc, int T) {
   if (validate_desc(desc) != MOE_OK || T <= 0 || T > kMaxTokens) return 0;
-  return 3;
+  return use_grouped(T, desc->fmt_gate, desc->fmt_down) ? 7 : 3;
 }
 
 const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {
-  static const char* names[] = {"router", "gateup", "down"};
+  static const char* gemv[] = {"router", "gateup", "down"};
+  static const char* grouped[] = {"router", "topk", "bucket", "gateup", "hquant", "down",
+                                  "combine"};
   const int n = moe_layer_stage_count(desc, T);
   if (stage < 0 || stage >= n) return nullptr;
-  return names[stage];
+  return n == 7 ? grouped[stage] : gemv[stage];
 }
 
 moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,

@@ -502,17 +502,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // w_out[r] (global or LDS). Each lane holds NC candidates (E <= 64 * NC),
 // expert e = lane + 64 * i in register i. Per rank: one 32-bit DPP max of the
 // keys, then ballots find the lowest index holding that key.
+// wave_topk_regs takes the logits already in registers (lg[i] = logit of expert
+// lane + 64 i; lanes past E may hold anything).
 template <int NC>
-__device__ __forceinline__ void wave_topk(const float* logits, const float* sel_bias, int E,
-                                          int k, int router, int norm_topk, float route_scale,
-                                          int* ids_out, float* w_out) {
+__device__ __forceinline__ void wave_topk_regs(float (&lg)[NC], const float* sel_bias, int E,
+                                               int k, int router, int norm_topk,
+                                               float route_scale, int* ids_out, float* w_out) {
   const int lane = threadIdx.x & 63;
   uint32_t key[NC];
-  float lg[NC];
   float sb[NC];
-  // all loads issued before any use (clamped indices, masked afterwards)
-#pragma unroll
-  for (int i = 0; i < NC; ++i) lg[i] = logits[min(lane + 64 * i, E - 1)];
   if (sel_bias) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) sb[i] = sel_bias[min(lane + 64 * i, E - 1)];
@@ -580,6 +578,18 @@ __device__ __forceinline__ void wave_topk(const float* logits, const float* sel_
     ids_out[lane] = my_id;
     w_out[lane] = w * route_scale;
   }
+}
+
+template <int NC>
+__device__ __forceinline__ void wave_topk(const float* logits, const float* sel_bias, int E,
+                                          int k, int router, int norm_topk, float route_scale,
+                                          int* ids_out, float* w_out) {
+  const int lane = threadIdx.x & 63;
+  float lg[NC];
+  // all loads issued before any use (clamped indices, masked afterwards)
+#pragma unroll
+  for (int i = 0; i < NC; ++i) lg[i] = logits[min(lane + 64 * i, E - 1)];
+  wave_topk_regs<NC>(lg, sel_bias, E, k, router, norm_topk, route_scale, ids_out, w_out);
 }
 
 }  // namespace dev

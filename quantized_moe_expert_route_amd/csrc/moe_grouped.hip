@@ -1,0 +1,650 @@
+// Expert-grouped HIP kernels of the routed-expert MoE FFN layer for gfx950,
+// for chunks of several tokens (verify and prefill chunks) with K-quant experts.
+//
+// Each selected expert's weights are streamed once per 16-token tile instead of
+// once per (token, slot) pair:
+//   k_router_mfma   router GEMM [T, H] x [H, E] on fp64 MFMA (16x16x4), split
+//                   over K slices into fp64 partials; extra waves quantize x
+//   k_topk_sum      per token: the K-slice partials summed in slice order, one
+//                   fp32 rounding, then top-k and routing weights
+//   k_bucket        one workgroup: stable counting sort of the (token, slot)
+//                   pairs by expert; tiles of <= 16 pairs with the expert's
+//                   resolved pointers; presence flags
+//   k_gu_grouped    per (tile, 64-row block): gate and up rows against the
+//                   tile's q8(x) rows, one int8 MFMA (16x16x32) per weight
+//                   sub-block, integer sub-block scaling, fp32 block rescale;
+//                   SwiGLU -> h
+//   k_hquant        q8 of h per present pair (blocks of 256)
+//   k_down_grouped  per (tile, 64-row block of H): down rows against q8(h);
+//                   bias and routing weight applied -> per-pair rows
+//   k_combine       y[t] = per-pair rows summed in slot order, shared expert last
+// The integer block partials are the same ones the decode path computes; only
+// the fp32 order of the block rescale differs. No float atomics.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+using namespace dev;
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef double v4d __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename K, typename... Args>
+hipError_t launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Ev ev,
+                  Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), s, ev.start, ev.stop,
+                          0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ long pk64(uint32_t lo, uint32_t hi) {
+  return static_cast<long>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ uint2 ld8(const void* p) {
+  const u32x2 v = *gp<u32x2>(p);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint2 ld_nt8(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(gp<u32x2>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float4 ldg_f4(const void* p) {
+  const v4f v = *gp<v4f>(p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ v4i mma_i8(long a, long b) {
+  const v4i z = {0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, z, 0, 0, 0);
+}
+
+// Lane roles in a 16x16 MFMA tile (wave64): g = lane / 16, c = lane % 16.
+// int8 16x16x32 and fp32 16x16x4: A[row c][k in lane group g], B[k in g][col c],
+// C[row 4g + i][col c] for i = 0..3. Rows are tokens, columns weight rows.
+// fp64 16x16x4: A[row c][k g], B[k g][col c], C[row g + 4i][col c].
+
+// q8 activations of one 256-element super-block as one lane feeds the MFMAs:
+// q[m] holds elements 32m + 8g .. 32m + 8g + 7 of the lane's A-row token
+// (group m is Q4_K sub-block m and Q6_K sub-blocks 2m, 2m + 1).
+struct ActSB {
+  uint2 q[8];
+  uint32_t bs[2];  // two int16 16-element sums = sub-block 4h + g's sum (Q4_K)
+  float dA;        // block scale of the A-row token
+  float dC[4];     // block scales of the C-row tokens 4g + i
+};
+
+struct ActRows {
+  const int8_t* qa;
+  const int16_t* bsa;
+  const float* da;
+  const float* dc[4];
+};
+
+template <bool BS>
+__device__ __forceinline__ void load_act(ActSB& r, const ActRows& x, int b, int g) {
+  const int8_t* p = x.qa + 256 * b + 8 * g;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) r.q[m] = ld8(p + 32 * m);
+  if constexpr (BS) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r.bs[h] = *gp<uint32_t>(x.bsa + 16 * b + 2 * (4 * h + g));
+  }
+  r.dA = *gp<float>(x.da + b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.dC[i] = *gp<float>(x.dc[i] + b);
+}
+
+// ---- Q4_K: sub-block j of 32, w = d sc_j q - dmin m_j.
+struct WQ4K {
+  uint4 hdr;
+  uint2 q[4];  // qs bytes 32c + 8g .. + 7: low nibbles sub-block 2c, high 2c + 1
+  static constexpr bool kBS = true;
+  __device__ __forceinline__ void load(const uint8_t* blk, int g) {
+    hdr = ld_nt16(blk);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q[c] = ld_nt8(blk + 16 + 32 * c + 8 * g);
+  }
+  // acc += dC * d * S1 (integer sub-block sums scaled by sc_j);
+  // mn += dA * bsum_j * dmin * m_j (min term, fp32 MFMA over the sub-blocks).
+  __device__ __forceinline__ void mma(const ActSB& x, int g, v4f& acc, v4f& mn) const {
+    const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;
+    const uint32_t sc03 = s0 & 0x3F3F3F3Fu, m03 = s1 & 0x3F3F3F3Fu;
+    const uint32_t sc47 = (s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u);
+    const uint32_t m47 = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
+    v4i S = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t lx = q[c].x, ly = q[c].y;
+      const v4i clo = mma_i8(pk64(x.q[2 * c].x, x.q[2 * c].y),
+                             pk64(lx & 0x0F0F0F0Fu, ly & 0x0F0F0F0Fu));
+      const v4i chi = mma_i8(pk64(x.q[2 * c + 1].x, x.q[2 * c + 1].y),
+                             pk64((lx >> 4) & 0x0F0F0F0Fu, (ly >> 4) & 0x0F0F0F0Fu));
+      const uint32_t scw = c < 2 ? sc03 : sc47;
+      const int sl = (scw >> (16 * (c & 1))) & 0xFF, sh = (scw >> (16 * (c & 1) + 8)) & 0xFF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[i] += sl * clo[i] + sh * chi[i];
+    }
+    const float d = half_bits_to_f32(hdr.x & 0xFFFF), dmin = half_bits_to_f32(hdr.x >> 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t mw = h ? m47 : m03;
+      const float mj = static_cast<float>((mw >> (8 * g)) & 0xFF);
+      const int bsum = static_cast<int>(static_cast<int16_t>(x.bs[h] & 0xFFFF)) +
+                       static_cast<int>(static_cast<int16_t>(x.bs[h] >> 16));
+      mn = __builtin_amdgcn_mfma_f32_16x16x4f32(x.dA * static_cast<float>(bsum), dmin * mj, mn,
+                                                0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += (x.dC[i] * d) * static_cast<float>(S[i]);
+  }
+};
+
+// ---- Q6_K: sub-block s of 16, w = d sc_s (q - 32), q - 32 fits int8.
+struct WQ6K {
+  uint2 l0[2], l1[2], qh[2], sc[2];
+  uint32_t dbits;
+  static constexpr bool kBS = false;
+  __device__ __forceinline__ void load(const uint8_t* blk, int g) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      l0[h] = load8_unaligned(blk + 64 * h + 8 * g);
+      l1[h] = load8_unaligned(blk + 64 * h + 32 + 8 * g);
+      qh[h] = load8_unaligned(blk + 128 + 32 * h + 8 * g);
+    }
+    sc[0] = load8_unaligned(blk + 192);
+    sc[1] = load8_unaligned(blk + 200);
+    dbits = ld_nt2(blk + 208);
+  }
+  // Group m = 4h + qq covers sub-blocks 2m (lane groups 0, 1) and 2m + 1
+  // (groups 2, 3): two MFMAs, each with the other half of B zeroed.
+  __device__ __forceinline__ void mma(const ActSB& x, int g, v4f& acc, v4f&) const {
+    v4i S = {0, 0, 0, 0};
+    const bool first = g < 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int m = 4 * h + qq;
+        const uint2 lo = (qq & 1) ? l1[h] : l0[h];
+        const int lsh = (qq >> 1) * 4, hsh = 2 * qq;
+        uint32_t w0 = ((lo.x >> lsh) & 0x0F0F0F0Fu) | (((qh[h].x >> hsh) & 0x03030303u) << 4);
+        uint32_t w1 = ((lo.y >> lsh) & 0x0F0F0F0Fu) | (((qh[h].y >> hsh) & 0x03030303u) << 4);
+        // bytes 0..63 -> q - 32 as int8, per byte without carries between bytes
+        w0 = ((w0 | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+        w1 = ((w1 | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+        const long av = pk64(x.q[m].x, x.q[m].y);
+        const long wv = pk64(w0, w1);
+        const v4i ca = mma_i8(av, first ? wv : 0L);
+        const v4i cb = mma_i8(av, first ? 0L : wv);
+        const uint2 sv = m < 4 ? sc[0] : sc[1];
+        const uint32_t sw = (m & 3) < 2 ? sv.x : sv.y;
+        const int sh = 16 * (m & 1);
+        const int sa = static_cast<int8_t>((sw >> sh) & 0xFF);
+        const int sb = static_cast<int8_t>((sw >> (sh + 8)) & 0xFF);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[i] += sa * ca[i] + sb * cb[i];
+      }
+    }
+    const float d = half_bits_to_f32(dbits);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += (x.dC[i] * d) * static_cast<float>(S[i]);
+  }
+};
+
+template <int FMT> struct WOf;
+template <> struct WOf<FMT_Q4_K> { using T = WQ4K; };
+template <> struct WOf<FMT_Q6_K> { using T = WQ6K; };
+
+// Work item of a grouped launch: items (tile, row block) are numbered tile-major;
+// each XCD (workgroup id % 8) takes a contiguous range, so the row blocks of a
+// tile (same activations) and the tiles of an expert (same weights) share an L2.
+// Returns -1 for workgroups beyond the chunk's items.
+__device__ __forceinline__ int grouped_item(int n_items) {
+  const int bid = blockIdx.x, xcd = bid & 7, j = bid >> 3;
+  const int chunk = (n_items + 7) >> 3;
+  const int item = xcd * chunk + j;
+  return (j < chunk && item < n_items) ? item : -1;
+}
+
+// Streams nb super-blocks of NM weight rows (one per matrix) against the tile's
+// activations, two super-blocks in flight.
+template <class W, int NM>
+__device__ __forceinline__ void stream_rows(const uint8_t* const (&wrow)[NM], const ActRows& x,
+                                            int nb, int g, v4f (&acc)[NM], v4f (&mn)[NM]) {
+  constexpr int BB = W::kBS ? 144 : 210;
+  ActSB xa, xb;
+  W wa[NM], wb[NM];
+  load_act<W::kBS>(xa, x, 0, g);
+#pragma unroll
+  for (int j = 0; j < NM; ++j) wa[j].load(wrow[j], g);
+  for (int b = 0; b < nb; b += 2) {
+    const int b1 = min(b + 1, nb - 1);
+    load_act<W::kBS>(xb, x, b1, g);
+#pragma unroll
+    for (int j = 0; j < NM; ++j) wb[j].load(wrow[j] + static_cast<size_t>(b1) * BB, g);
+#pragma unroll
+    for (int j = 0; j < NM; ++j) wa[j].mma(xa, g, acc[j], mn[j]);
+    const int b2 = min(b + 2, nb - 1);
+    load_act<W::kBS>(xa, x, b2, g);
+#pragma unroll
+    for (int j = 0; j < NM; ++j) wa[j].load(wrow[j] + static_cast<size_t>(b2) * BB, g);
+    if (b + 1 < nb) {
+#pragma unroll
+      for (int j = 0; j < NM; ++j) wb[j].mma(xb, g, acc[j], mn[j]);
+    }
+  }
+}
+
+// ================================================================== kernels
+
+// Router logits for many tokens: fp32 inputs, fp64 MFMA products and sums (the
+// products of fp32 values are exact in fp64). grid nwg_r + quant workgroups,
+// block 256. Router wave w: K slice w % KS of (token tile, expert tile) w / KS;
+// column E of the expert tiles is the shared-expert gate vector when present.
+// Quant waves: q8 of one 256-element piece of x.
+__global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS, int L, int n_et,
+                                                     int n_work, int nwg_r) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (static_cast<int>(blockIdx.x) >= nwg_r) {
+    if (!quant) return;
+    const int job = (blockIdx.x - nwg_r) * 4 + wave;
+    const int pieces = a.H >> 8;
+    const int t = job / pieces, pc = job - t * pieces;
+    if (t >= a.T) return;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = load_x(a.x, a.x_dtype, static_cast<size_t>(t) * a.H + pc * 256 + 4 * lane + i);
+    const size_t base = static_cast<size_t>(t) * a.H + pc * 256;
+    quant_wave<256>(v, true, lane, a.xqs + base, a.xd + base / 256, a.xbs + base / 16);
+    return;
+  }
+  const int wv = blockIdx.x * 4 + wave;
+  if (wv >= n_work) return;
+  const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
+  const int ks = wv % KS, r = wv / KS, et = r % n_et, tt = r / n_et;
+  const int g = lane >> 4, c = lane & 15;
+  const int t = min(tt * 16 + c, a.T - 1);
+  const int e = min(et * 16 + c, E1 - 1);
+  const float* wr = e < a.E ? a.w_router + static_cast<size_t>(e) * a.H : a.sh_gate_vec;
+  const int k0 = ks * L;
+  const int nst = (min(a.H, k0 + L) - k0) >> 4;  // steps of 16 (4 per lane group)
+  v4d acc = {0.0, 0.0, 0.0, 0.0};
+  auto step = [&](const float4& xv, const float4& wv4) {
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(xv.x),
+                                               static_cast<double>(wv4.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(xv.y),
+                                               static_cast<double>(wv4.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(xv.z),
+                                               static_cast<double>(wv4.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(xv.w),
+                                               static_cast<double>(wv4.w), acc, 0, 0, 0);
+  };
+  auto load_xv = [&](int kk) -> float4 {
+    const size_t o = static_cast<size_t>(t) * a.H + kk;
+    if (a.x_dtype == 0) return ldg_f4(static_cast<const float*>(a.x) + o);
+    const uint2 bb = ld8(static_cast<const uint16_t*>(a.x) + o);
+    return make_float4(bf16_bits_to_f32(bb.x & 0xFFFF), bf16_bits_to_f32(bb.x >> 16),
+                       bf16_bits_to_f32(bb.y & 0xFFFF), bf16_bits_to_f32(bb.y >> 16));
+  };
+  // MFMA step n, lane group g: k = k0 + 16 n + 4 g + s for s = 0..3 (the same
+  // k for A and B, so the k order is only a reordering of the sum)
+  int n = 0;
+  for (; n + 4 <= nst; n += 4) {
+    float4 xv[4], wv4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = k0 + 16 * (n + u) + 4 * g;
+      xv[u] = load_xv(kk);
+      wv4[u] = ldg_f4(wr + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) step(xv[u], wv4[u]);
+  }
+  for (; n < nst; ++n) {
+    const int kk = k0 + 16 * n + 4 * g;
+    step(load_xv(kk), ldg_f4(wr + kk));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = tt * 16 + g + 4 * i, ex = et * 16 + c;
+    if (tok < a.T && ex < E1)
+      a.rpart[(static_cast<size_t>(ks) * a.T + tok) * E1 + ex] = acc[i];
+  }
+}
+
+// Per token (one wave): logit = fp32(sum of the K-slice partials in slice order),
+// then top-k and weights; the shared gate sigmoid from column E.
+template <int NC>
+__global__ __launch_bounds__(256) void k_topk_sum(KArgs a, int KS) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int lane = threadIdx.x & 63;
+  const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
+  const double* rp = a.rpart + static_cast<size_t>(t) * E1;
+  const size_t kstride = static_cast<size_t>(a.T) * E1;
+  double s[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) s[i] = 0.0;
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) s[i] += rp[ks * kstride + min(lane + 64 * i, a.E - 1)];
+  }
+  float lg[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    lg[i] = static_cast<float>(s[i]);
+    if (lane + 64 * i < a.E) a.logits[static_cast<size_t>(t) * a.E + lane + 64 * i] = lg[i];
+  }
+  if (a.sh_gate_vec && lane == 0) {
+    double sg = 0.0;
+    for (int ks = 0; ks < KS; ++ks) sg += rp[ks * kstride + a.E];
+    a.shw[t] = static_cast<float>(1.0 / (1.0 + exp(-sg)));
+  }
+  wave_topk_regs<NC>(lg, a.sel_bias, a.E, a.k, a.router, a.norm_topk, a.route_scale,
+                     a.ids + t * a.k, a.w + t * a.k);
+}
+
+// Stable counting sort of the pairs by expert (one workgroup of 1024 threads).
+// Pair p = t * k + slot is present when its id is in range and the expert's
+// gate pointer is not NULL; the shared expert is pseudo-expert E with pairs
+// T * k + t. Output: plist sorted by (expert, pair), tiles of <= 16 consecutive
+// entries of one expert, the tile count in counters[0].
+__global__ __launch_bounds__(1024) void k_bucket(KArgs a) {
+  __shared__ int cnt[MOE_MAX_EXPERTS + 1];
+  __shared__ int off[MOE_MAX_EXPERTS + 2];
+  __shared__ int toff[MOE_MAX_EXPERTS + 2];
+  __shared__ int cur[MOE_MAX_EXPERTS + 1];
+  const int tid = threadIdx.x, E = a.E, NE = E + 1, Tk = a.T * a.k;
+  for (int i = tid; i < NE; i += 1024) {
+    cnt[i] = 0;
+    cur[i] = 0;
+  }
+  __syncthreads();
+  for (int p = tid; p < Tk; p += 1024) {
+    const int e = a.ids[p];
+    const bool ok = static_cast<unsigned>(e) < static_cast<unsigned>(E) && a.gate[e] != nullptr;
+    a.present[p] = ok;
+    if (ok) atomicAdd(&cnt[e], 1);
+  }
+  if (a.has_shared)
+    for (int t = tid; t < a.T; t += 1024) a.present[Tk + t] = 1;
+  if (tid == 0) cnt[E] = a.has_shared ? a.T : 0;
+  __syncthreads();
+  if (tid < 64) {  // exclusive scans of pair counts and tile counts (wave 0)
+    int cc = 0, ct = 0;
+    for (int base = 0; base < NE; base += 64) {
+      const int i = base + tid;
+      const int c = i < NE ? cnt[i] : 0, nt = (c + 15) >> 4;
+      int ic = c, it = nt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int oc = __shfl_up(ic, d), ot = __shfl_up(it, d);
+        if (tid >= d) {
+          ic += oc;
+          it += ot;
+        }
+      }
+      if (i < NE) {
+        off[i] = cc + ic - c;
+        toff[i] = ct + it - nt;
+      }
+      cc += __shfl(ic, 63);
+      ct += __shfl(it, 63);
+    }
+    if (tid == 0) {
+      off[NE] = cc;
+      toff[NE] = ct;
+      a.counters[0] = static_cast<uint32_t>(ct);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < NE; e += 1024) {
+    const int c = cnt[e];
+    if (c == 0) continue;
+    GTile tl;
+    tl.e = e;
+    tl.pad = 0;
+    if (e < E) {
+      tl.gate = static_cast<const uint8_t*>(a.gate[e]);
+      tl.up = static_cast<const uint8_t*>(a.up[e]);
+      tl.down = static_cast<const uint8_t*>(a.down[e]);
+      tl.b_gate = a.b_gate ? a.b_gate[e] : nullptr;
+      tl.b_up = a.b_up ? a.b_up[e] : nullptr;
+      tl.b_down = a.b_down ? a.b_down[e] : nullptr;
+    } else {
+      tl.gate = static_cast<const uint8_t*>(a.sh_gate);
+      tl.up = static_cast<const uint8_t*>(a.sh_up);
+      tl.down = static_cast<const uint8_t*>(a.sh_down);
+      tl.b_gate = tl.b_up = tl.b_down = nullptr;
+    }
+    for (int j = 0; 16 * j < c; ++j) {
+      tl.start = off[e] + 16 * j;
+      tl.cnt = min(16, c - 16 * j);
+      a.tiles[toff[e] + j] = tl;
+    }
+  }
+  for (int p = tid; p < Tk; p += 1024) {
+    if (a.present[p]) {
+      const int e = a.ids[p];
+      a.pair_tmp[off[e] + atomicAdd(&cur[e], 1)] = p;
+    }
+  }
+  if (a.has_shared)
+    for (int t = tid; t < a.T; t += 1024) a.plist[off[E] + t] = make_int2(Tk + t, t);
+  __threadfence_block();
+  __syncthreads();
+  // sorted position = bucket start + number of smaller pair ids in the bucket
+  const int nr = off[E];
+  for (int i = tid; i < nr; i += 1024) {
+    const int p = a.pair_tmp[i];
+    const int e = a.ids[p];
+    const int b0 = off[e], n = cnt[e];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) rank += a.pair_tmp[b0 + j] < p;
+    a.plist[b0 + rank] = make_int2(p, p / a.k);
+  }
+}
+
+// Gate/up rows of one tile: grid 8 * ceil(max items / 8), block 256. Item =
+// (tile, block of 64 rows of F); wave w takes rows 16 w .. 16 w + 15 of the block.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_gu_grouped(KArgs a, Div dRB) {
+  using W = typename WOf<FMT>::T;
+  const int n_tiles = static_cast<int>(*gp<uint32_t>(a.counters));
+  const int item = grouped_item(n_tiles * static_cast<int>(dRB.d));
+  if (item < 0) return;
+  const uint32_t tile = dRB.div(item);
+  const int rb = dRB.mod(item, tile);
+  const GTile tl = a.tiles[tile];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  const int cnt = tl.cnt;
+  const int2 pA = a.plist[tl.start + min(c, cnt - 1)];
+  int2 pC[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pC[i] = a.plist[tl.start + min(4 * g + i, cnt - 1)];
+  const int H = a.H, nb = H >> 8;
+  ActRows x;
+  x.qa = a.xqs + static_cast<size_t>(pA.y) * H;
+  x.bsa = a.xbs + static_cast<size_t>(pA.y) * (H >> 4);
+  x.da = a.xd + static_cast<size_t>(pA.y) * nb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x.dc[i] = a.xd + static_cast<size_t>(pC[i].y) * nb;
+  const int row = rb * 64 + wave * 16 + c;
+  const uint8_t* const wrow[2] = {tl.gate + static_cast<size_t>(row) * a.stride_gate,
+                                  tl.up + static_cast<size_t>(row) * a.stride_up};
+  v4f acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  v4f mn[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  stream_rows<W, 2>(wrow, x, nb, g, acc, mn);
+  const float bg = tl.b_gate ? tl.b_gate[row] : 0.0f;
+  const float bu = tl.b_up ? tl.b_up[row] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * g + i < cnt) {
+      const float gv = acc[0][i] - mn[0][i] + bg;
+      const float uv = acc[1][i] - mn[1][i] + bu;
+      a.h[static_cast<size_t>(pC[i].x) * a.F + row] =
+          act_fn(a.act, a.act_alpha, a.act_limit, gv, uv);
+    }
+  }
+}
+
+// q8 of h (blocks of 256, fp32 recipe) per present pair: one wave per
+// (pair, 256-element piece). grid ceil(P * F / 256 / 4), block 256.
+__global__ __launch_bounds__(256) void k_hquant(KArgs a, int P) {
+  const int lane = threadIdx.x & 63;
+  const int job = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int pieces = a.F >> 8;
+  const int p = job / pieces, pc = job - p * pieces;
+  if (p >= P || !a.present[p]) return;
+  const float4 hv = ldg_f4(a.h + static_cast<size_t>(p) * a.F + pc * 256 + 4 * lane);
+  const float v[4] = {hv.x, hv.y, hv.z, hv.w};
+  quant_wave<256>(v, true, lane, a.hqs + static_cast<size_t>(p) * a.F + pc * 256,
+                  a.hd + static_cast<size_t>(p) * (a.F >> 8) + pc,
+                  a.hbs + static_cast<size_t>(p) * (a.F >> 4) + pc * 16);
+}
+
+// Down rows of one tile: item = (tile, block of 64 rows of H). Writes
+// part[p] = w_p * (W_d q8(h_p) + b_d) for the tile's pairs.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_down_grouped(KArgs a, Div dRB) {
+  using W = typename WOf<FMT>::T;
+  const int n_tiles = static_cast<int>(*gp<uint32_t>(a.counters));
+  const int item = grouped_item(n_tiles * static_cast<int>(dRB.d));
+  if (item < 0) return;
+  const uint32_t tile = dRB.div(item);
+  const int rb = dRB.mod(item, tile);
+  const GTile tl = a.tiles[tile];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  const int cnt = tl.cnt;
+  const int2 pA = a.plist[tl.start + min(c, cnt - 1)];
+  int2 pC[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pC[i] = a.plist[tl.start + min(4 * g + i, cnt - 1)];
+  const int F = a.F, nb = F >> 8;
+  ActRows x;
+  x.qa = a.hqs + static_cast<size_t>(pA.x) * F;
+  x.bsa = a.hbs + static_cast<size_t>(pA.x) * (F >> 4);
+  x.da = a.hd + static_cast<size_t>(pA.x) * nb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x.dc[i] = a.hd + static_cast<size_t>(pC[i].x) * nb;
+  const int row = rb * 64 + wave * 16 + c;
+  const uint8_t* const wrow[1] = {tl.down + static_cast<size_t>(row) * a.stride_down};
+  v4f acc[1] = {{0, 0, 0, 0}};
+  v4f mn[1] = {{0, 0, 0, 0}};
+  stream_rows<W, 1>(wrow, x, nb, g, acc, mn);
+  const float bd = tl.b_down ? tl.b_down[row] : 0.0f;
+  const int Tk = a.T * a.k;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * g + i < cnt) {
+      const int p = pC[i].x;
+      const float wp = p < Tk ? a.w[p] : (a.sh_gate_vec ? a.shw[p - Tk] : 1.0f);
+      a.part[static_cast<size_t>(p) * a.H + row] = wp * (acc[0][i] - mn[0][i] + bd);
+    }
+  }
+}
+
+// y[t] = sum of the token's present pair rows in slot order, then the shared
+// expert's. grid (ceil(H / 1024), T), block 256, 4 outputs per thread.
+__global__ __launch_bounds__(256) void k_combine(KArgs a) {
+  const int t = blockIdx.y, h0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (h0 >= a.H) return;
+  float r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;
+  for (int s = 0; s < a.k; ++s) {
+    const int p = t * a.k + s;
+    if (a.present[p]) {
+      const float4 v = ldg_f4(a.part + static_cast<size_t>(p) * a.H + h0);
+      r0 += v.x; r1 += v.y; r2 += v.z; r3 += v.w;
+    }
+  }
+  if (a.has_shared) {
+    const float4 v = ldg_f4(a.part + static_cast<size_t>(a.T * a.k + t) * a.H + h0);
+    r0 += v.x; r1 += v.y; r2 += v.z; r3 += v.w;
+  }
+  *reinterpret_cast<float4*>(a.y + static_cast<size_t>(t) * a.H + h0) = make_float4(r0, r1, r2, r3);
+}
+
+int grouped_grid(int n_items_max) { return 8 * ((n_items_max + 7) / 8); }
+
+}  // namespace
+
+RouterSplit router_split(int T, int E, int H) {
+  const int E1 = E + 1;
+  const int tiles = ((T + 15) / 16) * ((E1 + 15) / 16);
+  int ks = (2048 + tiles - 1) / tiles;
+  if (ks > 16) ks = 16;
+  if (ks < 1) ks = 1;
+  const int steps = (H + 15) / 16;
+  if (ks > steps) ks = steps;
+  const int len = 16 * ((steps + ks - 1) / ks);
+  return RouterSplit{(H + len - 1) / len, len};
+}
+
+int max_tiles(int T, int k, int E, int has_shared) {
+  const int Tk = T * k;
+  return (E < Tk ? E : Tk) + Tk / 16 + (has_shared ? (T + 15) / 16 : 0);
+}
+
+hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hipStream_t s,
+                                 Ev ev) {
+  const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
+  const int n_et = (E1 + 15) / 16, n_tt = (a.T + 15) / 16;
+  const int n_work = n_tt * n_et * rs.ks;
+  const int nwg_r = (n_work + 3) / 4;
+  const int nq = quant ? (a.T * (a.H / 256) + 3) / 4 : 0;
+  return launch(k_router_mfma, dim3(nwg_r + nq), 256, 0, s, ev, a, quant ? 1 : 0, rs.ks, rs.len,
+                n_et, n_work, nwg_r);
+}
+
+hipError_t launch_topk_sum(const KArgs& a, RouterSplit rs, hipStream_t s, Ev ev) {
+  const dim3 grid((a.T + 3) / 4);
+  if (a.E <= 256) return launch(k_topk_sum<4>, grid, 256, 0, s, ev, a, rs.ks);
+  if (a.E <= 512) return launch(k_topk_sum<8>, grid, 256, 0, s, ev, a, rs.ks);
+  return launch(k_topk_sum<16>, grid, 256, 0, s, ev, a, rs.ks);
+}
+
+hipError_t launch_bucket(const KArgs& a, hipStream_t s, Ev ev) {
+  return launch(k_bucket, dim3(1), 1024, 0, s, ev, a);
+}
+
+hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s, Ev ev) {
+  const int RB = a.F / 64;
+  const dim3 grid(grouped_grid(max_tiles(a.T, a.k, a.E, a.has_shared) * RB));
+  const Div d = Div::make(RB);
+  if (a.fmt_gu == FMT_Q4_K) return launch(k_gu_grouped<FMT_Q4_K>, grid, 256, 0, s, ev, a, d);
+  return launch(k_gu_grouped<FMT_Q6_K>, grid, 256, 0, s, ev, a, d);
+}
+
+hipError_t launch_hquant(const KArgs& a, hipStream_t s, Ev ev) {
+  const int P = a.T * a.k + a.T * a.has_shared;
+  const int jobs = P * (a.F / 256);
+  return launch(k_hquant, dim3((jobs + 3) / 4), 256, 0, s, ev, a, P);
+}
+
+hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev) {
+  const int RB = a.H / 64;
+  const dim3 grid(grouped_grid(max_tiles(a.T, a.k, a.E, a.has_shared) * RB));
+  const Div d = Div::make(RB);
+  if (a.fmt_d == FMT_Q4_K) return launch(k_down_grouped<FMT_Q4_K>, grid, 256, 0, s, ev, a, d);
+  return launch(k_down_grouped<FMT_Q6_K>, grid, 256, 0, s, ev, a, d);
+}
+
+hipError_t launch_combine(const KArgs& a, hipStream_t s, Ev ev) {
+  return launch(k_combine, dim3((a.H + 1023) / 1024, a.T), 256, 0, s, ev, a);
+}
+
+}  // namespace moe

@@ -32,6 +32,21 @@ struct Div {
   }
 };
 
+// One token tile of the expert-grouped path: up to 16 (token, slot) pairs routed
+// to one expert, with that expert's resolved pointers. Written by k_bucket.
+struct GTile {
+  int32_t e;      // expert id (E: the shared expert)
+  int32_t start;  // first entry in the sorted pair list
+  int32_t cnt;    // pairs in the tile, 1..16
+  int32_t pad;
+  const uint8_t* gate;
+  const uint8_t* up;
+  const uint8_t* down;
+  const float* b_gate;  // nullptr: no biases
+  const float* b_up;
+  const float* b_down;
+};
+
 // Down-projection pointers of one (token, slot) pair, resolved by k_gateup.
 struct SlotRef {
   const uint8_t* down;  // nullptr: expert not present (slot contributes nothing)
@@ -75,20 +90,21 @@ struct KArgs {
   float* y;         // [T, H]
   uint32_t* counters;  // one word per (token, slot) pair, reset by the router kernel
   // grouped path
-  int32_t* counts;     // [E + 1]
-  int32_t* offsets;    // [E + 2]
-  int32_t* pair_list;  // [T * k] pair ids p = t * k + slot, grouped by expert
-  int32_t* active;     // [E + 1] active experts in increasing order (+ shared)
+  double* rpart;       // [KS, T, E1] router partial sums (E1 = E + shared gate row)
+  int32_t* pair_tmp;   // [P] pairs bucketed by expert, unordered within an expert
+  int2* plist;         // [P] (pair, token), sorted by (expert, pair); shared expert last
+  int32_t* present;    // [P] 1 if the pair's expert is present
+  GTile* tiles;        // [max tiles]
   int8_t* hqs;         // [P, F]
   float* hd;           // [P, F / 32]
   int16_t* hbs;        // [P, F / 16]
-  float* part;         // [P, H]
+  float* part;         // [P, H] routing-weighted expert outputs per pair
 };
 
 // Workspace layout (byte offsets from the base, each 256-aligned).
 struct WsLayout {
-  size_t counters, xqs, xd, xbs, logits, ids, w, shw, slots, h, counts, offsets, pair_list, active,
-      hqs, hd, hbs, part, total;
+  size_t counters, xqs, xd, xbs, logits, ids, w, shw, slots, h, hqs, hd, hbs, rpart, pair_tmp,
+      plist, present, tiles, part, total;
 };
 WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped);
 
@@ -99,7 +115,14 @@ constexpr size_t kMaxLds = 64 * 1024;
 bool gemv_fits(const KArgs& a);
 
 // Which expert-FFN path a chunk of T tokens takes (fixed rule, see moe_api.cpp).
-bool use_grouped(int T, int k);
+bool use_grouped(int T, int fmt_gate, int fmt_down);
+
+// Router split of the grouped path: K slices of `len` elements (multiple of 16).
+struct RouterSplit { int ks, len; };
+RouterSplit router_split(int T, int E1, int H);
+
+// Upper bound on the tiles k_bucket can emit.
+int max_tiles(int T, int k, int E, int has_shared);
 
 // Optional per-kernel timing events, recorded by the dispatch itself
 // (hipExtLaunchKernel start/stop), i.e. the kernel's execution window.
@@ -118,6 +141,14 @@ hipError_t launch_router(const KArgs& a, bool quant, int n_clear, hipStream_t s,
 hipError_t launch_topk(const KArgs& a, hipStream_t s);
 hipError_t launch_gateup(const KArgs& a, bool routing_given, hipStream_t s, Ev ev);
 hipError_t launch_down(const KArgs& a, hipStream_t s, Ev ev);
+// grouped path
+hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hipStream_t s, Ev ev);
+hipError_t launch_topk_sum(const KArgs& a, RouterSplit rs, hipStream_t s, Ev ev);
+hipError_t launch_bucket(const KArgs& a, hipStream_t s, Ev ev);
+hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s, Ev ev);
+hipError_t launch_hquant(const KArgs& a, hipStream_t s, Ev ev);
+hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev);
+hipError_t launch_combine(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_t stride,
                              const int8_t* qs, const float* d, const int16_t* bs,
                              int32_t* out, hipStream_t s);

@@ -168,8 +168,23 @@ def test_block_dots_validation():
             M.moe_test_block_dots(*a, FAKE, stream=0)
 
 
-def test_stage_names():
+def test_stage_names_and_path_rule():
+    """Dispatch rule: chunks of <= 4 tokens, and any layer with an MXFP4 matrix,
+    take the per-pair GEMV path (3 kernels); larger K-quant chunks the grouped
+    path (7 kernels)."""
     d = good_desc()
-    assert M.moe_layer_stage_count(d, 1) == 3
-    assert [M.moe_layer_stage_name(d, 1, i) for i in range(3)] == ["router", "gateup", "down"]
+    for T in (1, 4):
+        assert M.moe_layer_stage_count(d, T) == 3
+        assert [M.moe_layer_stage_name(d, T, i) for i in range(3)] == ["router", "gateup", "down"]
+    for T in (5, 16, 256, 2048):
+        assert M.moe_layer_stage_count(d, T) == 7
+    assert [M.moe_layer_stage_name(d, 16, i) for i in range(7)] == [
+        "router", "topk", "bucket", "gateup", "hquant", "down", "combine"]
     assert M.moe_layer_stage_name(d, 1, 9) is None
+    assert M.moe_layer_stage_count(d, 0) == 0
+    mx = good_desc(gen.CONFIGS["gpt-oss-20b"])
+    assert M.moe_layer_stage_count(mx, 16) == 3
+    q6 = good_desc(gen.CONFIGS["deepseek-v4-flash"])
+    assert M.moe_layer_stage_count(q6, 16) == 7
+    # the grouped workspace holds the per-pair rows: it grows with T * k * H
+    assert M.moe_workspace_size(d, 5) > M.moe_workspace_size(d, 4) + 5 * 9 * 2048 * 4

@@ -164,3 +164,24 @@ def test_full_size_decode_token(orc, genlib):
     yb, idb, _ = brute_layer(data, data.x[:1], dense=dense)
     assert np.array_equal(idb[0], r["ids"])
     assert _rel(r["y"], yb[0]) <= 1e-9
+
+
+def test_out_of_range_ids_contribute_nothing(orc, genlib):
+    """Given routing may carry ids outside [0, E) (a slot that is "not mine"):
+    such a slot adds nothing, exactly as a slot of weight 0 does, and equals the
+    brute-force sum over the remaining slots."""
+    cfg = SHRUNK["kimi-k2"].with_(shared=False)
+    data = gen.make_layer(cfg)
+    x, _ = gen.make_x(cfg, T=1)
+    L = oracle.Layer(data)
+    ids = np.arange(cfg.k, dtype=np.int32) * 2
+    w = np.linspace(0.5, 1.0, cfg.k).astype(np.float32)
+    for bad in (-1, cfg.E, 1 << 30):
+        ib = ids.copy()
+        ib[3] = bad
+        y_bad = L.expert_part(x[0], ib, w)
+        wz = w.copy()
+        wz[3] = 0.0
+        assert np.array_equal(y_bad, L.expert_part(x[0], ids, wz))
+    with pytest.raises(ValueError):
+        L.expert_part(x[0], ids[:3], w[:3])
