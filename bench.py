@@ -159,13 +159,17 @@ def main():
     uniq_mean = float(np.mean(uniq))
     sel_bytes = uniq_mean * cfg.expert_algo_bytes
     pairs = T * cfg.k + (T if cfg.shared else 0)
-    # algorithmic bytes per launch of the two expert kernels (every (token, slot)
-    # pair streams its expert's rows; NULL experts are not present here)
+    grouped = n_st == 7
+    # algorithmic bytes per launch of the two expert kernels: the per-pair path
+    # streams each (token, slot) pair's expert rows; the grouped path each
+    # selected expert's rows once (unique experts of the chunk + shared)
+    units = uniq_mean if grouped else pairs
     algo = {
-        "gateup": pairs * 2 * cfg.F * gen.row_bytes(cfg.fmt_gu, cfg.H),
-        "down": pairs * cfg.H * gen.row_bytes(cfg.fmt_d, cfg.F),
+        "gateup": units * 2 * cfg.F * gen.row_bytes(cfg.fmt_gu, cfg.H),
+        "down": units * cfg.H * gen.row_bytes(cfg.fmt_d, cfg.F),
     }
-    kern_names = {"gateup": "k_gateup", "down": "k_down"}
+    kern_names = ({"gateup": "k_gu_grouped", "down": "k_down_grouped"} if grouped
+                  else {"gateup": "k_gateup", "down": "k_down"})
     dom = max(("gateup", "down"), key=lambda k: stage_avg_us.get(k, 0.0))
     dom_us = stage_avg_us[dom]
     expert_us = stage_avg_us.get("gateup", 0) + stage_avg_us.get("down", 0)
@@ -179,7 +183,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "algo_bytes_per_launch": algo[dom],
+        "algo_bytes_per_launch": round(algo[dom]),
         "avg_launch_us": round(dom_us, 3),
     }
 
@@ -216,7 +220,7 @@ def main():
             "tokens_per_step": T,
             "layer_copies": copies,
             "x_pool": args.x_pool,
-            "path": "gemv" if T <= 4 else "grouped",
+            "path": "grouped" if grouped else "gemv",
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

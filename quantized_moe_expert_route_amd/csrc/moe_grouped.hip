@@ -10,12 +10,12 @@
 //   k_bucket        one workgroup: stable counting sort of the (token, slot)
 //                   pairs by expert; tiles of <= 16 pairs with the expert's
 //                   resolved pointers; presence flags
-//   k_gu_grouped    per (tile, 64-row block): gate and up rows against the
+//   k_gu_grouped    per (tile, row block): gate and up rows against the
 //                   tile's q8(x) rows, one int8 MFMA (16x16x32) per weight
 //                   sub-block, integer sub-block scaling, fp32 block rescale;
 //                   SwiGLU -> h
 //   k_hquant        q8 of h per present pair (blocks of 256)
-//   k_down_grouped  per (tile, 64-row block of H): down rows against q8(h);
+//   k_down_grouped  per (tile, row block of H): down rows against q8(h);
 //                   bias and routing weight applied -> per-pair rows
 //   k_combine       y[t] = per-pair rows summed in slot order, shared expert last
 // The integer block partials are the same ones the decode path computes; only
@@ -62,10 +62,27 @@ __device__ __forceinline__ uint2 ld_nt8(const void* p) {
   const u32x2 v = __builtin_nontemporal_load(gp<u32x2>(p));
   return make_uint2(v.x, v.y);
 }
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4 v = *gp<u32x4>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// 8 bytes at a 2-byte aligned address, cached (dword reads that each hold at
+// least one byte of [p, p + 8), as load8_unaligned).
+__device__ __forceinline__ uint2 ld8_a2(const uint8_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint8_t* w = reinterpret_cast<const uint8_t*>(a & ~static_cast<uintptr_t>(3));
+  const uint8_t* w_last = reinterpret_cast<const uint8_t*>((a + 7) & ~static_cast<uintptr_t>(3));
+  const uint32_t sh = static_cast<uint32_t>(a & 3);
+  const uint32_t w0 = *gp<uint32_t>(w), w1 = *gp<uint32_t>(w + 4), w2 = *gp<uint32_t>(w_last);
+  return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
+}
 __device__ __forceinline__ float4 ldg_f4(const void* p) {
   const v4f v = *gp<v4f>(p);
   return make_float4(v.x, v.y, v.z, v.w);
 }
+// c + a * b with 24-bit signed operands (full-rate v_mad_i32_i24); every
+// product here is a 6- or 8-bit scale times a sub-block dot of |.| < 2^17.
+__device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b) + c; }
 __device__ __forceinline__ v4i mma_i8(long a, long b) {
   const v4i z = {0, 0, 0, 0};
   return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, z, 0, 0, 0);
@@ -113,9 +130,9 @@ struct WQ4K {
   uint2 q[4];  // qs bytes 32c + 8g .. + 7: low nibbles sub-block 2c, high 2c + 1
   static constexpr bool kBS = true;
   __device__ __forceinline__ void load(const uint8_t* blk, int g) {
-    hdr = ld_nt16(blk);
+    hdr = ld16(blk);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) q[c] = ld_nt8(blk + 16 + 32 * c + 8 * g);
+    for (int c = 0; c < 4; ++c) q[c] = ld8(blk + 16 + 32 * c + 8 * g);
   }
   // acc += dC * d * S1 (integer sub-block sums scaled by sc_j);
   // mn += dA * bsum_j * dmin * m_j (min term, fp32 MFMA over the sub-blocks).
@@ -135,7 +152,7 @@ struct WQ4K {
       const uint32_t scw = c < 2 ? sc03 : sc47;
       const int sl = (scw >> (16 * (c & 1))) & 0xFF, sh = (scw >> (16 * (c & 1) + 8)) & 0xFF;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[i] += sl * clo[i] + sh * chi[i];
+      for (int i = 0; i < 4; ++i) S[i] = mad24(sh, chi[i], mad24(sl, clo[i], S[i]));
     }
     const float d = half_bits_to_f32(hdr.x & 0xFFFF), dmin = half_bits_to_f32(hdr.x >> 16);
 #pragma unroll
@@ -160,13 +177,13 @@ struct WQ6K {
   __device__ __forceinline__ void load(const uint8_t* blk, int g) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      l0[h] = load8_unaligned(blk + 64 * h + 8 * g);
-      l1[h] = load8_unaligned(blk + 64 * h + 32 + 8 * g);
-      qh[h] = load8_unaligned(blk + 128 + 32 * h + 8 * g);
+      l0[h] = ld8_a2(blk + 64 * h + 8 * g);
+      l1[h] = ld8_a2(blk + 64 * h + 32 + 8 * g);
+      qh[h] = ld8_a2(blk + 128 + 32 * h + 8 * g);
     }
-    sc[0] = load8_unaligned(blk + 192);
-    sc[1] = load8_unaligned(blk + 200);
-    dbits = ld_nt2(blk + 208);
+    sc[0] = ld8_a2(blk + 192);
+    sc[1] = ld8_a2(blk + 200);
+    dbits = *gp<uint16_t>(blk + 208);
   }
   // Group m = 4h + qq covers sub-blocks 2m (lane groups 0, 1) and 2m + 1
   // (groups 2, 3): two MFMAs, each with the other half of B zeroed.
@@ -195,7 +212,7 @@ struct WQ6K {
         const int sa = static_cast<int8_t>((sw >> sh) & 0xFF);
         const int sb = static_cast<int8_t>((sw >> (sh + 8)) & 0xFF);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[i] += sa * ca[i] + sb * cb[i];
+        for (int i = 0; i < 4; ++i) S[i] = mad24(sb, cb[i], mad24(sa, ca[i], S[i]));
       }
     }
     const float d = half_bits_to_f32(dbits);
@@ -220,31 +237,35 @@ __device__ __forceinline__ int grouped_item(int n_items) {
 }
 
 // Streams nb super-blocks of NM weight rows (one per matrix) against the tile's
-// activations, two super-blocks in flight.
+// activations. Two register stages: the loads of super-block b + 1 are in
+// flight while b is computed. Scheduling barriers keep the compiler from
+// sinking the loads below the compute (which would serialize every super-block
+// behind a full memory round trip).
 template <class W, int NM>
 __device__ __forceinline__ void stream_rows(const uint8_t* const (&wrow)[NM], const ActRows& x,
                                             int nb, int g, v4f (&acc)[NM], v4f (&mn)[NM]) {
   constexpr int BB = W::kBS ? 144 : 210;
-  ActSB xa, xb;
-  W wa[NM], wb[NM];
-  load_act<W::kBS>(xa, x, 0, g);
+  ActSB xs[2];
+  W ws[2][NM];
+  auto ld = [&](ActSB& xa, W (&wa)[NM], int b) {
+    load_act<W::kBS>(xa, x, b, g);
 #pragma unroll
-  for (int j = 0; j < NM; ++j) wa[j].load(wrow[j], g);
-  for (int b = 0; b < nb; b += 2) {
-    const int b1 = min(b + 1, nb - 1);
-    load_act<W::kBS>(xb, x, b1, g);
-#pragma unroll
-    for (int j = 0; j < NM; ++j) wb[j].load(wrow[j] + static_cast<size_t>(b1) * BB, g);
+    for (int j = 0; j < NM; ++j) wa[j].load(wrow[j] + static_cast<size_t>(b) * BB, g);
+  };
+  auto mm = [&](const ActSB& xa, const W (&wa)[NM]) {
 #pragma unroll
     for (int j = 0; j < NM; ++j) wa[j].mma(xa, g, acc[j], mn[j]);
-    const int b2 = min(b + 2, nb - 1);
-    load_act<W::kBS>(xa, x, b2, g);
-#pragma unroll
-    for (int j = 0; j < NM; ++j) wa[j].load(wrow[j] + static_cast<size_t>(b2) * BB, g);
-    if (b + 1 < nb) {
-#pragma unroll
-      for (int j = 0; j < NM; ++j) wb[j].mma(xb, g, acc[j], mn[j]);
-    }
+  };
+  ld(xs[0], ws[0], 0);
+  for (int b = 0; b < nb; b += 2) {
+    ld(xs[1], ws[1], min(b + 1, nb - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    mm(xs[0], ws[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    ld(xs[0], ws[0], min(b + 2, nb - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    if (b + 1 < nb) mm(xs[1], ws[1]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -459,9 +480,16 @@ __global__ __launch_bounds__(1024) void k_bucket(KArgs a) {
   }
 }
 
+// Row tiles of 16 per wave: gate/up (two weight streams per tile) and down.
+// Q6_K blocks hold more registers in flight than Q4_K, so they take fewer.
+template <int FMT> constexpr int gu_tiles() { return FMT == FMT_Q4_K ? 2 : 1; }
+template <int FMT> constexpr int down_tiles() { return FMT == FMT_Q4_K ? 4 : 2; }
+
 // Gate/up rows of one tile: grid 8 * ceil(max items / 8), block 256. Item =
-// (tile, block of 64 rows of F); wave w takes rows 16 w .. 16 w + 15 of the block.
-template <int FMT>
+// (tile, block of 64 NT rows of F); wave w takes row tiles 16 (NT w + r),
+// r < NT; its 2 NT weight streams (gate and up of each row tile) share one
+// activation stage.
+template <int FMT, int NT>
 __global__ __launch_bounds__(256) void k_gu_grouped(KArgs a, Div dRB) {
   using W = typename WOf<FMT>::T;
   const int n_tiles = static_cast<int>(*gp<uint32_t>(a.counters));
@@ -483,21 +511,30 @@ __global__ __launch_bounds__(256) void k_gu_grouped(KArgs a, Div dRB) {
   x.da = a.xd + static_cast<size_t>(pA.y) * nb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) x.dc[i] = a.xd + static_cast<size_t>(pC[i].y) * nb;
-  const int row = rb * 64 + wave * 16 + c;
-  const uint8_t* const wrow[2] = {tl.gate + static_cast<size_t>(row) * a.stride_gate,
-                                  tl.up + static_cast<size_t>(row) * a.stride_up};
-  v4f acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  v4f mn[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  stream_rows<W, 2>(wrow, x, nb, g, acc, mn);
-  const float bg = tl.b_gate ? tl.b_gate[row] : 0.0f;
-  const float bu = tl.b_up ? tl.b_up[row] : 0.0f;
+  const int row0 = (rb * 4 + wave) * 16 * NT + c;  // row tile r: row0 + 16 r
+  const uint8_t* wrow[2 * NT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (4 * g + i < cnt) {
-      const float gv = acc[0][i] - mn[0][i] + bg;
-      const float uv = acc[1][i] - mn[1][i] + bu;
-      a.h[static_cast<size_t>(pC[i].x) * a.F + row] =
-          act_fn(a.act, a.act_alpha, a.act_limit, gv, uv);
+  for (int r = 0; r < NT; ++r) {
+    wrow[2 * r] = tl.gate + static_cast<size_t>(row0 + 16 * r) * a.stride_gate;
+    wrow[2 * r + 1] = tl.up + static_cast<size_t>(row0 + 16 * r) * a.stride_up;
+  }
+  v4f acc[2 * NT], mn[2 * NT];
+#pragma unroll
+  for (int j = 0; j < 2 * NT; ++j) acc[j] = mn[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  stream_rows<W, 2 * NT>(wrow, x, nb, g, acc, mn);
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    const int row = row0 + 16 * r;
+    const float bg = tl.b_gate ? tl.b_gate[row] : 0.0f;
+    const float bu = tl.b_up ? tl.b_up[row] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * g + i < cnt) {
+        const float gv = acc[2 * r][i] - mn[2 * r][i] + bg;
+        const float uv = acc[2 * r + 1][i] - mn[2 * r + 1][i] + bu;
+        a.h[static_cast<size_t>(pC[i].x) * a.F + row] =
+            act_fn(a.act, a.act_alpha, a.act_limit, gv, uv);
+      }
     }
   }
 }
@@ -517,9 +554,10 @@ __global__ __launch_bounds__(256) void k_hquant(KArgs a, int P) {
                   a.hbs + static_cast<size_t>(p) * (a.F >> 4) + pc * 16);
 }
 
-// Down rows of one tile: item = (tile, block of 64 rows of H). Writes
-// part[p] = w_p * (W_d q8(h_p) + b_d) for the tile's pairs.
-template <int FMT>
+// Down rows of one tile: item = (tile, block of 64 NT rows of H); wave w takes
+// row tiles 16 (NT w + r), r < NT. Writes part[p] = w_p * (W_d q8(h_p) + b_d)
+// for the tile's pairs.
+template <int FMT, int NT>
 __global__ __launch_bounds__(256) void k_down_grouped(KArgs a, Div dRB) {
   using W = typename WOf<FMT>::T;
   const int n_tiles = static_cast<int>(*gp<uint32_t>(a.counters));
@@ -541,19 +579,29 @@ __global__ __launch_bounds__(256) void k_down_grouped(KArgs a, Div dRB) {
   x.da = a.hd + static_cast<size_t>(pA.x) * nb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) x.dc[i] = a.hd + static_cast<size_t>(pC[i].x) * nb;
-  const int row = rb * 64 + wave * 16 + c;
-  const uint8_t* const wrow[1] = {tl.down + static_cast<size_t>(row) * a.stride_down};
-  v4f acc[1] = {{0, 0, 0, 0}};
-  v4f mn[1] = {{0, 0, 0, 0}};
-  stream_rows<W, 1>(wrow, x, nb, g, acc, mn);
-  const float bd = tl.b_down ? tl.b_down[row] : 0.0f;
+  const int row0 = (rb * 4 + wave) * 16 * NT + c;  // row tile r: row0 + 16 r
+  const uint8_t* wrow[NT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r) wrow[r] = tl.down + static_cast<size_t>(row0 + 16 * r) * a.stride_down;
+  v4f acc[NT], mn[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = mn[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  stream_rows<W, NT>(wrow, x, nb, g, acc, mn);
   const int Tk = a.T * a.k;
+  float wp[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (4 * g + i < cnt) {
-      const int p = pC[i].x;
-      const float wp = p < Tk ? a.w[p] : (a.sh_gate_vec ? a.shw[p - Tk] : 1.0f);
-      a.part[static_cast<size_t>(p) * a.H + row] = wp * (acc[0][i] - mn[0][i] + bd);
+    const int p = pC[i].x;
+    wp[i] = p < Tk ? a.w[p] : (a.sh_gate_vec ? a.shw[p - Tk] : 1.0f);
+  }
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    const int row = row0 + 16 * r;
+    const float bd = tl.b_down ? tl.b_down[row] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * g + i < cnt)
+        a.part[static_cast<size_t>(pC[i].x) * a.H + row] = wp[i] * (acc[r][i] - mn[r][i] + bd);
     }
   }
 }
@@ -622,11 +670,17 @@ hipError_t launch_bucket(const KArgs& a, hipStream_t s, Ev ev) {
 }
 
 hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s, Ev ev) {
-  const int RB = a.F / 64;
-  const dim3 grid(grouped_grid(max_tiles(a.T, a.k, a.E, a.has_shared) * RB));
-  const Div d = Div::make(RB);
-  if (a.fmt_gu == FMT_Q4_K) return launch(k_gu_grouped<FMT_Q4_K>, grid, 256, 0, s, ev, a, d);
-  return launch(k_gu_grouped<FMT_Q6_K>, grid, 256, 0, s, ev, a, d);
+  const int mt = max_tiles(a.T, a.k, a.E, a.has_shared);
+  if (a.fmt_gu == FMT_Q4_K) {
+    constexpr int NT = gu_tiles<FMT_Q4_K>();
+    const int RB = a.F / (64 * NT);
+    return launch(k_gu_grouped<FMT_Q4_K, NT>, dim3(grouped_grid(mt * RB)), 256, 0, s, ev, a,
+                  Div::make(RB));
+  }
+  constexpr int NT = gu_tiles<FMT_Q6_K>();
+  const int RB = a.F / (64 * NT);
+  return launch(k_gu_grouped<FMT_Q6_K, NT>, dim3(grouped_grid(mt * RB)), 256, 0, s, ev, a,
+                Div::make(RB));
 }
 
 hipError_t launch_hquant(const KArgs& a, hipStream_t s, Ev ev) {
@@ -636,11 +690,17 @@ hipError_t launch_hquant(const KArgs& a, hipStream_t s, Ev ev) {
 }
 
 hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev) {
-  const int RB = a.H / 64;
-  const dim3 grid(grouped_grid(max_tiles(a.T, a.k, a.E, a.has_shared) * RB));
-  const Div d = Div::make(RB);
-  if (a.fmt_d == FMT_Q4_K) return launch(k_down_grouped<FMT_Q4_K>, grid, 256, 0, s, ev, a, d);
-  return launch(k_down_grouped<FMT_Q6_K>, grid, 256, 0, s, ev, a, d);
+  const int mt = max_tiles(a.T, a.k, a.E, a.has_shared);
+  if (a.fmt_d == FMT_Q4_K) {
+    constexpr int NT = down_tiles<FMT_Q4_K>();
+    const int RB = a.H / (64 * NT);
+    return launch(k_down_grouped<FMT_Q4_K, NT>, dim3(grouped_grid(mt * RB)), 256, 0, s, ev, a,
+                  Div::make(RB));
+  }
+  constexpr int NT = down_tiles<FMT_Q6_K>();
+  const int RB = a.H / (64 * NT);
+  return launch(k_down_grouped<FMT_Q6_K, NT>, dim3(grouped_grid(mt * RB)), 256, 0, s, ev, a,
+                Div::make(RB));
 }
 
 hipError_t launch_combine(const KArgs& a, hipStream_t s, Ev ev) {
