@@ -21,6 +21,8 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # never emit packed fp32 math (v_pk_{add,mul,fma}_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs (no accumulator-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

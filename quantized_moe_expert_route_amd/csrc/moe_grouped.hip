@@ -269,6 +269,244 @@ __device__ __forceinline__ void stream_rows(const uint8_t* const (&wrow)[NM], co
   }
 }
 
+// ------------------------------------------------ LDS-staged Q4_K tile stream
+// One work item streams the Q4_K rows of a few consecutive row blocks of one
+// tile through a 3-slot LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4), two super-blocks ahead of the compute, so no
+// weight bytes sit in registers while in flight. A slot holds one super-block
+// of 128 weight rows (gate/up: 64 rows of each; down: 128 rows) and of the
+// tile's 16 activation rows:
+constexpr int kStA = 128 * 144;          // 16 rows x 256 B of q8, 16-byte pieces XOR-swizzled
+constexpr int kStB = kStA + 16 * 256;    // 16 rows x 32 B of 16-element sums (+ 512 B pad)
+constexpr int kStD = kStB + 1024;        // 16 block scales (+ pad)
+constexpr int kStBytes = kStD + 256;     // 23808 B per slot
+
+#define MOE_LDS __attribute__((address_space(3)))
+// Direct global->LDS loads. Written as inline asm so that the compiler does not
+// track their LDS writes: its tracking loses count across the ring's loop and
+// would wait for every slot load in flight before any LDS read. Completion is
+// ordered by the explicit vmcnt waits and workgroup barriers of the ring. (The
+// compiler's own vmcnt waits for other loads stay sufficient: loads complete
+// in issue order, so extra ops it does not see only make them stronger.)
+// LDS byte address of a (wave-uniform) pointer into a __shared__ array, as an
+// SGPR value for M0.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* l) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const MOE_LDS uint8_t*)(l))));
+}
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* l) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr(l))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* l) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds_addr(l))
+               : "memory", "m0");
+}
+// Wait until at most N vector memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// MODE 0: gate/up (streams: gate and up rows of one 16-row tile per wave, 64
+// rows per row block). MODE 1: down (two 16-row tiles per wave, 128 rows per
+// row block). grid 8 * ceil(max items / 8), block 256 (4 waves, 2 per SIMD).
+// Item = (tile, ii): row blocks [ii RBG, min(RB, (ii + 1) RBG)). Layers without
+// expert biases only (those take the register-staged kernels).
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG, int RB) {
+  // three separate arrays: with the slot known at each access the compiler can
+  // tell a slot being filled from the slot being read (no forced vmcnt(0))
+  __shared__ __align__(16) uint8_t lds0[kStBytes];
+  __shared__ __align__(16) uint8_t lds1[kStBytes];
+  __shared__ __align__(16) uint8_t lds2[kStBytes];
+  const int n_tiles = static_cast<int>(*gp<uint32_t>(a.counters));
+  const int item = grouped_item(n_tiles * static_cast<int>(dIPT.d));
+  if (item < 0) return;
+  const uint32_t tile = dIPT.div(item);
+  const int ii = dIPT.mod(item, tile);
+  const int rb0 = ii * RBG, rb1 = min(RB, rb0 + RBG);
+  const GTile tl = a.tiles[tile];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  const int cnt = tl.cnt;
+  const int K = MODE == 0 ? a.H : a.F;  // reduction length
+  const int nb = K >> 8;
+  // activation rows of token slot ts (slots >= cnt repeat the last pair)
+  auto pair_of = [&](int ts) { return a.plist[tl.start + min(ts, cnt - 1)]; };
+  auto act_q = [&](int2 pr) -> const uint8_t* {
+    return MODE == 0 ? reinterpret_cast<const uint8_t*>(a.xqs) + static_cast<size_t>(pr.y) * K
+                     : reinterpret_cast<const uint8_t*>(a.hqs) + static_cast<size_t>(pr.x) * K;
+  };
+  auto act_bs = [&](int2 pr) -> const uint8_t* {
+    return MODE == 0 ? reinterpret_cast<const uint8_t*>(a.xbs + static_cast<size_t>(pr.y) * (K >> 4))
+                     : reinterpret_cast<const uint8_t*>(a.hbs + static_cast<size_t>(pr.x) * (K >> 4));
+  };
+  auto act_d = [&](int2 pr) -> const uint8_t* {
+    return MODE == 0 ? reinterpret_cast<const uint8_t*>(a.xd + static_cast<size_t>(pr.y) * nb)
+                     : reinterpret_cast<const uint8_t*>(a.hd + static_cast<size_t>(pr.x) * nb);
+  };
+  // ---- per-lane DMA sources. Wave w issues slot pieces j = w + 4u, u = 0..5:
+  // j < 18 weights (piece i = 64 j + lane: row R = i / 9, 16-byte part i % 9),
+  // 18..21 activation q8 (LDS piece (ts, ql) holds global piece ql ^ ts),
+  // 22 the 16-element sums, 23 (4-byte) the block scales.
+  const uint8_t* wsrc[5];
+  size_t wrbs[5];  // bytes between consecutive row blocks
+#pragma unroll
+  for (int u = 0; u < 5; ++u) {
+    const int j = min(wave + 4 * u, 17);
+    const int i = 64 * j + lane, R = i / 9, q = i - 9 * R;
+    const uint8_t* W;
+    size_t st;
+    int r;
+    if (MODE == 0) {
+      W = R < 64 ? tl.gate : tl.up;
+      st = R < 64 ? a.stride_gate : a.stride_up;
+      r = R & 63;
+    } else {
+      W = tl.down;
+      st = a.stride_down;
+      r = R;
+    }
+    wsrc[u] = W + static_cast<size_t>(r) * st + 16 * q;
+    wrbs[u] = (MODE == 0 ? 64 : 128) * st;
+  }
+  const uint8_t* asrc;  // activation q8 piece (waves 0..3: slot piece 20, 21, 18, 19)
+  {
+    const int j = wave < 2 ? 20 + wave : 16 + wave;
+    const int i = 64 * (j - 18) + lane, ts = i >> 4, ql = i & 15;
+    asrc = act_q(pair_of(ts)) + 16 * (ql ^ ts);
+  }
+  const uint8_t* xsrc;  // wave 2: sums (lanes 32..63 repeat 0..31); wave 3: scales
+  if (wave == 2) {
+    const int l = lane & 31;
+    xsrc = act_bs(pair_of(l >> 1)) + 16 * (l & 1);
+  } else {
+    xsrc = act_d(pair_of(lane & 15));
+  }
+  auto issue = [&](uint8_t* L, int rb, int b) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      dma16(wsrc[u] + rb * wrbs[u] + 144 * b, L + 1024 * (wave + 4 * u));
+    if (wave < 2) {
+      dma16(wsrc[4] + rb * wrbs[4] + 144 * b, L + 1024 * (wave + 16));
+      dma16(asrc + 256 * b, L + 1024 * (wave + 20));
+    } else {
+      dma16(asrc + 256 * b, L + 1024 * (wave + 16));
+      if (wave == 2) dma16(xsrc + 32 * b, L + kStB);
+      else dma4(xsrc + 4 * b, L + kStD);
+    }
+  };
+  // ---- compute-side lane roles
+  const int2 pA = pair_of(c);
+  int2 pC[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pC[i] = pair_of(4 * g + i);
+  int Rj[2];
+  if (MODE == 0) { Rj[0] = wave * 16 + c; Rj[1] = 64 + wave * 16 + c; }
+  else { Rj[0] = wave * 32 + c; Rj[1] = wave * 32 + 16 + c; }
+  auto row_of = [&](int j, int rb) {
+    return MODE == 0 ? rb * 64 + wave * 16 + c : rb * 128 + wave * 32 + 16 * j + c;
+  };
+  const int Tk = a.T * a.k;
+  float wp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (MODE == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = pC[i].x;
+      wp[i] = p < Tk ? *gp<float>(a.w + p) : (a.sh_gate_vec ? *gp<float>(a.shw + p - Tk) : 1.0f);
+    }
+  }
+  // make every register load complete here, before the ring is filled: a wait
+  // for them later (across the loop) would drain the in-flight slot loads
+#pragma unroll
+  for (int i = 0; i < 4; ++i) __asm__ volatile("" ::"v"(wp[i]), "v"(pC[i].x));
+  const int nst = (rb1 - rb0) * nb;
+  issue(lds0, rb0, 0);
+  if (nst > 1) issue(lds1, rb0 + (nb > 1 ? 0 : 1), nb > 1 ? 1 : 0);
+  v4f acc[2], mn[2];
+  int rb = rb0, b = 0;          // stage s: row block rb, super-block b
+  int rbn = rb0, bn = 0;        // stage s + 2
+  for (int k2 = 0; k2 < 2; ++k2) { if (++bn == nb) { bn = 0; ++rbn; } }
+  // stage s: read slot s % 3, refill slot (s + 2) % 3
+  auto step = [&](int s, const uint8_t* L, uint8_t* Lw) {
+    // Loads complete in issue order, so this wave's loads of stage s are done
+    // once at most the 6 of stage s + 1 are outstanding (stores may still be);
+    // the barrier then publishes every wave's share of the slot.
+    if (s + 1 < nst) wait_vm<6>(); else wait_vm<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    if (b == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[j] = mn[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // the slot of stage s - 1 is free: every wave has passed its compute
+    if (s + 2 < nst) issue(Lw, rbn, bn);
+    if (++bn == nb) { bn = 0; ++rbn; }
+    __builtin_amdgcn_sched_barrier(0);
+    ActSB x;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int qg = 2 * m + (g >> 1);
+      x.q[m] = *reinterpret_cast<const uint2*>(L + kStA + c * 256 + 16 * (qg ^ c) + 8 * (g & 1));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      x.bs[h] = *reinterpret_cast<const uint32_t*>(L + kStB + 32 * c + 4 * (4 * h + g));
+    x.dA = *reinterpret_cast<const float*>(L + kStD + 4 * c);
+    {
+      const float4 dc = *reinterpret_cast<const float4*>(L + kStD + 16 * g);
+      x.dC[0] = dc.x; x.dC[1] = dc.y; x.dC[2] = dc.z; x.dC[3] = dc.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      WQ4K w;
+      const uint8_t* blk = L + Rj[j] * 144;
+      w.hdr = *reinterpret_cast<const uint4*>(blk);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) w.q[cc] = *reinterpret_cast<const uint2*>(blk + 16 + 32 * cc + 8 * g);
+      w.mma(x, g, acc[j], mn[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (b == nb - 1) {  // row block done
+      if (MODE == 0) {
+        const int row = row_of(0, rb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * g + i < cnt) {
+            const float gv = acc[0][i] - mn[0][i];
+            const float uv = acc[1][i] - mn[1][i];
+            a.h[static_cast<size_t>(pC[i].x) * a.F + row] =
+                act_fn(a.act, a.act_alpha, a.act_limit, gv, uv);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = row_of(j, rb);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (4 * g + i < cnt)
+              a.part[static_cast<size_t>(pC[i].x) * a.H + row] = wp[i] * (acc[j][i] - mn[j][i]);
+          }
+        }
+      }
+    }
+    if (++b == nb) { b = 0; ++rb; }
+  };
+  for (int s = 0; s < nst; s += 3) {
+    step(s, lds0, lds2);
+    if (s + 1 < nst) step(s + 1, lds1, lds0);
+    if (s + 2 < nst) step(s + 2, lds2, lds1);
+  }
+}
+
 // ================================================================== kernels
 
 // Router logits for many tokens: fp32 inputs, fp64 MFMA products and sums (the
@@ -628,6 +866,15 @@ __global__ __launch_bounds__(256) void k_combine(KArgs a) {
 
 int grouped_grid(int n_items_max) { return 8 * ((n_items_max + 7) / 8); }
 
+// Row blocks per LDS-staged work item: long enough streams to amortize the
+// ring fill, while keeping about 4096 items at the bound on tiles.
+int glds_group(int RB, int max_tiles) {
+  int g = (RB * max_tiles + 4095) / 4096;
+  if (g < 1) g = 1;
+  if (g > RB) g = RB;
+  return g;
+}
+
 }  // namespace
 
 RouterSplit router_split(int T, int E, int H) {
@@ -671,6 +918,11 @@ hipError_t launch_bucket(const KArgs& a, hipStream_t s, Ev ev) {
 
 hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s, Ev ev) {
   const int mt = max_tiles(a.T, a.k, a.E, a.has_shared);
+  if (a.fmt_gu == FMT_Q4_K && a.b_gate == nullptr) {
+    const int RB = a.F / 64, RBG = glds_group(RB, mt), IPT = (RB + RBG - 1) / RBG;
+    return launch(k_glds_q4k<0>, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a, Div::make(IPT),
+                  RBG, RB);
+  }
   if (a.fmt_gu == FMT_Q4_K) {
     constexpr int NT = gu_tiles<FMT_Q4_K>();
     const int RB = a.F / (64 * NT);
@@ -691,6 +943,11 @@ hipError_t launch_hquant(const KArgs& a, hipStream_t s, Ev ev) {
 
 hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev) {
   const int mt = max_tiles(a.T, a.k, a.E, a.has_shared);
+  if (a.fmt_d == FMT_Q4_K && a.b_down == nullptr) {
+    const int RB = a.H / 128, RBG = glds_group(RB, mt), IPT = (RB + RBG - 1) / RBG;
+    return launch(k_glds_q4k<1>, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a, Div::make(IPT),
+                  RBG, RB);
+  }
   if (a.fmt_d == FMT_Q4_K) {
     constexpr int NT = down_tiles<FMT_Q4_K>();
     const int RB = a.H / (64 * NT);

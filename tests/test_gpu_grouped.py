@@ -31,6 +31,13 @@ def test_grouped_dense_k_equals_E():
     check_layer(cfg, T=40, x_index=1)
 
 
+def test_grouped_biases():
+    """Q4_K experts with gate/up/down biases (the register-staged tile kernels)
+    and Q6_K gate/up rows."""
+    check_layer(SHRUNK["kimi-k2"].with_(biases=True), T=11, x_index=5)
+    check_layer(SHRUNK["deepseek-v4-flash"].with_(fmt_gu=gen.Q6_K), T=9, x_index=5)
+
+
 def test_grouped_bf16_input():
     cfg = SHRUNK["kimi-k2"].with_(x_bf16=True)
     check_layer(cfg, T=9, x_index=4)
