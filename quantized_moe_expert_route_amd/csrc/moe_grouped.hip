@@ -507,6 +507,147 @@ __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG,
   }
 }
 
+// ------------------------------------------------ LDS-staged Q6_K down stream
+// Q6_K blocks are 210 bytes, so a row's super-block b is not 16-byte aligned:
+// a slot holds, per row, the 16-byte pieces that cover it (at most 14; the
+// block starts at byte (210 b) mod 16 of them; row pitch 240) for 64 rows,
+// plus the tile's 16 activation rows and block scales. Every piece loaded
+// holds at least one byte of the block, so no load leaves its page.
+constexpr int kQ6Row = 240;
+constexpr int kS6A = 64 * kQ6Row;        // 15360: 16 rows x 256 B of q8 (XOR-swizzled pieces)
+constexpr int kS6D = kS6A + 16 * 256;    // 19456: 16 block scales (+ pad)
+constexpr int kS6Bytes = kS6D + 256;     // 19712 B per slot
+
+// 8 bytes at byte offset off (even) of a 16-byte aligned LDS slot: dword
+// reads + byte align (offset arithmetic keeps the LDS address space visible).
+__device__ __forceinline__ uint2 lds8_a2(const uint8_t* L, int off) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(L + (off & ~3));
+  const uint32_t* wl = reinterpret_cast<const uint32_t*>(L + ((off + 7) & ~3));
+  const uint32_t sh = static_cast<uint32_t>(off & 3);
+  const uint32_t w0 = w[0], w1 = w[1], w2 = *wl;
+  return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
+}
+
+// Down rows of Q6_K experts: item = (tile, ii), row blocks of 64 rows of H,
+// wave w takes rows 16 w .. 16 w + 15 of a block. Same ring protocol as
+// k_glds_q4k, 5 slot loads per wave and stage. Layers without down biases.
+__global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int RBG, int RB) {
+  __shared__ __align__(16) uint8_t lds0[kS6Bytes];
+  __shared__ __align__(16) uint8_t lds1[kS6Bytes];
+  __shared__ __align__(16) uint8_t lds2[kS6Bytes];
+  const int n_tiles = static_cast<int>(*gp<uint32_t>(a.counters));
+  const int item = grouped_item(n_tiles * static_cast<int>(dIPT.d));
+  if (item < 0) return;
+  const uint32_t tile = dIPT.div(item);
+  const int ii = dIPT.mod(item, tile);
+  const int rb0 = ii * RBG, rb1 = min(RB, rb0 + RBG);
+  const GTile tl = a.tiles[tile];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  const int cnt = tl.cnt;
+  const int K = a.F, nb = K >> 8;
+  auto pair_of = [&](int ts) { return a.plist[tl.start + min(ts, cnt - 1)]; };
+  // slot loads j = wave + 4 u, u = 0..4: j < 15 weight pieces (i = 64 j + lane:
+  // row R = i / 15, piece i % 15), 15..18 q8(h) pieces, 19 (4-byte) scales
+  const uint8_t* wsrc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = min(wave + 4 * u, 14);
+    // a block needs at most 14 pieces (sh + 210 <= 224 bytes); the 15th of a
+    // row reloads the 14th, so no load starts past the block (the last block
+    // of the last row of an expert may end its allocation)
+    const int i = 64 * j + lane, R = i / 15, q = min(i - 15 * R, 13);
+    wsrc[u] = tl.down + static_cast<size_t>(R) * a.stride_down + 16 * q;
+  }
+  const size_t rbs = 64 * a.stride_down;
+  const uint8_t* asrc;
+  {
+    const int j = wave == 3 ? 15 : 16 + wave;
+    const int i = 64 * (j - 15) + lane, ts = i >> 4, ql = i & 15;
+    asrc = reinterpret_cast<const uint8_t*>(a.hqs) + static_cast<size_t>(pair_of(ts).x) * K +
+           16 * (ql ^ ts);
+  }
+  const uint8_t* dsrc =
+      reinterpret_cast<const uint8_t*>(a.hd + static_cast<size_t>(pair_of(lane & 15).x) * nb);
+  auto issue = [&](uint8_t* L, int rb, int b) {
+    const size_t wo = rb * rbs + ((210 * b) & ~15);
+#pragma unroll
+    for (int u = 0; u < 3; ++u) dma16(wsrc[u] + wo, L + 1024 * (wave + 4 * u));
+    if (wave < 3) {
+      dma16(wsrc[3] + wo, L + 1024 * (wave + 12));
+      dma16(asrc + 256 * b, L + 1024 * (wave + 16));
+    } else {
+      dma16(asrc + 256 * b, L + 1024 * 15);
+      dma4(dsrc + 4 * b, L + kS6D);
+    }
+  };
+  const int2 pA = pair_of(c);
+  (void)pA;
+  int2 pC[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pC[i] = pair_of(4 * g + i);
+  const int Tk = a.T * a.k;
+  float wp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = pC[i].x;
+    wp[i] = p < Tk ? *gp<float>(a.w + p) : (a.sh_gate_vec ? *gp<float>(a.shw + p - Tk) : 1.0f);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) __asm__ volatile("" ::"v"(wp[i]), "v"(pC[i].x));
+  const int nst = (rb1 - rb0) * nb;
+  issue(lds0, rb0, 0);
+  if (nst > 1) issue(lds1, rb0 + (nb > 1 ? 0 : 1), nb > 1 ? 1 : 0);
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f}, mn = acc;
+  int rb = rb0, b = 0, rbn = rb0, bn = 0;
+  for (int k2 = 0; k2 < 2; ++k2) { if (++bn == nb) { bn = 0; ++rbn; } }
+  auto step = [&](int s, const uint8_t* L, uint8_t* Lw) {
+    if (s + 1 < nst) wait_vm<5>(); else wait_vm<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (b == 0) acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    if (s + 2 < nst) issue(Lw, rbn, bn);
+    if (++bn == nb) { bn = 0; ++rbn; }
+    __builtin_amdgcn_sched_barrier(0);
+    ActSB x;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int qg = 2 * m + (g >> 1);
+      x.q[m] = *reinterpret_cast<const uint2*>(L + kS6A + c * 256 + 16 * (qg ^ c) + 8 * (g & 1));
+    }
+    {
+      const float4 dc = *reinterpret_cast<const float4*>(L + kS6D + 16 * g);
+      x.dC[0] = dc.x; x.dC[1] = dc.y; x.dC[2] = dc.z; x.dC[3] = dc.w;
+    }
+    WQ6K w;
+    const int blk = (wave * 16 + c) * kQ6Row + ((210 * b) & 15);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      w.l0[h] = lds8_a2(L, blk + 64 * h + 8 * g);
+      w.l1[h] = lds8_a2(L, blk + 64 * h + 32 + 8 * g);
+      w.qh[h] = lds8_a2(L, blk + 128 + 32 * h + 8 * g);
+    }
+    w.sc[0] = lds8_a2(L, blk + 192);
+    w.sc[1] = lds8_a2(L, blk + 200);
+    w.dbits = *reinterpret_cast<const uint16_t*>(L + blk + 208);
+    w.mma(x, g, acc, mn);
+    __builtin_amdgcn_sched_barrier(0);
+    if (b == nb - 1) {
+      const int row = rb * 64 + wave * 16 + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * g + i < cnt) a.part[static_cast<size_t>(pC[i].x) * a.H + row] = wp[i] * acc[i];
+    }
+    if (++b == nb) { b = 0; ++rb; }
+  };
+  for (int s = 0; s < nst; s += 3) {
+    step(s, lds0, lds2);
+    if (s + 1 < nst) step(s + 1, lds1, lds0);
+    if (s + 2 < nst) step(s + 2, lds2, lds1);
+  }
+}
+
 // ================================================================== kernels
 
 // Router logits for many tokens: fp32 inputs, fp64 MFMA products and sums (the
@@ -953,6 +1094,11 @@ hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev) {
     const int RB = a.H / (64 * NT);
     return launch(k_down_grouped<FMT_Q4_K, NT>, dim3(grouped_grid(mt * RB)), 256, 0, s, ev, a,
                   Div::make(RB));
+  }
+  if (a.b_down == nullptr) {
+    const int RB = a.H / 64, RBG = glds_group(RB, mt), IPT = (RB + RBG - 1) / RBG;
+    return launch(k_glds_q6k_down, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a,
+                  Div::make(IPT), RBG, RB);
   }
   constexpr int NT = down_tiles<FMT_Q6_K>();
   const int RB = a.H / (64 * NT);
