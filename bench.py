@@ -158,23 +158,14 @@ def main():
     uniq = [len(np.unique(r)) + (1 if cfg.shared else 0) for r in realized]
     uniq_mean = float(np.mean(uniq))
     sel_bytes = uniq_mean * cfg.expert_algo_bytes
-    pairs = T * cfg.k + (T if cfg.shared else 0)
-    grouped = n_st == 7
-    # algorithmic bytes per launch of the two expert kernels: the per-pair path
-    # streams each (token, slot) pair's expert rows; the grouped path each
-    # selected expert's rows once (unique experts of the chunk + shared)
-    units = uniq_mean if grouped else pairs
-    algo = {
-        "gateup": units * 2 * cfg.F * gen.row_bytes(cfg.fmt_gu, cfg.H),
-        "down": units * cfg.H * gen.row_bytes(cfg.fmt_d, cfg.F),
-    }
-    kern_names = ({"gateup": "k_gu_grouped", "down": "k_down_grouped"} if grouped
-                  else {"gateup": "k_gateup", "down": "k_down"})
+    path = "grouped" if n_st == 7 else "gemv"
+    algo = algo_bytes(cfg, path, uniq_mean)
+    kern_names = kernel_names(cfg, path)
     dom = max(("gateup", "down"), key=lambda k: stage_avg_us.get(k, 0.0))
     dom_us = stage_avg_us[dom]
     expert_us = stage_avg_us.get("gateup", 0) + stage_avg_us.get("down", 0)
     achieved = algo[dom] / (dom_us * 1e-6) / 1e9
-    traffic = _traffic_for(kern_names[dom], args.workload)
+    traffic = _traffic_for(kern_names[dom], args.workload, path)
     roofline = {
         "kernel": kern_names[dom],
         "bound": "hbm",
@@ -220,7 +211,7 @@ def main():
             "tokens_per_step": T,
             "layer_copies": copies,
             "x_pool": args.x_pool,
-            "path": "grouped" if grouped else "gemv",
+            "path": path,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -230,7 +221,7 @@ def main():
             "layer_GBps_selected_experts": round(sel_bytes / (ms_per_step * 1e-3) / 1e9, 1),
             "layer_hbm_frac": round(sel_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "expert_kernels_us": round(expert_us, 3),
-            "kernel_source_hash": _kernel_source_hash(),
+            "kernel_source_hash": kernel_source_hash(path),
             "expert_GBps": round(sel_bytes / (expert_us * 1e-6) / 1e9, 1) if expert_us else None,
             "stage_avg_us": {k: round(v, 3) for k, v in stage_avg_us.items()},
             "setup_s": round(setup_s, 1),
@@ -239,28 +230,70 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _kernel_source_hash() -> str:
+def algo_bytes(cfg, path: str, unique_experts: float) -> dict:
+    """Algorithmic bytes per launch of the two expert kernels. The per-pair path
+    streams every (token, slot) pair's expert rows (T k + shared pairs); the
+    grouped path each selected expert's rows once (unique experts + shared).
+    Padding bytes of a row are not counted."""
+    pairs = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
+    units = unique_experts if path == "grouped" else pairs
+    return {
+        "gateup": units * 2 * cfg.F * gen_row_bytes(cfg.fmt_gu, cfg.H),
+        "down": units * cfg.H * gen_row_bytes(cfg.fmt_d, cfg.F),
+        "router": 4 * cfg.E * cfg.H,
+    }
+
+
+def gen_row_bytes(fmt, K):
+    import gen
+    return gen.row_bytes(fmt, K)
+
+
+def kernel_names(cfg, path: str) -> dict:
+    """Kernel (as rocprofv3 names it) of each stage of a layer forward."""
+    import gen
+    if path == "gemv":
+        return {"router": "k_router<4>", "gateup": "k_gateup", "down": "k_down"}
+    nb = cfg.biases
+    gu = "k_glds_q4k<0>" if cfg.fmt_gu == gen.Q4_K and not nb else "k_gu_grouped"
+    if cfg.fmt_d == gen.Q4_K and not nb:
+        dn = "k_glds_q4k<1>"
+    elif cfg.fmt_d == gen.Q6_K and not nb:
+        dn = "k_glds_q6k_down"
+    else:
+        dn = "k_down_grouped"
+    return {"router": "k_router_mfma", "gateup": gu, "down": dn}
+
+
+_PATH_SOURCES = {
+    "gemv": ("moe_kernels.hip", "moe_device.h", "moe_internal.h"),
+    "grouped": ("moe_grouped.hip", "moe_device.h", "moe_internal.h"),
+}
+
+
+def kernel_source_hash(path: str) -> str:
+    """Hash of the kernel sources of one path (a committed counter measurement
+    stays valid while they are unchanged)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_moe_expert_route_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
-        if n.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, n), "rb").read())
+    for n in _PATH_SOURCES[path]:
+        h.update(open(os.path.join(csrc, n), "rb").read())
     return h.hexdigest()[:16]
 
 
-def _traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from the committed PMC summary, if it was taken on the
-    current kernel sources (else null)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _traffic_for(kernel: str, workload: str, path: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel sources of the path (else null)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path))
+        rec = json.load(open(p))
     except Exception:
         return None
-    if rec.get("source_hash") != _kernel_source_hash():
-        return None
     ent = rec.get("kernels", {}).get(f"{workload}:{kernel}")
-    return None if ent is None else ent.get("hbm_bytes_per_launch")
+    if ent is None or ent.get("source_hash") != kernel_source_hash(path):
+        return None
+    return ent.get("hbm_bytes_per_launch")
 
 
 def _oracle_token_s(cfg) -> float:
