@@ -324,31 +324,16 @@ __global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, D
   __shared__ const uint8_t* dptr[17];
   __shared__ const float* dbias[17];
   __shared__ float wslot[17];
-  __shared__ int pslot[17];
-  if (threadIdx.x < ns) {
-    const int s = threadIdx.x;
-    if (s < a.k) {
-      const SlotRef ref = a.slots[t * a.k + s];
-      dptr[s] = ref.down;
-      dbias[s] = ref.bias;
-      wslot[s] = a.w[t * a.k + s];
-      pslot[s] = t * a.k + s;
-    } else {
-      dptr[s] = static_cast<const uint8_t*>(a.sh_down);
-      dbias[s] = nullptr;
-      wslot[s] = a.sh_gate_vec ? a.shw[t] : 1.0f;
-      pslot[s] = a.T * a.k + t;
-    }
-  }
-  __syncthreads();
   const int G = 256 / F::LPB;
   const int grp = threadIdx.x / F::LPB, sub = threadIdx.x % F::LPB;
   const int total = ns * R * nb;
   typename F::Raw raw[TPG];
   // q8 of h for every present slot (fp32 recipe). Waves take 256-value pieces
-  // ("jobs"). The first kBatch jobs of each wave are loaded before the weight
-  // loads are issued, so quantizing them waits only for the h loads (memory
-  // counters complete in order) while the weights stay in flight.
+  // ("jobs"). h rows sit at fixed places (pair t k + s, shared T k + t), so the
+  // first kBatch jobs of each wave are loaded before the slot table is even
+  // read (an absent slot's row is loaded and ignored); the weight loads follow
+  // the slot table, and quantizing waits only for h (memory counters complete
+  // in order) while the weights stay in flight.
   constexpr int kBatch = 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int pieces = (K + 255) / 256;
@@ -359,11 +344,29 @@ __global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, D
   auto load_h = [&](int job) {
     const int jc = min(job, njobs - 1);
     const int s = dpc.div(jc), e0 = dpc.mod(jc, s) * 256 + 4 * lane;
-    const bool ok = job < njobs && dptr[s] != nullptr && e0 < K;
-    const float* src = ok ? a.h + static_cast<size_t>(pslot[s]) * K + e0
+    const int ps = s < a.k ? t * a.k + s : a.T * a.k + t;
+    const bool ok = job < njobs && e0 < K;
+    const float* src = ok ? a.h + static_cast<size_t>(ps) * K + e0
                           : reinterpret_cast<const float*>(dummy);
     return *reinterpret_cast<const float4*>(src);
   };
+  float4 hv[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) hv[u] = load_h(wave + 4 * u);
+  if (threadIdx.x < ns) {
+    const int s = threadIdx.x;
+    if (s < a.k) {
+      const SlotRef ref = a.slots[t * a.k + s];
+      dptr[s] = ref.down;
+      dbias[s] = ref.bias;
+      wslot[s] = a.w[t * a.k + s];
+    } else {
+      dptr[s] = static_cast<const uint8_t*>(a.sh_down);
+      dbias[s] = nullptr;
+      wslot[s] = a.sh_gate_vec ? a.shw[t] : 1.0f;
+    }
+  }
+  __syncthreads();
   auto quant_h = [&](int job, const float4& hv) {
     const int s = dpc.div(job), pc = dpc.mod(job, s);
     const bool valid = pc * 256 + 4 * lane < K;
@@ -377,9 +380,6 @@ __global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, D
                        ld + s * (K / 32) + pc * 8);
     }
   };
-  float4 hv[kBatch];
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) hv[u] = load_h(wave + 4 * u);
 #pragma unroll
   for (int i = 0; i < TPG; ++i) {
     const int task = grp + G * i;

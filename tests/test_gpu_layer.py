@@ -135,3 +135,36 @@ def test_layer_copies_identical():
     a = run_layer(dl, xt, 0, 2, copy=0)
     b = run_layer(dl, xt, 0, 2, copy=1)
     assert np.array_equal(a[0], b[0])
+
+
+@pytest.mark.parametrize("name,T", [("qwen3.6-35b-a3b", 1), ("tiny", 1), ("qwen3.6-35b-a3b", 3)])
+def test_expert_ffn_given_routing_decode(name, T):
+    """Caller-given routing on the decode path (the fused expert kernel at one
+    token): repeated and out-of-range ids, an absent expert, shared expert."""
+    cfg = gen.CONFIGS[name] if name == "tiny" else SHRUNK[name]
+    data = gen.make_layer(cfg)
+    x, _ = gen.make_x(cfg, T=T, x_index=11)
+    rng = np.random.default_rng(5)
+    ids = np.stack([rng.choice(cfg.E, cfg.k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[0, -1] = cfg.E  # out of range: contributes nothing
+    w = rng.random((T, cfg.k)).astype(np.float32)
+    present = np.ones(cfg.E, bool)
+    present[ids[0, 0]] = False  # an absent expert
+    dl = DeviceLayer(data, present=present)
+    B = 256
+    qs = torch.empty((T, cfg.H), dtype=torch.int8, device="cuda")
+    d = torch.empty((T, cfg.H // B), dtype=torch.float32, device="cuda")
+    bs = torch.empty((T, cfg.H // 16), dtype=torch.int16, device="cuda")
+    q = M.qact(qs, d, bs, M.MOE_AFMT_Q8_K, T, cfg.H)
+    xt = torch.from_numpy(x).cuda()
+    M.moe_quantize_act_q8k(xt, M.MOE_DTYPE_F32, T, cfg.H, M.MOE_AFMT_Q8_K, q)
+    y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+    ws = dl.workspace(T)
+    for _ in range(2):  # twice: the done flags are cleared per call
+        M.moe_expert_ffn(dl.desc, q, xt, M.MOE_DTYPE_F32, T, torch.from_numpy(ids).cuda(),
+                         torch.from_numpy(w).cuda(), y, ws, ws.numel())
+        torch.cuda.synchronize()
+        L = oracle.Layer(data, present=present)
+        for t in range(T):
+            ref = L.expert_part(x[t], ids[t], w[t])
+            assert rel_err(y[t].cpu().numpy(), ref) <= Y_TOL
