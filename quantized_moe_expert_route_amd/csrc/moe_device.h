@@ -500,8 +500,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // (norm_topk) or over all E, or sigmoid (normalized over the selected when
 // norm_topk), times route_scale. Lane r < k writes rank r to ids_out[r] and
 // w_out[r] (global or LDS). Each lane holds NC candidates (E <= 64 * NC),
-// expert e = lane + 64 * i in register i. Per rank: one 32-bit DPP max of the
-// keys, then ballots find the lowest index holding that key.
+// expert e = lane + 64 * i in register i. Per rank: one 64-bit DPP max of
+// (key, inverted index) pairs.
 // wave_topk_regs takes the logits already in registers (lg[i] = logit of expert
 // lane + 64 i; lanes past E may hold anything).
 template <int NC>
@@ -509,7 +509,6 @@ __device__ __forceinline__ void wave_topk_regs(float (&lg)[NC], const float* sel
                                                int k, int router, int norm_topk,
                                                float route_scale, int* ids_out, float* w_out) {
   const int lane = threadIdx.x & 63;
-  uint32_t key[NC];
   float sb[NC];
   if (sel_bias) {
 #pragma unroll
@@ -518,37 +517,35 @@ __device__ __forceinline__ void wave_topk_regs(float (&lg)[NC], const float* sel
 #pragma unroll
     for (int i = 0; i < NC; ++i) sb[i] = 0.0f;
   }
+  // 64-bit keys: selection key above, inverted expert index below, so keys are
+  // unique and the largest one is the highest key with the lowest index.
+  // 0 is below every real key (an absent or already taken candidate).
+  unsigned long long key[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const bool valid = lane + 64 * i < E;
-    // key 0 is below every real key: an absent (or later removed) candidate
-    key[i] = valid ? float_key(sel_bias ? lg[i] + sb[i] : lg[i]) : 0u;
+    const int e = lane + 64 * i;
+    const bool valid = e < E;
+    const uint32_t k32 = float_key(sel_bias ? lg[i] + sb[i] : lg[i]);
+    key[i] = valid ? (static_cast<unsigned long long>(k32) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e))
+                   : 0ull;
     lg[i] = valid ? lg[i] : -INFINITY;
   }
   int my_id = 0;
   float my_l = -INFINITY;
-  for (int r = 0; r < k; ++r) {
-    uint32_t bk = 0;
+  for (int r = 0; r < k; ++r) {  // branch-free: one wave max per rank
+    unsigned long long best = key[0];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) bk = max(bk, key[i]);
-    const uint32_t kmax = wave_max_u32(bk);
-    // lowest expert index holding kmax: first register i with a hit, then lowest lane
-    int e = -1;
-    float l = 0.0f;
+    for (int i = 1; i < NC; ++i) best = key[i] > best ? key[i] : best;
+    const unsigned long long kmax = wave_max_u64(best);
+    const uint32_t e = 0xFFFFFFFFu - static_cast<uint32_t>(kmax);  // wave-uniform
+    float lv = lg[0];  // the winner's logit: register e / 64 of lane e % 64
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const unsigned long long m = __ballot(key[i] == kmax);
-      if (e < 0 && m != 0ull) {
-        const int ln = __builtin_ctzll(m);
-        e = ln + 64 * i;
-        l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lg[i]), ln));
-        if (lane == ln) key[i] = 0;
-      }
-    }
-    if (lane == r) {
-      my_id = e;
-      my_l = l;
-    }
+    for (int i = 1; i < NC; ++i) lv = (e >> 6) == static_cast<uint32_t>(i) ? lg[i] : lv;
+    const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), e & 63));
+#pragma unroll
+    for (int i = 0; i < NC; ++i) key[i] = key[i] == kmax ? 0ull : key[i];
+    my_id = lane == r ? static_cast<int>(e) : my_id;
+    my_l = lane == r ? l : my_l;
   }
   // weights, one selected expert per lane (lanes >= k hold -inf / 0)
   float w;

@@ -437,17 +437,26 @@ __global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, D
     }
   }
   __syncthreads();
+  // weighted slot outputs, one thread per (row, slot), then the sum over the
+  // slots in slot order (shared expert last)
+  float* part = vals + ns * R * nb;  // [R][ns]
+  for (int i = threadIdx.x; i < R * ns; i += 256) {
+    const int r = i / ns, s = i - r * ns, row = row0 + r;
+    float v = 0.0f;
+    if (row < a.H && dptr[s] != nullptr) {
+      float o = 0.0f;
+      for (int b = 0; b < nb; ++b) o += vals[(s * R + r) * nb + b];
+      if (dbias[s]) o += dbias[s][row];
+      v = wslot[s] * o;
+    }
+    part[i] = v;
+  }
+  __syncthreads();
   for (int r = threadIdx.x; r < R; r += 256) {
     const int row = row0 + r;
     if (row >= a.H) break;
     float acc = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      if (dptr[s] == nullptr) continue;
-      float o = 0.0f;
-      for (int b = 0; b < nb; ++b) o += vals[(s * R + r) * nb + b];
-      if (dbias[s]) o += dbias[s][row];
-      acc += wslot[s] * o;
-    }
+    for (int s = 0; s < ns; ++s) acc += part[r * ns + s];
     a.y[static_cast<size_t>(t) * a.H + row] = acc;
   }
 }
@@ -482,15 +491,16 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* rows, int K, 
   }
 }
 
-// Rows per workgroup and tasks per lane group for a GEMV launch: aim for
-// >= 2 workgroups per CU while keeping every lane group busy.
+// Rows per workgroup and tasks per lane group for a GEMV launch: at least
+// min_wgs workgroups while keeping every lane group busy.
 struct GemvShape { int R, tpg; };
-GemvShape gemv_shape(int rows_total, int nmat, int nb, int lpb, int grid_y, int tpg_max) {
+GemvShape gemv_shape(int rows_total, int nmat, int nb, int lpb, int grid_y, int tpg_max,
+                     int min_wgs) {
   const int G = 256 / lpb;
   int R = (G * tpg_max) / (nmat * nb);
   if (R < 1) R = 1;
   if (R > rows_total) R = rows_total;
-  while (R > 1 && static_cast<long>((rows_total + R - 1) / R) * grid_y < 512) R = (R + 1) / 2;
+  while (R > 1 && static_cast<long>((rows_total + R - 1) / R) * grid_y < min_wgs) R = (R + 1) / 2;
   const int tpg = (nmat * R * nb + G - 1) / G;
   return {R, tpg};
 }
@@ -503,7 +513,7 @@ size_t gateup_lds(const KArgs& a, GemvShape* out) {
   const int P = a.T * a.k + a.T * a.has_shared;
   const int nb = a.H / F::BE;
   const int tpg_max = FMT == FMT_Q6_K ? 4 : 8;
-  GemvShape sh = gemv_shape(a.F, 2, nb, F::LPB, P, tpg_max);
+  GemvShape sh = gemv_shape(a.F, 2, nb, F::LPB, P, tpg_max, 512);
   if (out) *out = sh;
   const bool MX = FMT == FMT_MXFP4;
   return (MX ? 2 * a.H : a.H) + 4 * (a.H / 32) + 2 * (a.H / 16) +
@@ -516,11 +526,11 @@ size_t down_lds(const KArgs& a, GemvShape* out) {
   const int ns = a.k + a.has_shared;
   const int nb = a.F / F::BE;
   const int tpg_max = FMT == FMT_Q6_K ? 4 : 8;
-  GemvShape sh = gemv_shape(a.H, ns, nb, F::LPB, a.T, tpg_max);
+  GemvShape sh = gemv_shape(a.H, ns, nb, F::LPB, a.T, tpg_max, 512);
   if (out) *out = sh;
   const bool MX = FMT == FMT_MXFP4;
   return ns * ((MX ? 2 * a.F : a.F) + 4 * (a.F / 32) + 2 * (a.F / 16)) +
-         4 * static_cast<size_t>(ns * sh.R * nb);
+         4 * static_cast<size_t>(ns * sh.R * nb) + 4 * static_cast<size_t>(ns * sh.R);
 }
 
 template <int FMT, int NC>
