@@ -142,30 +142,6 @@ __device__ __forceinline__ int sum4(int v) {
   return v;
 }
 
-// One step of a DPP max over 64-bit keys; lanes without a source keep their value.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ unsigned long long dpp_max_step(unsigned long long v) {
-  const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-  const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
-  const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
-  const unsigned long long o = (static_cast<unsigned long long>(ohi) << 32) | olo;
-  return o > v ? o : v;
-}
-
-// Max of a 64-bit key over the wave (row_shr 1/2/4/8 inside 16-lane rows, then
-// row_bcast 15/31 across rows; lane 63 ends with the maximum), broadcast to all.
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-  v = dpp_max_step<0x111, 0xF>(v);
-  v = dpp_max_step<0x112, 0xF>(v);
-  v = dpp_max_step<0x114, 0xF>(v);
-  v = dpp_max_step<0x118, 0xF>(v);
-  v = dpp_max_step<0x142, 0xA>(v);
-  v = dpp_max_step<0x143, 0xC>(v);
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
-  return (static_cast<unsigned long long>(hi) << 32) | lo;
-}
-
 // ------------------------------------------------------------ q8 quantization
 // One wave quantizes 256 consecutive values, 4 per lane (lane l: 4l..4l+3), as
 // blocks of B = 256 (one block) or B = 32 (eight blocks of 8 lanes).
@@ -481,9 +457,10 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  // keys are compared as unsigned: use the integer max on DPP-moved values
+  // 0 is the identity of the unsigned max, so lanes without a DPP source may
+  // read 0 (bound_ctrl) and the move folds into one v_max_u32_dpp per step.
 #define MOE_DPP_UMAX(CTRL, RM) \
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, RM, 0xF, false)))
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, RM, 0xF, true)))
   MOE_DPP_UMAX(0x111, 0xF);
   MOE_DPP_UMAX(0x112, 0xF);
   MOE_DPP_UMAX(0x114, 0xF);
@@ -500,8 +477,11 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // (norm_topk) or over all E, or sigmoid (normalized over the selected when
 // norm_topk), times route_scale. Lane r < k writes rank r to ids_out[r] and
 // w_out[r] (global or LDS). Each lane holds NC candidates (E <= 64 * NC),
-// expert e = lane + 64 * i in register i. Per rank: one 64-bit DPP max of
-// (key, inverted index) pairs.
+// expert e = lane + 64 * i in register i.
+// Per rank: one 32-bit DPP max of the order-preserving keys, then one ballot
+// per register; the lowest index among equal keys comes from scalar bit scans
+// of the ballots. The winners' logits are fetched once at the end with lane
+// permutes.
 // wave_topk_regs takes the logits already in registers (lg[i] = logit of expert
 // lane + 64 i; lanes past E may hold anything).
 template <int NC>
@@ -517,36 +497,42 @@ __device__ __forceinline__ void wave_topk_regs(float (&lg)[NC], const float* sel
 #pragma unroll
     for (int i = 0; i < NC; ++i) sb[i] = 0.0f;
   }
-  // 64-bit keys: selection key above, inverted expert index below, so keys are
-  // unique and the largest one is the highest key with the lowest index.
-  // 0 is below every real key (an absent or already taken candidate).
-  unsigned long long key[NC];
+  // 0 is below every key of a finite or infinite logit: it marks absent and
+  // already taken candidates.
+  uint32_t key[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const int e = lane + 64 * i;
-    const bool valid = e < E;
-    const uint32_t k32 = float_key(sel_bias ? lg[i] + sb[i] : lg[i]);
-    key[i] = valid ? (static_cast<unsigned long long>(k32) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e))
-                   : 0ull;
+    const bool valid = lane + 64 * i < E;
+    key[i] = valid ? float_key(sel_bias ? lg[i] + sb[i] : lg[i]) : 0u;
     lg[i] = valid ? lg[i] : -INFINITY;
   }
   int my_id = 0;
-  float my_l = -INFINITY;
-  for (int r = 0; r < k; ++r) {  // branch-free: one wave max per rank
-    unsigned long long best = key[0];
+  for (int r = 0; r < k; ++r) {
+    uint32_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < NC; ++i) best = key[i] > best ? key[i] : best;
-    const unsigned long long kmax = wave_max_u64(best);
-    const uint32_t e = 0xFFFFFFFFu - static_cast<uint32_t>(kmax);  // wave-uniform
-    float lv = lg[0];  // the winner's logit: register e / 64 of lane e % 64
+    for (int i = 1; i < NC; ++i) best = max(best, key[i]);
+    const uint32_t kmax = wave_max_u32(best);
+    // the lowest hit lane of register i is candidate 64 i + lane; no hit
+    // leaves all ones, above every candidate
+    uint32_t e = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 1; i < NC; ++i) lv = (e >> 6) == static_cast<uint32_t>(i) ? lg[i] : lv;
-    const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), e & 63));
+    for (int i = 0; i < NC; ++i) {
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(key[i] == kmax);
+      const uint32_t c = hit ? static_cast<uint32_t>(__builtin_ctzll(hit)) + 64u * i : 0xFFFFFFFFu;
+      e = min(e, c);
+    }
 #pragma unroll
-    for (int i = 0; i < NC; ++i) key[i] = key[i] == kmax ? 0ull : key[i];
+    for (int i = 0; i < NC; ++i) key[i] = static_cast<uint32_t>(lane + 64 * i) == e ? 0u : key[i];
     my_id = lane == r ? static_cast<int>(e) : my_id;
-    my_l = lane == r ? l : my_l;
   }
+  const int my_reg = my_id >> 6, my_lane = my_id & 63;
+  float my_l = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const float v = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * my_lane, __float_as_int(lg[i])));
+    my_l = my_reg == i ? v : my_l;
+  }
+  if (lane >= k) my_l = -INFINITY;
   // weights, one selected expert per lane (lanes >= k hold -inf / 0)
   float w;
   if (router == 0) {

@@ -200,3 +200,50 @@ def test_route_ties_and_zero_input():
         rid = oracle.topk(ref_l, cfg.k)
         assert np.array_equal(ids3[t], rid)
         assert np.abs(w3[t] - oracle.route_weights(ref_l, rid, gen.SOFTMAX, 0)).max() <= 1e-6
+
+
+@pytest.mark.parametrize("E,router", [(256, gen.SOFTMAX), (384, gen.SIGMOID), (1024, gen.SOFTMAX)])
+def test_route_ties_across_registers(E, router):
+    """Exact logit ties between experts held in different registers and lanes of
+    the top-k wave (expert e sits in lane e % 64, register e // 64): the lowest
+    index must win. Checked through the routing entry point, the decode layer
+    (top-k inside the gate/up kernel) and the multi-token layer."""
+    cfg = gen.CONFIGS["qwen3.6-35b-a3b"].with_(name="ties", E=E, k=8, H=512, F=256,
+                                               router=router, norm_topk=1)
+    data = gen.make_layer(cfg, experts=[])
+    W = data.w_router
+    top = [5, 69, 133, 197]            # one lane, four registers
+    for e in top[1:]:
+        W[e] = W[top[0]]
+    W[70] = W[6]                       # lane 6, registers 1 and 0
+    W[E - 1] = W[2]                    # last expert ties with an early one
+    data.w_router = np.ascontiguousarray(W)
+    T = 6
+    x, _ = gen.make_x(cfg, T=T)
+    x[0] = 0.0                                         # every logit equal
+    x[1] = W[5] / np.linalg.norm(W[5]) * 10            # the four tied rows on top
+    x[2] = W[6] / np.linalg.norm(W[6]) * 10
+    x[3] = W[2] / np.linalg.norm(W[2]) * 10
+    xt = torch.from_numpy(x).cuda()
+    refs = [oracle.topk(oracle.router_logits(data.w_router, x[t]), cfg.k) for t in range(T)]
+    assert list(refs[0]) == list(range(8))
+    assert list(refs[1][:4]) == top
+    assert list(refs[2][:2]) == [6, 70]
+    assert list(refs[3][:2]) == [2, E - 1]
+    dl = DeviceLayer(data)
+    ids, _, _ = _route(dl, xt, M.MOE_DTYPE_F32, T, logits=False)
+    say(f"ties E={E}: route entry point")
+    for t in range(T):
+        assert np.array_equal(ids[t], refs[t]), ("route", t, ids[t], refs[t])
+    for Tl in (1, T):                  # decode path per token, then the grouped path
+        y = torch.empty((Tl, cfg.H), dtype=torch.float32, device="cuda")
+        idl = torch.empty((Tl, cfg.k), dtype=torch.int32, device="cuda")
+        wl = torch.empty((Tl, cfg.k), dtype=torch.float32, device="cuda")
+        ws = dl.workspace(Tl)
+        for t0 in range(0, T, Tl):
+            M.moe_layer_forward(dl.desc, xt[t0:t0 + Tl].contiguous(), M.MOE_DTYPE_F32, Tl, y,
+                                idl, wl, ws, ws.numel())
+            torch.cuda.synchronize()
+            got = idl.cpu().numpy()
+            for i in range(Tl):
+                assert np.array_equal(got[i], refs[t0 + i]), ("layer", Tl, t0 + i, got[i])
