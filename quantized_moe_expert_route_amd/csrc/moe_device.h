@@ -53,6 +53,18 @@ __device__ __forceinline__ float load_x(const void* x, int dtype, size_t i) {
                     : bf16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
 }
 
+// Four consecutive x values (i a multiple of 4) with one load.
+__device__ __forceinline__ void load_x4(const void* x, int dtype, size_t i, float (&v)[4]) {
+  if (dtype == 0) {
+    const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + i);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + i);
+    v[0] = bf16_bits_to_f32(b.x & 0xFFFF); v[1] = bf16_bits_to_f32(b.x >> 16);
+    v[2] = bf16_bits_to_f32(b.y & 0xFFFF); v[3] = bf16_bits_to_f32(b.y >> 16);
+  }
+}
+
 __device__ __forceinline__ float half_bits_to_f32(uint32_t bits) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }
@@ -73,10 +85,18 @@ __device__ __forceinline__ int sum8(int v) {
 // row_bcast 15/31 carry row results upward; lane 63 ends with the full value,
 // which readlane makes wave-uniform. For sums, lanes without a source add 0;
 // for max, they keep their own value.
+// Where 0 is the identity (sums, maxima of non-negative values) lanes without a
+// source read 0 (bound_ctrl), which lets the move fold into the DPP form of the
+// arithmetic instruction.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_add_f(float v) {
-  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true);
   return v + __int_as_float(o);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_amax_f(float v) {  // v >= 0
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true);
+  return fmaxf(v, __int_as_float(o));
 }
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_max_f(float v) {
@@ -114,6 +134,17 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Max of non-negative values over the wave.
+__device__ __forceinline__ float wave_amax(float v) {
+  v = dpp_amax_f<0x111, 0xF>(v);
+  v = dpp_amax_f<0x112, 0xF>(v);
+  v = dpp_amax_f<0x114, 0xF>(v);
+  v = dpp_amax_f<0x118, 0xF>(v);
+  v = dpp_amax_f<0x142, 0xA>(v);
+  v = dpp_amax_f<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
   v = dpp_add_d<0x111, 0xF>(v);
   v = dpp_add_d<0x112, 0xF>(v);
@@ -127,11 +158,12 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
 }
 
-// Max over aligned groups of 8 lanes (every lane of the group gets it).
+// Max of non-negative values over aligned groups of 8 lanes (every lane of the
+// group gets it; quad_perm and row_half_mirror give every lane a source).
 __device__ __forceinline__ float max8(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true)));
   return v;
 }
 
@@ -152,7 +184,7 @@ template <int B>
 __device__ __forceinline__ float quant_wave_q(const float v[4], int q[4]) {
   float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
   static_assert(B == 256 || B == 32, "block of 256 (one per wave) or 32 (8 lanes)");
-  amax = B == 256 ? wave_max(amax) : max8(amax);
+  amax = B == 256 ? wave_amax(amax) : max8(amax);
   if (amax == 0.0f) {
     q[0] = q[1] = q[2] = q[3] = 0;
     return 0.0f;
@@ -178,7 +210,7 @@ __device__ __forceinline__ void quant_wave_batch(const float4 (&hv)[NJ], int (&q
   for (int j = 0; j < NJ; ++j)
     am[j] = fmaxf(fmaxf(fabsf(hv[j].x), fabsf(hv[j].y)), fmaxf(fabsf(hv[j].z), fabsf(hv[j].w)));
   if constexpr (B == 256) {
-#define MOE_BSTEP(CTRL, RM) _Pragma("unroll") for (int j = 0; j < NJ; ++j) am[j] = dpp_max_f<CTRL, RM>(am[j]);
+#define MOE_BSTEP(CTRL, RM) _Pragma("unroll") for (int j = 0; j < NJ; ++j) am[j] = dpp_amax_f<CTRL, RM>(am[j]);
     MOE_BSTEP(0x111, 0xF) MOE_BSTEP(0x112, 0xF) MOE_BSTEP(0x114, 0xF) MOE_BSTEP(0x118, 0xF)
     MOE_BSTEP(0x142, 0xA) MOE_BSTEP(0x143, 0xC)
 #undef MOE_BSTEP
@@ -471,19 +503,75 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
-// Top-k of one token by one wave (all 64 lanes must call it). Rank order is
-// (key descending, index ascending) with key = logit (+ selection bias, one
-// fp32 add). Weights come from the unbiased logits: softmax over the selected
+// Top-k selection over order-preserving keys, expert e = lane + 64 i held in
+// register i of every lane. key 0 marks an absent candidate (every real key
+// is above it). On return rank[i] is the rank (0 = first) of that candidate,
+// or -1 when it is not among the k selected. Rank order is key descending,
+// index ascending.
+//
+// Fast path: k rounds of one 32-bit wave max each; every candidate equal to
+// the round's maximum takes rank r and leaves. That is exact when every
+// round's maximum is unique, which holds exactly when k candidates end up
+// ranked (each round ranks at least one). Otherwise (equal keys) the exact
+// path reruns the selection with the lowest index taken first among equal
+// keys: per round the lowest hit lane of each register's ballot gives a
+// candidate index, and the smallest of those wins.
+template <int NC>
+__device__ __forceinline__ void topk_select(const uint32_t (&key0)[NC], int k, int (&rank)[NC]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) { key[i] = key0[i]; rank[i] = -1; }
+  for (int r = 0; r < k; ++r) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < NC; ++i) best = max(best, key[i]);
+    const uint32_t kmax = wave_max_u32(best);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const bool hit = key[i] == kmax;
+      rank[i] = hit ? r : rank[i];
+      key[i] = hit ? 0u : key[i];
+    }
+  }
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(rank[i] >= 0));
+  if (n == k) return;  // wave-uniform
+#pragma unroll
+  for (int i = 0; i < NC; ++i) { key[i] = key0[i]; rank[i] = -1; }
+  for (int r = 0; r < k; ++r) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < NC; ++i) best = max(best, key[i]);
+    const uint32_t kmax = wave_max_u32(best);
+    // lowest hit lane of register i is candidate 64 i + lane; no hit leaves
+    // all ones, above every candidate
+    uint32_t e = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(key[i] == kmax);
+      const uint32_t c = hit ? static_cast<uint32_t>(__builtin_ctzll(hit)) + 64u * i : 0xFFFFFFFFu;
+      e = min(e, c);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const bool win = static_cast<uint32_t>(lane + 64 * i) == e;
+      rank[i] = win ? r : rank[i];
+      key[i] = win ? 0u : key[i];
+    }
+  }
+}
+
+// Top-k of one token by one wave (all 64 lanes must call it). Selection key =
+// logit (+ selection bias, one fp32 add); rank order as in topk_select.
+// Weights come from the unbiased logits: softmax over the selected
 // (norm_topk) or over all E, or sigmoid (normalized over the selected when
-// norm_topk), times route_scale. Lane r < k writes rank r to ids_out[r] and
-// w_out[r] (global or LDS). Each lane holds NC candidates (E <= 64 * NC),
-// expert e = lane + 64 * i in register i.
-// Per rank: one 32-bit DPP max of the order-preserving keys, then one ballot
-// per register; the lowest index among equal keys comes from scalar bit scans
-// of the ballots. The winners' logits are fetched once at the end with lane
-// permutes.
+// norm_topk), times route_scale. Rank r goes to ids_out[r] (written by the
+// lane that holds that expert) and w_out[r] (lane r); global or LDS.
 // wave_topk_regs takes the logits already in registers (lg[i] = logit of expert
-// lane + 64 i; lanes past E may hold anything).
+// lane + 64 i; lanes past E may hold anything). NC candidates per lane,
+// E <= 64 NC.
 template <int NC>
 __device__ __forceinline__ void wave_topk_regs(float (&lg)[NC], const float* sel_bias, int E,
                                                int k, int router, int norm_topk,
@@ -497,8 +585,6 @@ __device__ __forceinline__ void wave_topk_regs(float (&lg)[NC], const float* sel
 #pragma unroll
     for (int i = 0; i < NC; ++i) sb[i] = 0.0f;
   }
-  // 0 is below every key of a finite or infinite logit: it marks absent and
-  // already taken candidates.
   uint32_t key[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
@@ -506,34 +592,22 @@ __device__ __forceinline__ void wave_topk_regs(float (&lg)[NC], const float* sel
     key[i] = valid ? float_key(sel_bias ? lg[i] + sb[i] : lg[i]) : 0u;
     lg[i] = valid ? lg[i] : -INFINITY;
   }
-  int my_id = 0;
-  for (int r = 0; r < k; ++r) {
-    uint32_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < NC; ++i) best = max(best, key[i]);
-    const uint32_t kmax = wave_max_u32(best);
-    // the lowest hit lane of register i is candidate 64 i + lane; no hit
-    // leaves all ones, above every candidate
-    uint32_t e = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const unsigned long long hit = __builtin_amdgcn_ballot_w64(key[i] == kmax);
-      const uint32_t c = hit ? static_cast<uint32_t>(__builtin_ctzll(hit)) + 64u * i : 0xFFFFFFFFu;
-      e = min(e, c);
-    }
-#pragma unroll
-    for (int i = 0; i < NC; ++i) key[i] = static_cast<uint32_t>(lane + 64 * i) == e ? 0u : key[i];
-    my_id = lane == r ? static_cast<int>(e) : my_id;
-  }
-  const int my_reg = my_id >> 6, my_lane = my_id & 63;
-  float my_l = -INFINITY;
+  int rank[NC];
+  topk_select<NC>(key, k, rank);
+  // ids and the selected logits in rank order; lane r < k then holds rank r
+  __shared__ float s_rank_l[16][16];
+  float* rl = s_rank_l[(threadIdx.x >> 6) & 15];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const float v = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * my_lane, __float_as_int(lg[i])));
-    my_l = my_reg == i ? v : my_l;
+    if (rank[i] >= 0) {
+      ids_out[rank[i]] = lane + 64 * i;
+      rl[rank[i]] = lg[i];
+    }
   }
-  if (lane >= k) my_l = -INFINITY;
-  // weights, one selected expert per lane (lanes >= k hold -inf / 0)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float my_l = lane < k ? rl[lane] : -INFINITY;
   float w;
   if (router == 0) {
     float mx, z;
@@ -557,10 +631,7 @@ __device__ __forceinline__ void wave_topk_regs(float (&lg)[NC], const float* sel
     const float sg = lane < k ? 1.0f / (1.0f + expf(-my_l)) : 0.0f;
     w = norm_topk ? sg / wave_sum(sg) : sg;
   }
-  if (lane < k) {
-    ids_out[lane] = my_id;
-    w_out[lane] = w * route_scale;
-  }
+  if (lane < k) w_out[lane] = w * route_scale;
 }
 
 template <int NC>

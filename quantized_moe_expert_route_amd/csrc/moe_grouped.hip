@@ -665,9 +665,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
     const int t = job / pieces, pc = job - t * pieces;
     if (t >= a.T) return;
     float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[i] = load_x(a.x, a.x_dtype, static_cast<size_t>(t) * a.H + pc * 256 + 4 * lane + i);
+    load_x4(a.x, a.x_dtype, static_cast<size_t>(t) * a.H + pc * 256 + 4 * lane, v);
     const size_t base = static_cast<size_t>(t) * a.H + pc * 256;
     quant_wave<256>(v, true, lane, a.xqs + base, a.xd + base / 256, a.xbs + base / 16);
     return;

@@ -50,9 +50,9 @@ __global__ __launch_bounds__(64) void k_quant(const void* x, int dtype, int H, i
   const int e0 = blockIdx.x * 256 + 4 * lane;
   const bool valid = e0 < H;
   float v[4];
+  load_x4(x, dtype, static_cast<size_t>(t) * H + (valid ? e0 : 0), v);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    v[i] = valid ? load_x(x, dtype, static_cast<size_t>(t) * H + e0 + i) : 0.0f;
+  for (int i = 0; i < 4; ++i) v[i] = valid ? v[i] : 0.0f;
   const size_t base = static_cast<size_t>(t) * H + blockIdx.x * 256;
   quant_wave<B>(v, valid, lane, qs + base, d + base / B, bs ? bs + base / 16 : nullptr);
 }
@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void k_shared_gate(KArgs a) {
   __shared__ double red[4];
   const int t = blockIdx.x;
   double acc = 0.0;
+#pragma unroll 8
   for (int h = threadIdx.x; h < a.H; h += 256)
     acc += static_cast<double>(a.sh_gate_vec[h]) *
            static_cast<double>(load_x(a.x, a.x_dtype, static_cast<size_t>(t) * a.H + h));
@@ -83,7 +84,11 @@ __global__ __launch_bounds__(256) void k_shared_gate(KArgs a) {
 // logit of one expert for every token (TT at a time); wave E (if present) the
 // shared-expert gate; the remaining waves quantize x in 256-value pieces when
 // `quant` is set. Wave 0 also clears n_clear counters for the next kernel.
-template <int TT>
+// Each pass over the row issues all of its W_r and x loads (U float4 pieces
+// per lane and token) before the first multiply, so a row of up to 256 U
+// values costs one memory round trip. Pieces past H read a valid address and
+// are zeroed. XBF: x is bf16 (else fp32).
+template <int TT, int U, bool XBF>
 __global__ __launch_bounds__(64) void k_router(KArgs a, int quant, int n_clear) {
   const int lane = threadIdx.x, e = blockIdx.x;
   if (e == 0)
@@ -96,9 +101,9 @@ __global__ __launch_bounds__(64) void k_router(KArgs a, int quant, int n_clear) 
     const int e0 = pc * 256 + 4 * lane;
     const bool valid = e0 < a.H;
     float v[4];
+    load_x4(a.x, XBF ? 1 : 0, static_cast<size_t>(t) * a.H + (valid ? e0 : 0), v);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[i] = valid ? load_x(a.x, a.x_dtype, static_cast<size_t>(t) * a.H + e0 + i) : 0.0f;
+    for (int i = 0; i < 4; ++i) v[i] = valid ? v[i] : 0.0f;
     const size_t base = static_cast<size_t>(t) * a.H + pc * 256;
     if (a.fmt_gu == FMT_MXFP4)
       quant_wave<32>(v, valid, lane, a.xqs + base, a.xd + base / 32, nullptr);
@@ -111,25 +116,44 @@ __global__ __launch_bounds__(64) void k_router(KArgs a, int quant, int n_clear) 
     double acc[TT];
 #pragma unroll
     for (int i = 0; i < TT; ++i) acc[i] = 0.0;
-    for (int h = 4 * lane; h < a.H; h += 256) {
-      const float4 wv = *reinterpret_cast<const float4*>(wrow + h);
+    for (int hb = 0; hb < a.H; hb += 256 * U) {
+      float4 wv[U];
+      float xv[TT][U][4];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int h = hb + 256 * u + 4 * lane;
+        wv[u] = *reinterpret_cast<const float4*>(wrow + (h < a.H ? h : 0));
+      }
 #pragma unroll
       for (int i = 0; i < TT; ++i) {
-        if (t0 + i < a.T) {
-          const size_t xo = static_cast<size_t>(t0 + i) * a.H + h;
-          float xv[4];
-          if (a.x_dtype == 0) {
-            const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + xo);
-            xv[0] = f.x; xv[1] = f.y; xv[2] = f.z; xv[3] = f.w;
-          } else {
+        const int t = min(t0 + i, a.T - 1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int h = hb + 256 * u + 4 * lane;
+          const size_t xo = static_cast<size_t>(t) * a.H + (h < a.H ? h : 0);
+          if constexpr (XBF) {
             const uint2 bb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.x) + xo);
-            xv[0] = bf16_bits_to_f32(bb.x & 0xFFFF); xv[1] = bf16_bits_to_f32(bb.x >> 16);
-            xv[2] = bf16_bits_to_f32(bb.y & 0xFFFF); xv[3] = bf16_bits_to_f32(bb.y >> 16);
+            xv[i][u][0] = bf16_bits_to_f32(bb.x & 0xFFFF); xv[i][u][1] = bf16_bits_to_f32(bb.x >> 16);
+            xv[i][u][2] = bf16_bits_to_f32(bb.y & 0xFFFF); xv[i][u][3] = bf16_bits_to_f32(bb.y >> 16);
+          } else {
+            const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + xo);
+            xv[i][u][0] = f.x; xv[i][u][1] = f.y; xv[i][u][2] = f.z; xv[i][u][3] = f.w;
           }
-          acc[i] = fma(static_cast<double>(wv.x), static_cast<double>(xv[0]), acc[i]);
-          acc[i] = fma(static_cast<double>(wv.y), static_cast<double>(xv[1]), acc[i]);
-          acc[i] = fma(static_cast<double>(wv.z), static_cast<double>(xv[2]), acc[i]);
-          acc[i] = fma(static_cast<double>(wv.w), static_cast<double>(xv[3]), acc[i]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = hb + 256 * u + 4 * lane < a.H;
+        const double w0 = ok ? static_cast<double>(wv[u].x) : 0.0;
+        const double w1 = ok ? static_cast<double>(wv[u].y) : 0.0;
+        const double w2 = ok ? static_cast<double>(wv[u].z) : 0.0;
+        const double w3 = ok ? static_cast<double>(wv[u].w) : 0.0;
+#pragma unroll
+        for (int i = 0; i < TT; ++i) {
+          acc[i] = fma(w0, static_cast<double>(xv[i][u][0]), acc[i]);
+          acc[i] = fma(w1, static_cast<double>(xv[i][u][1]), acc[i]);
+          acc[i] = fma(w2, static_cast<double>(xv[i][u][2]), acc[i]);
+          acc[i] = fma(w3, static_cast<double>(xv[i][u][3]), acc[i]);
         }
       }
     }
@@ -602,7 +626,13 @@ hipError_t launch_shared_gate(const KArgs& a, hipStream_t s) {
 hipError_t launch_router(const KArgs& a, bool quant, int n_clear, hipStream_t s, Ev ev) {
   const int nq = quant ? a.T * ((a.H + 255) / 256) : 0;
   dim3 grid(a.E + (a.sh_gate_vec ? 1 : 0) + nq);
-  return launch(k_router<4>, grid, 64, 0, s, ev, a, quant ? 1 : 0, n_clear);
+  const int q = quant ? 1 : 0;
+  if (a.T == 1) {
+    if (a.x_dtype) return launch(k_router<1, 8, true>, grid, 64, 0, s, ev, a, q, n_clear);
+    return launch(k_router<1, 8, false>, grid, 64, 0, s, ev, a, q, n_clear);
+  }
+  if (a.x_dtype) return launch(k_router<4, 4, true>, grid, 64, 0, s, ev, a, q, n_clear);
+  return launch(k_router<4, 4, false>, grid, 64, 0, s, ev, a, q, n_clear);
 }
 
 hipError_t launch_topk(const KArgs& a, hipStream_t s) {
