@@ -327,11 +327,15 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
 }
 
 // ---------------------------------------------------------------- down GEMV
-// grid (ceil(H / R), T), block 256. For each present slot of token t (and the
-// shared expert): q8(h) staged into LDS, down rows [row0, row0 + R), then
+// grid (ceil(H / R), T), block 512. For each present slot of token t (and the
+// shared expert): down rows [row0, row0 + R) against q8(h), then
 // y = sum_slot w * (o + b_down) + shw * o_shared in slot order.
-template <int FMT, int TPG>
-__global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, Div dpc) {
+// Waves 0-3 stream the down rows (TPG block tasks per lane) and multiply them;
+// waves 4-7 meanwhile quantize h into LDS (fp32 recipe), so the VALU work of
+// the quantization overlaps the weight stream instead of queueing behind the
+// load issue.
+template <int FMT, int TPG, int JB>
+__global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, Div dpc) {
   using F = typename FmtOf<FMT>::T;
   constexpr bool MX = FMT == FMT_MXFP4;
   constexpr int B = MX ? 32 : 256;
@@ -348,23 +352,20 @@ __global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, D
   __shared__ const uint8_t* dptr[17];
   __shared__ const float* dbias[17];
   __shared__ float wslot[17];
-  const int G = 256 / F::LPB;
-  const int grp = threadIdx.x / F::LPB, sub = threadIdx.x % F::LPB;
-  const int total = ns * R * nb;
-  typename F::Raw raw[TPG];
-  // q8 of h for every present slot (fp32 recipe). Waves take 256-value pieces
-  // ("jobs"). h rows sit at fixed places (pair t k + s, shared T k + t), so the
-  // first kBatch jobs of each wave are loaded before the slot table is even
-  // read (an absent slot's row is loaded and ignored); the weight loads follow
-  // the slot table, and quantizing waits only for h (memory counters complete
-  // in order) while the weights stay in flight.
-  constexpr int kBatch = 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int pieces = (K + 255) / 256;
-  const int njobs = ns * pieces;
-  // loads are unconditional (idle jobs read a dummy workspace region) so the
+  const bool streamer = wave < 4;  // wave-uniform role
+  const int G = 256 / F::LPB;
+  const int grp = threadIdx.x / F::LPB, sub = threadIdx.x % F::LPB;  // streamers only
+  const int total = ns * R * nb;
+  // loads are unconditional (idle ones read a dummy workspace region) so the
   // compiler can count outstanding loads
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.counters);
+  // Quantizer jobs: 256-value pieces of h. h rows sit at fixed places (pair
+  // t k + s, shared T k + t), so a quantizer wave loads its first JB jobs
+  // before the slot table is read (an absent slot's row is loaded and ignored).
+  const int qw = wave - 4;
+  const int pieces = (K + 255) / 256;
+  const int njobs = ns * pieces;
   auto load_h = [&](int job) {
     const int jc = min(job, njobs - 1);
     const int s = dpc.div(jc), e0 = dpc.mod(jc, s) * 256 + 4 * lane;
@@ -374,9 +375,11 @@ __global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, D
                           : reinterpret_cast<const float*>(dummy);
     return *reinterpret_cast<const float4*>(src);
   };
-  float4 hv[kBatch];
+  float4 hv[JB];
+  if (!streamer) {
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) hv[u] = load_h(wave + 4 * u);
+    for (int u = 0; u < JB; ++u) hv[u] = load_h(qw + 4 * u);
+  }
   if (threadIdx.x < ns) {
     const int s = threadIdx.x;
     if (s < a.k) {
@@ -391,40 +394,52 @@ __global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, D
     }
   }
   __syncthreads();
-  auto quant_h = [&](int job, const float4& hv) {
-    const int s = dpc.div(job), pc = dpc.mod(job, s);
-    const bool valid = pc * 256 + 4 * lane < K;
-    const float v[4] = {hv.x, hv.y, hv.z, hv.w};
-    if constexpr (!MX) {
-      quant_wave<B>(v, valid, lane, reinterpret_cast<int8_t*>(p_act + s * act_bytes) + pc * 256,
-                    ld + s * (K / 32) + pc, lbs + s * (K / 16) + pc * 16);
-    } else {
-      quant_wave_pairs(v, valid, lane,
-                       reinterpret_cast<half2_t*>(p_act + s * act_bytes) + pc * 128,
-                       ld + s * (K / 32) + pc * 8);
+  // present slots as a wave-uniform bit mask (ns <= 17)
+  const uint32_t present = static_cast<uint32_t>(
+      __builtin_amdgcn_ballot_w64(lane < ns && dptr[min(lane, ns - 1)] != nullptr));
+  typename F::Raw raw[TPG];
+  if (streamer) {
+    // all slot-pointer reads first, then all weight loads
+    const uint8_t* wp[TPG];
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+      const int tc = min(grp + G * i, total - 1);
+      wp[i] = dptr[dR.div(dnb.div(tc))];
     }
-  };
 #pragma unroll
-  for (int i = 0; i < TPG; ++i) {
-    const int task = grp + G * i;
-    const int tc = min(task, total - 1);
-    const uint32_t q1 = dnb.div(tc), q2 = dR.div(q1);
-    const int b = dnb.mod(tc, q1), r = dR.mod(q1, q2), s = q2;
-    const bool ok = task < total && row0 + r < a.H && dptr[s] != nullptr;
-    F::load(raw[i], ok ? dptr[s] + static_cast<size_t>(row0 + r) * a.stride_down +
-                             static_cast<size_t>(b) * F::BB
-                       : dummy, sub);
-  }
-  {
-    int q[kBatch][4];
-    float dv[kBatch];
+    for (int i = 0; i < TPG; ++i) {
+      const int task = grp + G * i;
+      const int tc = min(task, total - 1);
+      const uint32_t q1 = dnb.div(tc), q2 = dR.div(q1);
+      const int b = dnb.mod(tc, q1), r = dR.mod(q1, q2);
+      const bool ok = task < total && row0 + r < a.H && wp[i] != nullptr;
+      F::load(raw[i], ok ? wp[i] + static_cast<size_t>(row0 + r) * a.stride_down +
+                               static_cast<size_t>(b) * F::BB
+                         : dummy, sub);
+    }
+  } else {
+    auto quant_h = [&](int job, const float4& hv1) {
+      const int s = dpc.div(job), pc = dpc.mod(job, s);
+      const bool valid = pc * 256 + 4 * lane < K;
+      const float v[4] = {hv1.x, hv1.y, hv1.z, hv1.w};
+      if constexpr (!MX) {
+        quant_wave<B>(v, valid, lane, reinterpret_cast<int8_t*>(p_act + s * act_bytes) + pc * 256,
+                      ld + s * (K / 32) + pc, lbs + s * (K / 16) + pc * 16);
+      } else {
+        quant_wave_pairs(v, valid, lane,
+                         reinterpret_cast<half2_t*>(p_act + s * act_bytes) + pc * 128,
+                         ld + s * (K / 32) + pc * 8);
+      }
+    };
     if constexpr (!MX) {
-      quant_wave_batch<B, kBatch>(hv, q, dv);
+      int q[JB][4];
+      float dv[JB];
+      quant_wave_batch<B, JB>(hv, q, dv);
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int job = wave + 4 * u;  // wave-uniform
+      for (int u = 0; u < JB; ++u) {
+        const int job = qw + 4 * u;  // wave-uniform
         const int js = dpc.div(job);
-        if (job < njobs && dptr[js] != nullptr) {
+        if (job < njobs && ((present >> js) & 1u)) {
           const int s = js, pc = dpc.mod(job, js);
           if (pc * 256 + 4 * lane < K) {
             reinterpret_cast<uint32_t*>(p_act + s * act_bytes + pc * 256)[lane] = pack_q8x4(q[u]);
@@ -437,37 +452,39 @@ __global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, D
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int job = wave + 4 * u;
-        if (job < njobs && dptr[dpc.div(job)] != nullptr) quant_h(job, hv[u]);
+      for (int u = 0; u < JB; ++u) {
+        const int job = qw + 4 * u;
+        if (job < njobs && ((present >> dpc.div(job)) & 1u)) quant_h(job, hv[u]);
       }
     }
-  }
-  for (int job = wave + 4 * kBatch; job < njobs; job += 4) {  // slots beyond the first batch
-    const float4 v = load_h(job);
-    if (dptr[dpc.div(job)] != nullptr) quant_h(job, v);
+    for (int job = qw + 4 * JB; job < njobs; job += 4) {  // jobs beyond the first batch
+      const float4 v = load_h(job);
+      if ((present >> dpc.div(job)) & 1u) quant_h(job, v);
+    }
   }
   __syncthreads();
+  if (streamer) {
 #pragma unroll
-  for (int i = 0; i < TPG; ++i) {
-    const int task = grp + G * i;
-    const uint32_t q1 = dnb.div(task), q2 = dR.div(q1);
-    const int b = dnb.mod(task, q1), r = dR.mod(q1, q2), s = q2;
-    if (task < total && row0 + r < a.H && dptr[s] != nullptr) {
-      ActView av{reinterpret_cast<const int8_t*>(p_act + s * act_bytes), ld + s * (K / 32),
-                 lbs + s * (K / 16), reinterpret_cast<const half2_t*>(p_act + s * act_bytes)};
-      const float v = block_value<F>(raw[i], av, b, sub);
-      if (sub == 0) vals[(s * R + r) * nb + b] = v;
+    for (int i = 0; i < TPG; ++i) {
+      const int task = grp + G * i;
+      const uint32_t q1 = dnb.div(task), q2 = dR.div(q1);
+      const int b = dnb.mod(task, q1), r = dR.mod(q1, q2), s = q2;
+      if (task < total && row0 + r < a.H && ((present >> s) & 1u)) {
+        ActView av{reinterpret_cast<const int8_t*>(p_act + s * act_bytes), ld + s * (K / 32),
+                   lbs + s * (K / 16), reinterpret_cast<const half2_t*>(p_act + s * act_bytes)};
+        const float v = block_value<F>(raw[i], av, b, sub);
+        if (sub == 0) vals[(s * R + r) * nb + b] = v;
+      }
     }
   }
   __syncthreads();
   // weighted slot outputs, one thread per (row, slot), then the sum over the
   // slots in slot order (shared expert last)
   float* part = vals + ns * R * nb;  // [R][ns]
-  for (int i = threadIdx.x; i < R * ns; i += 256) {
+  for (int i = threadIdx.x; i < R * ns; i += 512) {
     const int r = i / ns, s = i - r * ns, row = row0 + r;
     float v = 0.0f;
-    if (row < a.H && dptr[s] != nullptr) {
+    if (row < a.H && ((present >> s) & 1u)) {
       float o = 0.0f;
       for (int b = 0; b < nb; ++b) o += vals[(s * R + r) * nb + b];
       if (dbias[s]) o += dbias[s][row];
@@ -476,7 +493,7 @@ __global__ __launch_bounds__(256) void k_down(KArgs a, int R, Div dnb, Div dR, D
     part[i] = v;
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < R; r += 256) {
+  for (int r = threadIdx.x; r < R; r += 512) {
     const int row = row0 + r;
     if (row >= a.H) break;
     float acc = 0.0f;
@@ -550,7 +567,14 @@ size_t down_lds(const KArgs& a, GemvShape* out) {
   const int ns = a.k + a.has_shared;
   const int nb = a.F / F::BE;
   const int tpg_max = FMT == FMT_Q6_K ? 4 : 8;
-  GemvShape sh = gemv_shape(a.H, ns, nb, F::LPB, a.T, tpg_max, 512);
+  // Every workgroup re-quantizes its token's h (VALU work), so the target is
+  // one workgroup per compute unit (R = ceil(H T / 256)), as far as the cap
+  // on loads per lane allows.
+  const int G = 256 / F::LPB;
+  const int per_token = max(1, 256 / max(a.T, 1));
+  int R = min((G * tpg_max) / (ns * nb), (a.H + per_token - 1) / per_token);
+  R = max(1, min(R, a.H));
+  GemvShape sh{R, (ns * R * nb + G - 1) / G};
   if (out) *out = sh;
   const bool MX = FMT == FMT_MXFP4;
   return ns * ((MX ? 2 * a.F : a.F) + 4 * (a.F / 32) + 2 * (a.F / 16)) +
@@ -580,18 +604,29 @@ hipError_t gateup_dispatch(const KArgs& a, int routing_given, hipStream_t s, Ev 
   return gateup_dispatch_nc<FMT, 16>(a, routing_given, s, ev);
 }
 
+// h pieces quantized in lock-step per wave: 2, 5 or 8 (more run one at a time).
+template <int FMT, int TPG>
+hipError_t down_jb(int jobs_per_wave, dim3 grid, size_t lds, hipStream_t s, Ev ev, const KArgs& a,
+                   int R, Div dnb, Div dR, Div dpc) {
+  if (jobs_per_wave <= 2) return launch(k_down<FMT, TPG, 2>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
+  if (jobs_per_wave <= 5) return launch(k_down<FMT, TPG, 5>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
+  return launch(k_down<FMT, TPG, 8>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
+}
+
 template <int FMT>
 hipError_t down_dispatch(const KArgs& a, hipStream_t s, Ev ev) {
   GemvShape sh;
   const size_t lds = down_lds<FMT>(a, &sh);
   dim3 grid((a.H + sh.R - 1) / sh.R, a.T);
   using F = typename FmtOf<FMT>::T;
-  const Div dnb = Div::make(a.F / F::BE), dR = Div::make(sh.R), dpc = Div::make((a.F + 255) / 256);
+  const int pieces = (a.F + 255) / 256;
+  const Div dnb = Div::make(a.F / F::BE), dR = Div::make(sh.R), dpc = Div::make(pieces);
+  const int jobs_per_wave = ((a.k + a.has_shared) * pieces + 3) / 4;
   switch (tpg_bucket(sh.tpg)) {
-    case 1: return launch(k_down<FMT, 1>, grid, 256, lds, s, ev, a, sh.R, dnb, dR, dpc);
-    case 2: return launch(k_down<FMT, 2>, grid, 256, lds, s, ev, a, sh.R, dnb, dR, dpc);
-    case 4: return launch(k_down<FMT, 4>, grid, 256, lds, s, ev, a, sh.R, dnb, dR, dpc);
-    default: return launch(k_down<FMT, 8>, grid, 256, lds, s, ev, a, sh.R, dnb, dR, dpc);
+    case 1: return down_jb<FMT, 1>(jobs_per_wave, grid, lds, s, ev, a, sh.R, dnb, dR, dpc);
+    case 2: return down_jb<FMT, 2>(jobs_per_wave, grid, lds, s, ev, a, sh.R, dnb, dR, dpc);
+    case 4: return down_jb<FMT, 4>(jobs_per_wave, grid, lds, s, ev, a, sh.R, dnb, dR, dpc);
+    default: return down_jb<FMT, 8>(jobs_per_wave, grid, lds, s, ev, a, sh.R, dnb, dR, dpc);
   }
 }
 
