@@ -281,39 +281,6 @@ constexpr int kStB = kStA + 16 * 256;    // 16 rows x 32 B of 16-element sums (+
 constexpr int kStD = kStB + 1024;        // 16 block scales (+ pad)
 constexpr int kStBytes = kStD + 256;     // 23808 B per slot
 
-#define MOE_LDS __attribute__((address_space(3)))
-// Direct global->LDS loads. Written as inline asm so that the compiler does not
-// track their LDS writes: its tracking loses count across the ring's loop and
-// would wait for every slot load in flight before any LDS read. Completion is
-// ordered by the explicit vmcnt waits and workgroup barriers of the ring. (The
-// compiler's own vmcnt waits for other loads stay sufficient: loads complete
-// in issue order, so extra ops it does not see only make them stronger.)
-// LDS byte address of a (wave-uniform) pointer into a __shared__ array, as an
-// SGPR value for M0.
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* l) {
-  return __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const MOE_LDS uint8_t*)(l))));
-}
-__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* l) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_addr(l))
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* l) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(g), "s"(lds_addr(l))
-               : "memory", "m0");
-}
-// Wait until at most N vector memory operations of this wave are outstanding
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
-// left at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // MODE 0: gate/up (streams: gate and up rows of one 16-row tile per wave, 64
 // rows per row block). MODE 1: down (two 16-row tiles per wave, 128 rows per
 // row block). grid 8 * ceil(max items / 8), block 256 (4 waves, 2 per SIMD).

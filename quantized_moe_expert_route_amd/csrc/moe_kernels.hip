@@ -28,6 +28,14 @@ using namespace dev;
 
 namespace {
 
+// LDS layout of the down kernels: q8 of h per slot (qs, d, bsums), block
+// values [ns][R][nb], slot outputs [R][ns]; the LDS-staged variant then holds
+// the rows, 16-byte aligned.
+__host__ __device__ inline int down_lds_weights_offset(int ns, int K, int R, int nb) {
+  const int o = ns * K + ns * 4 * (K / 32) + ns * 2 * (K / 16) + 4 * ns * R * nb + 4 * ns * R;
+  return (o + 15) & ~15;
+}
+
 // ---------------------------------------------------------------- launching
 template <typename K, typename... Args>
 hipError_t launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Ev ev,
@@ -502,6 +510,151 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
   }
 }
 
+// Q4_K down with the rows staged in LDS. grid (ceil(H / R), T), block 512.
+// Same result as k_down. Waves 0-3 copy the down rows [row0, row0 + R) of
+// every present slot straight into LDS (global->LDS loads, 16-byte pieces; a
+// Q4_K row is 144 nb bytes, a multiple of 16) while waves 4-7 quantize h; then
+// all eight waves multiply out of LDS, TPG block tasks per 8-lane group.
+template <int TPG, int JB>
+__global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, Div dR, Div dpc,
+                                                      Div dq) {
+  using F = FmtQ4K;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int t = blockIdx.y, row0 = blockIdx.x * R;
+  const int K = a.F, nb = K / 256;
+  const int ns = a.k + a.has_shared;
+  const int row_bytes = nb * F::BB, npc = row_bytes / 16;
+  unsigned char* p_act = smem;
+  float* ld = reinterpret_cast<float*>(smem + ns * K);
+  int16_t* lbs = reinterpret_cast<int16_t*>(smem + ns * K + ns * 4 * (K / 32));
+  float* vals = reinterpret_cast<float*>(smem + ns * K + ns * 4 * (K / 32) + ns * 2 * (K / 16));
+  float* part = vals + ns * R * nb;  // [R][ns]
+  uint8_t* wl = smem + down_lds_weights_offset(ns, K, R, nb);
+  __shared__ const uint8_t* dptr[17];
+  __shared__ const float* dbias[17];
+  __shared__ float wslot[17];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool streamer = wave < 4;  // wave-uniform role
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.counters);
+  const int qw = wave - 4;
+  const int pieces = K / 256;
+  const int njobs = ns * pieces;
+  auto load_h = [&](int job) {
+    const int jc = min(job, njobs - 1);
+    const int s = dpc.div(jc), e0 = dpc.mod(jc, s) * 256 + 4 * lane;
+    const int ps = s < a.k ? t * a.k + s : a.T * a.k + t;
+    const float* src = job < njobs ? a.h + static_cast<size_t>(ps) * K + e0
+                                   : reinterpret_cast<const float*>(dummy);
+    return *reinterpret_cast<const float4*>(src);
+  };
+  float4 hv[JB];
+  if (!streamer) {
+#pragma unroll
+    for (int u = 0; u < JB; ++u) hv[u] = load_h(qw + 4 * u);
+  }
+  if (threadIdx.x < ns) {
+    const int s = threadIdx.x;
+    if (s < a.k) {
+      const SlotRef ref = a.slots[t * a.k + s];
+      dptr[s] = ref.down;
+      dbias[s] = ref.bias;
+      wslot[s] = a.w[t * a.k + s];
+    } else {
+      dptr[s] = static_cast<const uint8_t*>(a.sh_down);
+      dbias[s] = nullptr;
+      wslot[s] = a.sh_gate_vec ? a.shw[t] : 1.0f;
+    }
+  }
+  __syncthreads();
+  const uint32_t present = static_cast<uint32_t>(
+      __builtin_amdgcn_ballot_w64(lane < ns && dptr[min(lane, ns - 1)] != nullptr));
+  if (streamer) {
+    // piece j = ((s R + r) npc + q) -> LDS bytes [16 j, 16 j + 16); one
+    // instruction moves 64 consecutive pieces. Pieces of absent slots, rows
+    // past H and the tail of the last instruction read the dummy region.
+    const int npieces = ns * R * npc;
+    for (int j0 = wave * 64; j0 < npieces; j0 += 256) {
+      const int j = j0 + lane;
+      const int jc = min(j, npieces - 1);
+      const uint32_t sr = dq.div(jc), sl = dR.div(sr);
+      const int q = dq.mod(jc, sr), r = dR.mod(sr, sl);
+      const uint8_t* src = dptr[sl];
+      const bool ok = j < npieces && src != nullptr && row0 + r < a.H;
+      dma16_nt(ok ? src + static_cast<size_t>(row0 + r) * a.stride_down + 16 * q : dummy,
+               wl + 16 * j0);
+    }
+  } else {
+    int q[JB][4];
+    float dv[JB];
+    quant_wave_batch<256, JB>(hv, q, dv);
+#pragma unroll
+    for (int u = 0; u < JB; ++u) {
+      const int job = qw + 4 * u;  // wave-uniform
+      const int js = dpc.div(job);
+      if (job < njobs && ((present >> js) & 1u)) {
+        const int pc = dpc.mod(job, js);
+        reinterpret_cast<uint32_t*>(p_act + js * K + pc * 256)[lane] = pack_q8x4(q[u]);
+        if (lane == 0) ld[js * (K / 32) + pc] = dv[u];
+        const int sm = sum4(q[u][0] + q[u][1] + q[u][2] + q[u][3]);
+        if ((lane & 3) == 0) lbs[js * (K / 16) + pc * 16 + (lane >> 2)] = static_cast<int16_t>(sm);
+      }
+    }
+    for (int job = qw + 4 * JB; job < njobs; job += 4) {  // jobs beyond the first batch
+      const float4 v4 = load_h(job);
+      const int js = dpc.div(job), pc = dpc.mod(job, js);
+      if ((present >> js) & 1u) {
+        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+        quant_wave<256>(v, true, lane, reinterpret_cast<int8_t*>(p_act + js * K) + pc * 256,
+                        ld + js * (K / 32) + pc, lbs + js * (K / 16) + pc * 16);
+      }
+    }
+  }
+  wait_vm<0>();  // this wave's LDS copies have landed
+  __syncthreads();
+  {
+    const int grp = threadIdx.x >> 3, sub = threadIdx.x & 7;  // 64 groups of 8 lanes
+    const int total = ns * R * nb;
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+      const int task = grp + 64 * i;
+      if (task < total) {
+        const uint32_t q1 = dnb.div(task), sl = dR.div(q1);
+        const int b = dnb.mod(task, q1), r = dR.mod(q1, sl);
+        if (row0 + r < a.H && ((present >> sl) & 1u)) {
+          const uint8_t* blk = wl + static_cast<size_t>(q1) * row_bytes + b * F::BB;
+          F::Raw raw;
+          raw.hdr = *reinterpret_cast<const uint4*>(blk);
+          raw.q = *reinterpret_cast<const uint4*>(blk + 16 + 16 * sub);
+          const ActView av{reinterpret_cast<const int8_t*>(p_act + sl * K), ld + sl * (K / 32),
+                           lbs + sl * (K / 16), nullptr};
+          const float v = block_value<F>(raw, av, b, sub);
+          if (sub == 0) vals[task] = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R * ns; i += 512) {
+    const int r = i / ns, s = i - r * ns, row = row0 + r;
+    float v = 0.0f;
+    if (row < a.H && ((present >> s) & 1u)) {
+      float o = 0.0f;
+      for (int b = 0; b < nb; ++b) o += vals[(s * R + r) * nb + b];
+      if (dbias[s]) o += dbias[s][row];
+      v = wslot[s] * o;
+    }
+    part[i] = v;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += 512) {
+    const int row = row0 + r;
+    if (row >= a.H) break;
+    float acc = 0.0f;
+    for (int s = 0; s < ns; ++s) acc += part[r * ns + s];
+    a.y[static_cast<size_t>(t) * a.H + row] = acc;
+  }
+}
+
 // Integer block partials export through the same format routines.
 // grid n_rows, block 256.
 template <int FMT>
@@ -613,8 +766,50 @@ hipError_t down_jb(int jobs_per_wave, dim3 grid, size_t lds, hipStream_t s, Ev e
   return launch(k_down<FMT, TPG, 8>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
 }
 
+// Plan of the LDS-staged Q4_K down kernel: one workgroup per compute unit
+// where the LDS (q8 of h + R rows per slot) and 8 tasks per lane group allow.
+struct DownLdsPlan { int R, tpg; size_t lds; };
+bool down_lds_plan(const KArgs& a, DownLdsPlan* out) {
+  if (a.fmt_d != FMT_Q4_K) return false;
+  const int ns = a.k + a.has_shared, K = a.F, nb = K / 256, npc = nb * 9;
+  const int per_token = max(1, 256 / max(a.T, 1));
+  int R = max(1, min((a.H + per_token - 1) / per_token, a.H));
+  auto lds_of = [&](int r) {
+    const size_t pcs = static_cast<size_t>(ns) * r * npc;
+    return static_cast<size_t>(down_lds_weights_offset(ns, K, r, nb)) + 16 * ((pcs + 63) / 64 * 64);
+  };
+  while (R > 1 && (lds_of(R) > kMaxLds || ns * R * nb > 64 * 8)) --R;
+  if (lds_of(R) > kMaxLds || ns * R * nb > 64 * 8) return false;
+  *out = {R, (ns * R * nb + 63) / 64, lds_of(R)};
+  return true;
+}
+
+template <int TPG>
+hipError_t down_lds_jb(int jobs_per_wave, dim3 grid, size_t lds, hipStream_t s, Ev ev,
+                       const KArgs& a, int R, Div dnb, Div dR, Div dpc, Div dq) {
+  if (jobs_per_wave <= 2) return launch(k_down_q4k_lds<TPG, 2>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc, dq);
+  if (jobs_per_wave <= 5) return launch(k_down_q4k_lds<TPG, 5>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc, dq);
+  return launch(k_down_q4k_lds<TPG, 8>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc, dq);
+}
+
 template <int FMT>
 hipError_t down_dispatch(const KArgs& a, hipStream_t s, Ev ev) {
+  if constexpr (FMT == FMT_Q4_K) {
+    DownLdsPlan pl;
+    if (down_lds_plan(a, &pl)) {
+      const int nb = a.F / 256, pieces = a.F / 256;
+      const dim3 grid((a.H + pl.R - 1) / pl.R, a.T);
+      const Div dnb = Div::make(nb), dR = Div::make(pl.R), dpc = Div::make(pieces),
+                dq = Div::make(nb * 9);
+      const int jpw = ((a.k + a.has_shared) * pieces + 3) / 4;
+      switch (tpg_bucket(pl.tpg)) {
+        case 1: return down_lds_jb<1>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
+        case 2: return down_lds_jb<2>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
+        case 4: return down_lds_jb<4>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
+        default: return down_lds_jb<8>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
+      }
+    }
+  }
   GemvShape sh;
   const size_t lds = down_lds<FMT>(a, &sh);
   dim3 grid((a.H + sh.R - 1) / sh.R, a.T);
@@ -639,6 +834,8 @@ bool gemv_fits(const KArgs& a) {
   size_t d = a.fmt_d == FMT_Q4_K ? down_lds<FMT_Q4_K>(a, nullptr)
            : a.fmt_d == FMT_Q6_K ? down_lds<FMT_Q6_K>(a, nullptr)
                                  : down_lds<FMT_MXFP4>(a, nullptr);
+  DownLdsPlan pl;
+  if (down_lds_plan(a, &pl)) d = pl.lds;
   return g <= kMaxLds && d <= kMaxLds;
 }
 
