@@ -253,7 +253,8 @@ def kernel_names(cfg, path: str) -> dict:
     """Kernel (as rocprofv3 names it) of each stage of a layer forward."""
     import gen
     if path == "gemv":
-        return {"router": "k_router<4>", "gateup": "k_gateup", "down": "k_down"}
+        dn = "k_down_q4k_lds" if cfg.fmt_d == gen.Q4_K else "k_down"
+        return {"router": "k_router", "gateup": "k_gateup", "down": dn}
     nb = cfg.biases
     gu = "k_glds_q4k<0>" if cfg.fmt_gu == gen.Q4_K and not nb else "k_gu_grouped"
     if cfg.fmt_d == gen.Q4_K and not nb:
