@@ -607,6 +607,86 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key0)[NC], int k, i
   }
 }
 
+// Selection keys of one wave's candidates (expert e = lane + 64 i in register
+// i): key = order-preserving bits of logit (+ selection bias, one fp32 add),
+// 0 for e >= E; lg[i] of e >= E becomes -inf.
+template <int NC>
+__device__ __forceinline__ void topk_keys(float (&lg)[NC], const float* sel_bias, int E,
+                                          uint32_t (&key)[NC]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int e = lane + 64 * i;
+    const bool valid = e < E;
+    const float sb = sel_bias ? sel_bias[min(e, E - 1)] : 0.0f;
+    key[i] = valid ? float_key(sel_bias ? lg[i] + sb : lg[i]) : 0u;
+    lg[i] = valid ? lg[i] : -INFINITY;
+  }
+}
+
+// One exact selection round: the largest key, lowest index among equal keys;
+// returns its expert index (wave-uniform) and removes it from the candidates.
+template <int NC>
+__device__ __forceinline__ int topk_round(uint32_t (&key)[NC]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t best = key[0];
+#pragma unroll
+  for (int i = 1; i < NC; ++i) best = max(best, key[i]);
+  const uint32_t kmax = wave_max_u32(best);
+  uint32_t e = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(key[i] == kmax);
+    e = min(e, hit ? static_cast<uint32_t>(__builtin_ctzll(hit)) + 64u * i : 0xFFFFFFFFu);
+  }
+#pragma unroll
+  for (int i = 0; i < NC; ++i) key[i] = static_cast<uint32_t>(lane + 64 * i) == e ? 0u : key[i];
+  return static_cast<int>(e);
+}
+
+// Routing weights of the selected experts: lane r < k holds rank r's expert
+// my_id; lg as left by topk_keys. Softmax over the selected (norm_topk) or
+// over all E, or sigmoid (normalized over the selected when norm_topk), times
+// route_scale. Lane r < k writes w_out[r].
+template <int NC>
+__device__ __forceinline__ void topk_weights(const float (&lg)[NC], int my_id, int E, int k,
+                                             int router, int norm_topk, float route_scale,
+                                             float* w_out) {
+  const int lane = threadIdx.x & 63;
+  const int my_reg = my_id >> 6, my_lane = my_id & 63;
+  float my_l = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const float v = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * my_lane, __float_as_int(lg[i])));
+    my_l = my_reg == i ? v : my_l;
+  }
+  if (lane >= k) my_l = -INFINITY;
+  float w;
+  if (router == 0) {
+    float mx, z;
+    if (norm_topk) {
+      mx = wave_max(my_l);
+      const float ex = lane < k ? expf(my_l - mx) : 0.0f;
+      z = wave_sum(ex);
+      w = ex / z;
+    } else {
+      float lm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) lm = fmaxf(lm, lg[i]);
+      mx = wave_max(lm);
+      float zz = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) if (lane + 64 * i < E) zz += expf(lg[i] - mx);
+      z = wave_sum(zz);
+      w = lane < k ? expf(my_l - mx) / z : 0.0f;
+    }
+  } else {
+    const float sg = lane < k ? 1.0f / (1.0f + expf(-my_l)) : 0.0f;
+    w = norm_topk ? sg / wave_sum(sg) : sg;
+  }
+  if (lane < k) w_out[lane] = w * route_scale;
+}
+
 // Top-k of one token by one wave (all 64 lanes must call it). Selection key =
 // logit (+ selection bias, one fp32 add); rank order as in topk_select.
 // Weights come from the unbiased logits: softmax over the selected

@@ -265,6 +265,18 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
     const int slot = p - t * a.k;
     if (routing_given) {
       if (threadIdx.x == 0) s_e = a.ids[p];
+    } else if (!MX && blockIdx.x != 0) {
+      // only the slot's expert is needed here: ranks 0..slot, no weights (not
+      // for MXFP4, whose kernels lose occupancy to the extra registers)
+      float lg[NC];
+#pragma unroll
+      for (int i = 0; i < NC; ++i)
+        lg[i] = a.logits[static_cast<size_t>(t) * a.E + min(static_cast<int>(threadIdx.x) + 64 * i, a.E - 1)];
+      uint32_t key[NC];
+      topk_keys<NC>(lg, a.sel_bias, a.E, key);
+      int e = 0;
+      for (int r = 0; r <= slot; ++r) e = topk_round<NC>(key);
+      if (threadIdx.x == 0) s_e = e;
     } else {
       wave_topk<NC>(a.logits + static_cast<size_t>(t) * a.E, a.sel_bias, a.E, a.k, a.router,
                     a.norm_topk, a.route_scale, s_ids, s_w);
