@@ -124,6 +124,11 @@ struct Stages {
 // selected expert's weights once per 16 tokens routed to it.
 constexpr int kGroupedMinTokens = 5;
 
+// GEMV path rule: an MXFP4 down (q8 of h in 32-value blocks, F up to a few
+// thousand) gets h quantized once per pair by its own kernel; Q4_K / Q6_K downs
+// quantize h inside every down workgroup, overlapped with the row stream.
+bool gemv_hquant(int fmt_down) { return fmt_down == FMT_MXFP4; }
+
 bool use_grouped(int T, int fmt_gate, int fmt_down) {
   return T >= kGroupedMinTokens && fmt_gate != FMT_MXFP4 && fmt_down != FMT_MXFP4;
 }
@@ -155,7 +160,10 @@ WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool group
     L.tiles = take(static_cast<size_t>(max_tiles(T, k, E, has_shared)) * sizeof(GTile));
     L.part = take(P * H * 4);
   } else {
-    L.hqs = L.hd = L.hbs = 0;
+    // q8 of h for an MXFP4 down, quantized once per pair: fp16 pairs + scales
+    L.hqs = take(P * F * 2);
+    L.hd = take(P * (F / 32) * 4);
+    L.hbs = 0;
     L.rpart = L.pair_tmp = L.plist = L.present = L.tiles = L.part = 0;
   }
   L.total = off;
@@ -253,6 +261,7 @@ static moe_status expert_ffn_impl(KArgs& a, bool grouped, bool routing_given, hi
     if (e == hipSuccess) e = launch_combine(a, stream, st.next());
   } else {
     e = launch_gateup(a, routing_given, stream, st.next());
+    if (e == hipSuccess && gemv_hquant(a.fmt_d)) e = launch_hquant_pairs(a, stream, st.next());
     if (e == hipSuccess) e = launch_down(a, stream, st.next());
   }
   return hip_status(e);
@@ -341,16 +350,18 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, mo
 
 int moe_layer_stage_count(const moe_layer_desc* desc, int T) {
   if (validate_desc(desc) != MOE_OK || T <= 0 || T > kMaxTokens) return 0;
-  return use_grouped(T, desc->fmt_gate, desc->fmt_down) ? 7 : 3;
+  if (use_grouped(T, desc->fmt_gate, desc->fmt_down)) return 7;
+  return gemv_hquant(desc->fmt_down) ? 4 : 3;
 }
 
 const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {
   static const char* gemv[] = {"router", "gateup", "down"};
+  static const char* gemv_hq[] = {"router", "gateup", "hquant", "down"};
   static const char* grouped[] = {"router", "topk", "bucket", "gateup", "hquant", "down",
                                   "combine"};
   const int n = moe_layer_stage_count(desc, T);
   if (stage < 0 || stage >= n) return nullptr;
-  return n == 7 ? grouped[stage] : gemv[stage];
+  return n == 7 ? grouped[stage] : n == 4 ? gemv_hq[stage] : gemv[stage];
 }
 
 moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,

@@ -310,8 +310,10 @@ __device__ __forceinline__ void quant_wave(const float v[4], bool valid, int lan
 
 // B = 32 quantization stored as fp16 pairs (a[i], a[i+16]) per block, the layout
 // the MXFP4 dot reads: ap gets 128 pairs for the 256-value piece.
+// Stores the pairs element-major: ap[q * stride + block] (see ActView), with
+// ap pointing at the piece's first block column.
 __device__ __forceinline__ void quant_wave_pairs(const float v[4], bool valid, int lane,
-                                                 half2_t* ap, float* d) {
+                                                 half2_t* ap, int stride, float* d) {
   int q[4];
   const float dv = quant_wave_q<32>(v, q);
   int o[4];
@@ -322,7 +324,7 @@ __device__ __forceinline__ void quant_wave_pairs(const float v[4], bool valid, i
   if (valid && off < 16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      ap[16 * bl + off + i] = half2_t{static_cast<_Float16>(q[i]), static_cast<_Float16>(o[i])};
+      ap[(off + i) * stride + bl] = half2_t{static_cast<_Float16>(q[i]), static_cast<_Float16>(o[i])};
   }
   if (valid && (lane & 7) == 0) d[bl] = dv;
 }
@@ -332,7 +334,11 @@ struct ActView {
   const int8_t* qs;     // [K] (Q8_K)
   const float* d;       // [K / B]
   const int16_t* bs;    // [K / 16] (Q8_K)
-  const half2_t* ap;    // [K / 2] fp16 pairs (Q8_32): block b, i < 16: (a[32b+i], a[32b+16+i])
+  // [16][K / 32] fp16 pairs (Q8_32), element-major: ap[i * ap_stride + b] =
+  // (a[32b+i], a[32b+16+i]), ap_stride = K / 32, so lanes that take
+  // consecutive blocks read consecutive LDS words (no bank conflicts)
+  const half2_t* ap;
+  int ap_stride;
 };
 
 // ------------------------------------------------------------------ formats
@@ -455,20 +461,21 @@ struct FmtMXFP4 {
   // Exact: e2m1 values and int8 activations are exact in fp16, products exact in
   // fp32 and every partial sum is a multiple of 0.5 below 2^23.
   __device__ static __forceinline__ float dot(const Raw& r, const ActView& a, int b) {
-    const half2_t* ap = a.ap + 16 * b;
+    const half2_t* ap = a.ap + b;
+    const int st = a.ap_stride;
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t qw = r.sh == 3 ? r.w[i + 1]
                                     : __builtin_amdgcn_alignbyte(r.w[i + 1], r.w[i], r.sh + 1);
       acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 0),
-                                   ap[4 * i + 0], acc, false);
+                                   ap[(4 * i + 0) * st], acc, false);
       acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 1),
-                                   ap[4 * i + 1], acc, false);
+                                   ap[(4 * i + 1) * st], acc, false);
       acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 2),
-                                   ap[4 * i + 2], acc, false);
+                                   ap[(4 * i + 2) * st], acc, false);
       acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 3),
-                                   ap[4 * i + 3], acc, false);
+                                   ap[(4 * i + 3) * st], acc, false);
     }
     return acc;
   }
@@ -509,10 +516,10 @@ __device__ __forceinline__ void stage_act(const int8_t* qs, const float* d, cons
     }
     for (int i = tid; i < K / 256; i += nt) ld[i] = d[i];
   } else {
-    for (int i = tid; i < K / 2; i += nt) {
+    for (int i = tid; i < K / 2; i += nt) {  // element-major (see ActView)
       const int b = i / 16, ii = i % 16;
-      lap[i] = half2_t{static_cast<_Float16>(qs[32 * b + ii]),
-                       static_cast<_Float16>(qs[32 * b + 16 + ii])};
+      lap[ii * (K / 32) + b] = half2_t{static_cast<_Float16>(qs[32 * b + ii]),
+                                       static_cast<_Float16>(qs[32 * b + 16 + ii])};
     }
     for (int i = tid; i < K / 32; i += nt) ld[i] = d[i];
   }

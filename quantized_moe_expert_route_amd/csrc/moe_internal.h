@@ -95,8 +95,8 @@ struct KArgs {
   int2* plist;         // [P] (pair, token), sorted by (expert, pair); shared expert last
   int32_t* present;    // [P] 1 if the pair's expert is present
   GTile* tiles;        // [max tiles]
-  int8_t* hqs;         // [P, F]
-  float* hd;           // [P, F / 32]
+  int8_t* hqs;         // [P, F] int8 (grouped); [P, F / 2] fp16 pairs (GEMV path, MXFP4 down)
+  float* hd;           // [P, F / 256] (grouped); [P, F / 32] (GEMV path, MXFP4 down)
   int16_t* hbs;        // [P, F / 16]
   float* part;         // [P, H] routing-weighted expert outputs per pair
 };
@@ -116,6 +116,7 @@ bool gemv_fits(const KArgs& a);
 
 // Which expert-FFN path a chunk of T tokens takes (fixed rule, see moe_api.cpp).
 bool use_grouped(int T, int fmt_gate, int fmt_down);
+bool gemv_hquant(int fmt_down);
 
 // Router split of the grouped path: K slices of `len` elements (multiple of 16).
 struct RouterSplit { int ks, len; };
@@ -141,6 +142,7 @@ hipError_t launch_router(const KArgs& a, bool quant, int n_clear, hipStream_t s,
 hipError_t launch_topk(const KArgs& a, hipStream_t s);
 hipError_t launch_gateup(const KArgs& a, bool routing_given, hipStream_t s, Ev ev);
 hipError_t launch_down(const KArgs& a, hipStream_t s, Ev ev);
+hipError_t launch_hquant_pairs(const KArgs& a, hipStream_t s, Ev ev);
 // grouped path
 hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hipStream_t s, Ev ev);
 hipError_t launch_topk_sum(const KArgs& a, RouterSplit rs, hipStream_t s, Ev ev);

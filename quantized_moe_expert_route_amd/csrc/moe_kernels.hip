@@ -28,6 +28,9 @@ using namespace dev;
 
 namespace {
 
+// Rows of more blocks than this are summed in this many fixed chunks first.
+constexpr int kSumChunks = 8;
+
 // LDS layout of the down kernels: q8 of h per slot (qs, d, bsums), block
 // values [ns][R][nb], slot outputs [R][ns]; the LDS-staged variant then holds
 // the rows, 16-byte aligned.
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
   float* vals = reinterpret_cast<float*>(smem + act_bytes + 4 * (K / 32) + 2 * (K / 16));
   // gate/up pointer tables of all experts, read while wave 0 runs the top-k
   const void** ltab = reinterpret_cast<const void**>(
-      smem + act_bytes + 4 * (K / 32) + 2 * (K / 16) + 4 * ((2 * R * nb + 1) & ~1));
+      smem + act_bytes + 4 * (K / 32) + 2 * (K / 16) + 4 * ((2 * R * nb + 2 * R * kSumChunks + 1) & ~1));
   const int G = 256 / F::LPB;
   const int grp = threadIdx.x / F::LPB, sub = threadIdx.x % F::LPB;
   const int total = 2 * R * nb;
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
     issue_loads();
     if (a.b_gate) { bg = a.b_gate[e]; bu = a.b_up[e]; }
   }
-  ActView av{lqs, ld, lbs, lap};
+  ActView av{lqs, ld, lbs, lap, K / 32};
 #pragma unroll
   for (int i = 0; i < TPG; ++i) {
     const int task = grp + G * i;
@@ -328,12 +331,31 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
   }
   __syncthreads();
   float* hrow = a.h + static_cast<size_t>(p) * a.F;
+  // long rows (MXFP4: 32-value blocks): fixed chunks of blocks summed in
+  // parallel first, then the chunks in order
+  float* chunk = vals + 2 * R * nb;  // [2 R][kSumChunks]
+  const bool chunked = nb > kSumChunks;
+  if (chunked) {
+    const int L = (nb + kSumChunks - 1) / kSumChunks;
+    for (int i = threadIdx.x; i < 2 * R * kSumChunks; i += 256) {
+      const int mr = i / kSumChunks, c = i - mr * kSumChunks;
+      float o = 0.0f;
+      for (int b = c * L; b < min(nb, (c + 1) * L); ++b) o += vals[mr * nb + b];
+      chunk[i] = o;
+    }
+    __syncthreads();
+  }
   for (int r = threadIdx.x; r < R; r += 256) {
     const int row = row0 + r;
     if (row >= a.F) break;
     float g = 0.0f, u = 0.0f;
-    for (int b = 0; b < nb; ++b) g += vals[r * nb + b];
-    for (int b = 0; b < nb; ++b) u += vals[(R + r) * nb + b];
+    if (chunked) {
+      for (int c = 0; c < kSumChunks; ++c) g += chunk[r * kSumChunks + c];
+      for (int c = 0; c < kSumChunks; ++c) u += chunk[(R + r) * kSumChunks + c];
+    } else {
+      for (int b = 0; b < nb; ++b) g += vals[r * nb + b];
+      for (int b = 0; b < nb; ++b) u += vals[(R + r) * nb + b];
+    }
     if (bg) { g += bg[row]; u += bu[row]; }
     hrow[row] = act_fn(a.act, a.act_alpha, a.act_limit, g, u);
   }
@@ -346,6 +368,26 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
   }
 }
 
+// q8 (32-value blocks) of every pair's h for an MXFP4 down, once per pair,
+// stored as the down kernel's LDS image: fp16 pairs (a[32b + i], a[32b + 16 + i])
+// element-major ([i][block], as ActView reads them) and one scale per block. grid ceil(P pieces / 4), block 256: one wave per
+// 256-value piece (fp32 recipe; values past F belong to no block).
+__global__ __launch_bounds__(256) void k_hquant_pairs(KArgs a, int P, Div dpc) {
+  const int lane = threadIdx.x & 63;
+  const int job = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int p = dpc.div(job), pc = dpc.mod(job, p);
+  if (p >= P) return;
+  const int e0 = pc * 256 + 4 * lane;
+  const bool valid = e0 < a.F;
+  const float4 hv = *reinterpret_cast<const float4*>(a.h + static_cast<size_t>(p) * a.F +
+                                                      (valid ? e0 : 0));
+  const float v[4] = {valid ? hv.x : 0.0f, valid ? hv.y : 0.0f, valid ? hv.z : 0.0f,
+                      valid ? hv.w : 0.0f};
+  quant_wave_pairs(v, valid, lane,
+                   reinterpret_cast<half2_t*>(a.hqs) + static_cast<size_t>(p) * (a.F / 2) + pc * 8,
+                   a.F / 32, a.hd + static_cast<size_t>(p) * (a.F / 32) + pc * 8);
+}
+
 // ---------------------------------------------------------------- down GEMV
 // grid (ceil(H / R), T), block 512. For each present slot of token t (and the
 // shared expert): down rows [row0, row0 + R) against q8(h), then
@@ -354,7 +396,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
 // waves 4-7 meanwhile quantize h into LDS (fp32 recipe), so the VALU work of
 // the quantization overlaps the weight stream instead of queueing behind the
 // load issue.
-template <int FMT, int TPG, int JB>
+template <int FMT, int TPG, int JB, bool PRE>
 __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, Div dpc) {
   using F = typename FmtOf<FMT>::T;
   constexpr bool MX = FMT == FMT_MXFP4;
@@ -396,7 +438,7 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
     return *reinterpret_cast<const float4*>(src);
   };
   float4 hv[JB];
-  if (!streamer) {
+  if (!streamer && !PRE) {
 #pragma unroll
     for (int u = 0; u < JB; ++u) hv[u] = load_h(qw + 4 * u);
   }
@@ -437,6 +479,26 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
                                static_cast<size_t>(b) * F::BB
                          : dummy, sub);
     }
+  } else if constexpr (PRE) {
+    // h already quantized per pair (MXFP4 down): copy the LDS image of every
+    // present slot, 16 bytes per thread and step
+    const int qt = threadIdx.x - 256;
+    const int n16 = K / 8;  // 16-byte pieces of one slot's fp16 pairs (2K bytes)
+    for (int i = qt; i < ns * n16; i += 256) {
+      const int s = i / n16, j = i - s * n16;
+      if ((present >> s) & 1u) {
+        const int ps = s < a.k ? t * a.k + s : a.T * a.k + t;
+        reinterpret_cast<int4*>(p_act + s * act_bytes)[j] =
+            reinterpret_cast<const int4*>(a.hqs + static_cast<size_t>(ps) * (2 * K))[j];
+      }
+    }
+    for (int i = qt; i < ns * (K / 32); i += 256) {
+      const int s = i / (K / 32), j = i - s * (K / 32);
+      if ((present >> s) & 1u) {
+        const int ps = s < a.k ? t * a.k + s : a.T * a.k + t;
+        ld[s * (K / 32) + j] = a.hd[static_cast<size_t>(ps) * (K / 32) + j];
+      }
+    }
   } else {
     auto quant_h = [&](int job, const float4& hv1) {
       const int s = dpc.div(job), pc = dpc.mod(job, s);
@@ -447,7 +509,7 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
                       ld + s * (K / 32) + pc, lbs + s * (K / 16) + pc * 16);
       } else {
         quant_wave_pairs(v, valid, lane,
-                         reinterpret_cast<half2_t*>(p_act + s * act_bytes) + pc * 128,
+                         reinterpret_cast<half2_t*>(p_act + s * act_bytes) + pc * 8, K / 32,
                          ld + s * (K / 32) + pc * 8);
       }
     };
@@ -491,7 +553,8 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
       const int b = dnb.mod(task, q1), r = dR.mod(q1, q2), s = q2;
       if (task < total && row0 + r < a.H && ((present >> s) & 1u)) {
         ActView av{reinterpret_cast<const int8_t*>(p_act + s * act_bytes), ld + s * (K / 32),
-                   lbs + s * (K / 16), reinterpret_cast<const half2_t*>(p_act + s * act_bytes)};
+                   lbs + s * (K / 16), reinterpret_cast<const half2_t*>(p_act + s * act_bytes),
+                   K / 32};
         const float v = block_value<F>(raw[i], av, b, sub);
         if (sub == 0) vals[(s * R + r) * nb + b] = v;
       }
@@ -499,14 +562,32 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
   }
   __syncthreads();
   // weighted slot outputs, one thread per (row, slot), then the sum over the
-  // slots in slot order (shared expert last)
+  // slots in slot order (shared expert last). Long rows (MXFP4: 32-value
+  // blocks) first sum fixed chunks of blocks in parallel, then the chunks in
+  // order.
   float* part = vals + ns * R * nb;  // [R][ns]
+  float* chunk = part + ns * R;      // [ns R][kSumChunks]
+  const bool chunked = nb > kSumChunks;
+  if (chunked) {
+    const int L = (nb + kSumChunks - 1) / kSumChunks;
+    for (int i = threadIdx.x; i < ns * R * kSumChunks; i += 512) {
+      const int sr = i / kSumChunks, c = i - sr * kSumChunks;
+      float o = 0.0f;
+      for (int b = c * L; b < min(nb, (c + 1) * L); ++b) o += vals[sr * nb + b];
+      chunk[i] = o;
+    }
+    __syncthreads();
+  }
   for (int i = threadIdx.x; i < R * ns; i += 512) {
     const int r = i / ns, s = i - r * ns, row = row0 + r;
     float v = 0.0f;
     if (row < a.H && ((present >> s) & 1u)) {
       float o = 0.0f;
-      for (int b = 0; b < nb; ++b) o += vals[(s * R + r) * nb + b];
+      if (chunked) {
+        for (int c = 0; c < kSumChunks; ++c) o += chunk[(s * R + r) * kSumChunks + c];
+      } else {
+        for (int b = 0; b < nb; ++b) o += vals[(s * R + r) * nb + b];
+      }
       if (dbias[s]) o += dbias[s][row];
       v = wslot[s] * o;
     }
@@ -683,7 +764,7 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* rows, int K, 
   int16_t* lbs = reinterpret_cast<int16_t*>(smem + act_bytes + 4 * (K / 32));
   stage_act<MX>(qs, d, bs, K, lqs, ld, lbs, lap);
   __syncthreads();
-  ActView av{lqs, ld, lbs, lap};
+  ActView av{lqs, ld, lbs, lap, K / 32};
   const int r = blockIdx.x, nb = K / F::BE;
   const int G = 256 / F::LPB, grp = threadIdx.x / F::LPB, sub = threadIdx.x % F::LPB;
   for (int b = grp; b < nb; b += G) {
@@ -723,7 +804,8 @@ size_t gateup_lds(const KArgs& a, GemvShape* out) {
   if (out) *out = sh;
   const bool MX = FMT == FMT_MXFP4;
   return (MX ? 2 * a.H : a.H) + 4 * (a.H / 32) + 2 * (a.H / 16) +
-         4 * static_cast<size_t>((2 * sh.R * nb + 1) & ~1) + 16 * static_cast<size_t>(a.E);
+         4 * static_cast<size_t>((2 * sh.R * nb + 2 * sh.R * kSumChunks + 1) & ~1) +
+         16 * static_cast<size_t>(a.E);
 }
 
 template <int FMT>
@@ -743,7 +825,8 @@ size_t down_lds(const KArgs& a, GemvShape* out) {
   if (out) *out = sh;
   const bool MX = FMT == FMT_MXFP4;
   return ns * ((MX ? 2 * a.F : a.F) + 4 * (a.F / 32) + 2 * (a.F / 16)) +
-         4 * static_cast<size_t>(ns * sh.R * nb) + 4 * static_cast<size_t>(ns * sh.R);
+         4 * static_cast<size_t>(ns * sh.R * nb) + 4 * static_cast<size_t>(ns * sh.R) +
+         4 * static_cast<size_t>(ns * sh.R * kSumChunks);
 }
 
 template <int FMT, int NC>
@@ -773,9 +856,11 @@ hipError_t gateup_dispatch(const KArgs& a, int routing_given, hipStream_t s, Ev 
 template <int FMT, int TPG>
 hipError_t down_jb(int jobs_per_wave, dim3 grid, size_t lds, hipStream_t s, Ev ev, const KArgs& a,
                    int R, Div dnb, Div dR, Div dpc) {
-  if (jobs_per_wave <= 2) return launch(k_down<FMT, TPG, 2>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
-  if (jobs_per_wave <= 5) return launch(k_down<FMT, TPG, 5>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
-  return launch(k_down<FMT, TPG, 8>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
+  if constexpr (FMT == FMT_MXFP4)  // h quantized beforehand (k_hquant_pairs)
+    return launch(k_down<FMT, TPG, 2, true>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
+  if (jobs_per_wave <= 2) return launch(k_down<FMT, TPG, 2, false>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
+  if (jobs_per_wave <= 5) return launch(k_down<FMT, TPG, 5, false>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
+  return launch(k_down<FMT, TPG, 8, false>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
 }
 
 // Plan of the LDS-staged Q4_K down kernel: one workgroup per compute unit
@@ -890,6 +975,12 @@ hipError_t launch_gateup(const KArgs& a, bool routing_given, hipStream_t s, Ev e
     case FMT_Q6_K: return gateup_dispatch<FMT_Q6_K>(a, routing_given, s, ev);
     default: return gateup_dispatch<FMT_MXFP4>(a, routing_given, s, ev);
   }
+}
+
+hipError_t launch_hquant_pairs(const KArgs& a, hipStream_t s, Ev ev) {
+  const int P = a.T * a.k + a.T * a.has_shared;
+  const int pieces = (a.F + 255) / 256;
+  return launch(k_hquant_pairs, dim3((P * pieces + 3) / 4), 256, 0, s, ev, a, P, Div::make(pieces));
 }
 
 hipError_t launch_down(const KArgs& a, hipStream_t s, Ev ev) {

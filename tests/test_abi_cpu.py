@@ -170,8 +170,9 @@ def test_block_dots_validation():
 
 def test_stage_names_and_path_rule():
     """Dispatch rule: chunks of <= 4 tokens, and any layer with an MXFP4 matrix,
-    take the per-pair GEMV path (3 kernels); larger K-quant chunks the grouped
-    path (7 kernels)."""
+    take the per-pair GEMV path (3 kernels, or 4 with an MXFP4 down, whose h is
+    quantized by a kernel of its own); larger K-quant chunks the grouped path
+    (7 kernels)."""
     d = good_desc()
     for T in (1, 4):
         assert M.moe_layer_stage_count(d, T) == 3
@@ -183,7 +184,10 @@ def test_stage_names_and_path_rule():
     assert M.moe_layer_stage_name(d, 1, 9) is None
     assert M.moe_layer_stage_count(d, 0) == 0
     mx = good_desc(gen.CONFIGS["gpt-oss-20b"])
-    assert M.moe_layer_stage_count(mx, 16) == 3
+    for T in (1, 16):
+        assert M.moe_layer_stage_count(mx, T) == 4
+        assert [M.moe_layer_stage_name(mx, T, i) for i in range(4)] == [
+            "router", "gateup", "hquant", "down"]
     q6 = good_desc(gen.CONFIGS["deepseek-v4-flash"])
     assert M.moe_layer_stage_count(q6, 16) == 7
     # the grouped workspace holds the per-pair rows: it grows with T * k * H
