@@ -704,9 +704,24 @@ __global__ __launch_bounds__(256) void k_topk_sum(KArgs a, int KS) {
   double s[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) s[i] = 0.0;
-  for (int ks = 0; ks < KS; ++ks) {
+  // slices in batches whose loads are all issued before the first add (one
+  // memory round trip per batch); the sums still run in slice order
+  constexpr int KB = NC <= 8 ? 8 : 4;
+  for (int k0 = 0; k0 < KS; k0 += KB) {
+    double v[KB][NC];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) s[i] += rp[ks * kstride + min(lane + 64 * i, a.E - 1)];
+    for (int kb = 0; kb < KB; ++kb) {
+      const int ks = min(k0 + kb, KS - 1);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) v[kb][i] = rp[ks * kstride + min(lane + 64 * i, a.E - 1)];
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (k0 + kb < KS) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) s[i] += v[kb][i];
+      }
+    }
   }
   float lg[NC];
 #pragma unroll
