@@ -26,6 +26,31 @@ def test_layer_full_decode(name, T):
     check_layer(gen.CONFIGS[name], T=T, x_index=T)
 
 
+def _routed_layer(cfg, T, x_index):
+    """The full-size layer with only the experts the oracle routes these tokens
+    to (plus the shared expert) generated; the others stay zero and unused."""
+    base = gen.make_layer(cfg, experts=[])
+    x, _ = gen.make_x(cfg, T=T, x_index=x_index)
+    used = set()
+    for t in range(T):
+        used |= {int(e) for e in oracle.topk(oracle.router_logits(base.w_router, x[t]), cfg.k,
+                                             base.sel_bias)}
+    if cfg.shared:
+        used.add(cfg.E)  # the shared expert's pool slot
+    return gen.make_layer(cfg, experts=sorted(used))
+
+
+@pytest.mark.parametrize("name,T", [("deepseek-v4-flash", 1), ("deepseek-v4-flash", 3),
+                                    ("kimi-k2", 1), ("kimi-k2", 2)])
+def test_layer_full_decode_routed(name, T):
+    """Full-size DeepSeek-V4-Flash and Kimi-K2 layers through the per-pair path
+    (chunks of <= 4 tokens): sigmoid routers (DeepSeek with selection bias), E =
+    384 (16 candidates per lane in the top-k), Q6_K down rows in registers and
+    Q4_K down rows through LDS at H = 7168."""
+    cfg = gen.CONFIGS[name]
+    check_layer(cfg, data=_routed_layer(cfg, T, 30 + T), T=T, x_index=30 + T)
+
+
 def test_layer_full_verify_chunk_sampled():
     """DeepSeek-V4-Flash-shaped 16-token chunk at full size; the oracle checks
     every token."""
