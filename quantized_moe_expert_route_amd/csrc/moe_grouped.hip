@@ -370,7 +370,6 @@ __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG,
     }
   };
   // ---- compute-side lane roles
-  const int2 pA = pair_of(c);
   int2 pC[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pC[i] = pair_of(4 * g + i);
@@ -547,8 +546,6 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
       dma4(dsrc + 4 * b, L + kS6D);
     }
   };
-  const int2 pA = pair_of(c);
-  (void)pA;
   int2 pC[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pC[i] = pair_of(4 * g + i);
@@ -988,9 +985,10 @@ __global__ __launch_bounds__(256) void k_combine(KArgs a) {
 int grouped_grid(int n_items_max) { return 8 * ((n_items_max + 7) / 8); }
 
 // Row blocks per LDS-staged work item: long enough streams to amortize the
-// ring fill, while keeping about 4096 items at the bound on tiles.
+// ring fill, while keeping about 9216 items (18 rounds of two workgroups per
+// compute unit: a short tail) at the bound on tiles.
 int glds_group(int RB, int max_tiles) {
-  int g = (RB * max_tiles + 4095) / 4096;
+  int g = (RB * max_tiles + 9215) / 9216;
   if (g < 1) g = 1;
   if (g > RB) g = RB;
   return g;
