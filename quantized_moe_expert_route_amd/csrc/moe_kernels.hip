@@ -604,10 +604,12 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
 }
 
 // Q4_K down with the rows staged in LDS. grid (ceil(H / R), T), block 512.
-// Same result as k_down. Waves 0-3 copy the down rows [row0, row0 + R) of
+// Same result as k_down. Waves 0-2 copy the down rows [row0, row0 + R) of
 // every present slot straight into LDS (global->LDS loads, 16-byte pieces; a
-// Q4_K row is 144 nb bytes, a multiple of 16) while waves 4-7 quantize h; then
-// all eight waves multiply out of LDS, TPG block tasks per 8-lane group.
+// Q4_K row is 144 nb bytes, a multiple of 16) while waves 3-7 quantize h (the
+// longer of the two paths: 3:5 measured best of 2:6, 3:5 and 4:4); then all
+// eight waves multiply out of LDS, TPG block tasks per 8-lane group.
+constexpr int kStreamers = 3, kQuantizers = 8 - kStreamers;
 template <int TPG, int JB>
 __global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, Div dR, Div dpc,
                                                       Div dq) {
@@ -627,9 +629,9 @@ __global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, D
   __shared__ const float* dbias[17];
   __shared__ float wslot[17];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const bool streamer = wave < 4;  // wave-uniform role
+  const bool streamer = wave < kStreamers;  // wave-uniform role
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.counters);
-  const int qw = wave - 4;
+  const int qw = wave - kStreamers;
   const int pieces = K / 256;
   const int njobs = ns * pieces;
   auto load_h = [&](int job) {
@@ -643,7 +645,7 @@ __global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, D
   float4 hv[JB];
   if (!streamer) {
 #pragma unroll
-    for (int u = 0; u < JB; ++u) hv[u] = load_h(qw + 4 * u);
+    for (int u = 0; u < JB; ++u) hv[u] = load_h(qw + kQuantizers * u);
   }
   if (threadIdx.x < ns) {
     const int s = threadIdx.x;
@@ -666,7 +668,7 @@ __global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, D
     // instruction moves 64 consecutive pieces. Pieces of absent slots, rows
     // past H and the tail of the last instruction read the dummy region.
     const int npieces = ns * R * npc;
-    for (int j0 = wave * 64; j0 < npieces; j0 += 256) {
+    for (int j0 = wave * 64; j0 < npieces; j0 += 64 * kStreamers) {
       const int j = j0 + lane;
       const int jc = min(j, npieces - 1);
       const uint32_t sr = dq.div(jc), sl = dR.div(sr);
@@ -682,7 +684,7 @@ __global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, D
     quant_wave_batch<256, JB>(hv, q, dv);
 #pragma unroll
     for (int u = 0; u < JB; ++u) {
-      const int job = qw + 4 * u;  // wave-uniform
+      const int job = qw + kQuantizers * u;  // wave-uniform
       const int js = dpc.div(job);
       if (job < njobs && ((present >> js) & 1u)) {
         const int pc = dpc.mod(job, js);
@@ -692,7 +694,7 @@ __global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, D
         if ((lane & 3) == 0) lbs[js * (K / 16) + pc * 16 + (lane >> 2)] = static_cast<int16_t>(sm);
       }
     }
-    for (int job = qw + 4 * JB; job < njobs; job += 4) {  // jobs beyond the first batch
+    for (int job = qw + kQuantizers * JB; job < njobs; job += kQuantizers) {  // jobs beyond the first batch
       const float4 v4 = load_h(job);
       const int js = dpc.div(job), pc = dpc.mod(job, js);
       if ((present >> js) & 1u) {
@@ -898,7 +900,7 @@ hipError_t down_dispatch(const KArgs& a, hipStream_t s, Ev ev) {
       const dim3 grid((a.H + pl.R - 1) / pl.R, a.T);
       const Div dnb = Div::make(nb), dR = Div::make(pl.R), dpc = Div::make(pieces),
                 dq = Div::make(nb * 9);
-      const int jpw = ((a.k + a.has_shared) * pieces + 3) / 4;
+      const int jpw = ((a.k + a.has_shared) * pieces + kQuantizers - 1) / kQuantizers;
       switch (tpg_bucket(pl.tpg)) {
         case 1: return down_lds_jb<1>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
         case 2: return down_lds_jb<2>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
