@@ -191,7 +191,8 @@ def main():
         cpu_s = time.perf_counter() - t1
         cpu = {"value": round(n_tok / cpu_s, 2), "unit": "tokens/s", "cores": th, "kind": "oracle",
                "sample": f"{n_tok} tokens of the same workload (x pool members), whole layer per "
-                         f"token, fp64 oracle, {th} host threads, {cpu_s:.1f} s wall"}
+                         f"token, fp64 oracle, {th} host threads, {cpu_s:.1f} s wall "
+                         f"(~{cpu_s * th:.0f} thread-seconds of CPU work)"}
 
     out = {
         "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (% of peak), 1 MI355X",
