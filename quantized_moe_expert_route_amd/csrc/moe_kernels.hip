@@ -242,23 +242,29 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
       F::load(raw[i], blk, sub);
     }
   };
+  // The selection runs on one wave, chosen by the workgroup's place among
+  // those resident on a compute unit (dispatch order: 256 per round), so that
+  // the selection waves of co-resident workgroups run on different SIMDs.
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tkw = ((blockIdx.x + blockIdx.y * gridDim.x) >> 8) & 3;
   if (!routed) {
     gbase = static_cast<const uint8_t*>(a.sh_gate);
     ubase = static_cast<const uint8_t*>(a.sh_up);
     issue_loads();  // the shared expert does not wait for routing
-  } else if (threadIdx.x >= 64) {
+  } else if (wave != tkw) {
     // E <= 1024: at most 6 entries per thread; issue every load, then store
+    const int li = (wave - (wave > tkw ? 1 : 0)) * 64 + lane;  // 0..191
     const void* g[6];
     const void* u[6];
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
-      const int i = min(static_cast<int>(threadIdx.x) - 64 + 192 * j, a.E - 1);
+      const int i = min(li + 192 * j, a.E - 1);
       g[j] = a.gate[i];
       u[j] = a.up[i];
     }
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
-      const int i = static_cast<int>(threadIdx.x) - 64 + 192 * j;
+      const int i = li + 192 * j;
       if (i < a.E) {
         ltab[2 * i] = g[j];
         ltab[2 * i + 1] = u[j];
@@ -266,27 +272,30 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
     }
   } else {
     const int slot = p - t * a.k;
+    // the selection is one long dependent chain: issue priority over the
+    // co-resident workgroups' block arithmetic on this SIMD
+    __builtin_amdgcn_s_setprio(3);
     if (routing_given) {
-      if (threadIdx.x == 0) s_e = a.ids[p];
+      if (lane == 0) s_e = a.ids[p];
     } else if (!MX && blockIdx.x != 0) {
       // only the slot's expert is needed here: ranks 0..slot, no weights (not
       // for MXFP4, whose kernels lose occupancy to the extra registers)
       float lg[NC];
 #pragma unroll
       for (int i = 0; i < NC; ++i)
-        lg[i] = a.logits[static_cast<size_t>(t) * a.E + min(static_cast<int>(threadIdx.x) + 64 * i, a.E - 1)];
+        lg[i] = a.logits[static_cast<size_t>(t) * a.E + min(lane + 64 * i, a.E - 1)];
       uint32_t key[NC];
       topk_keys<NC>(lg, a.sel_bias, a.E, key);
       int e = 0;
       for (int r = 0; r <= slot; ++r) e = topk_round<NC>(key);
-      if (threadIdx.x == 0) s_e = e;
+      if (lane == 0) s_e = e;
     } else {
       wave_topk<NC>(a.logits + static_cast<size_t>(t) * a.E, a.sel_bias, a.E, a.k, a.router,
                     a.norm_topk, a.route_scale, s_ids, s_w);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (threadIdx.x == 0) {
+      if (lane == 0) {
         s_e = s_ids[slot];
         if (blockIdx.x == 0) {
           a.ids[p] = s_ids[slot];
@@ -294,6 +303,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   {
     const int Bx = MX ? 32 : 256;
