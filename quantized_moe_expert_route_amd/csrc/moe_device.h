@@ -651,6 +651,49 @@ __device__ __forceinline__ int topk_round(uint32_t (&key)[NC]) {
   return static_cast<int>(e);
 }
 
+// Expert index of rank n (0-based; n < the number of candidates), exact. Fast
+// path: n + 1 rounds of one wave max each, every candidate equal to the
+// round's maximum leaving; the rank-n expert is the one equal to the last
+// maximum. That is exact when every round's maximum is unique; the ballot
+// counts that check it sit off the dependent chain. Otherwise the exact
+// rounds (lowest index first among equal keys) run from the original keys.
+template <int NC>
+__device__ __forceinline__ int topk_nth(const uint32_t (&key0)[NC], int n) {
+  uint32_t key[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) key[i] = key0[i];
+  uint32_t kmax = 0;
+  int ties = 0;
+  for (int r = 0; r <= n; ++r) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < NC; ++i) best = max(best, key[i]);
+    kmax = wave_max_u32(best);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const bool hit = key[i] == kmax;
+      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(hit));
+      key[i] = hit ? 0u : key[i];
+    }
+    ties |= cnt != 1;
+  }
+  if (!ties) {  // wave-uniform
+    int e = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(key0[i] == kmax);
+      if (hit) e = min(e, static_cast<int>(__builtin_ctzll(hit)) + 64 * i);
+    }
+    return e;
+  }
+#pragma unroll
+  for (int i = 0; i < NC; ++i) key[i] = key0[i];
+  int e = 0;
+  for (int r = 0; r <= n; ++r) e = topk_round<NC>(key);
+  return e;
+}
+
 // Routing weights of the selected experts: lane r < k holds rank r's expert
 // my_id; lg as left by topk_keys. Softmax over the selected (norm_topk) or
 // over all E, or sigmoid (normalized over the selected when norm_topk), times

@@ -286,8 +286,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
         lg[i] = a.logits[static_cast<size_t>(t) * a.E + min(lane + 64 * i, a.E - 1)];
       uint32_t key[NC];
       topk_keys<NC>(lg, a.sel_bias, a.E, key);
-      int e = 0;
-      for (int r = 0; r <= slot; ++r) e = topk_round<NC>(key);
+      const int e = topk_nth<NC>(key, slot);
       if (lane == 0) s_e = e;
     } else {
       wave_topk<NC>(a.logits + static_cast<size_t>(t) * a.E, a.sel_bias, a.E, a.k, a.router,
