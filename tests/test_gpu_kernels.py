@@ -247,3 +247,47 @@ def test_route_ties_across_registers(E, router):
             got = idl.cpu().numpy()
             for i in range(Tl):
                 assert np.array_equal(got[i], refs[t0 + i]), ("layer", Tl, t0 + i, got[i])
+
+
+@pytest.mark.parametrize("E,router", [(256, gen.SOFTMAX), (384, gen.SIGMOID)])
+def test_decode_ties_outputs(E, router):
+    """Decode outputs under exact logit ties: every gate/up workgroup other than
+    the first of a pair selects its own slot's expert (the rank-n selection,
+    whose exact rounds run only after a tie), so a wrong choice among tied
+    experts changes y. The tied experts get distinct weights; y is checked
+    against the oracle token by token."""
+    from tests.gpu_common import Y_TOL, rel_err
+    cfg = gen.CONFIGS["qwen3.6-35b-a3b"].with_(name="ties-y", E=E, k=8, H=512, F=256,
+                                               router=router, norm_topk=1)
+    base = gen.make_layer(cfg, experts=[])
+    W = base.w_router
+    for e in (69, 133, 197):
+        W[e] = W[5]
+    W[70] = W[6]
+    W[E - 1] = W[2]
+    x, _ = gen.make_x(cfg, T=4)
+    x[0] = 0.0
+    x[1] = W[5] / np.linalg.norm(W[5]) * 10
+    x[2] = W[6] / np.linalg.norm(W[6]) * 10
+    x[3] = W[2] / np.linalg.norm(W[2]) * 10
+    used = set()
+    for t in range(4):
+        used |= {int(e) for e in oracle.topk(oracle.router_logits(W, x[t]), cfg.k)}
+    if cfg.shared:
+        used.add(cfg.E)
+    data = gen.make_layer(cfg, experts=sorted(used))
+    data.w_router = np.ascontiguousarray(W)
+    dl = DeviceLayer(data)
+    L = oracle.Layer(data)
+    y = torch.empty((1, cfg.H), dtype=torch.float32, device="cuda")
+    idl = torch.empty((1, cfg.k), dtype=torch.int32, device="cuda")
+    wl = torch.empty((1, cfg.k), dtype=torch.float32, device="cuda")
+    ws = dl.workspace(1)
+    for t in range(4):
+        say(f"decode ties E={E} token {t}")
+        M.moe_layer_forward(dl.desc, torch.from_numpy(x[t:t + 1]).cuda(), M.MOE_DTYPE_F32, 1, y,
+                            idl, wl, ws, ws.numel())
+        torch.cuda.synchronize()
+        ref = L.forward(x[t:t + 1])
+        assert np.array_equal(idl.cpu().numpy()[0], ref["ids"][0]), t
+        assert rel_err(y.cpu().numpy()[0], ref["y"][0]) <= Y_TOL, t
