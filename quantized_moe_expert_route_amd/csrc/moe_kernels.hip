@@ -242,6 +242,20 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
       F::load(raw[i], blk, sub);
     }
   };
+  // q8 activations (not MXFP4): this thread's first slice is loaded before the
+  // role work below, so that the selection wave does not issue it after its
+  // dependent chain; it goes to LDS after the roles.
+  int4 pre_q = make_int4(0, 0, 0, 0);
+  int16_t pre_bs = 0;
+  float pre_d = 0.0f;
+  if constexpr (!MX) {
+    const int tid = threadIdx.x;
+    if (tid < K / 16) {
+      pre_q = reinterpret_cast<const int4*>(a.xqs + static_cast<size_t>(t) * K)[tid];
+      pre_bs = a.xbs[static_cast<size_t>(t) * (K / 16) + tid];
+    }
+    if (tid < K / 256) pre_d = a.xd[static_cast<size_t>(t) * (K / 256) + tid];
+  }
   // The selection runs on one wave, chosen by the workgroup's place among
   // those resident on a compute unit (dispatch order: 256 per round), so that
   // the selection waves of co-resident workgroups run on different SIMDs.
@@ -304,10 +318,24 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
     }
     __builtin_amdgcn_s_setprio(0);
   }
-  {
-    const int Bx = MX ? 32 : 256;
-    stage_act<MX>(a.xqs + static_cast<size_t>(t) * K, a.xd + static_cast<size_t>(t) * (K / Bx),
-                  MX ? nullptr : a.xbs + static_cast<size_t>(t) * (K / 16), K, lqs, ld, lbs, lap);
+  if constexpr (MX) {
+    stage_act<true>(a.xqs + static_cast<size_t>(t) * K, a.xd + static_cast<size_t>(t) * (K / 32),
+                    nullptr, K, lqs, ld, lbs, lap);
+  } else {
+    const int tid = threadIdx.x;
+    const int8_t* qs = a.xqs + static_cast<size_t>(t) * K;
+    const int16_t* bs = a.xbs + static_cast<size_t>(t) * (K / 16);
+    const float* dd = a.xd + static_cast<size_t>(t) * (K / 256);
+    if (tid < K / 16) {
+      reinterpret_cast<int4*>(lqs)[tid] = pre_q;
+      lbs[tid] = pre_bs;
+    }
+    if (tid < K / 256) ld[tid] = pre_d;
+    for (int i = tid + 256; i < K / 16; i += 256) {
+      reinterpret_cast<int4*>(lqs)[i] = reinterpret_cast<const int4*>(qs)[i];
+      lbs[i] = bs[i];
+    }
+    for (int i = tid + 256; i < K / 256; i += 256) ld[i] = dd[i];
   }
   __syncthreads();
   const float* bg = nullptr;
