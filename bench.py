@@ -264,7 +264,8 @@ def kernel_names(cfg, path: str) -> dict:
         dn = "k_glds_q6k_down"
     else:
         dn = "k_down_grouped"
-    return {"router": "k_router_mfma", "gateup": gu, "down": dn}
+    rt = "k_router_mfma22" if cfg.T > 16 and cfg.E + 1 > 16 else "k_router_mfma"  # 2 x 2 blocked
+    return {"router": rt, "gateup": gu, "down": dn}
 
 
 _PATH_SOURCES = {

@@ -614,6 +614,17 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
 
 // ================================================================== kernels
 
+// q8 of one 256-element piece of x (job = token * pieces + piece), one wave.
+__device__ __forceinline__ void router_quant_wave(const KArgs& a, int job, int lane) {
+  const int pieces = a.H >> 8;
+  const int t = job / pieces, pc = job - t * pieces;
+  if (t >= a.T) return;
+  float v[4];
+  load_x4(a.x, a.x_dtype, static_cast<size_t>(t) * a.H + pc * 256 + 4 * lane, v);
+  const size_t base = static_cast<size_t>(t) * a.H + pc * 256;
+  quant_wave<256>(v, true, lane, a.xqs + base, a.xd + base / 256, a.xbs + base / 16);
+}
+
 // Router logits for many tokens: fp32 inputs, fp64 MFMA products and sums (the
 // products of fp32 values are exact in fp64). grid nwg_r + quant workgroups,
 // block 256. Router wave w: K slice w % KS of (token tile, expert tile) w / KS;
@@ -623,15 +634,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
                                                      int n_work, int nwg_r) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (static_cast<int>(blockIdx.x) >= nwg_r) {
-    if (!quant) return;
-    const int job = (blockIdx.x - nwg_r) * 4 + wave;
-    const int pieces = a.H >> 8;
-    const int t = job / pieces, pc = job - t * pieces;
-    if (t >= a.T) return;
-    float v[4];
-    load_x4(a.x, a.x_dtype, static_cast<size_t>(t) * a.H + pc * 256 + 4 * lane, v);
-    const size_t base = static_cast<size_t>(t) * a.H + pc * 256;
-    quant_wave<256>(v, true, lane, a.xqs + base, a.xd + base / 256, a.xbs + base / 16);
+    if (quant) router_quant_wave(a, (blockIdx.x - nwg_r) * 4 + wave, lane);
     return;
   }
   const int wv = blockIdx.x * 4 + wave;
@@ -686,6 +689,101 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
     if (tok < a.T && ex < E1)
       a.rpart[(static_cast<size_t>(ks) * a.T + tok) * E1 + ex] = acc[i];
   }
+}
+
+// Router logits, 2 x 2 register blocking (chunks of more than 16 tokens and
+// 16 experts): router wave w computes token tiles 2 tt .. 2 tt + 1 against
+// expert tiles 2 et .. 2 et + 1 over K slice w % KS, (tt, et) from w / KS.
+// Each loaded x and W fragment feeds two MFMAs, and the four accumulators are
+// independent chains. Same sums and partial layout as k_router_mfma (the k
+// order inside a slice is only a reordering of the sum). grid nwg_r + quant
+// workgroups, block 256.
+__global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int KS, int L,
+                                                       int n_et2, int n_work, int nwg_r) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (static_cast<int>(blockIdx.x) >= nwg_r) {
+    if (quant) router_quant_wave(a, (blockIdx.x - nwg_r) * 4 + wave, lane);
+    return;
+  }
+  const int wv = blockIdx.x * 4 + wave;
+  if (wv >= n_work) return;
+  const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
+  const int ks = wv % KS, r = wv / KS, et2 = r % n_et2, tt2 = r / n_et2;
+  const int g = lane >> 4, c = lane & 15;
+  int t[2];
+  const float* wr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    t[i] = min((2 * tt2 + i) * 16 + c, a.T - 1);
+    const int e = min((2 * et2 + i) * 16 + c, E1 - 1);
+    wr[i] = e < a.E ? a.w_router + static_cast<size_t>(e) * a.H : a.sh_gate_vec;
+  }
+  const int k0 = ks * L;
+  const int nst = (min(a.H, k0 + L) - k0) >> 4;  // steps of 16 (4 per lane group)
+  v4d acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
+  auto load_xv = [&](int tok, int kk) -> float4 {
+    const size_t o = static_cast<size_t>(tok) * a.H + kk;
+    if (a.x_dtype == 0) return ldg_f4(static_cast<const float*>(a.x) + o);
+    const uint2 bb = ld8(static_cast<const uint16_t*>(a.x) + o);
+    return make_float4(bf16_bits_to_f32(bb.x & 0xFFFF), bf16_bits_to_f32(bb.x >> 16),
+                       bf16_bits_to_f32(bb.y & 0xFFFF), bf16_bits_to_f32(bb.y >> 16));
+  };
+  auto step = [&](const float4 (&xv)[2], const float4 (&wv4)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            static_cast<double>(xv[i].x), static_cast<double>(wv4[j].x), acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            static_cast<double>(xv[i].y), static_cast<double>(wv4[j].y), acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            static_cast<double>(xv[i].z), static_cast<double>(wv4[j].z), acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            static_cast<double>(xv[i].w), static_cast<double>(wv4[j].w), acc[i][j], 0, 0, 0);
+      }
+  };
+  // MFMA step n, lane group g: k = k0 + 16 n + 4 g + s for s = 0..3
+  constexpr int U = 4;  // steps whose loads are issued together
+  int n = 0;
+  for (; n + U <= nst; n += U) {
+    float4 xv[U][2], wv4[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k0 + 16 * (n + u) + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        xv[u][i] = load_xv(t[i], kk);
+        wv4[u][i] = ldg_f4(wr[i] + kk);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) step(xv[u], wv4[u]);
+  }
+  for (; n < nst; ++n) {
+    const int kk = k0 + 16 * n + 4 * g;
+    float4 xv[2], wv4[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      xv[i] = load_xv(t[i], kk);
+      wv4[i] = ldg_f4(wr[i] + kk);
+    }
+    step(xv, wv4);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tok = (2 * tt2 + i) * 16 + g + 4 * q, ex = (2 * et2 + j) * 16 + c;
+        if (tok < a.T && ex < E1)
+          a.rpart[(static_cast<size_t>(ks) * a.T + tok) * E1 + ex] = acc[i][j][q];
+      }
 }
 
 // Per token (one wave): logit = fp32(sum of the K-slice partials in slice order),
@@ -996,10 +1094,19 @@ int glds_group(int RB, int max_tiles) {
 
 }  // namespace
 
+// The 2 x 2 blocked router kernel for chunks of more than 16 tokens and experts.
+bool router_blocked(int T, int E) { return T > 16 && E + 1 > 16; }
+
 RouterSplit router_split(int T, int E, int H) {
   const int E1 = E + 1;
-  const int tiles = ((T + 15) / 16) * ((E1 + 15) / 16);
-  int ks = (2048 + tiles - 1) / tiles;
+  int ks;
+  if (router_blocked(T, E)) {  // about one wave per SIMD (1024)
+    const int tiles2 = ((T + 31) / 32) * ((E1 + 31) / 32);
+    ks = 1024 / tiles2;
+  } else {
+    const int tiles = ((T + 15) / 16) * ((E1 + 15) / 16);
+    ks = (2048 + tiles - 1) / tiles;
+  }
   if (ks > 16) ks = 16;
   if (ks < 1) ks = 1;
   const int steps = (H + 15) / 16;
@@ -1016,10 +1123,17 @@ int max_tiles(int T, int k, int E, int has_shared) {
 hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hipStream_t s,
                                  Ev ev) {
   const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
+  const int nq = quant ? (a.T * (a.H / 256) + 3) / 4 : 0;
+  if (router_blocked(a.T, a.E)) {
+    const int n_et2 = (E1 + 31) / 32, n_tt2 = (a.T + 31) / 32;
+    const int n_work = n_tt2 * n_et2 * rs.ks;
+    const int nwg_r = (n_work + 3) / 4;
+    return launch(k_router_mfma22, dim3(nwg_r + nq), 256, 0, s, ev, a, quant ? 1 : 0, rs.ks,
+                  rs.len, n_et2, n_work, nwg_r);
+  }
   const int n_et = (E1 + 15) / 16, n_tt = (a.T + 15) / 16;
   const int n_work = n_tt * n_et * rs.ks;
   const int nwg_r = (n_work + 3) / 4;
-  const int nq = quant ? (a.T * (a.H / 256) + 3) / 4 : 0;
   return launch(k_router_mfma, dim3(nwg_r + nq), 256, 0, s, ev, a, quant ? 1 : 0, rs.ks, rs.len,
                 n_et, n_work, nwg_r);
 }
