@@ -161,7 +161,7 @@ WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool group
     L.part = take(P * H * 4);
   } else {
     // q8 of h for an MXFP4 down, quantized once per pair: fp16 pairs + scales
-    L.hqs = take(P * F * 2);
+    L.hqs = take(P * (F / 32) * 80);  // 80 bytes per 32-value block (kApPitch pairs)
     L.hd = take(P * (F / 32) * 4);
     L.hbs = 0;
     L.rpart = L.pair_tmp = L.plist = L.present = L.tiles = L.part = 0;

@@ -308,12 +308,17 @@ __device__ __forceinline__ void quant_wave(const float v[4], bool valid, int lan
   }
 }
 
+// fp16 pairs per block in the MXFP4 activation layout: 16 used + 4 of padding
+// (80 bytes), so that lanes reading consecutive blocks with 16-byte loads hit
+// different LDS banks.
+constexpr int kApPitch = 20;
+
 // B = 32 quantization stored as fp16 pairs (a[i], a[i+16]) per block, the layout
-// the MXFP4 dot reads: ap gets 128 pairs for the 256-value piece.
-// Stores the pairs element-major: ap[q * stride + block] (see ActView), with
-// ap pointing at the piece's first block column.
+// the MXFP4 dot reads: ap gets the 8 blocks of the 256-value piece.
+// Stores the pairs block-major: ap[block * kApPitch + q] (see ActView), with ap
+// pointing at the piece's first block; each lane writes 4 consecutive pairs.
 __device__ __forceinline__ void quant_wave_pairs(const float v[4], bool valid, int lane,
-                                                 half2_t* ap, int stride, float* d) {
+                                                 half2_t* ap, float* d) {
   int q[4];
   const float dv = quant_wave_q<32>(v, q);
   int o[4];
@@ -322,9 +327,11 @@ __device__ __forceinline__ void quant_wave_pairs(const float v[4], bool valid, i
     o[i] = __builtin_amdgcn_update_dpp(0, q[i], 0x104, 0xF, 0xF, false);
   const int bl = lane >> 3, off = 4 * (lane & 7);
   if (valid && off < 16) {
+    uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      ap[(off + i) * stride + bl] = half2_t{static_cast<_Float16>(q[i]), static_cast<_Float16>(o[i])};
+      w[i] = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(q[i]), static_cast<_Float16>(o[i])});
+    *reinterpret_cast<uint4*>(ap + bl * kApPitch + off) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   if (valid && (lane & 7) == 0) d[bl] = dv;
 }
@@ -334,11 +341,11 @@ struct ActView {
   const int8_t* qs;     // [K] (Q8_K)
   const float* d;       // [K / B]
   const int16_t* bs;    // [K / 16] (Q8_K)
-  // [16][K / 32] fp16 pairs (Q8_32), element-major: ap[i * ap_stride + b] =
-  // (a[32b+i], a[32b+16+i]), ap_stride = K / 32, so lanes that take
-  // consecutive blocks read consecutive LDS words (no bank conflicts)
+  // [K / 32][kApPitch] fp16 pairs (Q8_32), block-major: ap[b * kApPitch + i] =
+  // (a[32b+i], a[32b+16+i]) for i < 16 (then padding): one block is four
+  // 16-byte reads, and lanes that take consecutive blocks start 80 bytes
+  // apart (different banks)
   const half2_t* ap;
-  int ap_stride;
 };
 
 // ------------------------------------------------------------------ formats
@@ -461,21 +468,21 @@ struct FmtMXFP4 {
   // Exact: e2m1 values and int8 activations are exact in fp16, products exact in
   // fp32 and every partial sum is a multiple of 0.5 below 2^23.
   __device__ static __forceinline__ float dot(const Raw& r, const ActView& a, int b) {
-    const half2_t* ap = a.ap + b;
-    const int st = a.ap_stride;
+    const uint4* ap = reinterpret_cast<const uint4*>(a.ap + kApPitch * b);
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t qw = r.sh == 3 ? r.w[i + 1]
                                     : __builtin_amdgcn_alignbyte(r.w[i + 1], r.w[i], r.sh + 1);
+      const uint4 pr = ap[i];  // pairs 4 i .. 4 i + 3 (byte j of qw holds pair 4 i + j)
       acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 0),
-                                   ap[(4 * i + 0) * st], acc, false);
+                                   __builtin_bit_cast(half2_t, pr.x), acc, false);
       acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 1),
-                                   ap[(4 * i + 1) * st], acc, false);
+                                   __builtin_bit_cast(half2_t, pr.y), acc, false);
       acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 2),
-                                   ap[(4 * i + 2) * st], acc, false);
+                                   __builtin_bit_cast(half2_t, pr.z), acc, false);
       acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 3),
-                                   ap[(4 * i + 3) * st], acc, false);
+                                   __builtin_bit_cast(half2_t, pr.w), acc, false);
     }
     return acc;
   }
@@ -516,9 +523,9 @@ __device__ __forceinline__ void stage_act(const int8_t* qs, const float* d, cons
     }
     for (int i = tid; i < K / 256; i += nt) ld[i] = d[i];
   } else {
-    for (int i = tid; i < K / 2; i += nt) {  // element-major (see ActView)
+    for (int i = tid; i < K / 2; i += nt) {  // block-major, padded (see ActView)
       const int b = i / 16, ii = i % 16;
-      lap[ii * (K / 32) + b] = half2_t{static_cast<_Float16>(qs[32 * b + ii]),
+      lap[b * kApPitch + ii] = half2_t{static_cast<_Float16>(qs[32 * b + ii]),
                                        static_cast<_Float16>(qs[32 * b + 16 + ii])};
     }
     for (int i = tid; i < K / 32; i += nt) ld[i] = d[i];

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
   const int K = a.H, nb = K / F::BE;
   int8_t* lqs = reinterpret_cast<int8_t*>(smem);
   half2_t* lap = reinterpret_cast<half2_t*>(smem);
-  const int act_bytes = MX ? K * 2 : K;
+  const int act_bytes = MX ? K * 5 / 2 : K;  // MXFP4: 80 bytes per 32-value block
   float* ld = reinterpret_cast<float*>(smem + act_bytes);
   int16_t* lbs = reinterpret_cast<int16_t*>(smem + act_bytes + 4 * (K / 32));
   float* vals = reinterpret_cast<float*>(smem + act_bytes + 4 * (K / 32) + 2 * (K / 16));
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
     issue_loads();
     if (a.b_gate) { bg = a.b_gate[e]; bu = a.b_up[e]; }
   }
-  ActView av{lqs, ld, lbs, lap, K / 32};
+  ActView av{lqs, ld, lbs, lap};
 #pragma unroll
   for (int i = 0; i < TPG; ++i) {
     const int task = grp + G * i;
@@ -407,7 +407,8 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
 
 // q8 (32-value blocks) of every pair's h for an MXFP4 down, once per pair,
 // stored as the down kernel's LDS image: fp16 pairs (a[32b + i], a[32b + 16 + i])
-// element-major ([i][block], as ActView reads them) and one scale per block. grid ceil(P pieces / 4), block 256: one wave per
+// block-major and padded ([block][kApPitch], as ActView reads them) and one
+// scale per block. grid ceil(P pieces / 4), block 256: one wave per
 // 256-value piece (fp32 recipe; values past F belong to no block).
 __global__ __launch_bounds__(256) void k_hquant_pairs(KArgs a, int P, Div dpc) {
   const int lane = threadIdx.x & 63;
@@ -421,8 +422,9 @@ __global__ __launch_bounds__(256) void k_hquant_pairs(KArgs a, int P, Div dpc) {
   const float v[4] = {valid ? hv.x : 0.0f, valid ? hv.y : 0.0f, valid ? hv.z : 0.0f,
                       valid ? hv.w : 0.0f};
   quant_wave_pairs(v, valid, lane,
-                   reinterpret_cast<half2_t*>(a.hqs) + static_cast<size_t>(p) * (a.F / 2) + pc * 8,
-                   a.F / 32, a.hd + static_cast<size_t>(p) * (a.F / 32) + pc * 8);
+                   reinterpret_cast<half2_t*>(a.hqs) +
+                       (static_cast<size_t>(p) * (a.F / 32) + pc * 8) * kApPitch,
+                   a.hd + static_cast<size_t>(p) * (a.F / 32) + pc * 8);
 }
 
 // ---------------------------------------------------------------- down GEMV
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
   const int t = blockIdx.y, row0 = blockIdx.x * R;
   const int K = a.F, nb = K / F::BE;
   const int ns = a.k + a.has_shared;
-  const int act_bytes = MX ? K * 2 : K;
+  const int act_bytes = MX ? K * 5 / 2 : K;  // MXFP4: 80 bytes per 32-value block
   unsigned char* p_act = smem;
   float* ld = reinterpret_cast<float*>(smem + ns * act_bytes);
   int16_t* lbs = reinterpret_cast<int16_t*>(smem + ns * act_bytes + ns * 4 * (K / 32));
@@ -520,13 +522,13 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
     // h already quantized per pair (MXFP4 down): copy the LDS image of every
     // present slot, 16 bytes per thread and step
     const int qt = threadIdx.x - 256;
-    const int n16 = K / 8;  // 16-byte pieces of one slot's fp16 pairs (2K bytes)
+    const int n16 = act_bytes / 16;  // 16-byte pieces of one slot's fp16 pairs
     for (int i = qt; i < ns * n16; i += 256) {
       const int s = i / n16, j = i - s * n16;
       if ((present >> s) & 1u) {
         const int ps = s < a.k ? t * a.k + s : a.T * a.k + t;
         reinterpret_cast<int4*>(p_act + s * act_bytes)[j] =
-            reinterpret_cast<const int4*>(a.hqs + static_cast<size_t>(ps) * (2 * K))[j];
+            reinterpret_cast<const int4*>(a.hqs + static_cast<size_t>(ps) * act_bytes)[j];
       }
     }
     for (int i = qt; i < ns * (K / 32); i += 256) {
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
                       ld + s * (K / 32) + pc, lbs + s * (K / 16) + pc * 16);
       } else {
         quant_wave_pairs(v, valid, lane,
-                         reinterpret_cast<half2_t*>(p_act + s * act_bytes) + pc * 8, K / 32,
+                         reinterpret_cast<half2_t*>(p_act + s * act_bytes) + pc * 8 * kApPitch,
                          ld + s * (K / 32) + pc * 8);
       }
     };
@@ -590,8 +592,7 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
       const int b = dnb.mod(task, q1), r = dR.mod(q1, q2), s = q2;
       if (task < total && row0 + r < a.H && ((present >> s) & 1u)) {
         ActView av{reinterpret_cast<const int8_t*>(p_act + s * act_bytes), ld + s * (K / 32),
-                   lbs + s * (K / 16), reinterpret_cast<const half2_t*>(p_act + s * act_bytes),
-                   K / 32};
+                   lbs + s * (K / 16), reinterpret_cast<const half2_t*>(p_act + s * act_bytes)};
         const float v = block_value<F>(raw[i], av, b, sub);
         if (sub == 0) vals[(s * R + r) * nb + b] = v;
       }
@@ -796,14 +797,14 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* rows, int K, 
   using F = typename FmtOf<FMT>::T;
   constexpr bool MX = FMT == FMT_MXFP4;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int act_bytes = MX ? K * 2 : K;
+  const int act_bytes = MX ? K * 5 / 2 : K;
   int8_t* lqs = reinterpret_cast<int8_t*>(smem);
   half2_t* lap = reinterpret_cast<half2_t*>(smem);
   float* ld = reinterpret_cast<float*>(smem + act_bytes);
   int16_t* lbs = reinterpret_cast<int16_t*>(smem + act_bytes + 4 * (K / 32));
   stage_act<MX>(qs, d, bs, K, lqs, ld, lbs, lap);
   __syncthreads();
-  ActView av{lqs, ld, lbs, lap, K / 32};
+  ActView av{lqs, ld, lbs, lap};
   const int r = blockIdx.x, nb = K / F::BE;
   const int G = 256 / F::LPB, grp = threadIdx.x / F::LPB, sub = threadIdx.x % F::LPB;
   for (int b = grp; b < nb; b += G) {
@@ -842,7 +843,7 @@ size_t gateup_lds(const KArgs& a, GemvShape* out) {
   GemvShape sh = gemv_shape(a.F, 2, nb, F::LPB, P, tpg_max, 512);
   if (out) *out = sh;
   const bool MX = FMT == FMT_MXFP4;
-  return (MX ? 2 * a.H : a.H) + 4 * (a.H / 32) + 2 * (a.H / 16) +
+  return (MX ? 5 * a.H / 2 : a.H) + 4 * (a.H / 32) + 2 * (a.H / 16) +
          4 * static_cast<size_t>((2 * sh.R * nb + 2 * sh.R * kSumChunks + 1) & ~1) +
          16 * static_cast<size_t>(a.E);
 }
@@ -863,7 +864,7 @@ size_t down_lds(const KArgs& a, GemvShape* out) {
   GemvShape sh{R, (ns * R * nb + G - 1) / G};
   if (out) *out = sh;
   const bool MX = FMT == FMT_MXFP4;
-  return ns * ((MX ? 2 * a.F : a.F) + 4 * (a.F / 32) + 2 * (a.F / 16)) +
+  return ns * ((MX ? 5 * a.F / 2 : a.F) + 4 * (a.F / 32) + 2 * (a.F / 16)) +
          4 * static_cast<size_t>(ns * sh.R * nb) + 4 * static_cast<size_t>(ns * sh.R) +
          4 * static_cast<size_t>(ns * sh.R * kSumChunks);
 }
@@ -1034,7 +1035,7 @@ hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_
                              const int8_t* qs, const float* d, const int16_t* bs, int32_t* out,
                              hipStream_t s) {
   const uint8_t* r = static_cast<const uint8_t*>(rows);
-  const size_t lds = (fmt == FMT_MXFP4 ? 2 * K : K) + 4 * (K / 32) + 2 * (K / 16);
+  const size_t lds = (fmt == FMT_MXFP4 ? 5 * K / 2 : K) + 4 * (K / 32) + 2 * (K / 16);
   switch (fmt) {
     case FMT_Q4_K:
       return launch(k_block_dots<FMT_Q4_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
