@@ -692,11 +692,13 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
 }
 
 // Router logits, 2 x 2 register blocking (chunks of more than 16 tokens and
-// 16 experts): router wave w computes token tiles 2 tt .. 2 tt + 1 against
-// expert tiles 2 et .. 2 et + 1 over K slice w % KS, (tt, et) from w / KS.
-// Each loaded x and W fragment feeds two MFMAs, and the four accumulators are
-// independent chains. Same sums and partial layout as k_router_mfma (the k
-// order inside a slice is only a reordering of the sum). grid nwg_r + quant
+// 16 experts): a router wave computes token tiles 2 tt .. 2 tt + 1 against
+// expert tiles 2 et .. 2 et + 1 over one of 8 K slices. Each loaded x and W
+// fragment feeds two MFMAs, and the four accumulators are independent chains.
+// K slice s is computed by workgroups s, s + 8, s + 16, ..., the ones that run
+// on XCD s (dispatch order), so each slice's x and W are read into one L2. Same
+// sums and partial layout as k_router_mfma (the k order inside a slice is only
+// a reordering of the sum). grid nwg_r (8 per 4 tile pairs) + quant
 // workgroups, block 256.
 __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int KS, int L,
                                                        int n_et2, int n_work, int nwg_r) {
@@ -705,10 +707,11 @@ __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int K
     if (quant) router_quant_wave(a, (blockIdx.x - nwg_r) * 4 + wave, lane);
     return;
   }
-  const int wv = blockIdx.x * 4 + wave;
-  if (wv >= n_work) return;
+  const int ks = blockIdx.x & 7;  // KS == 8
+  const int r = (blockIdx.x >> 3) * 4 + wave;  // tile pair
+  if (r >= n_work || ks >= KS) return;
   const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
-  const int ks = wv % KS, r = wv / KS, et2 = r % n_et2, tt2 = r / n_et2;
+  const int et2 = r % n_et2, tt2 = r / n_et2;
   const int g = lane >> 4, c = lane & 15;
   int t[2];
   const float* wr[2];
@@ -1100,9 +1103,8 @@ bool router_blocked(int T, int E) { return T > 16 && E + 1 > 16; }
 RouterSplit router_split(int T, int E, int H) {
   const int E1 = E + 1;
   int ks;
-  if (router_blocked(T, E)) {  // about one wave per SIMD (1024)
-    const int tiles2 = ((T + 31) / 32) * ((E1 + 31) / 32);
-    ks = 1024 / tiles2;
+  if (router_blocked(T, E)) {  // 8 slices, one per XCD (H / 16 >= 16)
+    ks = 8;
   } else {
     const int tiles = ((T + 15) / 16) * ((E1 + 15) / 16);
     ks = (2048 + tiles - 1) / tiles;
@@ -1126,8 +1128,8 @@ hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hip
   const int nq = quant ? (a.T * (a.H / 256) + 3) / 4 : 0;
   if (router_blocked(a.T, a.E)) {
     const int n_et2 = (E1 + 31) / 32, n_tt2 = (a.T + 31) / 32;
-    const int n_work = n_tt2 * n_et2 * rs.ks;
-    const int nwg_r = (n_work + 3) / 4;
+    const int n_work = n_tt2 * n_et2;  // tile pairs, each in all 8 K slices
+    const int nwg_r = 8 * ((n_work + 3) / 4);
     return launch(k_router_mfma22, dim3(nwg_r + nq), 256, 0, s, ev, a, quant ? 1 : 0, rs.ks,
                   rs.len, n_et2, n_work, nwg_r);
   }
