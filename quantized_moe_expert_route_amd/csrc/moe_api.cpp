@@ -124,10 +124,6 @@ struct Stages {
 // selected expert's weights once per 16 tokens routed to it.
 constexpr int kGroupedMinTokens = 5;
 
-// GEMV path rule: an MXFP4 down (q8 of h in 32-value blocks, F up to a few
-// thousand) gets h quantized once per pair by its own kernel; Q4_K / Q6_K downs
-// quantize h inside every down workgroup, overlapped with the row stream.
-bool gemv_hquant(int fmt_down) { return fmt_down == FMT_MXFP4; }
 
 bool use_grouped(int T, int fmt_gate, int fmt_down) {
   return T >= kGroupedMinTokens && fmt_gate != FMT_MXFP4 && fmt_down != FMT_MXFP4;
@@ -261,7 +257,7 @@ static moe_status expert_ffn_impl(KArgs& a, bool grouped, bool routing_given, hi
     if (e == hipSuccess) e = launch_combine(a, stream, st.next());
   } else {
     e = launch_gateup(a, routing_given, stream, st.next());
-    if (e == hipSuccess && gemv_hquant(a.fmt_d)) e = launch_hquant_pairs(a, stream, st.next());
+    if (e == hipSuccess && gemv_hquant(a.fmt_d, a.F, a.k, a.has_shared)) e = launch_hquant_pairs(a, stream, st.next());
     if (e == hipSuccess) e = launch_down(a, stream, st.next());
   }
   return hip_status(e);
@@ -351,7 +347,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, mo
 int moe_layer_stage_count(const moe_layer_desc* desc, int T) {
   if (validate_desc(desc) != MOE_OK || T <= 0 || T > kMaxTokens) return 0;
   if (use_grouped(T, desc->fmt_gate, desc->fmt_down)) return 7;
-  return gemv_hquant(desc->fmt_down) ? 4 : 3;
+  return gemv_hquant(desc->fmt_down, desc->ffn, desc->top_k, desc->sh_gate != nullptr) ? 4 : 3;
 }
 
 const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {

@@ -499,6 +499,108 @@ template <> struct FmtOf<FMT_Q4_K> { using T = FmtQ4K; };
 template <> struct FmtOf<FMT_Q6_K> { using T = FmtQ6K; };
 template <> struct FmtOf<FMT_MXFP4> { using T = FmtMXFP4; };
 
+// ------------------------------------------------------- MXFP4 decode GEMV
+// A 17-byte block has no fixed alignment, so one lane per block would need five
+// dword loads spread over 17-byte steps; the memory pipeline then spends ~24
+// cycles per such load for 256 useful bytes. Instead a wave reads two rows at a
+// time as coalesced 16-byte pieces (piece j = lane + 64 m of the pair: row 0's
+// npc pieces, then row 1's), realigns them through its own LDS scratch, and
+// every lane dots the blocks it owns (b = lane + 64 i) against activation pairs
+// it keeps in registers.
+
+__host__ __device__ inline int mx_row_pieces(int nb) { return (17 * nb + 15) / 16; }
+// Per-wave scratch: two rows of pieces plus one dword that the five-dword
+// window of a row's last block may reach past them.
+__host__ __device__ inline int mx_scratch_bytes(int nb) { return 32 * mx_row_pieces(nb) + 16; }
+
+template <int NBL>
+struct MxAct {
+  half2_t ap[NBL][16];
+  float d[NBL];
+};
+
+// The lane's blocks of one activation vector from its LDS image (ActView layout).
+template <int NBL>
+__device__ __forceinline__ void mx_act_load(MxAct<NBL>& A, const half2_t* lap, const float* ld,
+                                            int nb, int lane) {
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    const int b = lane + 64 * i;
+    const uint4* p = reinterpret_cast<const uint4*>(lap + min(b, nb - 1) * kApPitch);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = p[c];
+      A.ap[i][4 * c] = __builtin_bit_cast(half2_t, v.x);
+      A.ap[i][4 * c + 1] = __builtin_bit_cast(half2_t, v.y);
+      A.ap[i][4 * c + 2] = __builtin_bit_cast(half2_t, v.z);
+      A.ap[i][4 * c + 3] = __builtin_bit_cast(half2_t, v.w);
+    }
+    A.d[i] = b < nb ? ld[b] : 0.0f;
+  }
+}
+
+// Dot of one block (five dwords from its aligned start, byte offset sh) with
+// its 16 activation pairs; exact as in FmtMXFP4::dot.
+__device__ __forceinline__ float mx_dot_regs(const FmtMXFP4::Raw& r, const half2_t (&ap)[16]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t qw = r.sh == 3 ? r.w[i + 1]
+                                  : __builtin_amdgcn_alignbyte(r.w[i + 1], r.w[i], r.sh + 1);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 0),
+                                 ap[4 * i], acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 1),
+                                 ap[4 * i + 1], acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 2),
+                                 ap[4 * i + 2], acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 3),
+                                 ap[4 * i + 3], acc, false);
+  }
+  return acc;
+}
+
+// One row pair: the lane's NL pieces go to the wave's scratch, then each lane
+// sums the values of its blocks in both rows; returns the two row sums (every
+// lane), reduced in a fixed order.
+template <int NL, int NBL>
+__device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, int nb,
+                                          const MxAct<NBL>& A, int lane) {
+  const int npc = mx_row_pieces(nb);
+#pragma unroll
+  for (int m = 0; m < NL; ++m) {
+    const int j = lane + 64 * m;
+    if (j < 2 * npc) reinterpret_cast<uint4*>(scr)[j] = pc[m];
+  }
+  // LDS operations of one wave complete in order: the fences only keep the
+  // compiler from moving the reads above the writes (and the next pair's
+  // writes above these reads)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    const int b = lane + 64 * i;
+    if (b < nb) {
+#pragma unroll
+      for (int row = 0; row < 2; ++row) {
+        const uint32_t o = static_cast<uint32_t>(row * 16 * npc + 17 * b);
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(scr + (o & ~3u));
+        FmtMXFP4::Raw r;
+#pragma unroll
+        for (int k = 0; k < 5; ++k) r.w[k] = wp[k];
+        r.sh = o & 3u;
+        const float v = FmtMXFP4::value_from_dot(r, mx_dot_regs(r, A.ap[i]), A.d[i]);
+        if (row == 0) s0 += v; else s1 += v;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return make_float2(wave_sum(s0), wave_sum(s1));
+}
+
 // fp32 value of one block for the lane's share (all LPB lanes get the value).
 template <class F>
 __device__ __forceinline__ float block_value(const typename F::Raw& r, const ActView& a, int b,

@@ -113,10 +113,13 @@ constexpr size_t kMaxLds = 64 * 1024;
 
 // Whether the GEMV kernels' LDS needs fit for this layer and chunk.
 bool gemv_fits(const KArgs& a);
+// GEMV path: whether the down projection needs h quantized by its own kernel
+// first (an MXFP4 down too large for the fused kernel). Otherwise every down
+// workgroup quantizes h itself, overlapped with its row stream.
+bool gemv_hquant(int fmt_down, int F, int k, int has_shared);
 
 // Which expert-FFN path a chunk of T tokens takes (fixed rule, see moe_api.cpp).
 bool use_grouped(int T, int fmt_gate, int fmt_down);
-bool gemv_hquant(int fmt_down);
 
 // Router split of the grouped path: K slices of `len` elements (multiple of 16).
 struct RouterSplit { int ks, len; };

@@ -427,6 +427,177 @@ __global__ __launch_bounds__(256) void k_hquant_pairs(KArgs a, int P, Div dpc) {
                    a.hd + static_cast<size_t>(p) * (a.F / 32) + pc * 8);
 }
 
+// MXFP4 gate/up (the rows realigned per wave, see mx_pair). grid
+// (ceil(F / (4 RPW)), P), block 256: wave w takes the row pairs (gate row r,
+// up row r), r = row0 + w + 4 i for i < RPW. Routing and pointer tables as in
+// k_gateup; each wave issues all its 16-byte row pieces as soon as the expert
+// is known, then reduces each pair and applies the activation on lane 0.
+// LDS: activation pairs [nb][kApPitch], scales [nb], 4 wave scratches, [E][2]
+// gate/up pointers.
+__host__ __device__ inline int mx_gu_scratch_offset(int nb) { return (84 * nb + 15) & ~15; }
+
+template <int RPW, int NL, int NBL, int NC>
+__global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_e;
+  __shared__ int s_ids[16];
+  __shared__ float s_w[16];
+  const int p = blockIdx.y, row0 = blockIdx.x * (4 * RPW);
+  const int Tk = a.T * a.k;
+  const bool routed = p < Tk;
+  const int t = routed ? p / a.k : p - Tk;
+  const int K = a.H, nb = K / 32, npc = mx_row_pieces(nb);
+  half2_t* lap = reinterpret_cast<half2_t*>(smem);
+  float* ld = reinterpret_cast<float*>(smem + 80 * nb);
+  const int scr_bytes = mx_scratch_bytes(nb);
+  uint8_t* scr0 = smem + mx_gu_scratch_offset(nb);
+  const void** ltab = reinterpret_cast<const void**>(scr0 + 4 * scr_bytes);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint8_t* gbase = nullptr;
+  const uint8_t* ubase = nullptr;
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.counters);
+  uint4 pcs[RPW][NL];
+  auto issue = [&]() {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int r = row0 + wave + 4 * i;
+#pragma unroll
+      for (int m = 0; m < NL; ++m) {
+        const int j = lane + 64 * m;
+        const bool up = j >= npc;
+        const int q = up ? j - npc : j;
+        const uint8_t* src = (j < 2 * npc && r < a.F)
+                                 ? (up ? ubase + static_cast<size_t>(r) * a.stride_up
+                                       : gbase + static_cast<size_t>(r) * a.stride_gate) + 16 * q
+                                 : dummy;
+        pcs[i][m] = ld_nt16(src);
+      }
+    }
+  };
+  // selection on one wave, rotated by the workgroup's residency index (see k_gateup)
+  const int tkw = ((blockIdx.x + blockIdx.y * gridDim.x) >> 8) & 3;
+  // the other three waves stage x's q8 as fp16 pairs, one 32-value block per
+  // thread; the first block's loads are issued before the role work
+  const int li = (wave - (wave > tkw ? 1 : 0)) * 64 + lane;  // 0..191 off the selection wave
+  const int8_t* xq = a.xqs + static_cast<size_t>(t) * K;
+  const float* xd = a.xd + static_cast<size_t>(t) * nb;
+  int4 xq0 = make_int4(0, 0, 0, 0), xq1 = xq0;
+  float xdv = 0.0f;
+  if (wave != tkw && li < nb) {
+    xq0 = reinterpret_cast<const int4*>(xq)[2 * li];
+    xq1 = reinterpret_cast<const int4*>(xq)[2 * li + 1];
+    xdv = xd[li];
+  }
+  if (!routed) {
+    gbase = static_cast<const uint8_t*>(a.sh_gate);
+    ubase = static_cast<const uint8_t*>(a.sh_up);
+    issue();  // the shared expert does not wait for routing
+  } else if (wave != tkw) {
+    const int li = (wave - (wave > tkw ? 1 : 0)) * 64 + lane;  // 0..191
+    const void* g[6];
+    const void* u[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int i = min(li + 192 * j, a.E - 1);
+      g[j] = a.gate[i];
+      u[j] = a.up[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int i = li + 192 * j;
+      if (i < a.E) {
+        ltab[2 * i] = g[j];
+        ltab[2 * i + 1] = u[j];
+      }
+    }
+  } else {
+    const int slot = p - t * a.k;
+    __builtin_amdgcn_s_setprio(3);
+    if (routing_given) {
+      if (lane == 0) s_e = a.ids[p];
+    } else {
+      wave_topk<NC>(a.logits + static_cast<size_t>(t) * a.E, a.sel_bias, a.E, a.k, a.router,
+                    a.norm_topk, a.route_scale, s_ids, s_w);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lane == 0) {
+        s_e = s_ids[slot];
+        if (blockIdx.x == 0) {
+          a.ids[p] = s_ids[slot];
+          a.w[p] = s_w[slot];
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+  if (wave != tkw) {
+    for (int b = li; b < nb; b += 192) {
+      if (b != li) {
+        xq0 = reinterpret_cast<const int4*>(xq)[2 * b];
+        xq1 = reinterpret_cast<const int4*>(xq)[2 * b + 1];
+        xdv = xd[b];
+      }
+      const uint32_t lo[4] = {static_cast<uint32_t>(xq0.x), static_cast<uint32_t>(xq0.y),
+                              static_cast<uint32_t>(xq0.z), static_cast<uint32_t>(xq0.w)};
+      const uint32_t hi[4] = {static_cast<uint32_t>(xq1.x), static_cast<uint32_t>(xq1.y),
+                              static_cast<uint32_t>(xq1.z), static_cast<uint32_t>(xq1.w)};
+      uint4* dst = reinterpret_cast<uint4*>(lap + b * kApPitch);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {  // pairs 4c..4c+3: (a[4c + j], a[16 + 4c + j])
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = __builtin_bit_cast(
+              uint32_t, half2_t{static_cast<_Float16>(static_cast<int8_t>(lo[c] >> (8 * j))),
+                                static_cast<_Float16>(static_cast<int8_t>(hi[c] >> (8 * j)))});
+        dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      ld[b] = xdv;
+    }
+  }
+  __syncthreads();
+  const float* bg = nullptr;
+  const float* bu = nullptr;
+  if (routed) {
+    const int e = s_e;
+    if (static_cast<unsigned>(e) >= static_cast<unsigned>(a.E)) {  // invalid id: no-op
+      if (blockIdx.x == 0 && threadIdx.x == 0) a.slots[p] = SlotRef{nullptr, nullptr};
+      return;
+    }
+    gbase = static_cast<const uint8_t*>(ltab[2 * e]);
+    if (gbase == nullptr) {  // expert not present: the slot contributes nothing
+      if (blockIdx.x == 0 && threadIdx.x == 0) a.slots[p] = SlotRef{nullptr, nullptr};
+      return;
+    }
+    ubase = static_cast<const uint8_t*>(ltab[2 * e + 1]);
+    issue();
+    if (a.b_gate) { bg = a.b_gate[e]; bu = a.b_up[e]; }
+  }
+  MxAct<NBL> A;
+  mx_act_load(A, lap, ld, nb, lane);
+  float* hrow = a.h + static_cast<size_t>(p) * a.F;
+  uint8_t* scr = scr0 + wave * scr_bytes;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int r = row0 + wave + 4 * i;
+    if (r < a.F) {
+      const float2 gu = mx_pair<NL, NBL>(pcs[i], scr, nb, A, lane);
+      if (lane == 0) {
+        float g = gu.x, u = gu.y;
+        if (bg) { g += bg[r]; u += bu[r]; }
+        hrow[r] = act_fn(a.act, a.act_alpha, a.act_limit, g, u);
+      }
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && routed) {
+    SlotRef ref;
+    ref.down = static_cast<const uint8_t*>(a.down[s_e]);
+    ref.bias = a.b_down ? a.b_down[s_e] : nullptr;
+    a.slots[p] = ref;
+  }
+}
+
 // ---------------------------------------------------------------- down GEMV
 // grid (ceil(H / R), T), block 512. For each present slot of token t (and the
 // shared expert): down rows [row0, row0 + R) against q8(h), then
@@ -788,6 +959,145 @@ __global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, D
   }
 }
 
+// MXFP4 down with the rows realigned per wave (see mx_pair). grid
+// (ceil(H / R), T), block 512, R even. Units are (slot s, row pair r, r + 1)
+// for s < ns, taken slot-major; wave w owns units [w upw, (w + 1) upw) and
+// issues up to RPW of them at a time. Each wave first loads the h pieces of
+// its quantization jobs (256 values of one slot's h, job = wave + 8 u), then
+// its first weight batch, then quantizes (32-value blocks, fp32 recipe) into
+// the LDS image: loads complete in issue order, so the quantization waits for
+// h only. The weighted slot outputs are then summed in slot order, as in
+// k_down.
+// LDS: activation pairs [ns][nb][kApPitch], scales [ns][nb], 8 wave
+// scratches, slot outputs [R][ns].
+// h quantization jobs per wave (256-value pieces of every slot over 8 waves);
+// the host keeps ns * ceil(F / 256) <= 8 * kMxDownJobs.
+constexpr int kMxDownJobs = 8;
+__host__ __device__ inline int mx_down_scratch_offset(int ns, int nb) {
+  return (84 * ns * nb + 15) & ~15;
+}
+
+template <int RPW, int NL, int NBL>
+__global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int t = blockIdx.y, row0 = blockIdx.x * R;
+  const int K = a.F, nb = K / 32, npc = mx_row_pieces(nb);
+  const int ns = a.k + a.has_shared;
+  const int act_bytes = 80 * nb;
+  unsigned char* p_act = smem;
+  float* ld = reinterpret_cast<float*>(smem + ns * act_bytes);
+  const int scr_bytes = mx_scratch_bytes(nb);
+  uint8_t* scr = smem + mx_down_scratch_offset(ns, nb) + (threadIdx.x >> 6) * scr_bytes;
+  float* part = reinterpret_cast<float*>(smem + mx_down_scratch_offset(ns, nb) + 8 * scr_bytes);
+  __shared__ const uint8_t* dptr[17];
+  __shared__ const float* dbias[17];
+  __shared__ float wslot[17];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.counters);
+  if (threadIdx.x < ns) {
+    const int s = threadIdx.x;
+    if (s < a.k) {
+      const SlotRef ref = a.slots[t * a.k + s];
+      dptr[s] = ref.down;
+      dbias[s] = ref.bias;
+      wslot[s] = a.w[t * a.k + s];
+    } else {
+      dptr[s] = static_cast<const uint8_t*>(a.sh_down);
+      dbias[s] = nullptr;
+      wslot[s] = a.sh_gate_vec ? a.shw[t] : 1.0f;
+    }
+  }
+  __syncthreads();
+  const uint32_t present = static_cast<uint32_t>(
+      __builtin_amdgcn_ballot_w64(lane < ns && dptr[min(lane, ns - 1)] != nullptr));
+  const int nrp = (R + 1) / 2, units = ns * nrp, upw = (units + 7) / 8;
+  const int u0 = wave * upw, u1 = min(u0 + upw, units);
+  uint4 pcs[RPW][NL];
+  auto issue = [&](int ub) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int u = ub + i;
+      const int s = u < u1 ? u / nrp : 0;
+      const int r = row0 + 2 * (u - s * nrp);
+      const uint8_t* base = (u < u1 && ((present >> s) & 1u)) ? dptr[s] : nullptr;
+#pragma unroll
+      for (int m = 0; m < NL; ++m) {
+        const int j = lane + 64 * m;
+        const int hi = j >= npc ? 1 : 0;
+        const int rr = r + hi;
+        const bool ok = base != nullptr && j < 2 * npc && rr < a.H;
+        pcs[i][m] = ld_nt16(ok ? base + static_cast<size_t>(rr) * a.stride_down +
+                                     16 * (j - hi * npc)
+                               : dummy);
+      }
+    }
+  };
+  const int pieces = (K + 255) / 256, njobs = ns * pieces;
+  float4 hv[kMxDownJobs];
+#pragma unroll
+  for (int u = 0; u < kMxDownJobs; ++u) {
+    const int job = wave + 8 * u;  // wave-uniform
+    if (job < njobs) {
+      const int s = job / pieces, e0 = (job - s * pieces) * 256 + 4 * lane;
+      const int ps = s < a.k ? t * a.k + s : a.T * a.k + t;
+      hv[u] = *reinterpret_cast<const float4*>(a.h + static_cast<size_t>(ps) * K +
+                                               (e0 < K ? e0 : 0));
+    }
+  }
+  issue(u0);
+#pragma unroll
+  for (int u = 0; u < kMxDownJobs; ++u) {
+    const int job = wave + 8 * u;
+    if (job < njobs) {
+      const int s = job / pieces, pc = job - s * pieces;
+      if ((present >> s) & 1u) {
+        const bool valid = pc * 256 + 4 * lane < K;
+        const float v[4] = {valid ? hv[u].x : 0.0f, valid ? hv[u].y : 0.0f,
+                            valid ? hv[u].z : 0.0f, valid ? hv[u].w : 0.0f};
+        quant_wave_pairs(v, valid, lane,
+                         reinterpret_cast<half2_t*>(p_act + s * act_bytes) + pc * 8 * kApPitch,
+                         ld + s * nb + pc * 8);
+      }
+    }
+  }
+  __syncthreads();
+  MxAct<NBL> A;
+  int cur = -1;  // slot whose activations A holds (wave-uniform)
+  for (int ub = u0; ub < u1; ub += RPW) {
+    if (ub != u0) issue(ub);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int u = ub + i;
+      if (u < u1) {
+        const int s = u / nrp, rp = u - s * nrp, r = row0 + 2 * rp;
+        if (((present >> s) & 1u) && r < a.H) {
+          if (s != cur) {
+            mx_act_load(A, reinterpret_cast<const half2_t*>(p_act + s * act_bytes), ld + s * nb,
+                        nb, lane);
+            cur = s;
+          }
+          const float2 o = mx_pair<NL, NBL>(pcs[i], scr, nb, A, lane);
+          if (lane == 0) {
+            const float* bias = dbias[s];
+            part[(2 * rp) * ns + s] = wslot[s] * (o.x + (bias ? bias[r] : 0.0f));
+            if (2 * rp + 1 < R && r + 1 < a.H)
+              part[(2 * rp + 1) * ns + s] = wslot[s] * (o.y + (bias ? bias[r + 1] : 0.0f));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += 512) {
+    const int row = row0 + r;
+    if (row >= a.H) break;
+    float acc = 0.0f;
+    for (int s = 0; s < ns; ++s)
+      if ((present >> s) & 1u) acc += part[r * ns + s];
+    a.y[static_cast<size_t>(t) * a.H + row] = acc;
+  }
+}
+
 // Integer block partials export through the same format routines.
 // grid n_rows, block 256.
 template <int FMT>
@@ -885,9 +1195,99 @@ hipError_t gateup_dispatch_nc(const KArgs& a, int routing_given, hipStream_t s, 
   }
 }
 
+// MXFP4 plans of k_gateup_mx / k_down_mx: NL 16-byte pieces per lane and row
+// pair, NBL blocks per lane, RPW row pairs per wave in flight (at most nine
+// pieces per lane).
+struct MxPlan { int nl, nbl, rpw; };
+bool mx_plan(int K, MxPlan* out) {
+  const int nb = K / 32, npc = mx_row_pieces(nb);
+  const int nl = (2 * npc + 63) / 64, nbl = (nb + 63) / 64;
+  if (nbl == 1) *out = {nl, 1, 3};  // nl <= 3
+  else if (nbl == 2) *out = nl <= 3 ? MxPlan{3, 2, 3} : MxPlan{5, 2, 1};
+  else if (nbl <= 4) *out = {9, 4, 1};
+  else return false;
+  return true;
+}
+
+size_t mx_gateup_lds(const KArgs& a) {
+  const int nb = a.H / 32;
+  return static_cast<size_t>(mx_gu_scratch_offset(nb)) + 4 * mx_scratch_bytes(nb) +
+         16 * static_cast<size_t>(a.E);
+}
+
+// Rows per k_down_mx workgroup: all (slot, row pair) units in one batch per
+// wave where ns <= 8 RPW.
+int mx_down_rows(const KArgs& a, const MxPlan& pl) {
+  const int ns = a.k + a.has_shared;
+  return 2 * max(1, 8 * pl.rpw / ns);
+}
+
+size_t mx_down_lds(const KArgs& a, const MxPlan& pl) {
+  const int ns = a.k + a.has_shared, nb = a.F / 32;
+  return static_cast<size_t>(mx_down_scratch_offset(ns, nb)) + 8 * mx_scratch_bytes(nb) +
+         4 * static_cast<size_t>(mx_down_rows(a, pl)) * ns;
+}
+
+bool mx_gateup_fits(const KArgs& a) {
+  MxPlan pl;
+  return a.fmt_gu == FMT_MXFP4 && mx_plan(a.H, &pl) && mx_gateup_lds(a) <= kMaxLds;
+}
+bool mx_down_fits(const KArgs& a) {
+  MxPlan pl;
+  const int ns = a.k + a.has_shared;
+  return a.fmt_d == FMT_MXFP4 && mx_plan(a.F, &pl) && mx_down_lds(a, pl) <= kMaxLds &&
+         ns * ((a.F + 255) / 256) <= 8 * kMxDownJobs;
+}
+
+template <int RPW, int NL, int NBL>
+hipError_t gateup_mx_launch(const KArgs& a, int routing_given, hipStream_t s, Ev ev) {
+  const int P = a.T * a.k + a.T * a.has_shared;
+  const dim3 grid((a.F + 4 * RPW - 1) / (4 * RPW), P);
+  const size_t lds = mx_gateup_lds(a);
+  if (a.E <= 256)
+    return launch(k_gateup_mx<RPW, NL, NBL, 4>, grid, 256, lds, s, ev, a, routing_given);
+  return launch(k_gateup_mx<RPW, NL, NBL, 16>, grid, 256, lds, s, ev, a, routing_given);
+}
+
+hipError_t gateup_mx(const KArgs& a, int routing_given, hipStream_t s, Ev ev) {
+  MxPlan pl;
+  mx_plan(a.H, &pl);
+  switch (pl.nl) {
+    case 1: return gateup_mx_launch<3, 1, 1>(a, routing_given, s, ev);
+    case 2: return gateup_mx_launch<3, 2, 1>(a, routing_given, s, ev);
+    case 3:
+      if (pl.nbl == 1) return gateup_mx_launch<3, 3, 1>(a, routing_given, s, ev);
+      return gateup_mx_launch<3, 3, 2>(a, routing_given, s, ev);
+    case 5: return gateup_mx_launch<1, 5, 2>(a, routing_given, s, ev);
+    default: return gateup_mx_launch<1, 9, 4>(a, routing_given, s, ev);
+  }
+}
+
+template <int RPW, int NL, int NBL>
+hipError_t down_mx_launch(const KArgs& a, const MxPlan& pl, hipStream_t s, Ev ev) {
+  const int R = mx_down_rows(a, pl);
+  const dim3 grid((a.H + R - 1) / R, a.T);
+  return launch(k_down_mx<RPW, NL, NBL>, grid, 512, mx_down_lds(a, pl), s, ev, a, R);
+}
+
+hipError_t down_mx(const KArgs& a, hipStream_t s, Ev ev) {
+  MxPlan pl;
+  mx_plan(a.F, &pl);
+  switch (pl.nl) {
+    case 1: return down_mx_launch<3, 1, 1>(a, pl, s, ev);
+    case 2: return down_mx_launch<3, 2, 1>(a, pl, s, ev);
+    case 3:
+      if (pl.nbl == 1) return down_mx_launch<3, 3, 1>(a, pl, s, ev);
+      return down_mx_launch<3, 3, 2>(a, pl, s, ev);
+    case 5: return down_mx_launch<1, 5, 2>(a, pl, s, ev);
+    default: return down_mx_launch<1, 9, 4>(a, pl, s, ev);
+  }
+}
+
 // Candidates per lane of the in-kernel top-k: 4 covers E <= 256.
 template <int FMT>
 hipError_t gateup_dispatch(const KArgs& a, int routing_given, hipStream_t s, Ev ev) {
+  if (FMT == FMT_MXFP4 && mx_gateup_fits(a)) return gateup_mx(a, routing_given, s, ev);
   if (a.E <= 256) return gateup_dispatch_nc<FMT, 4>(a, routing_given, s, ev);
   return gateup_dispatch_nc<FMT, 16>(a, routing_given, s, ev);
 }
@@ -931,6 +1331,7 @@ hipError_t down_lds_jb(int jobs_per_wave, dim3 grid, size_t lds, hipStream_t s, 
 
 template <int FMT>
 hipError_t down_dispatch(const KArgs& a, hipStream_t s, Ev ev) {
+  if (FMT == FMT_MXFP4 && mx_down_fits(a)) return down_mx(a, s, ev);
   if constexpr (FMT == FMT_Q4_K) {
     DownLdsPlan pl;
     if (down_lds_plan(a, &pl)) {
@@ -964,6 +1365,16 @@ hipError_t down_dispatch(const KArgs& a, hipStream_t s, Ev ev) {
 
 }  // namespace
 
+bool gemv_hquant(int fmt_down, int F, int k, int has_shared) {
+  if (fmt_down != FMT_MXFP4) return false;
+  KArgs a{};
+  a.fmt_d = fmt_down;
+  a.F = F;
+  a.k = k;
+  a.has_shared = has_shared;
+  return !mx_down_fits(a);
+}
+
 bool gemv_fits(const KArgs& a) {
   size_t g = a.fmt_gu == FMT_Q4_K ? gateup_lds<FMT_Q4_K>(a, nullptr)
            : a.fmt_gu == FMT_Q6_K ? gateup_lds<FMT_Q6_K>(a, nullptr)
@@ -973,6 +1384,8 @@ bool gemv_fits(const KArgs& a) {
                                  : down_lds<FMT_MXFP4>(a, nullptr);
   DownLdsPlan pl;
   if (down_lds_plan(a, &pl)) d = pl.lds;
+  if (mx_gateup_fits(a)) g = 0;
+  if (mx_down_fits(a)) d = 0;
   return g <= kMaxLds && d <= kMaxLds;
 }
 

@@ -170,9 +170,9 @@ def test_block_dots_validation():
 
 def test_stage_names_and_path_rule():
     """Dispatch rule: chunks of <= 4 tokens, and any layer with an MXFP4 matrix,
-    take the per-pair GEMV path (3 kernels, or 4 with an MXFP4 down, whose h is
-    quantized by a kernel of its own); larger K-quant chunks the grouped path
-    (7 kernels)."""
+    take the per-pair GEMV path (3 kernels, or 4 when an MXFP4 down is too large
+    for the kernel that quantizes h itself: h then gets a kernel of its own);
+    larger K-quant chunks the grouped path (7 kernels)."""
     d = good_desc()
     for T in (1, 4):
         assert M.moe_layer_stage_count(d, T) == 3
@@ -185,9 +185,14 @@ def test_stage_names_and_path_rule():
     assert M.moe_layer_stage_count(d, 0) == 0
     mx = good_desc(gen.CONFIGS["gpt-oss-20b"])
     for T in (1, 16):
-        assert M.moe_layer_stage_count(mx, T) == 4
-        assert [M.moe_layer_stage_name(mx, T, i) for i in range(4)] == [
-            "router", "gateup", "hquant", "down"]
+        assert M.moe_layer_stage_count(mx, T) == 3
+        assert [M.moe_layer_stage_name(mx, T, i) for i in range(3)] == [
+            "router", "gateup", "down"]
+    # nine slots of 2048-value h: their LDS images exceed the fused kernel's budget
+    mx9 = good_desc(gen.CONFIGS["gpt-oss-20b"].with_(E=16, F=2048, k=9))
+    assert M.moe_layer_stage_count(mx9, 1) == 4
+    assert [M.moe_layer_stage_name(mx9, 1, i) for i in range(4)] == [
+        "router", "gateup", "hquant", "down"]
     q6 = good_desc(gen.CONFIGS["deepseek-v4-flash"])
     assert M.moe_layer_stage_count(q6, 16) == 7
     # the grouped workspace holds the per-pair rows: it grows with T * k * H

@@ -26,6 +26,20 @@ def test_layer_full_decode(name, T):
     check_layer(gen.CONFIGS[name], T=T, x_index=T)
 
 
+@pytest.mark.parametrize("H,F,k,shared", [(1024, 2048, 4, False), (2048, 1024, 8, True),
+                                          (3584, 512, 2, False), (6144, 256, 2, True),
+                                          (2048, 2048, 8, True)])
+def test_layer_mxfp4_shapes(H, F, k, shared):
+    """MXFP4 layers whose rows take each plan of the realigned GEMV kernels (one
+    to nine 16-byte pieces per lane and row pair, one to four blocks per lane;
+    up to nine slots in the down kernel). At F = 2048 with nine slots the
+    activation images exceed the LDS budget and the down projection takes the
+    register-staged kernel instead."""
+    cfg = gen.CONFIGS["gpt-oss-20b"].with_(name=f"mx-{H}-{F}-{k}", E=16, H=H, F=F, k=k,
+                                           shared=shared, T=2)
+    check_layer(cfg)
+
+
 def _routed_layer(cfg, T, x_index):
     """The full-size layer with only the experts the oracle routes these tokens
     to (plus the shared expert) generated; the others stay zero and unused."""
