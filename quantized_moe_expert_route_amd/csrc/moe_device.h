@@ -317,10 +317,8 @@ constexpr int kApPitch = 20;
 // the MXFP4 dot reads: ap gets the 8 blocks of the 256-value piece.
 // Stores the pairs block-major: ap[block * kApPitch + q] (see ActView), with ap
 // pointing at the piece's first block; each lane writes 4 consecutive pairs.
-__device__ __forceinline__ void quant_wave_pairs(const float v[4], bool valid, int lane,
-                                                 half2_t* ap, float* d) {
-  int q[4];
-  const float dv = quant_wave_q<32>(v, q);
+__device__ __forceinline__ void store_pairs(const int (&q)[4], float dv, bool valid, int lane,
+                                            half2_t* ap, float* d) {
   int o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)  // partner 16 elements ahead: lane + 4 (DPP row_shl:4)
@@ -334,6 +332,12 @@ __device__ __forceinline__ void quant_wave_pairs(const float v[4], bool valid, i
     *reinterpret_cast<uint4*>(ap + bl * kApPitch + off) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   if (valid && (lane & 7) == 0) d[bl] = dv;
+}
+__device__ __forceinline__ void quant_wave_pairs(const float v[4], bool valid, int lane,
+                                                 half2_t* ap, float* d) {
+  int q[4];
+  const float dv = quant_wave_q<32>(v, q);
+  store_pairs(q, dv, valid, lane, ap, d);
 }
 
 // Activations of one row vector as the dot routines read them (LDS).

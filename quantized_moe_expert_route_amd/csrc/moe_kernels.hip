@@ -266,15 +266,17 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
     ubase = static_cast<const uint8_t*>(a.sh_up);
     issue_loads();  // the shared expert does not wait for routing
   } else if (wave != tkw) {
-    // E <= 1024: at most 6 entries per thread; issue every load, then store
+    // E <= 1024: at most 6 entries per thread; issue the loads, then store
     const int li = (wave - (wave > tkw ? 1 : 0)) * 64 + lane;  // 0..191
     const void* g[6];
     const void* u[6];
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
-      const int i = min(li + 192 * j, a.E - 1);
-      g[j] = a.gate[i];
-      u[j] = a.up[i];
+      if (192 * j < a.E) {  // wave-uniform: no loads past the table
+        const int i = min(li + 192 * j, a.E - 1);
+        g[j] = a.gate[i];
+        u[j] = a.up[i];
+      }
     }
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
@@ -493,14 +495,15 @@ __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
     ubase = static_cast<const uint8_t*>(a.sh_up);
     issue();  // the shared expert does not wait for routing
   } else if (wave != tkw) {
-    const int li = (wave - (wave > tkw ? 1 : 0)) * 64 + lane;  // 0..191
     const void* g[6];
     const void* u[6];
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
-      const int i = min(li + 192 * j, a.E - 1);
-      g[j] = a.gate[i];
-      u[j] = a.up[i];
+      if (192 * j < a.E) {  // wave-uniform: no loads past the table
+        const int i = min(li + 192 * j, a.E - 1);
+        g[j] = a.gate[i];
+        u[j] = a.up[i];
+      }
     }
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
@@ -1037,11 +1040,11 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
 #pragma unroll
   for (int u = 0; u < kMxDownJobs; ++u) {
     const int job = wave + 8 * u;  // wave-uniform
+    hv[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (job < njobs) {
       const int s = job / pieces, e0 = (job - s * pieces) * 256 + 4 * lane;
       const int ps = s < a.k ? t * a.k + s : a.T * a.k + t;
-      hv[u] = *reinterpret_cast<const float4*>(a.h + static_cast<size_t>(ps) * K +
-                                               (e0 < K ? e0 : 0));
+      if (e0 < K) hv[u] = *reinterpret_cast<const float4*>(a.h + static_cast<size_t>(ps) * K + e0);
     }
   }
   issue(u0);
@@ -1051,10 +1054,8 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
     if (job < njobs) {
       const int s = job / pieces, pc = job - s * pieces;
       if ((present >> s) & 1u) {
-        const bool valid = pc * 256 + 4 * lane < K;
-        const float v[4] = {valid ? hv[u].x : 0.0f, valid ? hv[u].y : 0.0f,
-                            valid ? hv[u].z : 0.0f, valid ? hv[u].w : 0.0f};
-        quant_wave_pairs(v, valid, lane,
+        const float v[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+        quant_wave_pairs(v, pc * 256 + 4 * lane < K, lane,
                          reinterpret_cast<half2_t*>(p_act + s * act_bytes) + pc * 8 * kApPitch,
                          ld + s * nb + pc * 8);
       }
