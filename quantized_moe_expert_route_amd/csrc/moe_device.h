@@ -523,13 +523,21 @@ struct MxAct {
   float d[NBL];
 };
 
+// Rows of 65..96 blocks: the 2 (nb - 64) tail blocks of a row pair (blocks
+// 64.. of row 0, then of row 1) fold onto lanes 0 .. 2 (nb - 64) - 1, so a
+// lane dots three blocks per pair instead of four. Its second activation
+// block is then 64 + lane mod (nb - 64).
+__device__ __forceinline__ bool mx_fold(int nb) { return nb > 64 && nb <= 96; }
+
 // The lane's blocks of one activation vector from its LDS image (ActView layout).
 template <int NBL>
 __device__ __forceinline__ void mx_act_load(MxAct<NBL>& A, const half2_t* lap, const float* ld,
                                             int nb, int lane) {
+  const int tail = nb - 64;
 #pragma unroll
   for (int i = 0; i < NBL; ++i) {
-    const int b = lane + 64 * i;
+    const int b = (NBL == 2 && i == 1 && mx_fold(nb)) ? 64 + (lane < tail ? lane : lane - tail)
+                                                      : lane + 64 * i;
     const uint4* p = reinterpret_cast<const uint4*>(lap + min(b, nb - 1) * kApPitch);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -582,20 +590,31 @@ __device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, i
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float s0 = 0.0f, s1 = 0.0f;
+  auto block = [&](int row, int b, int i) {
+    const uint32_t o = static_cast<uint32_t>(row * 16 * npc + 17 * b);
+    const uint32_t* wp = reinterpret_cast<const uint32_t*>(scr + (o & ~3u));
+    FmtMXFP4::Raw r;
 #pragma unroll
-  for (int i = 0; i < NBL; ++i) {
-    const int b = lane + 64 * i;
-    if (b < nb) {
+    for (int k = 0; k < 5; ++k) r.w[k] = wp[k];
+    r.sh = o & 3u;
+    return FmtMXFP4::value_from_dot(r, mx_dot_regs(r, A.ap[i]), A.d[i]);
+  };
+  if (NBL == 2 && mx_fold(nb)) {  // wave-uniform
+    s0 = block(0, lane, 0);
+    s1 = block(1, lane, 0);
+    const int tail = nb - 64;
+    if (lane < 2 * tail) {
+      const int row = lane < tail ? 0 : 1;
+      const float v = block(row, 64 + lane - row * tail, NBL - 1);
+      if (row == 0) s0 += v; else s1 += v;
+    }
+  } else {
 #pragma unroll
-      for (int row = 0; row < 2; ++row) {
-        const uint32_t o = static_cast<uint32_t>(row * 16 * npc + 17 * b);
-        const uint32_t* wp = reinterpret_cast<const uint32_t*>(scr + (o & ~3u));
-        FmtMXFP4::Raw r;
-#pragma unroll
-        for (int k = 0; k < 5; ++k) r.w[k] = wp[k];
-        r.sh = o & 3u;
-        const float v = FmtMXFP4::value_from_dot(r, mx_dot_regs(r, A.ap[i]), A.d[i]);
-        if (row == 0) s0 += v; else s1 += v;
+    for (int i = 0; i < NBL; ++i) {
+      const int b = lane + 64 * i;
+      if (b < nb) {
+        s0 += block(0, b, i);
+        s1 += block(1, b, i);
       }
     }
   }
