@@ -513,7 +513,7 @@ template <> struct FmtOf<FMT_MXFP4> { using T = FmtMXFP4; };
 // it keeps in registers.
 
 __host__ __device__ inline int mx_row_pieces(int nb) { return (17 * nb + 15) / 16; }
-// Per-wave scratch: two rows of pieces plus one dword that the five-dword
+// Per-wave scratch: two rows of pieces plus the bytes that the five-dword
 // window of a row's last block may reach past them.
 __host__ __device__ inline int mx_scratch_bytes(int nb) { return 32 * mx_row_pieces(nb) + 16; }
 
@@ -551,14 +551,15 @@ __device__ __forceinline__ void mx_act_load(MxAct<NBL>& A, const half2_t* lap, c
   }
 }
 
-// Dot of one block (five dwords from its aligned start, byte offset sh) with
-// its 16 activation pairs; exact as in FmtMXFP4::dot.
-__device__ __forceinline__ float mx_dot_regs(const FmtMXFP4::Raw& r, const half2_t (&ap)[16]) {
+// Dot of one block's 16 nibble bytes (five dwords w from the aligned dword
+// holding the first one, at byte offset sh) with its 16 activation pairs;
+// exact as in FmtMXFP4::dot.
+__device__ __forceinline__ float mx_dot_regs(const uint32_t (&w)[5], uint32_t sh,
+                                             const half2_t (&ap)[16]) {
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t qw = r.sh == 3 ? r.w[i + 1]
-                                  : __builtin_amdgcn_alignbyte(r.w[i + 1], r.w[i], r.sh + 1);
+    const uint32_t qw = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
     acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 0),
                                  ap[4 * i], acc, false);
     acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw, 1.0f, 1),
@@ -591,13 +592,13 @@ __device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, i
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float s0 = 0.0f, s1 = 0.0f;
   auto block = [&](int row, int b, int i) {
-    const uint32_t o = static_cast<uint32_t>(row * 16 * npc + 17 * b);
-    const uint32_t* wp = reinterpret_cast<const uint32_t*>(scr + (o & ~3u));
-    FmtMXFP4::Raw r;
+    const uint32_t o = static_cast<uint32_t>(row * 16 * npc + 17 * b);  // scale byte
+    const uint32_t* wp = reinterpret_cast<const uint32_t*>(scr + ((o + 1) & ~3u));
+    uint32_t w[5];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) r.w[k] = wp[k];
-    r.sh = o & 3u;
-    return FmtMXFP4::value_from_dot(r, mx_dot_regs(r, A.ap[i]), A.d[i]);
+    for (int k = 0; k < 5; ++k) w[k] = wp[k];
+    const int e = scr[o];
+    return A.d[i] * __builtin_ldexpf(mx_dot_regs(w, (o + 1) & 3u, A.ap[i]), e - 127);
   };
   if (NBL == 2 && mx_fold(nb)) {  // wave-uniform
     s0 = block(0, lane, 0);
