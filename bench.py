@@ -251,11 +251,14 @@ def gen_row_bytes(fmt, K):
 
 
 def kernel_names(cfg, path: str) -> dict:
-    """Kernel (as rocprofv3 names it) of each stage of a layer forward."""
+    """Kernel (as rocprofv3 names it) of each stage of a layer forward (MXFP4
+    layers: the realigning kernels, whose LDS budget every workload here fits)."""
     import gen
     if path == "gemv":
-        dn = "k_down_q4k_lds" if cfg.fmt_d == gen.Q4_K else "k_down"
-        return {"router": "k_router", "gateup": "k_gateup", "down": dn}
+        mx = gen.MXFP4
+        gu = "k_gateup_mx" if cfg.fmt_gu == mx else "k_gateup"
+        dn = {gen.Q4_K: "k_down_q4k_lds", mx: "k_down_mx"}.get(cfg.fmt_d, "k_down")
+        return {"router": "k_router", "gateup": gu, "down": dn}
     nb = cfg.biases
     gu = "k_glds_q4k<0>" if cfg.fmt_gu == gen.Q4_K and not nb else "k_gu_grouped"
     if cfg.fmt_d == gen.Q4_K and not nb:

@@ -101,8 +101,10 @@ typedef struct {
  *    only; routing weights use the unbiased logits.
  *  fmt_* / stride_*: weight format and row stride in bytes of the gate and up
  *    matrices ([F rows of H]) and of down ([H rows of F]). Rows are contiguous
- *    block streams; stride >= row bytes, stride % 16 == 0. gate and up must
- *    have the same format.
+ *    block streams; stride >= row bytes, stride % 16 == 0, and each matrix
+ *    spans rows * stride bytes (rows are read in whole 16-byte pieces, up to
+ *    the next multiple of 16 past a row's last block). gate and up must have
+ *    the same format.
  *  gate, up, down: device arrays of E device pointers to each expert's
  *    matrices (16-byte aligned). gate[e] == NULL means expert e is not present
  *    here: its slots contribute nothing and the other weights are not
