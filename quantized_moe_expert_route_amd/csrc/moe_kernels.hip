@@ -518,6 +518,16 @@ __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
     __builtin_amdgcn_s_setprio(3);
     if (routing_given) {
       if (lane == 0) s_e = a.ids[p];
+    } else if (blockIdx.x != 0) {
+      // only the slot's expert is needed here: ranks 0..slot, no weights
+      float lg[NC];
+#pragma unroll
+      for (int i = 0; i < NC; ++i)
+        lg[i] = a.logits[static_cast<size_t>(t) * a.E + min(lane + 64 * i, a.E - 1)];
+      uint32_t key[NC];
+      topk_keys<NC>(lg, a.sel_bias, a.E, key);
+      const int e = topk_nth<NC>(key, slot);
+      if (lane == 0) s_e = e;
     } else {
       wave_topk<NC>(a.logits + static_cast<size_t>(t) * a.E, a.sel_bias, a.E, a.k, a.router,
                     a.norm_topk, a.route_scale, s_ids, s_w);
