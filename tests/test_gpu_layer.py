@@ -176,13 +176,18 @@ def test_layer_copies_identical():
     assert np.array_equal(a[0], b[0])
 
 
-@pytest.mark.parametrize("name,T", [("qwen3.6-35b-a3b", 1), ("tiny", 1), ("qwen3.6-35b-a3b", 3)])
+@pytest.mark.parametrize("name,T", [("qwen3.6-35b-a3b", 1), ("tiny", 1), ("qwen3.6-35b-a3b", 3),
+                                    ("gpt-oss-20b", 1), ("gpt-oss-full", 2)])
 def test_expert_ffn_given_routing_decode(name, T):
     """Caller-given routing on the decode path (the fused expert kernel at one
-    token): repeated and out-of-range ids, an absent expert, shared expert."""
-    cfg = gen.CONFIGS[name] if name == "tiny" else SHRUNK[name]
+    token): repeated and out-of-range ids, an absent expert, shared expert; the
+    MXFP4 cases (q8 in 32-value blocks, bf16 x, biases) run the realigned
+    kernels, at full width for gpt-oss-full."""
+    cfg = (gen.CONFIGS[name] if name == "tiny" else
+           gen.CONFIGS["gpt-oss-20b"] if name == "gpt-oss-full" else SHRUNK[name])
+    mx = cfg.fmt_gu == gen.MXFP4
     data = gen.make_layer(cfg)
-    x, _ = gen.make_x(cfg, T=T, x_index=11)
+    x, xb = gen.make_x(cfg, T=T, x_index=11)
     rng = np.random.default_rng(5)
     ids = np.stack([rng.choice(cfg.E, cfg.k, replace=False) for _ in range(T)]).astype(np.int32)
     ids[0, -1] = cfg.E  # out of range: contributes nothing
@@ -190,17 +195,18 @@ def test_expert_ffn_given_routing_decode(name, T):
     present = np.ones(cfg.E, bool)
     present[ids[0, 0]] = False  # an absent expert
     dl = DeviceLayer(data, present=present)
-    B = 256
+    B = 32 if mx else 256
+    afmt = M.MOE_AFMT_Q8_32 if mx else M.MOE_AFMT_Q8_K
     qs = torch.empty((T, cfg.H), dtype=torch.int8, device="cuda")
     d = torch.empty((T, cfg.H // B), dtype=torch.float32, device="cuda")
-    bs = torch.empty((T, cfg.H // 16), dtype=torch.int16, device="cuda")
-    q = M.qact(qs, d, bs, M.MOE_AFMT_Q8_K, T, cfg.H)
-    xt = torch.from_numpy(x).cuda()
-    M.moe_quantize_act_q8k(xt, M.MOE_DTYPE_F32, T, cfg.H, M.MOE_AFMT_Q8_K, q)
+    bs = None if mx else torch.empty((T, cfg.H // 16), dtype=torch.int16, device="cuda")
+    q = M.qact(qs, d, bs, afmt, T, cfg.H)
+    xt, dt = x_to_device(data, x, xb)
+    M.moe_quantize_act_q8k(xt, dt, T, cfg.H, afmt, q)
     y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
     ws = dl.workspace(T)
     for _ in range(2):  # twice: the done flags are cleared per call
-        M.moe_expert_ffn(dl.desc, q, xt, M.MOE_DTYPE_F32, T, torch.from_numpy(ids).cuda(),
+        M.moe_expert_ffn(dl.desc, q, xt, dt, T, torch.from_numpy(ids).cuda(),
                          torch.from_numpy(w).cuda(), y, ws, ws.numel())
         torch.cuda.synchronize()
         L = oracle.Layer(data, present=present)
