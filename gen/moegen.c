@@ -2,9 +2,9 @@
  * moegen — seeded synthetic inputs (see moegen.h). Test and benchmark data only.
  *
  * The weight encoders are plain "covering" quantizers computed in fp64: every
- * sub-block gets a scale (and for Q4_K an offset) large enough that the whole
- * sub-block lies inside the representable range, so every element has the
- * closed-form round-trip bound |x - xhat| <= step/2 (Q4_K, Q6_K) or <= 2^E
+ * sub-block gets a scale (and for Q4_K / Q5_K an offset) large enough that the
+ * whole sub-block lies inside the representable range, so every element has the
+ * closed-form round-trip bound |x - xhat| <= step/2 (Q4_K, Q5_K, Q6_K) or <= 2^E
  * inside the MXFP4 grid. The pages do not say how float weights become blocks;
  * these encoders exist to make test data with known error bounds.
  */
@@ -130,7 +130,9 @@ static inline double rne(double v) {
   return t - 0x1.8p52;
 }
 
-size_t mg_block_bytes(int fmt) { return fmt == MG_Q4_K ? 144 : fmt == MG_Q6_K ? 210 : 17; }
+size_t mg_block_bytes(int fmt) {
+  return fmt == MG_Q4_K ? 144 : fmt == MG_Q6_K ? 210 : fmt == MG_Q5_K ? 176 : 17;
+}
 int mg_block_elems(int fmt) { return fmt == MG_MXFP4 ? 32 : 256; }
 
 /* ---- packers ------------------------------------------------------------------ */
@@ -148,6 +150,24 @@ void mg_pack_q4k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const u
   for (int c = 0; c < 4; ++c)
     for (int i = 0; i < 32; ++i)
       qs[32 * c + i] = (uint8_t)((q[64 * c + i] & 15) | ((q[64 * c + 32 + i] & 15) << 4));
+}
+
+/* Q5_K (176 B): Q4_K's d, dmin and scales, then qh[32] (bit 2c of qh[l]: fifth bit
+ * of weight 64c+l; bit 2c+1: of weight 64c+32+l), then Q4_K's nibbles. */
+void mg_pack_q5k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const uint8_t* m,
+                 const uint8_t* q, uint8_t* blk) {
+  uint8_t tmp[144];
+  mg_pack_q4k(d_bits, dmin_bits, sc, m, q, tmp);  /* low nibbles (masked), header */
+  memcpy(blk, tmp, 16);
+  memcpy(blk + 48, tmp + 16, 128);
+  uint8_t* qh = blk + 16;
+  for (int l = 0; l < 32; ++l) {
+    uint8_t h = 0;
+    for (int c = 0; c < 4; ++c)
+      h |= (uint8_t)((((q[64 * c + l] >> 4) & 1) << (2 * c)) |
+                     (((q[64 * c + 32 + l] >> 4) & 1) << (2 * c + 1)));
+    qh[l] = h;
+  }
 }
 
 void mg_pack_q6k(uint16_t d_bits, const int8_t* sc, const uint8_t* q, uint8_t* blk) {
@@ -173,7 +193,9 @@ void mg_pack_mxfp4(uint8_t e, const uint8_t* codes, uint8_t* blk) {
 }
 
 /* ---- covering encoders ----------------------------------------------------------- */
-void mg_encode_q4k(const float* x, uint8_t* blk) {
+/* Scales, mins and quants (0..qmax) of a Q4_K (qmax 15) or Q5_K (qmax 31) block. */
+static void encode_scale_min(const float* x, int qmax, uint16_t* d_out, uint16_t* dmin_out,
+                             uint8_t* sc, uint8_t* m, uint8_t* q) {
   double mn[8], mx[8], off[8], need[8], maxoff = 0.0, maxneed = 0.0;
   for (int j = 0; j < 8; ++j) {
     double lo = 0.0, hi = -INFINITY;
@@ -187,14 +209,13 @@ void mg_encode_q4k(const float* x, uint8_t* blk) {
   }
   uint16_t dmin_bits = mg_fp16_ceil_bits(maxoff / 63.0);
   double dmin = fp16_value(dmin_bits);
-  uint8_t m[8], sc[8], q[256];
   double mhat[8];
   for (int j = 0; j < 8; ++j) {
     double mj = dmin > 0.0 ? ceil(off[j] / dmin) : 0.0;
     if (mj > 63.0) mj = 63.0;
     m[j] = (uint8_t)mj;
     mhat[j] = dmin * mj;
-    need[j] = (mx[j] + mhat[j]) / 15.0;
+    need[j] = (mx[j] + mhat[j]) / qmax;
     if (need[j] < 0.0) need[j] = 0.0;
     if (need[j] > maxneed) maxneed = need[j];
   }
@@ -209,11 +230,26 @@ void mg_encode_q4k(const float* x, uint8_t* blk) {
     for (int i = 0; i < 32; ++i) {
       double v = shat > 0.0 ? rne(((double)x[32 * j + i] + mhat[j]) / shat) : 0.0;
       if (v < 0.0) v = 0.0;
-      if (v > 15.0) v = 15.0;
+      if (v > qmax) v = qmax;
       q[32 * j + i] = (uint8_t)v;
     }
   }
+  *d_out = d_bits;
+  *dmin_out = dmin_bits;
+}
+
+void mg_encode_q4k(const float* x, uint8_t* blk) {
+  uint16_t d_bits, dmin_bits;
+  uint8_t sc[8], m[8], q[256];
+  encode_scale_min(x, 15, &d_bits, &dmin_bits, sc, m, q);
   mg_pack_q4k(d_bits, dmin_bits, sc, m, q, blk);
+}
+
+void mg_encode_q5k(const float* x, uint8_t* blk) {
+  uint16_t d_bits, dmin_bits;
+  uint8_t sc[8], m[8], q[256];
+  encode_scale_min(x, 31, &d_bits, &dmin_bits, sc, m, q);
+  mg_pack_q5k(d_bits, dmin_bits, sc, m, q, blk);
 }
 
 void mg_encode_q6k(const float* x, uint8_t* blk) {
@@ -295,6 +331,7 @@ static void enc_rows(void* p, int r0, int r1) {
     const float* xr = c->x + (size_t)r * c->K;
     for (int b = 0; b < nb; ++b) {
       if (c->fmt == MG_Q4_K) mg_encode_q4k(xr + b * be, row + b * bb);
+      else if (c->fmt == MG_Q5_K) mg_encode_q5k(xr + b * be, row + b * bb);
       else if (c->fmt == MG_Q6_K) mg_encode_q6k(xr + b * be, row + b * bb);
       else mg_encode_mxfp4(xr + b * be, row + b * bb);
     }

@@ -36,11 +36,13 @@ double or_e2m1(uint8_t code) {
 }
 
 int or_block_elems(int fmt) { return fmt == OR_MXFP4 ? 32 : 256; }
-int or_block_bytes(int fmt) { return fmt == OR_Q4_K ? 144 : fmt == OR_Q6_K ? 210 : 17; }
+int or_block_bytes(int fmt) {
+  return fmt == OR_Q4_K ? 144 : fmt == OR_Q6_K ? 210 : fmt == OR_Q5_K ? 176 : 17;
+}
 
 static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
-/* Q4_K 6-bit sub-block scales and mins. The 12 scale bytes hold, for
+/* Q4_K (and Q5_K) 6-bit sub-block scales and mins. The 12 scale bytes hold, for
  * sub-blocks 0..3, sc and m in the low 6 bits of bytes 0..3 and 4..7; for
  * sub-blocks 4..7 the low 4 bits sit in bytes 8..11 (sc low nibble, m high
  * nibble) and the top 2 bits in bits 6..7 of bytes 0..3 (sc) and 4..7 (m). */
@@ -64,6 +66,18 @@ void or_block_quants(int fmt, const uint8_t* blk, int32_t* q) {
     for (int n = 0; n < 256; ++n) {
       int c = n / 64, i = n % 64;
       q[n] = i < 32 ? (qs[32 * c + i] & 15) : (qs[32 * c + i - 32] >> 4);
+    }
+  } else if (fmt == OR_Q5_K) {
+    /* Q4_K's nibble layout (at byte 48) plus a fifth bit: qh[l] (l < 32, at
+     * byte 16) holds, in bit 2c, the high bit of weight 64c+l and, in bit
+     * 2c+1, that of weight 64c+32+l. */
+    const uint8_t* qh = blk + 16;
+    const uint8_t* qs = blk + 48;
+    for (int n = 0; n < 256; ++n) {
+      int c = n / 64, i = n % 64, l = i % 32;
+      int lo = i < 32 ? (qs[32 * c + l] & 15) : (qs[32 * c + l] >> 4);
+      int hi = (qh[l] >> (2 * c + (i < 32 ? 0 : 1))) & 1;
+      q[n] = lo | (hi << 4);
     }
   } else if (fmt == OR_Q6_K) {
     /* Two halves of 128; in half h, element r = 32*quarter + i takes its low
@@ -90,7 +104,7 @@ void or_block_quants(int fmt, const uint8_t* blk, int32_t* q) {
 void or_dequant_block(int fmt, const uint8_t* blk, double* out) {
   int32_t q[256];
   or_block_quants(fmt, blk, q);
-  if (fmt == OR_Q4_K) {
+  if (fmt == OR_Q4_K || fmt == OR_Q5_K) {  /* same scales and formula; q < 16 or < 32 */
     double d = or_fp16(rd16(blk)), dmin = or_fp16(rd16(blk + 2));
     int sc[8], m[8];
     q4k_scales(blk, sc, m);
@@ -151,7 +165,7 @@ void or_block_partials(int fmt, const uint8_t* row, int K, const int8_t* qs,
     const uint8_t* blk = row + (size_t)b * bb;
     const int8_t* a = qs + (size_t)b * be;
     or_block_quants(fmt, blk, q);
-    if (fmt == OR_Q4_K) {
+    if (fmt == OR_Q4_K || fmt == OR_Q5_K) {
       int sc[8], m[8];
       q4k_scales(blk, sc, m);
       const int16_t* bs = bsums + (size_t)b * 16;
@@ -185,7 +199,7 @@ void or_block_partials(int fmt, const uint8_t* row, int K, const int8_t* qs,
 }
 
 double or_block_value(int fmt, const uint8_t* blk, const int32_t* p, float d8) {
-  if (fmt == OR_Q4_K) {
+  if (fmt == OR_Q4_K || fmt == OR_Q5_K) {
     double d = or_fp16(rd16(blk)), dmin = or_fp16(rd16(blk + 2));
     return (double)d8 * (d * p[0] - dmin * p[1]);
   } else if (fmt == OR_Q6_K) {

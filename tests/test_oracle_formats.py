@@ -62,6 +62,39 @@ def test_q4k_hand_packed_fields(orc, genlib):
         assert np.array_equal(orc.dequant_row(oracle.Q4_K, blk, 256), want)
 
 
+def test_q5k_hand_packed_fields(orc, genlib):
+    rng = np.random.default_rng(3)
+    for trial in range(50):
+        sc, m, _ = _q4k_fields(rng)
+        q = rng.integers(0, 32, 256).astype(np.uint8)
+        d_bits = int(rng.integers(0x1000, 0x3000))
+        dmin_bits = int(rng.integers(0x1000, 0x3000))
+        blk = gen.pack_q5k(d_bits, dmin_bits, sc, m, q)
+        d = float(np.array([d_bits], np.uint16).view(np.float16)[0])
+        dmin = float(np.array([dmin_bits], np.uint16).view(np.float16)[0])
+        assert np.array_equal(orc.block_quants(oracle.Q5_K, blk), q)
+        want = np.array([d * sc[n // 32] * q[n] - dmin * m[n // 32] for n in range(256)])
+        assert np.array_equal(orc.dequant_row(oracle.Q5_K, blk, 256), want)
+
+
+def test_q5k_byte_layout(orc):
+    """A Q5_K block written byte by byte: d = 1, dmin = 0, scales 1. The fifth
+    bit of weight 64c + l sits in bit 2c of qh[l] (byte 16 + l), that of weight
+    64c + 32 + l in bit 2c + 1; nibbles at byte 48 as in Q4_K."""
+    blk = np.zeros(176, np.uint8)
+    blk[0:2] = [0x00, 0x3C]          # d = 1.0 (fp16)
+    blk[4:8] = 1                     # sc_0..3 = 1 (low 6 bits), m = 0
+    blk[12:16] = 0x01                # sc_4..7 low bits = 1, m high nibble 0
+    blk[48 + 0] = 0x21               # weight 0: nibble 1; weight 32: nibble 2
+    blk[48 + 32 * 3 + 5] = 0xF7      # weight 197: 7; weight 229: 15
+    blk[16 + 0] = 0b00000011         # weight 0 and weight 32: + 16
+    blk[16 + 5] = 0b10000000         # weight 64*3 + 32 + 5 = 229: + 16
+    want = np.zeros(256, np.int64)
+    want[0], want[32], want[197], want[229] = 17, 18, 7, 31
+    assert np.array_equal(orc.block_quants(oracle.Q5_K, blk), want)
+    assert np.array_equal(orc.dequant_row(oracle.Q5_K, blk, 256), want.astype(np.float64))
+
+
 def test_q6k_hand_packed_fields(orc, genlib):
     rng = np.random.default_rng(1)
     for trial in range(50):
@@ -120,6 +153,24 @@ def test_q4k_round_trip_bound(orc, genlib, std):
             loose = (rng_j / 15 + d + 2 * abs(orc.fp16(int(blk[2]) | int(blk[3]) << 8))) / 2
             assert err[32 * j:32 * j + 32].max() <= loose * (1 + 1e-9) + 1e-300, (r, j)
         assert q.min() >= 0 and q.max() <= 15
+
+
+@pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])
+def test_q5k_round_trip_bound(orc, genlib, std):
+    x = _blocks(gen.Q5_K, 300, std, 14)
+    for r in range(x.shape[0]):
+        blk = gen.encode_block(gen.Q5_K, x[r])
+        xh = orc.dequant_row(oracle.Q5_K, blk, 256)
+        d = orc.fp16(int(blk[0]) | int(blk[1]) << 8)
+        q = orc.block_quants(oracle.Q5_K, blk)
+        err = np.abs(x[r].astype(np.float64) - xh)
+        for j in range(8):
+            xs = x[r, 32 * j:32 * j + 32].astype(np.float64)
+            rng_j = max(xs.max(), 0) - min(xs.min(), 0)
+            # as for Q4_K with 31 steps over the sub-block's range
+            loose = (rng_j / 31 + d + 2 * abs(orc.fp16(int(blk[2]) | int(blk[3]) << 8))) / 2
+            assert err[32 * j:32 * j + 32].max() <= loose * (1 + 1e-9) + 1e-300, (r, j)
+        assert q.min() >= 0 and q.max() <= 31
 
 
 @pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])
