@@ -274,6 +274,12 @@ CONFIGS = {
         "kimi-k2", H=7168, F=2048, E=384, k=8, T=256, seed=4, router=SIGMOID, shared=True,
         description="Kimi-K2-shaped 256-token prefill chunk: H 7168, 384 experts top-8 sigmoid "
                     "+ shared, F 2048, Q4_K"),
+    # a format extension measured on the Qwen3.6 decode shape (not one of the five workloads)
+    "qwen3.6-35b-a3b-q5k": LayerConfig(
+        "qwen3.6-35b-a3b-q5k", H=2048, F=512, E=256, k=8, T=1, seed=5, shared=True,
+        fmt_gu=Q5_K, fmt_d=Q5_K,
+        description="Qwen3.6-35B-A3B-shaped decode layer with Q5_K experts: H 2048, 256 experts "
+                    "top-8 softmax + shared, F 512, Q5_K"),
 }
 CONFIG_ORDER = ["tiny", "qwen3.6-35b-a3b", "gpt-oss-20b", "deepseek-v4-flash", "kimi-k2"]
 

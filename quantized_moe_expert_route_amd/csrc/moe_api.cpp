@@ -14,7 +14,9 @@ namespace {
 constexpr int kMaxTokens = 2048;
 
 int block_elems(int fmt) { return fmt == FMT_MXFP4 ? 32 : 256; }
-size_t block_bytes(int fmt) { return fmt == FMT_Q4_K ? 144 : fmt == FMT_Q6_K ? 210 : 17; }
+size_t block_bytes(int fmt) {
+  return fmt == FMT_Q4_K ? 144 : fmt == FMT_Q6_K ? 210 : fmt == FMT_Q5_K ? 176 : 17;
+}
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -28,7 +30,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_EINVAL;
   if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
   for (int f : {d->fmt_gate, d->fmt_up, d->fmt_down})
-    if (f != MOE_WFMT_Q4_K && f != MOE_WFMT_Q6_K && f != MOE_WFMT_MXFP4) return MOE_EINVAL;
+    if (f != MOE_WFMT_Q4_K && f != MOE_WFMT_Q6_K && f != MOE_WFMT_MXFP4 && f != MOE_WFMT_Q5_K)
+      return MOE_EINVAL;
   if (d->fmt_gate != d->fmt_up) return MOE_EUNSUPPORTED;
   if (H % block_elems(d->fmt_gate) != 0 || H % 32 != 0) return MOE_EINVAL;
   if (F % block_elems(d->fmt_down) != 0 || F % 32 != 0) return MOE_EINVAL;
@@ -118,15 +121,17 @@ struct Stages {
 }  // namespace
 
 // Dispatch rule between the two expert-FFN paths: chunks of up to 4 tokens,
-// and every chunk of a layer with an MXFP4 matrix, take the per-(token, slot)
-// GEMV path (moe_kernels.hip); larger chunks of K-quant layers take the
+// and every chunk of a layer with an MXFP4 or Q5_K matrix (formats without
+// MFMA tile kernels), take the per-(token, slot) GEMV path (moe_kernels.hip);
+// larger chunks of Q4_K / Q6_K layers take the
 // expert-grouped path (moe_grouped.hip), whose int8 MFMA tiles read each
 // selected expert's weights once per 16 tokens routed to it.
 constexpr int kGroupedMinTokens = 5;
 
 
 bool use_grouped(int T, int fmt_gate, int fmt_down) {
-  return T >= kGroupedMinTokens && fmt_gate != FMT_MXFP4 && fmt_down != FMT_MXFP4;
+  auto tiled = [](int f) { return f == FMT_Q4_K || f == FMT_Q6_K; };
+  return T >= kGroupedMinTokens && tiled(fmt_gate) && tiled(fmt_down);
 }
 
 WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped) {
@@ -362,7 +367,8 @@ const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {
 
 moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,
                                const moe_qact* xq, int token, int32_t* out, hipStream_t stream) {
-  if (fmt != MOE_WFMT_Q4_K && fmt != MOE_WFMT_Q6_K && fmt != MOE_WFMT_MXFP4) return MOE_EINVAL;
+  if (fmt != MOE_WFMT_Q4_K && fmt != MOE_WFMT_Q6_K && fmt != MOE_WFMT_MXFP4 && fmt != MOE_WFMT_Q5_K)
+    return MOE_EINVAL;
   if (!rows || !aligned(rows, 16) || !out || !xq || n_rows < 0 || K <= 0) return MOE_EINVAL;
   if (K % block_elems(fmt) != 0) return MOE_EINVAL;
   const size_t rb = static_cast<size_t>(K / block_elems(fmt)) * block_bytes(fmt);

@@ -381,10 +381,18 @@ struct FmtQ4K {
     dh = sdot4((r.q.y >> 4) & 0x0F0F0F0F, ahi.y, dh);
     dh = sdot4((r.q.z >> 4) & 0x0F0F0F0F, ahi.z, dh);
     dh = sdot4((r.q.w >> 4) & 0x0F0F0F0F, ahi.w, dh);
+    return scaled(r.hdr, dl, dh, a, b, sub);
+  }
+  // The lane's share of the block partials from its two sub-block dots (dl:
+  // sub-block 2c, dh: 2c + 1; c = sub / 2): sum over the 8 lanes of sc * dot and
+  // of m * (16-element activation sums).
+  __device__ static __forceinline__ int2 scaled(const uint4& hdr, int dl, int dh,
+                                                const ActView& a, int b, int sub) {
+    const int c = sub >> 1, hh = sub & 1;
     // 6-bit scales/mins of the 8 sub-blocks as bytes: sub-blocks 0..3 sit in the
     // low 6 bits of scale bytes 0..3 (sc) and 4..7 (m); 4..7 take their low 4
     // bits from bytes 8..11 and their top 2 bits from bits 6..7 of bytes 0..7.
-    const uint32_t s0 = r.hdr.y, s1 = r.hdr.z, s2 = r.hdr.w;
+    const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;
     const uint32_t sc03 = s0 & 0x3F3F3F3Fu, m03 = s1 & 0x3F3F3F3Fu;
     const uint32_t sc47 = (s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u);
     const uint32_t m47 = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
@@ -413,6 +421,42 @@ __device__ __forceinline__ uint2 load8_unaligned(const uint8_t* p) {
   const uint32_t w0 = ld_nt4(w), w1 = ld_nt4(w + 4), w2 = ld_nt4(w_last);
   return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
 }
+
+// Q5_K: Q4_K's header and nibble layout (nibbles at byte 48) plus 32 bytes of
+// fifth bits at byte 16: bit 2c of qh[l] belongs to weight 64c + l, bit 2c + 1
+// to weight 64c + 32 + l. Lane `sub` (chunk c = sub / 2, half hh = sub % 2)
+// needs qh[16 hh .. 16 hh + 15], the same l as its nibble bytes.
+struct FmtQ5K {
+  static constexpr int BE = 256, BB = 176, LPB = 8;
+  struct Raw { uint4 hdr, qh, q; };
+  __device__ static __forceinline__ void load(Raw& r, const uint8_t* blk, int sub) {
+    r.hdr = ld_nt16(blk);
+    r.qh = ld_nt16(blk + 16 + 16 * (sub & 1));
+    r.q = ld_nt16(blk + 48 + 16 * sub);
+  }
+  __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int sub) {
+    const int c = sub >> 1, hh = sub & 1;
+    const int4* ax = reinterpret_cast<const int4*>(a.qs + b * 256);
+    const int4 alo = ax[4 * c + hh];
+    const int4 ahi = ax[4 * c + 2 + hh];
+    const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    const uint32_t h[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
+    const int al[4] = {alo.x, alo.y, alo.z, alo.w}, ah[4] = {ahi.x, ahi.y, ahi.z, ahi.w};
+    int dl = 0, dh = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (q[i] & 0x0F0F0F0Fu) | (((h[i] >> (2 * c)) & 0x01010101u) << 4);
+      const uint32_t hi = ((q[i] >> 4) & 0x0F0F0F0Fu) | (((h[i] >> (2 * c + 1)) & 0x01010101u) << 4);
+      dl = sdot4(static_cast<int>(lo), al[i], dl);
+      dh = sdot4(static_cast<int>(hi), ah[i], dh);
+    }
+    return FmtQ4K::scaled(r.hdr, dl, dh, a, b, sub);
+  }
+  __device__ static __forceinline__ float value(const Raw& r, int2 p, float d8) {
+    const float d = half_bits_to_f32(r.hdr.x & 0xFFFF), dmin = half_bits_to_f32(r.hdr.x >> 16);
+    return d8 * (d * static_cast<float>(p.x) - dmin * static_cast<float>(p.y));
+  }
+};
 
 struct FmtQ6K {
   static constexpr int BE = 256, BB = 210, LPB = 8;
@@ -502,6 +546,7 @@ template <int FMT> struct FmtOf;
 template <> struct FmtOf<FMT_Q4_K> { using T = FmtQ4K; };
 template <> struct FmtOf<FMT_Q6_K> { using T = FmtQ6K; };
 template <> struct FmtOf<FMT_MXFP4> { using T = FmtMXFP4; };
+template <> struct FmtOf<FMT_Q5_K> { using T = FmtQ5K; };
 
 // ------------------------------------------------------- MXFP4 decode GEMV
 // A 17-byte block has no fixed alignment, so one lane per block would need five

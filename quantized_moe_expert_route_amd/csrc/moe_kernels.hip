@@ -1160,7 +1160,7 @@ size_t gateup_lds(const KArgs& a, GemvShape* out) {
   using F = typename FmtOf<FMT>::T;
   const int P = a.T * a.k + a.T * a.has_shared;
   const int nb = a.H / F::BE;
-  const int tpg_max = FMT == FMT_Q6_K ? 4 : 8;
+  const int tpg_max = FMT == FMT_Q6_K || FMT == FMT_Q5_K ? 4 : 8;  // Raw registers per task
   GemvShape sh = gemv_shape(a.F, 2, nb, F::LPB, P, tpg_max, 512);
   if (out) *out = sh;
   const bool MX = FMT == FMT_MXFP4;
@@ -1174,7 +1174,7 @@ size_t down_lds(const KArgs& a, GemvShape* out) {
   using F = typename FmtOf<FMT>::T;
   const int ns = a.k + a.has_shared;
   const int nb = a.F / F::BE;
-  const int tpg_max = FMT == FMT_Q6_K ? 4 : 8;
+  const int tpg_max = FMT == FMT_Q6_K || FMT == FMT_Q5_K ? 4 : 8;  // Raw registers per task
   // Every workgroup re-quantizes its token's h (VALU work), so the target is
   // one workgroup per compute unit (R = ceil(H T / 256)), as far as the cap
   // on loads per lane allows.
@@ -1389,9 +1389,11 @@ bool gemv_hquant(int fmt_down, int F, int k, int has_shared) {
 bool gemv_fits(const KArgs& a) {
   size_t g = a.fmt_gu == FMT_Q4_K ? gateup_lds<FMT_Q4_K>(a, nullptr)
            : a.fmt_gu == FMT_Q6_K ? gateup_lds<FMT_Q6_K>(a, nullptr)
+           : a.fmt_gu == FMT_Q5_K ? gateup_lds<FMT_Q5_K>(a, nullptr)
                                   : gateup_lds<FMT_MXFP4>(a, nullptr);
   size_t d = a.fmt_d == FMT_Q4_K ? down_lds<FMT_Q4_K>(a, nullptr)
            : a.fmt_d == FMT_Q6_K ? down_lds<FMT_Q6_K>(a, nullptr)
+           : a.fmt_d == FMT_Q5_K ? down_lds<FMT_Q5_K>(a, nullptr)
                                  : down_lds<FMT_MXFP4>(a, nullptr);
   DownLdsPlan pl;
   if (down_lds_plan(a, &pl)) d = pl.lds;
@@ -1437,6 +1439,7 @@ hipError_t launch_gateup(const KArgs& a, bool routing_given, hipStream_t s, Ev e
   switch (a.fmt_gu) {
     case FMT_Q4_K: return gateup_dispatch<FMT_Q4_K>(a, routing_given, s, ev);
     case FMT_Q6_K: return gateup_dispatch<FMT_Q6_K>(a, routing_given, s, ev);
+    case FMT_Q5_K: return gateup_dispatch<FMT_Q5_K>(a, routing_given, s, ev);
     default: return gateup_dispatch<FMT_MXFP4>(a, routing_given, s, ev);
   }
 }
@@ -1451,6 +1454,7 @@ hipError_t launch_down(const KArgs& a, hipStream_t s, Ev ev) {
   switch (a.fmt_d) {
     case FMT_Q4_K: return down_dispatch<FMT_Q4_K>(a, s, ev);
     case FMT_Q6_K: return down_dispatch<FMT_Q6_K>(a, s, ev);
+    case FMT_Q5_K: return down_dispatch<FMT_Q5_K>(a, s, ev);
     default: return down_dispatch<FMT_MXFP4>(a, s, ev);
   }
 }
@@ -1463,6 +1467,9 @@ hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_
   switch (fmt) {
     case FMT_Q4_K:
       return launch(k_block_dots<FMT_Q4_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
+                    bs, out);
+    case FMT_Q5_K:
+      return launch(k_block_dots<FMT_Q5_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
                     bs, out);
     case FMT_Q6_K:
       return launch(k_block_dots<FMT_Q6_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,

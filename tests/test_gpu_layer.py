@@ -40,6 +40,21 @@ def test_layer_mxfp4_shapes(H, F, k, shared):
     check_layer(cfg)
 
 
+@pytest.mark.parametrize("name,fmt_gu,fmt_d,T", [
+    ("qwen3.6-35b-a3b", "Q5_K", "Q5_K", 1), ("qwen3.6-35b-a3b", "Q5_K", "Q5_K", 6),
+    ("deepseek-v4-flash", "Q5_K", "Q6_K", 3), ("deepseek-v4-flash", "Q4_K", "Q5_K", 16),
+    ("qwen-full", "Q5_K", "Q5_K", 1)])
+def test_layer_q5k(name, fmt_gu, fmt_d, T):
+    """Q5_K experts (gate/up, down or both) through the per-pair GEMV kernels,
+    which every chunk of a Q5_K layer takes (no MFMA tile kernel for it): the
+    shrunk Qwen3.6 and DeepSeek-V4-Flash shapes, up to a 16-token chunk, and the
+    full Qwen3.6 shape at one token."""
+    f = {"Q4_K": gen.Q4_K, "Q5_K": gen.Q5_K, "Q6_K": gen.Q6_K}
+    base = gen.CONFIGS["qwen3.6-35b-a3b"] if name == "qwen-full" else SHRUNK[name]
+    cfg = base.with_(name=f"{base.name}-{fmt_gu}-{fmt_d}", fmt_gu=f[fmt_gu], fmt_d=f[fmt_d], T=T)
+    check_layer(cfg, x_index=T)
+
+
 def _routed_layer(cfg, T, x_index):
     """The full-size layer with only the experts the oracle routes these tokens
     to (plus the shared expert) generated; the others stay zero and unused."""
