@@ -365,6 +365,11 @@ struct FmtQ4K {
     r.hdr = ld_nt16(blk);
     r.q = ld_nt16(blk + 16 + 16 * sub);
   }
+  // the same share from a block staged in LDS
+  __device__ static __forceinline__ void lds_load(Raw& r, const uint8_t* blk, int sub) {
+    r.hdr = *reinterpret_cast<const uint4*>(blk);
+    r.q = *reinterpret_cast<const uint4*>(blk + 16 + 16 * sub);
+  }
   // Lane `sub` holds qs bytes 16*sub..16*sub+15: chunk c = sub/2, half hh = sub%2, i.e.
   // weights 64c+16hh+i (low nibbles, sub-block 2c) and 64c+32+16hh+i (high, 2c+1).
   __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int sub) {
@@ -433,6 +438,11 @@ struct FmtQ5K {
     r.hdr = ld_nt16(blk);
     r.qh = ld_nt16(blk + 16 + 16 * (sub & 1));
     r.q = ld_nt16(blk + 48 + 16 * sub);
+  }
+  __device__ static __forceinline__ void lds_load(Raw& r, const uint8_t* blk, int sub) {
+    r.hdr = *reinterpret_cast<const uint4*>(blk);
+    r.qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (sub & 1));
+    r.q = *reinterpret_cast<const uint4*>(blk + 48 + 16 * sub);
   }
   __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int sub) {
     const int c = sub >> 1, hh = sub & 1;

@@ -825,17 +825,17 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
   }
 }
 
-// Q4_K down with the rows staged in LDS. grid (ceil(H / R), T), block 512.
-// Same result as k_down. Waves 0-2 copy the down rows [row0, row0 + R) of
+// Q4_K / Q5_K down with the rows staged in LDS. grid (ceil(H / R), T), block
+// 512. Same result as k_down. Waves 0-2 copy the down rows [row0, row0 + R) of
 // every present slot straight into LDS (global->LDS loads, 16-byte pieces; a
-// Q4_K row is 144 nb bytes, a multiple of 16) while waves 3-7 quantize h (the
+// row is 144 nb or 176 nb bytes, a multiple of 16) while waves 3-7 quantize h (the
 // longer of the two paths: 3:5 measured best of 2:6, 3:5 and 4:4); then all
 // eight waves multiply out of LDS, TPG block tasks per 8-lane group.
 constexpr int kStreamers = 3, kQuantizers = 8 - kStreamers;
-template <int TPG, int JB>
-__global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, Div dR, Div dpc,
-                                                      Div dq) {
-  using F = FmtQ4K;
+template <int FMT, int TPG, int JB>
+__global__ __launch_bounds__(512) void k_down_lds(KArgs a, int R, Div dnb, Div dR, Div dpc,
+                                                  Div dq) {
+  using F = typename FmtOf<FMT>::T;
   extern __shared__ __align__(16) unsigned char smem[];
   const int t = blockIdx.y, row0 = blockIdx.x * R;
   const int K = a.F, nb = K / 256;
@@ -939,9 +939,8 @@ __global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, D
         const int b = dnb.mod(task, q1), r = dR.mod(q1, sl);
         if (row0 + r < a.H && ((present >> sl) & 1u)) {
           const uint8_t* blk = wl + static_cast<size_t>(q1) * row_bytes + b * F::BB;
-          F::Raw raw;
-          raw.hdr = *reinterpret_cast<const uint4*>(blk);
-          raw.q = *reinterpret_cast<const uint4*>(blk + 16 + 16 * sub);
+          typename F::Raw raw;
+          F::lds_load(raw, blk, sub);
           const ActView av{reinterpret_cast<const int8_t*>(p_act + sl * K), ld + sl * (K / 32),
                            lbs + sl * (K / 16), nullptr};
           const float v = block_value<F>(raw, av, b, sub);
@@ -974,8 +973,8 @@ __global__ __launch_bounds__(512) void k_down_q4k_lds(KArgs a, int R, Div dnb, D
 
 // MXFP4 down with the rows realigned per wave (see mx_pair). grid
 // (ceil(H / R), T), block 512, R even. Units are (slot s, row pair r, r + 1)
-// for s < ns, taken slot-major; wave w owns units [w upw, (w + 1) upw) and
-// issues up to RPW of them at a time. Each wave first loads the h pieces of
+// for s < ns, taken slot-major; wave w owns units [w upw, (w + 1) upw), upw <=
+// RPW (the host plan), and issues them at once. Each wave first loads the h pieces of
 // its quantization jobs (256 values of one slot's h, job = wave + 8 u), then
 // its first weight batch, then quantizes (32-value blocks, fp32 recipe) into
 // the LDS image: loads complete in issue order, so the quantization waits for
@@ -1074,26 +1073,23 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
   __syncthreads();
   MxAct<NBL> A;
   int cur = -1;  // slot whose activations A holds (wave-uniform)
-  for (int ub = u0; ub < u1; ub += RPW) {
-    if (ub != u0) issue(ub);
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int u = ub + i;
-      if (u < u1) {
-        const int s = u / nrp, rp = u - s * nrp, r = row0 + 2 * rp;
-        if (((present >> s) & 1u) && r < a.H) {
-          if (s != cur) {
-            mx_act_load(A, reinterpret_cast<const half2_t*>(p_act + s * act_bytes), ld + s * nb,
-                        nb, lane);
-            cur = s;
-          }
-          const float2 o = mx_pair<NL, NBL>(pcs[i], scr, nb, A, lane);
-          if (lane == 0) {
-            const float* bias = dbias[s];
-            part[(2 * rp) * ns + s] = wslot[s] * (o.x + (bias ? bias[r] : 0.0f));
-            if (2 * rp + 1 < R && r + 1 < a.H)
-              part[(2 * rp + 1) * ns + s] = wslot[s] * (o.y + (bias ? bias[r + 1] : 0.0f));
-          }
+  for (int i = 0; i < RPW; ++i) {
+    const int u = u0 + i;
+    if (u < u1) {
+      const int s = u / nrp, rp = u - s * nrp, r = row0 + 2 * rp;
+      if (((present >> s) & 1u) && r < a.H) {
+        if (s != cur) {
+          mx_act_load(A, reinterpret_cast<const half2_t*>(p_act + s * act_bytes), ld + s * nb,
+                      nb, lane);
+          cur = s;
+        }
+        const float2 o = mx_pair<NL, NBL>(pcs[i], scr, nb, A, lane);
+        if (lane == 0) {
+          const float* bias = dbias[s];
+          part[(2 * rp) * ns + s] = wslot[s] * (o.x + (bias ? bias[r] : 0.0f));
+          if (2 * rp + 1 < R && r + 1 < a.H)
+            part[(2 * rp + 1) * ns + s] = wslot[s] * (o.y + (bias ? bias[r + 1] : 0.0f));
         }
       }
     }
@@ -1245,8 +1241,10 @@ bool mx_gateup_fits(const KArgs& a) {
 }
 bool mx_down_fits(const KArgs& a) {
   MxPlan pl;
+  if (a.fmt_d != FMT_MXFP4 || !mx_plan(a.F, &pl)) return false;
   const int ns = a.k + a.has_shared;
-  return a.fmt_d == FMT_MXFP4 && mx_plan(a.F, &pl) && mx_down_lds(a, pl) <= kMaxLds &&
+  const int units = ns * (mx_down_rows(a, pl) / 2);  // every wave's units in one batch
+  return mx_down_lds(a, pl) <= kMaxLds && (units + 7) / 8 <= pl.rpw &&
          ns * ((a.F + 255) / 256) <= 8 * kMxDownJobs;
 }
 
@@ -1314,12 +1312,13 @@ hipError_t down_jb(int jobs_per_wave, dim3 grid, size_t lds, hipStream_t s, Ev e
   return launch(k_down<FMT, TPG, 8, false>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
 }
 
-// Plan of the LDS-staged Q4_K down kernel: one workgroup per compute unit
-// where the LDS (q8 of h + R rows per slot) and 8 tasks per lane group allow.
+// Plan of the LDS-staged down kernel (Q4_K, Q5_K): one workgroup per compute
+// unit where the LDS (q8 of h + R rows per slot) and 8 tasks per lane group allow.
 struct DownLdsPlan { int R, tpg; size_t lds; };
 bool down_lds_plan(const KArgs& a, DownLdsPlan* out) {
-  if (a.fmt_d != FMT_Q4_K) return false;
-  const int ns = a.k + a.has_shared, K = a.F, nb = K / 256, npc = nb * 9;
+  if (a.fmt_d != FMT_Q4_K && a.fmt_d != FMT_Q5_K) return false;
+  const int ns = a.k + a.has_shared, K = a.F, nb = K / 256;
+  const int npc = nb * (a.fmt_d == FMT_Q4_K ? 144 : 176) / 16;  // 16-byte pieces per row
   const int per_token = max(1, 256 / max(a.T, 1));
   int R = max(1, min((a.H + per_token - 1) / per_token, a.H));
   auto lds_of = [&](int r) {
@@ -1332,30 +1331,30 @@ bool down_lds_plan(const KArgs& a, DownLdsPlan* out) {
   return true;
 }
 
-template <int TPG>
+template <int FMT, int TPG>
 hipError_t down_lds_jb(int jobs_per_wave, dim3 grid, size_t lds, hipStream_t s, Ev ev,
                        const KArgs& a, int R, Div dnb, Div dR, Div dpc, Div dq) {
-  if (jobs_per_wave <= 2) return launch(k_down_q4k_lds<TPG, 2>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc, dq);
-  if (jobs_per_wave <= 5) return launch(k_down_q4k_lds<TPG, 5>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc, dq);
-  return launch(k_down_q4k_lds<TPG, 8>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc, dq);
+  if (jobs_per_wave <= 2) return launch(k_down_lds<FMT, TPG, 2>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc, dq);
+  if (jobs_per_wave <= 5) return launch(k_down_lds<FMT, TPG, 5>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc, dq);
+  return launch(k_down_lds<FMT, TPG, 8>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc, dq);
 }
 
 template <int FMT>
 hipError_t down_dispatch(const KArgs& a, hipStream_t s, Ev ev) {
   if (FMT == FMT_MXFP4 && mx_down_fits(a)) return down_mx(a, s, ev);
-  if constexpr (FMT == FMT_Q4_K) {
+  if constexpr (FMT == FMT_Q4_K || FMT == FMT_Q5_K) {
     DownLdsPlan pl;
     if (down_lds_plan(a, &pl)) {
       const int nb = a.F / 256, pieces = a.F / 256;
       const dim3 grid((a.H + pl.R - 1) / pl.R, a.T);
       const Div dnb = Div::make(nb), dR = Div::make(pl.R), dpc = Div::make(pieces),
-                dq = Div::make(nb * 9);
+                dq = Div::make(nb * FmtOf<FMT>::T::BB / 16);
       const int jpw = ((a.k + a.has_shared) * pieces + kQuantizers - 1) / kQuantizers;
       switch (tpg_bucket(pl.tpg)) {
-        case 1: return down_lds_jb<1>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
-        case 2: return down_lds_jb<2>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
-        case 4: return down_lds_jb<4>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
-        default: return down_lds_jb<8>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
+        case 1: return down_lds_jb<FMT, 1>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
+        case 2: return down_lds_jb<FMT, 2>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
+        case 4: return down_lds_jb<FMT, 4>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
+        default: return down_lds_jb<FMT, 8>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
       }
     }
   }
