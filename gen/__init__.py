@@ -18,10 +18,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoegen.so")
 _lib = None
 
-Q4_K, Q6_K, MXFP4, Q5_K = 0, 1, 2, 3
-FMT_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", MXFP4: "MXFP4", Q5_K: "Q5_K"}
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, MXFP4: 17, Q5_K: 176}
-BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, MXFP4: 32, Q5_K: 256}
+Q4_K, Q6_K, MXFP4, Q5_K, Q2_K = 0, 1, 2, 3, 4
+FMT_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", MXFP4: "MXFP4", Q5_K: "Q5_K", Q2_K: "Q2_K"}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, MXFP4: 17, Q5_K: 176, Q2_K: 84}
+BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, MXFP4: 32, Q5_K: 256, Q2_K: 256}
 
 T_ROUTER, T_X, T_GATE, T_UP, T_DOWN, T_BGATE, T_BUP, T_BDOWN, T_ZIPF, T_SHVEC = range(1, 11)
 
@@ -55,12 +55,14 @@ def lib():
         L.mg_round_bf16.argtypes = [vp, vp, sz]
         L.mg_fp16_ceil_bits.argtypes = [f64]
         L.mg_fp16_ceil_bits.restype = C.c_uint16
-        for n in ("mg_encode_q4k", "mg_encode_q6k", "mg_encode_mxfp4", "mg_encode_q5k"):
+        for n in ("mg_encode_q4k", "mg_encode_q6k", "mg_encode_mxfp4", "mg_encode_q5k",
+                  "mg_encode_q2k"):
             getattr(L, n).argtypes = [vp, vp]
         L.mg_encode_matrix.argtypes = [i32, vp, i32, i32, sz, vp, i32]
         L.mg_pack_q4k.argtypes = [C.c_uint16, C.c_uint16, vp, vp, vp, vp]
         L.mg_pack_q6k.argtypes = [C.c_uint16, vp, vp, vp]
         L.mg_pack_q5k.argtypes = [C.c_uint16, C.c_uint16, vp, vp, vp, vp]
+        L.mg_pack_q2k.argtypes = [C.c_uint16, C.c_uint16, vp, vp, vp, vp]
         L.mg_pack_mxfp4.argtypes = [C.c_uint8, vp, vp]
         L.mg_weight_matrix.argtypes = [u64, u32, u32, i32, i32, i32, sz, f64, vp, i32]
         L.mg_zipf_bias.argtypes = [u64, i32, f64, vp]
@@ -110,7 +112,7 @@ def encode_block(fmt: int, x: np.ndarray) -> np.ndarray:
     assert x.size == BLOCK_ELEMS[fmt]
     out = np.zeros(BLOCK_BYTES[fmt], dtype=np.uint8)
     fn = {Q4_K: "mg_encode_q4k", Q6_K: "mg_encode_q6k", MXFP4: "mg_encode_mxfp4",
-          Q5_K: "mg_encode_q5k"}[fmt]
+          Q5_K: "mg_encode_q5k", Q2_K: "mg_encode_q2k"}[fmt]
     getattr(lib(), fn)(_ptr(x), _ptr(out))
     return out
 
@@ -150,6 +152,15 @@ def pack_q5k(d_bits: int, dmin_bits: int, sc, m, q) -> np.ndarray:
     assert sc.size == 8 and m.size == 8 and q.size == 256
     out = np.zeros(176, dtype=np.uint8)
     lib().mg_pack_q5k(d_bits, dmin_bits, _ptr(sc), _ptr(m), _ptr(q), _ptr(out))
+    return out
+
+
+def pack_q2k(d_bits: int, dmin_bits: int, sc, m, q) -> np.ndarray:
+    sc = np.ascontiguousarray(sc, dtype=np.uint8); m = np.ascontiguousarray(m, dtype=np.uint8)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    assert sc.size == 16 and m.size == 16 and q.size == 256
+    out = np.zeros(84, dtype=np.uint8)
+    lib().mg_pack_q2k(d_bits, dmin_bits, _ptr(sc), _ptr(m), _ptr(q), _ptr(out))
     return out
 
 

@@ -131,7 +131,7 @@ static inline double rne(double v) {
 }
 
 size_t mg_block_bytes(int fmt) {
-  return fmt == MG_Q4_K ? 144 : fmt == MG_Q6_K ? 210 : fmt == MG_Q5_K ? 176 : 17;
+  return fmt == MG_Q4_K ? 144 : fmt == MG_Q6_K ? 210 : fmt == MG_Q5_K ? 176 : fmt == MG_Q2_K ? 84 : 17;
 }
 int mg_block_elems(int fmt) { return fmt == MG_MXFP4 ? 32 : 256; }
 
@@ -168,6 +168,23 @@ void mg_pack_q5k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const u
                      (((q[64 * c + 32 + l] >> 4) & 1) << (2 * c + 1)));
     qh[l] = h;
   }
+}
+
+/* Q2_K (84 B): scales[16] (scale low nibble, min high nibble, one per 16
+ * weights), qs[64] (half h: bits 2j..2j+1 of qs[32h + l] is weight 128h + 32j + l),
+ * fp16 d at 80, dmin at 82. */
+void mg_pack_q2k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const uint8_t* m,
+                 const uint8_t* q, uint8_t* blk) {
+  for (int s = 0; s < 16; ++s) blk[s] = (uint8_t)((sc[s] & 15) | ((m[s] & 15) << 4));
+  uint8_t* qs = blk + 16;
+  for (int h = 0; h < 2; ++h)
+    for (int l = 0; l < 32; ++l) {
+      uint8_t v = 0;
+      for (int j = 0; j < 4; ++j) v |= (uint8_t)((q[128 * h + 32 * j + l] & 3) << (2 * j));
+      qs[32 * h + l] = v;
+    }
+  blk[80] = (uint8_t)d_bits; blk[81] = (uint8_t)(d_bits >> 8);
+  blk[82] = (uint8_t)dmin_bits; blk[83] = (uint8_t)(dmin_bits >> 8);
 }
 
 void mg_pack_q6k(uint16_t d_bits, const int8_t* sc, const uint8_t* q, uint8_t* blk) {
@@ -243,6 +260,50 @@ void mg_encode_q4k(const float* x, uint8_t* blk) {
   uint8_t sc[8], m[8], q[256];
   encode_scale_min(x, 15, &d_bits, &dmin_bits, sc, m, q);
   mg_pack_q4k(d_bits, dmin_bits, sc, m, q, blk);
+}
+
+/* Q2_K: 16 sub-blocks of 16 with 4-bit scale and min, 2-bit quants. Covering:
+ * m_s * dmin >= -min of the sub-block, sc_s * d * 3 >= max + m_s * dmin. */
+void mg_encode_q2k(const float* x, uint8_t* blk) {
+  double mx[16], off[16], need[16], maxoff = 0.0, maxneed = 0.0;
+  for (int s = 0; s < 16; ++s) {
+    double lo = 0.0, hi = -INFINITY;
+    for (int i = 0; i < 16; ++i) {
+      double v = x[16 * s + i];
+      if (v < lo) lo = v;
+      if (v > hi) hi = v;
+    }
+    mx[s] = hi; off[s] = -lo;
+    if (off[s] > maxoff) maxoff = off[s];
+  }
+  uint16_t dmin_bits = mg_fp16_ceil_bits(maxoff / 15.0);
+  double dmin = fp16_value(dmin_bits);
+  uint8_t sc[16], m[16], q[256];
+  double mhat[16];
+  for (int s = 0; s < 16; ++s) {
+    double ms = dmin > 0.0 ? ceil(off[s] / dmin) : 0.0;
+    if (ms > 15.0) ms = 15.0;
+    m[s] = (uint8_t)ms;
+    mhat[s] = dmin * ms;
+    need[s] = (mx[s] + mhat[s]) / 3.0;
+    if (need[s] < 0.0) need[s] = 0.0;
+    if (need[s] > maxneed) maxneed = need[s];
+  }
+  uint16_t d_bits = mg_fp16_ceil_bits(maxneed / 15.0);
+  double d = fp16_value(d_bits);
+  for (int s = 0; s < 16; ++s) {
+    double c = d > 0.0 ? ceil(need[s] / d) : 0.0;
+    if (c > 15.0) c = 15.0;
+    sc[s] = (uint8_t)c;
+    double shat = d * c;
+    for (int i = 0; i < 16; ++i) {
+      double v = shat > 0.0 ? rne(((double)x[16 * s + i] + mhat[s]) / shat) : 0.0;
+      if (v < 0.0) v = 0.0;
+      if (v > 3.0) v = 3.0;
+      q[16 * s + i] = (uint8_t)v;
+    }
+  }
+  mg_pack_q2k(d_bits, dmin_bits, sc, m, q, blk);
 }
 
 void mg_encode_q5k(const float* x, uint8_t* blk) {
@@ -332,6 +393,7 @@ static void enc_rows(void* p, int r0, int r1) {
     for (int b = 0; b < nb; ++b) {
       if (c->fmt == MG_Q4_K) mg_encode_q4k(xr + b * be, row + b * bb);
       else if (c->fmt == MG_Q5_K) mg_encode_q5k(xr + b * be, row + b * bb);
+      else if (c->fmt == MG_Q2_K) mg_encode_q2k(xr + b * be, row + b * bb);
       else if (c->fmt == MG_Q6_K) mg_encode_q6k(xr + b * be, row + b * bb);
       else mg_encode_mxfp4(xr + b * be, row + b * bb);
     }

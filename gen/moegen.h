@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-enum { MG_Q4_K = 0, MG_Q6_K = 1, MG_MXFP4 = 2, MG_Q5_K = 3 };
+enum { MG_Q4_K = 0, MG_Q6_K = 1, MG_MXFP4 = 2, MG_Q5_K = 3, MG_Q2_K = 4 };
 
 /* Tensor identifiers that key the random streams. */
 enum {
@@ -58,6 +58,7 @@ uint16_t mg_fp16_ceil_bits(double v);
 /* Covering encoders: one block from 256 (Q4_K, Q5_K, Q6_K) or 32 (MXFP4) fp32 values. */
 void mg_encode_q4k(const float* x, uint8_t* blk);
 void mg_encode_q5k(const float* x, uint8_t* blk);
+void mg_encode_q2k(const float* x, uint8_t* blk);
 void mg_encode_q6k(const float* x, uint8_t* blk);
 void mg_encode_mxfp4(const float* x, uint8_t* blk);
 /* Encode a [rows x K] fp32 matrix into block rows at byte stride `stride`
@@ -72,6 +73,9 @@ void mg_encode_matrix(int fmt, const float* x, int rows, int K, size_t stride, u
 void mg_pack_q4k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const uint8_t* m,
                  const uint8_t* q, uint8_t* blk);
 void mg_pack_q6k(uint16_t d_bits, const int8_t* sc, const uint8_t* q, uint8_t* blk);
+/* q2k: sc[16], m[16] in 0..15, q[256] in 0..3. */
+void mg_pack_q2k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const uint8_t* m,
+                 const uint8_t* q, uint8_t* blk);
 /* q5k: as q4k with q[256] in 0..31. */
 void mg_pack_q5k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const uint8_t* m,
                  const uint8_t* q, uint8_t* blk);

@@ -37,7 +37,7 @@ double or_e2m1(uint8_t code) {
 
 int or_block_elems(int fmt) { return fmt == OR_MXFP4 ? 32 : 256; }
 int or_block_bytes(int fmt) {
-  return fmt == OR_Q4_K ? 144 : fmt == OR_Q6_K ? 210 : fmt == OR_Q5_K ? 176 : 17;
+  return fmt == OR_Q4_K ? 144 : fmt == OR_Q6_K ? 210 : fmt == OR_Q5_K ? 176 : fmt == OR_Q2_K ? 84 : 17;
 }
 
 static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
@@ -79,6 +79,14 @@ void or_block_quants(int fmt, const uint8_t* blk, int32_t* q) {
       int hi = (qh[l] >> (2 * c + (i < 32 ? 0 : 1))) & 1;
       q[n] = lo | (hi << 4);
     }
+  } else if (fmt == OR_Q2_K) {
+    /* Two halves of 128 over qs[32h .. 32h+31] (byte 16): in half h, weight
+     * 32j + l (l < 32) is bits 2j..2j+1 of qs[32h + l]. */
+    const uint8_t* qs = blk + 16;
+    for (int n = 0; n < 256; ++n) {
+      int h = n / 128, r = n % 128, j = r / 32, l = r % 32;
+      q[n] = (qs[32 * h + l] >> (2 * j)) & 3;
+    }
   } else if (fmt == OR_Q6_K) {
     /* Two halves of 128; in half h, element r = 32*quarter + i takes its low
      * 4 bits from ql and its high 2 bits from qh[32h+i] bits 2*quarter.. */
@@ -109,6 +117,11 @@ void or_dequant_block(int fmt, const uint8_t* blk, double* out) {
     int sc[8], m[8];
     q4k_scales(blk, sc, m);
     for (int n = 0; n < 256; ++n) out[n] = d * sc[n / 32] * q[n] - dmin * m[n / 32];
+  } else if (fmt == OR_Q2_K) {
+    /* scales[s] (s = n / 16): low nibble scale, high nibble min */
+    double d = or_fp16(rd16(blk + 80)), dmin = or_fp16(rd16(blk + 82));
+    for (int n = 0; n < 256; ++n)
+      out[n] = d * (blk[n / 16] & 15) * q[n] - dmin * (blk[n / 16] >> 4);
   } else if (fmt == OR_Q6_K) {
     double d = or_fp16(rd16(blk + 208));
     const int8_t* sc = (const int8_t*)(blk + 192);
@@ -178,6 +191,18 @@ void or_block_partials(int fmt, const uint8_t* row, int K, const int8_t* qs,
       }
       out[2 * b] = (int32_t)S1;
       out[2 * b + 1] = (int32_t)S2;
+    } else if (fmt == OR_Q2_K) {
+      /* per sub-block of 16: S1 += sc_s * dot_s, S2 += m_s * (sum of its activations) */
+      const int16_t* bs = bsums + (size_t)b * 16;
+      int64_t S1 = 0, S2 = 0;
+      for (int s = 0; s < 16; ++s) {
+        int64_t dot = 0;
+        for (int i = 0; i < 16; ++i) dot += (int64_t)q[16 * s + i] * a[16 * s + i];
+        S1 += (int64_t)(blk[s] & 15) * dot;
+        S2 += (int64_t)(blk[s] >> 4) * bs[s];
+      }
+      out[2 * b] = (int32_t)S1;
+      out[2 * b + 1] = (int32_t)S2;
     } else if (fmt == OR_Q6_K) {
       const int8_t* sc = (const int8_t*)(blk + 192);
       const int16_t* bs = bsums + (size_t)b * 16;
@@ -201,6 +226,9 @@ void or_block_partials(int fmt, const uint8_t* row, int K, const int8_t* qs,
 double or_block_value(int fmt, const uint8_t* blk, const int32_t* p, float d8) {
   if (fmt == OR_Q4_K || fmt == OR_Q5_K) {
     double d = or_fp16(rd16(blk)), dmin = or_fp16(rd16(blk + 2));
+    return (double)d8 * (d * p[0] - dmin * p[1]);
+  } else if (fmt == OR_Q2_K) {
+    double d = or_fp16(rd16(blk + 80)), dmin = or_fp16(rd16(blk + 82));
     return (double)d8 * (d * p[0] - dmin * p[1]);
   } else if (fmt == OR_Q6_K) {
     return (double)d8 * or_fp16(rd16(blk + 208)) * p[0];

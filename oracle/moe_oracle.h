@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-enum { OR_Q4_K = 0, OR_Q6_K = 1, OR_MXFP4 = 2, OR_Q5_K = 3 };
+enum { OR_Q4_K = 0, OR_Q6_K = 1, OR_MXFP4 = 2, OR_Q5_K = 3, OR_Q2_K = 4 };
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 enum { OR_SWIGLU = 0, OR_SWIGLU_OAI = 1 };
 

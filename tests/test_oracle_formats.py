@@ -95,6 +95,43 @@ def test_q5k_byte_layout(orc):
     assert np.array_equal(orc.dequant_row(oracle.Q5_K, blk, 256), want.astype(np.float64))
 
 
+def test_q2k_hand_packed_fields(orc, genlib):
+    rng = np.random.default_rng(4)
+    for trial in range(50):
+        sc = rng.integers(0, 16, 16).astype(np.uint8)
+        m = rng.integers(0, 16, 16).astype(np.uint8)
+        q = rng.integers(0, 4, 256).astype(np.uint8)
+        d_bits = int(rng.integers(0x1000, 0x3000))
+        dmin_bits = int(rng.integers(0x1000, 0x3000))
+        blk = gen.pack_q2k(d_bits, dmin_bits, sc, m, q)
+        d = float(np.array([d_bits], np.uint16).view(np.float16)[0])
+        dmin = float(np.array([dmin_bits], np.uint16).view(np.float16)[0])
+        assert np.array_equal(orc.block_quants(oracle.Q2_K, blk), q)
+        want = np.array([d * sc[n // 16] * q[n] - dmin * m[n // 16] for n in range(256)])
+        assert np.array_equal(orc.dequant_row(oracle.Q2_K, blk, 256), want)
+
+
+def test_q2k_byte_layout(orc):
+    """A Q2_K block written byte by byte: scales[s] = scale | min << 4 for the
+    16 weights of sub-block s; weight 128h + 32j + l is bits 2j..2j+1 of
+    qs[32h + l] (byte 16 + 32h + l); d at byte 80, dmin at 82."""
+    blk = np.zeros(84, np.uint8)
+    blk[80:82] = [0x00, 0x3C]          # d = 1.0
+    blk[82:84] = [0x00, 0x38]          # dmin = 0.5
+    blk[0] = 0x21                      # sub-block 0: scale 1, min 2
+    blk[15] = 0x03                     # sub-block 15: scale 3, min 0
+    blk[16 + 0] = 0b11100100           # weights 0, 32, 64, 96: 0, 1, 2, 3
+    blk[16 + 32 + 31] = 0b10000000     # weight 128 + 96 + 31 = 255: 2
+    want_q = np.zeros(256, np.int64)
+    want_q[[0, 32, 64, 96, 255]] = [0, 1, 2, 3, 2]
+    assert np.array_equal(orc.block_quants(oracle.Q2_K, blk), want_q)
+    want = np.zeros(256)
+    want[:16] = -1.0                   # sub-block 0: 1 * q - 0.5 * 2 with q = 0
+    want[255] = 3.0 * 2
+    want[32], want[64], want[96] = 0.0, 0.0, 0.0  # their sub-blocks have scale 0, min 0
+    assert np.array_equal(orc.dequant_row(oracle.Q2_K, blk, 256), want)
+
+
 def test_q6k_hand_packed_fields(orc, genlib):
     rng = np.random.default_rng(1)
     for trial in range(50):
@@ -171,6 +208,25 @@ def test_q5k_round_trip_bound(orc, genlib, std):
             loose = (rng_j / 31 + d + 2 * abs(orc.fp16(int(blk[2]) | int(blk[3]) << 8))) / 2
             assert err[32 * j:32 * j + 32].max() <= loose * (1 + 1e-9) + 1e-300, (r, j)
         assert q.min() >= 0 and q.max() <= 31
+
+
+@pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])
+def test_q2k_round_trip_bound(orc, genlib, std):
+    x = _blocks(gen.Q2_K, 300, std, 15)
+    for r in range(x.shape[0]):
+        blk = gen.encode_block(gen.Q2_K, x[r])
+        xh = orc.dequant_row(oracle.Q2_K, blk, 256)
+        d = orc.fp16(int(blk[80]) | int(blk[81]) << 8)
+        dmin = orc.fp16(int(blk[82]) | int(blk[83]) << 8)
+        q = orc.block_quants(oracle.Q2_K, blk)
+        err = np.abs(x[r].astype(np.float64) - xh)
+        for s in range(16):
+            xs = x[r, 16 * s:16 * s + 16].astype(np.float64)
+            rng_s = max(xs.max(), 0) - min(xs.min(), 0)
+            # covering step at most range/3 plus one unit of d and dmin, error half a step
+            loose = (rng_s / 3 + d + 2 * dmin) / 2
+            assert err[16 * s:16 * s + 16].max() <= loose * (1 + 1e-9) + 1e-300, (r, s)
+        assert q.min() >= 0 and q.max() <= 3
 
 
 @pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])

@@ -71,7 +71,7 @@ def _rand_act(K, seed):
 
 
 @pytest.mark.parametrize("fmt,K", [(gen.Q4_K, 1024), (gen.Q6_K, 1024), (gen.MXFP4, 1024),
-                                   (gen.Q5_K, 1024)])
+                                   (gen.Q5_K, 1024), (gen.Q2_K, 1024)])
 def test_block_dot_identity(orc, genlib, fmt, K):
     """Integer factorization == fp64 dot of fully dequantized weights and activations."""
     B = 32 if fmt == gen.MXFP4 else 256
