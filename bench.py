@@ -48,7 +48,7 @@ def parse():
 
 
 DEFAULT_COPIES = {"tiny": 1, "qwen3.6-35b-a3b": 40, "gpt-oss-20b": 24, "deepseek-v4-flash": 4,
-                  "kimi-k2": 2, "qwen3.6-35b-a3b-q5k": 40}
+                  "kimi-k2": 2, "qwen3.6-35b-a3b-q5k": 40, "qwen3.6-35b-a3b-q2k": 40}
 
 
 def main():

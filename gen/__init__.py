@@ -291,6 +291,11 @@ CONFIGS = {
         fmt_gu=Q5_K, fmt_d=Q5_K,
         description="Qwen3.6-35B-A3B-shaped decode layer with Q5_K experts: H 2048, 256 experts "
                     "top-8 softmax + shared, F 512, Q5_K"),
+    "qwen3.6-35b-a3b-q2k": LayerConfig(
+        "qwen3.6-35b-a3b-q2k", H=2048, F=512, E=256, k=8, T=1, seed=6, shared=True,
+        fmt_gu=Q2_K, fmt_d=Q2_K,
+        description="Qwen3.6-35B-A3B-shaped decode layer with Q2_K experts: H 2048, 256 experts "
+                    "top-8 softmax + shared, F 512, Q2_K"),
 }
 CONFIG_ORDER = ["tiny", "qwen3.6-35b-a3b", "gpt-oss-20b", "deepseek-v4-flash", "kimi-k2"]
 

@@ -63,16 +63,19 @@ typedef enum {
 
 /* Stored weight block formats (GGUF block layouts; MXFP4 as OCP MX v1.0):
  * Q4_K 144 B / 256 weights, Q6_K 210 B / 256, MXFP4 17 B / 32, Q5_K 176 B / 256
- * (Q4_K's fp16 d, dmin and 6-bit scales, 32 B of fifth bits, 128 B of nibbles).
- * Layers with a Q5_K matrix take the per-(token, slot) GEMV path for every T. */
+ * (Q4_K's fp16 d, dmin and 6-bit scales, 32 B of fifth bits, 128 B of nibbles),
+ * Q2_K 84 B / 256 (16 scale/min nibble pairs, 64 B of 2-bit quants, fp16 d,
+ * dmin). Layers with a Q5_K or Q2_K matrix take the per-(token, slot) GEMV path
+ * for every T. */
 typedef enum {
   MOE_WFMT_Q4_K = 0,
   MOE_WFMT_Q6_K = 1,
   MOE_WFMT_MXFP4 = 2,
-  MOE_WFMT_Q5_K = 3
+  MOE_WFMT_Q5_K = 3,
+  MOE_WFMT_Q2_K = 4
 } moe_wfmt;
 /* Activation quant formats: Q8_K = blocks of 256 with 16-element sums
- * (consumed by Q4_K, Q5_K and Q6_K rows); Q8_32 = blocks of 32 (MXFP4 rows). */
+ * (consumed by Q4_K, Q5_K, Q2_K and Q6_K rows); Q8_32 = blocks of 32 (MXFP4 rows). */
 typedef enum { MOE_AFMT_Q8_K = 0, MOE_AFMT_Q8_32 = 1 } moe_afmt;
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 } moe_router;

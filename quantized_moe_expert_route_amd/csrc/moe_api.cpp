@@ -15,7 +15,7 @@ constexpr int kMaxTokens = 2048;
 
 int block_elems(int fmt) { return fmt == FMT_MXFP4 ? 32 : 256; }
 size_t block_bytes(int fmt) {
-  return fmt == FMT_Q4_K ? 144 : fmt == FMT_Q6_K ? 210 : fmt == FMT_Q5_K ? 176 : 17;
+  return fmt == FMT_Q4_K ? 144 : fmt == FMT_Q6_K ? 210 : fmt == FMT_Q5_K ? 176 : fmt == FMT_Q2_K ? 84 : 17;
 }
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -30,7 +30,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_EINVAL;
   if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
   for (int f : {d->fmt_gate, d->fmt_up, d->fmt_down})
-    if (f != MOE_WFMT_Q4_K && f != MOE_WFMT_Q6_K && f != MOE_WFMT_MXFP4 && f != MOE_WFMT_Q5_K)
+    if (f != MOE_WFMT_Q4_K && f != MOE_WFMT_Q6_K && f != MOE_WFMT_MXFP4 && f != MOE_WFMT_Q5_K &&
+        f != MOE_WFMT_Q2_K)
       return MOE_EINVAL;
   if (d->fmt_gate != d->fmt_up) return MOE_EUNSUPPORTED;
   if (H % block_elems(d->fmt_gate) != 0 || H % 32 != 0) return MOE_EINVAL;
@@ -121,7 +122,7 @@ struct Stages {
 }  // namespace
 
 // Dispatch rule between the two expert-FFN paths: chunks of up to 4 tokens,
-// and every chunk of a layer with an MXFP4 or Q5_K matrix (formats without
+// and every chunk of a layer with an MXFP4, Q5_K or Q2_K matrix (formats without
 // MFMA tile kernels), take the per-(token, slot) GEMV path (moe_kernels.hip);
 // larger chunks of Q4_K / Q6_K layers take the
 // expert-grouped path (moe_grouped.hip), whose int8 MFMA tiles read each
@@ -367,7 +368,8 @@ const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {
 
 moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,
                                const moe_qact* xq, int token, int32_t* out, hipStream_t stream) {
-  if (fmt != MOE_WFMT_Q4_K && fmt != MOE_WFMT_Q6_K && fmt != MOE_WFMT_MXFP4 && fmt != MOE_WFMT_Q5_K)
+  if (fmt != MOE_WFMT_Q4_K && fmt != MOE_WFMT_Q6_K && fmt != MOE_WFMT_MXFP4 && fmt != MOE_WFMT_Q5_K &&
+      fmt != MOE_WFMT_Q2_K)
     return MOE_EINVAL;
   if (!rows || !aligned(rows, 16) || !out || !xq || n_rows < 0 || K <= 0) return MOE_EINVAL;
   if (K % block_elems(fmt) != 0) return MOE_EINVAL;

@@ -468,6 +468,45 @@ struct FmtQ5K {
   }
 };
 
+// Q2_K (84 B): scales[16] (scale | min << 4, one per 16 weights), qs[64] at
+// byte 16 (half h: bits 2j..2j+1 of qs[32h + l] is weight 128h + 32j + l), fp16 d
+// and dmin at byte 80. Lane `sub` (half h = sub / 4, k = sub % 4) takes qs bytes
+// 32h + 8k .. + 8, i.e. weights 128h + 32j + 8k + i (j < 4, i < 8) of sub-blocks
+// 8h + 2j + k / 2; all its fields are dword-aligned in the block.
+struct FmtQ2K {
+  static constexpr int BE = 256, BB = 84, LPB = 8;
+  struct Raw { uint2 q, sc; uint32_t dd; };
+  __device__ static __forceinline__ void load(Raw& r, const uint8_t* blk, int sub) {
+    const int h = sub >> 2, k = sub & 3;
+    const uint8_t* qs = blk + 16 + 32 * h + 8 * k;
+    r.q = make_uint2(ld_nt4(qs), ld_nt4(qs + 4));
+    r.sc = make_uint2(ld_nt4(blk + 8 * h), ld_nt4(blk + 8 * h + 4));
+    r.dd = ld_nt4(blk + 80);
+  }
+  __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int sub) {
+    const int h = sub >> 2, k = sub & 3;
+    const int8_t* ab = a.qs + b * 256 + 128 * h + 8 * k;
+    const int16_t* bs = a.bs + b * 16 + 8 * h + (k >> 1);
+    int S1 = 0, S2 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int2 av = *reinterpret_cast<const int2*>(ab + 32 * j);
+      int dot = sdot4(static_cast<int>((r.q.x >> (2 * j)) & 0x03030303u), av.x, 0);
+      dot = sdot4(static_cast<int>((r.q.y >> (2 * j)) & 0x03030303u), av.y, dot);
+      // scale byte 2j + k / 2 of the eight at 8h
+      const uint32_t sw = j < 2 ? r.sc.x : r.sc.y;
+      const int byte = (sw >> (8 * (2 * (j & 1) + (k >> 1)))) & 0xFF;
+      S1 += (byte & 15) * dot;
+      if ((k & 1) == 0) S2 += (byte >> 4) * bs[2 * j];  // one lane of each pair adds the min term
+    }
+    return make_int2(sum8(S1), sum8(S2));
+  }
+  __device__ static __forceinline__ float value(const Raw& r, int2 p, float d8) {
+    const float d = half_bits_to_f32(r.dd & 0xFFFF), dmin = half_bits_to_f32(r.dd >> 16);
+    return d8 * (d * static_cast<float>(p.x) - dmin * static_cast<float>(p.y));
+  }
+};
+
 struct FmtQ6K {
   static constexpr int BE = 256, BB = 210, LPB = 8;
   // Lane `sub`: half h = sub/4, j = sub%4 holds element i in [8j, 8j+8) of the four
@@ -557,6 +596,7 @@ template <> struct FmtOf<FMT_Q4_K> { using T = FmtQ4K; };
 template <> struct FmtOf<FMT_Q6_K> { using T = FmtQ6K; };
 template <> struct FmtOf<FMT_MXFP4> { using T = FmtMXFP4; };
 template <> struct FmtOf<FMT_Q5_K> { using T = FmtQ5K; };
+template <> struct FmtOf<FMT_Q2_K> { using T = FmtQ2K; };
 
 // ------------------------------------------------------- MXFP4 decode GEMV
 // A 17-byte block has no fixed alignment, so one lane per block would need five

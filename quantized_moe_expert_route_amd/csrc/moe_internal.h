@@ -9,7 +9,7 @@
 
 namespace moe {
 
-enum { FMT_Q4_K = 0, FMT_Q6_K = 1, FMT_MXFP4 = 2, FMT_Q5_K = 3 };
+enum { FMT_Q4_K = 0, FMT_Q6_K = 1, FMT_MXFP4 = 2, FMT_Q5_K = 3, FMT_Q2_K = 4 };
 
 // Unsigned division by a runtime constant d >= 1 without a divide sequence
 // (Granlund & Montgomery, "Division by invariant integers using

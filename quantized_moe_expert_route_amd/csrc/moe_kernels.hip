@@ -1389,10 +1389,12 @@ bool gemv_fits(const KArgs& a) {
   size_t g = a.fmt_gu == FMT_Q4_K ? gateup_lds<FMT_Q4_K>(a, nullptr)
            : a.fmt_gu == FMT_Q6_K ? gateup_lds<FMT_Q6_K>(a, nullptr)
            : a.fmt_gu == FMT_Q5_K ? gateup_lds<FMT_Q5_K>(a, nullptr)
+           : a.fmt_gu == FMT_Q2_K ? gateup_lds<FMT_Q2_K>(a, nullptr)
                                   : gateup_lds<FMT_MXFP4>(a, nullptr);
   size_t d = a.fmt_d == FMT_Q4_K ? down_lds<FMT_Q4_K>(a, nullptr)
            : a.fmt_d == FMT_Q6_K ? down_lds<FMT_Q6_K>(a, nullptr)
            : a.fmt_d == FMT_Q5_K ? down_lds<FMT_Q5_K>(a, nullptr)
+           : a.fmt_d == FMT_Q2_K ? down_lds<FMT_Q2_K>(a, nullptr)
                                  : down_lds<FMT_MXFP4>(a, nullptr);
   DownLdsPlan pl;
   if (down_lds_plan(a, &pl)) d = pl.lds;
@@ -1439,6 +1441,7 @@ hipError_t launch_gateup(const KArgs& a, bool routing_given, hipStream_t s, Ev e
     case FMT_Q4_K: return gateup_dispatch<FMT_Q4_K>(a, routing_given, s, ev);
     case FMT_Q6_K: return gateup_dispatch<FMT_Q6_K>(a, routing_given, s, ev);
     case FMT_Q5_K: return gateup_dispatch<FMT_Q5_K>(a, routing_given, s, ev);
+    case FMT_Q2_K: return gateup_dispatch<FMT_Q2_K>(a, routing_given, s, ev);
     default: return gateup_dispatch<FMT_MXFP4>(a, routing_given, s, ev);
   }
 }
@@ -1454,6 +1457,7 @@ hipError_t launch_down(const KArgs& a, hipStream_t s, Ev ev) {
     case FMT_Q4_K: return down_dispatch<FMT_Q4_K>(a, s, ev);
     case FMT_Q6_K: return down_dispatch<FMT_Q6_K>(a, s, ev);
     case FMT_Q5_K: return down_dispatch<FMT_Q5_K>(a, s, ev);
+    case FMT_Q2_K: return down_dispatch<FMT_Q2_K>(a, s, ev);
     default: return down_dispatch<FMT_MXFP4>(a, s, ev);
   }
 }
@@ -1469,6 +1473,9 @@ hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_
                     bs, out);
     case FMT_Q5_K:
       return launch(k_block_dots<FMT_Q5_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
+                    bs, out);
+    case FMT_Q2_K:
+      return launch(k_block_dots<FMT_Q2_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
                     bs, out);
     case FMT_Q6_K:
       return launch(k_block_dots<FMT_Q6_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,

@@ -195,8 +195,9 @@ def test_stage_names_and_path_rule():
         "router", "gateup", "hquant", "down"]
     q6 = good_desc(gen.CONFIGS["deepseek-v4-flash"])
     assert M.moe_layer_stage_count(q6, 16) == 7
-    # Q5_K layers (gate/up or down) take the GEMV path at every T
-    for fg, fd in ((gen.Q5_K, gen.Q5_K), (gen.Q4_K, gen.Q5_K), (gen.Q5_K, gen.Q6_K)):
+    # Q5_K and Q2_K layers (gate/up or down) take the GEMV path at every T
+    for fg, fd in ((gen.Q5_K, gen.Q5_K), (gen.Q4_K, gen.Q5_K), (gen.Q5_K, gen.Q6_K),
+                   (gen.Q2_K, gen.Q2_K), (gen.Q4_K, gen.Q2_K)):
         q5 = good_desc(gen.CONFIGS["deepseek-v4-flash"].with_(fmt_gu=fg, fmt_d=fd))
         assert M.moe_layer_stage_count(q5, 16) == 3
     # the grouped workspace holds the per-pair rows: it grows with T * k * H

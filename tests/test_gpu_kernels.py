@@ -87,6 +87,11 @@ def _random_blocks(fmt, n_rows, K, rng):
                                         int(rng.integers(0x0400, 0x3C00)),
                                         rng.integers(0, 64, 8), rng.integers(0, 64, 8),
                                         rng.integers(0, 32, 256)))
+            elif fmt == gen.Q2_K:
+                row.append(gen.pack_q2k(int(rng.integers(0x0400, 0x3C00)),
+                                        int(rng.integers(0x0400, 0x3C00)),
+                                        rng.integers(0, 16, 16), rng.integers(0, 16, 16),
+                                        rng.integers(0, 4, 256)))
             elif fmt == gen.Q6_K:
                 row.append(gen.pack_q6k(int(rng.integers(0x0400, 0x3C00)),
                                         rng.integers(-128, 128, 16).astype(np.int8),
@@ -99,7 +104,8 @@ def _random_blocks(fmt, n_rows, K, rng):
 
 @pytest.mark.parametrize("fmt,K", [(gen.Q4_K, 512), (gen.Q4_K, 7168), (gen.Q6_K, 768),
                                    (gen.Q6_K, 2048), (gen.MXFP4, 2880), (gen.MXFP4, 96),
-                                   (gen.Q5_K, 256), (gen.Q5_K, 2048)])
+                                   (gen.Q5_K, 256), (gen.Q5_K, 2048), (gen.Q2_K, 256),
+                                   (gen.Q2_K, 2048)])
 @pytest.mark.parametrize("kind", ["generated", "random_fields"])
 def test_block_dots_exact(fmt, K, kind):
     say(f"block_dots fmt={fmt} K={K} {kind}")

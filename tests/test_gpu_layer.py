@@ -55,6 +55,19 @@ def test_layer_q5k(name, fmt_gu, fmt_d, T):
     check_layer(cfg, x_index=T)
 
 
+@pytest.mark.parametrize("name,fmt_gu,fmt_d,T", [
+    ("qwen3.6-35b-a3b", "Q2_K", "Q2_K", 1), ("qwen3.6-35b-a3b", "Q2_K", "Q2_K", 6),
+    ("deepseek-v4-flash", "Q2_K", "Q6_K", 3), ("kimi-k2", "Q4_K", "Q2_K", 7),
+    ("qwen-full", "Q2_K", "Q5_K", 1)])
+def test_layer_q2k(name, fmt_gu, fmt_d, T):
+    """Q2_K experts through the per-pair GEMV kernels (every chunk of a Q2_K
+    layer takes them), alone and mixed with Q4_K, Q5_K and Q6_K matrices."""
+    f = {"Q4_K": gen.Q4_K, "Q5_K": gen.Q5_K, "Q6_K": gen.Q6_K, "Q2_K": gen.Q2_K}
+    base = gen.CONFIGS["qwen3.6-35b-a3b"] if name == "qwen-full" else SHRUNK[name]
+    cfg = base.with_(name=f"{base.name}-{fmt_gu}-{fmt_d}", fmt_gu=f[fmt_gu], fmt_d=f[fmt_d], T=T)
+    check_layer(cfg, x_index=T)
+
+
 def _routed_layer(cfg, T, x_index):
     """The full-size layer with only the experts the oracle routes these tokens
     to (plus the shared expert) generated; the others stay zero and unused."""
