@@ -483,6 +483,15 @@ struct FmtQ2K {
     r.sc = make_uint2(ld_nt4(blk + 8 * h), ld_nt4(blk + 8 * h + 4));
     r.dd = ld_nt4(blk + 80);
   }
+  // from a block staged in LDS at a dword-aligned address: dword reads only
+  __device__ static __forceinline__ void lds_load(Raw& r, const uint8_t* blk, int sub) {
+    const int h = sub >> 2, k = sub & 3;
+    const uint32_t* qs = reinterpret_cast<const uint32_t*>(blk + 16 + 32 * h + 8 * k);
+    const uint32_t* sc = reinterpret_cast<const uint32_t*>(blk + 8 * h);
+    r.q = make_uint2(qs[0], qs[1]);
+    r.sc = make_uint2(sc[0], sc[1]);
+    r.dd = *reinterpret_cast<const uint32_t*>(blk + 80);
+  }
   __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int sub) {
     const int h = sub >> 2, k = sub & 3;
     const int8_t* ab = a.qs + b * 256 + 128 * h + 8 * k;

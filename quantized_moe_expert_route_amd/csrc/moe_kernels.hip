@@ -825,10 +825,11 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
   }
 }
 
-// Q4_K / Q5_K down with the rows staged in LDS. grid (ceil(H / R), T), block
-// 512. Same result as k_down. Waves 0-2 copy the down rows [row0, row0 + R) of
-// every present slot straight into LDS (global->LDS loads, 16-byte pieces; a
-// row is 144 nb or 176 nb bytes, a multiple of 16) while waves 3-7 quantize h (the
+// Q4_K / Q5_K / Q2_K down with the rows staged in LDS. grid (ceil(H / R), T),
+// block 512. Same result as k_down. Waves 0-2 copy the down rows [row0, row0 +
+// R) of every present slot straight into LDS (global->LDS loads of the 16-byte
+// pieces covering each row; every block field the lanes read is dword-aligned
+// in LDS) while waves 3-7 quantize h (the
 // longer of the two paths: 3:5 measured best of 2:6, 3:5 and 4:4); then all
 // eight waves multiply out of LDS, TPG block tasks per 8-lane group.
 constexpr int kStreamers = 3, kQuantizers = 8 - kStreamers;
@@ -840,7 +841,8 @@ __global__ __launch_bounds__(512) void k_down_lds(KArgs a, int R, Div dnb, Div d
   const int t = blockIdx.y, row0 = blockIdx.x * R;
   const int K = a.F, nb = K / 256;
   const int ns = a.k + a.has_shared;
-  const int row_bytes = nb * F::BB, npc = row_bytes / 16;
+  // rows staged as whole 16-byte pieces (the last may run into the row's stride padding)
+  const int npc = (nb * F::BB + 15) / 16, pitch = 16 * npc;
   unsigned char* p_act = smem;
   float* ld = reinterpret_cast<float*>(smem + ns * K);
   int16_t* lbs = reinterpret_cast<int16_t*>(smem + ns * K + ns * 4 * (K / 32));
@@ -938,7 +940,7 @@ __global__ __launch_bounds__(512) void k_down_lds(KArgs a, int R, Div dnb, Div d
         const uint32_t q1 = dnb.div(task), sl = dR.div(q1);
         const int b = dnb.mod(task, q1), r = dR.mod(q1, sl);
         if (row0 + r < a.H && ((present >> sl) & 1u)) {
-          const uint8_t* blk = wl + static_cast<size_t>(q1) * row_bytes + b * F::BB;
+          const uint8_t* blk = wl + static_cast<size_t>(q1) * pitch + b * F::BB;
           typename F::Raw raw;
           F::lds_load(raw, blk, sub);
           const ActView av{reinterpret_cast<const int8_t*>(p_act + sl * K), ld + sl * (K / 32),
@@ -1312,13 +1314,15 @@ hipError_t down_jb(int jobs_per_wave, dim3 grid, size_t lds, hipStream_t s, Ev e
   return launch(k_down<FMT, TPG, 8, false>, grid, 512, lds, s, ev, a, R, dnb, dR, dpc);
 }
 
-// Plan of the LDS-staged down kernel (Q4_K, Q5_K): one workgroup per compute
-// unit where the LDS (q8 of h + R rows per slot) and 8 tasks per lane group allow.
+// Plan of the LDS-staged down kernel (Q4_K, Q5_K, Q2_K): one workgroup per
+// compute unit where the LDS (q8 of h + R rows per slot) and 8 tasks per lane
+// group allow.
+int down_lds_bb(int fmt) { return fmt == FMT_Q4_K ? 144 : fmt == FMT_Q5_K ? 176 : fmt == FMT_Q2_K ? 84 : 0; }
 struct DownLdsPlan { int R, tpg; size_t lds; };
 bool down_lds_plan(const KArgs& a, DownLdsPlan* out) {
-  if (a.fmt_d != FMT_Q4_K && a.fmt_d != FMT_Q5_K) return false;
+  if (down_lds_bb(a.fmt_d) == 0) return false;
   const int ns = a.k + a.has_shared, K = a.F, nb = K / 256;
-  const int npc = nb * (a.fmt_d == FMT_Q4_K ? 144 : 176) / 16;  // 16-byte pieces per row
+  const int npc = (nb * down_lds_bb(a.fmt_d) + 15) / 16;  // 16-byte pieces per row
   const int per_token = max(1, 256 / max(a.T, 1));
   int R = max(1, min((a.H + per_token - 1) / per_token, a.H));
   auto lds_of = [&](int r) {
@@ -1342,13 +1346,13 @@ hipError_t down_lds_jb(int jobs_per_wave, dim3 grid, size_t lds, hipStream_t s, 
 template <int FMT>
 hipError_t down_dispatch(const KArgs& a, hipStream_t s, Ev ev) {
   if (FMT == FMT_MXFP4 && mx_down_fits(a)) return down_mx(a, s, ev);
-  if constexpr (FMT == FMT_Q4_K || FMT == FMT_Q5_K) {
+  if constexpr (FMT == FMT_Q4_K || FMT == FMT_Q5_K || FMT == FMT_Q2_K) {
     DownLdsPlan pl;
     if (down_lds_plan(a, &pl)) {
       const int nb = a.F / 256, pieces = a.F / 256;
       const dim3 grid((a.H + pl.R - 1) / pl.R, a.T);
       const Div dnb = Div::make(nb), dR = Div::make(pl.R), dpc = Div::make(pieces),
-                dq = Div::make(nb * FmtOf<FMT>::T::BB / 16);
+                dq = Div::make((nb * FmtOf<FMT>::T::BB + 15) / 16);
       const int jpw = ((a.k + a.has_shared) * pieces + kQuantizers - 1) / kQuantizers;
       switch (tpg_bucket(pl.tpg)) {
         case 1: return down_lds_jb<FMT, 1>(jpw, grid, pl.lds, s, ev, a, pl.R, dnb, dR, dpc, dq);
