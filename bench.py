@@ -257,7 +257,10 @@ def kernel_names(cfg, path: str) -> dict:
     if path == "gemv":
         mx = gen.MXFP4
         gu = "k_gateup_mx" if cfg.fmt_gu == mx else "k_gateup"
-        dn = {gen.Q4_K: "k_down_lds", gen.Q5_K: "k_down_lds", mx: "k_down_mx"}.get(cfg.fmt_d, "k_down")
+        if cfg.fmt_d in (gen.Q4_K, gen.Q5_K, gen.Q2_K):  # rows staged through LDS
+            dn = "k_down_lds"
+        else:
+            dn = "k_down_mx" if cfg.fmt_d == mx else "k_down"
         return {"router": "k_router", "gateup": gu, "down": dn}
     nb = cfg.biases
     gu = "k_glds_q4k<0>" if cfg.fmt_gu == gen.Q4_K and not nb else "k_gu_grouped"
