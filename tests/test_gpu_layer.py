@@ -21,9 +21,12 @@ def test_layer_shrunk(name):
 
 @pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 13), ("qwen3.6-35b-a3b", 1),
                                     ("qwen3.6-35b-a3b", 4), ("gpt-oss-20b", 1),
-                                    ("gpt-oss-20b", 3)])
+                                    ("gpt-oss-20b", 3), ("gpt-oss-20b", 16)])
 def test_layer_full_decode(name, T):
-    check_layer(gen.CONFIGS[name], T=T, x_index=T)
+    """Full-size layers through the per-pair path; the gpt-oss shape also at 16
+    tokens (MXFP4 layers take it at every T: 64 gate/up pairs, 16 down rows of
+    workgroups)."""
+    check_layer(gen.CONFIGS[name], T=T, x_index=T, threads=16)
 
 
 @pytest.mark.parametrize("H,F,k,shared", [(1024, 2048, 4, False), (2048, 1024, 8, True),
