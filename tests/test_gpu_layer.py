@@ -158,8 +158,13 @@ def test_shared_gate_vector():
     check_layer(cfg, data=data, sh_gate_vec=data.sh_gate_vec)
 
 
-def test_determinism():
-    cfg = SHRUNK["deepseek-v4-flash"]
+@pytest.mark.parametrize("name", ["deepseek-v4-flash", "gpt-oss-full", "qwen-q2k"])
+def test_determinism(name):
+    """Two runs give identical bytes: the grouped path (16-token chunk), the
+    MXFP4 realigned kernels at full width, the Q2_K GEMV kernels."""
+    cfg = (gen.CONFIGS["gpt-oss-20b"] if name == "gpt-oss-full" else
+           SHRUNK["qwen3.6-35b-a3b"].with_(fmt_gu=gen.Q2_K, fmt_d=gen.Q2_K) if name == "qwen-q2k"
+           else SHRUNK[name])
     data = gen.make_layer(cfg)
     x, xb = gen.make_x(cfg, T=cfg.T)
     dl = DeviceLayer(data)
