@@ -195,7 +195,18 @@ MOE_API moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Whole layer: quantize, route, expert FFN. y fp32 [T, H] overwritten;
- * ids_out [T, k] and w_out [T, k] are optional copies of the routing. */
+ * ids_out [T, k] and w_out [T, k] are optional copies of the routing (device,
+ * int32 / fp32, or NULL). ws: workspace of at least moe_workspace_size(desc, T)
+ * bytes, 256-byte aligned, caller-owned; its contents on entry do not matter.
+ * The routing never leaves the device: the selected experts' pointers are
+ * resolved in the kernels, so the call is one enqueue with no readback.
+ * Errors: as above (MOE_EINVAL, MOE_EUNSUPPORTED when a launch shape does not
+ * fit the kernels, MOE_ENOWORKSPACE, MOE_EHIP), nothing enqueued on failure.
+ * Source: Pulsar README, MoE expert resolve (per-token router ids pick the
+ * experts whose gate/up/down pointers the launch gets; NULL = "not mine") and
+ * numerics notes (q8_K activations, integer dots); the DGX Spark article on
+ * running Kimi K3 with Pulsar (router readbacks and per-layer launches as the
+ * fixed cost of a token). */
 MOE_API moe_status moe_layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
                              float* y, int32_t* ids_out, float* w_out, void* ws,
                              size_t ws_bytes, hipStream_t stream);
@@ -214,12 +225,47 @@ MOE_API const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int 
 
 /* Test export: integer block partials of n_rows weight rows (device, K
  * columns, byte stride `stride`) against token `token` of xq, computed by the
- * same device routines the FFN kernels use. out int32 [n_rows, K / Bw, 2]:
- *   Q4_K : (S1, S2) with S1 = sum_j sc_j * dot_j, S2 = sum_j m_j * (bsums of sub-block j)
+ * same device routines the FFN kernels use (MXFP4 rows of up to 256 blocks:
+ * the realigning routine of the MXFP4 GEMV kernels; longer rows: the per-block
+ * routine). out int32 [n_rows, K / Bw, 2] (device):
+ *   Q4_K, Q5_K, Q2_K: (S1, S2) with S1 = sum_j sc_j * dot_j, S2 = sum_j m_j * (activation sums of sub-block j)
  *   Q6_K : (S, 0)   with S  = sum_s sc_s * sum_i (q_i - 32) * a_i
- *   MXFP4: (S, 0)   with S  = sum_i (2 * e2m1_i) * a_i  */
+ *   MXFP4: (S, 0)   with S  = sum_i (2 * e2m1_i) * a_i
+ * Errors: MOE_EINVAL for a bad format, pointer, width, stride or token.
+ * Source: Pulsar README, numerics notes (activations quantized to q8_0/q8_K,
+ * integer dp4a dots, rescaled per quant block). */
 MOE_API moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,
                                const moe_qact* xq, int token, int32_t* out, hipStream_t stream);
+
+/* Test export: the integer super-block sums of the multi-token path's int8
+ * MFMA tile kernels, computed by their production bodies (LDS ring, MFMA
+ * tiles) on one tile of n_tok (1..16) activation rows (tokens 0..n_tok-1 of
+ * xq, Q8_K, width K % 256 == 0) against n_rows weight rows (device, byte
+ * stride `stride`):
+ *   mode 0: Q4_K gate/up body, the rows serving as both the gate and the up
+ *           matrix, n_rows % 64 == 0: out int32 [2][n_tok][n_rows][K/256] = S1
+ *   mode 1: Q4_K down body, n_rows % 128 == 0: out [n_tok][n_rows][K/256] = S1
+ *   mode 2: Q6_K down body, n_rows % 64 == 0:  out [n_tok][n_rows][K/256] = S
+ * with S1 and S as in moe_test_block_dots. ws: device scratch of at least
+ * moe_test_tile_dots_ws(mode, n_rows, K, n_tok) bytes, 256-byte aligned.
+ * Errors: MOE_EINVAL, MOE_ENOWORKSPACE. Source: Pulsar README, prefill notes
+ * (grouped int8 tensor-core MoE that rescales per quant block). */
+MOE_API moe_status moe_test_tile_dots(int mode, const void* rows, int n_rows, int K, size_t stride,
+                              const moe_qact* xq, int n_tok, int32_t* out, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+MOE_API size_t moe_test_tile_dots_ws(int mode, int n_rows, int K, int n_tok);
+
+/* Test export: the gate (which = 0) or up (which = 1) pre-activations, bias
+ * included, that moe_expert_ffn's gate/up stage computes for the given routing
+ * (ids int32 [T, k]), by the same kernels and path (per-pair GEMV or
+ * expert-grouped MFMA tiles) with the activation replaced by the identity.
+ * out fp32 [T * k + T * (shared expert ? 1 : 0), F] (device): row t k + s for
+ * token t, slot s, then the shared expert's rows; rows of absent experts are
+ * left untouched. Other arguments and errors as moe_expert_ffn.
+ * Source: Pulsar README, numerics notes (integer dots rescaled per quant block). */
+MOE_API moe_status moe_test_preact(const moe_layer_desc* desc, const moe_qact* xq, int T,
+                           const int32_t* ids, int which, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -33,6 +33,7 @@ ABI_FUNCTIONS = (
     "moe_abi_version", "moe_status_str", "moe_workspace_size", "moe_quantize_act_q8k",
     "moe_route_topk", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_timed",
     "moe_layer_stage_count", "moe_layer_stage_name", "moe_test_block_dots",
+    "moe_test_tile_dots", "moe_test_tile_dots_ws", "moe_test_preact",
 )
 
 
@@ -93,8 +94,13 @@ def lib():
         L.moe_layer_stage_name.argtypes = [D, i32, i32]
         L.moe_layer_stage_name.restype = C.c_char_p
         L.moe_test_block_dots.argtypes = [i32, vp, i32, i32, sz, Q, i32, vp, vp]
+        L.moe_test_tile_dots.argtypes = [i32, vp, i32, i32, sz, Q, i32, vp, vp, sz, vp]
+        L.moe_test_tile_dots_ws.argtypes = [i32, i32, i32, i32]
+        L.moe_test_tile_dots_ws.restype = sz
+        L.moe_test_preact.argtypes = [D, Q, i32, vp, i32, vp, vp, sz, vp]
         for n in ("moe_quantize_act_q8k", "moe_route_topk", "moe_expert_ffn", "moe_layer_forward",
-                  "moe_layer_forward_timed", "moe_test_block_dots"):
+                  "moe_layer_forward_timed", "moe_test_block_dots", "moe_test_tile_dots",
+                  "moe_test_preact"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -181,6 +187,23 @@ def moe_test_block_dots(fmt, rows, n_rows, K, stride, xq: MoeQact, token, out, s
     _check("moe_test_block_dots",
            lib().moe_test_block_dots(fmt, _ptr(rows), n_rows, K, stride, C.byref(xq), token,
                                      _ptr(out), _stream(stream)))
+
+
+def moe_test_tile_dots(mode, rows, n_rows, K, stride, xq: MoeQact, n_tok, out, ws, ws_bytes,
+                       stream=None):
+    _check("moe_test_tile_dots",
+           lib().moe_test_tile_dots(mode, _ptr(rows), n_rows, K, stride, C.byref(xq), n_tok,
+                                    _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_test_tile_dots_ws(mode: int, n_rows: int, K: int, n_tok: int) -> int:
+    return lib().moe_test_tile_dots_ws(mode, n_rows, K, n_tok)
+
+
+def moe_test_preact(desc, xq: MoeQact, T, ids, which, out, ws, ws_bytes, stream=None):
+    _check("moe_test_preact",
+           lib().moe_test_preact(C.byref(desc), C.byref(xq), T, _ptr(ids), which, _ptr(out),
+                                 _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def qact(qs, d, bsums, fmt: int, T: int, H: int) -> MoeQact:

@@ -269,16 +269,22 @@ static moe_status expert_ffn_impl(KArgs& a, bool grouped, bool routing_given, hi
   return hip_status(e);
 }
 
+// q8 of x as the layer's gate/up rows consume it, for T tokens.
+static bool qact_ok(const moe_layer_desc* desc, const moe_qact* xq, int T) {
+  const int want_afmt = desc->fmt_gate == MOE_WFMT_MXFP4 ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K;
+  if (xq->fmt != want_afmt || xq->T < T || xq->H != desc->hidden) return false;
+  if (!xq->qs || !xq->d || !aligned(xq->qs, 16) || !aligned(xq->d, 4)) return false;
+  if (want_afmt == MOE_AFMT_Q8_K && (!xq->bsums || !aligned(xq->bsums, 4))) return false;
+  return true;
+}
+
 moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq, const void* x,
                           moe_dtype dtype, int T, const int32_t* ids, const float* w, float* y,
                           void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = validate_desc(desc);
   if (st != MOE_OK) return st;
   if (T < 0 || T > kMaxTokens || !xq || !ids || !w || !y) return MOE_EINVAL;
-  const int want_afmt = desc->fmt_gate == MOE_WFMT_MXFP4 ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K;
-  if (xq->fmt != want_afmt || xq->T < T || xq->H != desc->hidden) return MOE_EINVAL;
-  if (!xq->qs || !xq->d || !aligned(xq->qs, 16) || !aligned(xq->d, 4)) return MOE_EINVAL;
-  if (want_afmt == MOE_AFMT_Q8_K && (!xq->bsums || !aligned(xq->bsums, 4))) return MOE_EINVAL;
+  if (!qact_ok(desc, xq, T)) return MOE_EINVAL;
   if (desc->sh_gate_vec && validate_x(x, dtype) != MOE_OK) return MOE_EINVAL;
   if (!aligned(ids, 4) || !aligned(w, 4) || !aligned(y, 16)) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
@@ -385,6 +391,63 @@ moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K
       xq->d + static_cast<size_t>(token) * (K / B),
       want == MOE_AFMT_Q8_K ? xq->bsums + static_cast<size_t>(token) * (K / 16) : nullptr, out,
       stream));
+}
+
+moe_status moe_test_tile_dots(int mode, const void* rows, int n_rows, int K, size_t stride,
+                              const moe_qact* xq, int n_tok, int32_t* out, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  if (mode < 0 || mode > 2) return MOE_EINVAL;
+  const int fmt = mode == 2 ? FMT_Q6_K : FMT_Q4_K;
+  if (!rows || !aligned(rows, 16) || !out || !aligned(out, 4) || !xq) return MOE_EINVAL;
+  if (n_tok < 1 || n_tok > 16 || n_rows <= 0 || K <= 0 || K % 256 != 0) return MOE_EINVAL;
+  if (n_rows % (mode == 1 ? 128 : 64) != 0) return MOE_EINVAL;
+  const size_t rb = static_cast<size_t>(K / 256) * block_bytes(fmt);
+  if (stride < rb || stride % 16) return MOE_EINVAL;
+  if (xq->fmt != MOE_AFMT_Q8_K || xq->H != K || xq->T < n_tok) return MOE_EINVAL;
+  if (!xq->qs || !xq->d || !xq->bsums || !aligned(xq->qs, 16) || !aligned(xq->d, 4) ||
+      !aligned(xq->bsums, 16))
+    return MOE_EINVAL;
+  if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
+  if (ws_bytes < tile_dots_ws(mode, n_rows, K, n_tok)) return MOE_ENOWORKSPACE;
+  return hip_status(launch_tile_dots(mode, rows, n_rows, K, stride, xq->qs, xq->d, xq->bsums,
+                                     n_tok, out, ws, stream));
+}
+
+size_t moe_test_tile_dots_ws(int mode, int n_rows, int K, int n_tok) {
+  if (mode < 0 || mode > 2 || n_rows <= 0 || n_tok < 1 || n_tok > 16) return 0;
+  return tile_dots_ws(mode, n_rows, K, n_tok);
+}
+
+moe_status moe_test_preact(const moe_layer_desc* desc, const moe_qact* xq, int T,
+                           const int32_t* ids, int which, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st != MOE_OK) return st;
+  if (which != 0 && which != 1) return MOE_EINVAL;
+  if (T < 0 || T > kMaxTokens || !xq || !ids || !out) return MOE_EINVAL;
+  if (!qact_ok(desc, xq, T)) return MOE_EINVAL;
+  if (!aligned(ids, 4) || !aligned(out, 16)) return MOE_EINVAL;
+  if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
+  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
+  const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
+                               desc->sh_gate != nullptr, g);
+  if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
+  if (T == 0) return MOE_OK;
+  KArgs a = make_args(desc, T);
+  bind_ws(a, L, ws);
+  a.xqs = xq->qs; a.xd = xq->d; a.xbs = xq->bsums;
+  a.ids = const_cast<int32_t*>(ids);
+  a.h = out;
+  a.act = which ? ACT_PRE_UP : ACT_PRE_GATE;
+  if (!path_fits(a, g)) return MOE_EUNSUPPORTED;
+  hipError_t e;
+  if (g) {
+    e = launch_bucket(a, stream, Ev{});
+    if (e == hipSuccess) e = launch_gateup_grouped(a, stream, Ev{});
+  } else {
+    e = launch_gateup(a, true, stream, Ev{});
+  }
+  return hip_status(e);
 }
 
 }  // extern "C"

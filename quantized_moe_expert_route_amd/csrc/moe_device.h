@@ -676,12 +676,14 @@ __device__ __forceinline__ float mx_dot_regs(const uint32_t (&w)[5], uint32_t sh
   return acc;
 }
 
-// One row pair: the lane's NL pieces go to the wave's scratch, then each lane
-// sums the values of its blocks in both rows; returns the two row sums (every
-// lane), reduced in a fixed order.
-template <int NL, int NBL>
-__device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, int nb,
-                                          const MxAct<NBL>& A, int lane) {
+// One row pair: the lane's NL pieces go to the wave's scratch, then every
+// block the lane owns in either row is realigned from the scratch and dotted
+// with its activation pairs; f(row, b, i, dot, e) receives each block's exact
+// dot (sum of e2m1 value times activation quant, a multiple of 0.5) and scale
+// byte e, in a fixed order: for the lane's activation block i, row 0 then row 1.
+template <int NL, int NBL, class Fn>
+__device__ __forceinline__ void mx_pair_blocks(const uint4 (&pc)[NL], uint8_t* scr, int nb,
+                                               const MxAct<NBL>& A, int lane, Fn&& f) {
   const int npc = mx_row_pieces(nb);
 #pragma unroll
   for (int m = 0; m < NL; ++m) {
@@ -694,7 +696,6 @@ __device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, i
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float s0 = 0.0f, s1 = 0.0f;
   auto block = [&](int row, int b, int i) {
     const uint32_t o = static_cast<uint32_t>(row * 16 * npc + 17 * b);  // scale byte
     const uint32_t* wp = reinterpret_cast<const uint32_t*>(scr + ((o + 1) & ~3u));
@@ -702,30 +703,41 @@ __device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, i
 #pragma unroll
     for (int k = 0; k < 5; ++k) w[k] = wp[k];
     const int e = scr[o];
-    return A.d[i] * __builtin_ldexpf(mx_dot_regs(w, (o + 1) & 3u, A.ap[i]), e - 127);
+    f(row, b, i, mx_dot_regs(w, (o + 1) & 3u, A.ap[i]), e);
   };
   if (NBL == 2 && mx_fold(nb)) {  // wave-uniform
-    s0 = block(0, lane, 0);
-    s1 = block(1, lane, 0);
+    block(0, lane, 0);
+    block(1, lane, 0);
     const int tail = nb - 64;
     if (lane < 2 * tail) {
       const int row = lane < tail ? 0 : 1;
-      const float v = block(row, 64 + lane - row * tail, NBL - 1);
-      if (row == 0) s0 += v; else s1 += v;
+      block(row, 64 + lane - row * tail, NBL - 1);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < NBL; ++i) {
       const int b = lane + 64 * i;
       if (b < nb) {
-        s0 += block(0, b, i);
-        s1 += block(1, b, i);
+        block(0, b, i);
+        block(1, b, i);
       }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The two row sums of a row pair (every lane): block values d8 * 2^(e-127) *
+// dot summed per lane, then over the wave in a fixed order.
+template <int NL, int NBL>
+__device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, int nb,
+                                          const MxAct<NBL>& A, int lane) {
+  float s0 = 0.0f, s1 = 0.0f;
+  mx_pair_blocks<NL, NBL>(pc, scr, nb, A, lane, [&](int row, int, int i, float dot, int e) {
+    const float v = A.d[i] * __builtin_ldexpf(dot, e - 127);
+    if (row == 0) s0 += v; else s1 += v;
+  });
   return make_float2(wave_sum(s0), wave_sum(s1));
 }
 
@@ -764,6 +776,7 @@ __device__ __forceinline__ void stage_act(const int8_t* qs, const float* d, cons
 
 __device__ __forceinline__ float act_fn(int act, float alpha, float limit, float g, float u) {
   if (act == 0) return g / (1.0f + __expf(-g)) * u;
+  if (act >= ACT_PRE_GATE) return act == ACT_PRE_GATE ? g : u;  // pre-activation export
   const float gc = fminf(g, limit);
   const float uc = fminf(fmaxf(u, -limit), limit);
   return gc / (1.0f + __expf(-alpha * gc)) * (uc + 1.0f);

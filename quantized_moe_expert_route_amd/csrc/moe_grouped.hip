@@ -23,6 +23,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "../../include/moe.h"
 #include "moe_device.h"
@@ -134,13 +135,13 @@ struct WQ4K {
 #pragma unroll
     for (int c = 0; c < 4; ++c) q[c] = ld8(blk + 16 + 32 * c + 8 * g);
   }
-  // acc += dC * d * S1 (integer sub-block sums scaled by sc_j);
-  // mn += dA * bsum_j * dmin * m_j (min term, fp32 MFMA over the sub-blocks).
-  __device__ __forceinline__ void mma(const ActSB& x, int g, v4f& acc, v4f& mn) const {
-    const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;
-    const uint32_t sc03 = s0 & 0x3F3F3F3Fu, m03 = s1 & 0x3F3F3F3Fu;
+  // S[i] = S1 of C-row token 4g + i against this lane's weight row: the int32
+  // sub-block dots (two int8 MFMAs per 32-weight group: low and high nibbles)
+  // times the 6-bit scales sc_j, summed over the super-block.
+  __device__ __forceinline__ v4i sums(const ActSB& x) const {
+    const uint32_t s0 = hdr.y, s2 = hdr.w;
+    const uint32_t sc03 = s0 & 0x3F3F3F3Fu;
     const uint32_t sc47 = (s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u);
-    const uint32_t m47 = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
     v4i S = {0, 0, 0, 0};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -154,6 +155,15 @@ struct WQ4K {
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[i] = mad24(sh, chi[i], mad24(sl, clo[i], S[i]));
     }
+    return S;
+  }
+  // acc += dC * d * S1; mn += dA * bsum_j * dmin * m_j (min term, fp32 MFMA
+  // over the sub-blocks).
+  __device__ __forceinline__ void scale(const ActSB& x, int g, const v4i& S, v4f& acc,
+                                        v4f& mn) const {
+    const uint32_t s1 = hdr.z, s2 = hdr.w;
+    const uint32_t m03 = s1 & 0x3F3F3F3Fu;
+    const uint32_t m47 = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
     const float d = half_bits_to_f32(hdr.x & 0xFFFF), dmin = half_bits_to_f32(hdr.x >> 16);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -166,6 +176,9 @@ struct WQ4K {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += (x.dC[i] * d) * static_cast<float>(S[i]);
+  }
+  __device__ __forceinline__ void mma(const ActSB& x, int g, v4f& acc, v4f& mn) const {
+    scale(x, g, sums(x), acc, mn);
   }
 };
 
@@ -185,9 +198,11 @@ struct WQ6K {
     sc[1] = ld8_a2(blk + 200);
     dbits = *gp<uint16_t>(blk + 208);
   }
-  // Group m = 4h + qq covers sub-blocks 2m (lane groups 0, 1) and 2m + 1
-  // (groups 2, 3): two MFMAs, each with the other half of B zeroed.
-  __device__ __forceinline__ void mma(const ActSB& x, int g, v4f& acc, v4f&) const {
+  // S[i] = sum over the 16-weight sub-blocks s of sc_s * (int8 dot of q - 32
+  // with C-row token 4g + i). Group m = 4h + qq covers sub-blocks 2m (lane
+  // groups 0, 1) and 2m + 1 (groups 2, 3): two MFMAs, each with the other half
+  // of B zeroed.
+  __device__ __forceinline__ v4i sums(const ActSB& x, int g) const {
     v4i S = {0, 0, 0, 0};
     const bool first = g < 2;
 #pragma unroll
@@ -215,9 +230,15 @@ struct WQ6K {
         for (int i = 0; i < 4; ++i) S[i] = mad24(sb, cb[i], mad24(sa, ca[i], S[i]));
       }
     }
+    return S;
+  }
+  __device__ __forceinline__ void scale(const ActSB& x, const v4i& S, v4f& acc) const {
     const float d = half_bits_to_f32(dbits);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += (x.dC[i] * d) * static_cast<float>(S[i]);
+  }
+  __device__ __forceinline__ void mma(const ActSB& x, int g, v4f& acc, v4f&) const {
+    scale(x, sums(x, g), acc);
   }
 };
 
@@ -269,6 +290,18 @@ __device__ __forceinline__ void stream_rows(const uint8_t* const (&wrow)[NM], co
   }
 }
 
+// Test export of a tile kernel's integer super-block sums: dump[((m T + ts) n_rows
+// + row) nb + b] = S of token slot ts (= 4 g + i) against weight row `row` of
+// matrix m, super-block b.
+__device__ __forceinline__ void dump_sums(int32_t* dump, int m, int T, int n_rows, int nb,
+                                          int row, int b, int g, int cnt, const v4i& S) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ts = 4 * g + i;
+    if (ts < cnt) dump[((static_cast<size_t>(m) * T + ts) * n_rows + row) * nb + b] = S[i];
+  }
+}
+
 // ------------------------------------------------ LDS-staged Q4_K tile stream
 // One work item streams the Q4_K rows of a few consecutive row blocks of one
 // tile through a 3-slot LDS ring filled by direct global->LDS loads
@@ -286,7 +319,8 @@ constexpr int kStBytes = kStD + 256;     // 23808 B per slot
 // row block). grid 8 * ceil(max items / 8), block 256 (4 waves, 2 per SIMD).
 // Item = (tile, ii): row blocks [ii RBG, min(RB, (ii + 1) RBG)). Layers without
 // expert biases only (those take the register-staged kernels).
-template <int MODE>
+// DUMP: also write the integer super-block sums to a.dump (test export).
+template <int MODE, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG, int RB) {
   // three separate arrays: with the slot known at each access the compiler can
   // tell a slot being filled from the slot being read (no forced vmcnt(0))
@@ -437,7 +471,14 @@ __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG,
       w.hdr = *reinterpret_cast<const uint4*>(blk);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) w.q[cc] = *reinterpret_cast<const uint2*>(blk + 16 + 32 * cc + 8 * g);
-      w.mma(x, g, acc[j], mn[j]);
+      if constexpr (DUMP) {
+        const v4i S = w.sums(x);
+        dump_sums(a.dump, MODE == 0 ? j : 0, a.T, MODE == 0 ? a.F : a.H, nb,
+                  MODE == 0 ? row_of(0, rb) : row_of(j, rb), b, g, cnt, S);
+        w.scale(x, g, S, acc[j], mn[j]);
+      } else {
+        w.mma(x, g, acc[j], mn[j]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     if (b == nb - 1) {  // row block done
@@ -497,6 +538,7 @@ __device__ __forceinline__ uint2 lds8_a2(const uint8_t* L, int off) {
 // Down rows of Q6_K experts: item = (tile, ii), row blocks of 64 rows of H,
 // wave w takes rows 16 w .. 16 w + 15 of a block. Same ring protocol as
 // k_glds_q4k, 5 slot loads per wave and stage. Layers without down biases.
+template <bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int RBG, int RB) {
   __shared__ __align__(16) uint8_t lds0[kS6Bytes];
   __shared__ __align__(16) uint8_t lds1[kS6Bytes];
@@ -595,7 +637,13 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
     w.sc[0] = lds8_a2(L, blk + 192);
     w.sc[1] = lds8_a2(L, blk + 200);
     w.dbits = *reinterpret_cast<const uint16_t*>(L + blk + 208);
-    w.mma(x, g, acc, mn);
+    if constexpr (DUMP) {
+      const v4i S = w.sums(x, g);
+      dump_sums(a.dump, 0, a.T, a.H, nb, rb * 64 + wave * 16 + c, b, g, cnt, S);
+      w.scale(x, S, acc);
+    } else {
+      w.mma(x, g, acc, mn);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (b == nb - 1) {
       const int row = rb * 64 + wave * 16 + c;
@@ -1085,6 +1133,27 @@ __global__ __launch_bounds__(256) void k_combine(KArgs a) {
 
 int grouped_grid(int n_items_max) { return 8 * ((n_items_max + 7) / 8); }
 
+// One token tile for the tile-dots export: one tile of n_tok pairs (pair i =
+// token i) over the given rows as gate, up and down of expert 0, weight 1.
+__global__ void k_tile_setup(KArgs a, const uint8_t* rows, int n_tok) {
+  const int i = threadIdx.x;
+  if (i == 0) {
+    a.counters[0] = 1;
+    GTile tl;
+    tl.e = 0;
+    tl.start = 0;
+    tl.cnt = n_tok;
+    tl.pad = 0;
+    tl.gate = tl.up = tl.down = rows;
+    tl.b_gate = tl.b_up = tl.b_down = nullptr;
+    a.tiles[0] = tl;
+  }
+  if (i < n_tok) {
+    a.plist[i] = make_int2(i, i);
+    a.w[i] = 1.0f;
+  }
+}
+
 // Row blocks per LDS-staged work item: long enough streams to amortize the
 // ring fill, while keeping about 9216 items (18 rounds of two workgroups per
 // compute unit: a short tail) at the bound on tiles.
@@ -1155,7 +1224,7 @@ hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s, Ev ev) {
   const int mt = max_tiles(a.T, a.k, a.E, a.has_shared);
   if (a.fmt_gu == FMT_Q4_K && a.b_gate == nullptr) {
     const int RB = a.F / 64, RBG = glds_group(RB, mt), IPT = (RB + RBG - 1) / RBG;
-    return launch(k_glds_q4k<0>, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a, Div::make(IPT),
+    return launch(k_glds_q4k<0, false>, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a, Div::make(IPT),
                   RBG, RB);
   }
   if (a.fmt_gu == FMT_Q4_K) {
@@ -1180,7 +1249,7 @@ hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev) {
   const int mt = max_tiles(a.T, a.k, a.E, a.has_shared);
   if (a.fmt_d == FMT_Q4_K && a.b_down == nullptr) {
     const int RB = a.H / 128, RBG = glds_group(RB, mt), IPT = (RB + RBG - 1) / RBG;
-    return launch(k_glds_q4k<1>, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a, Div::make(IPT),
+    return launch(k_glds_q4k<1, false>, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a, Div::make(IPT),
                   RBG, RB);
   }
   if (a.fmt_d == FMT_Q4_K) {
@@ -1191,7 +1260,7 @@ hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev) {
   }
   if (a.b_down == nullptr) {
     const int RB = a.H / 64, RBG = glds_group(RB, mt), IPT = (RB + RBG - 1) / RBG;
-    return launch(k_glds_q6k_down, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a,
+    return launch(k_glds_q6k_down<false>, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a,
                   Div::make(IPT), RBG, RB);
   }
   constexpr int NT = down_tiles<FMT_Q6_K>();
@@ -1202,6 +1271,52 @@ hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev) {
 
 hipError_t launch_combine(const KArgs& a, hipStream_t s, Ev ev) {
   return launch(k_combine, dim3((a.H + 1023) / 1024, a.T), 256, 0, s, ev, a);
+}
+
+// Scratch of the tile-dots export: tile count, tile, pair list, weights (one
+// 256-byte region each), then the kernel's h (mode 0) or per-pair rows.
+size_t tile_dots_ws(int, int n_rows, int, int n_tok) {
+  return 1024 + 4 * static_cast<size_t>(n_tok) * n_rows;
+}
+
+hipError_t launch_tile_dots(int mode, const void* rows, int n_rows, int K, size_t stride,
+                            const int8_t* qs, const float* d, const int16_t* bs, int n_tok,
+                            int32_t* out, void* ws, hipStream_t s) {
+  KArgs a;
+  memset(&a, 0, sizeof a);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  a.T = n_tok;
+  a.k = 1;
+  a.E = 1;
+  a.counters = reinterpret_cast<uint32_t*>(w8);
+  a.tiles = reinterpret_cast<GTile*>(w8 + 256);
+  a.plist = reinterpret_cast<int2*>(w8 + 512);
+  a.w = reinterpret_cast<float*>(w8 + 768);
+  a.h = a.part = reinterpret_cast<float*>(w8 + 1024);
+  a.xqs = a.hqs = const_cast<int8_t*>(qs);
+  a.xd = a.hd = const_cast<float*>(d);
+  a.xbs = a.hbs = const_cast<int16_t*>(bs);
+  a.dump = out;
+  if (mode == 0) {
+    a.H = K;
+    a.F = n_rows;
+    a.stride_gate = a.stride_up = stride;
+  } else {
+    a.F = K;
+    a.H = n_rows;
+    a.stride_down = stride;
+  }
+  hipError_t e = launch(k_tile_setup, dim3(1), 64, 0, s, Ev{}, a,
+                        static_cast<const uint8_t*>(rows), n_tok);
+  if (e != hipSuccess) return e;
+  // two row blocks per work item where there are two, as the production
+  // grouping uses on long expert matrices (the ring then runs across them)
+  const int RB = mode == 0 ? n_rows / 64 : mode == 1 ? n_rows / 128 : n_rows / 64;
+  const int RBG = RB >= 2 ? 2 : 1, IPT = (RB + RBG - 1) / RBG;
+  const dim3 grid(grouped_grid(IPT));
+  if (mode == 0) return launch(k_glds_q4k<0, true>, grid, 256, 0, s, Ev{}, a, Div::make(IPT), RBG, RB);
+  if (mode == 1) return launch(k_glds_q4k<1, true>, grid, 256, 0, s, Ev{}, a, Div::make(IPT), RBG, RB);
+  return launch(k_glds_q6k_down<true>, grid, 256, 0, s, Ev{}, a, Div::make(IPT), RBG, RB);
 }
 
 }  // namespace moe

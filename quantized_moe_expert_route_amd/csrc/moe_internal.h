@@ -11,6 +11,10 @@ namespace moe {
 
 enum { FMT_Q4_K = 0, FMT_Q6_K = 1, FMT_MXFP4 = 2, FMT_Q5_K = 3, FMT_Q2_K = 4 };
 
+// Activation codes beyond moe_act, used only by the test export of the gate/up
+// pre-activations: the gate/up kernels then store g (or u) where h would go.
+enum { ACT_PRE_GATE = 100, ACT_PRE_UP = 101 };
+
 // Unsigned division by a runtime constant d >= 1 without a divide sequence
 // (Granlund & Montgomery, "Division by invariant integers using
 // multiplication", PLDI 1994): q = (umulhi(n, m) + n) >> s with
@@ -99,6 +103,8 @@ struct KArgs {
   float* hd;           // [P, F / 256] (grouped); [P, F / 32] (GEMV path, MXFP4 down)
   int16_t* hbs;        // [P, F / 16]
   float* part;         // [P, H] routing-weighted expert outputs per pair
+  // test export of the tile kernels' integer super-block sums (nullptr otherwise)
+  int32_t* dump;
 };
 
 // Workspace layout (byte offsets from the base, each 256-aligned).
@@ -157,5 +163,12 @@ hipError_t launch_combine(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_t stride,
                              const int8_t* qs, const float* d, const int16_t* bs,
                              int32_t* out, hipStream_t s);
+// Test export: one token tile (n_tok <= 16 activation rows) through the grouped
+// path's LDS-ring tile kernel of `mode` (0: Q4_K gate/up body, 1: Q4_K down
+// body, 2: Q6_K down body), dumping the int32 super-block sums. ws >= tile_dots_ws().
+size_t tile_dots_ws(int mode, int n_rows, int K, int n_tok);
+hipError_t launch_tile_dots(int mode, const void* rows, int n_rows, int K, size_t stride,
+                            const int8_t* qs, const float* d, const int16_t* bs, int n_tok,
+                            int32_t* out, void* ws, hipStream_t s);
 
 }  // namespace moe

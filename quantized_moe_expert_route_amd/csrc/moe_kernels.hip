@@ -1137,6 +1137,44 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* rows, int K, 
   }
 }
 
+// MXFP4 block partials through the routine the MXFP4 GEMV kernels run
+// (k_gateup_mx, k_down_mx): row pairs read as coalesced 16-byte pieces,
+// realigned through the wave's scratch by mx_pair_blocks and dotted against
+// fp16 activation pairs in registers; S = 2 * dot (exact). grid ceil(n_rows /
+// 2), block 64 (one wave per row pair). LDS as k_gateup_mx: activation pairs
+// [nb][kApPitch], scales [nb], then the scratch.
+template <int NL, int NBL>
+__global__ __launch_bounds__(64) void k_block_dots_mx(const uint8_t* rows, int n_rows, int K,
+                                                      size_t stride, const int8_t* qs,
+                                                      const float* d, int32_t* out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nb = K / 32, npc = mx_row_pieces(nb), lane = threadIdx.x;
+  half2_t* lap = reinterpret_cast<half2_t*>(smem);
+  float* ld = reinterpret_cast<float*>(smem + 80 * nb);
+  uint8_t* scr = smem + mx_gu_scratch_offset(nb);
+  stage_act<true>(qs, d, nullptr, K, nullptr, ld, nullptr, lap);
+  __syncthreads();
+  const int r0 = 2 * blockIdx.x;
+  uint4 pcs[NL];
+#pragma unroll
+  for (int m = 0; m < NL; ++m) {
+    const int j = lane + 64 * m;
+    const int hi = j >= npc ? 1 : 0;
+    const int r = r0 + hi;
+    const bool ok = j < 2 * npc && r < n_rows;
+    pcs[m] = ld_nt16(ok ? rows + static_cast<size_t>(r) * stride + 16 * (j - hi * npc) : rows);
+  }
+  MxAct<NBL> A;
+  mx_act_load(A, lap, ld, nb, lane);
+  mx_pair_blocks<NL, NBL>(pcs, scr, nb, A, lane, [&](int row, int b, int, float dot, int) {
+    const int r = r0 + row;
+    if (r < n_rows) {
+      out[(static_cast<size_t>(r) * nb + b) * 2] = static_cast<int>(2.0f * dot);
+      out[(static_cast<size_t>(r) * nb + b) * 2 + 1] = 0;
+    }
+  });
+}
+
 // Rows per workgroup and tasks per lane group for a GEMV launch: at least
 // min_wgs workgroups while keeping every lane group busy.
 struct GemvShape { int R, tpg; };
@@ -1390,21 +1428,33 @@ bool gemv_hquant(int fmt_down, int F, int k, int has_shared) {
 }
 
 bool gemv_fits(const KArgs& a) {
-  size_t g = a.fmt_gu == FMT_Q4_K ? gateup_lds<FMT_Q4_K>(a, nullptr)
-           : a.fmt_gu == FMT_Q6_K ? gateup_lds<FMT_Q6_K>(a, nullptr)
-           : a.fmt_gu == FMT_Q5_K ? gateup_lds<FMT_Q5_K>(a, nullptr)
-           : a.fmt_gu == FMT_Q2_K ? gateup_lds<FMT_Q2_K>(a, nullptr)
-                                  : gateup_lds<FMT_MXFP4>(a, nullptr);
-  size_t d = a.fmt_d == FMT_Q4_K ? down_lds<FMT_Q4_K>(a, nullptr)
-           : a.fmt_d == FMT_Q6_K ? down_lds<FMT_Q6_K>(a, nullptr)
-           : a.fmt_d == FMT_Q5_K ? down_lds<FMT_Q5_K>(a, nullptr)
-           : a.fmt_d == FMT_Q2_K ? down_lds<FMT_Q2_K>(a, nullptr)
-                                 : down_lds<FMT_MXFP4>(a, nullptr);
+  GemvShape gs{1, 1}, ds{1, 1};
+  size_t g = a.fmt_gu == FMT_Q4_K ? gateup_lds<FMT_Q4_K>(a, &gs)
+           : a.fmt_gu == FMT_Q6_K ? gateup_lds<FMT_Q6_K>(a, &gs)
+           : a.fmt_gu == FMT_Q5_K ? gateup_lds<FMT_Q5_K>(a, &gs)
+           : a.fmt_gu == FMT_Q2_K ? gateup_lds<FMT_Q2_K>(a, &gs)
+                                  : gateup_lds<FMT_MXFP4>(a, &gs);
+  size_t d = a.fmt_d == FMT_Q4_K ? down_lds<FMT_Q4_K>(a, &ds)
+           : a.fmt_d == FMT_Q6_K ? down_lds<FMT_Q6_K>(a, &ds)
+           : a.fmt_d == FMT_Q5_K ? down_lds<FMT_Q5_K>(a, &ds)
+           : a.fmt_d == FMT_Q2_K ? down_lds<FMT_Q2_K>(a, &ds)
+                                 : down_lds<FMT_MXFP4>(a, &ds);
   DownLdsPlan pl;
-  if (down_lds_plan(a, &pl)) d = pl.lds;
-  if (mx_gateup_fits(a)) g = 0;
-  if (mx_down_fits(a)) d = 0;
-  return g <= kMaxLds && d <= kMaxLds;
+  if (down_lds_plan(a, &pl)) {
+    d = pl.lds;
+    ds.tpg = pl.tpg;
+  }
+  if (mx_gateup_fits(a)) {
+    g = 0;
+    gs.tpg = 1;
+  }
+  if (mx_down_fits(a)) {
+    d = 0;
+    ds.tpg = 1;
+  }
+  // the GEMV kernels are instantiated for at most 8 block tasks per lane
+  // group (tpg_bucket): wider rows would leave blocks uncomputed
+  return g <= kMaxLds && d <= kMaxLds && gs.tpg <= 8 && ds.tpg <= 8;
 }
 
 hipError_t launch_quant(const void* x, int dtype, int T, int H, int B, int8_t* qs, float* d,
@@ -1466,11 +1516,33 @@ hipError_t launch_down(const KArgs& a, hipStream_t s, Ev ev) {
   }
 }
 
+template <int NL, int NBL>
+hipError_t block_dots_mx_launch(const uint8_t* r, int n_rows, int K, size_t stride,
+                                const int8_t* qs, const float* d, int32_t* out, hipStream_t s) {
+  const int nb = K / 32;
+  const size_t lds = static_cast<size_t>(mx_gu_scratch_offset(nb)) + mx_scratch_bytes(nb);
+  return launch(k_block_dots_mx<NL, NBL>, dim3((n_rows + 1) / 2), 64, lds, s, Ev{}, r, n_rows, K,
+                stride, qs, d, out);
+}
+
 hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_t stride,
                              const int8_t* qs, const float* d, const int16_t* bs, int32_t* out,
                              hipStream_t s) {
   const uint8_t* r = static_cast<const uint8_t*>(rows);
   const size_t lds = (fmt == FMT_MXFP4 ? 5 * K / 2 : K) + 4 * (K / 32) + 2 * (K / 16);
+  MxPlan pl;
+  if (fmt == FMT_MXFP4 && mx_plan(K, &pl)) {
+    // rows the realigning MXFP4 kernels take (the same plans as k_gateup_mx)
+    switch (pl.nl) {
+      case 1: return block_dots_mx_launch<1, 1>(r, n_rows, K, stride, qs, d, out, s);
+      case 2: return block_dots_mx_launch<2, 1>(r, n_rows, K, stride, qs, d, out, s);
+      case 3:
+        if (pl.nbl == 1) return block_dots_mx_launch<3, 1>(r, n_rows, K, stride, qs, d, out, s);
+        return block_dots_mx_launch<3, 2>(r, n_rows, K, stride, qs, d, out, s);
+      case 5: return block_dots_mx_launch<5, 2>(r, n_rows, K, stride, qs, d, out, s);
+      default: return block_dots_mx_launch<9, 4>(r, n_rows, K, stride, qs, d, out, s);
+    }
+  }
   switch (fmt) {
     case FMT_Q4_K:
       return launch(k_block_dots<FMT_Q4_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
@@ -1484,7 +1556,7 @@ hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_
     case FMT_Q6_K:
       return launch(k_block_dots<FMT_Q6_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
                     bs, out);
-    default:
+    default:  // MXFP4 rows past the realigning kernels' plans: the per-block routine
       return launch(k_block_dots<FMT_MXFP4>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs,
                     d, bs, out);
   }

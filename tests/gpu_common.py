@@ -56,3 +56,62 @@ def check_layer(cfg, data=None, T=None, x_index=0, tokens=None, present=None, to
     say(f"  max rel err {err.max():.3e} over {len(tokens)} tokens")
     assert err.max() <= tol, err
     return y, ids, w, ref
+
+
+def x_cases(T, H, seed):
+    x = gen.normal(seed, gen.T_X, 77, T, H, 1.0)
+    if T > 1:
+        x[1] = 0.0                       # all-zero row
+    if T > 2:
+        x[2, :32] = 0.0                  # a zero block
+        x[2, 40] = 1e4                   # a spike
+    if T > 3:
+        x[3] *= 1e-6
+    return x
+
+
+def upload_q8(x_rows, B):
+    T, K = x_rows.shape
+    qs = np.zeros((T, K), np.int8)
+    d = np.zeros((T, K // B), np.float32)
+    bs = np.zeros((T, K // 16), np.int16)
+    for t in range(T):
+        a, b, c = oracle.quantize_q8(x_rows[t], B)
+        qs[t], d[t] = a, b
+        if c is not None:
+            bs[t] = c
+    tq, td, tb = (torch.from_numpy(v).cuda() for v in (qs, d, bs))
+    afmt = M.MOE_AFMT_Q8_K if B == 256 else M.MOE_AFMT_Q8_32
+    return (qs, d, bs), M.qact(tq, td, tb if B == 256 else None, afmt, T, K), (tq, td, tb)
+
+
+def random_blocks(fmt, n_rows, K, rng):
+    """Blocks with arbitrary field values (negative Q6_K scales, every MXFP4 code)."""
+    nb = K // gen.BLOCK_ELEMS[fmt]
+    rows = []
+    for r in range(n_rows):
+        row = []
+        for b in range(nb):
+            if fmt == gen.Q4_K:
+                row.append(gen.pack_q4k(int(rng.integers(0x0400, 0x3C00)),
+                                        int(rng.integers(0x0400, 0x3C00)),
+                                        rng.integers(0, 64, 8), rng.integers(0, 64, 8),
+                                        rng.integers(0, 16, 256)))
+            elif fmt == gen.Q5_K:
+                row.append(gen.pack_q5k(int(rng.integers(0x0400, 0x3C00)),
+                                        int(rng.integers(0x0400, 0x3C00)),
+                                        rng.integers(0, 64, 8), rng.integers(0, 64, 8),
+                                        rng.integers(0, 32, 256)))
+            elif fmt == gen.Q2_K:
+                row.append(gen.pack_q2k(int(rng.integers(0x0400, 0x3C00)),
+                                        int(rng.integers(0x0400, 0x3C00)),
+                                        rng.integers(0, 16, 16), rng.integers(0, 16, 16),
+                                        rng.integers(0, 4, 256)))
+            elif fmt == gen.Q6_K:
+                row.append(gen.pack_q6k(int(rng.integers(0x0400, 0x3C00)),
+                                        rng.integers(-128, 128, 16).astype(np.int8),
+                                        rng.integers(0, 64, 256)))
+            else:
+                row.append(gen.pack_mxfp4(int(rng.integers(100, 150)), rng.integers(0, 16, 32)))
+        rows.append(np.concatenate(row))
+    return np.stack(rows)

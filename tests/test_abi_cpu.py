@@ -202,3 +202,65 @@ def test_stage_names_and_path_rule():
         assert M.moe_layer_stage_count(q5, 16) == 3
     # the grouped workspace holds the per-pair rows: it grows with T * k * H
     assert M.moe_workspace_size(d, 5) > M.moe_workspace_size(d, 4) + 5 * 9 * 2048 * 4
+
+
+def test_tile_dots_validation():
+    q = M.qact(FAKE, FAKE, FAKE, M.MOE_AFMT_Q8_K, 16, 2048)
+    assert M.moe_test_tile_dots_ws(0, 128, 2048, 16) >= 1024 + 4 * 16 * 128
+    assert M.moe_test_tile_dots_ws(3, 128, 2048, 16) == 0
+    assert M.moe_test_tile_dots_ws(0, 128, 2048, 17) == 0
+    ws = M.moe_test_tile_dots_ws(1, 256, 2048, 16)
+    bad = [
+        (3, FAKE, 128, 2048, 1152, q, 16),        # unknown mode
+        (0, FAKE, 100, 2048, 1152, q, 16),        # gate/up rows not a multiple of 64
+        (1, FAKE, 192, 2048, 1152, q, 16),        # down rows not a multiple of 128
+        (0, FAKE, 128, 2048, 1152, q, 17),        # more than 16 tokens
+        (0, FAKE, 128, 2048, 1152, q, 0),
+        (0, FAKE, 128, 2000, 1152, q, 16),        # width not a multiple of 256
+        (0, FAKE, 128, 2048, 1140, q, 16),        # stride below the row bytes
+        (2, FAKE, 128, 2048, 1672, q, 16),        # Q6_K stride not a multiple of 16
+        (0, FAKE + 8, 128, 2048, 1152, q, 16),    # misaligned rows
+        (0, FAKE, 128, 1024, 576, q, 16),         # activations of another width
+    ]
+    for a in bad:
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_test_tile_dots(*a, FAKE, FAKE, ws, stream=0)
+        assert ei.value.status == M.MOE_EINVAL, a
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_test_tile_dots(1, FAKE, 256, 2048, 1152, q, 16, FAKE, FAKE, ws - 1, stream=0)
+    assert ei.value.status == M.MOE_ENOWORKSPACE
+
+
+def test_preact_validation():
+    d = good_desc()
+    ws = M.moe_workspace_size(d, 4)
+    q = M.qact(FAKE, FAKE, FAKE, M.MOE_AFMT_Q8_K, 4, 2048)
+    for which, xq, ids in ((2, q, FAKE), (0, M.qact(FAKE, FAKE, FAKE, M.MOE_AFMT_Q8_32, 4, 2048),
+                                          FAKE), (0, q, 0)):
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_test_preact(d, xq, 4, ids, which, FAKE, FAKE, ws, stream=0)
+        assert ei.value.status == M.MOE_EINVAL
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_test_preact(d, q, 4, FAKE, 0, FAKE, FAKE, ws - 1, stream=0)
+    assert ei.value.status == M.MOE_ENOWORKSPACE
+
+
+def test_gemv_plan_rejects_rows_past_the_task_cap():
+    """The per-pair GEMV kernels take at most 8 block tasks per 8-lane group: a
+    Q4_K gate/up row of 129 super-blocks (H = 33024) would need more, so the
+    layer call refuses it on the host (nothing is launched) instead of leaving
+    blocks uncomputed."""
+    cfg = gen.CONFIGS["tiny"].with_(H=33024, F=256, E=8, k=2)
+    d = good_desc(cfg)
+    ws = M.moe_workspace_size(d, 1)
+    assert ws > 0
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_layer_forward(d, FAKE, 0, 1, FAKE, None, None, FAKE, ws, stream=0)
+    assert ei.value.status == M.MOE_EUNSUPPORTED
+    # and the down projection of a 129-super-block F row as well
+    cfg = gen.CONFIGS["tiny"].with_(H=512, F=33024, E=8, k=2, fmt_d=gen.Q6_K)
+    d = good_desc(cfg)
+    ws = M.moe_workspace_size(d, 1)
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_layer_forward(d, FAKE, 0, 1, FAKE, None, None, FAKE, ws, stream=0)
+    assert ei.value.status == M.MOE_EUNSUPPORTED

@@ -8,21 +8,9 @@ import gen
 import oracle
 import quantized_moe_expert_route_amd as M
 from gen.device import DeviceLayer, x_to_device
-from tests.gpu_common import say
+from tests.gpu_common import random_blocks, upload_q8, x_cases, say
 
 pytestmark = pytest.mark.gpu
-
-
-def _x_cases(T, H, seed):
-    x = gen.normal(seed, gen.T_X, 77, T, H, 1.0)
-    if T > 1:
-        x[1] = 0.0                       # all-zero row
-    if T > 2:
-        x[2, :32] = 0.0                  # a zero block
-        x[2, 40] = 1e4                   # a spike
-    if T > 3:
-        x[3] *= 1e-6
-    return x
 
 
 @pytest.mark.parametrize("afmt,B", [(M.MOE_AFMT_Q8_K, 256), (M.MOE_AFMT_Q8_32, 32)])
@@ -32,7 +20,7 @@ def test_quantize_bitexact(afmt, B, T, H, bf16):
     if H % B:
         pytest.skip("width not a multiple of the block")
     say(f"quant afmt={afmt} T={T} H={H} bf16={bf16}")
-    x = _x_cases(T, H, 3)
+    x = x_cases(T, H, 3)
     if bf16:
         xb = gen.round_bf16(x)
         x = gen.bf16_to_f32(xb)
@@ -55,55 +43,14 @@ def test_quantize_bitexact(afmt, B, T, H, bf16):
             assert np.array_equal(bs[t].cpu().numpy(), rb), t
 
 
-def _upload_q8(x_rows, B):
-    T, K = x_rows.shape
-    qs = np.zeros((T, K), np.int8)
-    d = np.zeros((T, K // B), np.float32)
-    bs = np.zeros((T, K // 16), np.int16)
-    for t in range(T):
-        a, b, c = oracle.quantize_q8(x_rows[t], B)
-        qs[t], d[t] = a, b
-        if c is not None:
-            bs[t] = c
-    tq, td, tb = (torch.from_numpy(v).cuda() for v in (qs, d, bs))
-    afmt = M.MOE_AFMT_Q8_K if B == 256 else M.MOE_AFMT_Q8_32
-    return (qs, d, bs), M.qact(tq, td, tb if B == 256 else None, afmt, T, K), (tq, td, tb)
-
-
-def _random_blocks(fmt, n_rows, K, rng):
-    """Blocks with arbitrary field values (negative Q6_K scales, every MXFP4 code)."""
-    nb = K // gen.BLOCK_ELEMS[fmt]
-    rows = []
-    for r in range(n_rows):
-        row = []
-        for b in range(nb):
-            if fmt == gen.Q4_K:
-                row.append(gen.pack_q4k(int(rng.integers(0x0400, 0x3C00)),
-                                        int(rng.integers(0x0400, 0x3C00)),
-                                        rng.integers(0, 64, 8), rng.integers(0, 64, 8),
-                                        rng.integers(0, 16, 256)))
-            elif fmt == gen.Q5_K:
-                row.append(gen.pack_q5k(int(rng.integers(0x0400, 0x3C00)),
-                                        int(rng.integers(0x0400, 0x3C00)),
-                                        rng.integers(0, 64, 8), rng.integers(0, 64, 8),
-                                        rng.integers(0, 32, 256)))
-            elif fmt == gen.Q2_K:
-                row.append(gen.pack_q2k(int(rng.integers(0x0400, 0x3C00)),
-                                        int(rng.integers(0x0400, 0x3C00)),
-                                        rng.integers(0, 16, 16), rng.integers(0, 16, 16),
-                                        rng.integers(0, 4, 256)))
-            elif fmt == gen.Q6_K:
-                row.append(gen.pack_q6k(int(rng.integers(0x0400, 0x3C00)),
-                                        rng.integers(-128, 128, 16).astype(np.int8),
-                                        rng.integers(0, 64, 256)))
-            else:
-                row.append(gen.pack_mxfp4(int(rng.integers(100, 150)), rng.integers(0, 16, 32)))
-        rows.append(np.concatenate(row))
-    return np.stack(rows)
-
-
+# MXFP4 widths cover every plan of the realigning routine (pieces per lane and
+# blocks per lane: 96 -> 1/1, 1024 -> 2/1, 2048 -> 3/1, 2880 -> 3/2 with the
+# tail blocks folded onto spare lanes, 4096 -> 5/2, 8192 -> 9/4) and a width
+# past them (8224: the per-block routine).
 @pytest.mark.parametrize("fmt,K", [(gen.Q4_K, 512), (gen.Q4_K, 7168), (gen.Q6_K, 768),
                                    (gen.Q6_K, 2048), (gen.MXFP4, 2880), (gen.MXFP4, 96),
+                                   (gen.MXFP4, 1024), (gen.MXFP4, 2048), (gen.MXFP4, 4096),
+                                   (gen.MXFP4, 8192), (gen.MXFP4, 8224),
                                    (gen.Q5_K, 256), (gen.Q5_K, 2048), (gen.Q2_K, 256),
                                    (gen.Q2_K, 2048)])
 @pytest.mark.parametrize("kind", ["generated", "random_fields"])
@@ -117,12 +64,12 @@ def test_block_dots_exact(fmt, K, kind):
         w[0] = 0
         mat = gen.encode_matrix(fmt, w)
     else:
-        raw = _random_blocks(fmt, n_rows, K, rng)
+        raw = random_blocks(fmt, n_rows, K, rng)
         stride = gen.row_stride(fmt, K)
         mat = np.zeros((n_rows, stride), np.uint8)
         mat[:, :raw.shape[1]] = raw
-    x = _x_cases(3, K, 9)
-    host, q, keep = _upload_q8(x, B)
+    x = x_cases(3, K, 9)
+    host, q, keep = upload_q8(x, B)
     rows = torch.from_numpy(mat).cuda()
     nb = K // gen.BLOCK_ELEMS[fmt]
     for token in range(3):

@@ -62,6 +62,85 @@ def test_q4k_hand_packed_fields(orc, genlib):
         assert np.array_equal(orc.dequant_row(oracle.Q4_K, blk, 256), want)
 
 
+def test_q4k_byte_layout(orc):
+    """A Q4_K block written byte by byte from the layout (no packer): d fp16 at
+    byte 0, dmin at 2, twelve scale bytes at 4, nibbles at 16. Scale bytes 0..3
+    hold sc_0..3 in bits 0..5 and bits 4..5 of sc_4..7 in bits 6..7; bytes 4..7
+    the same for m; bytes 8..11 bits 0..3 of sc_4..7 (low nibble) and of m_4..7
+    (high nibble). Chunk c = bytes 16 + 32c ..: byte i low nibble = weight
+    64c + i, high nibble = weight 64c + 32 + i."""
+    # sc = [1, 2, 3, 63, 17, 33, 48, 5], m = [0, 1, 62, 3, 20, 0, 35, 63]
+    scales = [0x41, 0x82, 0xC3, 0x3F,     # sc_0..3 | high bits of sc_4..7 (1, 2, 3, 0)
+              0x40, 0x01, 0xBE, 0xC3,     # m_0..3 | high bits of m_4..7 (1, 0, 2, 3)
+              0x41, 0x01, 0x30, 0xF5]     # low bits: sc_4..7 (1, 1, 0, 5), m_4..7 (4, 0, 3, 15)
+    blk = np.zeros(144, np.uint8)
+    blk[0:2] = [0x00, 0x3C]               # d = 1.0
+    blk[2:4] = [0x00, 0x38]               # dmin = 0.5
+    blk[4:16] = scales
+    blk[16 + 0] = 0x21                    # weight 0: 1, weight 32: 2
+    blk[16 + 64 + 7] = 0xE9               # weight 135: 9, weight 167: 14
+    blk[16 + 96 + 31] = 0xF0              # weight 223: 0, weight 255: 15
+    q = np.zeros(256, np.int64)
+    q[[0, 32, 135, 167, 255]] = [1, 2, 9, 14, 15]
+    assert np.array_equal(orc.block_quants(oracle.Q4_K, blk), q)
+    sc = [1, 2, 3, 63, 17, 33, 48, 5]
+    m = [0, 1, 62, 3, 20, 0, 35, 63]
+    want = np.array([sc[n // 32] * q[n] - 0.5 * m[n // 32] for n in range(256)])
+    assert want[0] == 1.0 and want[32] == 3.5 and want[135] == 143.0
+    assert want[167] == 462.0 and want[223] == -17.5 and want[255] == 43.5
+    assert np.array_equal(orc.dequant_row(oracle.Q4_K, blk, 256), want)
+
+
+def test_q6k_byte_layout(orc):
+    """A Q6_K block written byte by byte: ql[128] at 0, qh[64] at 128, int8
+    scales[16] at 192, fp16 d at 208. In half h, for i < 32 with g = qh[32h + i]:
+    weight 128h + i = low nibble of ql[64h + i] | (g & 3) << 4, weight
+    128h + 32 + i = low nibble of ql[64h + 32 + i] | (g >> 2 & 3) << 4, weight
+    128h + 64 + i = high nibble of ql[64h + i] | (g >> 4 & 3) << 4, weight
+    128h + 96 + i = high nibble of ql[64h + 32 + i] | (g >> 6 & 3) << 4;
+    w = d * scales[n / 16] * (q - 32)."""
+    blk = np.zeros(210, np.uint8)
+    blk[128:192] = 0xAA                   # every high-bit pair = 2: q = 32 + nibble
+    blk[192:208] = 1                      # scales 1 ...
+    blk[192 + 0] = 0xFE                   # ... scales[0] = -2
+    blk[192 + 9] = 0x7F                   # scales[9] = 127
+    blk[192 + 15] = 0x03                  # scales[15] = 3
+    blk[208:210] = [0x00, 0x38]           # d = 0.5
+    blk[0] = 0x53                         # weight 0: nibble 3; weight 64: nibble 5
+    blk[32 + 5] = 0x01                    # weight 37: nibble 1 ...
+    blk[128 + 5] = 0xA2                   # ... with high bits 0 (g >> 2 & 3 = 0)
+    blk[64 + 16] = 0x0F                   # weight 144 (h 1, i 16): nibble 15
+    blk[64 + 32 + 31] = 0x70              # weight 255 (h 1, i 31): high nibble 7 ...
+    blk[128 + 32 + 31] = 0x6A             # ... with high bits 1 (g >> 6 = 1)
+    q = np.full(256, 32, np.int64)
+    q[[0, 64, 37, 144, 255]] = [35, 37, 1, 47, 23]
+    assert np.array_equal(orc.block_quants(oracle.Q6_K, blk), q)
+    sc = np.ones(16)
+    sc[0], sc[9], sc[15] = -2, 127, 3
+    want = np.array([0.5 * sc[n // 16] * (q[n] - 32) for n in range(256)])
+    assert want[0] == -3.0 and want[64] == 2.5 and want[37] == -15.5
+    assert want[144] == 952.5 and want[255] == -13.5 and want[191] == 0.0
+    assert np.array_equal(orc.dequant_row(oracle.Q6_K, blk, 256), want)
+
+
+def test_mxfp4_byte_layout(orc):
+    """An MXFP4 block written byte by byte: E8M0 scale at byte 0, then 16
+    bytes: byte 1 + i low nibble = element i, high nibble = element i + 16;
+    nibble bit 3 = sign, bits 0..2 index {0, 0.5, 1, 1.5, 2, 3, 4, 6}."""
+    blk = np.zeros(17, np.uint8)
+    blk[0] = 128                          # scale 2
+    blk[1 + 0] = 0x9F                     # element 0: -6; element 16: -0.5
+    blk[1 + 15] = 0x25                    # element 15: 3; element 31: 1
+    blk[1 + 7] = 0x80                     # element 7: +0; element 23: -0 (equal to 0)
+    blk[1 + 3] = 0x4A                     # element 3: -1; element 19: 2
+    want = np.zeros(32)
+    want[[0, 16, 15, 31, 3, 19]] = [-12.0, -1.0, 6.0, 2.0, -2.0, 4.0]
+    got = orc.dequant_row(oracle.MXFP4, blk, 32)
+    assert np.array_equal(got, want)
+    # the raw quants are 2 * e2m1, which at scale 2 equal the values themselves
+    assert np.array_equal(orc.block_quants(oracle.MXFP4, blk), want.astype(np.int64))
+
+
 def test_q5k_hand_packed_fields(orc, genlib):
     rng = np.random.default_rng(3)
     for trial in range(50):
