@@ -211,6 +211,24 @@ MOE_API moe_status moe_layer_forward(const moe_layer_desc* desc, const void* x, 
                              float* y, int32_t* ids_out, float* w_out, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, with the workspace taken from a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it
+ * runs on until the process ends. The caller passes inputs and outputs only.
+ * Returns MOE_ENOWORKSPACE, with nothing enqueued, when
+ * moe_workspace_size(desc, T) exceeds that size (32 MiB covers up to 64 tokens
+ * of the Kimi-K2-shaped layer; larger chunks need moe_layer_forward and a
+ * caller workspace). It calls no allocation routine; the first call on a
+ * device looks the array's address up once. All calls on one GPU share its
+ * array: calls that can overlap on one GPU (other streams, other host
+ * threads) race and must be serialized by the caller. Other arguments and
+ * errors as moe_layer_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+MOE_API moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const void* x,
+                                     moe_dtype dtype, int T, float* y, int32_t* ids_out,
+                                     float* w_out, hipStream_t stream);
+
 /* moe_layer_forward with timing hooks: events holds n_events HIP events (may
  * be NULL); kernel i of the call records events[2i] when it starts and
  * events[2i + 1] when it ends (hipExtLaunchKernel start/stop events), for the

@@ -4,8 +4,19 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
 #include "../../include/moe.h"
 #include "moe_internal.h"
+
+// Device scratch of moe_layer_forward_noalloc: each GPU the library runs on
+// holds its own copy from the moment the code object is loaded on it until the
+// process ends. Host code never passes this name to a kernel: it stands for a
+// host-side shadow; the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace moe {
 
@@ -306,21 +317,28 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq, const 
   return expert_ffn_impl(a, g, true, stream, stg);
 }
 
-static moe_status layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
-                                float* y, int32_t* ids_out, float* w_out, void* ws,
-                                size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
-                                int n_events) {
+// Argument checks of a layer call (everything but the workspace), and the path
+// and workspace layout it takes.
+static moe_status check_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
+                                float* y, int32_t* ids_out, float* w_out, hipEvent_t* events,
+                                int n_events, bool* grouped, WsLayout* L) {
   moe_status st = validate_desc(desc);
   if (st != MOE_OK) return st;
   if (validate_x(x, dtype) != MOE_OK) return MOE_EINVAL;
   if (T < 0 || T > kMaxTokens || !y || !aligned(y, 16)) return MOE_EINVAL;
   if ((ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4))) return MOE_EINVAL;
-  if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
   if (events && n_events < 0) return MOE_EINVAL;
-  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
-  const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
-                               desc->sh_gate != nullptr, g);
-  if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
+  *grouped = use_grouped(T, desc->fmt_gate, desc->fmt_down);
+  *L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
+                 desc->sh_gate != nullptr, *grouped);
+  return MOE_OK;
+}
+
+// The layer's launch sequence on a checked call with its workspace bound.
+static moe_status run_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
+                              float* y, int32_t* ids_out, float* w_out, void* ws, bool g,
+                              const WsLayout& L, hipStream_t stream, hipEvent_t* events,
+                              int n_events) {
   if (T == 0) return MOE_OK;
   KArgs a = make_args(desc, T);
   bind_ws(a, L, ws);
@@ -342,10 +360,59 @@ static moe_status layer_forward(const moe_layer_desc* desc, const void* x, moe_d
   return expert_ffn_impl(a, false, false, stream, stg);
 }
 
+static moe_status layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
+                                float* y, int32_t* ids_out, float* w_out, void* ws,
+                                size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                                int n_events) {
+  bool g;
+  WsLayout L;
+  moe_status st = check_forward(desc, x, dtype, T, y, ids_out, w_out, events, n_events, &g, &L);
+  if (st != MOE_OK) return st;
+  if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
+  if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
+  return run_forward(desc, x, dtype, T, y, ids_out, w_out, ws, g, L, stream, events, n_events);
+}
+
+// Per-device address of `scratch`, looked up once per device with that device
+// current (each GPU holds its own copy at its own address).
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+static void* scratch_ptr(int dev) {
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
 moe_status moe_layer_forward(const moe_layer_desc* desc, const void* x, moe_dtype dtype, int T,
                              float* y, int32_t* ids_out, float* w_out, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
   return layer_forward(desc, x, dtype, T, y, ids_out, w_out, ws, ws_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const void* x, moe_dtype dtype,
+                                     int T, float* y, int32_t* ids_out, float* w_out,
+                                     hipStream_t stream) {
+  bool g;
+  WsLayout L;
+  moe_status st = check_forward(desc, x, dtype, T, y, ids_out, w_out, nullptr, 0, &g, &L);
+  if (st != MOE_OK) return st;
+  if (L.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ENOWORKSPACE;
+  if (T == 0) return MOE_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  void* ws = scratch_ptr(dev);
+  if (!ws) return MOE_EHIP;
+  return run_forward(desc, x, dtype, T, y, ids_out, w_out, ws, g, L, stream, nullptr, 0);
 }
 
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, moe_dtype dtype,

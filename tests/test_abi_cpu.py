@@ -264,3 +264,21 @@ def test_gemv_plan_rejects_rows_past_the_task_cap():
     with pytest.raises(M.MoeError) as ei:
         M.moe_layer_forward(d, FAKE, 0, 1, FAKE, None, None, FAKE, ws, stream=0)
     assert ei.value.status == M.MOE_EUNSUPPORTED
+
+
+def test_noalloc_refuses_chunks_past_the_scratch():
+    """moe_layer_forward_noalloc works out of a 32 MiB static device array: the
+    Kimi-K2-shaped 256-token chunk needs ~95 MB of workspace, so the call is
+    refused on the host before anything is enqueued (no device is touched)."""
+    cfg = gen.CONFIGS["kimi-k2"]
+    d = good_desc(cfg)
+    d.sh_gate, d.sh_up, d.sh_down = FAKE, FAKE + 256, FAKE + 512
+    assert M.moe_workspace_size(d, 256) > M.MOE_NOALLOC_SCRATCH_BYTES
+    assert M.moe_workspace_size(d, 64) <= M.MOE_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_layer_forward_noalloc(d, FAKE, 0, 256, FAKE, None, None, stream=0)
+    assert ei.value.status == M.MOE_ENOWORKSPACE
+    with pytest.raises(M.MoeError) as ei:  # argument checks come first
+        M.moe_layer_forward_noalloc(d, FAKE + 8, 0, 256, FAKE, None, None, stream=0)
+    assert ei.value.status == M.MOE_EINVAL
+    M.moe_layer_forward_noalloc(d, FAKE, 0, 0, FAKE, None, None, stream=0)  # T = 0: no-op
