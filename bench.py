@@ -1,18 +1,24 @@
 #!/usr/bin/env python3
-"""MoE-layer decode benchmark on one MI355X.
+"""MoE-layer benchmark on one MI355X.
 
 A step is one forward of the whole layer (q8 of x, router + top-k, gate/up,
 SwiGLU, down + routing-weighted combine + shared expert) for one chunk of
-synthetic tokens. The default workload is the Qwen3.6-35B-A3B-shaped decode
+synthetic tokens. The headline workload is the Qwen3.6-35B-A3B-shaped decode
 layer (H 2048, 256 experts, top-8 softmax + shared expert, F 512, Q4_K, one
 token). Steps rotate over layer copies at distinct HBM addresses (the model's
 40 layers) and over a pool of 64 inputs, so expert weights come from HBM, not
 from the 256 MB Infinity Cache or the L2s.
 
-Timed region: K steps replayed from a HIP graph, bracketed by synchronizes.
-Per-kernel durations for the roofline come from HIP events recorded between
-the layer's kernels on the library's stream (moe_layer_forward_timed).
-The CPU baseline is the fp64 oracle on a bounded sample of tokens.
+Headline timed region: exactly K steps, replayed from HIP graphs that hold
+whole rotations over the layer copies (the copy a step reads is the least
+recently used one), bracketed by synchronizes. Per-kernel durations for the
+roofline come from start/stop events that each kernel's dispatch records on
+the library's stream (moe_layer_forward_timed). The other workloads (gpt-oss,
+DeepSeek-V4-Flash and Kimi-K2 shapes) are timed in the same run as medians of
+graph replays and reported under detail.workloads. Measured ceilings: a
+non-temporal streaming read over 4 GiB and an int8 MFMA issue loop. The CPU
+baseline is the fp64 oracle on a bounded sample of tokens, on one host thread
+and on all of them.
 
 Prints ONE JSON line.
 """
@@ -21,13 +27,16 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
+import subprocess
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, AMD published
+I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, AMD published (5.0 POP/s)
 
 
 def parse():
@@ -36,12 +45,18 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="qwen3.6-35b-a3b")
+    p.add_argument("--extra", default="gpt-oss-20b,deepseek-v4-flash,kimi-k2",
+                   help="further workloads timed in the same run (comma list; '' for none)")
+    p.add_argument("--extra-reps", type=int, default=5, help="graph replays per extra workload")
     p.add_argument("--copies", type=int, default=None, help="layer copies rotated in HBM")
     p.add_argument("--x-pool", type=int, default=64)
     p.add_argument("--stage-iters", type=int, default=400)
     p.add_argument("--cpu-baseline", type=int, default=1)
-    p.add_argument("--cpu-tokens", type=int, default=None)
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="target wall time of each CPU-baseline leg")
     p.add_argument("--threads", type=int, default=None)
+    p.add_argument("--probes", type=int, default=1, help="measure the read wall and MFMA peak")
+    p.add_argument("--wall-gib", type=int, default=4)
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -51,12 +66,57 @@ DEFAULT_COPIES = {"tiny": 1, "qwen3.6-35b-a3b": 40, "gpt-oss-20b": 24, "deepseek
                   "kimi-k2": 2, "qwen3.6-35b-a3b-q5k": 40, "qwen3.6-35b-a3b-q2k": 40}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
-              "(expert-parallel sharding over several GPUs is not implemented)", file=sys.stderr)
-        sys.exit(2)
+def rotation(copies: int) -> int:
+    """Forwards per graph: whole rotations over the copies, at least 64."""
+    return copies * ((64 + copies - 1) // copies)
+
+
+# ------------------------------------------------------------------ probes
+def measure_probes(M, torch, wall_gib: int):
+    """Streaming read wall (GB/s) and int8 MFMA rates (TOPS) on this GPU."""
+    out = {}
+    stream = torch.cuda.Stream()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nbytes = wall_gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    best = 0.0
+    per = {}
+    for nwg in (2048, 4096, 8192):
+        ts = []
+        for _ in range(6):
+            a, b = M.HipEvent(), M.HipEvent()
+            a.record(stream)
+            M.moe_probe_read_wall(buf, nbytes, nwg, sink, stream)
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_ms(b))
+        ts = sorted(ts[1:])
+        gbs = nbytes / (ts[len(ts) // 2] * 1e-3) / 1e9
+        per[nwg] = round(gbs, 1)
+        best = max(best, gbs)
+    out["read_wall_GBps"] = round(best, 1)
+    out["read_wall_detail"] = {"bytes": nbytes, "GBps_by_workgroups": per,
+                               "kernel": "k_read_wall (non-temporal dwordx4, 8 in flight/lane)"}
+    del buf
+    for k64, name in ((0, "mfma_i32_16x16x32_i8"), (1, "mfma_i32_16x16x64_i8")):
+        nwg, iters = 2048, 400
+        ops = nwg * 4 * iters * 8 * 16 * 16 * (64 if k64 else 32) * 2
+        ts = []
+        for _ in range(5):
+            a, b = M.HipEvent(), M.HipEvent()
+            a.record(stream)
+            M.moe_probe_mfma_i8(k64, iters, nwg, sink, stream)
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_ms(b))
+        ts = sorted(ts[1:])
+        out[f"{name}_TOPS"] = round(ops / (ts[len(ts) // 2] * 1e-3) / 1e12, 1)
+    torch.cuda.synchronize()
+    return out
+
+
+# --------------------------------------------------------------- workloads
+def run_workload(args, name: str, headline: bool, probes: dict, th: int):
     import numpy as np
     import torch
 
@@ -64,10 +124,8 @@ def main():
     import quantized_moe_expert_route_amd as M
     from gen.device import DeviceLayer, x_to_device
 
-    torch.cuda.set_device(0)
-    cfg = gen.CONFIGS[args.workload]
-    th = args.threads or gen.default_threads()
-    copies = args.copies or DEFAULT_COPIES[args.workload]
+    cfg = gen.CONFIGS[name]
+    copies = (args.copies if headline and args.copies else None) or DEFAULT_COPIES[name]
     t0 = time.time()
     data = gen.make_layer(cfg, threads=th)
     dl = DeviceLayer(data, copies=copies)
@@ -88,54 +146,64 @@ def main():
                             ws.numel(), stream)
 
     stream = torch.cuda.Stream()
-    if args.calib_copy_mb:
-        # fp32 -> fp16 conversion: reads 4 B and writes 2 B per element (known traffic)
-        n = (args.calib_copy_mb << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty(n, dtype=torch.float16, device="cuda")
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    # ---- warmup (eager) and realized routing per copy
+    warm = args.warmup if headline else min(args.warmup, 2 * rotation(copies))
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
+        for i in range(warm):
             fwd(i)
     torch.cuda.synchronize()
 
-    # ---- graph of G forwards; K steps = (K // G) replays + a tail graph
-    K = args.steps
-    G = min(K, max(copies, 64))
-    graphs = {}
+    G = rotation(copies)
 
-    def graph_of(n, start):
+    def graph_of(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for j in range(n):
-                fwd(start + j)
+                fwd(j)
         return g
 
-    graphs["full"] = graph_of(G, 0)
-    tail = K % G
-    if tail:
-        graphs["tail"] = graph_of(tail, 0)
+    full = graph_of(G)
     for _ in range(2):
-        graphs["full"].replay()
+        full.replay()
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(K // G):
-        graphs["full"].replay()
-    if tail:
-        graphs["tail"].replay()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms_per_step = elapsed * 1e3 / K
-    tokens_per_s = T * K / elapsed
+    res = {"workload": cfg.description, "tokens_per_step": T, "layer_copies": copies,
+           "x_pool": args.x_pool, "forwards_per_graph": G}
+    if headline:
+        # exactly K steps: whole rotations, then the first K mod G forwards of
+        # one (their copies are the least recently used ones at that point)
+        K = args.steps
+        tail = graph_of(K % G) if K % G else None
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(K // G):
+            full.replay()
+        if tail is not None:
+            tail.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+        res["ms_per_step"] = elapsed * 1e3 / K
+        res["tokens_per_s"] = T * K / elapsed
+        res["steps_timed"] = K
+        res["copies_touched"] = min(copies, K)
+    else:
+        per = []
+        with torch.cuda.stream(stream):  # replay() launches on the current stream
+            for _ in range(args.extra_reps):
+                a, b = M.HipEvent(), M.HipEvent()
+                a.record(stream)
+                full.replay()
+                b.record(stream)
+                b.synchronize()
+                per.append(a.elapsed_ms(b) / G)
+        med = float(np.median(per))
+        res["ms_per_step"] = med
+        res["tokens_per_s"] = T / (med * 1e-3)
+        res["timing"] = f"median of {args.extra_reps} replays of a {G}-forward graph"
+    del full
 
-    # ---- per-kernel durations: start/stop events recorded by each kernel's dispatch
+    # per-kernel durations: start/stop events recorded by each kernel's dispatch
     n_st = M.moe_layer_stage_count(dl.desc, T)
     names = [M.moe_layer_stage_name(dl.desc, T, i) for i in range(n_st)]
-    R = args.stage_iters
+    R = args.stage_iters if headline else max(32, min(args.stage_iters, 4 * G))
     evs = [[M.HipEvent() for _ in range(2 * n_st)] for _ in range(R)]
     with torch.cuda.stream(stream):
         for i in range(R):
@@ -149,7 +217,7 @@ def main():
     skip = min(20, R // 4)
     stage_avg_us = {names[s]: float(stage_ms[skip:, s].mean() * 1e3) for s in range(n_st)}
 
-    # ---- bytes: selected experts (realized routing of the pool inputs on copy 0)
+    # realized routing of the pool inputs on copy 0: unique experts per step
     realized = []
     for i in range(args.x_pool):
         M.moe_layer_forward(dl.descs[0], xs[i], dtype, T, y, ids, w, ws, ws.numel())
@@ -160,72 +228,176 @@ def main():
     sel_bytes = uniq_mean * cfg.expert_algo_bytes
     path = "grouped" if n_st == 7 else "gemv"
     algo = algo_bytes(cfg, path, uniq_mean)
-    kern_names = kernel_names(cfg, path)
+    kn = kernel_names(cfg, path)
     dom = max(("gateup", "down"), key=lambda k: stage_avg_us.get(k, 0.0))
     dom_us = stage_avg_us[dom]
     expert_us = stage_avg_us.get("gateup", 0) + stage_avg_us.get("down", 0)
     achieved = algo[dom] / (dom_us * 1e-6) / 1e9
-    traffic = _traffic_for(kern_names[dom], args.workload, path)
-    roofline = {
-        "kernel": kern_names[dom],
+    wall = probes.get("read_wall_GBps")
+    roof = {
+        "kernel": kn[dom],
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": traffic,
+        "traffic": _traffic_for(kn[dom], name, path),
+        "measured_wall": wall,
+        "frac_of_measured_wall": round(achieved / wall, 4) if wall else None,
         "algo_bytes_per_launch": round(algo[dom]),
         "avg_launch_us": round(dom_us, 3),
     }
+    res.update({
+        "path": path,
+        "roofline": roof,
+        "selected_expert_bytes_per_step": round(sel_bytes),
+        "unique_experts_per_step": uniq_mean,
+        "layer_GBps_selected_experts": round(sel_bytes / (res["ms_per_step"] * 1e-3) / 1e9, 1),
+        "layer_hbm_frac": round(sel_bytes / (res["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "expert_kernels_us": round(expert_us, 3),
+        "expert_GBps": round(sel_bytes / (expert_us * 1e-6) / 1e9, 1) if expert_us else None,
+        "kernel_source_hash": kernel_source_hash(path),
+        "stage_avg_us": {k: round(v, 3) for k, v in stage_avg_us.items()},
+        "setup_s": round(setup_s, 1),
+    })
+    for k in ("gateup", "down"):
+        res[f"{k}_GBps"] = round(algo[k] / (stage_avg_us[k] * 1e-6) / 1e9, 1)
+        res[f"{k}_kernel"] = kn[k]
+    if path == "grouped":
+        # routed tokens per active expert in a chunk (realized histogram)
+        cnt = np.concatenate([np.bincount(r.ravel(), minlength=cfg.E) for r in realized])
+        act = cnt[cnt > 0]
+        res["tokens_per_active_expert"] = {
+            "mean": round(float(act.mean()), 2), "max": int(act.max()),
+            "hist_1_2_3_4-7_8-15_16+": [int((act == 1).sum()), int((act == 2).sum()),
+                                        int((act == 3).sum()),
+                                        int(((act >= 4) & (act < 8)).sum()),
+                                        int(((act >= 8) & (act < 16)).sum()),
+                                        int((act >= 16).sum())]}
+        # int8 MFMA work of the tile kernels: 2 H F per routed (token, slot) pair
+        # and matrix (algorithmic; padded tile rows are not counted)
+        P = T * cfg.k + (T if cfg.shared else 0)
+        ops = {"gateup": P * 2 * 2 * cfg.H * cfg.F, "down": P * 2 * cfg.H * cfg.F}
+        mf = {}
+        for k in ("gateup", "down"):
+            tops = ops[k] / (stage_avg_us[k] * 1e-6) / 1e12
+            mf[k] = {"kernel": kn[k], "int8_ops_per_launch": ops[k], "achieved_TOPS": round(tops, 1),
+                     "frac_of_peak": round(tops / I8_PEAK_TOPS, 4)}
+        res["mfma"] = {"peak_TOPS": I8_PEAK_TOPS,
+                       "measured_TOPS_16x16x32": probes.get("mfma_i32_16x16x32_i8_TOPS"),
+                       "measured_TOPS_16x16x64": probes.get("mfma_i32_16x16x64_i8_TOPS"),
+                       **mf}
+    keep = (data, cfg)
+    del dl, xs, ws, y, ids, w, evs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, keep
 
-    # ---- CPU baseline: the oracle on a bounded sample of tokens
-    cpu = None
-    if args.cpu_baseline:
-        import oracle
-        L = oracle.Layer(data)
-        n_tok = args.cpu_tokens or max(16, min(1024, int(20.0 / _oracle_token_s(cfg))))
-        xs_np = np.concatenate([gen.make_x(cfg, T=T, x_index=i)[0] for i in range(
-            (n_tok + T - 1) // T)])[:n_tok]
-        t1 = time.perf_counter()
-        L.forward(xs_np, threads=th)
-        cpu_s = time.perf_counter() - t1
-        cpu = {"value": round(n_tok / cpu_s, 2), "unit": "tokens/s", "cores": th, "kind": "oracle",
-               "sample": f"{n_tok} tokens of the same workload (x pool members), whole layer per "
-                         f"token, fp64 oracle, {th} host threads, {cpu_s:.1f} s wall "
-                         f"(~{cpu_s * th:.0f} thread-seconds of CPU work)"}
 
+def cpu_model() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(args, data, cfg, th: int):
+    """The oracle, unchanged, on a bounded sample of tokens of the workload:
+    one host thread, then all of them."""
+    import numpy as np
+
+    import gen
+    import oracle
+
+    L = oracle.Layer(data)
+    T = cfg.T
+    tok_s = _oracle_token_s(cfg)
+
+    def sample(n):
+        return np.concatenate([gen.make_x(cfg, T=T, x_index=i)[0]
+                               for i in range((n + T - 1) // T)])[:n]
+
+    n1 = max(4, int(args.cpu_seconds / tok_s))
+    x1 = sample(n1)
+    t = time.perf_counter()
+    L.forward(x1, threads=1)
+    s1 = time.perf_counter() - t
+    nn = max(16, int(args.cpu_seconds * th / tok_s))
+    xn = sample(nn)
+    t = time.perf_counter()
+    L.forward(xn, threads=th)
+    sn = time.perf_counter() - t
+    return {"value": round(nn / sn, 2), "unit": "tokens/s", "cores": th, "kind": "oracle",
+            "sample": f"{nn} tokens of the same workload (x pool members), whole layer per token, "
+                      f"fp64 oracle on {th} host threads, {sn:.1f} s wall; and {n1} tokens on one "
+                      f"thread, {s1:.1f} s",
+            "single_thread_value": round(n1 / s1, 2),
+            "nproc": os.cpu_count(), "threads_available": th, "cpu_model": cpu_model()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+              "(expert-parallel sharding over several GPUs is not implemented)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import gen
+    import quantized_moe_expert_route_amd as M
+
+    torch.cuda.set_device(0)
+    th = args.threads or gen.default_threads()
+    if args.calib_copy_mb:
+        # fp32 -> fp16 conversion: reads 4 B and writes 2 B per element (known traffic)
+        n = (args.calib_copy_mb << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty(n, dtype=torch.float16, device="cuda")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    probes = measure_probes(M, torch, args.wall_gib) if args.probes else {}
+    head, (data, cfg) = run_workload(args, args.workload, True, probes, th)
+    cpu = cpu_baseline(args, data, cfg, th) if args.cpu_baseline else None
+    del data
+    extras = {}
+    for name in [n for n in args.extra.split(",") if n and n != args.workload]:
+        r, _ = run_workload(args, name, False, probes, th)
+        extras[name] = r
     out = {
         "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (% of peak), 1 MI355X",
-        "value": round(tokens_per_s, 1),
+        "value": round(head["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(head["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
         "config": {
-            "workload": cfg.description,
-            "tokens_per_step": T,
-            "layer_copies": copies,
-            "x_pool": args.x_pool,
-            "path": path,
+            "workload": head["workload"],
+            "tokens_per_step": head["tokens_per_step"],
+            "layer_copies": head["layer_copies"],
+            "x_pool": head["x_pool"],
+            "path": head["path"],
         },
-        "roofline": roofline,
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "detail": {
-            "selected_expert_bytes_per_step": round(sel_bytes),
-            "unique_experts_per_step": uniq_mean,
-            "layer_GBps_selected_experts": round(sel_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-            "layer_hbm_frac": round(sel_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "expert_kernels_us": round(expert_us, 3),
-            "kernel_source_hash": kernel_source_hash(path),
-            "expert_GBps": round(sel_bytes / (expert_us * 1e-6) / 1e9, 1) if expert_us else None,
-            "stage_avg_us": {k: round(v, 3) for k, v in stage_avg_us.items()},
-            "setup_s": round(setup_s, 1),
+            **{k: v for k, v in head.items() if k not in (
+                "workload", "tokens_per_step", "layer_copies", "x_pool", "path", "roofline",
+                "tokens_per_s", "ms_per_step")},
+            "probes": probes,
+            "workloads": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
+                              for kk, vv in v.items()} for k, v in extras.items()},
         },
     }
     print(json.dumps(out), flush=True)
@@ -307,8 +479,7 @@ def _traffic_for(kernel: str, workload: str, path: str):
 
 def _oracle_token_s(cfg) -> float:
     """Rough single-thread oracle seconds per token (measured: ~1.1 ns per weight
-    for K-quants, ~16 ns for MXFP4); sizes the CPU sample to about 20 s of CPU
-    work."""
+    for K-quants, ~16 ns for MXFP4); sizes the CPU sample."""
     macs = (cfg.k + (1 if cfg.shared else 0)) * 3 * cfg.H * cfg.F
     ns_per_mac = 16.0 if cfg.fmt_gu == 2 else 1.1
     return macs * ns_per_mac * 1e-9

@@ -285,6 +285,25 @@ MOE_API moe_status moe_test_preact(const moe_layer_desc* desc, const moe_qact* x
                            const int32_t* ids, int which, float* out, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* Measurement probes (not part of the layer): ceilings measured on the chip
+ * that runs the layer, reported beside the datasheet peaks. Source: the memra
+ * architecture plan, header (a measured memory-read wall stated beside the
+ * peak bandwidth).
+ * moe_probe_read_wall: reads `bytes` (a multiple of 16) of the device buffer
+ * buf (16-byte aligned) once, as non-temporal 16-byte loads from nwg
+ * workgroups of 256 threads, eight loads in flight per thread. sink: one
+ * device uint32 that is written only in a practically impossible case (it
+ * keeps the loads live). Time it with events on `stream`.
+ * moe_probe_mfma_i8: nwg workgroups of four waves; every wave issues `iters`
+ * rounds of eight independent int8 MFMAs (k64 = 0: 16x16x32, the shape the
+ * tile kernels use; 1: 16x16x64). int8 operations per launch:
+ * nwg * 4 * iters * 8 * 16 * 16 * (k64 ? 64 : 32) * 2. sink as above.
+ * Errors: MOE_EINVAL for a bad pointer, size or count; MOE_EHIP. */
+MOE_API moe_status moe_probe_read_wall(const void* buf, size_t bytes, int nwg, uint32_t* sink,
+                               hipStream_t stream);
+MOE_API moe_status moe_probe_mfma_i8(int k64, int iters, int nwg, int32_t* sink,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,7 @@ ABI_FUNCTIONS = (
     "moe_route_topk", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_timed",
     "moe_layer_stage_count", "moe_layer_stage_name", "moe_test_block_dots",
     "moe_test_tile_dots", "moe_test_tile_dots_ws", "moe_test_preact",
-    "moe_layer_forward_noalloc",
+    "moe_layer_forward_noalloc", "moe_probe_read_wall", "moe_probe_mfma_i8",
 )
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -90,6 +90,8 @@ def lib():
         L.moe_expert_ffn.argtypes = [D, Q, vp, i32, i32, vp, vp, vp, vp, sz, vp]
         L.moe_layer_forward.argtypes = [D, vp, i32, i32, vp, vp, vp, vp, sz, vp]
         L.moe_layer_forward_noalloc.argtypes = [D, vp, i32, i32, vp, vp, vp, vp]
+        L.moe_probe_read_wall.argtypes = [vp, sz, i32, vp, vp]
+        L.moe_probe_mfma_i8.argtypes = [i32, i32, i32, vp, vp]
         L.moe_layer_forward_timed.argtypes = [D, vp, i32, i32, vp, vp, vp, vp, sz, vp,
                                               C.POINTER(vp), i32]
         L.moe_layer_stage_count.argtypes = [D, i32]
@@ -103,7 +105,8 @@ def lib():
         L.moe_test_preact.argtypes = [D, Q, i32, vp, i32, vp, vp, sz, vp]
         for n in ("moe_quantize_act_q8k", "moe_route_topk", "moe_expert_ffn", "moe_layer_forward",
                   "moe_layer_forward_timed", "moe_test_block_dots", "moe_test_tile_dots",
-                  "moe_test_preact", "moe_layer_forward_noalloc"):
+                  "moe_test_preact", "moe_layer_forward_noalloc", "moe_probe_read_wall",
+                  "moe_probe_mfma_i8"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -172,6 +175,16 @@ def moe_layer_forward_noalloc(desc, x, dtype, T, y, ids_out, w_out, stream=None)
     _check("moe_layer_forward_noalloc",
            lib().moe_layer_forward_noalloc(C.byref(desc), _ptr(x), dtype, T, _ptr(y),
                                            _ptr(ids_out), _ptr(w_out), _stream(stream)))
+
+
+def moe_probe_read_wall(buf, nbytes, nwg, sink, stream=None):
+    _check("moe_probe_read_wall",
+           lib().moe_probe_read_wall(_ptr(buf), nbytes, nwg, _ptr(sink), _stream(stream)))
+
+
+def moe_probe_mfma_i8(k64, iters, nwg, sink, stream=None):
+    _check("moe_probe_mfma_i8",
+           lib().moe_probe_mfma_i8(k64, iters, nwg, _ptr(sink), _stream(stream)))
 
 
 def moe_layer_forward_timed(desc, x, dtype, T, y, ids_out, w_out, ws, ws_bytes, stream,

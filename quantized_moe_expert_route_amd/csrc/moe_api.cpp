@@ -517,4 +517,19 @@ moe_status moe_test_preact(const moe_layer_desc* desc, const moe_qact* xq, int T
   return hip_status(e);
 }
 
+moe_status moe_probe_read_wall(const void* buf, size_t bytes, int nwg, uint32_t* sink,
+                               hipStream_t stream) {
+  if (!buf || !aligned(buf, 16) || bytes % 16 || !sink || !aligned(sink, 4)) return MOE_EINVAL;
+  if (nwg < 1 || nwg > (1 << 20)) return MOE_EINVAL;
+  if (bytes == 0) return MOE_OK;
+  return hip_status(launch_read_wall(buf, bytes, sink, nwg, stream));
+}
+
+moe_status moe_probe_mfma_i8(int k64, int iters, int nwg, int32_t* sink, hipStream_t stream) {
+  if ((k64 != 0 && k64 != 1) || iters < 0 || nwg < 1 || nwg > (1 << 20) || !sink ||
+      !aligned(sink, 4))
+    return MOE_EINVAL;
+  return hip_status(launch_mfma_i8(k64, iters, nwg, sink, stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,87 @@
+// Measurement probes for the roofline report: the chip's streaming read wall
+// (non-temporal 16-byte loads over a large buffer) and its int8 MFMA issue
+// rate. Neither is part of the layer; the benchmark times them with events so
+// that each kernel's fraction of peak can be stated against a measured
+// ceiling as well as the datasheet one.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Every thread streams 16-byte pieces i = tid + k * stride (grid-stride), U
+// loads in flight per round; the XOR of what it read goes to sink so the loads
+// are not dead. grid = nwg, block 256. n16 = number of 16-byte pieces.
+template <int U>
+__global__ __launch_bounds__(256) void k_read_wall(const u32x4* buf, size_t n16, uint32_t* sink) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * 256;
+  size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(buf + i + u * stride));
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = buf[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // practically never: keeps the loads live
+}
+
+// Back-to-back int8 MFMAs on NACC independent accumulators per wave (the
+// 16x16x32 shape the tile kernels use, or gfx950's 16x16x64). grid nwg, block
+// 256; every wave runs iters rounds of NACC MFMAs.
+template <int K64, int NACC>
+__global__ __launch_bounds__(256) void k_mfma_i8(int iters, int seed, int32_t* sink) {
+  v4i acc[NACC];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) acc[j] = v4i{0, 0, 0, 0};
+  const int l = threadIdx.x + seed;
+  if constexpr (K64) {
+    const v4i a = {l, l + 1, l + 2, l + 3}, b = {l * 3, l * 5, l * 7, l * 9};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < NACC; ++j)
+        acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
+    }
+  } else {
+    const long a = (static_cast<long>(l) << 32) | static_cast<uint32_t>(l * 3);
+    const long b = (static_cast<long>(l * 5) << 32) | static_cast<uint32_t>(l * 7);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < NACC; ++j)
+        acc[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, acc[j], 0, 0, 0);
+    }
+  }
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) s += acc[j][0] ^ acc[j][1] ^ acc[j][2] ^ acc[j][3];
+  if (s == 0x7F4A7C15) sink[0] = s;  // practically never: keeps the MFMAs live
+}
+
+}  // namespace
+
+hipError_t launch_read_wall(const void* buf, size_t bytes, uint32_t* sink, int nwg, hipStream_t s) {
+  auto kern = k_read_wall<8>;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, s, static_cast<const u32x4*>(buf), bytes / 16,
+                     sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_i8(int k64, int iters, int nwg, int32_t* sink, hipStream_t s) {
+  auto kern = k64 ? k_mfma_i8<1, 8> : k_mfma_i8<0, 8>;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, s, iters, nwg, sink);
+  return hipGetLastError();
+}
+
+}  // namespace moe
