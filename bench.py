@@ -49,6 +49,8 @@ def parse():
                    help="further workloads timed in the same run (comma list; '' for none)")
     p.add_argument("--extra-reps", type=int, default=5, help="graph replays per extra workload")
     p.add_argument("--copies", type=int, default=None, help="layer copies rotated in HBM")
+    p.add_argument("--tokens", type=int, default=None,
+                   help="tokens per step of the headline workload (default: the workload's)")
     p.add_argument("--x-pool", type=int, default=64)
     p.add_argument("--stage-iters", type=int, default=400)
     p.add_argument("--cpu-baseline", type=int, default=1)
@@ -57,6 +59,10 @@ def parse():
     p.add_argument("--threads", type=int, default=None)
     p.add_argument("--probes", type=int, default=1, help="measure the read wall and MFMA peak")
     p.add_argument("--wall-gib", type=int, default=4)
+    p.add_argument("--crossover", default="",
+                   help="comma list of workloads: time each on both expert-FFN paths at "
+                        "--crossover-tokens chunk sizes (reported under detail.crossover)")
+    p.add_argument("--crossover-tokens", default="1,2,3,4,6,8,12,16")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -125,6 +131,8 @@ def run_workload(args, name: str, headline: bool, probes: dict, th: int):
     from gen.device import DeviceLayer, x_to_device
 
     cfg = gen.CONFIGS[name]
+    if headline and args.tokens:
+        cfg = cfg.with_(T=args.tokens, description=f"{cfg.description}; {args.tokens}-token chunk")
     copies = (args.copies if headline and args.copies else None) or DEFAULT_COPIES[name]
     t0 = time.time()
     data = gen.make_layer(cfg, threads=th)
@@ -294,6 +302,73 @@ def run_workload(args, name: str, headline: bool, probes: dict, th: int):
     return res, keep
 
 
+def crossover(args, name: str, th: int) -> dict:
+    """Per-forward time of one workload on the per-pair GEMV path and on the
+    expert-grouped path (forced through the descriptor's path field) at several
+    chunk sizes, and the path the automatic rule picks."""
+    import numpy as np
+    import torch
+
+    import gen
+    import quantized_moe_expert_route_amd as M
+    from gen.device import DeviceLayer, x_to_device
+
+    cfg0 = gen.CONFIGS[name]
+    copies = min(DEFAULT_COPIES[name], 24)
+    data = gen.make_layer(cfg0, threads=th)
+    dl = DeviceLayer(data, copies=copies)
+    out = {}
+    for T in [int(v) for v in args.crossover_tokens.split(",") if v]:
+        cfg = cfg0.with_(T=T)
+        xs = [x_to_device(data, *gen.make_x(cfg, T=T, x_index=i))[0] for i in range(16)]
+        dt = M.MOE_DTYPE_BF16 if cfg.x_bf16 else M.MOE_DTYPE_F32
+        y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+        row = {}
+        for pname, path in (("auto", M.MOE_PATH_AUTO), ("gemv", M.MOE_PATH_GEMV),
+                            ("grouped", M.MOE_PATH_GROUPED)):
+            for d in dl.descs:
+                d.path = path
+            if pname == "auto":
+                row["auto_path"] = "grouped" if M.moe_layer_stage_count(dl.desc, T) == 7 else "gemv"
+                continue
+            ws = dl.workspace(T)
+            s = torch.cuda.Stream()
+            G = rotation(copies)
+
+            def fwd(i):
+                M.moe_layer_forward(dl.descs[i % copies], xs[i % 16], dt, T, y, ids, w, ws,
+                                    ws.numel(), s)
+
+            with torch.cuda.stream(s):
+                for i in range(G):
+                    fwd(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(G):
+                    fwd(i)
+            per = []
+            with torch.cuda.stream(s):
+                g.replay()
+                for _ in range(5):
+                    a, b = M.HipEvent(), M.HipEvent()
+                    a.record(s)
+                    g.replay()
+                    b.record(s)
+                    b.synchronize()
+                    per.append(a.elapsed_ms(b) * 1e3 / G)
+            row[f"{pname}_us"] = round(float(np.median(per)), 2)
+            del g, ws
+        out[T] = row
+    for d in dl.descs:
+        d.path = M.MOE_PATH_AUTO
+    del dl
+    torch.cuda.empty_cache()
+    return {"workload": cfg0.description, "layer_copies": copies, "per_forward": out}
+
+
 def cpu_model() -> str:
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
@@ -369,6 +444,7 @@ def main():
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
         r, _ = run_workload(args, name, False, probes, th)
         extras[name] = r
+    xover = {n: crossover(args, n, th) for n in args.crossover.split(",") if n}
     out = {
         "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (% of peak), 1 MI355X",
         "value": round(head["tokens_per_s"], 1),
@@ -396,6 +472,7 @@ def main():
                 "workload", "tokens_per_step", "layer_copies", "x_pool", "path", "roofline",
                 "tokens_per_s", "ms_per_step")},
             "probes": probes,
+            **({"crossover": xover} if xover else {}),
             "workloads": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                               for kk, vv in v.items()} for k, v in extras.items()},
         },

@@ -32,7 +32,8 @@ def x_to_device(data, x_np: np.ndarray | None = None, xb_np: np.ndarray | None =
 
 class DeviceLayer:
     def __init__(self, data, copies: int = 1, present=None, route_scale=None, norm_topk=None,
-                 use_shared: bool = True, sh_gate_vec=None, sel_bias="data", device="cuda"):
+                 use_shared: bool = True, sh_gate_vec=None, sel_bias="data", device="cuda",
+                 path: int = 0):
         cfg = data.cfg
         self.cfg = cfg
         self.device = device
@@ -89,6 +90,7 @@ class DeviceLayer:
                 sh = base + E * es
                 d.sh_gate, d.sh_up, d.sh_down = sh, sh + cfg.gate_bytes, sh + 2 * cfg.gate_bytes
             d.sh_gate_vec = None if self.sh_gate_vec is None else self.sh_gate_vec.data_ptr()
+            d.path = path  # moe_path: 0 auto, 1 per-pair GEMV, 2 expert-grouped
             self._tables.append(keep)
             self.descs.append(d)
 

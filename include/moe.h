@@ -49,7 +49,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
@@ -82,6 +82,15 @@ typedef enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 } moe_router;
 /* SWIGLU: h = silu(g) * u. SWIGLU_OAI (gpt-oss): g' = min(g, limit),
  * u' = clamp(u, -limit, limit), h = g' * sigmoid(alpha * g') * (u' + 1). */
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
+/* Expert-FFN path of a chunk. AUTO: layers with a matrix in a format without
+ * tile kernels (MXFP4, Q5_K, Q2_K) take the per-(token, slot) GEMV path; the
+ * others take the expert-grouped int8-MFMA path when one expert's block bytes
+ * reach 8 MB, or when T * (k + shared) * (block bytes of one expert) reaches
+ * 160 MB, else the GEMV path (the measured crossover: the grouped path reads
+ * each selected expert once per 16 tokens at the cost of more launches, and
+ * streams large experts faster even for one token). GEMV and GROUPED force a
+ * path (GROUPED only where the formats allow it). */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_path;
 
 /* q8 activations of T rows of width H, structure-of-arrays:
  *   qs    int8  [T, H]      quants, |q| <= 127
@@ -127,6 +136,7 @@ typedef struct {
  *  sh_gate, sh_up, sh_down: the shared expert (same formats, strides and
  *    shape as the routed experts) or all NULL. sh_gate_vec fp32 [H] or NULL:
  *    shared-expert weight sigmoid(sh_gate_vec . x), or 1 when NULL.
+ *  path: moe_path (0 = AUTO).
  */
 typedef struct {
   int32_t hidden;
@@ -153,6 +163,7 @@ typedef struct {
   const void* sh_up;
   const void* sh_down;
   const float* sh_gate_vec;
+  int32_t path;
 } moe_layer_desc;
 
 /* ABI version (MOE_ABI_VERSION) and a static message for a status. */

@@ -26,6 +26,7 @@ MOE_AFMT_Q8_K, MOE_AFMT_Q8_32 = range(2)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = range(2)
 MOE_ROUTER_SOFTMAX, MOE_ROUTER_SIGMOID = range(2)
 MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = range(2)
+MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GROUPED = range(3)
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
 
@@ -61,7 +62,7 @@ class MoeLayerDesc(C.Structure):
         ("b_gate", C.c_void_p), ("b_up", C.c_void_p), ("b_down", C.c_void_p),
         ("act", C.c_int32), ("act_alpha", C.c_float), ("act_limit", C.c_float),
         ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
-        ("sh_gate_vec", C.c_void_p),
+        ("sh_gate_vec", C.c_void_p), ("path", C.c_int32),
     ]
 
 

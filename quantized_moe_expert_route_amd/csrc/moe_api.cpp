@@ -40,6 +40,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->router != MOE_ROUTER_SOFTMAX && d->router != MOE_ROUTER_SIGMOID) return MOE_EINVAL;
   if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_EINVAL;
   if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
+  if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_GEMV && d->path != MOE_PATH_GROUPED)
+    return MOE_EINVAL;
   for (int f : {d->fmt_gate, d->fmt_up, d->fmt_down})
     if (f != MOE_WFMT_Q4_K && f != MOE_WFMT_Q6_K && f != MOE_WFMT_MXFP4 && f != MOE_WFMT_Q5_K &&
         f != MOE_WFMT_Q2_K)
@@ -132,18 +134,41 @@ struct Stages {
 
 }  // namespace
 
-// Dispatch rule between the two expert-FFN paths: chunks of up to 4 tokens,
-// and every chunk of a layer with an MXFP4, Q5_K or Q2_K matrix (formats without
-// MFMA tile kernels), take the per-(token, slot) GEMV path (moe_kernels.hip);
-// larger chunks of Q4_K / Q6_K layers take the
-// expert-grouped path (moe_grouped.hip), whose int8 MFMA tiles read each
-// selected expert's weights once per 16 tokens routed to it.
-constexpr int kGroupedMinTokens = 5;
+// Dispatch rule between the two expert-FFN paths (MOE_PATH_AUTO). The
+// per-(token, slot) GEMV path (moe_kernels.hip) streams every pair's expert
+// rows; the expert-grouped path (moe_grouped.hip) reads each selected expert's
+// rows once per 16 tokens routed to it through LDS-ring int8-MFMA tiles, at
+// the cost of seven launches. Measured on one MI355X (us per forward, GEMV /
+// grouped):
+//   Qwen3.6 shape, 1.77 MB experts, 8 + 1 slots, random routing: T = 1: 15.5 /
+//     42.6, T = 8: 52.2 / 59.5, T = 10: 63.6 / 70.3, T = 12: 74.5 / 72.6,
+//     T = 16: 92.7 / 84.0;
+//   DeepSeek-V4-Flash shape, 16.3 MB experts, 6 + 1 slots, Zipf routing:
+//     T = 1: 74.5 / 66.0, T = 2: 138.7 / 84.3, T = 16: 1010 / 168;
+//   Kimi-K2 shape, 24.8 MB experts, 8 + 1 slots: T = 1: 123 / 100.
+// So: grouped once the per-pair bytes T (k + shared) expert_bytes reach 160 MB
+// (the small-expert crossover lies between 159 and 191 MB), and at every T for
+// experts of 8 MB or more (the per-pair kernels stream such rows more slowly
+// than the tiles, even for one token). Layers with a matrix in a format without
+// tile kernels (MXFP4, Q5_K, Q2_K) take the GEMV path.
+constexpr double kGroupedMinPairBytes = 160e6;
+constexpr double kGroupedMinExpertBytes = 8e6;
 
+static size_t expert_block_bytes(const moe_layer_desc* d) {
+  const size_t gu = static_cast<size_t>(d->hidden / block_elems(d->fmt_gate)) * block_bytes(d->fmt_gate);
+  const size_t dn = static_cast<size_t>(d->ffn / block_elems(d->fmt_down)) * block_bytes(d->fmt_down);
+  return 2 * static_cast<size_t>(d->ffn) * gu + static_cast<size_t>(d->hidden) * dn;
+}
 
-bool use_grouped(int T, int fmt_gate, int fmt_down) {
+bool use_grouped(const moe_layer_desc* d, int T) {
   auto tiled = [](int f) { return f == FMT_Q4_K || f == FMT_Q6_K; };
-  return T >= kGroupedMinTokens && tiled(fmt_gate) && tiled(fmt_down);
+  if (!tiled(d->fmt_gate) || !tiled(d->fmt_down) || T < 1) return false;
+  if (d->path == MOE_PATH_GEMV) return false;
+  if (d->path == MOE_PATH_GROUPED) return true;
+  const double eb = static_cast<double>(expert_block_bytes(d));
+  if (eb >= kGroupedMinExpertBytes) return true;
+  const int slots = d->top_k + (d->sh_gate != nullptr ? 1 : 0);
+  return static_cast<double>(T) * slots * eb >= kGroupedMinPairBytes;
 }
 
 WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped) {
@@ -204,7 +229,7 @@ const char* moe_status_str(moe_status s) {
 
 size_t moe_workspace_size(const moe_layer_desc* desc, int T) {
   if (validate_desc(desc) != MOE_OK || T < 0 || T > kMaxTokens) return 0;
-  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
+  const bool g = use_grouped(desc, T);
   return ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
                    desc->sh_gate != nullptr, g).total;
 }
@@ -234,7 +259,7 @@ moe_status moe_route_topk(const moe_layer_desc* desc, const void* x, moe_dtype d
   if (T < 0 || T > kMaxTokens || !ids || !w) return MOE_EINVAL;
   if (!aligned(ids, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4))) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
-  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
+  const bool g = use_grouped(desc, T);
   const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
                                desc->sh_gate != nullptr, g);
   if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
@@ -299,7 +324,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq, const 
   if (desc->sh_gate_vec && validate_x(x, dtype) != MOE_OK) return MOE_EINVAL;
   if (!aligned(ids, 4) || !aligned(w, 4) || !aligned(y, 16)) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
-  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
+  const bool g = use_grouped(desc, T);
   const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
                                desc->sh_gate != nullptr, g);
   if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
@@ -328,7 +353,7 @@ static moe_status check_forward(const moe_layer_desc* desc, const void* x, moe_d
   if (T < 0 || T > kMaxTokens || !y || !aligned(y, 16)) return MOE_EINVAL;
   if ((ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4))) return MOE_EINVAL;
   if (events && n_events < 0) return MOE_EINVAL;
-  *grouped = use_grouped(T, desc->fmt_gate, desc->fmt_down);
+  *grouped = use_grouped(desc, T);
   *L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
                  desc->sh_gate != nullptr, *grouped);
   return MOE_OK;
@@ -425,7 +450,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, mo
 
 int moe_layer_stage_count(const moe_layer_desc* desc, int T) {
   if (validate_desc(desc) != MOE_OK || T <= 0 || T > kMaxTokens) return 0;
-  if (use_grouped(T, desc->fmt_gate, desc->fmt_down)) return 7;
+  if (use_grouped(desc, T)) return 7;
   return gemv_hquant(desc->fmt_down, desc->ffn, desc->top_k, desc->sh_gate != nullptr) ? 4 : 3;
 }
 
@@ -495,7 +520,7 @@ moe_status moe_test_preact(const moe_layer_desc* desc, const moe_qact* xq, int T
   if (!qact_ok(desc, xq, T)) return MOE_EINVAL;
   if (!aligned(ids, 4) || !aligned(out, 16)) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
-  const bool g = use_grouped(T, desc->fmt_gate, desc->fmt_down);
+  const bool g = use_grouped(desc, T);
   const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
                                desc->sh_gate != nullptr, g);
   if (ws_bytes < L.total) return MOE_ENOWORKSPACE;

@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "../../include/moe.h"
+
 namespace moe {
 
 enum { FMT_Q4_K = 0, FMT_Q6_K = 1, FMT_MXFP4 = 2, FMT_Q5_K = 3, FMT_Q2_K = 4 };
@@ -125,7 +127,7 @@ bool gemv_fits(const KArgs& a);
 bool gemv_hquant(int fmt_down, int F, int k, int has_shared);
 
 // Which expert-FFN path a chunk of T tokens takes (fixed rule, see moe_api.cpp).
-bool use_grouped(int T, int fmt_gate, int fmt_down);
+bool use_grouped(const moe_layer_desc* d, int T);
 
 // Router split of the grouped path: K slices of `len` elements (multiple of 16).
 struct RouterSplit { int ks, len; };

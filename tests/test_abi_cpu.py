@@ -31,7 +31,7 @@ def test_library_exports_header_symbols():
 
 
 def test_version_and_status_strings():
-    assert M.moe_abi_version() == 1
+    assert M.moe_abi_version() == 2
     for s in range(5):
         assert M.moe_status_str(s)
     assert M.moe_status_str(99) == "unknown status"
@@ -169,39 +169,56 @@ def test_block_dots_validation():
 
 
 def test_stage_names_and_path_rule():
-    """Dispatch rule: chunks of <= 4 tokens, and any layer with an MXFP4 matrix,
-    take the per-pair GEMV path (3 kernels, or 4 when an MXFP4 down is too large
-    for the kernel that quantizes h itself: h then gets a kernel of its own);
-    larger K-quant chunks the grouped path (7 kernels)."""
-    d = good_desc()
-    for T in (1, 4):
-        assert M.moe_layer_stage_count(d, T) == 3
+    """Dispatch rule (moe_path AUTO): any layer with an MXFP4 (or Q5_K / Q2_K)
+    matrix takes the per-pair GEMV path (3 kernels, or 4 when an MXFP4 down is
+    too large for the kernel that quantizes h itself: h then gets a kernel of
+    its own); other layers take the grouped path (7 kernels) when an expert has
+    8 MB of blocks or more, or once T (k + shared) times the expert's block
+    bytes reaches 160 MB. GEMV / GROUPED force a path where the formats allow it."""
+    d = good_desc()  # Qwen3.6 shape without the shared expert: 8 x 1.77 MB per token
+    for T in (1, 4, 5, 11):
+        assert M.moe_layer_stage_count(d, T) == 3, T
         assert [M.moe_layer_stage_name(d, T, i) for i in range(3)] == ["router", "gateup", "down"]
-    for T in (5, 16, 256, 2048):
-        assert M.moe_layer_stage_count(d, T) == 7
+    for T in (12, 16, 256, 2048):
+        assert M.moe_layer_stage_count(d, T) == 7, T
     assert [M.moe_layer_stage_name(d, 16, i) for i in range(7)] == [
         "router", "topk", "bucket", "gateup", "hquant", "down", "combine"]
     assert M.moe_layer_stage_name(d, 1, 9) is None
     assert M.moe_layer_stage_count(d, 0) == 0
+    d.sh_gate, d.sh_up, d.sh_down = FAKE, FAKE + 256, FAKE + 512  # + shared: 9 slots
+    assert M.moe_layer_stage_count(d, 10) == 3 and M.moe_layer_stage_count(d, 11) == 7
+    d.path = M.MOE_PATH_GEMV
+    assert M.moe_layer_stage_count(d, 256) == 3
+    d.path = M.MOE_PATH_GROUPED
+    assert M.moe_layer_stage_count(d, 1) == 7 and M.moe_layer_stage_count(d, 2) == 7
+    d.path = 3
+    assert M.moe_layer_stage_count(d, 1) == 0 and M.moe_workspace_size(d, 1) == 0
+    # 16.3 MB DeepSeek-V4-Flash-shaped experts: grouped at every T (>= 8 MB)
+    q6 = good_desc(gen.CONFIGS["deepseek-v4-flash"])
+    for T in (1, 2, 16):
+        assert M.moe_layer_stage_count(q6, T) == 7
+    q6.path = M.MOE_PATH_GEMV
+    assert M.moe_layer_stage_count(q6, 1) == 3
     mx = good_desc(gen.CONFIGS["gpt-oss-20b"])
-    for T in (1, 16):
+    for T in (1, 16, 256):
         assert M.moe_layer_stage_count(mx, T) == 3
         assert [M.moe_layer_stage_name(mx, T, i) for i in range(3)] == [
             "router", "gateup", "down"]
+    mx.path = M.MOE_PATH_GROUPED  # no MXFP4 tile kernels: the GEMV path regardless
+    assert M.moe_layer_stage_count(mx, 16) == 3
     # nine slots of 2048-value h: their LDS images exceed the fused kernel's budget
     mx9 = good_desc(gen.CONFIGS["gpt-oss-20b"].with_(E=16, F=2048, k=9))
     assert M.moe_layer_stage_count(mx9, 1) == 4
     assert [M.moe_layer_stage_name(mx9, 1, i) for i in range(4)] == [
         "router", "gateup", "hquant", "down"]
-    q6 = good_desc(gen.CONFIGS["deepseek-v4-flash"])
-    assert M.moe_layer_stage_count(q6, 16) == 7
     # Q5_K and Q2_K layers (gate/up or down) take the GEMV path at every T
     for fg, fd in ((gen.Q5_K, gen.Q5_K), (gen.Q4_K, gen.Q5_K), (gen.Q5_K, gen.Q6_K),
                    (gen.Q2_K, gen.Q2_K), (gen.Q4_K, gen.Q2_K)):
         q5 = good_desc(gen.CONFIGS["deepseek-v4-flash"].with_(fmt_gu=fg, fmt_d=fd))
         assert M.moe_layer_stage_count(q5, 16) == 3
     # the grouped workspace holds the per-pair rows: it grows with T * k * H
-    assert M.moe_workspace_size(d, 5) > M.moe_workspace_size(d, 4) + 5 * 9 * 2048 * 4
+    d = good_desc()
+    assert M.moe_workspace_size(d, 12) > M.moe_workspace_size(d, 11) + 12 * 8 * 2048 * 4
 
 
 def test_tile_dots_validation():
@@ -252,6 +269,7 @@ def test_gemv_plan_rejects_rows_past_the_task_cap():
     blocks uncomputed."""
     cfg = gen.CONFIGS["tiny"].with_(H=33024, F=256, E=8, k=2)
     d = good_desc(cfg)
+    d.path = M.MOE_PATH_GEMV  # (the automatic rule sends 14 MB experts to the tiles)
     ws = M.moe_workspace_size(d, 1)
     assert ws > 0
     with pytest.raises(M.MoeError) as ei:
@@ -260,6 +278,7 @@ def test_gemv_plan_rejects_rows_past_the_task_cap():
     # and the down projection of a 129-super-block F row as well
     cfg = gen.CONFIGS["tiny"].with_(H=512, F=33024, E=8, k=2, fmt_d=gen.Q6_K)
     d = good_desc(cfg)
+    d.path = M.MOE_PATH_GEMV
     ws = M.moe_workspace_size(d, 1)
     with pytest.raises(M.MoeError) as ei:
         M.moe_layer_forward(d, FAKE, 0, 1, FAKE, None, None, FAKE, ws, stream=0)

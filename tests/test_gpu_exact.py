@@ -125,7 +125,7 @@ def integer_x(T, H, B, rng) -> np.ndarray:
 
 
 EXACT_CASES = [
-    # name, layer overrides, T (T >= 5 with K-quant matrices: the grouped path)
+    # name, layer overrides, T ("grouped" in the name: the expert-grouped path)
     ("q4k-gemv", dict(), 1),
     ("q4k-gemv-3tok", dict(), 3),
     ("q4k-grouped-ring", dict(), 7),
@@ -151,7 +151,8 @@ def test_preact_integer_exact(name, over, T):
     data = exact_layer(cfg, rng)
     present = np.ones(cfg.E, bool)
     present[cfg.E - 1] = False  # one expert not present: its rows stay untouched
-    dl = DeviceLayer(data, present=present)
+    path = M.MOE_PATH_GROUPED if "grouped" in name else M.MOE_PATH_GEMV
+    dl = DeviceLayer(data, present=present, path=path)
     B = 32 if cfg.fmt_gu == gen.MXFP4 else 256
     x = integer_x(T, cfg.H, B, rng)
     host, q, keep = upload_q8(x, B)

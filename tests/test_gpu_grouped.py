@@ -1,5 +1,7 @@
 """GPU parity of the expert-grouped (multi-token, int8 MFMA) path against the
-oracle: ids exact, outputs within 2e-3 of ||y||_2 per token. Covers experts
+oracle, the path forced with the descriptor's path field (the automatic rule
+picks it only past ~160 MB of per-pair expert bytes, which these shrunk shapes
+never reach): ids exact, outputs within 2e-3 of ||y||_2 per token. Covers experts
 with several 16-token tiles, ragged tiles, the dense k = E case, bf16 input,
 Q6_K down rows, the shared-expert gate vector, NULL experts, invalid ids,
 agreement with the per-pair decode path, and the full Kimi-K2-shaped
@@ -16,37 +18,38 @@ from tests.gpu_common import Y_TOL, check_layer, rel_err, run_layer, say
 from tests.shrunk import SHRUNK
 
 pytestmark = pytest.mark.gpu
+GP = M.MOE_PATH_GROUPED
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 5), ("tiny", 37), ("deepseek-v4-flash", 33),
                                     ("kimi-k2", 20), ("qwen3.6-35b-a3b", 18)])
 def test_grouped_shrunk(name, T):
     """Ragged tiles and experts with more than 16 routed tokens."""
-    check_layer(SHRUNK[name], T=T, x_index=T)
+    check_layer(SHRUNK[name], T=T, x_index=T, path=GP)
 
 
 def test_grouped_dense_k_equals_E():
     """Every token routed to every expert: each expert gets 40 pairs (3 tiles)."""
     cfg = gen.CONFIGS["tiny"].with_(k=8)
-    check_layer(cfg, T=40, x_index=1)
+    check_layer(cfg, T=40, x_index=1, path=GP)
 
 
 def test_grouped_biases():
     """Q4_K experts with gate/up/down biases (the register-staged tile kernels)
     and Q6_K gate/up rows."""
-    check_layer(SHRUNK["kimi-k2"].with_(biases=True), T=11, x_index=5)
-    check_layer(SHRUNK["deepseek-v4-flash"].with_(fmt_gu=gen.Q6_K), T=9, x_index=5)
+    check_layer(SHRUNK["kimi-k2"].with_(biases=True), T=11, x_index=5, path=GP)
+    check_layer(SHRUNK["deepseek-v4-flash"].with_(fmt_gu=gen.Q6_K), T=9, x_index=5, path=GP)
 
 
 def test_grouped_bf16_input():
     cfg = SHRUNK["kimi-k2"].with_(x_bf16=True)
-    check_layer(cfg, T=9, x_index=4)
+    check_layer(cfg, T=9, x_index=4, path=GP)
 
 
 def test_grouped_shared_gate_vector():
     cfg = SHRUNK["kimi-k2"]
     data = gen.make_layer(cfg, with_sh_gate_vec=True)
-    check_layer(cfg, data=data, T=21, sh_gate_vec=data.sh_gate_vec)
+    check_layer(cfg, data=data, T=21, sh_gate_vec=data.sh_gate_vec, path=GP)
 
 
 def test_grouped_null_experts_and_partition():
@@ -57,7 +60,7 @@ def test_grouped_null_experts_and_partition():
     mask = np.random.default_rng(11).random(cfg.E) < 0.5
     outs = []
     for present in (None, mask, ~mask):
-        dl = DeviceLayer(data, present=present)
+        dl = DeviceLayer(data, present=present, path=GP)
         xt, dt = x_to_device(data, x, xb)
         outs.append(run_layer(dl, xt, dt, T))
     (yf, idf, wf), (ya, ida, _), (yb, idb, _) = outs
@@ -74,7 +77,7 @@ def test_grouped_all_absent():
     T = 8
     x, xb = gen.make_x(cfg, T=T, x_index=2)
     none = np.zeros(cfg.E, bool)
-    dl = DeviceLayer(data, present=none)
+    dl = DeviceLayer(data, present=none, path=GP)
     xt, dt = x_to_device(data, x, xb)
     y, ids, _ = run_layer(dl, xt, dt, T)
     ref = oracle.Layer(data, present=none).forward(x, threads=8)
@@ -82,7 +85,7 @@ def test_grouped_all_absent():
     assert rel_err(y, ref["y"]).max() <= Y_TOL
     cfg2 = cfg.with_(shared=False)
     data2 = gen.make_layer(cfg2)
-    dl2 = DeviceLayer(data2, present=none)
+    dl2 = DeviceLayer(data2, present=none, path=GP)
     y2, _, _ = run_layer(dl2, xt, dt, T)
     assert not y2.any()
 
@@ -94,10 +97,11 @@ def test_grouped_matches_decode_path():
     data = gen.make_layer(cfg)
     T = 12
     x, xb = gen.make_x(cfg, T=T, x_index=9)
-    dl = DeviceLayer(data)
+    dl = DeviceLayer(data, path=GP)
+    dlp = DeviceLayer(data, path=M.MOE_PATH_GEMV)
     xt, dt = x_to_device(data, x, xb)
     yg, idg, wg = run_layer(dl, xt, dt, T)
-    parts = [run_layer(dl, xt[i:i + 4].contiguous(), dt, 4) for i in range(0, T, 4)]
+    parts = [run_layer(dlp, xt[i:i + 4].contiguous(), dt, 4) for i in range(0, T, 4)]
     yd = np.concatenate([p[0] for p in parts])
     idd = np.concatenate([p[1] for p in parts])
     wd = np.concatenate([p[2] for p in parts])
@@ -118,7 +122,7 @@ def test_grouped_expert_ffn_invalid_ids():
     bad = ids.copy()
     bad[:, 0] = -1
     bad[2, 1] = cfg.E
-    dl = DeviceLayer(data)
+    dl = DeviceLayer(data, path=GP)
     xt = torch.from_numpy(x).cuda()
     qs = torch.empty((T, cfg.H), dtype=torch.int8, device="cuda")
     d = torch.empty((T, cfg.H // 256), dtype=torch.float32, device="cuda")

@@ -85,15 +85,20 @@ def _routed_layer(cfg, T, x_index):
     return gen.make_layer(cfg, experts=sorted(used))
 
 
-@pytest.mark.parametrize("name,T", [("deepseek-v4-flash", 1), ("deepseek-v4-flash", 3),
-                                    ("kimi-k2", 1), ("kimi-k2", 2)])
-def test_layer_full_decode_routed(name, T):
-    """Full-size DeepSeek-V4-Flash and Kimi-K2 layers through the per-pair path
-    (chunks of <= 4 tokens): sigmoid routers (DeepSeek with selection bias), E =
-    384 (16 candidates per lane in the top-k), Q6_K down rows in registers and
-    Q4_K down rows through LDS at H = 7168."""
+@pytest.mark.parametrize("name,T,path", [
+    ("deepseek-v4-flash", 1, M.MOE_PATH_GEMV), ("deepseek-v4-flash", 3, M.MOE_PATH_GEMV),
+    ("deepseek-v4-flash", 1, M.MOE_PATH_AUTO), ("deepseek-v4-flash", 3, M.MOE_PATH_AUTO),
+    ("kimi-k2", 1, M.MOE_PATH_GEMV), ("kimi-k2", 2, M.MOE_PATH_GEMV),
+    ("kimi-k2", 1, M.MOE_PATH_AUTO), ("kimi-k2", 2, M.MOE_PATH_AUTO)])
+def test_layer_full_decode_routed(name, T, path):
+    """Full-size DeepSeek-V4-Flash and Kimi-K2 layers at one to three tokens:
+    the per-pair path (sigmoid routers, DeepSeek with selection bias; E = 384,
+    16 candidates per lane in the top-k; Q6_K down rows in registers and Q4_K
+    down rows through LDS at H = 7168), and the same small chunks on the path
+    the automatic rule picks for them (expert-grouped: their experts hold 8 MB
+    or more of blocks)."""
     cfg = gen.CONFIGS[name]
-    check_layer(cfg, data=_routed_layer(cfg, T, 30 + T), T=T, x_index=30 + T)
+    check_layer(cfg, data=_routed_layer(cfg, T, 30 + T), T=T, x_index=30 + T, path=path)
 
 
 def test_layer_full_verify_chunk_sampled():
@@ -102,7 +107,8 @@ def test_layer_full_verify_chunk_sampled():
     check_layer(gen.CONFIGS["deepseek-v4-flash"], tokens=range(16), threads=16)
 
 
-def test_expert_ffn_given_routing():
+@pytest.mark.parametrize("path", [M.MOE_PATH_GEMV, M.MOE_PATH_GROUPED])
+def test_expert_ffn_given_routing(path):
     cfg = SHRUNK["kimi-k2"]
     data = gen.make_layer(cfg)
     T = cfg.T
@@ -111,7 +117,7 @@ def test_expert_ffn_given_routing():
     ids = np.stack([rng.choice(cfg.E, cfg.k, replace=False) for _ in range(T)]).astype(np.int32)
     ids[0] = ids[1]  # tokens sharing experts
     w = rng.random((T, cfg.k)).astype(np.float32)
-    dl = DeviceLayer(data)
+    dl = DeviceLayer(data, path=path)
     qs = torch.empty((T, cfg.H), dtype=torch.int8, device="cuda")
     d = torch.empty((T, cfg.H // 256), dtype=torch.float32, device="cuda")
     bs = torch.empty((T, cfg.H // 16), dtype=torch.int16, device="cuda")
@@ -129,8 +135,10 @@ def test_expert_ffn_given_routing():
         assert rel_err(y[t].cpu().numpy(), ref) <= Y_TOL
 
 
-@pytest.mark.parametrize("name", ["qwen3.6-35b-a3b", "gpt-oss-20b", "deepseek-v4-flash"])
-def test_null_mask_partition(name):
+@pytest.mark.parametrize("name,path", [("qwen3.6-35b-a3b", 0), ("gpt-oss-20b", 0),
+                                       ("deepseek-v4-flash", 0),
+                                       ("deepseek-v4-flash", M.MOE_PATH_GROUPED)])
+def test_null_mask_partition(name, path):
     """Experts split over two 'devices' by NULL pointers: the partial outputs sum
     to the full output (the expert-parallel sharding pattern on one GPU)."""
     cfg = SHRUNK[name].with_(shared=False)
@@ -140,7 +148,7 @@ def test_null_mask_partition(name):
     mask = np.random.default_rng(7).random(cfg.E) < 0.5
     outs = []
     for present in (None, mask, ~mask):
-        dl = DeviceLayer(data, present=present)
+        dl = DeviceLayer(data, present=present, path=path)
         xt, dt = x_to_device(data, x, xb)
         outs.append(run_layer(dl, xt, dt, T))
     (yf, idf, wf), (ya, ida, wa), (yb, idb, wb) = outs
@@ -160,14 +168,14 @@ def test_shared_gate_vector():
 
 @pytest.mark.parametrize("name", ["deepseek-v4-flash", "gpt-oss-full", "qwen-q2k"])
 def test_determinism(name):
-    """Two runs give identical bytes: the grouped path (16-token chunk), the
+    """Two runs give identical bytes: the grouped path (5-token chunk), the
     MXFP4 realigned kernels at full width, the Q2_K GEMV kernels."""
     cfg = (gen.CONFIGS["gpt-oss-20b"] if name == "gpt-oss-full" else
            SHRUNK["qwen3.6-35b-a3b"].with_(fmt_gu=gen.Q2_K, fmt_d=gen.Q2_K) if name == "qwen-q2k"
            else SHRUNK[name])
     data = gen.make_layer(cfg)
     x, xb = gen.make_x(cfg, T=cfg.T)
-    dl = DeviceLayer(data)
+    dl = DeviceLayer(data, path=M.MOE_PATH_GROUPED if name == "deepseek-v4-flash" else 0)
     xt, dt = x_to_device(data, x, xb)
     a = run_layer(dl, xt, dt, cfg.T)
     b = run_layer(dl, xt, dt, cfg.T)
