@@ -18,10 +18,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoegen.so")
 _lib = None
 
-Q4_K, Q6_K, MXFP4, Q5_K, Q2_K = 0, 1, 2, 3, 4
-FMT_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", MXFP4: "MXFP4", Q5_K: "Q5_K", Q2_K: "Q2_K"}
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, MXFP4: 17, Q5_K: 176, Q2_K: 84}
-BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, MXFP4: 32, Q5_K: 256, Q2_K: 256}
+Q4_K, Q6_K, MXFP4, Q5_K, Q2_K, Q3_K, Q4_0, Q5_1 = 0, 1, 2, 3, 4, 5, 6, 7
+FMT_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", MXFP4: "MXFP4", Q5_K: "Q5_K", Q2_K: "Q2_K",
+             Q3_K: "Q3_K", Q4_0: "Q4_0", Q5_1: "Q5_1"}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, MXFP4: 17, Q5_K: 176, Q2_K: 84, Q3_K: 110, Q4_0: 18,
+               Q5_1: 24}
+BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, MXFP4: 32, Q5_K: 256, Q2_K: 256, Q3_K: 256, Q4_0: 32,
+               Q5_1: 32}
 
 T_ROUTER, T_X, T_GATE, T_UP, T_DOWN, T_BGATE, T_BUP, T_BDOWN, T_ZIPF, T_SHVEC = range(1, 11)
 
@@ -56,7 +59,7 @@ def lib():
         L.mg_fp16_ceil_bits.argtypes = [f64]
         L.mg_fp16_ceil_bits.restype = C.c_uint16
         for n in ("mg_encode_q4k", "mg_encode_q6k", "mg_encode_mxfp4", "mg_encode_q5k",
-                  "mg_encode_q2k"):
+                  "mg_encode_q2k", "mg_encode_q3k", "mg_encode_q40", "mg_encode_q51"):
             getattr(L, n).argtypes = [vp, vp]
         L.mg_encode_matrix.argtypes = [i32, vp, i32, i32, sz, vp, i32]
         L.mg_pack_q4k.argtypes = [C.c_uint16, C.c_uint16, vp, vp, vp, vp]
@@ -64,6 +67,9 @@ def lib():
         L.mg_pack_q5k.argtypes = [C.c_uint16, C.c_uint16, vp, vp, vp, vp]
         L.mg_pack_q2k.argtypes = [C.c_uint16, C.c_uint16, vp, vp, vp, vp]
         L.mg_pack_mxfp4.argtypes = [C.c_uint8, vp, vp]
+        L.mg_pack_q3k.argtypes = [C.c_uint16, vp, vp, vp]
+        L.mg_pack_q40.argtypes = [C.c_uint16, vp, vp]
+        L.mg_pack_q51.argtypes = [C.c_uint16, C.c_uint16, vp, vp]
         L.mg_weight_matrix.argtypes = [u64, u32, u32, i32, i32, i32, sz, f64, vp, i32]
         L.mg_zipf_bias.argtypes = [u64, i32, f64, vp]
         _lib = L
@@ -112,7 +118,8 @@ def encode_block(fmt: int, x: np.ndarray) -> np.ndarray:
     assert x.size == BLOCK_ELEMS[fmt]
     out = np.zeros(BLOCK_BYTES[fmt], dtype=np.uint8)
     fn = {Q4_K: "mg_encode_q4k", Q6_K: "mg_encode_q6k", MXFP4: "mg_encode_mxfp4",
-          Q5_K: "mg_encode_q5k", Q2_K: "mg_encode_q2k"}[fmt]
+          Q5_K: "mg_encode_q5k", Q2_K: "mg_encode_q2k", Q3_K: "mg_encode_q3k",
+          Q4_0: "mg_encode_q40", Q5_1: "mg_encode_q51"}[fmt]
     getattr(lib(), fn)(_ptr(x), _ptr(out))
     return out
 
@@ -169,6 +176,31 @@ def pack_q6k(d_bits: int, sc, q) -> np.ndarray:
     assert sc.size == 16 and q.size == 256
     out = np.zeros(210, dtype=np.uint8)
     lib().mg_pack_q6k(d_bits, _ptr(sc), _ptr(q), _ptr(out))
+    return out
+
+
+def pack_q3k(d_bits: int, sc, q) -> np.ndarray:
+    """sc: 16 stored 6-bit scales (0..63, used as sc - 32); q: 256 values in -4..3."""
+    sc = np.ascontiguousarray(sc, dtype=np.uint8); q = np.ascontiguousarray(q, dtype=np.int8)
+    assert sc.size == 16 and q.size == 256
+    out = np.zeros(110, dtype=np.uint8)
+    lib().mg_pack_q3k(d_bits, _ptr(sc), _ptr(q), _ptr(out))
+    return out
+
+
+def pack_q40(d_bits: int, q) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    assert q.size == 32
+    out = np.zeros(18, dtype=np.uint8)
+    lib().mg_pack_q40(d_bits, _ptr(q), _ptr(out))
+    return out
+
+
+def pack_q51(d_bits: int, m_bits: int, q) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    assert q.size == 32
+    out = np.zeros(24, dtype=np.uint8)
+    lib().mg_pack_q51(d_bits, m_bits, _ptr(q), _ptr(out))
     return out
 
 

@@ -131,9 +131,20 @@ static inline double rne(double v) {
 }
 
 size_t mg_block_bytes(int fmt) {
-  return fmt == MG_Q4_K ? 144 : fmt == MG_Q6_K ? 210 : fmt == MG_Q5_K ? 176 : fmt == MG_Q2_K ? 84 : 17;
+  switch (fmt) {
+    case MG_Q4_K: return 144;
+    case MG_Q6_K: return 210;
+    case MG_Q5_K: return 176;
+    case MG_Q2_K: return 84;
+    case MG_Q3_K: return 110;
+    case MG_Q4_0: return 18;
+    case MG_Q5_1: return 24;
+    default: return 17;
+  }
 }
-int mg_block_elems(int fmt) { return fmt == MG_MXFP4 ? 32 : 256; }
+int mg_block_elems(int fmt) {
+  return (fmt == MG_MXFP4 || fmt == MG_Q4_0 || fmt == MG_Q5_1) ? 32 : 256;
+}
 
 /* ---- packers ------------------------------------------------------------------ */
 void mg_pack_q4k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const uint8_t* m,
@@ -201,6 +212,51 @@ void mg_pack_q6k(uint16_t d_bits, const int8_t* sc, const uint8_t* q, uint8_t* b
   }
   memcpy(blk + 192, sc, 16);
   blk[208] = (uint8_t)d_bits; blk[209] = (uint8_t)(d_bits >> 8);
+}
+
+/* Q3_K (110 B): hmask[32] @0, qs[64] @32, scales[12] @96, fp16 d @108. Weight
+ * n = 128 h + 32 j + l (l < 32) keeps bits 0..1 of q + 4 in bits 2j..2j+1 of
+ * qs[32 h + l] and bit 2 of q + 4 in bit 4h + j of hmask[l]. The 6-bit value
+ * of sub-block s (n / 16) keeps its low 4 bits in byte s mod 8 of scales (low
+ * nibble for s < 8, high nibble for s >= 8) and its top 2 bits in bits
+ * 2 (s / 4).. of scales[8 + s mod 4]. q in -4..3, sc in 0..63. */
+void mg_pack_q3k(uint16_t d_bits, const uint8_t* sc, const int8_t* q, uint8_t* blk) {
+  memset(blk, 0, 110);
+  for (int n = 0; n < 256; ++n) {
+    int h = n / 128, r = n % 128, j = r / 32, l = r % 32;
+    int u = q[n] + 4;
+    blk[32 + 32 * h + l] |= (uint8_t)((u & 3) << (2 * j));
+    blk[l] |= (uint8_t)((u >> 2) << (4 * h + j));
+  }
+  for (int s2 = 0; s2 < 16; ++s2) {
+    int lo = sc[s2] & 15, hi = sc[s2] >> 4;
+    blk[96 + s2 % 8] |= (uint8_t)(s2 < 8 ? lo : lo << 4);
+    blk[104 + s2 % 4] |= (uint8_t)(hi << (2 * (s2 / 4)));
+  }
+  blk[108] = (uint8_t)(d_bits & 0xFF);
+  blk[109] = (uint8_t)(d_bits >> 8);
+}
+
+/* Q4_0 (18 B): fp16 d @0, qs[16] @2; byte j holds element j (low nibble) and
+ * element j + 16 (high nibble); q in 0..15. */
+void mg_pack_q40(uint16_t d_bits, const uint8_t* q, uint8_t* blk) {
+  blk[0] = (uint8_t)(d_bits & 0xFF);
+  blk[1] = (uint8_t)(d_bits >> 8);
+  for (int j = 0; j < 16; ++j) blk[2 + j] = (uint8_t)((q[j] & 15) | ((q[j + 16] & 15) << 4));
+}
+
+/* Q5_1 (24 B): fp16 d @0, fp16 m @2, qh (32 bits, little-endian) @4, qs[16] @8;
+ * bit j of qh is the fifth bit of element j; byte j of qs holds the low 4 bits
+ * of element j (low nibble) and of element j + 16 (high nibble); q in 0..31. */
+void mg_pack_q51(uint16_t d_bits, uint16_t m_bits, const uint8_t* q, uint8_t* blk) {
+  uint32_t qh = 0;
+  for (int j = 0; j < 32; ++j) qh |= (uint32_t)((q[j] >> 4) & 1) << j;
+  blk[0] = (uint8_t)(d_bits & 0xFF);
+  blk[1] = (uint8_t)(d_bits >> 8);
+  blk[2] = (uint8_t)(m_bits & 0xFF);
+  blk[3] = (uint8_t)(m_bits >> 8);
+  for (int i = 0; i < 4; ++i) blk[4 + i] = (uint8_t)(qh >> (8 * i));
+  for (int j = 0; j < 16; ++j) blk[8 + j] = (uint8_t)((q[j] & 15) | ((q[j + 16] & 15) << 4));
 }
 
 void mg_pack_mxfp4(uint8_t e, const uint8_t* codes, uint8_t* blk) {
@@ -346,6 +402,86 @@ void mg_encode_q6k(const float* x, uint8_t* blk) {
   mg_pack_q6k(d_bits, sc, q, blk);
 }
 
+/* Q3_K: 16 sub-blocks of 16 with a signed scale (stored + 32) and q in -4..3.
+ * Covering: need_s = max(max x / 3, -min x / 4, 0); d = fp16_ceil(max need / 31);
+ * c_s = ceil(need_s / d) <= 31; every x of the sub-block lies in [-4 d c_s,
+ * 3 d c_s], so |x - x^| <= d c_s / 2. */
+void mg_encode_q3k(const float* x, uint8_t* blk) {
+  double need[16], maxneed = 0.0;
+  for (int s2 = 0; s2 < 16; ++s2) {
+    double lo = 0.0, hi = 0.0;
+    for (int i = 0; i < 16; ++i) {
+      double v = x[16 * s2 + i];
+      if (v < lo) lo = v;
+      if (v > hi) hi = v;
+    }
+    need[s2] = hi / 3.0 > -lo / 4.0 ? hi / 3.0 : -lo / 4.0;
+    if (need[s2] > maxneed) maxneed = need[s2];
+  }
+  uint16_t d_bits = mg_fp16_ceil_bits(maxneed / 31.0);
+  double d = fp16_value(d_bits);
+  uint8_t sc[16];
+  int8_t q[256];
+  for (int s2 = 0; s2 < 16; ++s2) {
+    double c = d > 0.0 ? ceil(need[s2] / d) : 0.0;
+    if (c > 31.0) c = 31.0;
+    sc[s2] = (uint8_t)(c + 32.0);
+    double shat = d * c;
+    for (int i = 0; i < 16; ++i) {
+      double v = shat > 0.0 ? rne((double)x[16 * s2 + i] / shat) : 0.0;
+      if (v < -4.0) v = -4.0;
+      if (v > 3.0) v = 3.0;
+      q[16 * s2 + i] = (int8_t)v;
+    }
+  }
+  mg_pack_q3k(d_bits, sc, q, blk);
+}
+
+/* Q4_0: d = fp16_ceil(max(max x / 7, -min x / 8, 0)), q = clamp(rne(x / d), -8, 7)
+ * + 8; every x lies in [-8 d, 7 d], so |x - x^| <= d / 2. */
+void mg_encode_q40(const float* x, uint8_t* blk) {
+  double lo = 0.0, hi = 0.0;
+  for (int i = 0; i < 32; ++i) {
+    if (x[i] < lo) lo = x[i];
+    if (x[i] > hi) hi = x[i];
+  }
+  double need = hi / 7.0 > -lo / 8.0 ? hi / 7.0 : -lo / 8.0;
+  uint16_t d_bits = mg_fp16_ceil_bits(need);
+  double d = fp16_value(d_bits);
+  uint8_t q[32];
+  for (int i = 0; i < 32; ++i) {
+    double v = d > 0.0 ? rne((double)x[i] / d) : 0.0;
+    if (v < -8.0) v = -8.0;
+    if (v > 7.0) v = 7.0;
+    q[i] = (uint8_t)(v + 8.0);
+  }
+  mg_pack_q40(d_bits, q, blk);
+}
+
+/* Q5_1: m = -fp16_ceil(-min x) (0 when min x >= 0), d = fp16_ceil((max x - m) / 31),
+ * q = clamp(rne((x - m) / d), 0, 31); every x lies in [m, m + 31 d], so
+ * |x - x^| <= d / 2. */
+void mg_encode_q51(const float* x, uint8_t* blk) {
+  double lo = 0.0, hi = 0.0;
+  for (int i = 0; i < 32; ++i) {
+    if (x[i] < lo) lo = x[i];
+    if (x[i] > hi) hi = x[i];
+  }
+  uint16_t mneg = mg_fp16_ceil_bits(-lo);  /* lo <= 0 */
+  double m = -fp16_value(mneg);
+  uint16_t m_bits = (uint16_t)(mneg ? (mneg | 0x8000) : 0);
+  uint16_t d_bits = mg_fp16_ceil_bits((hi - m) / 31.0);
+  double d = fp16_value(d_bits);
+  uint8_t q[32];
+  for (int i = 0; i < 32; ++i) {
+    double v = d > 0.0 ? rne(((double)x[i] - m) / d) : 0.0;
+    if (v < 0.0) v = 0.0;
+    if (v > 31.0) v = 31.0;
+    q[i] = (uint8_t)v;
+  }
+  mg_pack_q51(d_bits, m_bits, q, blk);
+}
+
 /* OCP MX v1.0: shared exponent floor(log2 amax) - emax(e2m1 = 2); elements rounded
  * to nearest on the e2m1 grid, ties to the even mantissa, saturating at 6. */
 void mg_encode_mxfp4(const float* x, uint8_t* blk) {
@@ -395,6 +531,9 @@ static void enc_rows(void* p, int r0, int r1) {
       else if (c->fmt == MG_Q5_K) mg_encode_q5k(xr + b * be, row + b * bb);
       else if (c->fmt == MG_Q2_K) mg_encode_q2k(xr + b * be, row + b * bb);
       else if (c->fmt == MG_Q6_K) mg_encode_q6k(xr + b * be, row + b * bb);
+      else if (c->fmt == MG_Q3_K) mg_encode_q3k(xr + b * be, row + b * bb);
+      else if (c->fmt == MG_Q4_0) mg_encode_q40(xr + b * be, row + b * bb);
+      else if (c->fmt == MG_Q5_1) mg_encode_q51(xr + b * be, row + b * bb);
       else mg_encode_mxfp4(xr + b * be, row + b * bb);
     }
     memset(row + nb * bb, 0, c->stride - nb * bb);

@@ -20,6 +20,8 @@
  *         fp16 d @208.
  *   MXFP4 17 B / 32 weights: E8M0 scale byte @0, 16 B of e2m1 nibbles @1
  *         (OCP Microscaling Formats v1.0).
+ *   Q5_K 176 B, Q2_K 84 B, Q3_K 110 B (256 weights), Q4_0 18 B and Q5_1 24 B
+ *         (32 weights): see the packers in moegen.c.
  */
 #ifndef MOEGEN_H
 #define MOEGEN_H
@@ -31,7 +33,8 @@
 extern "C" {
 #endif
 
-enum { MG_Q4_K = 0, MG_Q6_K = 1, MG_MXFP4 = 2, MG_Q5_K = 3, MG_Q2_K = 4 };
+enum { MG_Q4_K = 0, MG_Q6_K = 1, MG_MXFP4 = 2, MG_Q5_K = 3, MG_Q2_K = 4, MG_Q3_K = 5,
+       MG_Q4_0 = 6, MG_Q5_1 = 7 };
 
 /* Tensor identifiers that key the random streams. */
 enum {
@@ -61,6 +64,9 @@ void mg_encode_q5k(const float* x, uint8_t* blk);
 void mg_encode_q2k(const float* x, uint8_t* blk);
 void mg_encode_q6k(const float* x, uint8_t* blk);
 void mg_encode_mxfp4(const float* x, uint8_t* blk);
+void mg_encode_q3k(const float* x, uint8_t* blk);
+void mg_encode_q40(const float* x, uint8_t* blk);
+void mg_encode_q51(const float* x, uint8_t* blk);
 /* Encode a [rows x K] fp32 matrix into block rows at byte stride `stride`
  * (padding bytes are zeroed). K must be a multiple of the block size. */
 void mg_encode_matrix(int fmt, const float* x, int rows, int K, size_t stride, uint8_t* out,
@@ -80,6 +86,9 @@ void mg_pack_q2k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const u
 void mg_pack_q5k(uint16_t d_bits, uint16_t dmin_bits, const uint8_t* sc, const uint8_t* m,
                  const uint8_t* q, uint8_t* blk);
 void mg_pack_mxfp4(uint8_t e, const uint8_t* codes, uint8_t* blk);
+void mg_pack_q3k(uint16_t d_bits, const uint8_t* sc, const int8_t* q, uint8_t* blk);
+void mg_pack_q40(uint16_t d_bits, const uint8_t* q, uint8_t* blk);
+void mg_pack_q51(uint16_t d_bits, uint16_t m_bits, const uint8_t* q, uint8_t* blk);
 
 size_t mg_block_bytes(int fmt);
 int mg_block_elems(int fmt);

@@ -17,11 +17,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-Q4_K, Q6_K, MXFP4, Q5_K, Q2_K = 0, 1, 2, 3, 4
+Q4_K, Q6_K, MXFP4, Q5_K, Q2_K, Q3_K, Q4_0, Q5_1 = 0, 1, 2, 3, 4, 5, 6, 7
 SOFTMAX, SIGMOID = 0, 1
 SWIGLU, SWIGLU_OAI = 0, 1
-BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, MXFP4: 32, Q5_K: 256, Q2_K: 256}
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, MXFP4: 17, Q5_K: 176, Q2_K: 84}
+BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, MXFP4: 32, Q5_K: 256, Q2_K: 256, Q3_K: 256, Q4_0: 32,
+               Q5_1: 32}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, MXFP4: 17, Q5_K: 176, Q2_K: 84, Q3_K: 110, Q4_0: 18,
+               Q5_1: 24}
 
 
 def build(verbose: bool = False) -> str:

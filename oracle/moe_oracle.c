@@ -35,10 +35,24 @@ double or_e2m1(uint8_t code) {
   return s ? -v : v;
 }
 
-int or_block_elems(int fmt) { return fmt == OR_MXFP4 ? 32 : 256; }
-int or_block_bytes(int fmt) {
-  return fmt == OR_Q4_K ? 144 : fmt == OR_Q6_K ? 210 : fmt == OR_Q5_K ? 176 : fmt == OR_Q2_K ? 84 : 17;
+int or_block_elems(int fmt) {
+  return (fmt == OR_MXFP4 || fmt == OR_Q4_0 || fmt == OR_Q5_1) ? 32 : 256;
 }
+int or_block_bytes(int fmt) {
+  switch (fmt) {
+    case OR_Q4_K: return 144;
+    case OR_Q6_K: return 210;
+    case OR_Q5_K: return 176;
+    case OR_Q2_K: return 84;
+    case OR_Q3_K: return 110;
+    case OR_Q4_0: return 18;
+    case OR_Q5_1: return 24;
+    default: return 17;
+  }
+}
+/* Activation quant block for rows of this format: q8 blocks of 32 for the
+ * 32-weight formats, of 256 (with 16-element sums) for the 256-weight ones. */
+int or_act_block(int fmt) { return or_block_elems(fmt) == 32 ? 32 : 256; }
 
 static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
@@ -58,8 +72,44 @@ static void q4k_scales(const uint8_t* blk, int* sc, int* m) {
   }
 }
 
+/* Q3_K's sixteen 6-bit sub-block scales (used as sc - 32): sub-block s takes
+ * its low 4 bits from byte s mod 8 of the 12 scale bytes (at byte 96; the low
+ * nibble for s < 8, the high nibble for s >= 8) and its top 2 bits from bits
+ * 2 (s / 4).. of scale byte 8 + s mod 4. */
+static void q3k_scales(const uint8_t* blk, int* sc) {
+  const uint8_t* s = blk + 96;
+  for (int i = 0; i < 16; ++i) {
+    int lo = i < 8 ? (s[i % 8] & 15) : (s[i % 8] >> 4);
+    int hi = (s[8 + i % 4] >> (2 * (i / 4))) & 3;
+    sc[i] = lo | (hi << 4);
+  }
+}
+
 void or_block_quants(int fmt, const uint8_t* blk, int32_t* q) {
-  if (fmt == OR_Q4_K) {
+  if (fmt == OR_Q3_K) {
+    /* halves of 128: weight 32j + l (l < 32) of half h has its low 2 bits in
+     * bits 2j..2j+1 of qs[32h + l] (qs at byte 32) and its high bit in bit
+     * 4h + j of hmask[l] (byte l); q = low + 4 * high - 4, in -4..3 */
+    const uint8_t* hm = blk;
+    const uint8_t* qs = blk + 32;
+    for (int n = 0; n < 256; ++n) {
+      int h = n / 128, r = n % 128, j = r / 32, l = r % 32;
+      int lo = (qs[32 * h + l] >> (2 * j)) & 3;
+      int hi = (hm[l] >> (4 * h + j)) & 1;
+      q[n] = lo + 4 * hi - 4;
+    }
+  } else if (fmt == OR_Q4_0 || fmt == OR_Q5_1) {
+    /* byte j of the nibbles holds element j (low) and element j + 16 (high);
+     * Q5_1 adds bit j of its 32-bit qh (byte 4) as the fifth bit of element j */
+    const uint8_t* qs = blk + (fmt == OR_Q4_0 ? 2 : 8);
+    uint32_t qh = 0;
+    if (fmt == OR_Q5_1) qh = (uint32_t)blk[4] | ((uint32_t)blk[5] << 8) |
+                             ((uint32_t)blk[6] << 16) | ((uint32_t)blk[7] << 24);
+    for (int n = 0; n < 32; ++n) {
+      int lo = n < 16 ? (qs[n] & 15) : (qs[n - 16] >> 4);
+      q[n] = lo | (int)(((qh >> n) & 1) << 4);
+    }
+  } else if (fmt == OR_Q4_K) {
     /* 4 chunks of 64 weights over 32 quant bytes each: byte i of chunk c holds
      * weight 64c+i in its low nibble and weight 64c+32+i in its high nibble. */
     const uint8_t* qs = blk + 16;
@@ -126,6 +176,17 @@ void or_dequant_block(int fmt, const uint8_t* blk, double* out) {
     double d = or_fp16(rd16(blk + 208));
     const int8_t* sc = (const int8_t*)(blk + 192);
     for (int n = 0; n < 256; ++n) out[n] = d * sc[n / 16] * (q[n] - 32);
+  } else if (fmt == OR_Q3_K) {
+    double d = or_fp16(rd16(blk + 108));
+    int sc[16];
+    q3k_scales(blk, sc);
+    for (int n = 0; n < 256; ++n) out[n] = d * (sc[n / 16] - 32) * q[n];
+  } else if (fmt == OR_Q4_0) {
+    double d = or_fp16(rd16(blk));
+    for (int n = 0; n < 32; ++n) out[n] = d * (q[n] - 8);
+  } else if (fmt == OR_Q5_1) {
+    double d = or_fp16(rd16(blk)), m = or_fp16(rd16(blk + 2));
+    for (int n = 0; n < 32; ++n) out[n] = d * q[n] + m;
   } else {
     double s = or_e8m0(blk[0]);
     for (int n = 0; n < 32; ++n) out[n] = s * 0.5 * q[n];
@@ -214,6 +275,33 @@ void or_block_partials(int fmt, const uint8_t* row, int K, const int8_t* qs,
       }
       out[2 * b] = (int32_t)S;
       out[2 * b + 1] = 0;
+    } else if (fmt == OR_Q3_K) {
+      /* S = sum over sub-blocks of 16 of (sc_s - 32) * (dot of signed q with a) */
+      int sc[16];
+      q3k_scales(blk, sc);
+      int64_t S = 0;
+      for (int s = 0; s < 16; ++s) {
+        int64_t dot = 0;
+        for (int i = 0; i < 16; ++i) dot += (int64_t)q[16 * s + i] * a[16 * s + i];
+        S += (int64_t)(sc[s] - 32) * dot;
+      }
+      out[2 * b] = (int32_t)S;
+      out[2 * b + 1] = 0;
+    } else if (fmt == OR_Q4_0) {
+      /* S = sum of (q - 8) * a */
+      int64_t S = 0;
+      for (int i = 0; i < 32; ++i) S += (int64_t)(q[i] - 8) * a[i];
+      out[2 * b] = (int32_t)S;
+      out[2 * b + 1] = 0;
+    } else if (fmt == OR_Q5_1) {
+      /* S1 = sum of q * a, S2 = sum of a (the min term) */
+      int64_t S1 = 0, S2 = 0;
+      for (int i = 0; i < 32; ++i) {
+        S1 += (int64_t)q[i] * a[i];
+        S2 += a[i];
+      }
+      out[2 * b] = (int32_t)S1;
+      out[2 * b + 1] = (int32_t)S2;
     } else {
       int64_t S = 0;
       for (int i = 0; i < 32; ++i) S += (int64_t)q[i] * a[i];
@@ -232,6 +320,12 @@ double or_block_value(int fmt, const uint8_t* blk, const int32_t* p, float d8) {
     return (double)d8 * (d * p[0] - dmin * p[1]);
   } else if (fmt == OR_Q6_K) {
     return (double)d8 * or_fp16(rd16(blk + 208)) * p[0];
+  } else if (fmt == OR_Q3_K) {
+    return (double)d8 * or_fp16(rd16(blk + 108)) * p[0];
+  } else if (fmt == OR_Q4_0) {
+    return (double)d8 * or_fp16(rd16(blk)) * p[0];
+  } else if (fmt == OR_Q5_1) {
+    return (double)d8 * (or_fp16(rd16(blk)) * p[0] + or_fp16(rd16(blk + 2)) * p[1]);
   }
   /* e2m1 = k/2, so value = d8 * 2^(e-127) * S/2 */
   return (double)d8 * or_e8m0(blk[0]) * 0.5 * p[0];
@@ -322,7 +416,7 @@ void or_expert_ffn(const or_layer* L, const uint8_t* gate, const uint8_t* up,
                    const int8_t* xq, const float* xd, const int16_t* xbs, double* out,
                    float* h32) {
   const int H = L->H, F = L->F;
-  const int Bh = L->fmt_down == OR_MXFP4 ? 32 : 256;
+  const int Bh = or_act_block(L->fmt_down);
   float* h = (float*)malloc(sizeof(float) * (size_t)F);
   int8_t* hq = (int8_t*)malloc((size_t)F);
   float* hd = (float*)malloc(sizeof(float) * (size_t)(F / 32));
@@ -346,7 +440,7 @@ void or_expert_ffn(const or_layer* L, const uint8_t* gate, const uint8_t* up,
 
 typedef struct { int8_t* q; float* d; int16_t* bs; } q8buf;
 static q8buf q8_of(const or_layer* L, const float* x) {
-  const int Bx = L->fmt_gate == OR_MXFP4 ? 32 : 256;
+  const int Bx = or_act_block(L->fmt_gate);
   q8buf b;
   b.q = (int8_t*)malloc((size_t)L->H);
   b.d = (float*)malloc(sizeof(float) * (size_t)(L->H / 32));

@@ -21,7 +21,10 @@
  * the remaining weights are not renormalized.
  *
  * Block layouts are the ggml/GGUF conventions (the pages name the formats
- * only): Q4_K 144 B / 256, Q6_K 210 B / 256, MXFP4 17 B / 32 (OCP MX v1.0).
+ * only): Q4_K 144 B / 256, Q6_K 210 B / 256, MXFP4 17 B / 32 (OCP MX v1.0);
+ * further formats the pages list: Q5_K 176 B, Q2_K 84 B, Q3_K 110 B (256
+ * weights), Q4_0 18 B, Q5_1 24 B (32 weights). Rows of 32-weight formats
+ * consume q8 activations in blocks of 32, the others in blocks of 256.
  * GGUF byte-level interoperability is parity unpinned: no GGUF file or
  * reference decoder is available to check against.
  */
@@ -35,7 +38,8 @@
 extern "C" {
 #endif
 
-enum { OR_Q4_K = 0, OR_Q6_K = 1, OR_MXFP4 = 2, OR_Q5_K = 3, OR_Q2_K = 4 };
+enum { OR_Q4_K = 0, OR_Q6_K = 1, OR_MXFP4 = 2, OR_Q5_K = 3, OR_Q2_K = 4, OR_Q3_K = 5,
+       OR_Q4_0 = 6, OR_Q5_1 = 7 };
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 enum { OR_SWIGLU = 0, OR_SWIGLU_OAI = 1 };
 
@@ -47,7 +51,10 @@ double or_e2m1(uint8_t code);       /* OCP FP4 E2M1 value of a 4-bit code */
 /* ---- block formats ---- */
 int or_block_elems(int fmt);
 int or_block_bytes(int fmt);
-/* Raw integer quants of one block: Q4_K 0..15, Q6_K 0..63, MXFP4 2*e2m1 (signed). */
+/* q8 block size of the activations that rows of this format consume (32 or 256). */
+int or_act_block(int fmt);
+/* Raw integer quants of one block: Q4_K 0..15, Q5_K 0..31, Q6_K 0..63, Q2_K 0..3,
+ * Q3_K -4..3, Q4_0 0..15, Q5_1 0..31, MXFP4 2*e2m1 (signed). */
 void or_block_quants(int fmt, const uint8_t* blk, int32_t* q);
 /* Dequantize one block / one row of K values to fp64. */
 void or_dequant_block(int fmt, const uint8_t* blk, double* out);
@@ -63,7 +70,11 @@ void or_quantize_q8(const float* x, int n, int B, int8_t* qs, float* d, int16_t*
  * out[2b], out[2b+1] for block b:
  *   Q4_K : S1 = sum_j sc_j * dot_j,  S2 = sum_j m_j * (bsums[2j] + bsums[2j+1])
  *   Q6_K : S  = sum_s sc_s * (dot_s - 32 * bsums[s]),       second value 0
- *   MXFP4: S  = sum_i k_i * a_i with k = 2 * e2m1,          second value 0 */
+ *   MXFP4: S  = sum_i k_i * a_i with k = 2 * e2m1,          second value 0
+ *   Q5_K and Q2_K as Q4_K (sub-blocks of 32 and 16)
+ *   Q3_K : S  = sum_s (sc_s - 32) * dot_s (q in -4..3),     second value 0
+ *   Q4_0 : S  = sum_i (q_i - 8) * a_i,                      second value 0
+ *   Q5_1 : S1 = sum_i q_i * a_i,  S2 = sum_i a_i */
 void or_block_partials(int fmt, const uint8_t* row, int K, const int8_t* qs,
                        const int16_t* bsums, int32_t* out);
 /* fp64 value of one block from its partials and scales. */

@@ -5,6 +5,8 @@ numpy; routing uses numpy's lexsort and torch's softmax/sigmoid. Only the two
 separately pinned oracle primitives are reused: block dequantization and the
 q8 activation recipe."""
 import numpy as np
+
+import gen
 import torch
 
 import oracle
@@ -42,8 +44,8 @@ def brute_layer(data, x, present=None, route_scale=None, sh_gate_vec=None, dense
     present = np.ones(E, bool) if present is None else present
     rs = cfg.route_scale if route_scale is None else route_scale
     sb = data.sel_bias if isinstance(sel_bias, str) else sel_bias
-    Bx = 32 if cfg.fmt_gu == 2 else 256
-    Bh = 32 if cfg.fmt_d == 2 else 256
+    Bx = 32 if gen.BLOCK_ELEMS[cfg.fmt_gu] == 32 else 256
+    Bh = 32 if gen.BLOCK_ELEMS[cfg.fmt_d] == 32 else 256
     if dense is None:
         dense = dense_experts(data, range(cfg.n_pool))
     ys, idss, ws = [], [], []

@@ -88,7 +88,8 @@ def test_pool_layout_and_subset(genlib):
 
 
 @pytest.mark.parametrize("fmt,K", [(gen.Q4_K, 512), (gen.Q6_K, 256), (gen.MXFP4, 96),
-                                   (gen.Q5_K, 512), (gen.Q2_K, 512)])
+                                   (gen.Q5_K, 512), (gen.Q2_K, 512), (gen.Q3_K, 512),
+                                   (gen.Q4_0, 96), (gen.Q5_1, 96)])
 def test_encode_matrix_padding(genlib, fmt, K):
     x = gen.normal(0, 1, 0, 3, K, 0.02)
     stride = gen.row_stride(fmt, K) + 32

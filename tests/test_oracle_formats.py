@@ -141,6 +141,101 @@ def test_mxfp4_byte_layout(orc):
     assert np.array_equal(orc.block_quants(oracle.MXFP4, blk), want.astype(np.int64))
 
 
+def test_q3k_byte_layout(orc):
+    """A Q3_K block written byte by byte: hmask[32] at 0, qs[64] at 32, twelve
+    scale bytes at 96, fp16 d at 108. Weight 128h + 32j + l (l < 32) has its low
+    2 bits in bits 2j..2j+1 of qs[32h + l] and its high bit in bit 4h + j of
+    hmask[l]; q = low + 4 * high - 4. Sub-block s has a 6-bit scale whose low 4
+    bits are the low (s < 8) or high (s >= 8) nibble of scale byte s mod 8 and
+    whose top 2 bits are bits 2 (s / 4).. of scale byte 8 + s mod 4;
+    w = d * (scale - 32) * q."""
+    blk = np.zeros(110, np.uint8)
+    blk[0:32] = 0xFF                      # every high bit set: q = low bits
+    blk[108:110] = [0x00, 0x38]           # d = 0.5
+    blk[96 + 0] = 0x01                    # scale 0 low bits 1 (scale 8 low bits 0)
+    blk[96 + 1] = 0x80                    # scale 9 low bits 8 (high nibble)
+    blk[96 + 7] = 0xF0                    # scale 15 low bits 15 (high nibble)
+    blk[104:108] = [0xAA, 0xAA, 0xAA, 0xEA]  # top bits 2 for all, 3 for scale 15
+    blk[32 + 0] = 0x03                    # weight 0 (h 0, j 0, l 0): low bits 3
+    blk[32 + 32 + 22] = 0x01              # weight 150 (h 1, j 0, l 22): low bits 1 ...
+    blk[22] = 0xEF                        # ... high bit (bit 4) cleared: q = 1 - 4
+    blk[32 + 32 + 31] = 0x80              # weight 255 (h 1, j 3, l 31): low bits 2
+    q = np.zeros(256, np.int64)
+    q[[0, 150, 255]] = [3, -3, 2]
+    assert np.array_equal(orc.block_quants(oracle.Q3_K, blk), q)
+    sc = np.full(16, 32)
+    sc[0], sc[9], sc[15] = 33, 40, 63
+    want = np.array([0.5 * (sc[n // 16] - 32) * q[n] for n in range(256)])
+    assert want[0] == 1.5 and want[150] == -12.0 and want[255] == 31.0
+    assert np.array_equal(orc.dequant_row(oracle.Q3_K, blk, 256), want)
+
+
+def test_q40_byte_layout(orc):
+    """A Q4_0 block written byte by byte: fp16 d at 0, 16 nibble bytes at 2;
+    byte j holds element j (low nibble) and element j + 16 (high nibble);
+    w = d * (q - 8)."""
+    blk = np.full(18, 0x88, np.uint8)     # every q = 8: w = 0
+    blk[0:2] = [0x00, 0x34]               # d = 0.25
+    blk[2 + 0] = 0x8F                     # element 0: 15; element 16: 8
+    blk[2 + 15] = 0x08                    # element 15: 8; element 31: 0
+    blk[2 + 5] = 0x38                     # element 5: 8; element 21: 3
+    q = np.full(32, 8, np.int64)
+    q[[0, 31, 21]] = [15, 0, 3]
+    assert np.array_equal(orc.block_quants(oracle.Q4_0, blk), q)
+    want = 0.25 * (q - 8).astype(np.float64)
+    assert want[0] == 1.75 and want[31] == -2.0 and want[21] == -1.25
+    assert np.array_equal(orc.dequant_row(oracle.Q4_0, blk, 32), want)
+
+
+def test_q51_byte_layout(orc):
+    """A Q5_1 block written byte by byte: fp16 d at 0, fp16 m at 2, 32-bit qh
+    (little-endian) at 4, 16 nibble bytes at 8; bit j of qh is the fifth bit of
+    element j; byte j holds the low 4 bits of element j (low nibble) and of
+    element j + 16 (high nibble); w = d * q + m."""
+    blk = np.zeros(24, np.uint8)
+    blk[0:2] = [0x00, 0x38]               # d = 0.5
+    blk[2:4] = [0x00, 0xBC]               # m = -1.0
+    blk[4:8] = [0x01, 0x02, 0x00, 0x80]   # fifth bits of elements 0, 9 and 31
+    blk[8 + 0] = 0x25                     # element 0: 5 (+16); element 16: 2
+    blk[8 + 15] = 0xF0                    # element 15: 0; element 31: 15 (+16)
+    q = np.zeros(32, np.int64)
+    q[[0, 16, 31, 9]] = [21, 2, 31, 16]
+    assert np.array_equal(orc.block_quants(oracle.Q5_1, blk), q)
+    want = 0.5 * q.astype(np.float64) - 1.0
+    assert want[0] == 9.5 and want[16] == 0.0 and want[31] == 14.5 and want[9] == 7.0
+    assert np.array_equal(orc.dequant_row(oracle.Q5_1, blk, 32), want)
+
+
+def test_q3k_hand_packed_fields(orc, genlib):
+    rng = np.random.default_rng(6)
+    for trial in range(50):
+        sc = rng.integers(0, 64, 16).astype(np.uint8)
+        q = rng.integers(-4, 4, 256).astype(np.int8)
+        d_bits = int(rng.integers(0x0400, 0x3C00))
+        blk = gen.pack_q3k(d_bits, sc, q)
+        d = float(np.array([d_bits], np.uint16).view(np.float16)[0])
+        assert np.array_equal(orc.block_quants(oracle.Q3_K, blk), q)
+        want = np.array([d * (int(sc[n // 16]) - 32) * int(q[n]) for n in range(256)])
+        assert np.array_equal(orc.dequant_row(oracle.Q3_K, blk, 256), want)
+
+
+def test_q40_q51_hand_packed_fields(orc, genlib):
+    rng = np.random.default_rng(7)
+    for trial in range(50):
+        d_bits = int(rng.integers(0x0400, 0x3C00))
+        m_bits = int(rng.integers(0x0400, 0x3C00)) | (0x8000 if trial % 2 else 0)
+        d = float(np.array([d_bits], np.uint16).view(np.float16)[0])
+        m = float(np.array([m_bits], np.uint16).view(np.float16)[0])
+        q4 = rng.integers(0, 16, 32).astype(np.uint8)
+        b4 = gen.pack_q40(d_bits, q4)
+        assert np.array_equal(orc.block_quants(oracle.Q4_0, b4), q4)
+        assert np.array_equal(orc.dequant_row(oracle.Q4_0, b4, 32), d * (q4.astype(np.float64) - 8))
+        q5 = rng.integers(0, 32, 32).astype(np.uint8)
+        b5 = gen.pack_q51(d_bits, m_bits, q5)
+        assert np.array_equal(orc.block_quants(oracle.Q5_1, b5), q5)
+        assert np.array_equal(orc.dequant_row(oracle.Q5_1, b5, 32), d * q5.astype(np.float64) + m)
+
+
 def test_q5k_hand_packed_fields(orc, genlib):
     rng = np.random.default_rng(3)
     for trial in range(50):
@@ -323,6 +418,43 @@ def test_q6k_round_trip_bound(orc, genlib, std):
             xs = x[r, 16 * s:16 * s + 16].astype(np.float64)
             need = max(xs.max() / 31, -xs.min() / 32, 0)
             assert step <= need + d * (1 + 1e-12)  # covering step is the smallest that fits
+
+
+@pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])
+def test_q3k_round_trip_bound(orc, genlib, std):
+    x = _blocks(gen.Q3_K, 300, std, 16)
+    for r in range(x.shape[0]):
+        blk = gen.encode_block(gen.Q3_K, x[r])
+        xh = orc.dequant_row(oracle.Q3_K, blk, 256)
+        d = orc.fp16(int(blk[108]) | int(blk[109]) << 8)
+        q = orc.block_quants(oracle.Q3_K, blk)
+        err = np.abs(x[r].astype(np.float64) - xh)
+        for s2 in range(16):
+            xs = x[r, 16 * s2:16 * s2 + 16].astype(np.float64)
+            need = max(xs.max() / 3, -xs.min() / 4, 0)
+            # the covering step lies in [need, need + d] and the error is half a step
+            assert err[16 * s2:16 * s2 + 16].max() <= (need + d) / 2 * (1 + 1e-9) + 1e-300
+        assert q.min() >= -4 and q.max() <= 3
+
+
+@pytest.mark.parametrize("fmt", [gen.Q4_0, gen.Q5_1])
+@pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])
+def test_q40_q51_round_trip_bound(orc, genlib, fmt, std):
+    x = _blocks(fmt, 600, std, 17 + fmt)
+    for r in range(x.shape[0]):
+        blk = gen.encode_block(fmt, x[r])
+        xh = orc.dequant_row(fmt, blk, 32)
+        d = orc.fp16(int(blk[0]) | int(blk[1]) << 8)
+        err = np.abs(x[r].astype(np.float64) - xh)
+        assert err.max() <= d / 2 * (1 + 1e-12) + 1e-300, r
+        xs = x[r].astype(np.float64)
+        if fmt == gen.Q4_0:
+            need = max(xs.max() / 7, -xs.min() / 8, 0)
+        else:
+            m = orc.fp16(int(blk[2]) | int(blk[3]) << 8)
+            assert m <= min(xs.min(), 0)
+            need = (max(xs.max(), 0) - m) / 31
+        assert d <= need * (1 + 2 ** -10) + 2 ** -24  # the smallest fp16 step that covers
 
 
 @pytest.mark.parametrize("std", [0.02, 1.0, 1e-4])

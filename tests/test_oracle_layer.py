@@ -26,6 +26,23 @@ def test_layer_matches_dense_brute_force(orc, genlib, name):
         assert _rel(out["y"][t], yb[t]) <= 1e-9, (name, t)
 
 
+@pytest.mark.parametrize("fmt_gu,fmt_d", [(gen.Q3_K, gen.Q3_K), (gen.Q4_0, gen.Q4_0),
+                                          (gen.Q5_1, gen.Q5_1), (gen.Q4_0, gen.Q3_K),
+                                          (gen.Q3_K, gen.Q5_1), (gen.Q4_K, gen.Q4_0)])
+def test_layer_formats_match_dense_brute_force(orc, genlib, fmt_gu, fmt_d):
+    """Layers with Q3_K, Q4_0 and Q5_1 matrices (and mixes): the oracle equals a
+    brute-force fp64 FFN on the dequantized matrices, with q8 blocks of 32 for
+    the 32-weight formats."""
+    cfg = SHRUNK["qwen3.6-35b-a3b"].with_(fmt_gu=fmt_gu, fmt_d=fmt_d)
+    data = gen.make_layer(cfg)
+    x, _ = gen.make_x(cfg, T=cfg.T, x_index=1)
+    ref = oracle.Layer(data).forward(x)
+    yb, idb, wb = brute_layer(data, x)
+    assert np.array_equal(ref["ids"], idb)
+    for t in range(cfg.T):
+        assert np.abs(ref["y"][t] - yb[t]).max() <= 1e-9 * np.linalg.norm(yb[t])
+
+
 def test_shared_gate_vector_brute_force(orc, genlib):
     cfg = SHRUNK["qwen3.6-35b-a3b"]
     data = gen.make_layer(cfg, with_sh_gate_vec=True)

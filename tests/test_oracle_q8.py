@@ -71,10 +71,11 @@ def _rand_act(K, seed):
 
 
 @pytest.mark.parametrize("fmt,K", [(gen.Q4_K, 1024), (gen.Q6_K, 1024), (gen.MXFP4, 1024),
-                                   (gen.Q5_K, 1024), (gen.Q2_K, 1024)])
+                                   (gen.Q5_K, 1024), (gen.Q2_K, 1024), (gen.Q3_K, 1024),
+                                   (gen.Q4_0, 1024), (gen.Q5_1, 1024)])
 def test_block_dot_identity(orc, genlib, fmt, K):
     """Integer factorization == fp64 dot of fully dequantized weights and activations."""
-    B = 32 if fmt == gen.MXFP4 else 256
+    B = 32 if gen.BLOCK_ELEMS[fmt] == 32 else 256
     w = gen.normal(3, gen.T_GATE, fmt, 40, K, 0.02)
     w[0] = 0
     w[1] = np.abs(w[1])
@@ -126,3 +127,11 @@ def test_partial_ranges_fit_int32(orc, genlib):
     bm = gen.pack_mxfp4(127, np.full(32, 7))
     p = orc.block_partials(oracle.MXFP4, bm, 32, qs32, None)
     assert p[0, 0] == 12 * 127 * 32
+    b3 = gen.pack_q3k(0x3C00, np.zeros(16, np.uint8), np.full(256, -4, np.int8))
+    p = orc.block_partials(oracle.Q3_K, b3, 256, qs, bs)
+    assert p[0, 0] == -32 * -4 * 127 * 256
+    p = orc.block_partials(oracle.Q4_0, gen.pack_q40(0x3C00, np.zeros(32)), 32, qs32, None)
+    assert p[0, 0] == -8 * 127 * 32
+    p = orc.block_partials(oracle.Q5_1, gen.pack_q51(0x3C00, 0x3C00, np.full(32, 31)), 32, qs32,
+                           None)
+    assert p[0, 0] == 31 * 127 * 32 and p[0, 1] == 127 * 32
