@@ -65,17 +65,24 @@ typedef enum {
  * Q4_K 144 B / 256 weights, Q6_K 210 B / 256, MXFP4 17 B / 32, Q5_K 176 B / 256
  * (Q4_K's fp16 d, dmin and 6-bit scales, 32 B of fifth bits, 128 B of nibbles),
  * Q2_K 84 B / 256 (16 scale/min nibble pairs, 64 B of 2-bit quants, fp16 d,
- * dmin). Layers with a Q5_K or Q2_K matrix take the per-(token, slot) GEMV path
- * for every T. */
+ * dmin), Q3_K 110 B / 256 (32 B of high bits, 64 B of 2-bit quants, 12 B of
+ * 6-bit scales, fp16 d), Q4_0 18 B / 32 (fp16 d, 16 B of nibbles) and Q5_1
+ * 24 B / 32 (fp16 d and m, 32 fifth bits, 16 B of nibbles). Layers with a
+ * matrix in any format other than Q4_K and Q6_K take the per-(token, slot)
+ * GEMV path for every T. */
 typedef enum {
   MOE_WFMT_Q4_K = 0,
   MOE_WFMT_Q6_K = 1,
   MOE_WFMT_MXFP4 = 2,
   MOE_WFMT_Q5_K = 3,
-  MOE_WFMT_Q2_K = 4
+  MOE_WFMT_Q2_K = 4,
+  MOE_WFMT_Q3_K = 5,
+  MOE_WFMT_Q4_0 = 6,
+  MOE_WFMT_Q5_1 = 7
 } moe_wfmt;
 /* Activation quant formats: Q8_K = blocks of 256 with 16-element sums
- * (consumed by Q4_K, Q5_K, Q2_K and Q6_K rows); Q8_32 = blocks of 32 (MXFP4 rows). */
+ * (consumed by Q4_K, Q5_K, Q2_K, Q3_K and Q6_K rows); Q8_32 = blocks of 32
+ * (MXFP4, Q4_0 and Q5_1 rows). */
 typedef enum { MOE_AFMT_Q8_K = 0, MOE_AFMT_Q8_32 = 1 } moe_afmt;
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 } moe_router;
@@ -83,7 +90,7 @@ typedef enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 } moe_router;
  * u' = clamp(u, -limit, limit), h = g' * sigmoid(alpha * g') * (u' + 1). */
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
 /* Expert-FFN path of a chunk. AUTO: layers with a matrix in a format without
- * tile kernels (MXFP4, Q5_K, Q2_K) take the per-(token, slot) GEMV path; the
+ * tile kernels (all but Q4_K and Q6_K) take the per-(token, slot) GEMV path; the
  * others take the expert-grouped int8-MFMA path when one expert's block bytes
  * reach 8 MB, or when T * (k + shared) * (block bytes of one expert) reaches
  * 160 MB, else the GEMV path (the measured crossover: the grouped path reads
@@ -260,6 +267,9 @@ MOE_API const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int 
  *   Q4_K, Q5_K, Q2_K: (S1, S2) with S1 = sum_j sc_j * dot_j, S2 = sum_j m_j * (activation sums of sub-block j)
  *   Q6_K : (S, 0)   with S  = sum_s sc_s * sum_i (q_i - 32) * a_i
  *   MXFP4: (S, 0)   with S  = sum_i (2 * e2m1_i) * a_i
+ *   Q3_K : (S, 0)   with S  = sum_s (sc_s - 32) * sum_i q_i * a_i, q in -4..3
+ *   Q4_0 : (S, 0)   with S  = sum_i (q_i - 8) * a_i
+ *   Q5_1 : (S1, S2) with S1 = sum_i q_i * a_i, S2 = sum_i a_i
  * Errors: MOE_EINVAL for a bad format, pointer, width, stride or token.
  * Source: Pulsar README, numerics notes (activations quantized to q8_0/q8_K,
  * integer dp4a dots, rescaled per quant block). */

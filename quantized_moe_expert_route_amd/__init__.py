@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_route.so")
 
 # enums (include/moe.h)
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOWORKSPACE, MOE_EHIP = range(5)
-MOE_WFMT_Q4_K, MOE_WFMT_Q6_K, MOE_WFMT_MXFP4, MOE_WFMT_Q5_K, MOE_WFMT_Q2_K = range(5)
+(MOE_WFMT_Q4_K, MOE_WFMT_Q6_K, MOE_WFMT_MXFP4, MOE_WFMT_Q5_K, MOE_WFMT_Q2_K, MOE_WFMT_Q3_K,
+ MOE_WFMT_Q4_0, MOE_WFMT_Q5_1) = range(8)
 MOE_AFMT_Q8_K, MOE_AFMT_Q8_32 = range(2)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = range(2)
 MOE_ROUTER_SOFTMAX, MOE_ROUTER_SIGMOID = range(2)

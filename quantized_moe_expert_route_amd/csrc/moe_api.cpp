@@ -24,10 +24,22 @@ namespace {
 
 constexpr int kMaxTokens = 2048;
 
-int block_elems(int fmt) { return fmt == FMT_MXFP4 ? 32 : 256; }
+bool known_fmt(int fmt) { return fmt >= MOE_WFMT_Q4_K && fmt <= MOE_WFMT_Q5_1; }
+int block_elems(int fmt) { return act32(fmt) ? 32 : 256; }
 size_t block_bytes(int fmt) {
-  return fmt == FMT_Q4_K ? 144 : fmt == FMT_Q6_K ? 210 : fmt == FMT_Q5_K ? 176 : fmt == FMT_Q2_K ? 84 : 17;
+  switch (fmt) {
+    case FMT_Q4_K: return 144;
+    case FMT_Q6_K: return 210;
+    case FMT_MXFP4: return 17;
+    case FMT_Q5_K: return 176;
+    case FMT_Q2_K: return 84;
+    case FMT_Q3_K: return 110;
+    case FMT_Q4_0: return 18;
+    default: return 24;  // Q5_1
+  }
 }
+// q8 format of the activations that rows of a weight format consume
+int act_fmt(int fmt) { return act32(fmt) ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K; }
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -43,9 +55,7 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_GEMV && d->path != MOE_PATH_GROUPED)
     return MOE_EINVAL;
   for (int f : {d->fmt_gate, d->fmt_up, d->fmt_down})
-    if (f != MOE_WFMT_Q4_K && f != MOE_WFMT_Q6_K && f != MOE_WFMT_MXFP4 && f != MOE_WFMT_Q5_K &&
-        f != MOE_WFMT_Q2_K)
-      return MOE_EINVAL;
+    if (!known_fmt(f)) return MOE_EINVAL;
   if (d->fmt_gate != d->fmt_up) return MOE_EUNSUPPORTED;
   if (H % block_elems(d->fmt_gate) != 0 || H % 32 != 0) return MOE_EINVAL;
   if (F % block_elems(d->fmt_down) != 0 || F % 32 != 0) return MOE_EINVAL;
@@ -307,7 +317,7 @@ static moe_status expert_ffn_impl(KArgs& a, bool grouped, bool routing_given, hi
 
 // q8 of x as the layer's gate/up rows consume it, for T tokens.
 static bool qact_ok(const moe_layer_desc* desc, const moe_qact* xq, int T) {
-  const int want_afmt = desc->fmt_gate == MOE_WFMT_MXFP4 ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K;
+  const int want_afmt = act_fmt(desc->fmt_gate);
   if (xq->fmt != want_afmt || xq->T < T || xq->H != desc->hidden) return false;
   if (!xq->qs || !xq->d || !aligned(xq->qs, 16) || !aligned(xq->d, 4)) return false;
   if (want_afmt == MOE_AFMT_Q8_K && (!xq->bsums || !aligned(xq->bsums, 4))) return false;
@@ -466,14 +476,12 @@ const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {
 
 moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,
                                const moe_qact* xq, int token, int32_t* out, hipStream_t stream) {
-  if (fmt != MOE_WFMT_Q4_K && fmt != MOE_WFMT_Q6_K && fmt != MOE_WFMT_MXFP4 && fmt != MOE_WFMT_Q5_K &&
-      fmt != MOE_WFMT_Q2_K)
-    return MOE_EINVAL;
+  if (!known_fmt(fmt)) return MOE_EINVAL;
   if (!rows || !aligned(rows, 16) || !out || !xq || n_rows < 0 || K <= 0) return MOE_EINVAL;
   if (K % block_elems(fmt) != 0) return MOE_EINVAL;
   const size_t rb = static_cast<size_t>(K / block_elems(fmt)) * block_bytes(fmt);
   if (stride < rb || stride % 16) return MOE_EINVAL;
-  const int want = fmt == MOE_WFMT_MXFP4 ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K;
+  const int want = act_fmt(fmt);
   if (xq->fmt != want || xq->H != K || token < 0 || token >= xq->T) return MOE_EINVAL;
   if (!xq->qs || !xq->d || (want == MOE_AFMT_Q8_K && !xq->bsums)) return MOE_EINVAL;
   if (n_rows == 0) return MOE_OK;

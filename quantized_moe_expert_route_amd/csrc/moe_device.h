@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -600,12 +602,143 @@ struct FmtMXFP4 {
   }
 };
 
+// Q3_K (110 B): hmask[32] @0, qs[64] @32, 12 scale bytes @96, fp16 d @108.
+// Weight 128h + 32j + l has low bits 2j..2j+1 of qs[32h + l] and high bit
+// 4h + j of hmask[l]; q = low + 4 high - 4 in -4..3. Sub-block s (16
+// weights) has a 6-bit scale (used as sc - 32): low 4 bits in scale byte
+// s mod 8 (low nibble for s < 8, high for s >= 8), top 2 bits at 2 (s / 4) of
+// scale byte 8 + s mod 4. Lane `sub` (half h = sub / 4, k = sub % 4) takes
+// weights 128h + 32j + 8k + i (j < 4, i < 8): qs[32h + 8k ..] and hmask[8k ..]
+// (8 bytes each), one sub-block per j.
+struct FmtQ3K {
+  static constexpr int BE = 256, BB = 110, LPB = 8;
+  struct Raw { uint2 q, hm; uint32_t sc[3]; uint32_t dbits; };
+  __device__ static __forceinline__ void load(Raw& r, const uint8_t* blk, int sub) {
+    const int h = sub >> 2, k = sub & 3;
+    r.q = load8_unaligned(blk + 32 + 32 * h + 8 * k);
+    r.hm = load8_unaligned(blk + 8 * k);
+    const uint2 s01 = load8_unaligned(blk + 96);
+    r.sc[0] = s01.x; r.sc[1] = s01.y;
+    const uint2 s2d = load8_unaligned(blk + 102);  // bytes 102..109: scale bytes 8..11, d
+    r.sc[2] = (s2d.x >> 16) | (s2d.y << 16);
+    r.dbits = s2d.y >> 16;
+  }
+  __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int sub) {
+    const int h = sub >> 2, k = sub & 3;
+    const int8_t* ab = a.qs + b * 256 + 128 * h + 8 * k;
+    int S = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // q + 4 per byte: low 2 bits | high bit << 2, then - 4 without carries
+      const uint32_t hb = 4 * h + j;
+      uint32_t w0 = ((r.q.x >> (2 * j)) & 0x03030303u) | (((r.hm.x >> hb) & 0x01010101u) << 2);
+      uint32_t w1 = ((r.q.y >> (2 * j)) & 0x03030303u) | (((r.hm.y >> hb) & 0x01010101u) << 2);
+      w0 = ((w0 | 0x80808080u) - 0x04040404u) ^ 0x80808080u;
+      w1 = ((w1 | 0x80808080u) - 0x04040404u) ^ 0x80808080u;
+      const int2 av = *reinterpret_cast<const int2*>(ab + 32 * j);
+      int dot = sdot4(static_cast<int>(w0), av.x, 0);
+      dot = sdot4(static_cast<int>(w1), av.y, dot);
+      const int s = 8 * h + 2 * j + (k >> 1);  // sub-block
+      const uint32_t lw = r.sc[(s & 7) >> 2];
+      const int lo = ((lw >> (8 * (s & 3))) >> (s >= 8 ? 4 : 0)) & 15;
+      const int hi = (r.sc[2] >> (8 * (s & 3) + 2 * (s >> 2))) & 3;
+      S += ((lo | (hi << 4)) - 32) * dot;
+    }
+    return make_int2(sum8(S), 0);
+  }
+  __device__ static __forceinline__ float value(const Raw& r, int2 p, float d8) {
+    return d8 * half_bits_to_f32(r.dbits) * static_cast<float>(p.x);
+  }
+};
+
+// Bits 0..3 of v spread to bit 0 of bytes 0..3 (the four shifted copies of
+// the 4-bit value do not overlap, so the product is a plain OR of them).
+__device__ __forceinline__ uint32_t spread4(uint32_t v) {
+  return ((v & 0xFu) * 0x00204081u) & 0x01010101u;
+}
+
+// Q4_0 (18 B: fp16 d, 16 bytes of nibbles; byte j = element j low, j + 16
+// high; w = d (q - 8)) and Q5_1 (24 B: fp16 d, fp16 m, 32-bit qh whose bit j is
+// element j's fifth bit, 16 nibble bytes; w = d q + m), against q8 activations
+// in blocks of 32 (int8 quants, one scale per block). One lane per block.
+struct FmtQ40 {
+  static constexpr int BE = 32, BB = 18, LPB = 1;
+  // Five dwords from the aligned one holding byte 0 (blocks are 2-byte
+  // aligned, sh = 0 or 2): each starts inside the block.
+  struct Raw { uint32_t w[5]; uint32_t sh; };
+  __device__ static __forceinline__ void load(Raw& r, const uint8_t* blk, int) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(blk);
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(a & ~static_cast<uintptr_t>(3));
+    r.sh = static_cast<uint32_t>(a & 3);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) r.w[i] = ld_nt4(p + 4 * i);
+  }
+  // nibble bytes 4i..4i+3 (block bytes 2 + 4i ..)
+  __device__ static __forceinline__ uint32_t nib(const Raw& r, int i) {
+    return r.sh == 2 ? r.w[i + 1] : __builtin_amdgcn_alignbyte(r.w[i + 1], r.w[i], 2);
+  }
+  __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int) {
+    const int4* ax = reinterpret_cast<const int4*>(a.qs + b * 32);
+    const int4 alo = ax[0], ahi = ax[1];
+    const int al[4] = {alo.x, alo.y, alo.z, alo.w}, ah[4] = {ahi.x, ahi.y, ahi.z, ahi.w};
+    int S = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t nb = nib(r, i);
+      uint32_t lo = nb & 0x0F0F0F0Fu, hi = (nb >> 4) & 0x0F0F0F0Fu;
+      lo = ((lo | 0x80808080u) - 0x08080808u) ^ 0x80808080u;  // q - 8 per byte
+      hi = ((hi | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
+      S = sdot4(static_cast<int>(lo), al[i], S);
+      S = sdot4(static_cast<int>(hi), ah[i], S);
+    }
+    return make_int2(S, 0);
+  }
+  __device__ static __forceinline__ float value(const Raw& r, int2 p, float d8) {
+    return d8 * half_bits_to_f32((r.w[0] >> (8 * r.sh)) & 0xFFFF) * static_cast<float>(p.x);
+  }
+};
+
+struct FmtQ51 {
+  static constexpr int BE = 32, BB = 24, LPB = 1;
+  struct Raw { uint32_t dm, qh, q[4]; };  // blocks are 4-byte aligned
+  __device__ static __forceinline__ void load(Raw& r, const uint8_t* blk, int) {
+    const uint2 a = make_uint2(ld_nt4(blk), ld_nt4(blk + 4));
+    r.dm = a.x;
+    r.qh = a.y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.q[i] = ld_nt4(blk + 8 + 4 * i);
+  }
+  __device__ static __forceinline__ int2 partials(const Raw& r, const ActView& a, int b, int) {
+    const int4* ax = reinterpret_cast<const int4*>(a.qs + b * 32);
+    const int4 alo = ax[0], ahi = ax[1];
+    const int al[4] = {alo.x, alo.y, alo.z, alo.w}, ah[4] = {ahi.x, ahi.y, ahi.z, ahi.w};
+    int S1 = 0, S2 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (r.q[i] & 0x0F0F0F0Fu) | (spread4(r.qh >> (4 * i)) << 4);
+      const uint32_t hi = ((r.q[i] >> 4) & 0x0F0F0F0Fu) | (spread4(r.qh >> (16 + 4 * i)) << 4);
+      S1 = sdot4(static_cast<int>(lo), al[i], S1);
+      S1 = sdot4(static_cast<int>(hi), ah[i], S1);
+      S2 = sdot4(0x01010101, al[i], S2);
+      S2 = sdot4(0x01010101, ah[i], S2);
+    }
+    return make_int2(S1, S2);
+  }
+  __device__ static __forceinline__ float value(const Raw& r, int2 p, float d8) {
+    const float d = half_bits_to_f32(r.dm & 0xFFFF), m = half_bits_to_f32(r.dm >> 16);
+    return d8 * (d * static_cast<float>(p.x) + m * static_cast<float>(p.y));
+  }
+};
+
 template <int FMT> struct FmtOf;
 template <> struct FmtOf<FMT_Q4_K> { using T = FmtQ4K; };
 template <> struct FmtOf<FMT_Q6_K> { using T = FmtQ6K; };
 template <> struct FmtOf<FMT_MXFP4> { using T = FmtMXFP4; };
 template <> struct FmtOf<FMT_Q5_K> { using T = FmtQ5K; };
 template <> struct FmtOf<FMT_Q2_K> { using T = FmtQ2K; };
+template <> struct FmtOf<FMT_Q3_K> { using T = FmtQ3K; };
+template <> struct FmtOf<FMT_Q4_0> { using T = FmtQ40; };
+template <> struct FmtOf<FMT_Q5_1> { using T = FmtQ51; };
 
 // ------------------------------------------------------- MXFP4 decode GEMV
 // A 17-byte block has no fixed alignment, so one lane per block would need five
@@ -745,25 +878,38 @@ __device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, i
 template <class F>
 __device__ __forceinline__ float block_value(const typename F::Raw& r, const ActView& a, int b,
                                              int sub) {
-  if constexpr (F::LPB == 1) {
+  if constexpr (std::is_same<F, FmtMXFP4>::value) {
     return F::value_from_dot(r, F::dot(r, a, b), a.d[b]);
   } else {
     return F::value(r, F::partials(r, a, b, sub), a.d[b]);
   }
 }
 
+// Activation layouts in LDS: q8_K (int8, scale per 256, 16-element sums),
+// fp16 pairs of q8_32 (MXFP4 rows) and int8 q8_32 (Q4_0 and Q5_1 rows).
+enum { ACT_Q8K = 0, ACT_PAIRS = 1, ACT_I8_32 = 2 };
+template <int FMT>
+struct ActMode {
+  static constexpr int v = FMT == FMT_MXFP4 ? ACT_PAIRS
+                           : (FMT == FMT_Q4_0 || FMT == FMT_Q5_1) ? ACT_I8_32 : ACT_Q8K;
+};
+
 // Stage q8 activations (global, one token) into LDS in the layout the format reads.
-template <int AFMT_MX>
+template <int MODE>
 __device__ __forceinline__ void stage_act(const int8_t* qs, const float* d, const int16_t* bs,
                                           int K, int8_t* lqs, float* ld, int16_t* lbs,
                                           half2_t* lap) {
   const int tid = threadIdx.x, nt = blockDim.x;
-  if constexpr (!AFMT_MX) {
+  if constexpr (MODE == ACT_Q8K) {
     for (int i = tid; i < K / 16; i += nt) {
       reinterpret_cast<int4*>(lqs)[i] = reinterpret_cast<const int4*>(qs)[i];
       lbs[i] = bs[i];
     }
     for (int i = tid; i < K / 256; i += nt) ld[i] = d[i];
+  } else if constexpr (MODE == ACT_I8_32) {
+    for (int i = tid; i < K / 16; i += nt)
+      reinterpret_cast<int4*>(lqs)[i] = reinterpret_cast<const int4*>(qs)[i];
+    for (int i = tid; i < K / 32; i += nt) ld[i] = d[i];
   } else {
     for (int i = tid; i < K / 2; i += nt) {  // block-major, padded (see ActView)
       const int b = i / 16, ii = i % 16;

@@ -11,7 +11,15 @@
 
 namespace moe {
 
-enum { FMT_Q4_K = 0, FMT_Q6_K = 1, FMT_MXFP4 = 2, FMT_Q5_K = 3, FMT_Q2_K = 4 };
+enum { FMT_Q4_K = 0, FMT_Q6_K = 1, FMT_MXFP4 = 2, FMT_Q5_K = 3, FMT_Q2_K = 4, FMT_Q3_K = 5,
+       FMT_Q4_0 = 6, FMT_Q5_1 = 7 };
+
+// Rows of 32-weight formats consume q8 activations in blocks of 32 (MXFP4 as
+// fp16 pairs inside its kernels, Q4_0 and Q5_1 as int8); the others blocks of
+// 256 with 16-element sums.
+__host__ __device__ inline bool act32(int fmt) {
+  return fmt == FMT_MXFP4 || fmt == FMT_Q4_0 || fmt == FMT_Q5_1;
+}
 
 // Activation codes beyond moe_act, used only by the test export of the gate/up
 // pre-activations: the gate/up kernels then store g (or u) where h would go.

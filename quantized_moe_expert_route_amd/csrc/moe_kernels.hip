@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64) void k_router(KArgs a, int quant, int n_clear) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = valid ? v[i] : 0.0f;
     const size_t base = static_cast<size_t>(t) * a.H + pc * 256;
-    if (a.fmt_gu == FMT_MXFP4)
+    if (act32(a.fmt_gu))
       quant_wave<32>(v, valid, lane, a.xqs + base, a.xd + base / 32, nullptr);
     else
       quant_wave<256>(v, valid, lane, a.xqs + base, a.xd + base / 256, a.xbs + base / 16);
@@ -200,6 +200,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
                                                 Div dR) {
   using F = typename FmtOf<FMT>::T;
   constexpr bool MX = FMT == FMT_MXFP4;
+  constexpr bool I32 = ActMode<FMT>::v == ACT_I8_32;  // int8 q8_32 (no 16-element sums)
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_e;
   __shared__ int s_ids[16];
@@ -252,9 +253,9 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
     const int tid = threadIdx.x;
     if (tid < K / 16) {
       pre_q = reinterpret_cast<const int4*>(a.xqs + static_cast<size_t>(t) * K)[tid];
-      pre_bs = a.xbs[static_cast<size_t>(t) * (K / 16) + tid];
+      if constexpr (!I32) pre_bs = a.xbs[static_cast<size_t>(t) * (K / 16) + tid];
     }
-    if (tid < K / 256) pre_d = a.xd[static_cast<size_t>(t) * (K / 256) + tid];
+    if (tid < K / F::BE) pre_d = a.xd[static_cast<size_t>(t) * (K / F::BE) + tid];
   }
   // The selection runs on one wave, chosen by the workgroup's place among
   // those resident on a compute unit (dispatch order: 256 per round), so that
@@ -321,23 +322,22 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
     __builtin_amdgcn_s_setprio(0);
   }
   if constexpr (MX) {
-    stage_act<true>(a.xqs + static_cast<size_t>(t) * K, a.xd + static_cast<size_t>(t) * (K / 32),
-                    nullptr, K, lqs, ld, lbs, lap);
+    stage_act<ACT_PAIRS>(a.xqs + static_cast<size_t>(t) * K,
+                         a.xd + static_cast<size_t>(t) * (K / 32), nullptr, K, lqs, ld, lbs, lap);
   } else {
     const int tid = threadIdx.x;
     const int8_t* qs = a.xqs + static_cast<size_t>(t) * K;
-    const int16_t* bs = a.xbs + static_cast<size_t>(t) * (K / 16);
-    const float* dd = a.xd + static_cast<size_t>(t) * (K / 256);
+    const float* dd = a.xd + static_cast<size_t>(t) * (K / F::BE);
     if (tid < K / 16) {
       reinterpret_cast<int4*>(lqs)[tid] = pre_q;
-      lbs[tid] = pre_bs;
+      if constexpr (!I32) lbs[tid] = pre_bs;
     }
-    if (tid < K / 256) ld[tid] = pre_d;
+    if (tid < K / F::BE) ld[tid] = pre_d;
     for (int i = tid + 256; i < K / 16; i += 256) {
       reinterpret_cast<int4*>(lqs)[i] = reinterpret_cast<const int4*>(qs)[i];
-      lbs[i] = bs[i];
+      if constexpr (!I32) lbs[i] = a.xbs[static_cast<size_t>(t) * (K / 16) + i];
     }
-    for (int i = tid + 256; i < K / 256; i += 256) ld[i] = dd[i];
+    for (int i = tid + 256; i < K / F::BE; i += 256) ld[i] = dd[i];
   }
   __syncthreads();
   const float* bg = nullptr;
@@ -623,7 +623,7 @@ template <int FMT, int TPG, int JB, bool PRE>
 __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, Div dpc) {
   using F = typename FmtOf<FMT>::T;
   constexpr bool MX = FMT == FMT_MXFP4;
-  constexpr int B = MX ? 32 : 256;
+  constexpr int B = F::BE == 32 ? 32 : 256;  // q8 block of h
   extern __shared__ __align__(16) unsigned char smem[];
   const int t = blockIdx.y, row0 = blockIdx.x * R;
   const int K = a.F, nb = K / F::BE;
@@ -729,7 +729,7 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
       const float v[4] = {hv1.x, hv1.y, hv1.z, hv1.w};
       if constexpr (!MX) {
         quant_wave<B>(v, valid, lane, reinterpret_cast<int8_t*>(p_act + s * act_bytes) + pc * 256,
-                      ld + s * (K / 32) + pc, lbs + s * (K / 16) + pc * 16);
+                      ld + s * (K / 32) + pc * (256 / B), lbs + s * (K / 16) + pc * 16);
       } else {
         quant_wave_pairs(v, valid, lane,
                          reinterpret_cast<half2_t*>(p_act + s * act_bytes) + pc * 8 * kApPitch,
@@ -748,11 +748,14 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
           const int s = js, pc = dpc.mod(job, js);
           if (pc * 256 + 4 * lane < K) {
             reinterpret_cast<uint32_t*>(p_act + s * act_bytes + pc * 256)[lane] = pack_q8x4(q[u]);
-            if (lane == 0) ld[s * (K / 32) + pc] = dv[u];
+            if (B == 32 && (lane & 7) == 0) ld[s * (K / 32) + pc * 8 + (lane >> 3)] = dv[u];
+            if (B == 256 && lane == 0) ld[s * (K / 32) + pc] = dv[u];
           }
-          const int sm = sum4(q[u][0] + q[u][1] + q[u][2] + q[u][3]);
-          if ((lane & 3) == 0 && pc * 256 + 4 * lane < K)
-            lbs[s * (K / 16) + pc * 16 + (lane >> 2)] = static_cast<int16_t>(sm);
+          if constexpr (B == 256) {
+            const int sm = sum4(q[u][0] + q[u][1] + q[u][2] + q[u][3]);
+            if ((lane & 3) == 0 && pc * 256 + 4 * lane < K)
+              lbs[s * (K / 16) + pc * 16 + (lane >> 2)] = static_cast<int16_t>(sm);
+          }
         }
       }
     } else {
@@ -1121,7 +1124,7 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* rows, int K, 
   half2_t* lap = reinterpret_cast<half2_t*>(smem);
   float* ld = reinterpret_cast<float*>(smem + act_bytes);
   int16_t* lbs = reinterpret_cast<int16_t*>(smem + act_bytes + 4 * (K / 32));
-  stage_act<MX>(qs, d, bs, K, lqs, ld, lbs, lap);
+  stage_act<ActMode<FMT>::v>(qs, d, bs, K, lqs, ld, lbs, lap);
   __syncthreads();
   ActView av{lqs, ld, lbs, lap};
   const int r = blockIdx.x, nb = K / F::BE;
@@ -1152,7 +1155,7 @@ __global__ __launch_bounds__(64) void k_block_dots_mx(const uint8_t* rows, int n
   half2_t* lap = reinterpret_cast<half2_t*>(smem);
   float* ld = reinterpret_cast<float*>(smem + 80 * nb);
   uint8_t* scr = smem + mx_gu_scratch_offset(nb);
-  stage_act<true>(qs, d, nullptr, K, nullptr, ld, nullptr, lap);
+  stage_act<ACT_PAIRS>(qs, d, nullptr, K, nullptr, ld, nullptr, lap);
   __syncthreads();
   const int r0 = 2 * blockIdx.x;
   uint4 pcs[NL];
@@ -1173,6 +1176,23 @@ __global__ __launch_bounds__(64) void k_block_dots_mx(const uint8_t* rows, int n
       out[(static_cast<size_t>(r) * nb + b) * 2 + 1] = 0;
     }
   });
+}
+
+// Calls f(std::integral_constant<int, FMT>) for a format enum (nothing for
+// an unknown one).
+template <class Fn>
+void with_fmt(int fmt, Fn&& f) {
+  switch (fmt) {
+    case FMT_Q4_K: f(std::integral_constant<int, FMT_Q4_K>{}); break;
+    case FMT_Q6_K: f(std::integral_constant<int, FMT_Q6_K>{}); break;
+    case FMT_MXFP4: f(std::integral_constant<int, FMT_MXFP4>{}); break;
+    case FMT_Q5_K: f(std::integral_constant<int, FMT_Q5_K>{}); break;
+    case FMT_Q2_K: f(std::integral_constant<int, FMT_Q2_K>{}); break;
+    case FMT_Q3_K: f(std::integral_constant<int, FMT_Q3_K>{}); break;
+    case FMT_Q4_0: f(std::integral_constant<int, FMT_Q4_0>{}); break;
+    case FMT_Q5_1: f(std::integral_constant<int, FMT_Q5_1>{}); break;
+    default: break;
+  }
 }
 
 // Rows per workgroup and tasks per lane group for a GEMV launch: at least
@@ -1196,7 +1216,7 @@ size_t gateup_lds(const KArgs& a, GemvShape* out) {
   using F = typename FmtOf<FMT>::T;
   const int P = a.T * a.k + a.T * a.has_shared;
   const int nb = a.H / F::BE;
-  const int tpg_max = FMT == FMT_Q6_K || FMT == FMT_Q5_K ? 4 : 8;  // Raw registers per task
+  const int tpg_max = FMT == FMT_Q6_K || FMT == FMT_Q5_K || FMT == FMT_Q3_K ? 4 : 8;  // Raw registers per task
   GemvShape sh = gemv_shape(a.F, 2, nb, F::LPB, P, tpg_max, 512);
   if (out) *out = sh;
   const bool MX = FMT == FMT_MXFP4;
@@ -1210,7 +1230,7 @@ size_t down_lds(const KArgs& a, GemvShape* out) {
   using F = typename FmtOf<FMT>::T;
   const int ns = a.k + a.has_shared;
   const int nb = a.F / F::BE;
-  const int tpg_max = FMT == FMT_Q6_K || FMT == FMT_Q5_K ? 4 : 8;  // Raw registers per task
+  const int tpg_max = FMT == FMT_Q6_K || FMT == FMT_Q5_K || FMT == FMT_Q3_K ? 4 : 8;  // Raw registers per task
   // Every workgroup re-quantizes its token's h (VALU work), so the target is
   // one workgroup per compute unit (R = ceil(H T / 256)), as far as the cap
   // on loads per lane allows.
@@ -1429,16 +1449,9 @@ bool gemv_hquant(int fmt_down, int F, int k, int has_shared) {
 
 bool gemv_fits(const KArgs& a) {
   GemvShape gs{1, 1}, ds{1, 1};
-  size_t g = a.fmt_gu == FMT_Q4_K ? gateup_lds<FMT_Q4_K>(a, &gs)
-           : a.fmt_gu == FMT_Q6_K ? gateup_lds<FMT_Q6_K>(a, &gs)
-           : a.fmt_gu == FMT_Q5_K ? gateup_lds<FMT_Q5_K>(a, &gs)
-           : a.fmt_gu == FMT_Q2_K ? gateup_lds<FMT_Q2_K>(a, &gs)
-                                  : gateup_lds<FMT_MXFP4>(a, &gs);
-  size_t d = a.fmt_d == FMT_Q4_K ? down_lds<FMT_Q4_K>(a, &ds)
-           : a.fmt_d == FMT_Q6_K ? down_lds<FMT_Q6_K>(a, &ds)
-           : a.fmt_d == FMT_Q5_K ? down_lds<FMT_Q5_K>(a, &ds)
-           : a.fmt_d == FMT_Q2_K ? down_lds<FMT_Q2_K>(a, &ds)
-                                 : down_lds<FMT_MXFP4>(a, &ds);
+  size_t g = 0, d = 0;
+  with_fmt(a.fmt_gu, [&](auto f) { g = gateup_lds<decltype(f)::value>(a, &gs); });
+  with_fmt(a.fmt_d, [&](auto f) { d = down_lds<decltype(f)::value>(a, &ds); });
   DownLdsPlan pl;
   if (down_lds_plan(a, &pl)) {
     d = pl.lds;
@@ -1491,13 +1504,9 @@ hipError_t launch_topk(const KArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gateup(const KArgs& a, bool routing_given, hipStream_t s, Ev ev) {
-  switch (a.fmt_gu) {
-    case FMT_Q4_K: return gateup_dispatch<FMT_Q4_K>(a, routing_given, s, ev);
-    case FMT_Q6_K: return gateup_dispatch<FMT_Q6_K>(a, routing_given, s, ev);
-    case FMT_Q5_K: return gateup_dispatch<FMT_Q5_K>(a, routing_given, s, ev);
-    case FMT_Q2_K: return gateup_dispatch<FMT_Q2_K>(a, routing_given, s, ev);
-    default: return gateup_dispatch<FMT_MXFP4>(a, routing_given, s, ev);
-  }
+  hipError_t e = hipErrorInvalidValue;
+  with_fmt(a.fmt_gu, [&](auto f) { e = gateup_dispatch<decltype(f)::value>(a, routing_given, s, ev); });
+  return e;
 }
 
 hipError_t launch_hquant_pairs(const KArgs& a, hipStream_t s, Ev ev) {
@@ -1507,13 +1516,9 @@ hipError_t launch_hquant_pairs(const KArgs& a, hipStream_t s, Ev ev) {
 }
 
 hipError_t launch_down(const KArgs& a, hipStream_t s, Ev ev) {
-  switch (a.fmt_d) {
-    case FMT_Q4_K: return down_dispatch<FMT_Q4_K>(a, s, ev);
-    case FMT_Q6_K: return down_dispatch<FMT_Q6_K>(a, s, ev);
-    case FMT_Q5_K: return down_dispatch<FMT_Q5_K>(a, s, ev);
-    case FMT_Q2_K: return down_dispatch<FMT_Q2_K>(a, s, ev);
-    default: return down_dispatch<FMT_MXFP4>(a, s, ev);
-  }
+  hipError_t e = hipErrorInvalidValue;
+  with_fmt(a.fmt_d, [&](auto f) { e = down_dispatch<decltype(f)::value>(a, s, ev); });
+  return e;
 }
 
 template <int NL, int NBL>
@@ -1530,6 +1535,7 @@ hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_
                              hipStream_t s) {
   const uint8_t* r = static_cast<const uint8_t*>(rows);
   const size_t lds = (fmt == FMT_MXFP4 ? 5 * K / 2 : K) + 4 * (K / 32) + 2 * (K / 16);
+  if (fmt < FMT_Q4_K || fmt > FMT_Q5_1) return hipErrorInvalidValue;
   MxPlan pl;
   if (fmt == FMT_MXFP4 && mx_plan(K, &pl)) {
     // rows the realigning MXFP4 kernels take (the same plans as k_gateup_mx)
@@ -1543,23 +1549,13 @@ hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_
       default: return block_dots_mx_launch<9, 4>(r, n_rows, K, stride, qs, d, out, s);
     }
   }
-  switch (fmt) {
-    case FMT_Q4_K:
-      return launch(k_block_dots<FMT_Q4_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
-                    bs, out);
-    case FMT_Q5_K:
-      return launch(k_block_dots<FMT_Q5_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
-                    bs, out);
-    case FMT_Q2_K:
-      return launch(k_block_dots<FMT_Q2_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
-                    bs, out);
-    case FMT_Q6_K:
-      return launch(k_block_dots<FMT_Q6_K>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs, d,
-                    bs, out);
-    default:  // MXFP4 rows past the realigning kernels' plans: the per-block routine
-      return launch(k_block_dots<FMT_MXFP4>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs,
-                    d, bs, out);
-  }
+  hipError_t e = hipErrorInvalidValue;
+  // MXFP4 rows past the realigning kernels' plans take the per-block routine
+  with_fmt(fmt, [&](auto f) {
+    e = launch(k_block_dots<decltype(f)::value>, dim3(n_rows), 256, lds, s, Ev{}, r, K, stride, qs,
+               d, bs, out);
+  });
+  return e;
 }
 
 }  // namespace moe

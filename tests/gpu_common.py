@@ -64,7 +64,7 @@ def x_cases(T, H, seed):
         x[1] = 0.0                       # all-zero row
     if T > 2:
         x[2, :32] = 0.0                  # a zero block
-        x[2, 40] = 1e4                   # a spike
+        x[2, min(40, H - 1)] = 1e4       # a spike
     if T > 3:
         x[3] *= 1e-6
     return x
@@ -86,7 +86,8 @@ def upload_q8(x_rows, B):
 
 
 def random_blocks(fmt, n_rows, K, rng):
-    """Blocks with arbitrary field values (negative Q6_K scales, every MXFP4 code)."""
+    """Blocks with arbitrary field values (negative Q6_K scales, every MXFP4 code,
+    negative Q5_1 minimums, every Q3_K scale)."""
     nb = K // gen.BLOCK_ELEMS[fmt]
     rows = []
     for r in range(n_rows):
@@ -111,6 +112,15 @@ def random_blocks(fmt, n_rows, K, rng):
                 row.append(gen.pack_q6k(int(rng.integers(0x0400, 0x3C00)),
                                         rng.integers(-128, 128, 16).astype(np.int8),
                                         rng.integers(0, 64, 256)))
+            elif fmt == gen.Q3_K:
+                row.append(gen.pack_q3k(int(rng.integers(0x0400, 0x3C00)), rng.integers(0, 64, 16),
+                                        rng.integers(-4, 4, 256)))
+            elif fmt == gen.Q4_0:
+                row.append(gen.pack_q40(int(rng.integers(0x0400, 0x3C00)), rng.integers(0, 16, 32)))
+            elif fmt == gen.Q5_1:
+                row.append(gen.pack_q51(int(rng.integers(0x0400, 0x3C00)),
+                                        int(rng.integers(0x0400, 0x3C00)) | (rng.integers(2) << 15),
+                                        rng.integers(0, 32, 32)))
             else:
                 row.append(gen.pack_mxfp4(int(rng.integers(100, 150)), rng.integers(0, 16, 32)))
         rows.append(np.concatenate(row))

@@ -70,7 +70,8 @@ def test_workspace_size_valid_and_invalid():
 MUTATIONS = [
     ("hidden", 0), ("hidden", 2048 + 32), ("ffn", 100), ("n_expert", 0), ("n_expert", 1025),
     ("top_k", 0), ("top_k", 257), ("top_k", 17), ("router", 2), ("norm_topk", 2), ("act", 5),
-    ("fmt_gate", 3), ("fmt_down", -1), ("stride_gate", 1024), ("stride_gate", 1152 + 8),
+    ("fmt_gate", 3), ("fmt_gate", 8), ("fmt_down", -1), ("fmt_down", 8), ("stride_gate", 1024),
+    ("stride_gate", 1152 + 8),
     ("stride_down", 280), ("w_router", 0), ("w_router", FAKE + 4), ("gate", 0), ("down", 0),
     ("up", FAKE + 2), ("sh_gate", FAKE),
 ]
@@ -161,7 +162,11 @@ def test_block_dots_validation():
         (M.MOE_WFMT_Q4_K, FAKE, 1, 512, 280, q, 0),
         (M.MOE_WFMT_Q4_K, FAKE, 1, 512, 288, q, 1),
         (M.MOE_WFMT_MXFP4, FAKE, 1, 512, 288, q, 0),
-        (5, FAKE, 1, 512, 288, q, 0),
+        (8, FAKE, 1, 512, 288, q, 0),
+        (-1, FAKE, 1, 512, 288, q, 0),
+        (M.MOE_WFMT_Q4_0, FAKE, 1, 512, 288, q, 0),   # Q4_0 rows take q8_32 activations
+        (M.MOE_WFMT_Q5_1, FAKE, 1, 512, 288, q, 0),
+        (M.MOE_WFMT_Q3_K, FAKE, 1, 512, 208, q, 0),   # row of 2 Q3_K blocks is 220 bytes
     ]
     for a in bad:
         with pytest.raises(M.MoeError):
@@ -169,8 +174,8 @@ def test_block_dots_validation():
 
 
 def test_stage_names_and_path_rule():
-    """Dispatch rule (moe_path AUTO): any layer with an MXFP4 (or Q5_K / Q2_K)
-    matrix takes the per-pair GEMV path (3 kernels, or 4 when an MXFP4 down is
+    """Dispatch rule (moe_path AUTO): any layer with a matrix in a format other
+    than Q4_K and Q6_K takes the per-pair GEMV path (3 kernels, or 4 when an MXFP4 down is
     too large for the kernel that quantizes h itself: h then gets a kernel of
     its own); other layers take the grouped path (7 kernels) when an expert has
     8 MB of blocks or more, or once T (k + shared) times the expert's block
@@ -211,9 +216,11 @@ def test_stage_names_and_path_rule():
     assert M.moe_layer_stage_count(mx9, 1) == 4
     assert [M.moe_layer_stage_name(mx9, 1, i) for i in range(4)] == [
         "router", "gateup", "hquant", "down"]
-    # Q5_K and Q2_K layers (gate/up or down) take the GEMV path at every T
+    # Q5_K, Q2_K, Q3_K, Q4_0 and Q5_1 layers (gate/up or down) take the GEMV path at every T
     for fg, fd in ((gen.Q5_K, gen.Q5_K), (gen.Q4_K, gen.Q5_K), (gen.Q5_K, gen.Q6_K),
-                   (gen.Q2_K, gen.Q2_K), (gen.Q4_K, gen.Q2_K)):
+                   (gen.Q2_K, gen.Q2_K), (gen.Q4_K, gen.Q2_K), (gen.Q3_K, gen.Q3_K),
+                   (gen.Q4_K, gen.Q3_K), (gen.Q4_0, gen.Q4_0), (gen.Q5_1, gen.Q6_K),
+                   (gen.Q4_K, gen.Q5_1)):
         q5 = good_desc(gen.CONFIGS["deepseek-v4-flash"].with_(fmt_gu=fg, fmt_d=fd))
         assert M.moe_layer_stage_count(q5, 16) == 3
     # the grouped workspace holds the per-pair rows: it grows with T * k * H

@@ -10,7 +10,8 @@ Two exports, both running the code the layer runs:
     d8 = 1): every pre-activation is then an integer (MXFP4: a multiple of 0.5)
     below 2^24, so the kernels' fp32 block rescale and sums are exact and must
     equal the oracle's summed integer partials bitwise. Covers the per-pair GEMV
-    kernels (Q4_K, Q6_K, Q5_K, Q2_K, MXFP4 realigned and per-block) and the
+    kernels (Q4_K, Q6_K, Q5_K, Q2_K, Q3_K, Q4_0, Q5_1, MXFP4 realigned and
+    per-block) and the
     grouped MFMA kernels (LDS ring, and register-staged with biases).
 """
 import zlib
@@ -89,6 +90,28 @@ def exact_blocks(fmt: int, n: int, rng) -> np.ndarray:
         b[:, 80:82] = [0x00, 0x3C]                # d = 1
         b[:, 82:84] = 0                           # dmin = 0
         return b
+    if fmt == gen.Q3_K:
+        b = rng.integers(0, 256, (n, 110), dtype=np.uint8)
+        # stored scales 30..33 (used as -2..1): low nibbles 14, 15, 0, 1 with
+        # top bits 1, 1, 2, 2
+        sc = rng.integers(30, 34, (n, 16))
+        for s in range(16):
+            lo, hi = sc[:, s] & 15, sc[:, s] >> 4
+            j = 96 + s % 8
+            b[:, j] = (b[:, j] & 0xF0) | lo if s < 8 else (b[:, j] & 0x0F) | (lo << 4)
+            k, sh = 104 + s % 4, 2 * (s // 4)
+            b[:, k] = (b[:, k] & (0xFF ^ (3 << sh))) | (hi << sh)
+        b[:, 108:110] = [0x00, 0x3C]              # d = 1
+        return b
+    if fmt == gen.Q4_0:
+        b = rng.integers(0, 256, (n, 18), dtype=np.uint8)
+        b[:, 0:2] = [0x00, 0x3C]                  # d = 1
+        return b
+    if fmt == gen.Q5_1:
+        b = rng.integers(0, 256, (n, 24), dtype=np.uint8)
+        b[:, 0:2] = [0x00, 0x3C]                  # d = 1
+        b[:, 2:4] = 0                             # m = 0
+        return b
     b = rng.integers(0, 256, (n, 17), dtype=np.uint8)
     b[:, 0] = 127                                 # E8M0 scale 2^0
     return b
@@ -139,6 +162,10 @@ EXACT_CASES = [
     ("mxfp4-realigned", dict(fmt_gu=gen.MXFP4, fmt_d=gen.MXFP4), 2),
     ("mxfp4-realigned-8tok", dict(fmt_gu=gen.MXFP4, fmt_d=gen.MXFP4), 8),
     ("mxfp4-per-block", dict(fmt_gu=gen.MXFP4, fmt_d=gen.MXFP4, H=8224, F=64, E=4), 2),
+    ("q3k-gemv", dict(fmt_gu=gen.Q3_K, fmt_d=gen.Q3_K), 2),
+    ("q40-gemv", dict(fmt_gu=gen.Q4_0, fmt_d=gen.Q4_0), 3),
+    ("q40-gemv-ragged", dict(fmt_gu=gen.Q4_0, fmt_d=gen.Q4_0, H=1056, F=96), 2),
+    ("q51-gemv", dict(fmt_gu=gen.Q5_1, fmt_d=gen.Q5_1), 2),
 ]
 
 
@@ -153,7 +180,7 @@ def test_preact_integer_exact(name, over, T):
     present[cfg.E - 1] = False  # one expert not present: its rows stay untouched
     path = M.MOE_PATH_GROUPED if "grouped" in name else M.MOE_PATH_GEMV
     dl = DeviceLayer(data, present=present, path=path)
-    B = 32 if cfg.fmt_gu == gen.MXFP4 else 256
+    B = gen.BLOCK_ELEMS[cfg.fmt_gu]  # q8 block of the gate/up activations
     x = integer_x(T, cfg.H, B, rng)
     host, q, keep = upload_q8(x, B)
     assert np.all(host[1] == 1.0) and np.array_equal(host[0], x.astype(np.int8))

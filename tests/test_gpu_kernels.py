@@ -52,11 +52,14 @@ def test_quantize_bitexact(afmt, B, T, H, bf16):
                                    (gen.MXFP4, 1024), (gen.MXFP4, 2048), (gen.MXFP4, 4096),
                                    (gen.MXFP4, 8192), (gen.MXFP4, 8224),
                                    (gen.Q5_K, 256), (gen.Q5_K, 2048), (gen.Q2_K, 256),
-                                   (gen.Q2_K, 2048)])
+                                   (gen.Q2_K, 2048), (gen.Q3_K, 256), (gen.Q3_K, 2048),
+                                   (gen.Q3_K, 7168), (gen.Q4_0, 32), (gen.Q4_0, 96),
+                                   (gen.Q4_0, 2880), (gen.Q5_1, 64), (gen.Q5_1, 2880),
+                                   (gen.Q5_1, 4096)])
 @pytest.mark.parametrize("kind", ["generated", "random_fields"])
 def test_block_dots_exact(fmt, K, kind):
     say(f"block_dots fmt={fmt} K={K} {kind}")
-    B = 32 if fmt == gen.MXFP4 else 256
+    B = gen.BLOCK_ELEMS[fmt]  # q8 block of the activations these rows consume
     n_rows = 37
     rng = np.random.default_rng(fmt * 100 + K)
     if kind == "generated":

@@ -71,6 +71,31 @@ def test_layer_q2k(name, fmt_gu, fmt_d, T):
     check_layer(cfg, x_index=T)
 
 
+FMTS = {"Q4_K": gen.Q4_K, "Q6_K": gen.Q6_K, "Q5_K": gen.Q5_K, "Q2_K": gen.Q2_K,
+        "Q3_K": gen.Q3_K, "Q4_0": gen.Q4_0, "Q5_1": gen.Q5_1}
+
+
+@pytest.mark.parametrize("name,fmt_gu,fmt_d,T", [
+    ("qwen3.6-35b-a3b", "Q3_K", "Q3_K", 1), ("qwen3.6-35b-a3b", "Q3_K", "Q3_K", 6),
+    ("deepseek-v4-flash", "Q3_K", "Q6_K", 3), ("kimi-k2", "Q4_K", "Q3_K", 7),
+    ("qwen3.6-35b-a3b", "Q4_0", "Q4_0", 1), ("qwen3.6-35b-a3b", "Q4_0", "Q4_0", 5),
+    ("gpt-oss-20b", "Q4_0", "Q5_1", 3), ("kimi-k2", "Q5_1", "Q5_1", 7),
+    ("deepseek-v4-flash", "Q5_1", "Q4_K", 4), ("kimi-k2", "Q4_K", "Q4_0", 2),
+    ("qwen-full", "Q3_K", "Q4_0", 1), ("gptoss-full", "Q5_1", "Q4_0", 1)])
+def test_layer_q3k_q40_q51(name, fmt_gu, fmt_d, T):
+    """Q3_K (256-weight blocks, q8_K activations) and Q4_0 / Q5_1 (32-weight
+    blocks, int8 q8_32 activations) experts through the per-pair GEMV kernels,
+    alone and mixed with each other and with Q4_K and Q6_K: the shrunk shapes
+    (gpt-oss's 320 / 288 widths are 10 and 9 blocks of 32, with biases and the
+    clamped SwiGLU), up to a 7-token chunk, and the full Qwen3.6 and gpt-oss
+    shapes at one token."""
+    base = (gen.CONFIGS["qwen3.6-35b-a3b"] if name == "qwen-full"
+            else gen.CONFIGS["gpt-oss-20b"] if name == "gptoss-full" else SHRUNK[name])
+    cfg = base.with_(name=f"{base.name}-{fmt_gu}-{fmt_d}", fmt_gu=FMTS[fmt_gu],
+                     fmt_d=FMTS[fmt_d], T=T)
+    check_layer(cfg, x_index=T)
+
+
 def _routed_layer(cfg, T, x_index):
     """The full-size layer with only the experts the oracle routes these tokens
     to (plus the shared expert) generated; the others stay zero and unused."""
