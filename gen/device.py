@@ -30,17 +30,37 @@ def x_to_device(data, x_np: np.ndarray | None = None, xb_np: np.ndarray | None =
     return _dev(x.astype(np.float32), device), M.MOE_DTYPE_F32
 
 
+def interleave_gate_up(data) -> np.ndarray:
+    """The pool with each expert's gate and up matrices stored as one fused
+    tensor of alternating rows (gate row r at 2r, up row r at 2r + 1), as
+    checkpoints that keep a fused gate_up projection do; the stacked form
+    (all gate rows, then all up rows) is the default pool layout."""
+    cfg = data.cfg
+    pool = data.pool.copy()
+    n, s = cfg.F, cfg.stride_gu
+    for e in range(pool.shape[0]):
+        g = data.pool[e, :n * s].reshape(n, s)
+        u = data.pool[e, n * s:2 * n * s].reshape(n, s)
+        fused = pool[e, :2 * n * s].reshape(n, 2, s)
+        fused[:, 0], fused[:, 1] = g, u
+    return pool
+
+
 class DeviceLayer:
     def __init__(self, data, copies: int = 1, present=None, route_scale=None, norm_topk=None,
                  use_shared: bool = True, sh_gate_vec=None, sel_bias="data", device="cuda",
-                 path: int = 0):
+                 path: int = 0, interleaved: bool = False):
         cfg = data.cfg
         self.cfg = cfg
         self.device = device
         E = cfg.E
         present = np.ones(E, bool) if present is None else np.asarray(present, bool)
         self.present = present
-        pool0 = _dev(data.pool, device)
+        # gate/up row r of an expert: interleaved at (2r, 2r + 1) of one fused
+        # tensor, else stacked (gate matrix, then up matrix)
+        up_off = cfg.stride_gu if interleaved else cfg.gate_bytes
+        gu_stride = 2 * cfg.stride_gu if interleaved else cfg.stride_gu
+        pool0 = _dev(interleave_gate_up(data) if interleaved else data.pool, device)
         self.pools = [pool0] + [pool0.clone() for _ in range(1, copies)]
         self.w_router = _dev(data.w_router, device)
         sb = data.sel_bias if isinstance(sel_bias, str) else sel_bias
@@ -58,7 +78,7 @@ class DeviceLayer:
         for pool in self.pools:
             base = pool.data_ptr()
             g = [base + e * es if present[e] else 0 for e in range(E)]
-            u = [base + e * es + cfg.gate_bytes if present[e] else 0 for e in range(E)]
+            u = [base + e * es + up_off if present[e] else 0 for e in range(E)]
             dn = [base + e * es + 2 * cfg.gate_bytes if present[e] else 0 for e in range(E)]
             tg = torch.tensor(g, dtype=torch.int64, device=device)
             tu = torch.tensor(u, dtype=torch.int64, device=device)
@@ -73,7 +93,7 @@ class DeviceLayer:
             d.sel_bias = None if self.sel_bias is None else self.sel_bias.data_ptr()
             d.fmt_gate = d.fmt_up = cfg.fmt_gu
             d.fmt_down = cfg.fmt_d
-            d.stride_gate = d.stride_up = cfg.stride_gu
+            d.stride_gate = d.stride_up = gu_stride
             d.stride_down = cfg.stride_d
             d.gate, d.up, d.down = tg.data_ptr(), tu.data_ptr(), td.data_ptr()
             if self.b_gate is not None:
@@ -88,7 +108,7 @@ class DeviceLayer:
             d.act_alpha, d.act_limit = cfg.act_alpha, cfg.act_limit
             if cfg.shared and use_shared:
                 sh = base + E * es
-                d.sh_gate, d.sh_up, d.sh_down = sh, sh + cfg.gate_bytes, sh + 2 * cfg.gate_bytes
+                d.sh_gate, d.sh_up, d.sh_down = sh, sh + up_off, sh + 2 * cfg.gate_bytes
             d.sh_gate_vec = None if self.sh_gate_vec is None else self.sh_gate_vec.data_ptr()
             d.path = path  # moe_path: 0 auto, 1 per-pair GEMV, 2 expert-grouped
             self._tables.append(keep)

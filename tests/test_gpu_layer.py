@@ -96,6 +96,40 @@ def test_layer_q3k_q40_q51(name, fmt_gu, fmt_d, T):
     check_layer(cfg, x_index=T)
 
 
+@pytest.mark.parametrize("name,T,path", [
+    ("qwen3.6-35b-a3b", 1, M.MOE_PATH_GEMV), ("qwen3.6-35b-a3b", 16, M.MOE_PATH_GROUPED),
+    ("deepseek-v4-flash", 5, M.MOE_PATH_GROUPED), ("gpt-oss-20b", 3, M.MOE_PATH_AUTO),
+    ("kimi-k2", 7, M.MOE_PATH_GEMV)])
+def test_fused_gate_up_interleaved(name, T, path):
+    """Experts stored with one fused gate_up tensor of alternating gate and up
+    rows: the descriptor's up pointer is one row past the gate pointer and both
+    strides are two rows. Same outputs as the stacked layout (bitwise) and the
+    oracle, on the per-pair GEMV and the expert-grouped paths."""
+    cfg = SHRUNK[name].with_(T=T)
+    data = gen.make_layer(cfg)
+    y, ids, w, _ = check_layer(cfg, data=data, x_index=T, path=path, interleaved=True)
+    x, xb = gen.make_x(cfg, T=T, x_index=T)
+    dl = DeviceLayer(data, path=path)
+    xt, dt = x_to_device(data, x, xb)
+    y2, ids2, w2 = run_layer(dl, xt, dt, T)
+    assert np.array_equal(ids, ids2) and np.array_equal(w, w2)
+    assert np.array_equal(y, y2)
+
+
+@pytest.mark.parametrize("fmt_gu,fmt_d,F,T", [
+    ("Q4_K", "Q4_0", 1440, 1), ("Q4_K", "Q5_1", 1440, 4), ("Q6_K", "Q4_0", 352, 3),
+    ("Q5_1", "Q5_1", 1440, 2), ("MXFP4", "MXFP4", 1440, 2)])
+def test_expert_width_not_multiple_of_256(fmt_gu, fmt_d, F, T):
+    """Expert widths F that are not multiples of 256 (1440 = 45 blocks of 32,
+    352 = 11): gate/up rows of any format are F rows, and the down rows of
+    width F take a 32-weight format."""
+    f = dict(FMTS, MXFP4=gen.MXFP4)
+    base = SHRUNK["qwen3.6-35b-a3b"]
+    cfg = base.with_(name=f"qwen-F{F}-{fmt_gu}-{fmt_d}", fmt_gu=f[fmt_gu], fmt_d=f[fmt_d],
+                     F=F, T=T)
+    check_layer(cfg, x_index=T)
+
+
 def _routed_layer(cfg, T, x_index):
     """The full-size layer with only the experts the oracle routes these tokens
     to (plus the shared expert) generated; the others stay zero and unused."""
