@@ -256,6 +256,7 @@ class LayerConfig:
     router_std: float = 0.02
     bias_std: float = 0.01
     x_std: float = 1.0
+    act_quant: int = 0  # activation numerics: 0 q8, 1 MXFP8 (MXFP4 layers, block-scaled MMA)
     description: str = ""
 
     @property

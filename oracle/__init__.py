@@ -20,6 +20,7 @@ _lib = None
 Q4_K, Q6_K, MXFP4, Q5_K, Q2_K, Q3_K, Q4_0, Q5_1 = 0, 1, 2, 3, 4, 5, 6, 7
 SOFTMAX, SIGMOID = 0, 1
 SWIGLU, SWIGLU_OAI = 0, 1
+ACTQ_Q8, ACTQ_MXFP8 = 0, 1
 BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, MXFP4: 32, Q5_K: 256, Q2_K: 256, Q3_K: 256, Q4_0: 32,
                Q5_1: 32}
 BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, MXFP4: 17, Q5_K: 176, Q2_K: 84, Q3_K: 110, Q4_0: 18,
@@ -46,7 +47,7 @@ class OrLayer(C.Structure):
         ("b_gate", C.c_void_p), ("b_up", C.c_void_p), ("b_down", C.c_void_p),
         ("act", C.c_int), ("act_alpha", C.c_double), ("act_limit", C.c_double),
         ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
-        ("sh_gate_vec", C.c_void_p),
+        ("sh_gate_vec", C.c_void_p), ("act_quant", C.c_int),
     ]
 
 
@@ -60,6 +61,10 @@ def lib():
         L.or_fp16.argtypes = [u16]; L.or_fp16.restype = f64
         L.or_e8m0.argtypes = [u8]; L.or_e8m0.restype = f64
         L.or_e2m1.argtypes = [u8]; L.or_e2m1.restype = f64
+        L.or_e4m3.argtypes = [u8]; L.or_e4m3.restype = f64
+        L.or_e4m3_round.argtypes = [f64]; L.or_e4m3_round.restype = u8
+        L.or_quantize_mx8.argtypes = [vp, i32, vp, vp]
+        L.or_row_dot_mx8.argtypes = [vp, i32, vp, vp]; L.or_row_dot_mx8.restype = f64
         L.or_block_quants.argtypes = [i32, vp, vp]
         L.or_dequant_block.argtypes = [i32, vp, vp]
         L.or_dequant_row.argtypes = [i32, vp, i32, vp]
@@ -97,6 +102,32 @@ def e8m0(e: int) -> float:
 
 def e2m1(code: int) -> float:
     return lib().or_e2m1(code)
+
+
+def e4m3(code: int) -> float:
+    return lib().or_e4m3(code)
+
+
+def e4m3_round(v: float) -> int:
+    """Nearest finite E4M3 code (ties to even, saturating at +-448, zero -> +0)."""
+    return int(lib().or_e4m3_round(float(v)))
+
+
+def quantize_mx8(x: np.ndarray):
+    """MXFP8 of a 1-D fp32 vector: (E4M3 codes uint8 [n], E8M0 scale bytes uint8 [n/32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.size
+    q = np.empty(n, dtype=np.uint8)
+    e = np.empty(n // 32, dtype=np.uint8)
+    lib().or_quantize_mx8(_p(x), n, _p(q), _p(e))
+    return q, e
+
+
+def row_dot_mx8(row: np.ndarray, K: int, q, e) -> float:
+    """Exact fp64 dot of one MXFP4 row with MXFP8 activations."""
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    return lib().or_row_dot_mx8(_p(row), K, _p(np.ascontiguousarray(q, np.uint8)),
+                                _p(np.ascontiguousarray(e, np.uint8)))
 
 
 def block_quants(fmt: int, blk: np.ndarray) -> np.ndarray:
@@ -242,6 +273,7 @@ class Layer:
             shv = np.ascontiguousarray(shv, np.float32)
             self._keep.append(shv)
         L.sh_gate_vec = _p(shv)
+        L.act_quant = getattr(cfg, "act_quant", ACTQ_Q8)
         self.L = L
 
     def token(self, x_row: np.ndarray, want_h: bool = False):

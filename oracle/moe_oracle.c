@@ -35,6 +35,71 @@ double or_e2m1(uint8_t code) {
   return s ? -v : v;
 }
 
+/* OCP FP8 E4M3 (MX v1.0, §5.3.3): sign bit 7, exponent bits 6..3 (bias 7),
+ * mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2^-6); 0x7F/0xFF are
+ * NaN; no infinities. */
+double or_e4m3(uint8_t code) {
+  int s = code >> 7, ex = (code >> 3) & 15, m = code & 7;
+  if (ex == 15 && m == 7) return NAN;
+  double v = ex == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, ex - 7);
+  return s ? -v : v;
+}
+
+/* Nearest finite E4M3 magnitude by exhaustive comparison over the 127 codes
+ * 0x00..0x7E (ties: the even code); beyond 448 every value saturates. */
+uint8_t or_e4m3_round(double v) {
+  double a = fabs(v);
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(or_e4m3((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  if (best == 0) return 0;
+  return (uint8_t)(v < 0 ? (best | 0x80) : best);
+}
+
+void or_quantize_mx8(const float* x, int n, uint8_t* q, uint8_t* e) {
+  for (int b = 0; b < n / 32; ++b) {
+    const float* xb = x + (size_t)b * 32;
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+      float a = fabsf(xb[i]);
+      if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+      e[b] = 0;
+      for (int i = 0; i < 32; ++i) q[(size_t)b * 32 + i] = 0;
+      continue;
+    }
+    int k;
+    frexp((double)amax, &k);          /* amax = f 2^k, f in [0.5, 1): floor(log2) = k - 1 */
+    int sb = (k - 1) - 8 + 127;
+    if (sb < 0) sb = 0;
+    if (sb > 254) sb = 254;
+    e[b] = (uint8_t)sb;
+    for (int i = 0; i < 32; ++i)
+      q[(size_t)b * 32 + i] = or_e4m3_round(ldexp((double)xb[i], 127 - sb));  /* exact */
+  }
+}
+
+double or_row_dot_mx8(const uint8_t* row, int K, const uint8_t* q, const uint8_t* e) {
+  double acc = 0.0;
+  for (int b = 0; b < K / 32; ++b) {
+    const uint8_t* blk = row + (size_t)b * 17;
+    double s = 0.0;  /* exact: products and their sum are well inside fp64 */
+    for (int i = 0; i < 32; ++i) {
+      uint8_t code = i < 16 ? (blk[1 + i] & 15) : (blk[1 + i - 16] >> 4);
+      s += or_e2m1(code) * or_e4m3(q[(size_t)b * 32 + i]);
+    }
+    acc += or_e8m0(blk[0]) * or_e8m0(e[b]) * s;
+  }
+  return acc;
+}
+
 int or_block_elems(int fmt) {
   return (fmt == OR_MXFP4 || fmt == OR_Q4_0 || fmt == OR_Q5_1) ? 32 : 256;
 }
@@ -411,6 +476,32 @@ double or_act(int act, double alpha, double limit, double g, double u) {
   return gc * sigmoid(alpha * gc) * (uc + 1.0);
 }
 
+/* MXFP8 mode of one expert: x already quantized (codes xq8, scales xe). */
+static void expert_ffn_mx8(const or_layer* L, const uint8_t* gate, const uint8_t* up,
+                           const uint8_t* down, const float* bg, const float* bu,
+                           const float* bd, const uint8_t* xq8, const uint8_t* xe, double* out,
+                           float* h32) {
+  const int H = L->H, F = L->F;
+  float* h = (float*)malloc(sizeof(float) * (size_t)F);
+  uint8_t* hq = (uint8_t*)malloc((size_t)F);
+  uint8_t* he = (uint8_t*)malloc((size_t)(F / 32));
+  for (int r = 0; r < F; ++r) {
+    double g = or_row_dot_mx8(gate + (size_t)r * L->stride_gate, H, xq8, xe);
+    double u = or_row_dot_mx8(up + (size_t)r * L->stride_up, H, xq8, xe);
+    if (bg) g += bg[r];
+    if (bu) u += bu[r];
+    h[r] = (float)or_act(L->act, L->act_alpha, L->act_limit, g, u);
+  }
+  if (h32) memcpy(h32, h, sizeof(float) * (size_t)F);
+  or_quantize_mx8(h, F, hq, he);
+  for (int i = 0; i < H; ++i) {
+    double o = or_row_dot_mx8(down + (size_t)i * L->stride_down, F, hq, he);
+    if (bd) o += bd[i];
+    out[i] = o;
+  }
+  free(h); free(hq); free(he);
+}
+
 void or_expert_ffn(const or_layer* L, const uint8_t* gate, const uint8_t* up,
                    const uint8_t* down, const float* bg, const float* bu, const float* bd,
                    const int8_t* xq, const float* xd, const int16_t* xbs, double* out,
@@ -438,17 +529,32 @@ void or_expert_ffn(const or_layer* L, const uint8_t* gate, const uint8_t* up,
   free(h); free(hq); free(hd); free(hbs);
 }
 
-typedef struct { int8_t* q; float* d; int16_t* bs; } q8buf;
+/* x quantized as the layer's gate/up rows consume it: q8 (q, d, bs), or
+ * MXFP8 (codes in q, scale bytes in e). */
+typedef struct { int8_t* q; float* d; int16_t* bs; uint8_t* e; } q8buf;
 static q8buf q8_of(const or_layer* L, const float* x) {
   const int Bx = or_act_block(L->fmt_gate);
   q8buf b;
   b.q = (int8_t*)malloc((size_t)L->H);
   b.d = (float*)malloc(sizeof(float) * (size_t)(L->H / 32));
   b.bs = (int16_t*)malloc(sizeof(int16_t) * (size_t)(L->H / 16));
-  or_quantize_q8(x, L->H, Bx, b.q, b.d, b.bs);
+  b.e = (uint8_t*)malloc((size_t)(L->H / 32));
+  if (L->act_quant == OR_ACTQ_MXFP8)
+    or_quantize_mx8(x, L->H, (uint8_t*)b.q, b.e);
+  else
+    or_quantize_q8(x, L->H, Bx, b.q, b.d, b.bs);
   return b;
 }
-static void q8_free(q8buf b) { free(b.q); free(b.d); free(b.bs); }
+static void q8_free(q8buf b) { free(b.q); free(b.d); free(b.bs); free(b.e); }
+
+static void run_expert(const or_layer* L, const uint8_t* gate, const uint8_t* up,
+                       const uint8_t* down, const float* bg, const float* bu, const float* bd,
+                       const q8buf* xq, double* out, float* h32) {
+  if (L->act_quant == OR_ACTQ_MXFP8)
+    expert_ffn_mx8(L, gate, up, down, bg, bu, bd, (const uint8_t*)xq->q, xq->e, out, h32);
+  else
+    or_expert_ffn(L, gate, up, down, bg, bu, bd, xq->q, xq->d, xq->bs, out, h32);
+}
 
 static double shared_weight(const or_layer* L, const float* x) {
   if (!L->sh_gate_vec) return 1.0;
@@ -468,15 +574,15 @@ static void add_experts(const or_layer* L, const float* x, const int32_t* ids,
     /* an id outside [0, E) or a NULL expert is a slot that is "not mine": it
        contributes nothing (given routing may carry such ids) */
     if (e < 0 || e >= L->E || !L->gate[e]) continue;
-    or_expert_ffn(L, L->gate[e], L->up[e], L->down[e], L->b_gate ? L->b_gate[e] : NULL,
-                  L->b_up ? L->b_up[e] : NULL, L->b_down ? L->b_down[e] : NULL, xq.q, xq.d,
-                  xq.bs, o, h32 ? h32 + (size_t)j * F : NULL);
+    run_expert(L, L->gate[e], L->up[e], L->down[e], L->b_gate ? L->b_gate[e] : NULL,
+               L->b_up ? L->b_up[e] : NULL, L->b_down ? L->b_down[e] : NULL, &xq, o,
+               h32 ? h32 + (size_t)j * F : NULL);
     for (int i = 0; i < H; ++i) y[i] += w[j] * o[i];
   }
   if (L->sh_gate) {
     double ws = shared_weight(L, x);
-    or_expert_ffn(L, L->sh_gate, L->sh_up, L->sh_down, NULL, NULL, NULL, xq.q, xq.d, xq.bs, o,
-                  h32 ? h32 + (size_t)L->k * F : NULL);
+    run_expert(L, L->sh_gate, L->sh_up, L->sh_down, NULL, NULL, NULL, &xq, o,
+               h32 ? h32 + (size_t)L->k * F : NULL);
     for (int i = 0; i < H; ++i) y[i] += ws * o[i];
   }
   free(o);

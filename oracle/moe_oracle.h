@@ -27,6 +27,13 @@
  * consume q8 activations in blocks of 32, the others in blocks of 256.
  * GGUF byte-level interoperability is parity unpinned: no GGUF file or
  * reference decoder is available to check against.
+ *
+ * MXFP8 activation mode (act_quant = OR_ACTQ_MXFP8, MXFP4 layers only): the
+ * numerics of a block-scaled MX matrix path (memra ARCHITECTURE.md, §0 item 3
+ * and the §2 ledger row on MXFP4 / block-scale mma). x and h are quantized per
+ * block of 32 to OCP MX v1.0 MXFP8 (E4M3 elements, one E8M0 scale; the
+ * shared-scale rule of the MX spec, §6.3) instead of q8, and every block dot
+ * is the exact fp64 value 2^(ew-127) 2^(ea-127) sum_i e2m1(w_i) e4m3(a_i).
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -42,11 +49,16 @@ enum { OR_Q4_K = 0, OR_Q6_K = 1, OR_MXFP4 = 2, OR_Q5_K = 3, OR_Q2_K = 4, OR_Q3_K
        OR_Q4_0 = 6, OR_Q5_1 = 7 };
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 enum { OR_SWIGLU = 0, OR_SWIGLU_OAI = 1 };
+enum { OR_ACTQ_Q8 = 0, OR_ACTQ_MXFP8 = 1 };
 
 /* ---- scalar decoders ---- */
 double or_fp16(uint16_t bits);      /* IEEE binary16 -> double */
 double or_e8m0(uint8_t e);          /* 2^(e - 127) */
 double or_e2m1(uint8_t code);       /* OCP FP4 E2M1 value of a 4-bit code */
+double or_e4m3(uint8_t code);       /* OCP FP8 E4M3 value of a byte (NaN for 0x7F, 0xFF) */
+/* The finite E4M3 code nearest to v (ties to the even code), saturating at
+ * +-448; a result of magnitude zero is +0 (code 0x00). */
+uint8_t or_e4m3_round(double v);
 
 /* ---- block formats ---- */
 int or_block_elems(int fmt);
@@ -65,6 +77,15 @@ void or_dequant_row(int fmt, const uint8_t* row, int K, double* out);
  * else iscale = 127/amax, q = clamp(rne(x*iscale), -127, 127), d = amax/127,
  * all in IEEE fp32. bsums (B = 256 only, may be NULL) = sum of q over each 16. */
 void or_quantize_q8(const float* x, int n, int B, int8_t* qs, float* d, int16_t* bsums);
+
+/* ---- MXFP8 activation quantization (OCP MX v1.0, §6.3) ----
+ * Per block of 32: amax = max |x| (fp32); amax == 0 -> scale byte 0 and all
+ * codes 0; else the shared exponent is floor(log2(amax)) - 8 (8 = E4M3's
+ * largest normal exponent), scale byte e = shared + 127 clamped to [0, 254],
+ * and code_i = or_e4m3_round(x_i / 2^(e - 127)). q[n] codes, e[n / 32]. */
+void or_quantize_mx8(const float* x, int n, uint8_t* q, uint8_t* e);
+/* Exact fp64 dot of one MXFP4 row (K values) with MXFP8 activations. */
+double or_row_dot_mx8(const uint8_t* row, int K, const uint8_t* q, const uint8_t* e);
 
 /* ---- integer block partials of one weight row against q8 activations ----
  * out[2b], out[2b+1] for block b:
@@ -110,6 +131,7 @@ typedef struct {
   const uint8_t* sh_up;
   const uint8_t* sh_down;
   const float* sh_gate_vec;              /* [H] or NULL (weight 1) */
+  int act_quant;                         /* OR_ACTQ_Q8, or OR_ACTQ_MXFP8 (MXFP4 only) */
 } or_layer;
 
 /* Activation function on one (g, u) pair, fp64. */

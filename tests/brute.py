@@ -1,9 +1,9 @@
 """Brute-force dense fp64 evaluation of the layer for the oracle pins (numpy/torch).
 
 Weights are fully dequantized into dense fp64 matrices and multiplied with
-numpy; routing uses numpy's lexsort and torch's softmax/sigmoid. Only the two
-separately pinned oracle primitives are reused: block dequantization and the
-q8 activation recipe."""
+numpy; routing uses numpy's lexsort and torch's softmax/sigmoid. Only separately
+pinned oracle primitives are reused: block dequantization and the q8 and
+MXFP8 activation recipes."""
 import numpy as np
 
 import gen
@@ -62,7 +62,8 @@ def brute_layer(data, x, present=None, route_scale=None, sh_gate_vec=None, dense
             s = torch.sigmoid(lt[ids]).numpy()
             w = s / s.sum() if cfg.norm_topk else s
         w = w * rs
-        a = qdeq(xt, Bx)
+        mx8 = getattr(cfg, "act_quant", 0) == 1
+        a = mx8deq(xt) if mx8 else qdeq(xt, Bx)
         y = np.zeros(cfg.H)
 
         def ffn(e, bias_idx):
@@ -73,7 +74,7 @@ def brute_layer(data, x, present=None, route_scale=None, sh_gate_vec=None, dense
                 g = g + data.b_gate[bias_idx]
                 u = u + data.b_up[bias_idx]
             h32 = act(cfg, g, u).astype(np.float32)
-            o = Wd @ qdeq(h32, Bh)
+            o = Wd @ (mx8deq(h32) if mx8 else qdeq(h32, Bh))
             if bias_idx is not None and data.b_down is not None:
                 o = o + data.b_down[bias_idx]
             return o
@@ -91,3 +92,11 @@ def brute_layer(data, x, present=None, route_scale=None, sh_gate_vec=None, dense
         idss.append(ids)
         ws.append(w)
     return np.stack(ys), np.stack(idss), np.stack(ws)
+
+
+def mx8deq(v):
+    """MXFP8 (OCP MX v1.0) round trip of a vector through the oracle's
+    separately pinned quantizer and element decode."""
+    q, e = oracle.quantize_mx8(v.astype(np.float32))
+    vals = np.array([oracle.e4m3(int(c)) for c in range(256)])
+    return vals[q] * np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32)
