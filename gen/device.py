@@ -111,6 +111,7 @@ class DeviceLayer:
                 d.sh_gate, d.sh_up, d.sh_down = sh, sh + up_off, sh + 2 * cfg.gate_bytes
             d.sh_gate_vec = None if self.sh_gate_vec is None else self.sh_gate_vec.data_ptr()
             d.path = path  # moe_path: 0 auto, 1 per-pair GEMV, 2 expert-grouped
+            d.act_quant = getattr(cfg, "act_quant", 0)  # moe_actq: 0 q8, 1 MXFP8
             self._tables.append(keep)
             self.descs.append(d)
 

@@ -49,7 +49,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
@@ -82,8 +82,17 @@ typedef enum {
 } moe_wfmt;
 /* Activation quant formats: Q8_K = blocks of 256 with 16-element sums
  * (consumed by Q4_K, Q5_K, Q2_K, Q3_K and Q6_K rows); Q8_32 = blocks of 32
- * (MXFP4, Q4_0 and Q5_1 rows). */
-typedef enum { MOE_AFMT_Q8_K = 0, MOE_AFMT_Q8_32 = 1 } moe_afmt;
+ * (MXFP4, Q4_0 and Q5_1 rows); MXFP8 = OCP MX v1.0 blocks of 32 E4M3 values
+ * with one E8M0 scale (MXFP4 rows of layers with act_quant = MXFP8). */
+typedef enum { MOE_AFMT_Q8_K = 0, MOE_AFMT_Q8_32 = 1, MOE_AFMT_MXFP8 = 2 } moe_afmt;
+/* Activation numerics of a layer (which quantization x and h get before the
+ * expert rows). Q8: q8_K / q8_32 by weight format, integer block dots (Pulsar
+ * README, numerics notes). MXFP8: MXFP4 experts only, x and h quantized per
+ * block of 32 to MXFP8 (shared exponent floor(log2 amax) - 8, E4M3 elements
+ * rounded to nearest-even and saturated at 448) and multiplied on the
+ * block-scaled MFMA path at every T (memra ARCHITECTURE.md, §0 item 3 and the
+ * §2 ledger row on MXFP4 / block-scale mma). */
+typedef enum { MOE_ACTQ_Q8 = 0, MOE_ACTQ_MXFP8 = 1 } moe_actq;
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 } moe_router;
 /* SWIGLU: h = silu(g) * u. SWIGLU_OAI (gpt-oss): g' = min(g, limit),
@@ -99,12 +108,17 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
  * path (GROUPED only where the formats allow it). */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_path;
 
-/* q8 activations of T rows of width H, structure-of-arrays:
- *   qs    int8  [T, H]      quants, |q| <= 127
- *   d     fp32  [T, H / B]  per-block scale (B = 256 for Q8_K, 32 for Q8_32), a = d * q
- *   bsums int16 [T, H / 16] sum of the quants of each 16 elements (Q8_K only;
- *                           NULL for Q8_32)
- * All three are device pointers, 16-byte aligned. */
+/* Quantized activations of T rows of width H, structure-of-arrays:
+ *   qs    int8  [T, H]      q8 quants, |q| <= 127 (Q8_K, Q8_32); MXFP8: E4M3
+ *                           codes, each block of 32 pair-interleaved (byte 2j =
+ *                           element j, byte 2j + 1 = element j + 16, the pairing
+ *                           of an MXFP4 block's nibble bytes)
+ *   d     fp32  [T, H / B]  q8 per-block scale (B = 256 for Q8_K, 32 for Q8_32),
+ *                           a = d * q; NULL for MXFP8
+ *   bsums int16 [T, H / 16] sum of the quants of each 16 elements (Q8_K only)
+ *   scales uint8 [T, S]     MXFP8 only: E8M0 block scales, rows padded to
+ *                           S = 16 * ceil(H / 512) bytes; a = 2^(s - 127) e4m3(q)
+ * Device pointers, 16-byte aligned. */
 typedef struct {
   int8_t* qs;
   float* d;
@@ -112,6 +126,7 @@ typedef struct {
   int32_t fmt; /* moe_afmt */
   int32_t T;
   int32_t H;
+  uint8_t* scales;
 } moe_qact;
 
 /* One MoE layer. Host struct; every pointer in it is a device pointer.
@@ -144,6 +159,8 @@ typedef struct {
  *    shape as the routed experts) or all NULL. sh_gate_vec fp32 [H] or NULL:
  *    shared-expert weight sigmoid(sh_gate_vec . x), or 1 when NULL.
  *  path: moe_path (0 = AUTO).
+ *  act_quant: moe_actq (0 = Q8). MXFP8 needs MXFP4 gate, up and down and a
+ *    path other than GEMV (MOE_EUNSUPPORTED otherwise).
  */
 typedef struct {
   int32_t hidden;
@@ -171,6 +188,7 @@ typedef struct {
   const void* sh_down;
   const float* sh_gate_vec;
   int32_t path;
+  int32_t act_quant;
 } moe_layer_desc;
 
 /* ABI version (MOE_ABI_VERSION) and a static message for a status. */
@@ -186,9 +204,13 @@ MOE_API size_t moe_workspace_size(const moe_layer_desc* desc, int T);
 /* Activation quantization. x: device [T, H] fp32 or bf16 (bf16 is upcast
  * exactly). Per block of B values: amax = max |x|; amax == 0 gives d = 0 and
  * q = 0; otherwise iscale = 127/amax, q = clamp(rne(x * iscale), -127, 127) and
- * d = amax/127, every step in IEEE fp32. out: host struct whose qs, d (and
- * bsums for Q8_K) point to caller device buffers; fmt, T and H are filled in.
- * Source: Pulsar README, numerics notes (activations quantized to q8_0/q8_K). */
+ * d = amax/127, every step in IEEE fp32. MXFP8 (H % 32 == 0): per block of 32,
+ * scale byte s = floor(log2 amax) - 8 + 127 within [0, 254] (0 for amax 0) and
+ * codes rne_e4m3(x / 2^(s - 127)) saturated at +-448, zero as +0, stored
+ * pair-interleaved (see moe_qact). out: host struct whose qs, d (and bsums for
+ * Q8_K; scales for MXFP8) point to caller device buffers; fmt, T and H are
+ * filled in. Sources: Pulsar README, numerics notes (activations quantized to
+ * q8_0/q8_K); OCP MX v1.0 §6.3 for MXFP8. */
 MOE_API moe_status moe_quantize_act_q8k(const void* x, moe_dtype dtype, int T, int H, moe_afmt fmt,
                                 moe_qact* out, hipStream_t stream);
 

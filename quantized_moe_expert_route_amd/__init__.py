@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_route.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOWORKSPACE, MOE_EHIP = range(5)
 (MOE_WFMT_Q4_K, MOE_WFMT_Q6_K, MOE_WFMT_MXFP4, MOE_WFMT_Q5_K, MOE_WFMT_Q2_K, MOE_WFMT_Q3_K,
  MOE_WFMT_Q4_0, MOE_WFMT_Q5_1) = range(8)
-MOE_AFMT_Q8_K, MOE_AFMT_Q8_32 = range(2)
+MOE_AFMT_Q8_K, MOE_AFMT_Q8_32, MOE_AFMT_MXFP8 = range(3)
+MOE_ACTQ_Q8, MOE_ACTQ_MXFP8 = range(2)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = range(2)
 MOE_ROUTER_SOFTMAX, MOE_ROUTER_SIGMOID = range(2)
 MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = range(2)
@@ -49,7 +50,8 @@ class MoeError(RuntimeError):
 
 class MoeQact(C.Structure):
     _fields_ = [("qs", C.c_void_p), ("d", C.c_void_p), ("bsums", C.c_void_p),
-                ("fmt", C.c_int32), ("T", C.c_int32), ("H", C.c_int32)]
+                ("fmt", C.c_int32), ("T", C.c_int32), ("H", C.c_int32),
+                ("scales", C.c_void_p)]
 
 
 class MoeLayerDesc(C.Structure):
@@ -63,7 +65,7 @@ class MoeLayerDesc(C.Structure):
         ("b_gate", C.c_void_p), ("b_up", C.c_void_p), ("b_down", C.c_void_p),
         ("act", C.c_int32), ("act_alpha", C.c_float), ("act_limit", C.c_float),
         ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
-        ("sh_gate_vec", C.c_void_p), ("path", C.c_int32),
+        ("sh_gate_vec", C.c_void_p), ("path", C.c_int32), ("act_quant", C.c_int32),
     ]
 
 
@@ -230,9 +232,14 @@ def moe_test_preact(desc, xq: MoeQact, T, ids, which, out, ws, ws_bytes, stream=
                                  _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def qact(qs, d, bsums, fmt: int, T: int, H: int) -> MoeQact:
-    """A moe_qact over caller buffers."""
-    return MoeQact(_ptr(qs), _ptr(d), _ptr(bsums), fmt, T, H)
+def qact(qs, d, bsums, fmt: int, T: int, H: int, scales=None) -> MoeQact:
+    """A moe_qact over caller buffers (scales: MXFP8 E8M0 rows)."""
+    return MoeQact(_ptr(qs), _ptr(d), _ptr(bsums), fmt, T, H, _ptr(scales))
+
+
+def mx8_scale_pitch(H: int) -> int:
+    """Bytes per row of MXFP8 scales (H / 32 rounded up to a multiple of 16)."""
+    return (H // 32 + 15) // 16 * 16
 
 
 # ------------------------------------------------------------------ HIP events

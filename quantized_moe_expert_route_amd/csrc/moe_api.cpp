@@ -54,9 +54,14 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
   if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_GEMV && d->path != MOE_PATH_GROUPED)
     return MOE_EINVAL;
+  if (d->act_quant != MOE_ACTQ_Q8 && d->act_quant != MOE_ACTQ_MXFP8) return MOE_EINVAL;
   for (int f : {d->fmt_gate, d->fmt_up, d->fmt_down})
     if (!known_fmt(f)) return MOE_EINVAL;
   if (d->fmt_gate != d->fmt_up) return MOE_EUNSUPPORTED;
+  // MXFP8 activations: MXFP4 experts on the block-scaled MFMA path only
+  if (d->act_quant == MOE_ACTQ_MXFP8 &&
+      (d->fmt_gate != MOE_WFMT_MXFP4 || d->fmt_down != MOE_WFMT_MXFP4 || d->path == MOE_PATH_GEMV))
+    return MOE_EUNSUPPORTED;
   if (H % block_elems(d->fmt_gate) != 0 || H % 32 != 0) return MOE_EINVAL;
   if (F % block_elems(d->fmt_down) != 0 || F % 32 != 0) return MOE_EINVAL;
   const size_t rb_gu = static_cast<size_t>(H / block_elems(d->fmt_gate)) * block_bytes(d->fmt_gate);
@@ -100,6 +105,7 @@ KArgs make_args(const moe_layer_desc* d, int T) {
   a.sh_gate = d->sh_gate; a.sh_up = d->sh_up; a.sh_down = d->sh_down;
   a.sh_gate_vec = d->sh_gate_vec;
   a.has_shared = d->sh_gate != nullptr;
+  a.mx8 = d->act_quant == MOE_ACTQ_MXFP8;
   return a;
 }
 
@@ -124,6 +130,8 @@ void bind_ws(KArgs& a, const WsLayout& L, void* ws) {
   a.present = reinterpret_cast<int32_t*>(b + L.present);
   a.tiles = reinterpret_cast<GTile*>(b + L.tiles);
   a.part = reinterpret_cast<float*>(b + L.part);
+  a.xe = L.xe ? b + L.xe : nullptr;
+  a.he = L.he ? b + L.he : nullptr;
 }
 
 // Per-kernel (start, stop) event pairs of moe_layer_forward_timed.
@@ -171,6 +179,7 @@ static size_t expert_block_bytes(const moe_layer_desc* d) {
 }
 
 bool use_grouped(const moe_layer_desc* d, int T) {
+  if (d->act_quant == MOE_ACTQ_MXFP8) return T >= 1;  // block-scaled MFMA tiles at every T
   auto tiled = [](int f) { return f == FMT_Q4_K || f == FMT_Q6_K; };
   if (!tiled(d->fmt_gate) || !tiled(d->fmt_down) || T < 1) return false;
   if (d->path == MOE_PATH_GEMV) return false;
@@ -181,7 +190,7 @@ bool use_grouped(const moe_layer_desc* d, int T) {
   return static_cast<double>(T) * slots * eb >= kGroupedMinPairBytes;
 }
 
-WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped) {
+WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped, bool mx8) {
   WsLayout L;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
@@ -207,15 +216,22 @@ WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool group
     L.present = take(P * 4);
     L.tiles = take(static_cast<size_t>(max_tiles(T, k, E, has_shared)) * sizeof(GTile));
     L.part = take(P * H * 4);
+    L.xe = mx8 ? take(static_cast<size_t>(T) * mx8_pitch(H)) : 0;
+    L.he = mx8 ? take(P * mx8_pitch(F)) : 0;
   } else {
     // q8 of h for an MXFP4 down, quantized once per pair: fp16 pairs + scales
     L.hqs = take(P * (F / 32) * 80);  // 80 bytes per 32-value block (kApPitch pairs)
     L.hd = take(P * (F / 32) * 4);
     L.hbs = 0;
-    L.rpart = L.pair_tmp = L.plist = L.present = L.tiles = L.part = 0;
+    L.rpart = L.pair_tmp = L.plist = L.present = L.tiles = L.part = L.xe = L.he = 0;
   }
   L.total = off;
   return L;
+}
+
+static WsLayout ws_of(const moe_layer_desc* d, int T, bool grouped) {
+  return ws_layout(d->hidden, d->ffn, d->n_expert, d->top_k, T, d->sh_gate != nullptr, grouped,
+                   d->act_quant == MOE_ACTQ_MXFP8);
 }
 
 }  // namespace moe
@@ -240,13 +256,23 @@ const char* moe_status_str(moe_status s) {
 size_t moe_workspace_size(const moe_layer_desc* desc, int T) {
   if (validate_desc(desc) != MOE_OK || T < 0 || T > kMaxTokens) return 0;
   const bool g = use_grouped(desc, T);
-  return ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
-                   desc->sh_gate != nullptr, g).total;
+  return ws_of(desc, T, g).total;
 }
 
 moe_status moe_quantize_act_q8k(const void* x, moe_dtype dtype, int T, int H, moe_afmt fmt,
                                 moe_qact* out, hipStream_t stream) {
   if (validate_x(x, dtype) != MOE_OK || !out) return MOE_EINVAL;
+  if (fmt == MOE_AFMT_MXFP8) {
+    if (T < 0 || H <= 0 || H % 32 != 0) return MOE_EINVAL;
+    if (!out->qs || !out->scales || !aligned(out->qs, 16) || !aligned(out->scales, 16))
+      return MOE_EINVAL;
+    out->fmt = fmt;
+    out->T = T;
+    out->H = H;
+    if (T == 0) return MOE_OK;
+    return hip_status(launch_quant_mx8(x, dtype, T, H, reinterpret_cast<uint8_t*>(out->qs),
+                                       out->scales, stream, Ev{}));
+  }
   if (fmt != MOE_AFMT_Q8_K && fmt != MOE_AFMT_Q8_32) return MOE_EINVAL;
   const int B = fmt == MOE_AFMT_Q8_K ? 256 : 32;
   if (T < 0 || H <= 0 || H % B != 0) return MOE_EINVAL;
@@ -270,8 +296,7 @@ moe_status moe_route_topk(const moe_layer_desc* desc, const void* x, moe_dtype d
   if (!aligned(ids, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4))) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
   const bool g = use_grouped(desc, T);
-  const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
-                               desc->sh_gate != nullptr, g);
+  const WsLayout L = ws_of(desc, T, g);
   if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
   if (T == 0) return MOE_OK;
   KArgs a = make_args(desc, T);
@@ -301,7 +326,14 @@ static bool path_fits(const KArgs& a, bool grouped) { return grouped || gemv_fit
 static moe_status expert_ffn_impl(KArgs& a, bool grouped, bool routing_given, hipStream_t stream,
                                   Stages& st) {
   hipError_t e;
-  if (grouped) {
+  if (grouped && a.mx8) {
+    const int mt = max_tiles(a.T, a.k, a.E, a.has_shared);
+    e = launch_bucket(a, stream, st.next());
+    if (e == hipSuccess) e = launch_gateup_mx(a, mt, stream, st.next());
+    if (e == hipSuccess) e = launch_hquant_mx8(a, stream, st.next());
+    if (e == hipSuccess) e = launch_down_mx(a, mt, stream, st.next());
+    if (e == hipSuccess) e = launch_combine(a, stream, st.next());
+  } else if (grouped) {
     e = launch_bucket(a, stream, st.next());
     if (e == hipSuccess) e = launch_gateup_grouped(a, stream, st.next());
     if (e == hipSuccess) e = launch_hquant(a, stream, st.next());
@@ -315,8 +347,11 @@ static moe_status expert_ffn_impl(KArgs& a, bool grouped, bool routing_given, hi
   return hip_status(e);
 }
 
-// q8 of x as the layer's gate/up rows consume it, for T tokens.
+// Quantized x as the layer's gate/up rows consume it, for T tokens.
 static bool qact_ok(const moe_layer_desc* desc, const moe_qact* xq, int T) {
+  if (desc->act_quant == MOE_ACTQ_MXFP8)
+    return xq->fmt == MOE_AFMT_MXFP8 && xq->T >= T && xq->H == desc->hidden && xq->qs &&
+           xq->scales && aligned(xq->qs, 16) && aligned(xq->scales, 16);
   const int want_afmt = act_fmt(desc->fmt_gate);
   if (xq->fmt != want_afmt || xq->T < T || xq->H != desc->hidden) return false;
   if (!xq->qs || !xq->d || !aligned(xq->qs, 16) || !aligned(xq->d, 4)) return false;
@@ -335,14 +370,14 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_qact* xq, const 
   if (!aligned(ids, 4) || !aligned(w, 4) || !aligned(y, 16)) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
   const bool g = use_grouped(desc, T);
-  const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
-                               desc->sh_gate != nullptr, g);
+  const WsLayout L = ws_of(desc, T, g);
   if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
   if (T == 0) return MOE_OK;
   KArgs a = make_args(desc, T);
   bind_ws(a, L, ws);
   a.x = x; a.x_dtype = dtype;
   a.xqs = xq->qs; a.xd = xq->d; a.xbs = xq->bsums;
+  if (a.mx8) a.xe = xq->scales;
   a.ids = const_cast<int32_t*>(ids);
   a.w = const_cast<float*>(w);
   a.y = y;
@@ -364,8 +399,7 @@ static moe_status check_forward(const moe_layer_desc* desc, const void* x, moe_d
   if ((ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4))) return MOE_EINVAL;
   if (events && n_events < 0) return MOE_EINVAL;
   *grouped = use_grouped(desc, T);
-  *L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
-                 desc->sh_gate != nullptr, *grouped);
+  *L = ws_of(desc, T, *grouped);
   return MOE_OK;
 }
 
@@ -529,13 +563,13 @@ moe_status moe_test_preact(const moe_layer_desc* desc, const moe_qact* xq, int T
   if (!aligned(ids, 4) || !aligned(out, 16)) return MOE_EINVAL;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
   const bool g = use_grouped(desc, T);
-  const WsLayout L = ws_layout(desc->hidden, desc->ffn, desc->n_expert, desc->top_k, T,
-                               desc->sh_gate != nullptr, g);
+  const WsLayout L = ws_of(desc, T, g);
   if (ws_bytes < L.total) return MOE_ENOWORKSPACE;
   if (T == 0) return MOE_OK;
   KArgs a = make_args(desc, T);
   bind_ws(a, L, ws);
   a.xqs = xq->qs; a.xd = xq->d; a.xbs = xq->bsums;
+  if (a.mx8) a.xe = xq->scales;
   a.ids = const_cast<int32_t*>(ids);
   a.h = out;
   a.act = which ? ACT_PRE_UP : ACT_PRE_GATE;
@@ -543,7 +577,9 @@ moe_status moe_test_preact(const moe_layer_desc* desc, const moe_qact* xq, int T
   hipError_t e;
   if (g) {
     e = launch_bucket(a, stream, Ev{});
-    if (e == hipSuccess) e = launch_gateup_grouped(a, stream, Ev{});
+    if (e == hipSuccess)
+      e = a.mx8 ? launch_gateup_mx(a, max_tiles(a.T, a.k, a.E, a.has_shared), stream, Ev{})
+                : launch_gateup_grouped(a, stream, Ev{});
   } else {
     e = launch_gateup(a, true, stream, Ev{});
   }

@@ -310,6 +310,59 @@ __device__ __forceinline__ void quant_wave(const float v[4], bool valid, int lan
   }
 }
 
+// ---------------------------------------------------------------- MXFP8
+// OCP MX v1.0 MXFP8 (E4M3 elements, one E8M0 scale per 32). Code of the E4M3
+// value nearest to y (ties to even), saturating at +-448; zero -> +0.
+// Normal range (|y| >= 2^-6): the fp32 bits rounded to 3 mantissa bits (the
+// carry moves into the exponent), rebiased from 127 to 7; below: multiples of
+// the smallest subnormal 2^-9 (8 of them is the smallest normal, code 0x08).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t bits = __float_as_uint(y), mag = bits & 0x7FFFFFFFu;
+  uint32_t c;
+  if (mag >= 0x3C800000u) {  // 2^-6
+    const uint32_t r = mag + 0x7FFFFu + ((mag >> 20) & 1u);
+    c = min((r >> 20) - (120u << 3), 0x7Eu);
+  } else {
+    c = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(mag) * 512.0f));
+  }
+  return c == 0 ? 0u : (c | ((bits >> 24) & 0x80u));
+}
+
+// Scale byte of a block with maximum magnitude amax: floor(log2 amax) - 8
+// (8 = E4M3's largest normal exponent) + 127, within [0, 254]; 0 for amax 0.
+__device__ __forceinline__ int mx8_scale_byte(float amax) {
+  if (amax == 0.0f) return 0;
+  const int k = __builtin_amdgcn_frexp_expf(amax);  // amax = f 2^k, f in [0.5, 1)
+  return min(max(k - 1 - 8 + 127, 0), 254);
+}
+
+// One wave quantizes a 256-value piece (lane l holds elements 4l .. 4l + 3;
+// 8 lanes per block of 32) to MXFP8 and stores each block pair-interleaved:
+// byte 2j = element j, byte 2j + 1 = element j + 16 (the pairing of an MXFP4
+// block's nibble bytes, and the K order of the block-scaled MFMA). q points at
+// the piece's first block, e at its first scale byte. valid: lane's 4 values
+// exist (whole blocks are valid or not).
+__device__ __forceinline__ void quant_wave_mx8(const float (&v)[4], bool valid, int lane,
+                                               uint8_t* q, uint8_t* e) {
+  float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  am = max8(am);
+  const int sb = mx8_scale_byte(am);
+  uint32_t c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = e4m3_code(__builtin_ldexpf(v[i], 127 - sb));
+  const uint32_t mine = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  // the lane 4 ahead holds elements 16.. of the same positions (row_shl:4)
+  const uint32_t other = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(mine), 0x104, 0xF, 0xF, false));
+  const int bl = lane >> 3, j = lane & 7;  // block, lane in block
+  if (valid && j < 4) {
+    const uint32_t lo = __builtin_amdgcn_perm(other, mine, 0x05010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(other, mine, 0x07030602u);
+    *reinterpret_cast<uint2*>(q + 32 * bl + 8 * j) = make_uint2(lo, hi);
+  }
+  if (valid && j == 0) e[bl] = static_cast<uint8_t>(sb);
+}
+
 // fp16 pairs per block in the MXFP4 activation layout: 16 used + 4 of padding
 // (80 bytes), so that lanes reading consecutive blocks with 16-byte loads hit
 // different LDS banks.

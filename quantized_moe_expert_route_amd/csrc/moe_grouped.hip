@@ -662,8 +662,23 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
 
 // ================================================================== kernels
 
-// q8 of one 256-element piece of x (job = token * pieces + piece), one wave.
+// q8 of one 256-element piece of x (job = token * pieces + piece), one wave;
+// MXFP8 layers: MXFP8 of the piece (H a multiple of 32: the last piece may be
+// partial, with whole blocks).
 __device__ __forceinline__ void router_quant_wave(const KArgs& a, int job, int lane) {
+  if (a.mx8) {
+    const int pieces = (a.H + 255) >> 8;
+    const int t = job / pieces, pc = job - t * pieces;
+    if (t >= a.T) return;
+    const int e0 = pc * 256 + 4 * lane;
+    const bool valid = e0 < a.H;
+    float v[4];
+    load_x4(a.x, a.x_dtype, static_cast<size_t>(t) * a.H + (valid ? e0 : 0), v);
+    quant_wave_mx8(v, valid, lane,
+                   reinterpret_cast<uint8_t*>(a.xqs) + static_cast<size_t>(t) * a.H + pc * 256,
+                   a.xe + static_cast<size_t>(t) * mx8_pitch(a.H) + pc * 8);
+    return;
+  }
   const int pieces = a.H >> 8;
   const int t = job / pieces, pc = job - t * pieces;
   if (t >= a.T) return;
@@ -1194,7 +1209,8 @@ int max_tiles(int T, int k, int E, int has_shared) {
 hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hipStream_t s,
                                  Ev ev) {
   const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
-  const int nq = quant ? (a.T * (a.H / 256) + 3) / 4 : 0;
+  const int pieces = a.mx8 ? (a.H + 255) / 256 : a.H / 256;
+  const int nq = quant ? (a.T * pieces + 3) / 4 : 0;
   if (router_blocked(a.T, a.E)) {
     const int n_et2 = (E1 + 31) / 32, n_tt2 = (a.T + 31) / 32;
     const int n_work = n_tt2 * n_et2;  // tile pairs, each in all 8 K slices

@@ -115,14 +115,20 @@ struct KArgs {
   float* part;         // [P, H] routing-weighted expert outputs per pair
   // test export of the tile kernels' integer super-block sums (nullptr otherwise)
   int32_t* dump;
+  // MXFP8 activation numerics (MXFP4 layers on the block-scaled MFMA path):
+  // x codes in xqs and h codes in hqs (E4M3, pair-interleaved per block), their
+  // E8M0 scale rows here (pitch mx8_pitch(K) bytes)
+  int mx8;
+  uint8_t* xe;         // [T, mx8_pitch(H)]
+  uint8_t* he;         // [P, mx8_pitch(F)]
 };
 
 // Workspace layout (byte offsets from the base, each 256-aligned).
 struct WsLayout {
   size_t counters, xqs, xd, xbs, logits, ids, w, shw, slots, h, hqs, hd, hbs, rpart, pair_tmp,
-      plist, present, tiles, part, total;
+      plist, present, tiles, part, xe, he, total;
 };
-WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped);
+WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped, bool mx8);
 
 // Dynamic LDS a workgroup may use (bytes).
 constexpr size_t kMaxLds = 64 * 1024;
@@ -170,6 +176,15 @@ hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_hquant(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_combine(const KArgs& a, hipStream_t s, Ev ev);
+// MX path (moe_mx.hip): bytes per row of MXFP8 scales of a row of width K (K /
+// 32 rounded up to a multiple of 16); standalone MXFP8 quantization, tile
+// kernels and h quantization.
+__host__ __device__ inline int mx8_pitch(int K) { return ((K / 32 + 15) / 16) * 16; }
+hipError_t launch_quant_mx8(const void* x, int dtype, int T, int H, uint8_t* q, uint8_t* e,
+                            hipStream_t s, Ev ev);
+hipError_t launch_gateup_mx(const KArgs& a, int max_tiles, hipStream_t s, Ev ev);
+hipError_t launch_hquant_mx8(const KArgs& a, hipStream_t s, Ev ev);
+hipError_t launch_down_mx(const KArgs& a, int max_tiles, hipStream_t s, Ev ev);
 hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_t stride,
                              const int8_t* qs, const float* d, const int16_t* bs,
                              int32_t* out, hipStream_t s);

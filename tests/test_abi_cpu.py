@@ -31,7 +31,7 @@ def test_library_exports_header_symbols():
 
 
 def test_version_and_status_strings():
-    assert M.moe_abi_version() == 2
+    assert M.moe_abi_version() == 3
     for s in range(5):
         assert M.moe_status_str(s)
     assert M.moe_status_str(99) == "unknown status"
