@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, AMD published
 I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, AMD published (5.0 POP/s)
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, AMD published (5.0 PFLOP/s)
 
 
 def parse():
@@ -45,7 +46,8 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="qwen3.6-35b-a3b")
-    p.add_argument("--extra", default="gpt-oss-20b,deepseek-v4-flash,kimi-k2",
+    p.add_argument("--extra", default="gpt-oss-20b,deepseek-v4-flash,kimi-k2,gpt-oss-20b-t16,"
+                                      "gpt-oss-20b-mx8",
                    help="further workloads timed in the same run (comma list; '' for none)")
     p.add_argument("--extra-reps", type=int, default=5, help="graph replays per extra workload")
     p.add_argument("--copies", type=int, default=None, help="layer copies rotated in HBM")
@@ -69,7 +71,8 @@ def parse():
 
 
 DEFAULT_COPIES = {"tiny": 1, "qwen3.6-35b-a3b": 40, "gpt-oss-20b": 24, "deepseek-v4-flash": 4,
-                  "kimi-k2": 2, "qwen3.6-35b-a3b-q5k": 40, "qwen3.6-35b-a3b-q2k": 40}
+                  "kimi-k2": 2, "qwen3.6-35b-a3b-q5k": 40, "qwen3.6-35b-a3b-q2k": 40,
+                  "gpt-oss-20b-t16": 8, "gpt-oss-20b-mx8": 8}
 
 
 def rotation(copies: int) -> int:
@@ -234,7 +237,7 @@ def run_workload(args, name: str, headline: bool, probes: dict, th: int):
     uniq = [len(np.unique(r)) + (1 if cfg.shared else 0) for r in realized]
     uniq_mean = float(np.mean(uniq))
     sel_bytes = uniq_mean * cfg.expert_algo_bytes
-    path = "grouped" if n_st == 7 else "gemv"
+    path = ("grouped_mx" if cfg.act_quant else "grouped") if n_st == 7 else "gemv"
     algo = algo_bytes(cfg, path, uniq_mean)
     kn = kernel_names(cfg, path)
     dom = max(("gateup", "down"), key=lambda k: stage_avg_us.get(k, 0.0))
@@ -271,7 +274,7 @@ def run_workload(args, name: str, headline: bool, probes: dict, th: int):
     for k in ("gateup", "down"):
         res[f"{k}_GBps"] = round(algo[k] / (stage_avg_us[k] * 1e-6) / 1e9, 1)
         res[f"{k}_kernel"] = kn[k]
-    if path == "grouped":
+    if path in ("grouped", "grouped_mx"):
         # routed tokens per active expert in a chunk (realized histogram)
         cnt = np.concatenate([np.bincount(r.ravel(), minlength=cfg.E) for r in realized])
         act = cnt[cnt > 0]
@@ -282,18 +285,22 @@ def run_workload(args, name: str, headline: bool, probes: dict, th: int):
                                         int(((act >= 4) & (act < 8)).sum()),
                                         int(((act >= 8) & (act < 16)).sum()),
                                         int((act >= 16).sum())]}
-        # int8 MFMA work of the tile kernels: 2 H F per routed (token, slot) pair
-        # and matrix (algorithmic; padded tile rows are not counted)
+        # MFMA work of the tile kernels: 2 H F per routed (token, slot) pair
+        # and matrix (algorithmic; padded tile rows are not counted). int8 MFMA
+        # on the q8 path; block-scaled fp8 x fp4 MFMA (priced at the dense fp8
+        # peak) on the MX path
         P = T * cfg.k + (T if cfg.shared else 0)
         ops = {"gateup": P * 2 * 2 * cfg.H * cfg.F, "down": P * 2 * cfg.H * cfg.F}
+        peak = FP8_PEAK_TFLOPS if path == "grouped_mx" else I8_PEAK_TOPS
         mf = {}
         for k in ("gateup", "down"):
             tops = ops[k] / (stage_avg_us[k] * 1e-6) / 1e12
-            mf[k] = {"kernel": kn[k], "int8_ops_per_launch": ops[k], "achieved_TOPS": round(tops, 1),
-                     "frac_of_peak": round(tops / I8_PEAK_TOPS, 4)}
-        res["mfma"] = {"peak_TOPS": I8_PEAK_TOPS,
-                       "measured_TOPS_16x16x32": probes.get("mfma_i32_16x16x32_i8_TOPS"),
-                       "measured_TOPS_16x16x64": probes.get("mfma_i32_16x16x64_i8_TOPS"),
+            mf[k] = {"kernel": kn[k], "ops_per_launch": ops[k], "achieved_T_per_s": round(tops, 1),
+                     "frac_of_peak": round(tops / peak, 4)}
+        res["mfma"] = {"op": "f8f6f4 block-scaled" if path == "grouped_mx" else "int8",
+                       "peak_T_per_s": peak,
+                       "measured_int8_TOPS_16x16x32": probes.get("mfma_i32_16x16x32_i8_TOPS"),
+                       "measured_int8_TOPS_16x16x64": probes.get("mfma_i32_16x16x64_i8_TOPS"),
                        **mf}
     keep = (data, cfg)
     del dl, xs, ws, y, ids, w, evs
@@ -486,7 +493,7 @@ def algo_bytes(cfg, path: str, unique_experts: float) -> dict:
     grouped path each selected expert's rows once (unique experts + shared).
     Padding bytes of a row are not counted."""
     pairs = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
-    units = unique_experts if path == "grouped" else pairs
+    units = unique_experts if path in ("grouped", "grouped_mx") else pairs
     return {
         "gateup": units * 2 * cfg.F * gen_row_bytes(cfg.fmt_gu, cfg.H),
         "down": units * cfg.H * gen_row_bytes(cfg.fmt_d, cfg.F),
@@ -511,6 +518,9 @@ def kernel_names(cfg, path: str) -> dict:
         else:
             dn = "k_down_mx" if cfg.fmt_d == mx else "k_down"
         return {"router": "k_router", "gateup": gu, "down": dn}
+    rt = "k_router_mfma22" if cfg.T > 16 and cfg.E + 1 > 16 else "k_router_mfma"  # 2 x 2 blocked
+    if path == "grouped_mx":
+        return {"router": rt, "gateup": "k_gmx<0>", "down": "k_gmx<1>"}
     nb = cfg.biases
     gu = "k_glds_q4k<0>" if cfg.fmt_gu == gen.Q4_K and not nb else "k_gu_grouped"
     if cfg.fmt_d == gen.Q4_K and not nb:
@@ -519,13 +529,13 @@ def kernel_names(cfg, path: str) -> dict:
         dn = "k_glds_q6k_down"
     else:
         dn = "k_down_grouped"
-    rt = "k_router_mfma22" if cfg.T > 16 and cfg.E + 1 > 16 else "k_router_mfma"  # 2 x 2 blocked
     return {"router": rt, "gateup": gu, "down": dn}
 
 
 _PATH_SOURCES = {
     "gemv": ("moe_kernels.hip", "moe_device.h", "moe_internal.h"),
     "grouped": ("moe_grouped.hip", "moe_device.h", "moe_internal.h"),
+    "grouped_mx": ("moe_mx.hip", "moe_grouped.hip", "moe_device.h", "moe_internal.h"),
 }
 
 

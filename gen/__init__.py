@@ -329,6 +329,19 @@ CONFIGS = {
         fmt_gu=Q2_K, fmt_d=Q2_K,
         description="Qwen3.6-35B-A3B-shaped decode layer with Q2_K experts: H 2048, 256 experts "
                     "top-8 softmax + shared, F 512, Q2_K"),
+    # the gpt-oss shape as a 16-token verify chunk: the q8 per-pair path and the
+    # MXFP8-activation block-scaled MFMA path (not one of the five workloads)
+    "gpt-oss-20b-t16": LayerConfig(
+        "gpt-oss-20b-t16", H=2880, F=2880, E=32, k=4, T=16, seed=2, fmt_gu=MXFP4, fmt_d=MXFP4,
+        act=SWIGLU_OAI, biases=True, x_bf16=True,
+        description="gpt-oss-20B-shaped 16-token chunk: H 2880, 32 experts top-4 softmax, "
+                    "F 2880, MXFP4 + fp32 biases, clamped SwiGLU, bf16 x, q8 activations"),
+    "gpt-oss-20b-mx8": LayerConfig(
+        "gpt-oss-20b-mx8", H=2880, F=2880, E=32, k=4, T=16, seed=2, fmt_gu=MXFP4, fmt_d=MXFP4,
+        act=SWIGLU_OAI, biases=True, x_bf16=True, act_quant=1,
+        description="gpt-oss-20B-shaped 16-token chunk: H 2880, 32 experts top-4 softmax, "
+                    "F 2880, MXFP4 + fp32 biases, clamped SwiGLU, bf16 x, MXFP8 activations "
+                    "on the block-scaled MFMA"),
 }
 CONFIG_ORDER = ["tiny", "qwen3.6-35b-a3b", "gpt-oss-20b", "deepseek-v4-flash", "kimi-k2"]
 
