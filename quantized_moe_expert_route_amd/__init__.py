@@ -38,6 +38,9 @@ ABI_FUNCTIONS = (
     "moe_layer_stage_count", "moe_layer_stage_name", "moe_test_block_dots",
     "moe_test_tile_dots", "moe_test_tile_dots_ws", "moe_test_preact",
     "moe_layer_forward_noalloc", "moe_probe_read_wall", "moe_probe_mfma_i8",
+    # expert pool (include/moe_pool.h)
+    "moe_pool_create", "moe_pool_destroy", "moe_pool_host_slab", "moe_pool_layer_tables",
+    "moe_pool_resolve", "moe_pool_prefetch", "moe_pool_get_stats", "moe_pool_policy_trace",
 )
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -52,6 +55,21 @@ class MoeQact(C.Structure):
     _fields_ = [("qs", C.c_void_p), ("d", C.c_void_p), ("bsums", C.c_void_p),
                 ("fmt", C.c_int32), ("T", C.c_int32), ("H", C.c_int32),
                 ("scales", C.c_void_p)]
+
+
+class MoePoolConfig(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("n_experts", C.c_int32), ("slab_bytes", C.c_size_t),
+                ("up_offset", C.c_size_t), ("down_offset", C.c_size_t),
+                ("n_slots", C.c_int32), ("n_transient", C.c_int32)]
+
+
+POOL_STAT_FIELDS = ("epochs", "requests", "hits_resident", "hits_transient", "admitted",
+                    "transient_loads", "promotions", "evictions", "prefetch_loads",
+                    "prefetch_hits", "bytes_h2d")
+
+
+class MoePoolStats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in POOL_STAT_FIELDS]
 
 
 class MoeLayerDesc(C.Structure):
@@ -107,10 +125,23 @@ def lib():
         L.moe_test_tile_dots_ws.argtypes = [i32, i32, i32, i32]
         L.moe_test_tile_dots_ws.restype = sz
         L.moe_test_preact.argtypes = [D, Q, i32, vp, i32, vp, vp, sz, vp]
+        PC = C.POINTER(MoePoolConfig)
+        L.moe_pool_create.argtypes = [PC, C.POINTER(vp)]
+        L.moe_pool_destroy.argtypes = [vp]
+        L.moe_pool_destroy.restype = None
+        L.moe_pool_host_slab.argtypes = [vp, i32, i32]
+        L.moe_pool_host_slab.restype = vp
+        L.moe_pool_layer_tables.argtypes = [vp, i32, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp)]
+        L.moe_pool_resolve.argtypes = [vp, i32, vp, i32, vp]
+        L.moe_pool_prefetch.argtypes = [vp, i32, vp, i32, vp]
+        L.moe_pool_get_stats.argtypes = [vp, C.POINTER(MoePoolStats)]
+        L.moe_pool_policy_trace.argtypes = [PC, i32, vp, vp, vp, vp, vp, vp, vp]
         for n in ("moe_quantize_act_q8k", "moe_route_topk", "moe_expert_ffn", "moe_layer_forward",
                   "moe_layer_forward_timed", "moe_test_block_dots", "moe_test_tile_dots",
                   "moe_test_preact", "moe_layer_forward_noalloc", "moe_probe_read_wall",
-                  "moe_probe_mfma_i8"):
+                  "moe_probe_mfma_i8", "moe_pool_create", "moe_pool_layer_tables",
+                  "moe_pool_resolve", "moe_pool_prefetch", "moe_pool_get_stats",
+                  "moe_pool_policy_trace"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -292,3 +323,90 @@ class HipEvent:
                 hip().hipEventDestroy(self.h)
         except Exception:
             pass
+
+
+# ------------------------------------------------------------------ expert pool
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+class Pool:
+    """moe_pool: pinned host tier + device slot arena (include/moe_pool.h)."""
+
+    def __init__(self, n_layers, n_experts, slab_bytes, up_offset, down_offset, n_slots,
+                 n_transient):
+        self.cfg = MoePoolConfig(n_layers, n_experts, slab_bytes, up_offset, down_offset,
+                                 n_slots, n_transient)
+        h = C.c_void_p()
+        _check("moe_pool_create", lib().moe_pool_create(C.byref(self.cfg), C.byref(h)))
+        self.h = h
+
+    def host_slab(self, layer, expert):
+        """numpy uint8 view of one expert's pinned host slab."""
+        import numpy as np
+        p = lib().moe_pool_host_slab(self.h, layer, expert)
+        if not p:
+            raise IndexError((layer, expert))
+        return np.ctypeslib.as_array((C.c_uint8 * self.cfg.slab_bytes).from_address(p))
+
+    def tables(self, layer):
+        g, u, d = C.c_void_p(), C.c_void_p(), C.c_void_p()
+        _check("moe_pool_layer_tables",
+               lib().moe_pool_layer_tables(self.h, layer, C.byref(g), C.byref(u), C.byref(d)))
+        return g.value, u.value, d.value
+
+    def resolve(self, layer, ids_host, stream=None):
+        import numpy as np
+        ids = np.ascontiguousarray(ids_host, np.int32).ravel()
+        _check("moe_pool_resolve", lib().moe_pool_resolve(self.h, layer, _np_ptr(ids), ids.size,
+                                                          _stream(stream)))
+
+    def prefetch(self, layer, ids_host, stream=None):
+        import numpy as np
+        ids = np.ascontiguousarray(ids_host, np.int32).ravel()
+        _check("moe_pool_prefetch", lib().moe_pool_prefetch(self.h, layer, _np_ptr(ids), ids.size,
+                                                            _stream(stream)))
+
+    def stats(self) -> dict:
+        s = MoePoolStats()
+        _check("moe_pool_get_stats", lib().moe_pool_get_stats(self.h, C.byref(s)))
+        return {n: getattr(s, n) for n in POOL_STAT_FIELDS}
+
+    def close(self):
+        if self.h:
+            lib().moe_pool_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def moe_pool_policy_trace(cfg: MoePoolConfig, ops):
+    """Run the slot policy alone over ops = [(kind 0 resolve / 1 prefetch, layer,
+    ids)]; returns (per-op list of (key, slot, copy) or None for a failed
+    resolve, stats dict without bytes_h2d)."""
+    import numpy as np
+    kind = np.array([o[0] for o in ops], np.int32)
+    layer = np.array([o[1] for o in ops], np.int32)
+    lens = [len(o[2]) for o in ops]
+    off = np.zeros(len(ops) + 1, np.int32)
+    off[1:] = np.cumsum(lens)
+    ids = np.concatenate([np.asarray(o[2], np.int32) for o in ops]) if ops else np.zeros(0, np.int32)
+    out = np.zeros(3 * max(1, int(off[-1])), np.int32)
+    n_out = np.zeros(len(ops), np.int32)
+    stats = np.zeros(10, np.int64)
+    _check("moe_pool_policy_trace",
+           lib().moe_pool_policy_trace(C.byref(cfg), len(ops), _np_ptr(kind), _np_ptr(layer),
+                                       _np_ptr(off), _np_ptr(ids), _np_ptr(out), _np_ptr(n_out),
+                                       _np_ptr(stats)))
+    res, w = [], 0
+    for n in n_out:
+        if n < 0:
+            res.append(None)
+            continue
+        res.append([tuple(int(v) for v in out[3 * (w + i):3 * (w + i) + 3]) for i in range(n)])
+        w += n
+    return res, dict(zip(POOL_STAT_FIELDS[:10], (int(v) for v in stats)))

@@ -8,7 +8,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_route.so")
-SOURCES = ["moe_kernels.hip", "moe_grouped.hip", "moe_mx.hip", "moe_probe.hip", "moe_api.cpp"]
+SOURCES = ["moe_kernels.hip", "moe_grouped.hip", "moe_mx.hip", "moe_probe.hip", "moe_api.cpp",
+           "moe_pool.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -16,9 +16,13 @@ FAKE = 0x7F0000000000  # 256-aligned address that is never dereferenced
 
 
 def header_functions():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            src = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_header_symbols():
