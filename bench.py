@@ -60,6 +60,12 @@ def parse():
                    help="target wall time of each CPU-baseline leg")
     p.add_argument("--threads", type=int, default=None)
     p.add_argument("--probes", type=int, default=1, help="measure the read wall and MFMA peak")
+    p.add_argument("--pool-layers", type=int, default=8,
+                   help="layers of the expert-pool decode leg (0: skip it)")
+    p.add_argument("--pool-frac", type=float, default=0.25,
+                   help="device slots of the pool leg as a fraction of its experts")
+    p.add_argument("--pool-steps", type=int, default=96)
+    p.add_argument("--pool-warmup", type=int, default=96)
     p.add_argument("--wall-gib", type=int, default=4)
     p.add_argument("--crossover", default="",
                    help="comma list of workloads: time each on both expert-FFN paths at "
@@ -376,6 +382,129 @@ def crossover(args, name: str, th: int) -> dict:
     return {"workload": cfg0.description, "layer_copies": copies, "per_forward": out}
 
 
+def pool_leg(args, th: int) -> dict:
+    """A decode stack larger than its device arena: L Qwen3.6-shaped layers
+    (own routers, Zipf(1.1) selection skew, one set of expert bytes reused by
+    every layer) whose routed experts live in the pool's pinned host tier; the
+    arena holds a fraction of them. Per step and layer: moe_pool_layer_step
+    (route, ids to the host, resolve, optional prefetch of the next layer's
+    predicted experts, quantize, expert FFN), then x += y. Compared with the same
+    stack fully resident (moe_layer_forward per layer, no host round trip), and
+    with an arena that holds every expert (the round-trip cost alone)."""
+    import ctypes as C
+
+    import torch
+
+    import gen
+    import quantized_moe_expert_route_amd as M
+    from gen.device import DeviceLayer
+
+    L = args.pool_layers
+    cfg = gen.CONFIGS["qwen3.6-35b-a3b"].with_(zipf_s=1.1, T=1)
+    t0 = time.time()
+    data0 = gen.make_layer(cfg, threads=th)
+    layers = []
+    for l in range(L):
+        r = data0 if l == 0 else gen.make_layer(cfg.with_(seed=cfg.seed + 97 * l), experts=[])
+        layers.append(gen.LayerData(cfg, r.w_router, r.sel_bias, data0.pool, None, None, None,
+                                    data0.x, None))
+    dls = [DeviceLayer(d) for d in layers]
+    del layers
+    E, k, H = cfg.E, cfg.k, cfg.H
+    n_trans = 64
+    state = {}
+
+    def new_pool(n_slots):
+        pool = M.Pool(L, E, cfg.expert_bytes, cfg.gate_bytes, 2 * cfg.gate_bytes, n_slots, n_trans)
+        for l in range(L):
+            for e in range(E):
+                pool.host_slab(l, e)[:] = data0.pool[e]
+        descs = []
+        for l, dl in enumerate(dls):
+            d = M.MoeLayerDesc()
+            C.pointer(d)[0] = dl.desc
+            d.gate, d.up, d.down = pool.tables(l)
+            descs.append(d)
+        state["pool"], state["descs"] = pool, descs
+        return pool
+
+    setup_s = time.time() - t0
+    T = 1
+    stream = torch.cuda.Stream()
+    ws_n = max(M.moe_pool_step_workspace(dl.desc, T) for dl in dls)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    xs = [torch.from_numpy(gen.make_x(cfg, T=T, x_index=i)[0]).cuda() for i in range(256)]
+
+    def step_resident(x):
+        for l in range(L):
+            M.moe_layer_forward(dls[l].desc, x, M.MOE_DTYPE_F32, T, y, ids, w, ws, ws_n, stream)
+            x = x + y
+        return x
+
+    def step_pool(x, prefetch):
+        pool, descs = state["pool"], state["descs"]
+        for l in range(L):
+            nd = descs[l + 1] if prefetch and l + 1 < L else None
+            pool.layer_step(l, descs[l], nd, x, M.MOE_DTYPE_F32, T, ids, w, y, ws, ws_n, stream)
+            x = x + y
+        return x
+
+    W = args.pool_warmup
+
+    def timed(fn, steps, pool):
+        # warm-up steps fill the hot set; the timed ones use inputs not seen in it
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                fn(xs[i % len(xs)])
+            torch.cuda.synchronize()
+            st0 = pool.stats() if pool else None
+            t = time.perf_counter()
+            for i in range(steps):
+                fn(xs[(W + i) % len(xs)])
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t
+        if not pool:
+            return dt, None
+        st1 = pool.stats()
+        return dt, {kk: st1[kk] - st0[kk] for kk in st1}
+
+    S = args.pool_steps
+    res = {"workload": f"{L}-layer stack of {cfg.description}, Zipf(1.1) selection skew, "
+                       f"decode (1 token), 256 distinct inputs",
+           "layers": L, "experts_total": L * E, "expert_bytes": cfg.expert_algo_bytes,
+           "host_tier_GB": round(L * E * cfg.expert_bytes / 1e9, 2),
+           "transient_slots": n_trans, "steps": S, "warmup_steps": W,
+           "setup_s": round(setup_s, 1),
+           "step": "moe_pool_layer_step per layer (route, ids to host, resolve, optional "
+                   "next-layer prefetch, quantize, expert FFN), then x += y"}
+    dt, _ = timed(step_resident, S, None)
+    res["resident_tokens_per_s"] = round(S / dt, 1)
+    res["resident_us_per_layer"] = round(dt / (S * L) * 1e6, 2)
+    for name, frac, pf in (("pool_all_fit", 1.0, False), ("pool", args.pool_frac, False),
+                           ("pool_prefetch", args.pool_frac, True)):
+        slots = L * E + n_trans if frac >= 1.0 else max(n_trans + 8, int(frac * L * E))
+        pool = new_pool(slots)
+        dt, st = timed(lambda x: step_pool(x, pf), S, pool)
+        req = max(1, st["requests"])
+        res[name] = {
+            "arena_slots": slots, "arena_frac": round(slots / (L * E), 3),
+            "tokens_per_s": round(S / dt, 1),
+            "us_per_layer": round(dt / (S * L) * 1e6, 2),
+            "hit_rate": round((st["hits_resident"] + st["hits_transient"]) / req, 4),
+            "h2d_GB_per_s": round(st["bytes_h2d"] / dt / 1e9, 2),
+            "h2d_bytes_per_token": round(st["bytes_h2d"] / S),
+            "stats": st,
+        }
+        pool.close()
+        state.clear()
+    del dls, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_model() -> str:
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
@@ -452,6 +581,7 @@ def main():
         r, _ = run_workload(args, name, False, probes, th)
         extras[name] = r
     xover = {n: crossover(args, n, th) for n in args.crossover.split(",") if n}
+    pool = pool_leg(args, th) if args.pool_layers > 0 else None
     out = {
         "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (% of peak), 1 MI355X",
         "value": round(head["tokens_per_s"], 1),
@@ -480,6 +610,7 @@ def main():
                 "tokens_per_s", "ms_per_step")},
             "probes": probes,
             **({"crossover": xover} if xover else {}),
+            **({"expert_pool": pool} if pool else {}),
             "workloads": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                               for kk, vv in v.items()} for k, v in extras.items()},
         },

@@ -82,6 +82,24 @@ MOE_API moe_status moe_pool_prefetch(moe_pool* pool, int layer, const int32_t* i
                                      hipStream_t stream);
 MOE_API moe_status moe_pool_get_stats(const moe_pool* pool, moe_pool_stats* out);
 
+/* One layer step of a pool-backed stack, natively: routes x [T, H] with
+ * `desc` into ids / w (device [T, k]), copies the ids to the host, resolves
+ * them into `layer`'s tables; if next_desc is not NULL, routes x with the next
+ * layer's router and prefetches the predicted experts into layer + 1 (the
+ * next layer's input is not known yet: its router on this input is the
+ * prediction, as in the Pulsar README's resolve list); then quantizes x and
+ * runs the expert FFN into y [T, H]. desc's gate/up/down must be this pool's
+ * tables of `layer` (next_desc's those of layer + 1). ws: device scratch of
+ * moe_pool_step_workspace(desc, T) bytes, 256-byte aligned. The call waits for
+ * the routing (host round trip) and returns with the FFN enqueued on stream.
+ * Errors: those of the calls it makes. */
+MOE_API moe_status moe_pool_layer_step(moe_pool* pool, int layer, const moe_layer_desc* desc,
+                                       const moe_layer_desc* next_desc, const void* x,
+                                       moe_dtype dtype, int T, int32_t* ids, float* w, float* y,
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
+/* Workspace of moe_pool_layer_step (0 for an invalid descriptor or T). */
+MOE_API size_t moe_pool_step_workspace(const moe_layer_desc* desc, int T);
+
 /* Test export (host only, no device work): the slot policy of a pool with
  * this config run over n_ops operations. Operation i is a resolve (kind[i] =
  * 0) or a prefetch (kind[i] = 1) of layer[i] with ids[off[i] .. off[i + 1]).

@@ -41,6 +41,7 @@ ABI_FUNCTIONS = (
     # expert pool (include/moe_pool.h)
     "moe_pool_create", "moe_pool_destroy", "moe_pool_host_slab", "moe_pool_layer_tables",
     "moe_pool_resolve", "moe_pool_prefetch", "moe_pool_get_stats", "moe_pool_policy_trace",
+    "moe_pool_layer_step", "moe_pool_step_workspace",
 )
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -136,12 +137,15 @@ def lib():
         L.moe_pool_prefetch.argtypes = [vp, i32, vp, i32, vp]
         L.moe_pool_get_stats.argtypes = [vp, C.POINTER(MoePoolStats)]
         L.moe_pool_policy_trace.argtypes = [PC, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_pool_layer_step.argtypes = [vp, i32, D, D, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_pool_step_workspace.argtypes = [D, i32]
+        L.moe_pool_step_workspace.restype = sz
         for n in ("moe_quantize_act_q8k", "moe_route_topk", "moe_expert_ffn", "moe_layer_forward",
                   "moe_layer_forward_timed", "moe_test_block_dots", "moe_test_tile_dots",
                   "moe_test_preact", "moe_layer_forward_noalloc", "moe_probe_read_wall",
                   "moe_probe_mfma_i8", "moe_pool_create", "moe_pool_layer_tables",
                   "moe_pool_resolve", "moe_pool_prefetch", "moe_pool_get_stats",
-                  "moe_pool_policy_trace"):
+                  "moe_pool_policy_trace", "moe_pool_layer_step"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -367,6 +371,16 @@ class Pool:
         _check("moe_pool_prefetch", lib().moe_pool_prefetch(self.h, layer, _np_ptr(ids), ids.size,
                                                             _stream(stream)))
 
+    def layer_step(self, layer, desc, next_desc, x, dtype, T, ids, w, y, ws, ws_bytes,
+                   stream=None):
+        """moe_pool_layer_step: route, resolve (+ prefetch of layer + 1 when
+        next_desc is given), quantize and expert FFN of one layer."""
+        _check("moe_pool_layer_step",
+               lib().moe_pool_layer_step(self.h, layer, C.byref(desc),
+                                         C.byref(next_desc) if next_desc is not None else None,
+                                         _ptr(x), dtype, T, _ptr(ids), _ptr(w), _ptr(y), _ptr(ws),
+                                         ws_bytes, _stream(stream)))
+
     def stats(self) -> dict:
         s = MoePoolStats()
         _check("moe_pool_get_stats", lib().moe_pool_get_stats(self.h, C.byref(s)))
@@ -382,6 +396,10 @@ class Pool:
             self.close()
         except Exception:
             pass
+
+
+def moe_pool_step_workspace(desc, T: int) -> int:
+    return lib().moe_pool_step_workspace(C.byref(desc), T)
 
 
 def moe_pool_policy_trace(cfg: MoePoolConfig, ops):

@@ -50,6 +50,8 @@ struct moe_pool {
   int next_mirror = 0;
   hipStream_t copy = nullptr;
   hipEvent_t ev_compute = nullptr, ev_copy = nullptr;
+  int32_t* ids_host = nullptr;  // pinned, for moe_pool_layer_step
+  size_t ids_host_n = 0;
   int64_t bytes_h2d = 0;
   std::vector<PoolPolicy::Place> places;
 
@@ -93,6 +95,9 @@ moe_status moe_pool_create(const moe_pool_config* cfg, moe_pool** out) {
              hipSuccess &&
          hipEventCreateWithFlags(&p->mirror_ev[i], hipEventDisableTiming) == hipSuccess;
   }
+  p->ids_host_n = static_cast<size_t>(2048) * MOE_MAX_TOPK;  // tokens x slots of one step
+  ok = ok && hipHostMalloc(reinterpret_cast<void**>(&p->ids_host), p->ids_host_n * 4,
+                           hipHostMallocDefault) == hipSuccess;
   ok = ok && hipStreamCreateWithFlags(&p->copy, hipStreamNonBlocking) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&p->ev_compute, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&p->ev_copy, hipEventDisableTiming) == hipSuccess;
@@ -118,6 +123,7 @@ void moe_pool_destroy(moe_pool* p) {
   if (p->ev_compute) (void)hipEventDestroy(p->ev_compute);
   if (p->ev_copy) (void)hipEventDestroy(p->ev_copy);
   if (p->copy) (void)hipStreamDestroy(p->copy);
+  if (p->ids_host) (void)hipHostFree(p->ids_host);
   if (p->dtab) (void)hipFree(p->dtab);
   if (p->arena) (void)hipFree(p->arena);
   if (p->host) (void)hipHostFree(p->host);
@@ -185,6 +191,88 @@ moe_status moe_pool_get_stats(const moe_pool* p, moe_pool_stats* out) {
                         s.admitted,        s.transient_loads, s.promotions, s.evictions,
                         s.prefetch_loads,  s.prefetch_hits,   p->bytes_h2d};
   return MOE_OK;
+}
+
+// Step scratch: the layer's workspace, then q8 of x, then the predicted ids
+// and weights of the next layer.
+struct StepWs { size_t layer, qs, d, bs, pids, pw, total; };
+static StepWs step_ws(const moe_layer_desc* d, int T) {
+  StepWs w{};
+  const size_t lw = moe_workspace_size(d, T);
+  if (lw == 0) return w;
+  auto up = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
+  const size_t H = static_cast<size_t>(d->hidden), t = static_cast<size_t>(T);
+  w.layer = 0;
+  w.qs = up(lw);
+  w.d = up(w.qs + t * H);
+  // q8 scales, or MXFP8 scale rows (16 ceil(H / 512) bytes each)
+  const size_t d_bytes = t * (H / 32) * 4, e_bytes = t * 16 * ((H / 32 + 15) / 16);
+  w.bs = up(w.d + (d_bytes > e_bytes ? d_bytes : e_bytes));
+  w.pids = up(w.bs + t * (H / 16) * 2 + 16);
+  w.pw = up(w.pids + t * d->top_k * 4);
+  w.total = up(w.pw + t * d->top_k * 4);
+  return w;
+}
+
+size_t moe_pool_step_workspace(const moe_layer_desc* desc, int T) {
+  if (T < 1) return 0;
+  return step_ws(desc, T).total;
+}
+
+moe_status moe_pool_layer_step(moe_pool* p, int layer, const moe_layer_desc* desc,
+                               const moe_layer_desc* next_desc, const void* x, moe_dtype dtype,
+                               int T, int32_t* ids, float* w, float* y, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (!p || !desc || layer < 0 || layer >= p->cfg.n_layers || T < 1 || !ws) return MOE_EINVAL;
+  if (desc->n_expert != p->cfg.n_experts) return MOE_EINVAL;
+  if (next_desc && (layer + 1 >= p->cfg.n_layers || next_desc->n_expert != p->cfg.n_experts ||
+                    next_desc->top_k != desc->top_k || next_desc->hidden != desc->hidden))
+    return MOE_EINVAL;
+  const StepWs sw = step_ws(desc, T);
+  if (sw.total == 0) return MOE_EINVAL;
+  if (ws_bytes < sw.total) return MOE_ENOWORKSPACE;
+  const size_t nk = static_cast<size_t>(T) * desc->top_k;
+  if (nk > p->ids_host_n) return MOE_EINVAL;
+  const size_t lw = moe_workspace_size(desc, T);
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  moe_status st = moe_route_topk(desc, x, dtype, T, ids, w, nullptr, b, lw, stream);
+  if (st != MOE_OK) return st;
+  if (hipMemcpyAsync(p->ids_host, ids, nk * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MOE_EHIP;
+  st = moe_pool_resolve(p, layer, p->ids_host, static_cast<int>(nk), stream);
+  if (st != MOE_OK) return st;
+  if (next_desc) {
+    int32_t* pids = reinterpret_cast<int32_t*>(b + sw.pids);
+    float* pw = reinterpret_cast<float*>(b + sw.pw);
+    const size_t nlw = moe_workspace_size(next_desc, T);
+    if (nlw == 0 || nlw > lw) return MOE_EINVAL;  // routing the next layer reuses this scratch
+    st = moe_route_topk(next_desc, x, dtype, T, pids, pw, nullptr, b, lw, stream);
+    if (st != MOE_OK) return st;
+    if (hipMemcpyAsync(p->ids_host, pids, nk * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return MOE_EHIP;
+    st = moe_pool_prefetch(p, layer + 1, p->ids_host, static_cast<int>(nk), stream);
+    if (st != MOE_OK) return st;
+  }
+  moe_qact q{};
+  q.qs = reinterpret_cast<int8_t*>(b + sw.qs);
+  q.d = reinterpret_cast<float*>(b + sw.d);
+  q.bsums = reinterpret_cast<int16_t*>(b + sw.bs);
+  const bool mx8 = desc->act_quant == MOE_ACTQ_MXFP8;
+  const bool q32 = desc->fmt_gate == MOE_WFMT_MXFP4 || desc->fmt_gate == MOE_WFMT_Q4_0 ||
+                   desc->fmt_gate == MOE_WFMT_Q5_1;
+  const moe_afmt af = mx8 ? MOE_AFMT_MXFP8 : (q32 ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K);
+  if (mx8) {
+    q.scales = reinterpret_cast<uint8_t*>(b + sw.d);  // [T, 16 ceil(H / 512)]
+    q.d = nullptr;
+    q.bsums = nullptr;
+  } else if (af == MOE_AFMT_Q8_32) {
+    q.bsums = nullptr;
+  }
+  st = moe_quantize_act_q8k(x, dtype, T, desc->hidden, af, &q, stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_ffn(desc, &q, x, dtype, T, ids, w, y, b, lw, stream);
 }
 
 moe_status moe_pool_policy_trace(const moe_pool_config* cfg, int n_ops, const int32_t* kind,

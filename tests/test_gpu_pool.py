@@ -125,3 +125,44 @@ def test_pool_resolve_too_many_unique_experts():
     assert np.all(host[:6] != 0) and np.all(host[6:base.E] == 0)
     assert np.all(host[base.E + 6:2 * base.E] == 0)
     pool.close()
+
+
+@pytest.mark.parametrize("name,T,prefetch", [("qwen3.6-35b-a3b", 2, True),
+                                             ("gpt-oss-20b", 3, False)])
+def test_pool_layer_step_matches_resident(name, T, prefetch):
+    """moe_pool_layer_step (route, host round trip, resolve, prefetch, quantize,
+    FFN in one native call) over a residual stack: bitwise the resident run."""
+    L, steps = 3, 4
+    base = SHRUNK[name].with_(T=T)
+    stack = make_stack(base, L)
+    dls = [DeviceLayer(data) for data in stack]
+    cfg = base
+    # transient slots >= the unique experts of one step (T k, at most E)
+    n_tr = min(cfg.E, T * cfg.k)
+    pool = M.Pool(L, cfg.E, cfg.expert_bytes, cfg.gate_bytes, 2 * cfg.gate_bytes, n_tr + 8, n_tr)
+    for l, data in enumerate(stack):
+        for e in range(cfg.E):
+            pool.host_slab(l, e)[:] = data.pool[e]
+    pdescs = [pool_desc(dl, pool, l) for l, dl in enumerate(dls)]
+    rdescs = [dl.desc for dl in dls]
+    ws_n = max(M.moe_pool_step_workspace(d, T) for d in pdescs)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    for step in range(steps):
+        x0, _ = gen.make_x(base, T=T, x_index=step)
+        x = torch.from_numpy(x0.astype(np.float32)).cuda()
+        want = run_stack(rdescs, cfg, x0.astype(np.float32))
+        for l in range(L):
+            y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+            nd = pdescs[l + 1] if prefetch and l + 1 < L else None
+            pool.layer_step(l, pdescs[l], nd, x, M.MOE_DTYPE_F32, T, ids, w, y, ws, ws_n)
+            torch.cuda.synchronize()
+            assert np.array_equal(ids.cpu().numpy(), want[l][1]), (step, l)
+            assert np.array_equal(y.cpu().numpy(), want[l][0]), (step, l)
+            x = x + y
+    st = pool.stats()
+    assert st["evictions"] > 0
+    if prefetch:
+        assert st["prefetch_loads"] > 0
+    pool.close()
