@@ -111,8 +111,12 @@ __global__ __launch_bounds__(256, 2) void k_gmx(KArgs a, Div dIPT, int RBG, int 
   };
   // ---- DMA roles. Wave w issues slot pieces j = w + 4 u, u = 0..6: j < 17
   // weights (piece i = 64 j + lane: row R = i / 17, part q = i % 17), 17..24
-  // activations (LDS piece (ts, ql) holds global piece ql ^ ts), 25 scale
-  // bytes (4 per lane), 26 biases (4 bytes per lane; layers with biases).
+  // activations (LDS piece (ts, ql) holds global piece ql ^ ts; only the
+  // slots holding one of the tile's cnt token rows), 25 scale bytes (4 per
+  // lane), 26 biases (4 bytes per lane; layers with biases). Each wave's count
+  // per stage is fixed for the tile (my_loads), which the ring's waits need:
+  // the issue code indexes no register array dynamically (a spill to scratch
+  // would add memory operations of its own).
   int wR[5], wq[5];
 #pragma unroll
   for (int u = 0; u < 5; ++u) {
@@ -144,23 +148,28 @@ __global__ __launch_bounds__(256, 2) void k_gmx(KArgs a, Div dIPT, int RBG, int 
     return static_cast<const uint8_t*>(tl.down) + static_cast<size_t>(row) * a.stride_down +
            16 * qq;
   };
+  // the wave's activation slots: 17 + (w + 3) % 4 and 4 more (token rows
+  // 2 (j - 17) and 2 (j - 17) + 1 each)
+  const int ja = 17 + ((wave + 3) & 3);
+  // issue order inside a stage is free: the ring waits for whole stages
   auto issue = [&](uint8_t* L, int rb, int s) {
 #pragma unroll
-    for (int u = 0; u < 7; ++u) {
-      const int j = wave + 4 * u;  // wave-uniform
-      if (j < 17) {
-        dma16_nt(weight_src(wR[u < 5 ? u : 4], wq[u < 5 ? u : 4], rb, s), L + 1024 * j);
-      } else if (j < 25) {
-        const int v = (j - 17) >> 2;  // the wave's first (17..20) or second activation slot
-        dma16(arow[v] + 16 * min(32 * s + aq[v], qmax_a), L + kMxA + 1024 * (j - 17));
-      } else if (j == 25) {
-        dma4(srow + 16 * s + 4 * (lane & 3), L + kMxE);
-      } else if (j == 26 && has_bias) {
-        const float* bsrc;
-        if (MODE == 0) bsrc = lane < 32 ? tl.b_gate + rb * 32 + lane : tl.b_up + rb * 32 + lane - 32;
-        else bsrc = tl.b_down + min(rb * 64 + lane, N - 1);
-        dma4(reinterpret_cast<const uint8_t*>(bsrc), L + kMxBias);
-      }
+    for (int u = 0; u < 5; ++u) {
+      const int j = wave + 4 * u;  // wave-uniform; j < 17 for u < 4, and for wave 0 at u = 4
+      if (j < 17) dma16_nt(weight_src(wR[u], wq[u], rb, s), L + 1024 * j);
+    }
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int j = ja + 4 * v;
+      if (2 * (j - 17) >= cnt) continue;  // rows past the tile's count: not loaded
+      dma16(arow[v] + 16 * min(32 * s + aq[v], qmax_a), L + kMxA + 1024 * (j - 17));
+    }
+    if (wave == 1) dma4(srow + 16 * s + 4 * (lane & 3), L + kMxE);
+    if (wave == 2 && has_bias) {
+      const float* bsrc;
+      if (MODE == 0) bsrc = lane < 32 ? tl.b_gate + rb * 32 + lane : tl.b_up + rb * 32 + lane - 32;
+      else bsrc = tl.b_down + min(rb * 64 + lane, N - 1);
+      dma4(reinterpret_cast<const uint8_t*>(bsrc), L + kMxBias);
     }
   };
   // ---- compute-side lane roles
@@ -188,13 +197,21 @@ __global__ __launch_bounds__(256, 2) void k_gmx(KArgs a, Div dIPT, int RBG, int 
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   int rb = rb0, sb = 0, rbn = rb0, sbn = 0;
   for (int k2 = 0; k2 < 2; ++k2) { if (++sbn == nbs) { sbn = 0; ++rbn; } }
-  const int my_loads = (wave < 2 || (wave == 2 && has_bias)) ? 7 : 6;
+  // this wave's slot loads per stage (weights, activations, scales, biases)
+  const int n_act = (2 * (ja - 17) < cnt ? 1 : 0) + (2 * (ja + 4 - 17) < cnt ? 1 : 0);
+  const int my_loads = (wave == 0 ? 5 : 4) + n_act + (wave == 1 ? 1 : 0) +
+                       (wave == 2 && has_bias ? 1 : 0);
   auto step = [&](int st, const uint8_t* L, uint8_t* Lw) {
     // loads complete in issue order: this wave's loads of stage st are done
     // once at most its loads of stage st + 1 are outstanding; the barrier
     // then publishes every wave's share of the slot
     if (st + 1 < nst) {
-      if (my_loads == 7) wait_vm<7>(); else wait_vm<6>();
+      switch (my_loads) {  // wave-uniform
+        case 7: wait_vm<7>(); break;
+        case 6: wait_vm<6>(); break;
+        case 5: wait_vm<5>(); break;
+        default: wait_vm<4>(); break;
+      }
     } else {
       wait_vm<0>();
     }
@@ -225,6 +242,8 @@ __global__ __launch_bounds__(256, 2) void k_gmx(KArgs a, Div dIPT, int RBG, int 
           B[k] = static_cast<int>(sh == 3 ? w[k + 1] : __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh + 1));
         int sbw = static_cast<int>((w[0] >> (8 * sh)) & 0xFF);
         // A: bytes 16 (g % 2) .. of blocks 4m + g/2 and 4m + 2 + g/2 of token row c
+        // token rows past the tile's count are not loaded: their MFMA rows
+        // (garbage, rows are independent) are never stored
         const uint8_t* arow_l = L + kMxA + 512 * c;
         const int p0 = 8 * m + g, p1 = 8 * m + 4 + g;  // global pieces of the stage row
         const uint4 a0 = *reinterpret_cast<const uint4*>(arow_l + 16 * (p0 ^ c));
@@ -311,8 +330,10 @@ __global__ __launch_bounds__(64) void k_quant_mx8(const void* x, int dtype, int 
 
 int mx_grid(int n_items_max) { return 8 * ((n_items_max + 7) / 8); }
 
-// Row blocks per work item: enough to amortize the ring fill while keeping
-// about 9216 items at the bound on tiles.
+// Row blocks per work item, about 9216 items at the bound on tiles (measured
+// on the gpt-oss shape at 16 and 64 tokens: one row block per item beat groups
+// sized for one or two rounds of workgroups by 20-25%; the finer items balance
+// the chip better than a long ring per item saves on fills).
 int mx_group(int RB, int max_tiles) {
   int g = (RB * max_tiles + 9215) / 9216;
   return g < 1 ? 1 : (g > RB ? RB : g);
