@@ -922,7 +922,11 @@ __device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, i
   float s0 = 0.0f, s1 = 0.0f;
   mx_pair_blocks<NL, NBL>(pc, scr, nb, A, lane, [&](int row, int, int i, float dot, int e) {
     const float v = A.d[i] * __builtin_ldexpf(dot, e - 127);
-    if (row == 0) s0 += v; else s1 += v;
+    // selects, not a branch: with a per-lane row (folded tail blocks) a branch
+    // made the compiler keep {s0, s1} in scratch memory
+    const bool r0 = row == 0;
+    s0 += r0 ? v : 0.0f;
+    s1 += r0 ? 0.0f : v;
   });
   return make_float2(wave_sum(s0), wave_sum(s1));
 }
