@@ -156,6 +156,10 @@ __global__ __launch_bounds__(256, 2) void k_gmx(KArgs a, Div dIPT, int RBG, int 
 #pragma unroll
     for (int u = 0; u < 5; ++u) {
       const int j = wave + 4 * u;  // wave-uniform; j < 17 for u < 4, and for wave 0 at u = 4
+      // non-temporal: a stage's 272 bytes per row end mid 64-byte segment, so
+      // the segment it shares with the next stage is fetched twice (HBM
+      // traffic 1.2x); cached loads avoid that but evict the router weights
+      // the next forward reads, which costs more than the tiles gain
       if (j < 17) dma16_nt(weight_src(wR[u], wq[u], rb, s), L + 1024 * j);
     }
 #pragma unroll
