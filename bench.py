@@ -113,6 +113,29 @@ def measure_probes(M, torch, wall_gib: int):
     out["read_wall_detail"] = {"bytes": nbytes, "GBps_by_workgroups": per,
                                "kernel": "k_read_wall (non-temporal dwordx4, 8 in flight/lane)"}
     del buf
+    # launch-chain floor: per forward of n empty kernels, replayed from a graph
+    # of 64 forwards as the layer timing is (n = the layer call's kernels)
+    chain = {}
+    s = torch.cuda.Stream()
+    for n in (3, 4, 7):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(64):
+                M.moe_probe_empty_chain(n, s)
+        ts = []
+        with torch.cuda.stream(s):
+            g.replay()
+            for _ in range(6):
+                a, b = M.HipEvent(), M.HipEvent()
+                a.record(s)
+                g.replay()
+                b.record(s)
+                b.synchronize()
+                ts.append(a.elapsed_ms(b) * 1e3 / 64)
+        ts = sorted(ts[1:])
+        chain[str(n)] = round(ts[len(ts) // 2], 3)
+        del g
+    out["empty_chain_us_per_forward"] = chain
     for k64, name in ((0, "mfma_i32_16x16x32_i8"), (1, "mfma_i32_16x16x64_i8")):
         nwg, iters = 2048, 400
         ops = nwg * 4 * iters * 8 * 16 * 16 * (64 if k64 else 32) * 2
@@ -261,6 +284,9 @@ def run_workload(args, name: str, headline: bool, probes: dict, th: int):
         "traffic": _traffic_for(kn[dom], name, path),
         "measured_wall": wall,
         "frac_of_measured_wall": round(achieved / wall, 4) if wall else None,
+        # the same number of empty kernels, replayed the same way: the time a
+        # forward of this schedule cannot go below whatever the kernels do
+        "launch_chain_floor_us": probes.get("empty_chain_us_per_forward", {}).get(str(n_st)),
         "algo_bytes_per_launch": round(algo[dom]),
         "avg_launch_us": round(dom_us, 3),
     }

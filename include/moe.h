@@ -344,6 +344,10 @@ MOE_API moe_status moe_test_preact(const moe_layer_desc* desc, const moe_qact* x
  * Errors: MOE_EINVAL for a bad pointer, size or count; MOE_EHIP. */
 MOE_API moe_status moe_probe_read_wall(const void* buf, size_t bytes, int nwg, uint32_t* sink,
                                hipStream_t stream);
+/* moe_probe_empty_chain: n (1..4096) launches of an empty kernel back to back
+ * on `stream`: the launch-chain floor of a layer call with that many kernels
+ * (time it with events, or capture it in a graph as the layer calls are). */
+MOE_API moe_status moe_probe_empty_chain(int n, hipStream_t stream);
 MOE_API moe_status moe_probe_mfma_i8(int k64, int iters, int nwg, int32_t* sink,
                              hipStream_t stream);
 

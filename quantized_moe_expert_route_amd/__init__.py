@@ -38,6 +38,7 @@ ABI_FUNCTIONS = (
     "moe_layer_stage_count", "moe_layer_stage_name", "moe_test_block_dots",
     "moe_test_tile_dots", "moe_test_tile_dots_ws", "moe_test_preact",
     "moe_layer_forward_noalloc", "moe_probe_read_wall", "moe_probe_mfma_i8",
+    "moe_probe_empty_chain",
     # expert pool (include/moe_pool.h)
     "moe_pool_create", "moe_pool_destroy", "moe_pool_host_slab", "moe_pool_layer_tables",
     "moe_pool_resolve", "moe_pool_prefetch", "moe_pool_get_stats", "moe_pool_policy_trace",
@@ -115,6 +116,7 @@ def lib():
         L.moe_layer_forward_noalloc.argtypes = [D, vp, i32, i32, vp, vp, vp, vp]
         L.moe_probe_read_wall.argtypes = [vp, sz, i32, vp, vp]
         L.moe_probe_mfma_i8.argtypes = [i32, i32, i32, vp, vp]
+        L.moe_probe_empty_chain.argtypes = [i32, vp]
         L.moe_layer_forward_timed.argtypes = [D, vp, i32, i32, vp, vp, vp, vp, sz, vp,
                                               C.POINTER(vp), i32]
         L.moe_layer_stage_count.argtypes = [D, i32]
@@ -143,7 +145,7 @@ def lib():
         for n in ("moe_quantize_act_q8k", "moe_route_topk", "moe_expert_ffn", "moe_layer_forward",
                   "moe_layer_forward_timed", "moe_test_block_dots", "moe_test_tile_dots",
                   "moe_test_preact", "moe_layer_forward_noalloc", "moe_probe_read_wall",
-                  "moe_probe_mfma_i8", "moe_pool_create", "moe_pool_layer_tables",
+                  "moe_probe_mfma_i8", "moe_probe_empty_chain", "moe_pool_create", "moe_pool_layer_tables",
                   "moe_pool_resolve", "moe_pool_prefetch", "moe_pool_get_stats",
                   "moe_pool_policy_trace", "moe_pool_layer_step"):
             getattr(L, n).restype = i32
@@ -219,6 +221,10 @@ def moe_layer_forward_noalloc(desc, x, dtype, T, y, ids_out, w_out, stream=None)
 def moe_probe_read_wall(buf, nbytes, nwg, sink, stream=None):
     _check("moe_probe_read_wall",
            lib().moe_probe_read_wall(_ptr(buf), nbytes, nwg, _ptr(sink), _stream(stream)))
+
+
+def moe_probe_empty_chain(n: int, stream=None):
+    _check("moe_probe_empty_chain", lib().moe_probe_empty_chain(n, _stream(stream)))
 
 
 def moe_probe_mfma_i8(k64, iters, nwg, sink, stream=None):

@@ -594,6 +594,11 @@ moe_status moe_probe_read_wall(const void* buf, size_t bytes, int nwg, uint32_t*
   return hip_status(launch_read_wall(buf, bytes, sink, nwg, stream));
 }
 
+moe_status moe_probe_empty_chain(int n, hipStream_t stream) {
+  if (n < 1 || n > 4096) return MOE_EINVAL;
+  return hip_status(launch_empty_chain(n, stream));
+}
+
 moe_status moe_probe_mfma_i8(int k64, int iters, int nwg, int32_t* sink, hipStream_t stream) {
   if ((k64 != 0 && k64 != 1) || iters < 0 || nwg < 1 || nwg > (1 << 20) || !sink ||
       !aligned(sink, 4))

@@ -195,6 +195,7 @@ size_t tile_dots_ws(int mode, int n_rows, int K, int n_tok);
 // Measurement probes (moe_probe.hip).
 hipError_t launch_read_wall(const void* buf, size_t bytes, uint32_t* sink, int nwg, hipStream_t s);
 hipError_t launch_mfma_i8(int k64, int iters, int nwg, int32_t* sink, hipStream_t s);
+hipError_t launch_empty_chain(int n, hipStream_t s);
 hipError_t launch_tile_dots(int mode, const void* rows, int n_rows, int K, size_t stride,
                             const int8_t* qs, const float* d, const int16_t* bs, int n_tok,
                             int32_t* out, void* ws, hipStream_t s);

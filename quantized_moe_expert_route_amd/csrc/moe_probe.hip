@@ -78,6 +78,19 @@ hipError_t launch_read_wall(const void* buf, size_t bytes, uint32_t* sink, int n
   return hipGetLastError();
 }
 
+// Launch-chain floor: n dependent launches of an empty kernel (one workgroup of
+// 64 threads that does nothing) on one stream.
+__global__ __launch_bounds__(64) void k_empty() {}
+
+hipError_t launch_empty_chain(int n, hipStream_t s) {
+  for (int i = 0; i < n; ++i) {
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_mfma_i8(int k64, int iters, int nwg, int32_t* sink, hipStream_t s) {
   auto kern = k64 ? k_mfma_i8<1, 8> : k_mfma_i8<0, 8>;
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, s, iters, nwg, sink);

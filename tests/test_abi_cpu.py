@@ -312,3 +312,19 @@ def test_noalloc_refuses_chunks_past_the_scratch():
         M.moe_layer_forward_noalloc(d, FAKE + 8, 0, 256, FAKE, None, None, stream=0)
     assert ei.value.status == M.MOE_EINVAL
     M.moe_layer_forward_noalloc(d, FAKE, 0, 0, FAKE, None, None, stream=0)  # T = 0: no-op
+
+
+def test_probe_validation():
+    """The measurement probes reject bad arguments before any launch."""
+    for n in (0, -1, 4097):
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_probe_empty_chain(n, stream=0)
+        assert ei.value.status == M.MOE_EINVAL
+    with pytest.raises(M.MoeError):
+        M.moe_probe_read_wall(FAKE + 8, 1 << 20, 64, FAKE, stream=0)
+    with pytest.raises(M.MoeError):
+        M.moe_probe_read_wall(FAKE, (1 << 20) + 4, 64, FAKE, stream=0)
+    with pytest.raises(M.MoeError):
+        M.moe_probe_mfma_i8(2, 10, 64, FAKE, stream=0)
+    with pytest.raises(M.MoeError):
+        M.moe_probe_mfma_i8(0, 10, 0, FAKE, stream=0)
