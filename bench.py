@@ -71,6 +71,10 @@ def parse():
                    help="comma list of workloads: time each on both expert-FFN paths at "
                         "--crossover-tokens chunk sizes (reported under detail.crossover)")
     p.add_argument("--crossover-tokens", default="1,2,3,4,6,8,12,16")
+    p.add_argument("--layout", default="auto", choices=("auto", "rows", "tile64"),
+                   help="order of the expert blocks on the device: auto = 64-row tiles for "
+                        "layers that take the grouped path at every chunk size (an expert of "
+                        "8 MB or more), row order otherwise")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -154,6 +158,18 @@ def measure_probes(M, torch, wall_gib: int):
 
 
 # --------------------------------------------------------------- workloads
+def pick_layout(args, cfg) -> int:
+    """moe_layout of a workload's expert matrices (see --layout)."""
+    import gen
+    if args.layout == "rows":
+        return 0
+    tiles_ok = (cfg.fmt_gu == gen.Q4_K and cfg.fmt_d in (gen.Q4_K, gen.Q6_K) and not cfg.biases
+                and not cfg.act_quant)
+    if args.layout == "tile64":
+        return 1 if tiles_ok else 0
+    return 1 if tiles_ok and cfg.expert_algo_bytes >= 8e6 else 0
+
+
 def run_workload(args, name: str, headline: bool, probes: dict, th: int):
     import numpy as np
     import torch
@@ -166,6 +182,7 @@ def run_workload(args, name: str, headline: bool, probes: dict, th: int):
     if headline and args.tokens:
         cfg = cfg.with_(T=args.tokens, description=f"{cfg.description}; {args.tokens}-token chunk")
     copies = (args.copies if headline and args.copies else None) or DEFAULT_COPIES[name]
+    cfg = cfg.with_(layout=pick_layout(args, cfg))
     t0 = time.time()
     data = gen.make_layer(cfg, threads=th)
     dl = DeviceLayer(data, copies=copies)
@@ -206,7 +223,8 @@ def run_workload(args, name: str, headline: bool, probes: dict, th: int):
         full.replay()
     torch.cuda.synchronize()
     res = {"workload": cfg.description, "tokens_per_step": T, "layer_copies": copies,
-           "x_pool": args.x_pool, "forwards_per_graph": G}
+           "x_pool": args.x_pool, "forwards_per_graph": G,
+           "expert_layout": "tile64" if cfg.layout else "rows"}
     if headline:
         # exactly K steps: whole rotations, then the first K mod G forwards of
         # one (their copies are the least recently used ones at that point)
@@ -627,12 +645,14 @@ def main():
             "layer_copies": head["layer_copies"],
             "x_pool": head["x_pool"],
             "path": head["path"],
+            "expert_layout": head["expert_layout"],
         },
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "detail": {
             **{k: v for k, v in head.items() if k not in (
-                "workload", "tokens_per_step", "layer_copies", "x_pool", "path", "roofline",
+                "workload", "tokens_per_step", "layer_copies", "x_pool", "path", "expert_layout",
+                "roofline",
                 "tokens_per_s", "ms_per_step")},
             "probes": probes,
             **({"crossover": xover} if xover else {}),

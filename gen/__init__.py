@@ -257,6 +257,9 @@ class LayerConfig:
     bias_std: float = 0.01
     x_std: float = 1.0
     act_quant: int = 0  # activation numerics: 0 q8, 1 MXFP8 (MXFP4 layers, block-scaled MMA)
+    # order of the expert matrices' blocks on the device: 0 rows (GGUF order),
+    # 1 64-row tiles (moe_layout TILE64; layers on the grouped path at every T)
+    layout: int = 0
     description: str = ""
 
     @property

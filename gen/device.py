@@ -46,21 +46,44 @@ def interleave_gate_up(data) -> np.ndarray:
     return pool
 
 
+def tile_pool(cfg, pool_rows: torch.Tensor) -> torch.Tensor:
+    """The pool with every expert matrix (the shared expert's too) reordered
+    by the library into 64-row tiles (moe_layout TILE64), each at the offset
+    its row-order matrix had."""
+    out = torch.zeros_like(pool_rows)
+    es = cfg.expert_bytes
+    s = torch.cuda.current_stream().cuda_stream
+    for e in range(cfg.n_pool):
+        base = e * es
+        for off, fmt, n, K, st in ((0, cfg.fmt_gu, cfg.F, cfg.H, cfg.stride_gu),
+                                   (cfg.gate_bytes, cfg.fmt_gu, cfg.F, cfg.H, cfg.stride_gu),
+                                   (2 * cfg.gate_bytes, cfg.fmt_d, cfg.H, cfg.F, cfg.stride_d)):
+            M.moe_repack_tile64(fmt, pool_rows.data_ptr() + base + off, st, n, K,
+                                out.data_ptr() + base + off, stream=s)
+    torch.cuda.synchronize()
+    return out
+
+
 class DeviceLayer:
     def __init__(self, data, copies: int = 1, present=None, route_scale=None, norm_topk=None,
                  use_shared: bool = True, sh_gate_vec=None, sel_bias="data", device="cuda",
-                 path: int = 0, interleaved: bool = False):
+                 path: int = 0, interleaved: bool = False, layout: int | None = None):
         cfg = data.cfg
         self.cfg = cfg
         self.device = device
         E = cfg.E
         present = np.ones(E, bool) if present is None else np.asarray(present, bool)
         self.present = present
+        self.layout = cfg.layout if layout is None else layout
+        if self.layout and interleaved:
+            raise ValueError("64-row tiles have their own order: no interleaved gate/up")
         # gate/up row r of an expert: interleaved at (2r, 2r + 1) of one fused
         # tensor, else stacked (gate matrix, then up matrix)
         up_off = cfg.stride_gu if interleaved else cfg.gate_bytes
         gu_stride = 2 * cfg.stride_gu if interleaved else cfg.stride_gu
         pool0 = _dev(interleave_gate_up(data) if interleaved else data.pool, device)
+        if self.layout == M.MOE_LAYOUT_TILE64:
+            pool0 = tile_pool(cfg, pool0)
         self.pools = [pool0] + [pool0.clone() for _ in range(1, copies)]
         self.w_router = _dev(data.w_router, device)
         sb = data.sel_bias if isinstance(sel_bias, str) else sel_bias
@@ -112,6 +135,7 @@ class DeviceLayer:
             d.sh_gate_vec = None if self.sh_gate_vec is None else self.sh_gate_vec.data_ptr()
             d.path = path  # moe_path: 0 auto, 1 per-pair GEMV, 2 expert-grouped
             d.act_quant = getattr(cfg, "act_quant", 0)  # moe_actq: 0 q8, 1 MXFP8
+            d.layout = self.layout  # moe_layout: 0 rows, 1 64-row tiles
             self._tables.append(keep)
             self.descs.append(d)
 

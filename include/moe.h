@@ -49,7 +49,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
@@ -107,6 +107,22 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
  * streams large experts faster even for one token). GEMV and GROUPED force a
  * path (GROUPED only where the formats allow it). */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_path;
+/* Order of the blocks of every expert matrix of a layer (gate, up, down and the
+ * shared expert's). The blocks themselves are the stored format's; only their
+ * order differs.
+ *  ROWS: row r of a matrix at r * stride, its blocks in order along the row
+ *    (the GGUF tensor order).
+ *  TILE64: rows form tiles of 64, and tile i holds super-block 0 of its 64
+ *    rows (row 64 i first), then their super-block 1, and so on: block b of
+ *    row r of a matrix with nb blocks per row sits at byte
+ *    ((r / 64) * nb + b) * 64 * BB + (r % 64) * BB (BB: block bytes), and the
+ *    stride fields are not used. One stage of the grouped tile kernels (one
+ *    super-block of 64 or 128 rows) is then a single contiguous read instead of
+ *    a block from each of 64 rows. Needs Q4_K gate and up, Q4_K or Q6_K down,
+ *    no biases, Q8 activations and a path other than GEMV (MOE_EUNSUPPORTED
+ *    otherwise); such layers take the grouped path at every T.
+ *    moe_repack_tile64 converts a matrix from ROWS order. */
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILE64 = 1 } moe_layout;
 
 /* Quantized activations of T rows of width H, structure-of-arrays:
  *   qs    int8  [T, H]      q8 quants, |q| <= 127 (Q8_K, Q8_32); MXFP8: E4M3
@@ -161,6 +177,7 @@ typedef struct {
  *  path: moe_path (0 = AUTO).
  *  act_quant: moe_actq (0 = Q8). MXFP8 needs MXFP4 gate, up and down and a
  *    path other than GEMV (MOE_EUNSUPPORTED otherwise).
+ *  layout: moe_layout (0 = ROWS) of every expert matrix.
  */
 typedef struct {
   int32_t hidden;
@@ -189,6 +206,7 @@ typedef struct {
   const float* sh_gate_vec;
   int32_t path;
   int32_t act_quant;
+  int32_t layout;
 } moe_layer_desc;
 
 /* ABI version (MOE_ABI_VERSION) and a static message for a status. */
@@ -280,6 +298,18 @@ MOE_API moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const voi
                                    int n_events);
 MOE_API int moe_layer_stage_count(const moe_layer_desc* desc, int T);
 MOE_API const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage);
+
+/* Reorders one expert matrix from ROWS to TILE64 order (moe_layout): n_rows
+ * rows of K weights in format fmt (Q4_K or Q6_K), row r at src + r * src_stride,
+ * into n_rows * (K / 256) * BB bytes at dst. Whole blocks move; no byte of a
+ * block changes. Needs n_rows % 64 == 0, K % 256 == 0, src_stride >= the row's
+ * bytes and even, src and dst 16-byte aligned and not overlapping (MOE_EINVAL
+ * otherwise); a failed launch gives MOE_EHIP. Enqueued on stream; the caller
+ * owns both buffers. Source: Pulsar README, formats paragraph (routed experts
+ * as stored GGUF quant blocks); the order of the blocks in device memory is
+ * this library's choice. */
+MOE_API moe_status moe_repack_tile64(moe_wfmt fmt, const void* src, size_t src_stride, int n_rows,
+                                     int K, void* dst, hipStream_t stream);
 
 /* Test export: integer block partials of n_rows weight rows (device, K
  * columns, byte stride `stride`) against token `token` of xq, computed by the

@@ -29,6 +29,7 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = range(2)
 MOE_ROUTER_SOFTMAX, MOE_ROUTER_SIGMOID = range(2)
 MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = range(2)
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GROUPED = range(3)
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE64 = range(2)
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
 
@@ -38,7 +39,7 @@ ABI_FUNCTIONS = (
     "moe_layer_stage_count", "moe_layer_stage_name", "moe_test_block_dots",
     "moe_test_tile_dots", "moe_test_tile_dots_ws", "moe_test_preact",
     "moe_layer_forward_noalloc", "moe_probe_read_wall", "moe_probe_mfma_i8",
-    "moe_probe_empty_chain",
+    "moe_probe_empty_chain", "moe_repack_tile64",
     # expert pool (include/moe_pool.h)
     "moe_pool_create", "moe_pool_destroy", "moe_pool_host_slab", "moe_pool_layer_tables",
     "moe_pool_resolve", "moe_pool_prefetch", "moe_pool_get_stats", "moe_pool_policy_trace",
@@ -86,6 +87,7 @@ class MoeLayerDesc(C.Structure):
         ("act", C.c_int32), ("act_alpha", C.c_float), ("act_limit", C.c_float),
         ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
         ("sh_gate_vec", C.c_void_p), ("path", C.c_int32), ("act_quant", C.c_int32),
+        ("layout", C.c_int32),
     ]
 
 
@@ -124,6 +126,7 @@ def lib():
         L.moe_layer_stage_name.argtypes = [D, i32, i32]
         L.moe_layer_stage_name.restype = C.c_char_p
         L.moe_test_block_dots.argtypes = [i32, vp, i32, i32, sz, Q, i32, vp, vp]
+        L.moe_repack_tile64.argtypes = [i32, vp, sz, i32, i32, vp, vp]
         L.moe_test_tile_dots.argtypes = [i32, vp, i32, i32, sz, Q, i32, vp, vp, sz, vp]
         L.moe_test_tile_dots_ws.argtypes = [i32, i32, i32, i32]
         L.moe_test_tile_dots_ws.restype = sz
@@ -248,6 +251,18 @@ def moe_layer_stage_count(desc, T: int) -> int:
 def moe_layer_stage_name(desc, T: int, stage: int) -> str | None:
     r = lib().moe_layer_stage_name(C.byref(desc), T, stage)
     return None if r is None else r.decode()
+
+
+def moe_repack_tile64(fmt, src, src_stride, n_rows, K, dst, stream=None):
+    """One expert matrix from row order into 64-row tiles (moe_layout TILE64)."""
+    _check("moe_repack_tile64",
+           lib().moe_repack_tile64(fmt, _ptr(src), src_stride, n_rows, K, _ptr(dst),
+                                   _stream(stream)))
+
+
+def tile64_bytes(fmt, n_rows, K) -> int:
+    """Bytes of one matrix in TILE64 order (no row padding)."""
+    return n_rows * (K // 256) * {MOE_WFMT_Q4_K: 144, MOE_WFMT_Q6_K: 210}[fmt]
 
 
 def moe_test_block_dots(fmt, rows, n_rows, K, stride, xq: MoeQact, token, out, stream=None):

@@ -55,6 +55,7 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_GEMV && d->path != MOE_PATH_GROUPED)
     return MOE_EINVAL;
   if (d->act_quant != MOE_ACTQ_Q8 && d->act_quant != MOE_ACTQ_MXFP8) return MOE_EINVAL;
+  if (d->layout != MOE_LAYOUT_ROWS && d->layout != MOE_LAYOUT_TILE64) return MOE_EINVAL;
   for (int f : {d->fmt_gate, d->fmt_up, d->fmt_down})
     if (!known_fmt(f)) return MOE_EINVAL;
   if (d->fmt_gate != d->fmt_up) return MOE_EUNSUPPORTED;
@@ -80,6 +81,12 @@ moe_status validate_desc(const moe_layer_desc* d) {
     return MOE_EINVAL;
   if (d->sh_gate_vec && (nsh == 0 || !aligned(d->sh_gate_vec, 16))) return MOE_EINVAL;
   if (!(d->act_limit > 0.0f) && d->act == MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
+  // 64-row tiles: read by the grouped Q4_K / Q6_K ring kernels only
+  if (d->layout == MOE_LAYOUT_TILE64 &&
+      (d->fmt_gate != MOE_WFMT_Q4_K ||
+       (d->fmt_down != MOE_WFMT_Q4_K && d->fmt_down != MOE_WFMT_Q6_K) || d->b_gate || d->b_down ||
+       d->act_quant != MOE_ACTQ_Q8 || d->path == MOE_PATH_GEMV))
+    return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -106,6 +113,7 @@ KArgs make_args(const moe_layer_desc* d, int T) {
   a.sh_gate_vec = d->sh_gate_vec;
   a.has_shared = d->sh_gate != nullptr;
   a.mx8 = d->act_quant == MOE_ACTQ_MXFP8;
+  a.tiled = d->layout == MOE_LAYOUT_TILE64;
   return a;
 }
 
@@ -180,6 +188,7 @@ static size_t expert_block_bytes(const moe_layer_desc* d) {
 
 bool use_grouped(const moe_layer_desc* d, int T) {
   if (d->act_quant == MOE_ACTQ_MXFP8) return T >= 1;  // block-scaled MFMA tiles at every T
+  if (d->layout == MOE_LAYOUT_TILE64) return T >= 1;  // only the ring kernels read tiles
   auto tiled = [](int f) { return f == FMT_Q4_K || f == FMT_Q6_K; };
   if (!tiled(d->fmt_gate) || !tiled(d->fmt_down) || T < 1) return false;
   if (d->path == MOE_PATH_GEMV) return false;
@@ -506,6 +515,22 @@ const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {
   const int n = moe_layer_stage_count(desc, T);
   if (stage < 0 || stage >= n) return nullptr;
   return n == 7 ? grouped[stage] : n == 4 ? gemv_hq[stage] : gemv[stage];
+}
+
+moe_status moe_repack_tile64(moe_wfmt fmt, const void* src, size_t src_stride, int n_rows, int K,
+                             void* dst, hipStream_t stream) {
+  if (fmt != MOE_WFMT_Q4_K && fmt != MOE_WFMT_Q6_K) return MOE_EINVAL;
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return MOE_EINVAL;
+  if (n_rows <= 0 || n_rows % 64 || K <= 0 || K % 256) return MOE_EINVAL;
+  const int nb = K / 256;
+  const size_t BB = block_bytes(fmt), row = static_cast<size_t>(nb) * BB;
+  if (src_stride < row || src_stride % 2) return MOE_EINVAL;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t s1 = s0 + (static_cast<size_t>(n_rows) - 1) * src_stride + row;
+  const uintptr_t d1 = d0 + static_cast<size_t>(n_rows) * row;
+  if (s0 < d1 && d0 < s1) return MOE_EINVAL;  // overlapping buffers
+  return hip_status(launch_repack_tile64(static_cast<const uint8_t*>(src), src_stride, n_rows, nb,
+                                         static_cast<int>(BB), static_cast<uint8_t*>(dst), stream));
 }
 
 moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,

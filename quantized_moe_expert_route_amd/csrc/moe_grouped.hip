@@ -356,8 +356,12 @@ __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG,
   // j < 18 weights (piece i = 64 j + lane: row R = i / 9, 16-byte part i % 9),
   // 18..21 activation q8 (LDS piece (ts, ql) holds global piece ql ^ ts),
   // 22 the 16-element sums, 23 (4-byte) the block scales.
+  // Row order: piece (R, q) of super-block b at row R's start + 144 b + 16 q.
+  // 64-row tiles: the 64 blocks of a tile's super-block are one 9216-byte run
+  // in row order, so a stage is one run per 64 rows.
   const uint8_t* wsrc[5];
   size_t wrbs[5];  // bytes between consecutive row blocks
+  const size_t bstep = a.tiled ? 9216 : 144;  // bytes between consecutive super-blocks
 #pragma unroll
   for (int u = 0; u < 5; ++u) {
     const int j = min(wave + 4 * u, 17);
@@ -374,8 +378,16 @@ __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG,
       st = a.stride_down;
       r = R;
     }
-    wsrc[u] = W + static_cast<size_t>(r) * st + 16 * q;
-    wrbs[u] = (MODE == 0 ? 64 : 128) * st;
+    if (a.tiled) {
+      // row block rb = tile rb (gate/up) or tiles 2 rb, 2 rb + 1 (down)
+      const size_t tile_bytes = static_cast<size_t>(nb) * 9216;
+      wsrc[u] = W + (MODE == 0 ? 0 : static_cast<size_t>(R >> 6) * tile_bytes) +
+                16 * (i - 576 * (R >> 6));
+      wrbs[u] = (MODE == 0 ? 1 : 2) * tile_bytes;
+    } else {
+      wsrc[u] = W + static_cast<size_t>(r) * st + 16 * q;
+      wrbs[u] = (MODE == 0 ? 64 : 128) * st;
+    }
   }
   const uint8_t* asrc;  // activation q8 piece (waves 0..3: slot piece 20, 21, 18, 19)
   {
@@ -393,9 +405,9 @@ __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG,
   auto issue = [&](uint8_t* L, int rb, int b) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      dma16(wsrc[u] + rb * wrbs[u] + 144 * b, L + 1024 * (wave + 4 * u));
+      dma16(wsrc[u] + rb * wrbs[u] + bstep * b, L + 1024 * (wave + 4 * u));
     if (wave < 2) {
-      dma16(wsrc[4] + rb * wrbs[4] + 144 * b, L + 1024 * (wave + 16));
+      dma16(wsrc[4] + rb * wrbs[4] + bstep * b, L + 1024 * (wave + 16));
       dma16(asrc + 256 * b, L + 1024 * (wave + 20));
     } else {
       dma16(asrc + 256 * b, L + 1024 * (wave + 16));
@@ -538,6 +550,8 @@ __device__ __forceinline__ uint2 lds8_a2(const uint8_t* L, int off) {
 // Down rows of Q6_K experts: item = (tile, ii), row blocks of 64 rows of H,
 // wave w takes rows 16 w .. 16 w + 15 of a block. Same ring protocol as
 // k_glds_q4k, 5 slot loads per wave and stage. Layers without down biases.
+// With 64-row tiles a stage is one 13440-byte run, held in the slot as is
+// (row pitch 210 instead of kQ6Row).
 template <bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int RBG, int RB) {
   __shared__ __align__(16) uint8_t lds0[kS6Bytes];
@@ -560,13 +574,20 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int j = min(wave + 4 * u, 14);
-    // a block needs at most 14 pieces (sh + 210 <= 224 bytes); the 15th of a
-    // row reloads the 14th, so no load starts past the block (the last block
-    // of the last row of an expert may end its allocation)
-    const int i = 64 * j + lane, R = i / 15, q = min(i - 15 * R, 13);
-    wsrc[u] = tl.down + static_cast<size_t>(R) * a.stride_down + 16 * q;
+    const int i = 64 * j + lane;
+    if (a.tiled) {
+      // 840 pieces per stage; lanes past them reload the last one (their LDS
+      // bytes lie past the 64 blocks and are not read)
+      wsrc[u] = tl.down + 16 * min(i, 839);
+    } else {
+      // a block needs at most 14 pieces (sh + 210 <= 224 bytes); the 15th of a
+      // row reloads the 14th, so no load starts past the block (the last block
+      // of the last row of an expert may end its allocation)
+      const int R = i / 15, q = min(i - 15 * R, 13);
+      wsrc[u] = tl.down + static_cast<size_t>(R) * a.stride_down + 16 * q;
+    }
   }
-  const size_t rbs = 64 * a.stride_down;
+  const size_t rbs = a.tiled ? static_cast<size_t>(nb) * 13440 : 64 * a.stride_down;
   const uint8_t* asrc;
   {
     const int j = wave == 3 ? 15 : 16 + wave;
@@ -577,7 +598,7 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
   const uint8_t* dsrc =
       reinterpret_cast<const uint8_t*>(a.hd + static_cast<size_t>(pair_of(lane & 15).x) * nb);
   auto issue = [&](uint8_t* L, int rb, int b) {
-    const size_t wo = rb * rbs + ((210 * b) & ~15);
+    const size_t wo = rb * rbs + (a.tiled ? static_cast<size_t>(13440) * b : (210 * b) & ~15);
 #pragma unroll
     for (int u = 0; u < 3; ++u) dma16(wsrc[u] + wo, L + 1024 * (wave + 4 * u));
     if (wave < 3) {
@@ -627,7 +648,7 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
       x.dC[0] = dc.x; x.dC[1] = dc.y; x.dC[2] = dc.z; x.dC[3] = dc.w;
     }
     WQ6K w;
-    const int blk = (wave * 16 + c) * kQ6Row + ((210 * b) & 15);
+    const int blk = a.tiled ? (wave * 16 + c) * 210 : (wave * 16 + c) * kQ6Row + ((210 * b) & 15);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       w.l0[h] = lds8_a2(L, blk + 64 * h + 8 * g);
@@ -657,6 +678,24 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
     step(s, lds0, lds2);
     if (s + 1 < nst) step(s + 1, lds1, lds0);
     if (s + 2 < nst) step(s + 2, lds2, lds1);
+  }
+}
+
+// Row order -> 64-row tiles, one 2-byte unit per thread (blocks are 2-byte
+// aligned in both orders): destination block (tile, b, r) is source block
+// (64 tile + r, b).
+__global__ __launch_bounds__(256) void k_repack_tile64(const uint8_t* src, size_t stride, int nb,
+                                                       int BB, uint8_t* dst, size_t units) {
+  const size_t n_thr = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t u = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < units;
+       u += n_thr) {
+    const size_t byte = 2 * u, blk = byte / BB;
+    const int off = static_cast<int>(byte - blk * BB);
+    const int r = static_cast<int>(blk & 63);
+    const size_t tb = blk >> 6, tile = tb / nb;
+    const int b = static_cast<int>(tb - tile * nb);
+    const uint8_t* p = src + (64 * tile + r) * stride + static_cast<size_t>(b) * BB + off;
+    reinterpret_cast<uint16_t*>(dst)[u] = *reinterpret_cast<const uint16_t*>(p);
   }
 }
 
@@ -1230,6 +1269,14 @@ hipError_t launch_topk_sum(const KArgs& a, RouterSplit rs, hipStream_t s, Ev ev)
   if (a.E <= 256) return launch(k_topk_sum<4>, grid, 256, 0, s, ev, a, rs.ks);
   if (a.E <= 512) return launch(k_topk_sum<8>, grid, 256, 0, s, ev, a, rs.ks);
   return launch(k_topk_sum<16>, grid, 256, 0, s, ev, a, rs.ks);
+}
+
+hipError_t launch_repack_tile64(const uint8_t* src, size_t stride, int n_rows, int nb, int BB,
+                                uint8_t* dst, hipStream_t s) {
+  const size_t units = static_cast<size_t>(n_rows) * nb * BB / 2;
+  const size_t want = (units + 255) / 256;
+  const int grid = static_cast<int>(want < 8192 ? want : 8192);
+  return launch(k_repack_tile64, dim3(grid), 256, 0, s, Ev{}, src, stride, nb, BB, dst, units);
 }
 
 hipError_t launch_bucket(const KArgs& a, hipStream_t s, Ev ev) {

@@ -121,6 +121,9 @@ struct KArgs {
   int mx8;
   uint8_t* xe;         // [T, mx8_pitch(H)]
   uint8_t* he;         // [P, mx8_pitch(F)]
+  // expert matrices in 64-row tiles, super-block-major inside a tile (block b
+  // of row r at ((r / 64) nb + b) 64 BB + (r % 64) BB); strides unused
+  int tiled;
 };
 
 // Workspace layout (byte offsets from the base, each 256-aligned).
@@ -172,6 +175,10 @@ hipError_t launch_hquant_pairs(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hipStream_t s, Ev ev);
 hipError_t launch_topk_sum(const KArgs& a, RouterSplit rs, hipStream_t s, Ev ev);
 hipError_t launch_bucket(const KArgs& a, hipStream_t s, Ev ev);
+// One matrix (n_rows of nb blocks of BB bytes, row stride `stride`) from row
+// order into 64-row tiles.
+hipError_t launch_repack_tile64(const uint8_t* src, size_t stride, int n_rows, int nb, int BB,
+                                uint8_t* dst, hipStream_t s);
 hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_hquant(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev);

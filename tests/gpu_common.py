@@ -38,15 +38,16 @@ def run_layer(dl: DeviceLayer, xt: torch.Tensor, dtype: int, T: int, copy: int =
 
 
 def check_layer(cfg, data=None, T=None, x_index=0, tokens=None, present=None, tol=Y_TOL,
-                sh_gate_vec=None, threads=8, path=0, interleaved=False):
+                sh_gate_vec=None, threads=8, path=0, interleaved=False, layout=None):
     """Run the whole layer on the GPU and compare with the oracle on `tokens`."""
     data = data or gen.make_layer(cfg)
     T = cfg.T if T is None else T
     x, xb = gen.make_x(cfg, T=T, x_index=x_index)
     dl = DeviceLayer(data, present=present, sh_gate_vec=sh_gate_vec, path=path,
-                     interleaved=interleaved)
+                     interleaved=interleaved, layout=layout)
     xt, dt = x_to_device(data, x, xb)
-    say(f"layer {cfg.name} T={T} x_index={x_index} path={path} interleaved={interleaved}")
+    say(f"layer {cfg.name} T={T} x_index={x_index} path={path} interleaved={interleaved} "
+        f"layout={dl.layout}")
     y, ids, w = run_layer(dl, xt, dt, T)
     L = oracle.Layer(data, present=present, sh_gate_vec=sh_gate_vec)
     tokens = list(range(T)) if tokens is None else list(tokens)

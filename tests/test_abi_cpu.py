@@ -35,7 +35,7 @@ def test_library_exports_header_symbols():
 
 
 def test_version_and_status_strings():
-    assert M.moe_abi_version() == 3
+    assert M.moe_abi_version() == 4
     for s in range(5):
         assert M.moe_status_str(s)
     assert M.moe_status_str(99) == "unknown status"
@@ -175,6 +175,66 @@ def test_block_dots_validation():
     for a in bad:
         with pytest.raises(M.MoeError):
             M.moe_test_block_dots(*a, FAKE, stream=0)
+
+
+def test_tile64_layout_rules():
+    """TILE64 (64-row tiles, super-block-major inside a tile) is read by the
+    grouped Q4_K / Q6_K ring kernels only: such a layer takes the grouped path
+    at every T, and other formats, biases, MXFP8 activations or a forced GEMV
+    path are refused before anything is enqueued."""
+    for name in ("deepseek-v4-flash", "qwen3.6-35b-a3b", "kimi-k2"):
+        d = good_desc(gen.CONFIGS[name])
+        d.layout = M.MOE_LAYOUT_TILE64
+        for T in (1, 2, 16, 256):
+            assert M.moe_layer_stage_count(d, T) == 7, (name, T)
+        assert M.moe_workspace_size(d, 1) > 0
+    bad = []
+    for field, value in (("layout", 2), ("layout", -1), ("path", M.MOE_PATH_GEMV),
+                         ("fmt_gate", M.MOE_WFMT_Q6_K), ("fmt_down", M.MOE_WFMT_Q5_K),
+                         ("b_gate", FAKE), ("b_down", FAKE)):
+        d = good_desc(gen.CONFIGS["deepseek-v4-flash"])
+        d.layout = M.MOE_LAYOUT_TILE64
+        setattr(d, field, value)
+        if field == "fmt_gate":  # Q6_K rows: 210 bytes per 256 weights
+            d.fmt_up = value
+            d.stride_gate = d.stride_up = (d.hidden // 256 * 210 + 15) // 16 * 16
+        if field == "b_gate":
+            d.b_up = FAKE
+        bad.append((field, d))
+    mx = good_desc(gen.CONFIGS["gpt-oss-20b"])
+    mx.layout = M.MOE_LAYOUT_TILE64
+    bad.append(("mxfp4", mx))
+    for field, d in bad:
+        assert M.moe_workspace_size(d, 1) == 0, field
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_layer_forward(d, FAKE, 0, 1, FAKE, None, None, FAKE, 1 << 40, stream=0)
+        want = M.MOE_EINVAL if field == "layout" else M.MOE_EUNSUPPORTED
+        assert ei.value.status == want, field
+
+
+def test_repack_tile64_validation():
+    """moe_repack_tile64 arguments are checked on the host (nothing enqueued)."""
+    Q4, Q6 = M.MOE_WFMT_Q4_K, M.MOE_WFMT_Q6_K
+    big = 1 << 30
+    bad = [
+        (M.MOE_WFMT_MXFP4, FAKE, 288, 64, 512, FAKE + big),
+        (M.MOE_WFMT_Q5_K, FAKE, 352, 64, 512, FAKE + big),
+        (Q4, 0, 288, 64, 512, FAKE + big),
+        (Q4, FAKE, 288, 64, 512, 0),
+        (Q4, FAKE + 8, 288, 64, 512, FAKE + big),
+        (Q4, FAKE, 288, 64, 512, FAKE + big + 2),
+        (Q4, FAKE, 288, 32, 512, FAKE + big),        # rows not a multiple of 64
+        (Q4, FAKE, 288, 0, 512, FAKE + big),
+        (Q4, FAKE, 288, 64, 500, FAKE + big),        # K not a multiple of 256
+        (Q4, FAKE, 280, 64, 512, FAKE + big),        # stride below the row's 288 bytes
+        (Q6, FAKE, 421, 64, 512, FAKE + big),        # odd stride
+        (Q4, FAKE, 288, 64, 512, FAKE + 4096),       # destination overlaps the source
+        (Q4, FAKE + 4096, 288, 64, 512, FAKE),
+    ]
+    for i, a in enumerate(bad):
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_repack_tile64(*a, stream=0)
+        assert ei.value.status == M.MOE_EINVAL, i
 
 
 def test_stage_names_and_path_rule():

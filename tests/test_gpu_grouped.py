@@ -4,8 +4,10 @@ picks it only past ~160 MB of per-pair expert bytes, which these shrunk shapes
 never reach): ids exact, outputs within 2e-3 of ||y||_2 per token. Covers experts
 with several 16-token tiles, ragged tiles, the dense k = E case, bf16 input,
 Q6_K down rows, the shared-expert gate vector, NULL experts, invalid ids,
-agreement with the per-pair decode path, and the full Kimi-K2-shaped
-256-token chunk (routing on every token, outputs on 40)."""
+agreement with the per-pair decode path, expert matrices stored in 64-row
+tiles (the same bytes as row order, and the repack itself byte-exact), and
+the full Kimi-K2-shaped 256-token chunk (routing on every token, outputs on
+40) in both block orders."""
 import numpy as np
 import pytest
 import torch
@@ -19,6 +21,7 @@ from tests.shrunk import SHRUNK
 
 pytestmark = pytest.mark.gpu
 GP = M.MOE_PATH_GROUPED
+TILE = M.MOE_LAYOUT_TILE64
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 5), ("tiny", 37), ("deepseek-v4-flash", 33),
@@ -26,6 +29,80 @@ GP = M.MOE_PATH_GROUPED
 def test_grouped_shrunk(name, T):
     """Ragged tiles and experts with more than 16 routed tokens."""
     check_layer(SHRUNK[name], T=T, x_index=T, path=GP)
+
+
+def tile64_reference(rows: np.ndarray, n_rows: int, nb: int, BB: int) -> np.ndarray:
+    """TILE64 order written out from its definition: block b of row r at
+    ((r // 64) nb + b) 64 BB + (r % 64) BB."""
+    out = np.zeros(n_rows * nb * BB, np.uint8)
+    for r in range(n_rows):
+        for b in range(nb):
+            o = ((r // 64) * nb + b) * 64 * BB + (r % 64) * BB
+            out[o:o + BB] = rows[r, b * BB:(b + 1) * BB]
+    return out
+
+
+@pytest.mark.parametrize("fmt,BB,n_rows,K,stride", [(M.MOE_WFMT_Q4_K, 144, 128, 512, 304),
+                                                     (M.MOE_WFMT_Q6_K, 210, 192, 768, 640),
+                                                     (M.MOE_WFMT_Q4_K, 144, 64, 256, 144)])
+def test_repack_tile64_bytes(fmt, BB, n_rows, K, stride):
+    """The repack moves whole blocks to where the definition puts them; row
+    padding is dropped."""
+    rng = np.random.default_rng(n_rows + K)
+    rows = rng.integers(0, 256, (n_rows, stride), dtype=np.uint8)
+    src = torch.from_numpy(rows.reshape(-1)).cuda()
+    nbytes = M.tile64_bytes(fmt, n_rows, K)
+    dst = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    M.moe_repack_tile64(fmt, src, stride, n_rows, K, dst)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:nbytes], tile64_reference(rows, n_rows, K // 256, BB))
+    assert (got[nbytes:] == 0xA5).all()  # nothing written past the matrix
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 37), ("deepseek-v4-flash", 33), ("kimi-k2", 20),
+                                    ("qwen3.6-35b-a3b", 18), ("deepseek-v4-flash", 1)])
+def test_grouped_tile64(name, T):
+    """Expert matrices in 64-row tiles: oracle parity, and the same bytes as the
+    grouped path over row-order matrices (the kernels do the same arithmetic;
+    only the addresses of a stage's blocks differ)."""
+    cfg = SHRUNK[name]
+    data = gen.make_layer(cfg)
+    y, ids, w, _ = check_layer(cfg, data=data, T=T, x_index=T + 1, layout=TILE)
+    x, xb = gen.make_x(cfg, T=T, x_index=T + 1)
+    dr = DeviceLayer(data, path=GP, layout=M.MOE_LAYOUT_ROWS)
+    xt, dt = x_to_device(data, x, xb)
+    yr, idr, wr = run_layer(dr, xt, dt, T)
+    assert np.array_equal(ids, idr) and np.array_equal(w, wr)
+    assert np.array_equal(y.view(np.uint32), yr.view(np.uint32))
+
+
+def test_grouped_tile64_null_experts_and_given_routing():
+    """64-row tiles with NULL experts and caller-given routing (moe_expert_ffn)."""
+    cfg = SHRUNK["deepseek-v4-flash"]
+    mask = np.random.default_rng(5).random(cfg.E) < 0.6
+    check_layer(cfg, T=14, x_index=3, present=mask, layout=TILE)
+    data = gen.make_layer(cfg)
+    T = 9
+    x, _ = gen.make_x(cfg, T=T, x_index=4)
+    rng = np.random.default_rng(8)
+    ids = np.stack([rng.choice(cfg.E, cfg.k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, cfg.k)).astype(np.float32)
+    dl = DeviceLayer(data, layout=TILE)
+    xt = torch.from_numpy(x).cuda()
+    qs = torch.empty((T, cfg.H), dtype=torch.int8, device="cuda")
+    d = torch.empty((T, cfg.H // 256), dtype=torch.float32, device="cuda")
+    bs = torch.empty((T, cfg.H // 16), dtype=torch.int16, device="cuda")
+    q = M.qact(qs, d, bs, M.MOE_AFMT_Q8_K, T, cfg.H)
+    M.moe_quantize_act_q8k(xt, M.MOE_DTYPE_F32, T, cfg.H, M.MOE_AFMT_Q8_K, q)
+    y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+    ws = dl.workspace(T)
+    M.moe_expert_ffn(dl.desc, q, xt, M.MOE_DTYPE_F32, T, torch.from_numpy(ids).cuda(),
+                     torch.from_numpy(w).cuda(), y, ws, ws.numel())
+    torch.cuda.synchronize()
+    L = oracle.Layer(data)
+    for t in range(T):
+        assert rel_err(y[t].cpu().numpy(), L.expert_part(x[t], ids[t], w[t])) <= Y_TOL, t
 
 
 def test_grouped_dense_k_equals_E():
@@ -146,18 +223,26 @@ def test_grouped_expert_ffn_invalid_ids():
 
 def test_grouped_full_kimi_k2():
     """Kimi-K2-shaped layer at full size (384 experts, H 7168, F 2048, 9.5 GB of
-    Q4_K experts), one 256-token chunk as the benchmark runs it. Routing (ids
-    exact, weights within 1e-6) is checked on all 256 tokens against the
-    oracle's router and top-k; the layer output on 40 tokens (first, last and
-    a spread in between)."""
+    Q4_K experts), one 256-token chunk as the benchmark runs it (experts in
+    64-row tiles), and the same chunk over row-order experts (identical bytes
+    out). Routing (ids exact, weights within 1e-6) is checked on all 256
+    tokens against the oracle's router and top-k; the layer output on 40
+    tokens (first, last and a spread in between)."""
     cfg = gen.CONFIGS["kimi-k2"]
     say("kimi-k2 full: generating the layer")
     data = gen.make_layer(cfg)
     T = cfg.T
     x, xb = gen.make_x(cfg, T=T, x_index=0)
-    dl = DeviceLayer(data)
+    dl = DeviceLayer(data, layout=TILE)
     xt, dt = x_to_device(data, x, xb)
     y, ids, w = run_layer(dl, xt, dt, T)
+    del dl
+    say("kimi-k2 full: row-order experts")
+    dr = DeviceLayer(data, layout=M.MOE_LAYOUT_ROWS)
+    yr, idr, wr = run_layer(dr, xt, dt, T)
+    del dr
+    assert np.array_equal(ids, idr) and np.array_equal(w, wr)
+    assert np.array_equal(y.view(np.uint32), yr.view(np.uint32))
     say("kimi-k2 full: oracle routing of all 256 tokens")
     for t in range(T):
         lg = oracle.router_logits(data.w_router, x[t])

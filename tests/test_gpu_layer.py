@@ -148,22 +148,36 @@ def _routed_layer(cfg, T, x_index):
     ("deepseek-v4-flash", 1, M.MOE_PATH_GEMV), ("deepseek-v4-flash", 3, M.MOE_PATH_GEMV),
     ("deepseek-v4-flash", 1, M.MOE_PATH_AUTO), ("deepseek-v4-flash", 3, M.MOE_PATH_AUTO),
     ("kimi-k2", 1, M.MOE_PATH_GEMV), ("kimi-k2", 2, M.MOE_PATH_GEMV),
-    ("kimi-k2", 1, M.MOE_PATH_AUTO), ("kimi-k2", 2, M.MOE_PATH_AUTO)])
+    ("kimi-k2", 1, M.MOE_PATH_AUTO), ("kimi-k2", 2, M.MOE_PATH_AUTO),
+    ("deepseek-v4-flash", 1, "tile64"), ("kimi-k2", 2, "tile64")])
 def test_layer_full_decode_routed(name, T, path):
     """Full-size DeepSeek-V4-Flash and Kimi-K2 layers at one to three tokens:
     the per-pair path (sigmoid routers, DeepSeek with selection bias; E = 384,
     16 candidates per lane in the top-k; Q6_K down rows in registers and Q4_K
     down rows through LDS at H = 7168), and the same small chunks on the path
     the automatic rule picks for them (expert-grouped: their experts hold 8 MB
-    or more of blocks)."""
+    or more of blocks), also with the experts in 64-row tiles."""
     cfg = gen.CONFIGS[name]
-    check_layer(cfg, data=_routed_layer(cfg, T, 30 + T), T=T, x_index=30 + T, path=path)
+    layout = M.MOE_LAYOUT_TILE64 if path == "tile64" else M.MOE_LAYOUT_ROWS
+    path = M.MOE_PATH_AUTO if path == "tile64" else path
+    check_layer(cfg, data=_routed_layer(cfg, T, 30 + T), T=T, x_index=30 + T, path=path,
+                layout=layout)
 
 
 def test_layer_full_verify_chunk_sampled():
-    """DeepSeek-V4-Flash-shaped 16-token chunk at full size; the oracle checks
-    every token."""
-    check_layer(gen.CONFIGS["deepseek-v4-flash"], tokens=range(16), threads=16)
+    """DeepSeek-V4-Flash-shaped 16-token chunk at full size, experts in 64-row
+    tiles as the benchmark runs it; the oracle checks every token. The same
+    chunk over row-order experts gives the same bytes."""
+    cfg = gen.CONFIGS["deepseek-v4-flash"]
+    data = gen.make_layer(cfg)
+    y, ids, w, _ = check_layer(cfg, data=data, tokens=range(16), threads=16,
+                               layout=M.MOE_LAYOUT_TILE64)
+    x, xb = gen.make_x(cfg, T=cfg.T, x_index=0)
+    dr = DeviceLayer(data, layout=M.MOE_LAYOUT_ROWS)
+    xt, dt = x_to_device(data, x, xb)
+    yr, idr, wr = run_layer(dr, xt, dt, cfg.T)
+    assert np.array_equal(ids, idr) and np.array_equal(w, wr)
+    assert np.array_equal(y.view(np.uint32), yr.view(np.uint32))
 
 
 @pytest.mark.parametrize("path", [M.MOE_PATH_GEMV, M.MOE_PATH_GROUPED])
