@@ -22,7 +22,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kMaxTokens = 2048;
 
 bool known_fmt(int fmt) { return fmt >= MOE_WFMT_Q4_K && fmt <= MOE_WFMT_Q5_1; }
 int block_elems(int fmt) { return act32(fmt) ? 32 : 256; }
@@ -133,7 +132,6 @@ void bind_ws(KArgs& a, const WsLayout& L, void* ws) {
   a.hd = reinterpret_cast<float*>(b + L.hd);
   a.hbs = reinterpret_cast<int16_t*>(b + L.hbs);
   a.rpart = reinterpret_cast<double*>(b + L.rpart);
-  a.pair_tmp = reinterpret_cast<int32_t*>(b + L.pair_tmp);
   a.plist = reinterpret_cast<int2*>(b + L.plist);
   a.present = reinterpret_cast<int32_t*>(b + L.present);
   a.tiles = reinterpret_cast<GTile*>(b + L.tiles);
@@ -220,7 +218,6 @@ WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool group
     L.hd = take(P * (F / 256) * 4);
     L.hbs = take(P * (F / 16) * 2);
     L.rpart = take(static_cast<size_t>(rs.ks) * T * (E + 1) * 8);
-    L.pair_tmp = take(P * 4);
     L.plist = take(P * 8);
     L.present = take(P * 4);
     L.tiles = take(static_cast<size_t>(max_tiles(T, k, E, has_shared)) * sizeof(GTile));
@@ -232,7 +229,7 @@ WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool group
     L.hqs = take(P * (F / 32) * 80);  // 80 bytes per 32-value block (kApPitch pairs)
     L.hd = take(P * (F / 32) * 4);
     L.hbs = 0;
-    L.rpart = L.pair_tmp = L.plist = L.present = L.tiles = L.part = L.xe = L.he = 0;
+    L.rpart = L.plist = L.present = L.tiles = L.part = L.xe = L.he = 0;
   }
   L.total = off;
   return L;

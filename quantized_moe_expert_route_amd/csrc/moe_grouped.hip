@@ -731,7 +731,9 @@ __device__ __forceinline__ void router_quant_wave(const KArgs& a, int job, int l
 // products of fp32 values are exact in fp64). grid nwg_r + quant workgroups,
 // block 256. Router wave w: K slice w % KS of (token tile, expert tile) w / KS;
 // column E of the expert tiles is the shared-expert gate vector when present.
-// Quant waves: q8 of one 256-element piece of x.
+// Quant waves: q8 of one 256-element piece of x. BF: x in bf16 (else fp32), a
+// template argument so that no dtype branch sits between the batched loads.
+template <bool BF>
 __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS, int L, int n_et,
                                                      int n_work, int nwg_r) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -762,28 +764,28 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
   };
   auto load_xv = [&](int kk) -> float4 {
     const size_t o = static_cast<size_t>(t) * a.H + kk;
-    if (a.x_dtype == 0) return ldg_f4(static_cast<const float*>(a.x) + o);
+    if constexpr (!BF) return ldg_f4(static_cast<const float*>(a.x) + o);
     const uint2 bb = ld8(static_cast<const uint16_t*>(a.x) + o);
     return make_float4(bf16_bits_to_f32(bb.x & 0xFFFF), bf16_bits_to_f32(bb.x >> 16),
                        bf16_bits_to_f32(bb.y & 0xFFFF), bf16_bits_to_f32(bb.y >> 16));
   };
   // MFMA step n, lane group g: k = k0 + 16 n + 4 g + s for s = 0..3 (the same
-  // k for A and B, so the k order is only a reordering of the sum)
-  int n = 0;
-  for (; n + 4 <= nst; n += 4) {
-    float4 xv[4], wv4[4];
+  // k for A and B, so the k order is only a reordering of the sum). The loads
+  // of U steps are issued before their MFMAs: one memory round trip per U
+  // steps (a slice of up to 256 k is one round trip); steps past the slice
+  // reload its last step and are not multiplied.
+  constexpr int U = 16;
+  for (int n = 0; n < nst; n += U) {
+    float4 xv[U], wv4[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kk = k0 + 16 * (n + u) + 4 * g;
+    for (int u = 0; u < U; ++u) {
+      const int kk = k0 + 16 * min(n + u, nst - 1) + 4 * g;
       xv[u] = load_xv(kk);
       wv4[u] = ldg_f4(wr + kk);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) step(xv[u], wv4[u]);
-  }
-  for (; n < nst; ++n) {
-    const int kk = k0 + 16 * n + 4 * g;
-    step(load_xv(kk), ldg_f4(wr + kk));
+    for (int u = 0; u < U; ++u)
+      if (n + u < nst) step(xv[u], wv4[u]);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -801,7 +803,8 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
 // on XCD s (dispatch order), so each slice's x and W are read into one L2. Same
 // sums and partial layout as k_router_mfma (the k order inside a slice is only
 // a reordering of the sum). grid nwg_r (8 per 4 tile pairs) + quant
-// workgroups, block 256.
+// workgroups, block 256. BF as in k_router_mfma.
+template <bool BF>
 __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int KS, int L,
                                                        int n_et2, int n_work, int nwg_r) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -832,7 +835,7 @@ __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int K
     for (int j = 0; j < 2; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
   auto load_xv = [&](int tok, int kk) -> float4 {
     const size_t o = static_cast<size_t>(tok) * a.H + kk;
-    if (a.x_dtype == 0) return ldg_f4(static_cast<const float*>(a.x) + o);
+    if constexpr (!BF) return ldg_f4(static_cast<const float*>(a.x) + o);
     const uint2 bb = ld8(static_cast<const uint16_t*>(a.x) + o);
     return make_float4(bf16_bits_to_f32(bb.x & 0xFFFF), bf16_bits_to_f32(bb.x >> 16),
                        bf16_bits_to_f32(bb.y & 0xFFFF), bf16_bits_to_f32(bb.y >> 16));
@@ -853,7 +856,7 @@ __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int K
       }
   };
   // MFMA step n, lane group g: k = k0 + 16 n + 4 g + s for s = 0..3
-  constexpr int U = 4;  // steps whose loads are issued together
+  constexpr int U = 8;  // steps whose loads are issued together
   int n = 0;
   for (; n + U <= nst; n += U) {
     float4 xv[U][2], wv4[U][2];
@@ -906,7 +909,7 @@ __global__ __launch_bounds__(256) void k_topk_sum(KArgs a, int KS) {
   for (int i = 0; i < NC; ++i) s[i] = 0.0;
   // slices in batches whose loads are all issued before the first add (one
   // memory round trip per batch); the sums still run in slice order
-  constexpr int KB = NC <= 8 ? 8 : 4;
+  constexpr int KB = NC <= 4 ? 16 : NC <= 8 ? 8 : 4;
   for (int k0 = 0; k0 < KS; k0 += KB) {
     double v[KB][NC];
 #pragma unroll
@@ -915,6 +918,9 @@ __global__ __launch_bounds__(256) void k_topk_sum(KArgs a, int KS) {
 #pragma unroll
       for (int i = 0; i < NC; ++i) v[kb][i] = rp[ks * kstride + min(lane + 64 * i, a.E - 1)];
     }
+    // keep the compiler from interleaving the adds with the loads (it would
+    // otherwise keep only a few loads in flight)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       if (k0 + kb < KS) {
@@ -942,21 +948,45 @@ __global__ __launch_bounds__(256) void k_topk_sum(KArgs a, int KS) {
 // Pair p = t * k + slot is present when its id is in range and the expert's
 // gate pointer is not NULL; the shared expert is pseudo-expert E with pairs
 // T * k + t. Output: plist sorted by (expert, pair), tiles of <= 16 consecutive
-// entries of one expert, the tile count in counters[0].
+// entries of one expert, the tile count in counters[0], the presence flags.
+// Every global load (ids, the experts' pointers) is issued at the start; the
+// sort itself runs in LDS (pair and expert ids fit 16 bits).
+constexpr int kMaxPairs = kMaxTokens * MOE_MAX_TOPK;
+static_assert(kMaxPairs <= 65536 && MOE_MAX_EXPERTS < 65535, "16-bit pair and expert ids");
 __global__ __launch_bounds__(1024) void k_bucket(KArgs a) {
   __shared__ int cnt[MOE_MAX_EXPERTS + 1];
   __shared__ int off[MOE_MAX_EXPERTS + 2];
   __shared__ int toff[MOE_MAX_EXPERTS + 2];
   __shared__ int cur[MOE_MAX_EXPERTS + 1];
+  __shared__ uint8_t have[MOE_MAX_EXPERTS];  // gate[e] != NULL
+  __shared__ uint16_t s_e[kMaxPairs];        // expert of pair p, 0xFFFF when absent
+  __shared__ uint16_t s_grp[kMaxPairs];      // pairs grouped by expert, unordered inside
   const int tid = threadIdx.x, E = a.E, NE = E + 1, Tk = a.T * a.k;
+  constexpr uint16_t kNone = 0xFFFF;
+  // this thread's expert (tid < E <= 1024): its pointers, loaded up front
+  const void *pg = nullptr, *pu = nullptr, *pd = nullptr;
+  const float *bg = nullptr, *bu = nullptr, *bd = nullptr;
+  if (tid < E) {
+    pg = a.gate[tid];
+    pu = a.up[tid];
+    pd = a.down[tid];
+    if (a.b_gate) { bg = a.b_gate[tid]; bu = a.b_up[tid]; }
+    if (a.b_down) bd = a.b_down[tid];
+  }
+  for (int p = tid; p < Tk; p += 1024) {
+    const int e = a.ids[p];
+    s_e[p] = static_cast<unsigned>(e) < static_cast<unsigned>(E) ? static_cast<uint16_t>(e) : kNone;
+  }
   for (int i = tid; i < NE; i += 1024) {
     cnt[i] = 0;
     cur[i] = 0;
   }
+  if (tid < E) have[tid] = pg != nullptr;
   __syncthreads();
   for (int p = tid; p < Tk; p += 1024) {
-    const int e = a.ids[p];
-    const bool ok = static_cast<unsigned>(e) < static_cast<unsigned>(E) && a.gate[e] != nullptr;
+    const int e = s_e[p];
+    const bool ok = e != kNone && have[e];
+    if (!ok) s_e[p] = kNone;
     a.present[p] = ok;
     if (ok) atomicAdd(&cnt[e], 1);
   }
@@ -998,13 +1028,13 @@ __global__ __launch_bounds__(1024) void k_bucket(KArgs a) {
     GTile tl;
     tl.e = e;
     tl.pad = 0;
-    if (e < E) {
-      tl.gate = static_cast<const uint8_t*>(a.gate[e]);
-      tl.up = static_cast<const uint8_t*>(a.up[e]);
-      tl.down = static_cast<const uint8_t*>(a.down[e]);
-      tl.b_gate = a.b_gate ? a.b_gate[e] : nullptr;
-      tl.b_up = a.b_up ? a.b_up[e] : nullptr;
-      tl.b_down = a.b_down ? a.b_down[e] : nullptr;
+    if (e < E) {  // e == tid: this thread's pointers
+      tl.gate = static_cast<const uint8_t*>(pg);
+      tl.up = static_cast<const uint8_t*>(pu);
+      tl.down = static_cast<const uint8_t*>(pd);
+      tl.b_gate = bg;
+      tl.b_up = bu;
+      tl.b_down = bd;
     } else {
       tl.gate = static_cast<const uint8_t*>(a.sh_gate);
       tl.up = static_cast<const uint8_t*>(a.sh_up);
@@ -1018,23 +1048,20 @@ __global__ __launch_bounds__(1024) void k_bucket(KArgs a) {
     }
   }
   for (int p = tid; p < Tk; p += 1024) {
-    if (a.present[p]) {
-      const int e = a.ids[p];
-      a.pair_tmp[off[e] + atomicAdd(&cur[e], 1)] = p;
-    }
+    const int e = s_e[p];
+    if (e != kNone) s_grp[off[e] + atomicAdd(&cur[e], 1)] = static_cast<uint16_t>(p);
   }
   if (a.has_shared)
     for (int t = tid; t < a.T; t += 1024) a.plist[off[E] + t] = make_int2(Tk + t, t);
-  __threadfence_block();
   __syncthreads();
   // sorted position = bucket start + number of smaller pair ids in the bucket
   const int nr = off[E];
   for (int i = tid; i < nr; i += 1024) {
-    const int p = a.pair_tmp[i];
-    const int e = a.ids[p];
+    const int p = s_grp[i];
+    const int e = s_e[p];
     const int b0 = off[e], n = cnt[e];
     int rank = 0;
-    for (int j = 0; j < n; ++j) rank += a.pair_tmp[b0 + j] < p;
+    for (int j = 0; j < n; ++j) rank += s_grp[b0 + j] < p;
     a.plist[b0 + rank] = make_int2(p, p / a.k);
   }
 }
@@ -1254,14 +1281,14 @@ hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hip
     const int n_et2 = (E1 + 31) / 32, n_tt2 = (a.T + 31) / 32;
     const int n_work = n_tt2 * n_et2;  // tile pairs, each in all 8 K slices
     const int nwg_r = 8 * ((n_work + 3) / 4);
-    return launch(k_router_mfma22, dim3(nwg_r + nq), 256, 0, s, ev, a, quant ? 1 : 0, rs.ks,
-                  rs.len, n_et2, n_work, nwg_r);
+    return launch(a.x_dtype ? k_router_mfma22<true> : k_router_mfma22<false>, dim3(nwg_r + nq),
+                  256, 0, s, ev, a, quant ? 1 : 0, rs.ks, rs.len, n_et2, n_work, nwg_r);
   }
   const int n_et = (E1 + 15) / 16, n_tt = (a.T + 15) / 16;
   const int n_work = n_tt * n_et * rs.ks;
   const int nwg_r = (n_work + 3) / 4;
-  return launch(k_router_mfma, dim3(nwg_r + nq), 256, 0, s, ev, a, quant ? 1 : 0, rs.ks, rs.len,
-                n_et, n_work, nwg_r);
+  return launch(a.x_dtype ? k_router_mfma<true> : k_router_mfma<false>, dim3(nwg_r + nq), 256,
+                0, s, ev, a, quant ? 1 : 0, rs.ks, rs.len, n_et, n_work, nwg_r);
 }
 
 hipError_t launch_topk_sum(const KArgs& a, RouterSplit rs, hipStream_t s, Ev ev) {

@@ -105,7 +105,6 @@ struct KArgs {
   uint32_t* counters;  // one word per (token, slot) pair, reset by the router kernel
   // grouped path
   double* rpart;       // [KS, T, E1] router partial sums (E1 = E + shared gate row)
-  int32_t* pair_tmp;   // [P] pairs bucketed by expert, unordered within an expert
   int2* plist;         // [P] (pair, token), sorted by (expert, pair); shared expert last
   int32_t* present;    // [P] 1 if the pair's expert is present
   GTile* tiles;        // [max tiles]
@@ -128,13 +127,17 @@ struct KArgs {
 
 // Workspace layout (byte offsets from the base, each 256-aligned).
 struct WsLayout {
-  size_t counters, xqs, xd, xbs, logits, ids, w, shw, slots, h, hqs, hd, hbs, rpart, pair_tmp,
-      plist, present, tiles, part, xe, he, total;
+  size_t counters, xqs, xd, xbs, logits, ids, w, shw, slots, h, hqs, hd, hbs, rpart, plist,
+      present, tiles, part, xe, he, total;
 };
 WsLayout ws_layout(int H, int F, int E, int k, int T, int has_shared, bool grouped, bool mx8);
 
 // Dynamic LDS a workgroup may use (bytes).
 constexpr size_t kMaxLds = 64 * 1024;
+
+// Largest chunk (tokens) of one call, and so at most kMaxTokens * MOE_MAX_TOPK
+// routed (token, slot) pairs.
+constexpr int kMaxTokens = 2048;
 
 // Whether the GEMV kernels' LDS needs fit for this layer and chunk.
 bool gemv_fits(const KArgs& a);
