@@ -490,11 +490,7 @@ __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
     xq1 = reinterpret_cast<const int4*>(xq)[2 * li + 1];
     xdv = xd[li];
   }
-  if (!routed) {
-    gbase = static_cast<const uint8_t*>(a.sh_gate);
-    ubase = static_cast<const uint8_t*>(a.sh_up);
-    issue();  // the shared expert does not wait for routing
-  } else if (wave != tkw) {
+  if (routed && wave != tkw) {
     const void* g[6];
     const void* u[6];
 #pragma unroll
@@ -513,7 +509,7 @@ __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
         ltab[2 * i + 1] = u[j];
       }
     }
-  } else {
+  } else if (routed) {
     const int slot = p - t * a.k;
     __builtin_amdgcn_s_setprio(3);
     if (routing_given) {
@@ -584,9 +580,17 @@ __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
       return;
     }
     ubase = static_cast<const uint8_t*>(ltab[2 * e + 1]);
-    issue();
     if (a.b_gate) { bg = a.b_gate[e]; bu = a.b_up[e]; }
+  } else {
+    gbase = static_cast<const uint8_t*>(a.sh_gate);
+    ubase = static_cast<const uint8_t*>(a.sh_up);
   }
+  // One issue site for both kinds of pair, after the bias pointer loads: loads
+  // complete in issue order, so a pointer loaded after the rows could only be
+  // used once all of them had arrived, and row registers merged from two
+  // issue sites are copied, which waits for every load in flight. Either way
+  // the first pair's dots would wait for the wave's whole stream.
+  issue();
   MxAct<NBL> A;
   mx_act_load(A, lap, ld, nb, lane);
   float* hrow = a.h + static_cast<size_t>(p) * a.F;
