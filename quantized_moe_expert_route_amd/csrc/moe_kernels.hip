@@ -262,11 +262,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
   // the selection waves of co-resident workgroups run on different SIMDs.
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tkw = ((blockIdx.x + blockIdx.y * gridDim.x) >> 8) & 3;
-  if (!routed) {
-    gbase = static_cast<const uint8_t*>(a.sh_gate);
-    ubase = static_cast<const uint8_t*>(a.sh_up);
-    issue_loads();  // the shared expert does not wait for routing
-  } else if (wave != tkw) {
+  if (routed && wave != tkw) {
     // E <= 1024: at most 6 entries per thread; issue the loads, then store
     const int li = (wave - (wave > tkw ? 1 : 0)) * 64 + lane;  // 0..191
     const void* g[6];
@@ -287,7 +283,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
         ltab[2 * i + 1] = u[j];
       }
     }
-  } else {
+  } else if (routed) {
     const int slot = p - t * a.k;
     // the selection is one long dependent chain: issue priority over the
     // co-resident workgroups' block arithmetic on this SIMD
@@ -354,9 +350,16 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
       return;
     }
     ubase = static_cast<const uint8_t*>(ltab[2 * e + 1]);
-    issue_loads();
     if (a.b_gate) { bg = a.b_gate[e]; bu = a.b_up[e]; }
+  } else {
+    gbase = static_cast<const uint8_t*>(a.sh_gate);
+    ubase = static_cast<const uint8_t*>(a.sh_up);
   }
+  // One issue site for both kinds of pair, after the bias pointer loads: a
+  // pointer loaded after the blocks could only be used once all of them had
+  // arrived (loads complete in issue order), and block registers merged from
+  // two issue sites are copied, which waits for every load in flight.
+  issue_loads();
   ActView av{lqs, ld, lbs, lap};
 #pragma unroll
   for (int i = 0; i < TPG; ++i) {
