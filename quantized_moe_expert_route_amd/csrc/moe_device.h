@@ -1007,22 +1007,125 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
+// Per-wave LDS scratch of the candidate ranking below (workgroups of at most
+// four waves): up to 64 composite keys and their ranks.
+struct TopkLds {
+  uint64_t* cand;
+  int* rank;
+};
+__device__ __forceinline__ TopkLds topk_lds() {
+  __shared__ __align__(16) uint64_t cand[4][64];
+  __shared__ int rank[4][64];
+  const int w = (threadIdx.x >> 6) & 3;
+  return TopkLds{cand[w], rank[w]};
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One-pass ranking of the keys that can be among the 8 largest (keys as in
+// topk_select: expert e = lane + 64 i in register i, 0 = absent).
+//
+// The lanes form 8 groups of 8; the maxima of the groups are keys of 8
+// different experts, so at least 8 keys reach tau, the smallest group maximum,
+// and so does every key among the 8 largest. A key that outranks a candidate
+// (a present key >= tau) is a candidate itself, so a candidate's rank among the
+// candidates is its rank among all keys. The candidates are written to LDS as
+// (key << 32 | ~expert): distinct, and ordered as (key descending, expert
+// ascending). Lane l < C then counts the candidates above cand[l]; every rank
+// comes out of one pass instead of one wave reduction per rank.
+//
+// Returns C, the number of candidates (wave-uniform), or 0 when more than 64
+// keys reach tau (equal keys at the threshold); nothing is ranked then. For
+// C > 0: lane l < C holds the rank r of candidate mine = cand[l]; pos[i] is
+// the list position of register i's key, or -1 when it is not a candidate.
+template <int NC>
+__device__ __forceinline__ int topk_rank8(const uint32_t (&key)[NC], uint64_t* cand, int& r,
+                                          uint64_t& mine, int (&pos)[NC]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t m = key[0];
+#pragma unroll
+  for (int i = 1; i < NC; ++i) m = max(m, key[i]);
+  // maxima over 8 consecutive lanes (row shifts by 1, 2, 4 within rows of 16;
+  // lanes without a source read 0, the identity of the unsigned max): lane
+  // 8 g + 7 then holds group g's maximum
+  m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x111, 0xF, 0xF, true)));
+  m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x112, 0xF, 0xF, true)));
+  m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x114, 0xF, 0xF, true)));
+  uint32_t tau = 0xFFFFFFFFu;
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+    tau = min(tau, static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(m), 8 * g + 7)));
+  const uint32_t th = max(tau, 1u);  // a group of absent keys only: every present key
+  int C = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const bool c = key[i] >= th;
+    const unsigned long long b = __builtin_amdgcn_ballot_w64(c);
+    const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(b >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
+    pos[i] = c ? C + below : -1;
+    C += __builtin_popcountll(b);
+  }
+  if (C > 64) return 0;  // wave-uniform
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+    if (pos[i] >= 0)
+      cand[pos[i]] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(~(lane + 64 * i));
+  if (lane >= C) cand[lane] = 0;  // below every candidate
+  wave_lds_sync();
+  mine = cand[lane];
+  int cnt = 0;
+  for (int j = 0; j < C; j += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = cand[j + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cnt += v[u] > mine ? 1 : 0;
+  }
+  r = cnt;
+  return C;
+}
+
 // Top-k selection over order-preserving keys, expert e = lane + 64 i held in
 // register i of every lane. key 0 marks an absent candidate (every real key
 // is above it). On return rank[i] is the rank (0 = first) of that candidate,
 // or -1 when it is not among the k selected. Rank order is key descending,
 // index ascending.
 //
-// Fast path: k rounds of one 32-bit wave max each; every candidate equal to
-// the round's maximum takes rank r and leaves. That is exact when every
+// k <= 8 and E > 64: the one-pass candidate ranking (topk_rank8; for E <= 64
+// every key is a candidate, and the gpt-oss shape, E = 32 and k = 4, measured
+// slower with it than with the rounds). Otherwise, and when more than 64 keys
+// reach its threshold, rounds of one wave reduction each.
+// Their fast path: k rounds of one 32-bit wave max each; every candidate equal
+// to the round's maximum takes rank r and leaves. That is exact when every
 // round's maximum is unique, which holds exactly when k candidates end up
 // ranked (each round ranks at least one). Otherwise (equal keys) the exact
 // path reruns the selection with the lowest index taken first among equal
 // keys: per round the lowest hit lane of each register's ballot gives a
 // candidate index, and the smallest of those wins.
 template <int NC>
-__device__ __forceinline__ void topk_select(const uint32_t (&key0)[NC], int k, int (&rank)[NC]) {
+__device__ __forceinline__ void topk_select(const uint32_t (&key0)[NC], int E, int k,
+                                            int (&rank)[NC]) {
   const int lane = threadIdx.x & 63;
+  if (E > 64 && k <= 8) {  // one-pass candidate ranking (wave-uniform branches)
+    const TopkLds s = topk_lds();
+    int r, pos[NC];
+    uint64_t mine;
+    if (topk_rank8<NC>(key0, s.cand, r, mine, pos) > 0) {
+      s.rank[lane] = r;  // lanes past the candidates store a rank nobody reads
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int rr = s.rank[pos[i] < 0 ? 0 : pos[i]];
+        rank[i] = pos[i] >= 0 && rr < k ? rr : -1;
+      }
+      return;
+    }
+  }
   uint32_t key[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) { key[i] = key0[i]; rank[i] = -1; }
@@ -1104,14 +1207,30 @@ __device__ __forceinline__ int topk_round(uint32_t (&key)[NC]) {
   return static_cast<int>(e);
 }
 
-// Expert index of rank n (0-based; n < the number of candidates), exact. Fast
-// path: n + 1 rounds of one wave max each, every candidate equal to the
+// Expert index of rank n (0-based; n < the number of candidates), exact.
+// n < 8 and E > 64: the one-pass candidate ranking (topk_rank8). Otherwise,
+// and when more than 64 keys reach its threshold, rounds. Their fast path: n + 1
+// rounds of one wave max each, every candidate equal to the
 // round's maximum leaving; the rank-n expert is the one equal to the last
 // maximum. That is exact when every round's maximum is unique; the ballot
 // counts that check it sit off the dependent chain. Otherwise the exact
 // rounds (lowest index first among equal keys) run from the original keys.
 template <int NC>
-__device__ __forceinline__ int topk_nth(const uint32_t (&key0)[NC], int n) {
+__device__ __forceinline__ int topk_nth(const uint32_t (&key0)[NC], int E, int n) {
+  if (E > 64 && n < 8) {  // one-pass candidate ranking (wave-uniform branches)
+    const int lane = threadIdx.x & 63;
+    const TopkLds s = topk_lds();
+    int r, pos[NC];
+    uint64_t mine;
+    const int C = topk_rank8<NC>(key0, s.cand, r, mine, pos);
+    if (C > 0) {
+      // ranks 0..C-1 are held once each, and n < 8 <= C or n < E = C
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < C && r == n);
+      const int l = static_cast<int>(__builtin_ctzll(hit));
+      return static_cast<int>(~static_cast<uint32_t>(
+          __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(mine)), l)));
+    }
+  }
   uint32_t key[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) key[i] = key0[i];
@@ -1220,7 +1339,7 @@ __device__ __forceinline__ void wave_topk_regs(float (&lg)[NC], const float* sel
     lg[i] = valid ? lg[i] : -INFINITY;
   }
   int rank[NC];
-  topk_select<NC>(key, k, rank);
+  topk_select<NC>(key, E, k, rank);
   // ids and the selected logits in rank order; lane r < k then holds rank r
   __shared__ float s_rank_l[16][16];
   float* rl = s_rank_l[(threadIdx.x >> 6) & 15];

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) void k_gateup(KArgs a, int R, int routing_give
         lg[i] = a.logits[static_cast<size_t>(t) * a.E + min(lane + 64 * i, a.E - 1)];
       uint32_t key[NC];
       topk_keys<NC>(lg, a.sel_bias, a.E, key);
-      const int e = topk_nth<NC>(key, slot);
+      const int e = topk_nth<NC>(key, a.E, slot);
       if (lane == 0) s_e = e;
     } else {
       wave_topk<NC>(a.logits + static_cast<size_t>(t) * a.E, a.sel_bias, a.E, a.k, a.router,
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
         lg[i] = a.logits[static_cast<size_t>(t) * a.E + min(lane + 64 * i, a.E - 1)];
       uint32_t key[NC];
       topk_keys<NC>(lg, a.sel_bias, a.E, key);
-      const int e = topk_nth<NC>(key, slot);
+      const int e = topk_nth<NC>(key, a.E, slot);
       if (lane == 0) s_e = e;
     } else {
       wave_topk<NC>(a.logits + static_cast<size_t>(t) * a.E, a.sel_bias, a.E, a.k, a.router,

@@ -253,3 +253,78 @@ def test_decode_ties_outputs(E, router):
         ref = L.forward(x[t:t + 1])
         assert np.array_equal(idl.cpu().numpy()[0], ref["ids"][0]), t
         assert rel_err(y.cpu().numpy()[0], ref["y"][0]) <= Y_TOL, t
+
+
+def _tie_rows(W, rng, E, n_tied, base, per_group):
+    """Rows of n_tied experts made identical to row `base`; with per_group, at
+    least one of them in each group of 8 top-k lanes (expert e sits in lane
+    e % 64), so that every group maximum is the tied key."""
+    pool = [e for e in range(E) if e != base]
+    tied = set()
+    if per_group:
+        for g in range(8):
+            lanes = [e for e in pool if (e % 64) // 8 == g]
+            tied.add(int(rng.choice(lanes)))
+    rest = [e for e in pool if e not in tied]
+    tied |= {int(e) for e in rng.choice(rest, n_tied - 1 - len(tied), replace=False)}
+    for e in tied:
+        W[e] = W[base]
+    return sorted(tied | {base})
+
+
+@pytest.mark.parametrize("case", ["tied60", "tied70", "boundary", "spread"])
+def test_topk_candidate_threshold(case):
+    """The one-pass top-k ranks the keys that reach the smallest of 8 lane-group
+    maxima when there are at most 64 of them, and falls back to rounds
+    otherwise. Equal top keys just under and over 64 (every group holding one),
+    equal keys straddling rank k, and a tie group without a member in some
+    lane groups: ids through the routing entry point and the decode layer, and
+    the decode output against the oracle."""
+    from tests.gpu_common import Y_TOL, rel_err
+    E = 256
+    cfg = gen.CONFIGS["qwen3.6-35b-a3b"].with_(name="cand-" + case, E=E, k=8, H=512, F=256,
+                                               router=gen.SOFTMAX, norm_topk=1)
+    base = gen.make_layer(cfg, experts=[])
+    W = base.w_router
+    rng = np.random.default_rng(11)
+    b = 37
+    if case == "tied60":
+        tied = _tie_rows(W, rng, E, 60, b, True)
+    elif case == "tied70":
+        tied = _tie_rows(W, rng, E, 70, b, True)
+    elif case == "boundary":
+        tied = _tie_rows(W, rng, E, 12, b, False)
+        tops = [e for e in range(E) if e not in tied][::51][:5]
+        for i, e in enumerate(tops):          # five distinct keys above the tied ones
+            W[e] = W[b] * np.float32(1.5 + 0.1 * i)
+    else:                                    # tie group absent from some lane groups
+        tied = [b, 37 + 64, 37 + 128, 37 + 192, 40, 41]
+        for e in tied:
+            W[e] = W[b]
+    x = np.zeros((2, cfg.H), np.float32)
+    x[0] = W[b] / np.linalg.norm(W[b]) * 10
+    x[1] = W[b] / np.linalg.norm(W[b]) * 10 + rng.standard_normal(cfg.H).astype(np.float32) * 0.5
+    refs = [oracle.topk(oracle.router_logits(W, x[t]), cfg.k) for t in range(2)]
+    if case in ("tied60", "tied70"):
+        assert list(refs[0]) == tied[:8]
+    used = {int(e) for r in refs for e in r} | {cfg.E}
+    data = gen.make_layer(cfg, experts=sorted(used))
+    data.w_router = np.ascontiguousarray(W)
+    dl = DeviceLayer(data)
+    xt = torch.from_numpy(x).cuda()
+    ids, _, _ = _route(dl, xt, M.MOE_DTYPE_F32, 2, logits=False)
+    for t in range(2):
+        assert np.array_equal(ids[t], refs[t]), (case, "route", t, ids[t], refs[t])
+    L = oracle.Layer(data)
+    y = torch.empty((1, cfg.H), dtype=torch.float32, device="cuda")
+    idl = torch.empty((1, cfg.k), dtype=torch.int32, device="cuda")
+    wl = torch.empty((1, cfg.k), dtype=torch.float32, device="cuda")
+    ws = dl.workspace(1)
+    for t in range(2):
+        say(f"candidate top-k {case} token {t}")
+        M.moe_layer_forward(dl.desc, xt[t:t + 1].contiguous(), M.MOE_DTYPE_F32, 1, y, idl, wl,
+                            ws, ws.numel())
+        torch.cuda.synchronize()
+        ref = L.forward(x[t:t + 1])
+        assert np.array_equal(idl.cpu().numpy()[0], ref["ids"][0]), (case, t)
+        assert rel_err(y.cpu().numpy()[0], ref["y"][0]) <= Y_TOL, (case, t)
