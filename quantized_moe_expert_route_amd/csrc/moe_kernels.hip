@@ -618,6 +618,27 @@ __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
   }
 }
 
+// Row tile and token of a down workgroup (grid: row tiles x tokens). When
+// tokens of a chunk share an expert, the workgroups of one row tile read the
+// same rows. Workgroups go to the 8 XCDs round robin by linear id, so the
+// tokens of a row tile are given adjacent ids with one residue mod 8: they run
+// at the same time on one XCD, and a shared expert's rows come from HBM once
+// and from that XCD's L2 for the other tokens. One token: the identity.
+__device__ __forceinline__ void down_tile_token(int& x, int& t) {
+  const int gx = gridDim.x, T = gridDim.y;
+  const int lin = blockIdx.x + gx * blockIdx.y;
+  const int full = gx & ~7;  // row tiles in whole groups of 8
+  if (lin < full * T) {
+    const int rest = lin >> 3;
+    t = rest % T;
+    x = (rest / T) * 8 + (lin & 7);
+  } else {
+    const int r = lin - full * T, tail = gx - full;
+    t = r / tail;
+    x = full + (r - t * tail);
+  }
+}
+
 // ---------------------------------------------------------------- down GEMV
 // grid (ceil(H / R), T), block 512. For each present slot of token t (and the
 // shared expert): down rows [row0, row0 + R) against q8(h), then
@@ -632,7 +653,9 @@ __global__ __launch_bounds__(512) void k_down(KArgs a, int R, Div dnb, Div dR, D
   constexpr bool MX = FMT == FMT_MXFP4;
   constexpr int B = F::BE == 32 ? 32 : 256;  // q8 block of h
   extern __shared__ __align__(16) unsigned char smem[];
-  const int t = blockIdx.y, row0 = blockIdx.x * R;
+  int tile, t;
+  down_tile_token(tile, t);
+  const int row0 = tile * R;
   const int K = a.F, nb = K / F::BE;
   const int ns = a.k + a.has_shared;
   const int act_bytes = MX ? K * 5 / 2 : K;  // MXFP4: 80 bytes per 32-value block
@@ -848,7 +871,9 @@ __global__ __launch_bounds__(512) void k_down_lds(KArgs a, int R, Div dnb, Div d
                                                   Div dq) {
   using F = typename FmtOf<FMT>::T;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int t = blockIdx.y, row0 = blockIdx.x * R;
+  int tile, t;
+  down_tile_token(tile, t);
+  const int row0 = tile * R;
   const int K = a.F, nb = K / 256;
   const int ns = a.k + a.has_shared;
   // rows staged as whole 16-byte pieces (the last may run into the row's stride padding)
@@ -1004,7 +1029,9 @@ __host__ __device__ inline int mx_down_scratch_offset(int ns, int nb) {
 template <int RPW, int NL, int NBL>
 __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int t = blockIdx.y, row0 = blockIdx.x * R;
+  int tile, t;
+  down_tile_token(tile, t);
+  const int row0 = tile * R;
   const int K = a.F, nb = K / 32, npc = mx_row_pieces(nb);
   const int ns = a.k + a.has_shared;
   const int act_bytes = 80 * nb;
