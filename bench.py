@@ -71,10 +71,11 @@ def parse():
                    help="comma list of workloads: time each on both expert-FFN paths at "
                         "--crossover-tokens chunk sizes (reported under detail.crossover)")
     p.add_argument("--crossover-tokens", default="1,2,3,4,6,8,12,16")
-    p.add_argument("--layout", default="auto", choices=("auto", "rows", "tile64"),
-                   help="order of the expert blocks on the device: auto = 64-row tiles for "
-                        "layers that take the grouped path at every chunk size (an expert of "
-                        "8 MB or more), row order otherwise")
+    p.add_argument("--layout", default="auto", choices=("auto", "rows", "tile64", "mx16"),
+                   help="order of the expert blocks on the device: auto = MX16 rows for "
+                        "MXFP4 layers on the per-pair path, 64-row tiles for layers that take "
+                        "the grouped path at every chunk size (an expert of 8 MB or more), row "
+                        "order otherwise")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -165,8 +166,15 @@ def pick_layout(args, cfg) -> int:
         return 0
     tiles_ok = (cfg.fmt_gu == gen.Q4_K and cfg.fmt_d in (gen.Q4_K, gen.Q6_K) and not cfg.biases
                 and not cfg.act_quant)
+    # MX16: MXFP4 rows with aligned nibble fields, for the per-pair MXFP4 kernels
+    mx16_ok = (cfg.fmt_gu == gen.MXFP4 and cfg.fmt_d == gen.MXFP4 and not cfg.act_quant
+               and cfg.H <= 32 * 256 and cfg.F <= 32 * 256)
     if args.layout == "tile64":
         return 1 if tiles_ok else 0
+    if args.layout == "mx16":
+        return 2 if mx16_ok else 0
+    if mx16_ok:
+        return 2
     return 1 if tiles_ok and cfg.expert_algo_bytes >= 8e6 else 0
 
 
@@ -224,7 +232,7 @@ def run_workload(args, name: str, headline: bool, probes: dict, th: int):
     torch.cuda.synchronize()
     res = {"workload": cfg.description, "tokens_per_step": T, "layer_copies": copies,
            "x_pool": args.x_pool, "forwards_per_graph": G,
-           "expert_layout": "tile64" if cfg.layout else "rows"}
+           "expert_layout": ("rows", "tile64", "mx16")[cfg.layout]}
     if headline:
         # exactly K steps: whole rotations, then the first K mod G forwards of
         # one (their copies are the least recently used ones at that point)

@@ -64,6 +64,24 @@ def tile_pool(cfg, pool_rows: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def mx16_pool(cfg, pool_rows: torch.Tensor) -> torch.Tensor:
+    """The pool with every MXFP4 row (the shared expert's too) reordered by the
+    library into the MX16 order (moe_layout MX16): per row, the 16 nibble bytes
+    of every block, then the scale bytes; same row strides. Rows are repacked
+    one by one, so stacked and interleaved gate/up tensors alike."""
+    out = torch.zeros_like(pool_rows)
+    es = cfg.expert_bytes
+    s = torch.cuda.current_stream().cuda_stream
+    for e in range(cfg.n_pool):
+        base = e * es
+        for off, n, K, st in ((0, 2 * cfg.F, cfg.H, cfg.stride_gu),
+                              (2 * cfg.gate_bytes, cfg.H, cfg.F, cfg.stride_d)):
+            M.moe_repack_mx16(pool_rows.data_ptr() + base + off, st, n, K,
+                              out.data_ptr() + base + off, st, stream=s)
+    torch.cuda.synchronize()
+    return out
+
+
 class DeviceLayer:
     def __init__(self, data, copies: int = 1, present=None, route_scale=None, norm_topk=None,
                  use_shared: bool = True, sh_gate_vec=None, sel_bias="data", device="cuda",
@@ -75,7 +93,7 @@ class DeviceLayer:
         present = np.ones(E, bool) if present is None else np.asarray(present, bool)
         self.present = present
         self.layout = cfg.layout if layout is None else layout
-        if self.layout and interleaved:
+        if self.layout == M.MOE_LAYOUT_TILE64 and interleaved:
             raise ValueError("64-row tiles have their own order: no interleaved gate/up")
         # gate/up row r of an expert: interleaved at (2r, 2r + 1) of one fused
         # tensor, else stacked (gate matrix, then up matrix)
@@ -84,6 +102,8 @@ class DeviceLayer:
         pool0 = _dev(interleave_gate_up(data) if interleaved else data.pool, device)
         if self.layout == M.MOE_LAYOUT_TILE64:
             pool0 = tile_pool(cfg, pool0)
+        elif self.layout == M.MOE_LAYOUT_MX16:
+            pool0 = mx16_pool(cfg, pool0)
         self.pools = [pool0] + [pool0.clone() for _ in range(1, copies)]
         self.w_router = _dev(data.w_router, device)
         sb = data.sel_bias if isinstance(sel_bias, str) else sel_bias
@@ -135,7 +155,7 @@ class DeviceLayer:
             d.sh_gate_vec = None if self.sh_gate_vec is None else self.sh_gate_vec.data_ptr()
             d.path = path  # moe_path: 0 auto, 1 per-pair GEMV, 2 expert-grouped
             d.act_quant = getattr(cfg, "act_quant", 0)  # moe_actq: 0 q8, 1 MXFP8
-            d.layout = self.layout  # moe_layout: 0 rows, 1 64-row tiles
+            d.layout = self.layout  # moe_layout: 0 rows, 1 64-row tiles, 2 MX16 rows
             self._tables.append(keep)
             self.descs.append(d)
 

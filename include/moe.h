@@ -49,7 +49,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
@@ -121,8 +121,19 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_
  *    a block from each of 64 rows. Needs Q4_K gate and up, Q4_K or Q6_K down,
  *    no biases, Q8 activations and a path other than GEMV (MOE_EUNSUPPORTED
  *    otherwise); such layers take the grouped path at every T.
- *    moe_repack_tile64 converts a matrix from ROWS order. */
-typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILE64 = 1 } moe_layout;
+ *    moe_repack_tile64 converts a matrix from ROWS order.
+ *  MX16: MXFP4 rows with the fields of their 17-byte blocks regrouped: row r
+ *    at r * stride holds the 16 nibble bytes of block b at byte 16 b (the
+ *    block's bytes 1..16, unchanged) and, after all of them, the scale byte of
+ *    block b at byte 16 nb + b (nb = blocks per row); the scale run is read as
+ *    whole dwords, so strides must reach 16 nb + nb rounded up to 4. Every
+ *    field is aligned, so the per-pair GEMV kernels load each block straight
+ *    into registers instead of realigning 17-byte blocks. Needs MXFP4 gate, up
+ *    and down, Q8 activations, a path other than GROUPED, and widths the
+ *    per-pair MXFP4 kernels take (up to 256 blocks per row within their LDS
+ *    budget) (MOE_EUNSUPPORTED otherwise); such layers take the GEMV path at
+ *    every T. moe_repack_mx16 converts a matrix from ROWS order. */
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILE64 = 1, MOE_LAYOUT_MX16 = 2 } moe_layout;
 
 /* Quantized activations of T rows of width H, structure-of-arrays:
  *   qs    int8  [T, H]      q8 quants, |q| <= 127 (Q8_K, Q8_32); MXFP8: E4M3
@@ -311,6 +322,20 @@ MOE_API const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int 
 MOE_API moe_status moe_repack_tile64(moe_wfmt fmt, const void* src, size_t src_stride, int n_rows,
                                      int K, void* dst, hipStream_t stream);
 
+/* Reorders one MXFP4 matrix from ROWS to MX16 order (moe_layout): n_rows rows
+ * of K weights (K % 32 == 0), row r at src + r * src_stride (>= 17 K / 32),
+ * into rows at dst + r * dst_stride (dst_stride a multiple of 16 and at least
+ * 16 nb + nb rounded up to 4, nb = K / 32). Only the order of each block's
+ * bytes changes (nibble fields first, then the scale bytes); the bytes past
+ * the scale run up to the next multiple of 4 are written as zero, the rest of
+ * each dst row is not touched. src and dst 16-byte aligned and not
+ * overlapping (MOE_EINVAL otherwise); a failed launch gives MOE_EHIP. Enqueued
+ * on stream; the caller owns both buffers. Source: Pulsar README, formats
+ * paragraph (MXFP4 routed experts as stored quant blocks); the order of the
+ * fields in device memory is this library's choice. */
+MOE_API moe_status moe_repack_mx16(const void* src, size_t src_stride, int n_rows, int K, void* dst,
+                                   size_t dst_stride, hipStream_t stream);
+
 /* Test export: integer block partials of n_rows weight rows (device, K
  * columns, byte stride `stride`) against token `token` of xq, computed by the
  * same device routines the FFN kernels use (MXFP4 rows of up to 256 blocks:
@@ -327,6 +352,16 @@ MOE_API moe_status moe_repack_tile64(moe_wfmt fmt, const void* src, size_t src_s
  * integer dp4a dots, rescaled per quant block). */
 MOE_API moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,
                                const moe_qact* xq, int token, int32_t* out, hipStream_t stream);
+
+/* Test export: the same partials (S = 2 dot, 0) for MXFP4 rows in the MX16
+ * order (row stride >= 16 nb + nb rounded up to 4, a multiple of 16; K / 32 <=
+ * 256), through the loads and dots of the MX16 GEMV kernels. xq: Q8_32.
+ * Errors: MOE_EINVAL for a bad pointer, width, stride or token;
+ * MOE_EUNSUPPORTED past 256 blocks per row. Source: Pulsar README, numerics
+ * notes (integer dots rescaled per quant block). */
+MOE_API moe_status moe_test_block_dots_mx16(const void* rows, int n_rows, int K, size_t stride,
+                                            const moe_qact* xq, int token, int32_t* out,
+                                            hipStream_t stream);
 
 /* Test export: the integer super-block sums of the multi-token path's int8
  * MFMA tile kernels, computed by their production bodies (LDS ring, MFMA

@@ -29,7 +29,7 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = range(2)
 MOE_ROUTER_SOFTMAX, MOE_ROUTER_SIGMOID = range(2)
 MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = range(2)
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GROUPED = range(3)
-MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE64 = range(2)
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE64, MOE_LAYOUT_MX16 = range(3)
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
 
@@ -39,7 +39,7 @@ ABI_FUNCTIONS = (
     "moe_layer_stage_count", "moe_layer_stage_name", "moe_test_block_dots",
     "moe_test_tile_dots", "moe_test_tile_dots_ws", "moe_test_preact",
     "moe_layer_forward_noalloc", "moe_probe_read_wall", "moe_probe_mfma_i8",
-    "moe_probe_empty_chain", "moe_repack_tile64",
+    "moe_probe_empty_chain", "moe_repack_tile64", "moe_repack_mx16", "moe_test_block_dots_mx16",
     # expert pool (include/moe_pool.h)
     "moe_pool_create", "moe_pool_destroy", "moe_pool_host_slab", "moe_pool_layer_tables",
     "moe_pool_resolve", "moe_pool_prefetch", "moe_pool_get_stats", "moe_pool_policy_trace",
@@ -127,6 +127,8 @@ def lib():
         L.moe_layer_stage_name.restype = C.c_char_p
         L.moe_test_block_dots.argtypes = [i32, vp, i32, i32, sz, Q, i32, vp, vp]
         L.moe_repack_tile64.argtypes = [i32, vp, sz, i32, i32, vp, vp]
+        L.moe_repack_mx16.argtypes = [vp, sz, i32, i32, vp, sz, vp]
+        L.moe_test_block_dots_mx16.argtypes = [vp, i32, i32, sz, Q, i32, vp, vp]
         L.moe_test_tile_dots.argtypes = [i32, vp, i32, i32, sz, Q, i32, vp, vp, sz, vp]
         L.moe_test_tile_dots_ws.argtypes = [i32, i32, i32, i32]
         L.moe_test_tile_dots_ws.restype = sz
@@ -269,6 +271,19 @@ def moe_test_block_dots(fmt, rows, n_rows, K, stride, xq: MoeQact, token, out, s
     _check("moe_test_block_dots",
            lib().moe_test_block_dots(fmt, _ptr(rows), n_rows, K, stride, C.byref(xq), token,
                                      _ptr(out), _stream(stream)))
+
+
+def moe_test_block_dots_mx16(rows, n_rows, K, stride, xq: MoeQact, token, out, stream=None):
+    _check("moe_test_block_dots_mx16",
+           lib().moe_test_block_dots_mx16(_ptr(rows), n_rows, K, stride, C.byref(xq), token,
+                                          _ptr(out), _stream(stream)))
+
+
+def moe_repack_mx16(src, src_stride, n_rows, K, dst, dst_stride, stream=None):
+    """One MXFP4 matrix from row order into the MX16 order (moe_layout MX16)."""
+    _check("moe_repack_mx16",
+           lib().moe_repack_mx16(_ptr(src), src_stride, n_rows, K, _ptr(dst), dst_stride,
+                                 _stream(stream)))
 
 
 def moe_test_tile_dots(mode, rows, n_rows, K, stride, xq: MoeQact, n_tok, out, ws, ws_bytes,

@@ -41,6 +41,7 @@ size_t block_bytes(int fmt) {
 int act_fmt(int fmt) { return act32(fmt) ? MOE_AFMT_Q8_32 : MOE_AFMT_Q8_K; }
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+KArgs make_args(const moe_layer_desc* d, int T);
 
 moe_status validate_desc(const moe_layer_desc* d) {
   if (!d) return MOE_EINVAL;
@@ -54,7 +55,9 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_GEMV && d->path != MOE_PATH_GROUPED)
     return MOE_EINVAL;
   if (d->act_quant != MOE_ACTQ_Q8 && d->act_quant != MOE_ACTQ_MXFP8) return MOE_EINVAL;
-  if (d->layout != MOE_LAYOUT_ROWS && d->layout != MOE_LAYOUT_TILE64) return MOE_EINVAL;
+  if (d->layout != MOE_LAYOUT_ROWS && d->layout != MOE_LAYOUT_TILE64 &&
+      d->layout != MOE_LAYOUT_MX16)
+    return MOE_EINVAL;
   for (int f : {d->fmt_gate, d->fmt_up, d->fmt_down})
     if (!known_fmt(f)) return MOE_EINVAL;
   if (d->fmt_gate != d->fmt_up) return MOE_EUNSUPPORTED;
@@ -86,6 +89,17 @@ moe_status validate_desc(const moe_layer_desc* d) {
        (d->fmt_down != MOE_WFMT_Q4_K && d->fmt_down != MOE_WFMT_Q6_K) || d->b_gate || d->b_down ||
        d->act_quant != MOE_ACTQ_Q8 || d->path == MOE_PATH_GEMV))
     return MOE_EUNSUPPORTED;
+  // MX16 rows: read by the per-pair MXFP4 kernels only, whose row plans cover
+  // up to 256 blocks per row within the LDS budget
+  if (d->layout == MOE_LAYOUT_MX16) {
+    if (d->fmt_gate != MOE_WFMT_MXFP4 || d->fmt_down != MOE_WFMT_MXFP4 ||
+        d->act_quant != MOE_ACTQ_Q8 || d->path == MOE_PATH_GROUPED)
+      return MOE_EUNSUPPORTED;
+    if (!mx16_fits(make_args(d, 1))) return MOE_EUNSUPPORTED;
+    if (d->stride_gate < mx16_row_bytes(H / 32) || d->stride_up < mx16_row_bytes(H / 32) ||
+        d->stride_down < mx16_row_bytes(F / 32))
+      return MOE_EINVAL;
+  }
   return MOE_OK;
 }
 
@@ -113,6 +127,7 @@ KArgs make_args(const moe_layer_desc* d, int T) {
   a.has_shared = d->sh_gate != nullptr;
   a.mx8 = d->act_quant == MOE_ACTQ_MXFP8;
   a.tiled = d->layout == MOE_LAYOUT_TILE64;
+  a.mx16 = d->layout == MOE_LAYOUT_MX16;
   return a;
 }
 
@@ -347,7 +362,7 @@ static moe_status expert_ffn_impl(KArgs& a, bool grouped, bool routing_given, hi
     if (e == hipSuccess) e = launch_combine(a, stream, st.next());
   } else {
     e = launch_gateup(a, routing_given, stream, st.next());
-    if (e == hipSuccess && gemv_hquant(a.fmt_d, a.F, a.k, a.has_shared)) e = launch_hquant_pairs(a, stream, st.next());
+    if (e == hipSuccess && gemv_hquant(a.fmt_d, a.F, a.k, a.has_shared, a.mx16)) e = launch_hquant_pairs(a, stream, st.next());
     if (e == hipSuccess) e = launch_down(a, stream, st.next());
   }
   return hip_status(e);
@@ -501,7 +516,8 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* x, mo
 int moe_layer_stage_count(const moe_layer_desc* desc, int T) {
   if (validate_desc(desc) != MOE_OK || T <= 0 || T > kMaxTokens) return 0;
   if (use_grouped(desc, T)) return 7;
-  return gemv_hquant(desc->fmt_down, desc->ffn, desc->top_k, desc->sh_gate != nullptr) ? 4 : 3;
+  return gemv_hquant(desc->fmt_down, desc->ffn, desc->top_k, desc->sh_gate != nullptr,
+                     desc->layout == MOE_LAYOUT_MX16) ? 4 : 3;
 }
 
 const char* moe_layer_stage_name(const moe_layer_desc* desc, int T, int stage) {
@@ -528,6 +544,36 @@ moe_status moe_repack_tile64(moe_wfmt fmt, const void* src, size_t src_stride, i
   if (s0 < d1 && d0 < s1) return MOE_EINVAL;  // overlapping buffers
   return hip_status(launch_repack_tile64(static_cast<const uint8_t*>(src), src_stride, n_rows, nb,
                                          static_cast<int>(BB), static_cast<uint8_t*>(dst), stream));
+}
+
+moe_status moe_repack_mx16(const void* src, size_t src_stride, int n_rows, int K, void* dst,
+                           size_t dst_stride, hipStream_t stream) {
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return MOE_EINVAL;
+  if (n_rows <= 0 || K <= 0 || K % 32) return MOE_EINVAL;
+  const int nb = K / 32;
+  if (src_stride < 17 * static_cast<size_t>(nb)) return MOE_EINVAL;
+  if (dst_stride < mx16_row_bytes(nb) || dst_stride % 16) return MOE_EINVAL;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t s1 = s0 + (static_cast<size_t>(n_rows) - 1) * src_stride + 17 * static_cast<size_t>(nb);
+  const uintptr_t d1 = d0 + (static_cast<size_t>(n_rows) - 1) * dst_stride + mx16_row_bytes(nb);
+  if (s0 < d1 && d0 < s1) return MOE_EINVAL;  // overlapping buffers
+  return hip_status(launch_repack_mx16(static_cast<const uint8_t*>(src), src_stride, n_rows, nb,
+                                       static_cast<uint8_t*>(dst), dst_stride, stream));
+}
+
+moe_status moe_test_block_dots_mx16(const void* rows, int n_rows, int K, size_t stride,
+                                    const moe_qact* xq, int token, int32_t* out,
+                                    hipStream_t stream) {
+  if (!rows || !aligned(rows, 16) || !out || !xq || n_rows < 0 || K <= 0 || K % 32) return MOE_EINVAL;
+  if (K / 32 > 256) return MOE_EUNSUPPORTED;
+  if (stride < mx16_row_bytes(K / 32) || stride % 16) return MOE_EINVAL;
+  if (xq->fmt != MOE_AFMT_Q8_32 || xq->H != K || token < 0 || token >= xq->T) return MOE_EINVAL;
+  if (!xq->qs || !xq->d) return MOE_EINVAL;
+  if (n_rows == 0) return MOE_OK;
+  return hip_status(launch_block_dots_mx16(rows, n_rows, K, stride,
+                                           xq->qs + static_cast<size_t>(token) * K,
+                                           xq->d + static_cast<size_t>(token) * (K / 32), out,
+                                           stream));
 }
 
 moe_status moe_test_block_dots(moe_wfmt fmt, const void* rows, int n_rows, int K, size_t stride,

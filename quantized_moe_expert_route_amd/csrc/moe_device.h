@@ -921,9 +921,109 @@ __device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, i
                                           const MxAct<NBL>& A, int lane) {
   float s0 = 0.0f, s1 = 0.0f;
   mx_pair_blocks<NL, NBL>(pc, scr, nb, A, lane, [&](int row, int, int i, float dot, int e) {
-    const float v = A.d[i] * __builtin_ldexpf(dot, e - 127);
+    float v = A.d[i] * __builtin_ldexpf(dot, e - 127);
+    // the product is rounded on its own, never fused into the sum below, so
+    // that every row layout (and every unrolled form) rounds the same way
+    asm volatile("" : "+v"(v));
     // selects, not a branch: with a per-lane row (folded tail blocks) a branch
     // made the compiler keep {s0, s1} in scratch memory
+    const bool r0 = row == 0;
+    s0 += r0 ? v : 0.0f;
+    s1 += r0 ? 0.0f : v;
+  });
+  return make_float2(wave_sum(s0), wave_sum(s1));
+}
+
+// ------------------------------------------ MXFP4 rows in the MX16 order
+// A row of nb blocks stored in the MX16 order (moe_layout MX16): the 16 nibble
+// bytes of block b at byte 16 b, the scale bytes of all blocks after them
+// (block b's at byte 16 nb + b). Every field is aligned, so a lane loads each
+// block it owns as one 16-byte piece straight into registers, and its scale
+// byte from the dword that holds it: no realignment through LDS.
+//
+// The blocks of a row pair that a lane owns, slot j < NS, are those of
+// mx_pair_blocks in the same order (for activation block i, row 0 then row 1);
+// NS = 3 for rows of 65..96 blocks (block lane of both rows, then one folded
+// tail block), 2 NBL otherwise.
+struct Mx16Slot {
+  int row, b, i;
+  bool ok;
+};
+template <int NS>
+__device__ __forceinline__ Mx16Slot mx16_slot(int j, int nb, int lane) {
+  if constexpr (NS == 3) {
+    if (j < 2) return Mx16Slot{j, lane, 0, true};
+    const int tail = nb - 64, row = lane < tail ? 0 : 1;
+    return Mx16Slot{row, 64 + lane - row * tail, 1, lane < 2 * tail};
+  }
+  const int b = lane + 64 * (j >> 1);
+  return Mx16Slot{j & 1, b, j >> 1, b < nb};
+}
+
+template <int NS>
+struct Mx16Unit {
+  uint4 q[NS];
+  uint32_t s[NS];
+};
+
+// The loads of one row pair: rows r0 and r1 (ok0 / ok1: the row exists);
+// absent blocks read the dummy line.
+template <int NS>
+__device__ __forceinline__ void mx16_issue(Mx16Unit<NS>& u, const uint8_t* r0, const uint8_t* r1,
+                                           bool ok0, bool ok1, int nb, int lane,
+                                           const uint8_t* dummy) {
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const Mx16Slot sl = mx16_slot<NS>(j, nb, lane);
+    const bool v = sl.ok && (sl.row ? ok1 : ok0);
+    const uint8_t* rb = sl.row ? r1 : r0;
+    u.q[j] = ld_nt16(v ? rb + 16 * sl.b : dummy);
+    u.s[j] = ld_nt4(v ? rb + 16 * nb + (sl.b & ~3) : dummy);
+  }
+}
+
+// Dot of one block's 16 nibble bytes with its 16 activation pairs: the
+// operations of mx_dot_regs on the same bytes, so the same exact value.
+__device__ __forceinline__ float mx16_dot(const uint4& q, const half2_t (&ap)[16]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0),
+                                 ap[4 * i], acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1),
+                                 ap[4 * i + 1], acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2),
+                                 ap[4 * i + 2], acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3),
+                                 ap[4 * i + 3], acc, false);
+  }
+  return acc;
+}
+
+// f(row, b, i, dot, e) for every block the lane owns, in slot order.
+template <int NS, int NBL, class Fn>
+__device__ __forceinline__ void mx16_pair_blocks(const Mx16Unit<NS>& u, const MxAct<NBL>& A,
+                                                 int nb, int lane, Fn&& f) {
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const Mx16Slot sl = mx16_slot<NS>(j, nb, lane);
+    if (sl.ok) {
+      const int e = static_cast<int>((u.s[j] >> (8 * (sl.b & 3))) & 0xFFu);
+      f(sl.row, sl.b, sl.i, mx16_dot(u.q[j], A.ap[sl.i]), e);
+    }
+  }
+}
+
+// The two row sums of a row pair, summed as mx_pair sums them (products and
+// sums rounded one by one in both).
+template <int NS, int NBL>
+__device__ __forceinline__ float2 mx16_pair(const Mx16Unit<NS>& u, const MxAct<NBL>& A, int nb,
+                                            int lane) {
+  float s0 = 0.0f, s1 = 0.0f;
+  mx16_pair_blocks<NS, NBL>(u, A, nb, lane, [&](int row, int, int i, float dot, int e) {
+    float v = A.d[i] * __builtin_ldexpf(dot, e - 127);
+    asm volatile("" : "+v"(v));  // rounded on its own, as in mx_pair
     const bool r0 = row == 0;
     s0 += r0 ? v : 0.0f;
     s1 += r0 ? 0.0f : v;

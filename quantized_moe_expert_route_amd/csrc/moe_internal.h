@@ -123,6 +123,9 @@ struct KArgs {
   // expert matrices in 64-row tiles, super-block-major inside a tile (block b
   // of row r at ((r / 64) nb + b) 64 BB + (r % 64) BB); strides unused
   int tiled;
+  // MXFP4 rows in the MX16 order (nibble fields of all blocks, then the scale
+  // bytes): read by the MX16 variants of k_gateup_mx and k_down_mx
+  int mx16;
 };
 
 // Workspace layout (byte offsets from the base, each 256-aligned).
@@ -141,10 +144,21 @@ constexpr int kMaxTokens = 2048;
 
 // Whether the GEMV kernels' LDS needs fit for this layer and chunk.
 bool gemv_fits(const KArgs& a);
-// GEMV path: whether the down projection needs h quantized by its own kernel
-// first (an MXFP4 down too large for the fused kernel). Otherwise every down
-// workgroup quantizes h itself, overlapped with its row stream.
-bool gemv_hquant(int fmt_down, int F, int k, int has_shared);
+// GEMV path: whether the down projection takes h quantized once per pair by a
+// kernel of its own (an MXFP4 down too large for the fused kernel, or MX16
+// rows). Otherwise every down workgroup quantizes h itself, overlapped with
+// its row stream.
+bool gemv_hquant(int fmt_down, int F, int k, int has_shared, bool mx16);
+
+// Whether the per-pair MXFP4 kernels (k_gateup_mx, k_down_mx) take this
+// layer's gate/up and down rows: the widths their row plans cover, within the
+// LDS budget. MX16 layers need both.
+bool mx16_fits(const KArgs& a);
+// Bytes an MXFP4 row of nb blocks spans in the MX16 order: the nibble fields,
+// then the scale bytes, read as whole dwords.
+__host__ __device__ inline size_t mx16_row_bytes(int nb) {
+  return 16 * static_cast<size_t>(nb) + ((static_cast<size_t>(nb) + 3) & ~static_cast<size_t>(3));
+}
 
 // Which expert-FFN path a chunk of T tokens takes (fixed rule, see moe_api.cpp).
 bool use_grouped(const moe_layer_desc* d, int T);
@@ -182,6 +196,10 @@ hipError_t launch_bucket(const KArgs& a, hipStream_t s, Ev ev);
 // order into 64-row tiles.
 hipError_t launch_repack_tile64(const uint8_t* src, size_t stride, int n_rows, int nb, int BB,
                                 uint8_t* dst, hipStream_t s);
+// One MXFP4 matrix (n_rows of nb 17-byte blocks, row stride `stride`) into the
+// MX16 order at dst (row stride dst_stride).
+hipError_t launch_repack_mx16(const uint8_t* src, size_t stride, int n_rows, int nb, uint8_t* dst,
+                              size_t dst_stride, hipStream_t s);
 hipError_t launch_gateup_grouped(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_hquant(const KArgs& a, hipStream_t s, Ev ev);
 hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev);
@@ -198,6 +216,9 @@ hipError_t launch_down_mx(const KArgs& a, int max_tiles, hipStream_t s, Ev ev);
 hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_t stride,
                              const int8_t* qs, const float* d, const int16_t* bs,
                              int32_t* out, hipStream_t s);
+// The same for MXFP4 rows in the MX16 order, through the MX16 kernels' routine.
+hipError_t launch_block_dots_mx16(const void* rows, int n_rows, int K, size_t stride,
+                                  const int8_t* qs, const float* d, int32_t* out, hipStream_t s);
 // Test export: one token tile (n_tok <= 16 activation rows) through the grouped
 // path's LDS-ring tile kernel of `mode` (0: Q4_K gate/up body, 1: Q4_K down
 // body, 2: Q6_K down body), dumping the int32 super-block sums. ws >= tile_dots_ws().

@@ -15,6 +15,8 @@
 // chip fences and same-address atomics cost more than a launch.
 // plus k_quant (moe_quantize_act_q8k), k_topk (moe_route_topk) and the
 // block-dot export. No float atomics; every reduction has a fixed order.
+#include <algorithm>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -441,7 +443,9 @@ __global__ __launch_bounds__(256) void k_hquant_pairs(KArgs a, int P, Div dpc) {
 // gate/up pointers.
 __host__ __device__ inline int mx_gu_scratch_offset(int nb) { return (84 * nb + 15) & ~15; }
 
-template <int RPW, int NL, int NBL, int NC>
+// NS = 0: rows of 17-byte blocks (realigned through LDS); NS > 0: rows in the
+// MX16 order, NS blocks per lane and row pair straight into registers.
+template <int RPW, int NL, int NBL, int NC, int NS>
 __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_e;
@@ -461,11 +465,18 @@ __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
   const uint8_t* gbase = nullptr;
   const uint8_t* ubase = nullptr;
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.counters);
-  uint4 pcs[RPW][NL];
+  uint4 pcs[RPW][NS ? 1 : NL];
+  Mx16Unit<NS ? NS : 1> u16[NS ? RPW : 1];
   auto issue = [&]() {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int r = row0 + wave + 4 * i;
+      if constexpr (NS > 0) {
+        const bool ok = r < a.F;
+        mx16_issue<NS>(u16[i], gbase + static_cast<size_t>(r) * a.stride_gate,
+                       ubase + static_cast<size_t>(r) * a.stride_up, ok, ok, nb, lane, dummy);
+        continue;
+      }
 #pragma unroll
       for (int m = 0; m < NL; ++m) {
         const int j = lane + 64 * m;
@@ -602,7 +613,9 @@ __global__ __launch_bounds__(256) void k_gateup_mx(KArgs a, int routing_given) {
   for (int i = 0; i < RPW; ++i) {
     const int r = row0 + wave + 4 * i;
     if (r < a.F) {
-      const float2 gu = mx_pair<NL, NBL>(pcs[i], scr, nb, A, lane);
+      float2 gu;
+      if constexpr (NS > 0) gu = mx16_pair<NS, NBL>(u16[i], A, nb, lane);
+      else gu = mx_pair<NL, NBL>(pcs[i], scr, nb, A, lane);
       if (lane == 0) {
         float g = gu.x, u = gu.y;
         if (bg) { g += bg[r]; u += bu[r]; }
@@ -1026,7 +1039,8 @@ __host__ __device__ inline int mx_down_scratch_offset(int ns, int nb) {
   return (84 * ns * nb + 15) & ~15;
 }
 
-template <int RPW, int NL, int NBL>
+// NS as in k_gateup_mx.
+template <int RPW, int NL, int NBL, int NS>
 __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
   extern __shared__ __align__(16) unsigned char smem[];
   int tile, t;
@@ -1039,7 +1053,8 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
   float* ld = reinterpret_cast<float*>(smem + ns * act_bytes);
   const int scr_bytes = mx_scratch_bytes(nb);
   uint8_t* scr = smem + mx_down_scratch_offset(ns, nb) + (threadIdx.x >> 6) * scr_bytes;
-  float* part = reinterpret_cast<float*>(smem + mx_down_scratch_offset(ns, nb) + 8 * scr_bytes);
+  // [R][ns] slot outputs (MX16 rows: the only LDS the kernel uses)
+  float* part = reinterpret_cast<float*>(NS ? smem : smem + mx_down_scratch_offset(ns, nb) + 8 * scr_bytes);
   __shared__ const uint8_t* dptr[17];
   __shared__ const float* dbias[17];
   __shared__ float wslot[17];
@@ -1063,7 +1078,8 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
       __builtin_amdgcn_ballot_w64(lane < ns && dptr[min(lane, ns - 1)] != nullptr));
   const int nrp = (R + 1) / 2, units = ns * nrp, upw = (units + 7) / 8;
   const int u0 = wave * upw, u1 = min(u0 + upw, units);
-  uint4 pcs[RPW][NL];
+  uint4 pcs[RPW][NS ? 1 : NL];
+  Mx16Unit<NS ? NS : 1> u16[NS ? RPW : 1];
   auto issue = [&](int ub) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -1071,6 +1087,13 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
       const int s = u < u1 ? u / nrp : 0;
       const int r = row0 + 2 * (u - s * nrp);
       const uint8_t* base = (u < u1 && ((present >> s) & 1u)) ? dptr[s] : nullptr;
+      if constexpr (NS > 0) {
+        const uint8_t* rb = base ? base : dummy;
+        mx16_issue<NS>(u16[i], rb + static_cast<size_t>(r) * a.stride_down,
+                       rb + static_cast<size_t>(r + 1) * a.stride_down, base && r < a.H,
+                       base && r + 1 < a.H, nb, lane, dummy);
+        continue;
+      }
 #pragma unroll
       for (int m = 0; m < NL; ++m) {
         const int j = lane + 64 * m;
@@ -1084,9 +1107,25 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
     }
   };
   const int pieces = (K + 255) / 256, njobs = ns * pieces;
-  float4 hv[kMxDownJobs];
+  MxAct<NBL> A;
+  int cur = -1;  // slot whose activations A holds (wave-uniform)
+  // MX16 rows (NS > 0): h was quantized once per pair by k_hquant_pairs into
+  // this kernel's LDS image in the workspace, and each lane reads its
+  // activation blocks from there (L2). Those of the wave's first slot are
+  // loaded before the rows, so they arrive first.
+  auto act_of = [&](int s) {
+    const int ps = s < a.k ? t * a.k + s : a.T * a.k + t;
+    mx_act_load(A, reinterpret_cast<const half2_t*>(a.hqs) + static_cast<size_t>(ps) * nb * kApPitch,
+                a.hd + static_cast<size_t>(ps) * nb, nb, lane);
+    cur = s;
+  };
+  if constexpr (NS > 0) {
+    if (u0 < u1) act_of(u0 / nrp);
+    issue(u0);
+  }
+  float4 hv[NS ? 1 : kMxDownJobs];
 #pragma unroll
-  for (int u = 0; u < kMxDownJobs; ++u) {
+  for (int u = 0; u < (NS ? 0 : kMxDownJobs); ++u) {
     const int job = wave + 8 * u;  // wave-uniform
     hv[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (job < njobs) {
@@ -1095,9 +1134,9 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
       if (e0 < K) hv[u] = *reinterpret_cast<const float4*>(a.h + static_cast<size_t>(ps) * K + e0);
     }
   }
-  issue(u0);
+  if constexpr (NS == 0) issue(u0);
 #pragma unroll
-  for (int u = 0; u < kMxDownJobs; ++u) {
+  for (int u = 0; u < (NS ? 0 : kMxDownJobs); ++u) {
     const int job = wave + 8 * u;
     if (job < njobs) {
       const int s = job / pieces, pc = job - s * pieces;
@@ -1109,9 +1148,7 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
       }
     }
   }
-  __syncthreads();
-  MxAct<NBL> A;
-  int cur = -1;  // slot whose activations A holds (wave-uniform)
+  if constexpr (NS == 0) __syncthreads();
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int u = u0 + i;
@@ -1119,11 +1156,17 @@ __global__ __launch_bounds__(512) void k_down_mx(KArgs a, int R) {
       const int s = u / nrp, rp = u - s * nrp, r = row0 + 2 * rp;
       if (((present >> s) & 1u) && r < a.H) {
         if (s != cur) {
-          mx_act_load(A, reinterpret_cast<const half2_t*>(p_act + s * act_bytes), ld + s * nb,
-                      nb, lane);
-          cur = s;
+          if constexpr (NS > 0) {
+            act_of(s);
+          } else {
+            mx_act_load(A, reinterpret_cast<const half2_t*>(p_act + s * act_bytes), ld + s * nb,
+                        nb, lane);
+            cur = s;
+          }
         }
-        const float2 o = mx_pair<NL, NBL>(pcs[i], scr, nb, A, lane);
+        float2 o;
+        if constexpr (NS > 0) o = mx16_pair<NS, NBL>(u16[i], A, nb, lane);
+        else o = mx_pair<NL, NBL>(pcs[i], scr, nb, A, lane);
         if (lane == 0) {
           const float* bias = dbias[s];
           part[(2 * rp) * ns + s] = wslot[s] * (o.x + (bias ? bias[r] : 0.0f));
@@ -1210,6 +1253,54 @@ __global__ __launch_bounds__(64) void k_block_dots_mx(const uint8_t* rows, int n
       out[(static_cast<size_t>(r) * nb + b) * 2 + 1] = 0;
     }
   });
+}
+
+// The same export for MXFP4 rows in the MX16 order, through the MX16 kernels'
+// loads and dots (mx16_issue, mx16_pair_blocks). grid ceil(n_rows / 2), block
+// 64; LDS: activation pairs [nb][kApPitch], scales [nb].
+template <int NS, int NBL>
+__global__ __launch_bounds__(64) void k_block_dots_mx16(const uint8_t* rows, int n_rows, int K,
+                                                        size_t stride, const int8_t* qs,
+                                                        const float* d, int32_t* out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nb = K / 32, lane = threadIdx.x;
+  half2_t* lap = reinterpret_cast<half2_t*>(smem);
+  float* ld = reinterpret_cast<float*>(smem + 80 * nb);
+  stage_act<ACT_PAIRS>(qs, d, nullptr, K, nullptr, ld, nullptr, lap);
+  __syncthreads();
+  const int r0 = 2 * blockIdx.x;
+  Mx16Unit<NS> u;
+  mx16_issue<NS>(u, rows + static_cast<size_t>(r0) * stride,
+                 rows + static_cast<size_t>(min(r0 + 1, n_rows - 1)) * stride, true,
+                 r0 + 1 < n_rows, nb, lane, rows);
+  MxAct<NBL> A;
+  mx_act_load(A, lap, ld, nb, lane);
+  mx16_pair_blocks<NS, NBL>(u, A, nb, lane, [&](int row, int b, int, float dot, int) {
+    const int r = r0 + row;
+    if (r < n_rows) {
+      out[(static_cast<size_t>(r) * nb + b) * 2] = static_cast<int>(2.0f * dot);
+      out[(static_cast<size_t>(r) * nb + b) * 2 + 1] = 0;
+    }
+  });
+}
+
+// One MXFP4 matrix from rows of 17-byte blocks into the MX16 order, one output
+// byte per thread (row r, byte o < mx16_row_bytes(nb)): the nibble fields,
+// then the scale bytes, then zeros up to the next dword.
+__global__ __launch_bounds__(256) void k_repack_mx16(const uint8_t* src, size_t stride, int nb,
+                                                     uint8_t* dst, size_t dst_stride, int rb,
+                                                     size_t total) {
+  const size_t n_thr = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += n_thr) {
+    const size_t r = i / rb;
+    const int o = static_cast<int>(i - r * rb);
+    const uint8_t* row = src + r * stride;
+    uint8_t v = 0;
+    if (o < 16 * nb) v = row[17 * (o >> 4) + 1 + (o & 15)];
+    else if (o < 17 * nb) v = row[17 * (o - 16 * nb)];
+    dst[r * dst_stride + o] = v;
+  }
 }
 
 // Calls f(std::integral_constant<int, FMT>) for a format enum (nothing for
@@ -1342,49 +1433,72 @@ bool mx_down_fits(const KArgs& a) {
          ns * ((a.F + 255) / 256) <= 8 * kMxDownJobs;
 }
 
-template <int RPW, int NL, int NBL>
+template <int RPW, int NL, int NBL, int NS>
 hipError_t gateup_mx_launch(const KArgs& a, int routing_given, hipStream_t s, Ev ev) {
   const int P = a.T * a.k + a.T * a.has_shared;
   const dim3 grid((a.F + 4 * RPW - 1) / (4 * RPW), P);
   const size_t lds = mx_gateup_lds(a);
   if (a.E <= 256)
-    return launch(k_gateup_mx<RPW, NL, NBL, 4>, grid, 256, lds, s, ev, a, routing_given);
-  return launch(k_gateup_mx<RPW, NL, NBL, 16>, grid, 256, lds, s, ev, a, routing_given);
+    return launch(k_gateup_mx<RPW, NL, NBL, 4, NS>, grid, 256, lds, s, ev, a, routing_given);
+  return launch(k_gateup_mx<RPW, NL, NBL, 16, NS>, grid, 256, lds, s, ev, a, routing_given);
 }
 
-hipError_t gateup_mx(const KArgs& a, int routing_given, hipStream_t s, Ev ev) {
+// Blocks per lane and row pair of the MX16 kernels for rows of nb blocks.
+int mx16_ns(int nb) { return nb <= 64 ? 2 : nb <= 96 ? 3 : nb <= 128 ? 4 : 8; }
+
+// Calls f(RPW, NL, NBL, NS) as integral constants for the plan of rows of K
+// weights (NS = 0: 17-byte rows; else the MX16 slots).
+template <class Fn>
+hipError_t with_mx_plan(int K, bool mx16, Fn&& f) {
+  using std::integral_constant;
   MxPlan pl;
-  mx_plan(a.H, &pl);
+  mx_plan(K, &pl);
+  const int ns = mx16 ? mx16_ns(K / 32) : 0;
+  auto go = [&](auto rpw, auto nl, auto nbl) -> hipError_t {
+    constexpr int NBL = decltype(nbl)::value;
+    switch (ns) {
+      case 0: return f(rpw, nl, nbl, integral_constant<int, 0>{});
+      case 2: if constexpr (NBL == 1) return f(rpw, nl, nbl, integral_constant<int, 2>{}); break;
+      case 3: if constexpr (NBL == 2) return f(rpw, nl, nbl, integral_constant<int, 3>{}); break;
+      case 4: if constexpr (NBL == 2) return f(rpw, nl, nbl, integral_constant<int, 4>{}); break;
+      case 8: if constexpr (NBL == 4) return f(rpw, nl, nbl, integral_constant<int, 8>{}); break;
+    }
+    return hipErrorInvalidValue;
+  };
   switch (pl.nl) {
-    case 1: return gateup_mx_launch<3, 1, 1>(a, routing_given, s, ev);
-    case 2: return gateup_mx_launch<3, 2, 1>(a, routing_given, s, ev);
+    case 1: return go(integral_constant<int, 3>{}, integral_constant<int, 1>{}, integral_constant<int, 1>{});
+    case 2: return go(integral_constant<int, 3>{}, integral_constant<int, 2>{}, integral_constant<int, 1>{});
     case 3:
-      if (pl.nbl == 1) return gateup_mx_launch<3, 3, 1>(a, routing_given, s, ev);
-      return gateup_mx_launch<3, 3, 2>(a, routing_given, s, ev);
-    case 5: return gateup_mx_launch<1, 5, 2>(a, routing_given, s, ev);
-    default: return gateup_mx_launch<1, 9, 4>(a, routing_given, s, ev);
+      if (pl.nbl == 1)
+        return go(integral_constant<int, 3>{}, integral_constant<int, 3>{}, integral_constant<int, 1>{});
+      return go(integral_constant<int, 3>{}, integral_constant<int, 3>{}, integral_constant<int, 2>{});
+    case 5: return go(integral_constant<int, 1>{}, integral_constant<int, 5>{}, integral_constant<int, 2>{});
+    default: return go(integral_constant<int, 1>{}, integral_constant<int, 9>{}, integral_constant<int, 4>{});
   }
 }
 
-template <int RPW, int NL, int NBL>
+hipError_t gateup_mx(const KArgs& a, int routing_given, hipStream_t s, Ev ev) {
+  return with_mx_plan(a.H, a.mx16, [&](auto rpw, auto nl, auto nbl, auto ns) {
+    return gateup_mx_launch<decltype(rpw)::value, decltype(nl)::value, decltype(nbl)::value,
+                            decltype(ns)::value>(a, routing_given, s, ev);
+  });
+}
+
+template <int RPW, int NL, int NBL, int NS>
 hipError_t down_mx_launch(const KArgs& a, const MxPlan& pl, hipStream_t s, Ev ev) {
   const int R = mx_down_rows(a, pl);
   const dim3 grid((a.H + R - 1) / R, a.T);
-  return launch(k_down_mx<RPW, NL, NBL>, grid, 512, mx_down_lds(a, pl), s, ev, a, R);
+  const size_t lds = NS ? 4 * static_cast<size_t>(R) * (a.k + a.has_shared) : mx_down_lds(a, pl);
+  return launch(k_down_mx<RPW, NL, NBL, NS>, grid, 512, lds, s, ev, a, R);
 }
 
 hipError_t down_mx(const KArgs& a, hipStream_t s, Ev ev) {
   MxPlan pl;
   mx_plan(a.F, &pl);
-  switch (pl.nl) {
-    case 1: return down_mx_launch<3, 1, 1>(a, pl, s, ev);
-    case 2: return down_mx_launch<3, 2, 1>(a, pl, s, ev);
-    case 3:
-      if (pl.nbl == 1) return down_mx_launch<3, 3, 1>(a, pl, s, ev);
-      return down_mx_launch<3, 3, 2>(a, pl, s, ev);
-    case 5: return down_mx_launch<1, 5, 2>(a, pl, s, ev);
-    default: return down_mx_launch<1, 9, 4>(a, pl, s, ev);
-  }
+  return with_mx_plan(a.F, a.mx16, [&](auto rpw, auto nl, auto nbl, auto ns) {
+    return down_mx_launch<decltype(rpw)::value, decltype(nl)::value, decltype(nbl)::value,
+                          decltype(ns)::value>(a, pl, s, ev);
+  });
 }
 
 // Candidates per lane of the in-kernel top-k: 4 covers E <= 256.
@@ -1471,8 +1585,9 @@ hipError_t down_dispatch(const KArgs& a, hipStream_t s, Ev ev) {
 
 }  // namespace
 
-bool gemv_hquant(int fmt_down, int F, int k, int has_shared) {
+bool gemv_hquant(int fmt_down, int F, int k, int has_shared, bool mx16) {
   if (fmt_down != FMT_MXFP4) return false;
+  if (mx16) return true;
   KArgs a{};
   a.fmt_d = fmt_down;
   a.F = F;
@@ -1480,6 +1595,8 @@ bool gemv_hquant(int fmt_down, int F, int k, int has_shared) {
   a.has_shared = has_shared;
   return !mx_down_fits(a);
 }
+
+bool mx16_fits(const KArgs& a) { return mx_gateup_fits(a) && mx_down_fits(a); }
 
 bool gemv_fits(const KArgs& a) {
   GemvShape gs{1, 1}, ds{1, 1};
@@ -1590,6 +1707,28 @@ hipError_t launch_block_dots(int fmt, const void* rows, int n_rows, int K, size_
                d, bs, out);
   });
   return e;
+}
+
+hipError_t launch_block_dots_mx16(const void* rows, int n_rows, int K, size_t stride,
+                                  const int8_t* qs, const float* d, int32_t* out, hipStream_t s) {
+  const uint8_t* r = static_cast<const uint8_t*>(rows);
+  const size_t lds = static_cast<size_t>(84) * (K / 32);
+  return with_mx_plan(K, true, [&](auto, auto, auto nbl, auto ns) -> hipError_t {
+    constexpr int NS = decltype(ns)::value, NBL = decltype(nbl)::value;
+    if constexpr (NS == 0) return hipErrorInvalidValue;
+    else
+      return launch(k_block_dots_mx16<NS, NBL>, dim3((n_rows + 1) / 2), 64, lds, s, Ev{}, r,
+                    n_rows, K, stride, qs, d, out);
+  });
+}
+
+hipError_t launch_repack_mx16(const uint8_t* src, size_t stride, int n_rows, int nb, uint8_t* dst,
+                              size_t dst_stride, hipStream_t s) {
+  const int rb = static_cast<int>(mx16_row_bytes(nb));
+  const size_t total = static_cast<size_t>(n_rows) * rb;
+  const size_t grid = std::min<size_t>((total + 255) / 256, 65536);
+  return launch(k_repack_mx16, dim3(static_cast<unsigned>(grid)), 256, 0, s, Ev{}, src, stride, nb,
+                dst, dst_stride, rb, total);
 }
 
 }  // namespace moe

@@ -35,7 +35,7 @@ def test_library_exports_header_symbols():
 
 
 def test_version_and_status_strings():
-    assert M.moe_abi_version() == 4
+    assert M.moe_abi_version() == 5
     for s in range(5):
         assert M.moe_status_str(s)
     assert M.moe_status_str(99) == "unknown status"
@@ -189,7 +189,7 @@ def test_tile64_layout_rules():
             assert M.moe_layer_stage_count(d, T) == 7, (name, T)
         assert M.moe_workspace_size(d, 1) > 0
     bad = []
-    for field, value in (("layout", 2), ("layout", -1), ("path", M.MOE_PATH_GEMV),
+    for field, value in (("layout", 3), ("layout", -1), ("path", M.MOE_PATH_GEMV),
                          ("fmt_gate", M.MOE_WFMT_Q6_K), ("fmt_down", M.MOE_WFMT_Q5_K),
                          ("b_gate", FAKE), ("b_down", FAKE)):
         d = good_desc(gen.CONFIGS["deepseek-v4-flash"])
@@ -210,6 +210,77 @@ def test_tile64_layout_rules():
             M.moe_layer_forward(d, FAKE, 0, 1, FAKE, None, None, FAKE, 1 << 40, stream=0)
         want = M.MOE_EINVAL if field == "layout" else M.MOE_EUNSUPPORTED
         assert ei.value.status == want, field
+
+
+def test_mx16_layout_rules():
+    """MX16 (MXFP4 rows with the nibble fields first, then the scale bytes) is
+    read by the per-pair MXFP4 kernels only: such a layer takes the GEMV path at
+    every T, with h quantized once per pair by a kernel of its own; other
+    formats, MXFP8 activations, a forced grouped path and widths past those
+    kernels' plans (256 blocks per row) are refused before anything is
+    enqueued."""
+    d = good_desc(gen.CONFIGS["gpt-oss-20b"])
+    d.layout = M.MOE_LAYOUT_MX16
+    for T in (1, 2, 16, 256):
+        assert M.moe_layer_stage_count(d, T) == 4, T
+        assert [M.moe_layer_stage_name(d, T, i) for i in range(4)] == [
+            "router", "gateup", "hquant", "down"]
+    assert M.moe_workspace_size(d, 1) > 0
+    bad = []
+    for field, value in (("path", M.MOE_PATH_GROUPED), ("act_quant", M.MOE_ACTQ_MXFP8)):
+        d = good_desc(gen.CONFIGS["gpt-oss-20b"])
+        d.layout = M.MOE_LAYOUT_MX16
+        setattr(d, field, value)
+        bad.append((field, d))
+    for name in ("qwen3.6-35b-a3b", "deepseek-v4-flash"):
+        d = good_desc(gen.CONFIGS[name])
+        d.layout = M.MOE_LAYOUT_MX16
+        bad.append((name, d))
+    wide = good_desc(gen.CONFIGS["gpt-oss-20b"].with_(H=32 * 257))
+    wide.layout = M.MOE_LAYOUT_MX16
+    bad.append(("257 blocks", wide))
+    for field, d in bad:
+        assert M.moe_workspace_size(d, 1) == 0, field
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_layer_forward(d, FAKE, 0, 1, FAKE, None, None, FAKE, 1 << 40, stream=0)
+        assert ei.value.status == M.MOE_EUNSUPPORTED, field
+    ok = good_desc(gen.CONFIGS["gpt-oss-20b"].with_(H=32 * 256))
+    ok.layout = M.MOE_LAYOUT_MX16
+    assert M.moe_workspace_size(ok, 1) > 0
+
+
+def test_repack_mx16_validation():
+    """moe_repack_mx16 and moe_test_block_dots_mx16 arguments are checked on the
+    host (nothing enqueued)."""
+    big = 1 << 30
+    bad = [
+        (0, 1536, 4, 2880, FAKE + big, 1536),
+        (FAKE, 1536, 4, 2880, 0, 1536),
+        (FAKE + 8, 1536, 4, 2880, FAKE + big, 1536),
+        (FAKE, 1536, 4, 2880, FAKE + big + 8, 1536),
+        (FAKE, 1536, 0, 2880, FAKE + big, 1536),       # no rows
+        (FAKE, 1536, 4, 2870, FAKE + big, 1536),       # K not a multiple of 32
+        (FAKE, 1529, 4, 2880, FAKE + big, 1536),       # source row shorter than 90 blocks
+        (FAKE, 1536, 4, 2880, FAKE + big, 1520),       # destination row below 1440 + 92
+        (FAKE, 1536, 4, 2880, FAKE + big, 1544),       # destination stride not 16-aligned
+        (FAKE, 1536, 4, 2880, FAKE + 4096, 1536),      # destination overlaps the source
+        (FAKE + 4096, 1536, 4, 2880, FAKE, 1536),
+    ]
+    for i, a in enumerate(bad):
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_repack_mx16(*a, stream=0)
+        assert ei.value.status == M.MOE_EINVAL, i
+    q = M.qact(FAKE, FAKE, None, M.MOE_AFMT_Q8_32, 1, 2880)
+    for i, (stride, K, tok) in enumerate(((1520, 2880, 0), (1536, 2870, 0), (1536, 2880, 1),
+                                         (1544, 2880, 0))):
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_test_block_dots_mx16(FAKE, 4, K, stride, q, tok, FAKE, stream=0)
+        assert ei.value.status == M.MOE_EINVAL, i
+    qw = M.qact(FAKE, FAKE, None, M.MOE_AFMT_Q8_32, 1, 32 * 257)
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_test_block_dots_mx16(FAKE, 4, 32 * 257, 4384, qw, 0, FAKE,
+                                   stream=0)
+    assert ei.value.status == M.MOE_EUNSUPPORTED
 
 
 def test_repack_tile64_validation():
