@@ -939,7 +939,8 @@ __device__ __forceinline__ float2 mx_pair(const uint4 (&pc)[NL], uint8_t* scr, i
 // bytes of block b at byte 16 b, the scale bytes of all blocks after them
 // (block b's at byte 16 nb + b). Every field is aligned, so a lane loads each
 // block it owns as one 16-byte piece straight into registers, and its scale
-// byte from the dword that holds it: no realignment through LDS.
+// byte from its row's scale run, loaded as one dword per lane and handed
+// around the wave: no realignment through LDS.
 //
 // The blocks of a row pair that a lane owns, slot j < NS, are those of
 // mx_pair_blocks in the same order (for activation block i, row 0 then row 1);
@@ -963,11 +964,14 @@ __device__ __forceinline__ Mx16Slot mx16_slot(int j, int nb, int lane) {
 template <int NS>
 struct Mx16Unit {
   uint4 q[NS];
-  uint32_t s[NS];
+  // scale runs of the two rows, one dword per lane: rows of up to 128 blocks
+  // (32 dwords) share one register (lane 32 row + dword); longer rows (NS =
+  // 8) take one register per row
+  uint32_t sd[NS == 8 ? 2 : 1];
 };
 
 // The loads of one row pair: rows r0 and r1 (ok0 / ok1: the row exists);
-// absent blocks read the dummy line.
+// absent blocks and lanes past a scale run read the dummy line.
 template <int NS>
 __device__ __forceinline__ void mx16_issue(Mx16Unit<NS>& u, const uint8_t* r0, const uint8_t* r1,
                                            bool ok0, bool ok1, int nb, int lane,
@@ -978,8 +982,27 @@ __device__ __forceinline__ void mx16_issue(Mx16Unit<NS>& u, const uint8_t* r0, c
     const bool v = sl.ok && (sl.row ? ok1 : ok0);
     const uint8_t* rb = sl.row ? r1 : r0;
     u.q[j] = ld_nt16(v ? rb + 16 * sl.b : dummy);
-    u.s[j] = ld_nt4(v ? rb + 16 * nb + (sl.b & ~3) : dummy);
   }
+  const int nd = (nb + 3) >> 2;  // dwords of a scale run
+  if constexpr (NS == 8) {
+    u.sd[0] = ld_nt4(ok0 && lane < nd ? r0 + 16 * nb + 4 * lane : dummy);
+    u.sd[1] = ld_nt4(ok1 && lane < nd ? r1 + 16 * nb + 4 * lane : dummy);
+  } else {
+    const int row = lane >> 5, dw = lane & 31;
+    const bool ok = (row ? ok1 : ok0) && dw < nd;
+    u.sd[0] = ld_nt4(ok ? (row ? r1 : r0) + 16 * nb + 4 * dw : dummy);
+  }
+}
+
+// Scale byte of slot j's block, from the lane that loaded its dword (all lanes
+// take part in the exchange).
+template <int NS>
+__device__ __forceinline__ int mx16_scale(const Mx16Unit<NS>& u, const Mx16Slot& sl) {
+  const int src = NS == 8 ? sl.b >> 2 : 32 * sl.row + (sl.b >> 2);
+  const uint32_t reg = NS == 8 ? u.sd[sl.row] : u.sd[0];
+  const uint32_t w = static_cast<uint32_t>(
+      __builtin_amdgcn_ds_bpermute(4 * (src & 63), static_cast<int>(reg)));
+  return static_cast<int>((w >> (8 * (sl.b & 3))) & 0xFFu);
 }
 
 // Dot of one block's 16 nibble bytes with its 16 activation pairs: the
@@ -1005,13 +1028,13 @@ __device__ __forceinline__ float mx16_dot(const uint4& q, const half2_t (&ap)[16
 template <int NS, int NBL, class Fn>
 __device__ __forceinline__ void mx16_pair_blocks(const Mx16Unit<NS>& u, const MxAct<NBL>& A,
                                                  int nb, int lane, Fn&& f) {
+  int e[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) e[j] = mx16_scale<NS>(u, mx16_slot<NS>(j, nb, lane));
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const Mx16Slot sl = mx16_slot<NS>(j, nb, lane);
-    if (sl.ok) {
-      const int e = static_cast<int>((u.s[j] >> (8 * (sl.b & 3))) & 0xFFu);
-      f(sl.row, sl.b, sl.i, mx16_dot(u.q[j], A.ap[sl.i]), e);
-    }
+    if (sl.ok) f(sl.row, sl.b, sl.i, mx16_dot(u.q[j], A.ap[sl.i]), e[j]);
   }
 }
 
