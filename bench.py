@@ -693,7 +693,8 @@ def gen_row_bytes(fmt, K):
 
 def kernel_names(cfg, path: str) -> dict:
     """Kernel (as rocprofv3 names it) of each stage of a layer forward (MXFP4
-    layers: the realigning kernels, whose LDS budget every workload here fits)."""
+    layers: the per-pair MXFP4 kernels, whose LDS budget every workload here
+    fits; rows in either order)."""
     import gen
     if path == "gemv":
         mx = gen.MXFP4
