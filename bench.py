@@ -673,16 +673,18 @@ def main():
 
 
 def algo_bytes(cfg, path: str, unique_experts: float) -> dict:
-    """Algorithmic bytes per launch of the two expert kernels. The per-pair path
-    streams every (token, slot) pair's expert rows (T k + shared pairs); the
-    grouped path each selected expert's rows once (unique experts + shared).
-    Padding bytes of a row are not counted."""
+    """Algorithmic bytes per launch of the two expert kernels and the router. The
+    per-pair path streams every (token, slot) pair's expert rows (T k + shared
+    pairs); the grouped path each selected expert's rows once (unique experts
+    + shared). Padding bytes of a row are not counted. The router reads W_r and
+    x."""
     pairs = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
     units = unique_experts if path in ("grouped", "grouped_mx") else pairs
     return {
         "gateup": units * 2 * cfg.F * gen_row_bytes(cfg.fmt_gu, cfg.H),
         "down": units * cfg.H * gen_row_bytes(cfg.fmt_d, cfg.F),
-        "router": 4 * cfg.E * cfg.H,
+        # router weights and the activations they are dotted with
+        "router": 4 * cfg.E * cfg.H + (2 if cfg.x_bf16 else 4) * cfg.T * cfg.H,
     }
 
 
