@@ -66,20 +66,24 @@ def run_stack(descs, cfg, x0, pool=None, prefetch=False, route_descs=None):
     return out
 
 
-@pytest.mark.parametrize("name,T,slots,trans,prefetch", [
-    ("qwen3.6-35b-a3b", 2, 24, 16, False), ("qwen3.6-35b-a3b", 2, 24, 16, True),
-    ("qwen3.6-35b-a3b", 1, 12, 8, True), ("gpt-oss-20b", 3, 14, 12, True),
-    ("deepseek-v4-flash", 2, 20, 12, False)])
-def test_pool_stack_matches_resident(name, T, slots, trans, prefetch):
+@pytest.mark.parametrize("name,T,slots,trans,prefetch,layout", [
+    ("qwen3.6-35b-a3b", 2, 24, 16, False, 0), ("qwen3.6-35b-a3b", 2, 24, 16, True, 0),
+    ("qwen3.6-35b-a3b", 1, 12, 8, True, 0), ("gpt-oss-20b", 3, 14, 12, True, 0),
+    ("deepseek-v4-flash", 2, 20, 12, False, 0),
+    ("gpt-oss-20b", 2, 14, 12, False, M.MOE_LAYOUT_MX16)])
+def test_pool_stack_matches_resident(name, T, slots, trans, prefetch, layout):
     L, steps = 4, 6
     base = SHRUNK[name].with_(T=T)
     stack = make_stack(base, L)
-    dls = [DeviceLayer(data) for data in stack]
+    dls = [DeviceLayer(data, layout=layout) for data in stack]
     cfg = base
     pool = M.Pool(L, cfg.E, cfg.expert_bytes, cfg.gate_bytes, 2 * cfg.gate_bytes, slots, trans)
-    for l, data in enumerate(stack):
+    for l, (data, dl) in enumerate(zip(stack, dls)):
+        # the host tier holds the experts in the layer's own byte order (MX16:
+        # the device repack of the row-order bytes)
+        src = data.pool if layout == 0 else dl.pools[0].cpu().numpy().reshape(data.pool.shape[0], -1)
         for e in range(cfg.E):
-            pool.host_slab(l, e)[:] = data.pool[e]
+            pool.host_slab(l, e)[:] = src[e]
     pdescs = [pool_desc(dl, pool, l) for l, dl in enumerate(dls)]
     rdescs = [dl.desc for dl in dls]
     say(f"pool {name} T={T} slots={slots}/{trans} prefetch={prefetch}")

@@ -33,16 +33,20 @@ def _noalloc(dl, xt, dt, T):
     # the reverse order on the Qwen3.6 decode shape at full size
     [("kimi-k2", 20), ("kimi-k2", 3), ("gpt-oss-20b", 2)],
     [("qwen3.6-35b-a3b-full", 1), ("qwen3.6-35b-a3b-full", 9), ("deepseek-v4-flash", 1)],
+    # MXFP4 rows in the MX16 order: h quantized once per pair in the scratch
+    [("gpt-oss-20b-mx16", 3), ("gpt-oss-20b-mx16", 1)],
 ])
 def test_noalloc_matches_forward(seq):
     for name, T in seq:
-        cfg = gen.CONFIGS["qwen3.6-35b-a3b"] if name.endswith("-full") else SHRUNK[name]
+        cfg = (gen.CONFIGS["qwen3.6-35b-a3b"] if name.endswith("-full")
+               else SHRUNK[name.replace("-mx16", "")])
         say(f"noalloc {cfg.name} T={T}")
         data = gen.make_layer(cfg)
         x, xb = gen.make_x(cfg, T=T, x_index=T + 3)
         # the shrunk Kimi-K2 chunk on the expert-grouped path, the rest as the
         # automatic rule picks
-        dl = DeviceLayer(data, path=M.MOE_PATH_GROUPED if (name, T) == ("kimi-k2", 20) else 0)
+        dl = DeviceLayer(data, path=M.MOE_PATH_GROUPED if (name, T) == ("kimi-k2", 20) else 0,
+                         layout=M.MOE_LAYOUT_MX16 if name.endswith("-mx16") else None)
         xt, dt = x_to_device(data, x, xb)
         assert M.moe_workspace_size(dl.desc, T) <= M.MOE_NOALLOC_SCRATCH_BYTES
         y0, ids0, w0 = run_layer(dl, xt, dt, T)
