@@ -258,7 +258,8 @@ class LayerConfig:
     x_std: float = 1.0
     act_quant: int = 0  # activation numerics: 0 q8, 1 MXFP8 (MXFP4 layers, block-scaled MMA)
     # order of the expert matrices' blocks on the device: 0 rows (GGUF order),
-    # 1 64-row tiles (moe_layout TILE64; layers on the grouped path at every T)
+    # 1 64-row tiles (moe_layout TILE64; layers on the grouped path at every T),
+    # 2 MX16 (MXFP4 rows with aligned nibble fields; the per-pair path)
     layout: int = 0
     description: str = ""
 

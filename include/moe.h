@@ -102,7 +102,8 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
  * tile kernels (all but Q4_K and Q6_K) take the per-(token, slot) GEMV path; the
  * others take the expert-grouped int8-MFMA path when one expert's block bytes
  * reach 8 MB, or when T * (k + shared) * (block bytes of one expert) reaches
- * 160 MB, else the GEMV path (the measured crossover: the grouped path reads
+ * 160 MB, or when the GEMV kernels do not take the shape (LDS budget), else
+ * the GEMV path (the measured crossover: the grouped path reads
  * each selected expert once per 16 tokens at the cost of more launches, and
  * streams large experts faster even for one token). GEMV and GROUPED force a
  * path (GROUPED only where the formats allow it). */
@@ -226,8 +227,11 @@ MOE_API const char* moe_status_str(moe_status s);
 
 /* Bytes of device workspace (256-byte aligned base) that moe_route_topk,
  * moe_expert_ffn and moe_layer_forward need for T tokens of this layer.
- * Returns 0 if the descriptor or T is invalid. The workspace is scratch: its
- * contents on entry do not matter. */
+ * Returns 0 if the descriptor or T is invalid. A valid layer whose expert FFN
+ * no kernel takes (a per-pair shape past the GEMV kernels' LDS budget, in
+ * formats without tile kernels) still gets its size: routing works, and
+ * moe_expert_ffn / moe_layer_forward return MOE_EUNSUPPORTED. The workspace is
+ * scratch: its contents on entry do not matter. */
 MOE_API size_t moe_workspace_size(const moe_layer_desc* desc, int T);
 
 /* Activation quantization. x: device [T, H] fp32 or bf16 (bf16 is upcast

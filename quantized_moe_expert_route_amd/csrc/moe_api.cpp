@@ -206,6 +206,8 @@ bool use_grouped(const moe_layer_desc* d, int T) {
   if (!tiled(d->fmt_gate) || !tiled(d->fmt_down) || T < 1) return false;
   if (d->path == MOE_PATH_GEMV) return false;
   if (d->path == MOE_PATH_GROUPED) return true;
+  // per-pair shapes past the GEMV kernels' LDS budget or task plans: the tiles
+  if (!gemv_fits(make_args(d, T))) return true;
   const double eb = static_cast<double>(expert_block_bytes(d));
   if (eb >= kGroupedMinExpertBytes) return true;
   const int slots = d->top_k + (d->sh_gate != nullptr ? 1 : 0);
