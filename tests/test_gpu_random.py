@@ -1,4 +1,5 @@
-"""Seeded random layers against the oracle: formats (gate/up and down each of
+"""Seeded random layers against the oracle (q8 activations, and MXFP4 layers with
+MXFP8 activations on the block-scaled MFMA path): formats (gate/up and down each of
 the eight), widths, expert counts, top-k up to 16, chunk sizes, routers, shared
 experts, biases, activations, bf16 inputs, row orders (rows, 64-row tiles,
 MX16) and forced paths, combined at random within what the boundary accepts.
@@ -103,6 +104,51 @@ def test_random_layer(case):
         assert err.status == M.MOE_EUNSUPPORTED and (not tiles or path == M.MOE_PATH_GEMV)
         assert M.moe_layer_stage_count(dl.desc, cfg.T) != 7
         pytest.skip("expert FFN refused (MOE_EUNSUPPORTED): routing only")
+    ref = oracle.Layer(data).forward(x, threads=8)
+    assert np.array_equal(ids, ref["ids"]), "expert ids differ"
+    assert np.abs(w - ref["w"]).max() <= 2e-6
+    err = rel_err(y, ref["y"])
+    say(f"  max rel err {err.max():.3e}")
+    assert err.max() <= Y_TOL, err
+
+
+def draw_mx8(case: int):
+    """MXFP4 layers with MXFP8 activations (the block-scaled MFMA path at every T)."""
+    rng = np.random.default_rng(104729 * case + 7)
+    H = int(rng.integers(1, 96 + 1)) * 32
+    F = int(rng.integers(1, 96 + 1)) * 32
+    E = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128]))
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.choice([1, 2, 3, 5, 8, 16, 17, 33]))
+    while T * k > 96 and T > 1:
+        T -= 1
+    return gen.LayerConfig(
+        f"randmx{case}", H=H, F=F, E=E, k=k, T=T, seed=300 + case,
+        router=int(rng.integers(0, 2)), norm_topk=int(rng.integers(0, 2)),
+        fmt_gu=gen.MXFP4, fmt_d=gen.MXFP4, shared=bool(rng.integers(0, 2)),
+        act=int(rng.integers(0, 2)), biases=bool(rng.integers(0, 2)),
+        x_bf16=bool(rng.integers(0, 2)), act_quant=1)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_layer_mx8(case):
+    cfg = draw_mx8(case)
+    say(f"random mx8 case {case}: H={cfg.H} F={cfg.F} E={cfg.E} k={cfg.k} T={cfg.T} "
+        f"router={cfg.router} norm={cfg.norm_topk} shared={cfg.shared} act={cfg.act} "
+        f"biases={cfg.biases} bf16={cfg.x_bf16}")
+    base = gen.make_layer(cfg, experts=[])
+    x, xb = gen.make_x(cfg, T=cfg.T, x_index=case)
+    used = set()
+    for t in range(cfg.T):
+        lg = oracle.router_logits(base.w_router, x[t])
+        used |= {int(e) for e in oracle.topk(lg, cfg.k, base.sel_bias)}
+    if cfg.shared:
+        used.add(cfg.E)
+    data = gen.make_layer(cfg, experts=sorted(used))
+    dl = DeviceLayer(data)
+    assert M.moe_layer_stage_count(dl.desc, cfg.T) == 7
+    xt, dt = x_to_device(data, x, xb)
+    y, ids, w = run_layer(dl, xt, dt, cfg.T)
     ref = oracle.Layer(data).forward(x, threads=8)
     assert np.array_equal(ids, ref["ids"]), "expert ids differ"
     assert np.abs(w - ref["w"]).max() <= 2e-6
