@@ -587,8 +587,9 @@ def cpu_baseline(args, data, cfg, th: int):
     n1 = max(4, int(args.cpu_seconds / tok_s))
     x1 = sample(n1)
     t = time.perf_counter()
-    L.forward(x1, threads=1)
+    ref = L.forward(x1, threads=1)
     s1 = time.perf_counter() - t
+    parity = parity_vs_oracle(data, cfg, x1, ref)
     nn = max(16, int(args.cpu_seconds * th / tok_s))
     xn = sample(nn)
     t = time.perf_counter()
@@ -599,7 +600,47 @@ def cpu_baseline(args, data, cfg, th: int):
                       f"fp64 oracle on {th} host threads, {sn:.1f} s wall; and {n1} tokens on one "
                       f"thread, {s1:.1f} s",
             "single_thread_value": round(n1 / s1, 2),
-            "nproc": os.cpu_count(), "threads_available": th, "cpu_model": cpu_model()}
+            "nproc": os.cpu_count(), "threads_available": th, "cpu_model": cpu_model(),
+            "parity": parity}
+
+
+def parity_vs_oracle(data, cfg, x, ref):
+    """The single-thread sample's tokens through the library (chunks of the
+    workload's T on one layer copy, the benchmark's path and expert order)
+    against the oracle's outputs for them: expert ids exact, routing weights
+    and per-token max |dy| / ||y_ref||."""
+    import numpy as np
+    import torch
+
+    import gen
+    import quantized_moe_expert_route_amd as M
+    from gen.device import DeviceLayer, x_to_device
+
+    dl = DeviceLayer(data)
+    T = cfg.T
+    n = (x.shape[0] // T) * T
+    if n == 0:
+        return None
+    ys, idss, ws_ = [], [], []
+    y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    wsp = dl.workspace(T)
+    for t0 in range(0, n, T):
+        xc = np.ascontiguousarray(x[t0:t0 + T])
+        xt, dt = x_to_device(data, xc, gen.round_bf16(xc) if cfg.x_bf16 else None)
+        M.moe_layer_forward(dl.desc, xt, dt, T, y, ids, w, wsp, wsp.numel())
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy().copy())
+        idss.append(ids.cpu().numpy().copy())
+        ws_.append(w.cpu().numpy().copy())
+    yg, ig, wg = np.concatenate(ys), np.concatenate(idss), np.concatenate(ws_)
+    yr = ref["y"][:n]
+    err = np.abs(yg.astype(np.float64) - yr).max(axis=1) / np.maximum(np.linalg.norm(yr, axis=1), 1e-30)
+    return {"tokens": int(n), "ids_exact": bool(np.array_equal(ig, ref["ids"][:n])),
+            "w_max_abs_err": float(np.abs(wg - ref["w"][:n]).max()),
+            "y_max_rel_err": float(err.max()), "y_tolerance": 2e-3,
+            "pass": bool(np.array_equal(ig, ref["ids"][:n]) and err.max() <= 2e-3)}
 
 
 def main():
