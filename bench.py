@@ -607,8 +607,8 @@ def cpu_baseline(args, data, cfg, th: int):
 def parity_vs_oracle(data, cfg, x, ref):
     """The single-thread sample's tokens through the library (chunks of the
     workload's T on one layer copy, the benchmark's path and expert order)
-    against the oracle's outputs for them: expert ids exact, routing weights
-    and per-token max |dy| / ||y_ref||."""
+    against the oracle's outputs for them: q8 of x bitwise, expert ids exact,
+    routing weights and per-token max |dy| / ||y_ref||."""
     import numpy as np
     import torch
 
@@ -636,8 +636,30 @@ def parity_vs_oracle(data, cfg, x, ref):
         ws_.append(w.cpu().numpy().copy())
     yg, ig, wg = np.concatenate(ys), np.concatenate(idss), np.concatenate(ws_)
     yr = ref["y"][:n]
+    # q8 of x (the q8 format the gate/up rows consume; MXFP8 layers have their
+    # own quantizer): the library's quantizer against the oracle's, bitwise
+    q8_exact = None
+    if not cfg.act_quant:
+        import oracle
+        B = gen.BLOCK_ELEMS[cfg.fmt_gu]
+        afmt = M.MOE_AFMT_Q8_K if B == 256 else M.MOE_AFMT_Q8_32
+        H = cfg.H
+        qs = torch.empty((n, H), dtype=torch.int8, device="cuda")
+        qd = torch.empty((n, H // B), dtype=torch.float32, device="cuda")
+        qb = torch.empty((n, H // 16), dtype=torch.int16, device="cuda")
+        xin = np.ascontiguousarray(x[:n])
+        xt, dt = x_to_device(data, xin, gen.round_bf16(xin) if cfg.x_bf16 else None)
+        M.moe_quantize_act_q8k(xt, dt, n, H, afmt, M.qact(qs, qd, qb if B == 256 else None, afmt, n, H))
+        torch.cuda.synchronize()
+        gq, gd, gb = qs.cpu().numpy(), qd.cpu().numpy(), qb.cpu().numpy()
+        q8_exact = True
+        for t in range(n):
+            a, b, c = oracle.quantize_q8(xin[t], B)
+            q8_exact &= bool(np.array_equal(gq[t], a) and np.array_equal(gd[t].view(np.uint32), b.view(np.uint32))
+                             and (c is None or np.array_equal(gb[t], c)))
     err = np.abs(yg.astype(np.float64) - yr).max(axis=1) / np.maximum(np.linalg.norm(yr, axis=1), 1e-30)
-    return {"tokens": int(n), "ids_exact": bool(np.array_equal(ig, ref["ids"][:n])),
+    return {"tokens": int(n), "q8_x_bitexact": q8_exact,
+            "ids_exact": bool(np.array_equal(ig, ref["ids"][:n])),
             "w_max_abs_err": float(np.abs(wg - ref["w"][:n]).max()),
             "y_max_rel_err": float(err.max()), "y_tolerance": 2e-3,
             "pass": bool(np.array_equal(ig, ref["ids"][:n]) and err.max() <= 2e-3)}
