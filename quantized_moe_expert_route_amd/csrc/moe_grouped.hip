@@ -304,8 +304,8 @@ __device__ __forceinline__ void dump_sums(int32_t* dump, int m, int T, int n_row
 
 // ------------------------------------------------ LDS-staged Q4_K tile stream
 // One work item streams the Q4_K rows of a few consecutive row blocks of one
-// tile through a 3-slot LDS ring filled by direct global->LDS loads
-// (global_load_lds_dwordx4), two super-blocks ahead of the compute, so no
+// tile through a 2-slot LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4), one super-block ahead of the compute, so no
 // weight bytes sit in registers while in flight. A slot holds one super-block
 // of 128 weight rows (gate/up: 64 rows of each; down: 128 rows) and of the
 // tile's 16 activation rows:
@@ -316,17 +316,19 @@ constexpr int kStBytes = kStD + 256;     // 23808 B per slot
 
 // MODE 0: gate/up (streams: gate and up rows of one 16-row tile per wave, 64
 // rows per row block). MODE 1: down (two 16-row tiles per wave, 128 rows per
-// row block). grid 8 * ceil(max items / 8), block 256 (4 waves, 2 per SIMD).
+// row block). grid 8 * ceil(max items / 8), block 256 (4 waves). Two slots
+// (47.6 KB) let three workgroups share a compute unit, so each ring's stage
+// waits and barriers are covered by two others (three slots, one more stage
+// in flight per ring but only two workgroups per unit, measured slower).
 // Item = (tile, ii): row blocks [ii RBG, min(RB, (ii + 1) RBG)). Layers without
 // expert biases only (those take the register-staged kernels).
 // DUMP: also write the integer super-block sums to a.dump (test export).
 template <int MODE, bool DUMP>
-__global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG, int RB) {
-  // three separate arrays: with the slot known at each access the compiler can
-  // tell a slot being filled from the slot being read (no forced vmcnt(0))
+__global__ __launch_bounds__(256, DUMP ? 2 : 3) void k_glds_q4k(KArgs a, Div dIPT, int RBG, int RB) {
+  // separate arrays: with the slot known at each access the compiler can tell
+  // a slot being filled from the slot being read (no forced vmcnt(0))
   __shared__ __align__(16) uint8_t lds0[kStBytes];
   __shared__ __align__(16) uint8_t lds1[kStBytes];
-  __shared__ __align__(16) uint8_t lds2[kStBytes];
   const int n_tiles = static_cast<int>(*gp<uint32_t>(a.counters));
   const int item = grouped_item(n_tiles * static_cast<int>(dIPT.d));
   if (item < 0) return;
@@ -440,17 +442,15 @@ __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG,
   for (int i = 0; i < 4; ++i) __asm__ volatile("" ::"v"(wp[i]), "v"(pC[i].x));
   const int nst = (rb1 - rb0) * nb;
   issue(lds0, rb0, 0);
-  if (nst > 1) issue(lds1, rb0 + (nb > 1 ? 0 : 1), nb > 1 ? 1 : 0);
   v4f acc[2], mn[2];
   int rb = rb0, b = 0;          // stage s: row block rb, super-block b
-  int rbn = rb0, bn = 0;        // stage s + 2
-  for (int k2 = 0; k2 < 2; ++k2) { if (++bn == nb) { bn = 0; ++rbn; } }
-  // stage s: read slot s % 3, refill slot (s + 2) % 3
+  int rbn = rb0, bn = 0;        // stage s + 1
+  if (++bn == nb) { bn = 0; ++rbn; }
+  // stage s: read slot s % 2, refill the other slot with stage s + 1
   auto step = [&](int s, const uint8_t* L, uint8_t* Lw) {
-    // Loads complete in issue order, so this wave's loads of stage s are done
-    // once at most the 6 of stage s + 1 are outstanding (stores may still be);
-    // the barrier then publishes every wave's share of the slot.
-    if (s + 1 < nst) wait_vm<6>(); else wait_vm<0>();
+    // this wave's loads of stage s are the only ones outstanding: once they
+    // are done, the barrier publishes every wave's share of the slot
+    wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG,
       for (int j = 0; j < 2; ++j) acc[j] = mn[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
     // the slot of stage s - 1 is free: every wave has passed its compute
-    if (s + 2 < nst) issue(Lw, rbn, bn);
+    if (s + 1 < nst) issue(Lw, rbn, bn);
     if (++bn == nb) { bn = 0; ++rbn; }
     __builtin_amdgcn_sched_barrier(0);
     ActSB x;
@@ -519,10 +519,9 @@ __global__ __launch_bounds__(256, 2) void k_glds_q4k(KArgs a, Div dIPT, int RBG,
     }
     if (++b == nb) { b = 0; ++rb; }
   };
-  for (int s = 0; s < nst; s += 3) {
-    step(s, lds0, lds2);
+  for (int s = 0; s < nst; s += 2) {
+    step(s, lds0, lds1);
     if (s + 1 < nst) step(s + 1, lds1, lds0);
-    if (s + 2 < nst) step(s + 2, lds2, lds1);
   }
 }
 
@@ -548,15 +547,18 @@ __device__ __forceinline__ uint2 lds8_a2(const uint8_t* L, int off) {
 }
 
 // Down rows of Q6_K experts: item = (tile, ii), row blocks of 64 rows of H,
-// wave w takes rows 16 w .. 16 w + 15 of a block. Same ring protocol as
-// k_glds_q4k, 5 slot loads per wave and stage. Layers without down biases.
-// With 64-row tiles a stage is one 13440-byte run, held in the slot as is
-// (row pitch 210 instead of kQ6Row).
-template <bool DUMP>
-__global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int RBG, int RB) {
+// wave w takes rows 16 w .. 16 w + 15 of a block. Same 2-slot ring protocol
+// as k_glds_q4k, 5 slot loads per wave and stage. Layers without down biases.
+// TILED (64-row tiles): a stage is one 13440-byte run, held in the slot's
+// weight pieces as is (row pitch 210 instead of kQ6Row). Two slots of 19712
+// bytes let four 4-wave workgroups share a compute unit's 160 KB of LDS, so
+// each ring's stage waits and barriers are covered by three others.
+template <bool DUMP, bool TILED>
+__global__ __launch_bounds__(256, DUMP ? 2 : 4) void k_glds_q6k_down(KArgs a, Div dIPT, int RBG,
+                                                                     int RB) {
+  static_assert(4 * 2 * kS6Bytes <= 160 * 1024, "four workgroups per compute unit");
   __shared__ __align__(16) uint8_t lds0[kS6Bytes];
   __shared__ __align__(16) uint8_t lds1[kS6Bytes];
-  __shared__ __align__(16) uint8_t lds2[kS6Bytes];
   const int n_tiles = static_cast<int>(*gp<uint32_t>(a.counters));
   const int item = grouped_item(n_tiles * static_cast<int>(dIPT.d));
   if (item < 0) return;
@@ -575,7 +577,7 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
   for (int u = 0; u < 4; ++u) {
     const int j = min(wave + 4 * u, 14);
     const int i = 64 * j + lane;
-    if (a.tiled) {
+    if (TILED) {
       // 840 pieces per stage; lanes past them reload the last one (their LDS
       // bytes lie past the 64 blocks and are not read)
       wsrc[u] = tl.down + 16 * min(i, 839);
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
       wsrc[u] = tl.down + static_cast<size_t>(R) * a.stride_down + 16 * q;
     }
   }
-  const size_t rbs = a.tiled ? static_cast<size_t>(nb) * 13440 : 64 * a.stride_down;
+  const size_t rbs = TILED ? static_cast<size_t>(nb) * 13440 : 64 * a.stride_down;
   const uint8_t* asrc;
   {
     const int j = wave == 3 ? 15 : 16 + wave;
@@ -598,7 +600,7 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
   const uint8_t* dsrc =
       reinterpret_cast<const uint8_t*>(a.hd + static_cast<size_t>(pair_of(lane & 15).x) * nb);
   auto issue = [&](uint8_t* L, int rb, int b) {
-    const size_t wo = rb * rbs + (a.tiled ? static_cast<size_t>(13440) * b : (210 * b) & ~15);
+    const size_t wo = rb * rbs + (TILED ? static_cast<size_t>(13440) * b : (210 * b) & ~15);
 #pragma unroll
     for (int u = 0; u < 3; ++u) dma16(wsrc[u] + wo, L + 1024 * (wave + 4 * u));
     if (wave < 3) {
@@ -623,18 +625,17 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
   for (int i = 0; i < 4; ++i) __asm__ volatile("" ::"v"(wp[i]), "v"(pC[i].x));
   const int nst = (rb1 - rb0) * nb;
   issue(lds0, rb0, 0);
-  if (nst > 1) issue(lds1, rb0 + (nb > 1 ? 0 : 1), nb > 1 ? 1 : 0);
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f}, mn = acc;
   int rb = rb0, b = 0, rbn = rb0, bn = 0;
-  for (int k2 = 0; k2 < 2; ++k2) { if (++bn == nb) { bn = 0; ++rbn; } }
+  if (++bn == nb) { bn = 0; ++rbn; }  // stage s + 1
   auto step = [&](int s, const uint8_t* L, uint8_t* Lw) {
-    if (s + 1 < nst) wait_vm<5>(); else wait_vm<0>();
+    wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     if (b == 0) acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    if (s + 2 < nst) issue(Lw, rbn, bn);
+    if (s + 1 < nst) issue(Lw, rbn, bn);
     if (++bn == nb) { bn = 0; ++rbn; }
     __builtin_amdgcn_sched_barrier(0);
     ActSB x;
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
       x.dC[0] = dc.x; x.dC[1] = dc.y; x.dC[2] = dc.z; x.dC[3] = dc.w;
     }
     WQ6K w;
-    const int blk = a.tiled ? (wave * 16 + c) * 210 : (wave * 16 + c) * kQ6Row + ((210 * b) & 15);
+    const int blk = TILED ? (wave * 16 + c) * 210 : (wave * 16 + c) * kQ6Row + ((210 * b) & 15);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       w.l0[h] = lds8_a2(L, blk + 64 * h + 8 * g);
@@ -674,10 +675,9 @@ __global__ __launch_bounds__(256, 2) void k_glds_q6k_down(KArgs a, Div dIPT, int
     }
     if (++b == nb) { b = 0; ++rb; }
   };
-  for (int s = 0; s < nst; s += 3) {
-    step(s, lds0, lds2);
+  for (int s = 0; s < nst; s += 2) {
+    step(s, lds0, lds1);
     if (s + 1 < nst) step(s + 1, lds1, lds0);
-    if (s + 2 < nst) step(s + 2, lds2, lds1);
   }
 }
 
@@ -1236,8 +1236,9 @@ __global__ void k_tile_setup(KArgs a, const uint8_t* rows, int n_tok) {
 }
 
 // Row blocks per LDS-staged work item: long enough streams to amortize the
-// ring fill, while keeping about 9216 items (18 rounds of two workgroups per
-// compute unit: a short tail) at the bound on tiles.
+// ring fill, while keeping about 9216 items at the bound on tiles (12 rounds
+// of the Q4_K kernel's three workgroups per compute unit, 9 of the Q6_K
+// kernel's four: a short tail).
 int glds_group(int RB, int max_tiles) {
   int g = (RB * max_tiles + 9215) / 9216;
   if (g < 1) g = 1;
@@ -1350,8 +1351,8 @@ hipError_t launch_down_grouped(const KArgs& a, hipStream_t s, Ev ev) {
   }
   if (a.b_down == nullptr) {
     const int RB = a.H / 64, RBG = glds_group(RB, mt), IPT = (RB + RBG - 1) / RBG;
-    return launch(k_glds_q6k_down<false>, dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a,
-                  Div::make(IPT), RBG, RB);
+    return launch(a.tiled ? k_glds_q6k_down<false, true> : k_glds_q6k_down<false, false>,
+                  dim3(grouped_grid(mt * IPT)), 256, 0, s, ev, a, Div::make(IPT), RBG, RB);
   }
   constexpr int NT = down_tiles<FMT_Q6_K>();
   const int RB = a.H / (64 * NT);
@@ -1406,7 +1407,7 @@ hipError_t launch_tile_dots(int mode, const void* rows, int n_rows, int K, size_
   const dim3 grid(grouped_grid(IPT));
   if (mode == 0) return launch(k_glds_q4k<0, true>, grid, 256, 0, s, Ev{}, a, Div::make(IPT), RBG, RB);
   if (mode == 1) return launch(k_glds_q4k<1, true>, grid, 256, 0, s, Ev{}, a, Div::make(IPT), RBG, RB);
-  return launch(k_glds_q6k_down<true>, grid, 256, 0, s, Ev{}, a, Div::make(IPT), RBG, RB);
+  return launch(k_glds_q6k_down<true, false>, grid, 256, 0, s, Ev{}, a, Div::make(IPT), RBG, RB);
 }
 
 }  // namespace moe

@@ -79,10 +79,10 @@ constexpr int kMxSlot = kMxBias + 256;        // 26112 B per slot
 // computes rows 16 w .. 16 w + 15. Item = (tile, ii): row blocks [ii RBG,
 // min(RB, (ii + 1) RBG)). grid 8 * ceil(max items / 8), block 256.
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void k_gmx(KArgs a, Div dIPT, int RBG, int RB) {
+__global__ __launch_bounds__(256, 3) void k_gmx(KArgs a, Div dIPT, int RBG, int RB) {
+  // two slots (52.2 KB): three workgroups share a compute unit
   __shared__ __align__(16) uint8_t lds0[kMxSlot];
   __shared__ __align__(16) uint8_t lds1[kMxSlot];
-  __shared__ __align__(16) uint8_t lds2[kMxSlot];
   const int n_tiles = static_cast<int>(*gp<uint32_t>(a.counters));
   const int item = mx_item(n_tiles * static_cast<int>(dIPT.d));
   if (item < 0) return;
@@ -113,10 +113,9 @@ __global__ __launch_bounds__(256, 2) void k_gmx(KArgs a, Div dIPT, int RBG, int 
   // weights (piece i = 64 j + lane: row R = i / 17, part q = i % 17), 17..24
   // activations (LDS piece (ts, ql) holds global piece ql ^ ts; only the
   // slots holding one of the tile's cnt token rows), 25 scale bytes (4 per
-  // lane), 26 biases (4 bytes per lane; layers with biases). Each wave's count
-  // per stage is fixed for the tile (my_loads), which the ring's waits need:
-  // the issue code indexes no register array dynamically (a spill to scratch
-  // would add memory operations of its own).
+  // lane), 26 biases (4 bytes per lane; layers with biases). The issue code
+  // indexes no register array dynamically (a spill to scratch would add
+  // memory operations of its own).
   int wR[5], wq[5];
 #pragma unroll
   for (int u = 0; u < 5; ++u) {
@@ -197,34 +196,20 @@ __global__ __launch_bounds__(256, 2) void k_gmx(KArgs a, Div dIPT, int RBG, int 
   const int nst = (rb1 - rb0) * nbs;
   // stage st -> (row block, stage within the row block)
   issue(lds0, rb0, 0);
-  if (nst > 1) issue(lds1, rb0 + (nbs > 1 ? 0 : 1), nbs > 1 ? 1 : 0);
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   int rb = rb0, sb = 0, rbn = rb0, sbn = 0;
-  for (int k2 = 0; k2 < 2; ++k2) { if (++sbn == nbs) { sbn = 0; ++rbn; } }
-  // this wave's slot loads per stage (weights, activations, scales, biases)
-  const int n_act = (2 * (ja - 17) < cnt ? 1 : 0) + (2 * (ja + 4 - 17) < cnt ? 1 : 0);
-  const int my_loads = (wave == 0 ? 5 : 4) + n_act + (wave == 1 ? 1 : 0) +
-                       (wave == 2 && has_bias ? 1 : 0);
+  if (++sbn == nbs) { sbn = 0; ++rbn; }  // stage st + 1
+  // stage st: read slot st % 2, refill the other slot with stage st + 1
   auto step = [&](int st, const uint8_t* L, uint8_t* Lw) {
-    // loads complete in issue order: this wave's loads of stage st are done
-    // once at most its loads of stage st + 1 are outstanding; the barrier
-    // then publishes every wave's share of the slot
-    if (st + 1 < nst) {
-      switch (my_loads) {  // wave-uniform
-        case 7: wait_vm<7>(); break;
-        case 6: wait_vm<6>(); break;
-        case 5: wait_vm<5>(); break;
-        default: wait_vm<4>(); break;
-      }
-    } else {
-      wait_vm<0>();
-    }
+    // this wave's loads of stage st are the only ones outstanding: once they
+    // are done, the barrier publishes every wave's share of the slot
+    wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     if (sb == 0) acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     // the slot of stage st - 1 is free: every wave has passed its compute
-    if (st + 2 < nst) issue(Lw, rbn, sbn);
+    if (st + 1 < nst) issue(Lw, rbn, sbn);
     if (++sbn == nbs) { sbn = 0; ++rbn; }
     __builtin_amdgcn_sched_barrier(0);
     const int nbv = min(kMxBlocks, nb - sb * kMxBlocks);  // valid blocks in this stage
@@ -297,10 +282,9 @@ __global__ __launch_bounds__(256, 2) void k_gmx(KArgs a, Div dIPT, int RBG, int 
     }
     if (++sb == nbs) { sb = 0; ++rb; }
   };
-  for (int st = 0; st < nst; st += 3) {
-    step(st, lds0, lds2);
+  for (int st = 0; st < nst; st += 2) {
+    step(st, lds0, lds1);
     if (st + 1 < nst) step(st + 1, lds1, lds0);
-    if (st + 2 < nst) step(st + 2, lds2, lds1);
   }
 }
 
