@@ -729,10 +729,13 @@ __device__ __forceinline__ void router_quant_wave(const KArgs& a, int job, int l
 
 // Router logits for many tokens: fp32 inputs, fp64 MFMA products and sums (the
 // products of fp32 values are exact in fp64). grid nwg_r + quant workgroups,
-// block 256. Router wave w: K slice w % KS of (token tile, expert tile) w / KS;
-// column E of the expert tiles is the shared-expert gate vector when present.
-// Quant waves: q8 of one 256-element piece of x. BF: x in bf16 (else fp32), a
-// template argument so that no dtype branch sits between the batched loads.
+// block 256. Router workgroup w: K slice w % KS of (token tile, expert tile)
+// w / KS, its four waves taking every fourth 16-k step of the slice (four
+// short MFMA chains on four SIMDs instead of one long one), their fp64 sums
+// added in wave order in LDS; column E of the expert tiles is the
+// shared-expert gate vector when present. Quant waves: q8 of one 256-element
+// piece of x. BF: x in bf16 (else fp32), a template argument so that no dtype
+// branch sits between the batched loads.
 template <bool BF>
 __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS, int L, int n_et,
                                                      int n_work, int nwg_r) {
@@ -741,8 +744,9 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
     if (quant) router_quant_wave(a, (blockIdx.x - nwg_r) * 4 + wave, lane);
     return;
   }
-  const int wv = blockIdx.x * 4 + wave;
+  const int wv = blockIdx.x;  // workgroup-uniform: the early exit skips no barrier
   if (wv >= n_work) return;
+  __shared__ v4d red[3][64];
   const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
   const int ks = wv % KS, r = wv / KS, et = r % n_et, tt = r / n_et;
   const int g = lane >> 4, c = lane & 15;
@@ -769,23 +773,32 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
     return make_float4(bf16_bits_to_f32(bb.x & 0xFFFF), bf16_bits_to_f32(bb.x >> 16),
                        bf16_bits_to_f32(bb.y & 0xFFFF), bf16_bits_to_f32(bb.y >> 16));
   };
-  // MFMA step n, lane group g: k = k0 + 16 n + 4 g + s for s = 0..3 (the same
-  // k for A and B, so the k order is only a reordering of the sum). The loads
-  // of U steps are issued before their MFMAs: one memory round trip per U
-  // steps (a slice of up to 256 k is one round trip); steps past the slice
-  // reload its last step and are not multiplied.
+  // MFMA step n (wave n % 4), lane group g: k = k0 + 16 n + 4 g + s for
+  // s = 0..3 (the same k for A and B, so the k order is only a reordering of
+  // the sum). The loads of U steps are issued before their MFMAs: one memory
+  // round trip per U steps of the wave (a slice of up to 1024 k is one round
+  // trip); steps past the slice reload its last step and are not multiplied.
   constexpr int U = 16;
-  for (int n = 0; n < nst; n += U) {
+  for (int n = wave; n < nst; n += 4 * U) {
     float4 xv[U], wv4[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kk = k0 + 16 * min(n + u, nst - 1) + 4 * g;
+      const int kk = k0 + 16 * min(n + 4 * u, nst - 1) + 4 * g;
       xv[u] = load_xv(kk);
       wv4[u] = ldg_f4(wr + kk);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (n + u < nst) step(xv[u], wv4[u]);
+      if (n + 4 * u < nst) step(xv[u], wv4[u]);
+  }
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    const v4d o = red[w][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += o[i];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1286,8 +1299,8 @@ hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hip
                   256, 0, s, ev, a, quant ? 1 : 0, rs.ks, rs.len, n_et2, n_work, nwg_r);
   }
   const int n_et = (E1 + 15) / 16, n_tt = (a.T + 15) / 16;
-  const int n_work = n_tt * n_et * rs.ks;
-  const int nwg_r = (n_work + 3) / 4;
+  const int n_work = n_tt * n_et * rs.ks;  // one workgroup per (tile pair, slice)
+  const int nwg_r = n_work;
   return launch(a.x_dtype ? k_router_mfma<true> : k_router_mfma<false>, dim3(nwg_r + nq), 256,
                 0, s, ev, a, quant ? 1 : 0, rs.ks, rs.len, n_et, n_work, nwg_r);
 }
