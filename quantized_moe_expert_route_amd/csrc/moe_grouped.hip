@@ -809,14 +809,15 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
 }
 
 // Router logits, 2 x 2 register blocking (chunks of more than 16 tokens and
-// 16 experts): a router wave computes token tiles 2 tt .. 2 tt + 1 against
-// expert tiles 2 et .. 2 et + 1 over one of 8 K slices. Each loaded x and W
-// fragment feeds two MFMAs, and the four accumulators are independent chains.
-// K slice s is computed by workgroups s, s + 8, s + 16, ..., the ones that run
-// on XCD s (dispatch order), so each slice's x and W are read into one L2. Same
-// sums and partial layout as k_router_mfma (the k order inside a slice is only
-// a reordering of the sum). grid nwg_r (8 per 4 tile pairs) + quant
-// workgroups, block 256. BF as in k_router_mfma.
+// 16 experts): a router workgroup computes token tiles 2 tt .. 2 tt + 1
+// against expert tiles 2 et .. 2 et + 1 over one of 8 K slices, its four waves
+// taking every fourth 16-k step and adding their fp64 sums in wave order in
+// LDS. Each loaded x and W fragment feeds two MFMAs, and the four accumulators
+// are independent chains. K slice s is computed by workgroups s, s + 8, s + 16,
+// ..., the ones that run on XCD s (dispatch order), so each slice's x and W are
+// read into one L2. Same sums and partial layout as k_router_mfma (the k order
+// inside a slice is only a reordering of the sum). grid nwg_r (8 per tile
+// pair) + quant workgroups, block 256. BF as in k_router_mfma.
 template <bool BF>
 __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int KS, int L,
                                                        int n_et2, int n_work, int nwg_r) {
@@ -826,8 +827,9 @@ __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int K
     return;
   }
   const int ks = blockIdx.x & 7;  // KS == 8
-  const int r = (blockIdx.x >> 3) * 4 + wave;  // tile pair
+  const int r = blockIdx.x >> 3;  // tile pair (workgroup-uniform: the exit skips no barrier)
   if (r >= n_work || ks >= KS) return;
+  __shared__ v4d red[3][2][2][64];
   const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
   const int et2 = r % n_et2, tt2 = r / n_et2;
   const int g = lane >> 4, c = lane & 15;
@@ -868,14 +870,14 @@ __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int K
             static_cast<double>(xv[i].w), static_cast<double>(wv4[j].w), acc[i][j], 0, 0, 0);
       }
   };
-  // MFMA step n, lane group g: k = k0 + 16 n + 4 g + s for s = 0..3
-  constexpr int U = 8;  // steps whose loads are issued together
-  int n = 0;
-  for (; n + U <= nst; n += U) {
+  // MFMA step n (wave n % 4), lane group g: k = k0 + 16 n + 4 g + s for s = 0..3
+  // (steps past the slice reload its last step and are not multiplied)
+  constexpr int U = 4;  // steps of the wave whose loads are issued together
+  for (int n = wave; n < nst; n += 4 * U) {
     float4 xv[U][2], wv4[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kk = k0 + 16 * (n + u) + 4 * g;
+      const int kk = k0 + 16 * min(n + 4 * u, nst - 1) + 4 * g;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         xv[u][i] = load_xv(t[i], kk);
@@ -883,18 +885,26 @@ __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int K
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) step(xv[u], wv4[u]);
+    for (int u = 0; u < U; ++u)
+      if (n + 4 * u < nst) step(xv[u], wv4[u]);
   }
-  for (; n < nst; ++n) {
-    const int kk = k0 + 16 * n + 4 * g;
-    float4 xv[2], wv4[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      xv[i] = load_xv(t[i], kk);
-      wv4[i] = ldg_f4(wr[i] + kk);
-    }
-    step(xv, wv4);
-  }
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (wave > 0) red[wave - 1][i][j][lane] = acc[i][j];
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const v4d o = red[w][i][j][lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][q] += o[q];
+      }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1294,7 +1304,7 @@ hipError_t launch_router_grouped(const KArgs& a, bool quant, RouterSplit rs, hip
   if (router_blocked(a.T, a.E)) {
     const int n_et2 = (E1 + 31) / 32, n_tt2 = (a.T + 31) / 32;
     const int n_work = n_tt2 * n_et2;  // tile pairs, each in all 8 K slices
-    const int nwg_r = 8 * ((n_work + 3) / 4);
+    const int nwg_r = 8 * n_work;
     return launch(a.x_dtype ? k_router_mfma22<true> : k_router_mfma22<false>, dim3(nwg_r + nq),
                   256, 0, s, ev, a, quant ? 1 : 0, rs.ks, rs.len, n_et2, n_work, nwg_r);
   }
