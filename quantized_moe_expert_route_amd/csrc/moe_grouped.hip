@@ -776,9 +776,10 @@ __global__ __launch_bounds__(256) void k_router_mfma(KArgs a, int quant, int KS,
   // MFMA step n (wave n % 4), lane group g: k = k0 + 16 n + 4 g + s for
   // s = 0..3 (the same k for A and B, so the k order is only a reordering of
   // the sum). The loads of U steps are issued before their MFMAs: one memory
-  // round trip per U steps of the wave (a slice of up to 1024 k is one round
-  // trip); steps past the slice reload its last step and are not multiplied.
-  constexpr int U = 16;
+  // round trip per U steps of the wave (a slice of up to 256 k is one round
+  // trip; short batches keep the registers, and so the waves per SIMD, in
+  // bounds); steps past the slice reload its last step and are not multiplied.
+  constexpr int U = 4;
   for (int n = wave; n < nst; n += 4 * U) {
     float4 xv[U], wv4[U];
 #pragma unroll
@@ -872,7 +873,7 @@ __global__ __launch_bounds__(256) void k_router_mfma22(KArgs a, int quant, int K
   };
   // MFMA step n (wave n % 4), lane group g: k = k0 + 16 n + 4 g + s for s = 0..3
   // (steps past the slice reload its last step and are not multiplied)
-  constexpr int U = 4;  // steps of the wave whose loads are issued together
+  constexpr int U = 2;  // steps of the wave whose loads are issued together
   for (int n = wave; n < nst; n += 4 * U) {
     float4 xv[U][2], wv4[U][2];
 #pragma unroll
