@@ -928,19 +928,22 @@ __global__ __launch_bounds__(256) void k_topk_sum(KArgs a, int KS) {
   const int E1 = a.E + (a.sh_gate_vec ? 1 : 0);
   const double* rp = a.rpart + static_cast<size_t>(t) * E1;
   const size_t kstride = static_cast<size_t>(a.T) * E1;
-  double s[NC];
+  double s[NC], sg = 0.0;
 #pragma unroll
   for (int i = 0; i < NC; ++i) s[i] = 0.0;
+  // column E (the shared-expert gate, when present) rides in the same batches
+  const int col_sh = a.sh_gate_vec ? a.E : a.E - 1;
   // slices in batches whose loads are all issued before the first add (one
   // memory round trip per batch); the sums still run in slice order
   constexpr int KB = NC <= 4 ? 16 : NC <= 8 ? 8 : 4;
   for (int k0 = 0; k0 < KS; k0 += KB) {
-    double v[KB][NC];
+    double v[KB][NC], vs[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int ks = min(k0 + kb, KS - 1);
 #pragma unroll
       for (int i = 0; i < NC; ++i) v[kb][i] = rp[ks * kstride + min(lane + 64 * i, a.E - 1)];
+      vs[kb] = rp[ks * kstride + col_sh];
     }
     // keep the compiler from interleaving the adds with the loads (it would
     // otherwise keep only a few loads in flight)
@@ -950,6 +953,7 @@ __global__ __launch_bounds__(256) void k_topk_sum(KArgs a, int KS) {
       if (k0 + kb < KS) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) s[i] += v[kb][i];
+        sg += vs[kb];
       }
     }
   }
@@ -959,11 +963,7 @@ __global__ __launch_bounds__(256) void k_topk_sum(KArgs a, int KS) {
     lg[i] = static_cast<float>(s[i]);
     if (lane + 64 * i < a.E) a.logits[static_cast<size_t>(t) * a.E + lane + 64 * i] = lg[i];
   }
-  if (a.sh_gate_vec && lane == 0) {
-    double sg = 0.0;
-    for (int ks = 0; ks < KS; ++ks) sg += rp[ks * kstride + a.E];
-    a.shw[t] = static_cast<float>(1.0 / (1.0 + exp(-sg)));
-  }
+  if (a.sh_gate_vec && lane == 0) a.shw[t] = static_cast<float>(1.0 / (1.0 + exp(-sg)));
   wave_topk_regs<NC>(lg, a.sel_bias, a.E, a.k, a.router, a.norm_topk, a.route_scale,
                      a.ids + t * a.k, a.w + t * a.k);
 }
